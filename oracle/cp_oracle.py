@@ -1,0 +1,293 @@
+"""CPU oracle for the THD context-parallel token layout and the owner gradient return.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library imports this module; only the
+tests, the smoke check and the CPU-baseline leg of the benchmark call it.  It
+shares no code, header, table or constant with the HIP library.
+
+Everything here is a plain, slow, literal restatement of what the method
+computes, in numpy (integer index arrays, fancy indexing as the gather
+primitive, float32 adds one slot at a time).  Every function is exact: the
+token layouts are permutations, and the gradient sums are defined by one fixed
+order, so each output has exactly one correct bit pattern.
+
+Sources (the pages; see their titles):
+  * "[PyTorch] Add experimental packed-contiguous THD all-gather CP"
+    (TransformerEngine PR 3221), sections "Conversation" (commit messages),
+    "Why" and "Scope and constraints": the per-document DualChunkSwap partition
+    (every document cut into 2*cp_size chunks) and the packed-contiguous policy
+    (the whole physical buffer cut into cp_size equal chunks, document
+    boundaries kept through per-rank sequence metadata).
+  * "Add stream-ordered CP gradient return primitive" (TransformerEngine PR
+    3235), sections "Description", "Sequence Diagram" and the author's reply
+    on the ownership rule: owner o receives native sequence chunks o and
+    2N-1-o; writers scatter global dK/dV into owner slots indexed
+    [owner][writer], publish an epoch, owners wait for all epochs and then
+    accumulate slots 0..cp_size-1.
+  * "Low Latency Communication Kernels with NVSHMEM" (GPU MODE lecture 87
+    notes), exercise list: the 1 KB - 16 MB sum sweep.
+
+Readings where the pages are silent (the design notes list them all):
+  * a DualChunkSwap rank stores its tokens document-major, and inside a
+    document chunk r before chunk 2W-1-r, so its local cu_seqlens are cu/W;
+  * a document whose length is not a multiple of 2W (DualChunkSwap) or a
+    total length not a multiple of W (packed-contiguous) is rejected;
+  * packed-contiguous local cu_seqlens are the sorted set of boundaries that
+    fall inside the rank's slice, plus 0 and the slice length, padded with
+    the slice length up to num_docs+1 entries;
+  * the owner's output is overwritten with the sum (not accumulated into);
+  * the fp32 accumulator is seeded with slot 0 (so -0.0 survives) and slots
+    are added in writer order 0..W-1;
+  * fp32 -> bf16 is round-to-nearest-even on the bit pattern; NaN stays a
+    quiet NaN with its sign; denormals are kept.
+
+bf16 tensors are represented here as numpy uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+DUAL_CHUNK_SWAP = "dual_chunk_swap"
+PACKED_CONTIGUOUS = "packed_contiguous"
+POLICIES = (DUAL_CHUNK_SWAP, PACKED_CONTIGUOUS)
+
+
+# --------------------------------------------------------------------------
+# cu_seqlens validation (PR 3221 "Scope and constraints"; PR 3235 reply on
+# CP-size-generic ownership).
+# --------------------------------------------------------------------------
+def cu_violations(cu, total_tokens, cp_size, policy):
+    """Return the set of named conditions a cu_seqlens array violates.
+
+    Names: "first_not_zero", "decreasing", "last_not_total",
+    "doc_not_divisible" (DualChunkSwap: some document length is not a multiple
+    of 2*cp_size), "total_not_divisible" (packed-contiguous: total tokens not a
+    multiple of cp_size).
+    """
+    cu = [int(v) for v in cu]
+    bad = set()
+    if cu[0] != 0:
+        bad.add("first_not_zero")
+    for b in range(len(cu) - 1):
+        if cu[b + 1] < cu[b]:
+            bad.add("decreasing")
+    if cu[-1] != total_tokens:
+        bad.add("last_not_total")
+    if policy == DUAL_CHUNK_SWAP:
+        for b in range(len(cu) - 1):
+            if (cu[b + 1] - cu[b]) % (2 * cp_size) != 0:
+                bad.add("doc_not_divisible")
+    elif policy == PACKED_CONTIGUOUS:
+        if total_tokens % cp_size != 0:
+            bad.add("total_not_divisible")
+    else:
+        raise ValueError(policy)
+    return bad
+
+
+def _require_valid(cu, total_tokens, cp_size, policy):
+    bad = cu_violations(cu, total_tokens, cp_size, policy)
+    if bad:
+        raise ValueError(f"invalid cu_seqlens for {policy}, W={cp_size}: {sorted(bad)}")
+
+
+# --------------------------------------------------------------------------
+# Ownership maps: which global token each rank's local rows hold.
+# --------------------------------------------------------------------------
+def dcs_rank_rows(cu, cp_size, rank):
+    """Global token index of every local row of `rank` under DualChunkSwap.
+
+    PR 3221 "Why": every sequence is divided into 2*cp_size chunks; PR 3235
+    reply: owner o receives chunks o and 2N-1-o.  Each document is cut into
+    2W equal chunks and the rank keeps chunk `rank` followed by chunk
+    2W-1-rank, document after document.
+    """
+    W = cp_size
+    pieces = []
+    for b in range(len(cu) - 1):
+        doc = np.arange(int(cu[b]), int(cu[b + 1]), dtype=np.int64)
+        chunks = np.split(doc, 2 * W)  # raises unless len(doc) % 2W == 0
+        pieces.append(chunks[rank])
+        pieces.append(chunks[2 * W - 1 - rank])
+    if not pieces:
+        return np.zeros(0, dtype=np.int64)
+    return np.concatenate(pieces)
+
+
+def pc_rank_rows(total_tokens, cp_size, rank):
+    """Global token index of every local row of `rank` under packed-contiguous.
+
+    PR 3221 commit messages: one contiguous chunk per CP rank, cp_size equal
+    chunks; rank r holds tokens [r*T/W, (r+1)*T/W).
+    """
+    n = total_tokens // cp_size
+    return np.arange(rank * n, (rank + 1) * n, dtype=np.int64)
+
+
+def rank_rows(cu, total_tokens, cp_size, policy, rank):
+    _require_valid(cu, total_tokens, cp_size, policy)
+    if policy == DUAL_CHUNK_SWAP:
+        return dcs_rank_rows(cu, cp_size, rank)
+    return pc_rank_rows(total_tokens, cp_size, rank)
+
+
+# --------------------------------------------------------------------------
+# Per-rank sequence metadata (PR 3221: document boundaries retained through
+# sequence metadata; packed metadata is one chunk per rank).
+# --------------------------------------------------------------------------
+def local_cu_seqlens(cu, total_tokens, cp_size, policy):
+    """Per-rank local cu_seqlens, returned as (local_cu [W][B+1], n_local [W]).
+
+    DualChunkSwap: each document contributes L_b/W tokens to every rank, so
+    every rank's local cu is cu/W and holds all B documents.
+    Packed-contiguous: rank r's slice [r*n, (r+1)*n) keeps every document
+    boundary strictly inside it, shifted by -r*n, between 0 and n; the list
+    is stored compact (n_local = its length - 1) and padded with n.
+    """
+    _require_valid(cu, total_tokens, cp_size, policy)
+    W = cp_size
+    B = len(cu) - 1
+    local = np.zeros((W, B + 1), dtype=np.int32)
+    n_local = np.zeros(W, dtype=np.int32)
+    n = total_tokens // W
+    for r in range(W):
+        if policy == DUAL_CHUNK_SWAP:
+            # Count the rows each document leaves on rank r (its two chunks).
+            acc = 0
+            local[r, 0] = 0
+            for b in range(B):
+                acc += len(dcs_rank_rows([cu[b], cu[b + 1]], W, r))
+                local[r, b + 1] = acc
+            n_local[r] = B
+        else:
+            lo, hi = r * n, (r + 1) * n
+            bounds = {0, n}
+            for v in cu:
+                v = int(v)
+                if lo < v < hi:
+                    bounds.add(v - lo)
+            ordered = sorted(bounds)
+            n_local[r] = len(ordered) - 1
+            row = ordered + [n] * (B + 1 - len(ordered))
+            local[r, :] = row
+    return local, n_local
+
+
+# --------------------------------------------------------------------------
+# Partition and inverse gather of a packed [T, H, D] tensor (bit copies).
+# --------------------------------------------------------------------------
+def partition(x, cu, cp_size, policy):
+    """parts[r][i] = x[g_r(i)]; returns an array [W, T/W, ...] of x's dtype."""
+    T = x.shape[0]
+    W = cp_size
+    parts = np.empty((W, T // W) + x.shape[1:], dtype=x.dtype)
+    for r in range(W):
+        parts[r] = x[rank_rows(cu, T, W, policy, r)]
+    return parts
+
+
+def gather(parts, cu, cp_size, policy):
+    """Inverse of partition: x[g_r(i)] = parts[r][i]."""
+    W = cp_size
+    T = parts.shape[0] * parts.shape[1]
+    x = np.empty((T,) + parts.shape[2:], dtype=parts.dtype)
+    written = np.zeros(T, dtype=bool)
+    for r in range(W):
+        rows = rank_rows(cu, T, W, policy, r)
+        assert not written[rows].any()
+        x[rows] = parts[r]
+        written[rows] = True
+    assert written.all()
+    return x
+
+
+# --------------------------------------------------------------------------
+# bf16 handling (bit patterns in uint16).
+# --------------------------------------------------------------------------
+def bf16_to_f32(u16):
+    """Exact widening: the bf16 bits are the top half of the fp32 bits."""
+    u16 = np.asarray(u16, dtype=np.uint16)
+    return (u16.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16_rne(f32):
+    """Round fp32 to bf16, nearest-even, on the bit pattern; NaN -> quiet NaN."""
+    f32 = np.ascontiguousarray(f32, dtype=np.float32)
+    u = f32.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    rounded = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint32)
+    nan = np.isnan(f32)
+    quiet = ((u >> np.uint64(16)) | np.uint64(0x0040)).astype(np.uint32)
+    return np.where(nan, quiet, rounded).astype(np.uint16)
+
+
+def _widen(a, dtype):
+    if dtype == "f32":
+        assert a.dtype == np.float32
+        return a
+    if dtype == "bf16":
+        assert a.dtype == np.uint16
+        return bf16_to_f32(a)
+    raise ValueError(dtype)
+
+
+def _narrow(acc, dtype):
+    if dtype == "f32":
+        return acc
+    if dtype == "bf16":
+        return f32_to_bf16_rne(acc)
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------
+# Owner gradient return (PR 3235 "Description" and "Sequence Diagram").
+# --------------------------------------------------------------------------
+def slot_sum(slots, in_dtype, out_dtype):
+    """Sum W slot arrays in fp32, slot 0 first, one add per further slot."""
+    acc = _widen(slots[0], in_dtype).astype(np.float32, copy=True)
+    for w in range(1, len(slots)):
+        acc = (acc + _widen(slots[w], in_dtype)).astype(np.float32)
+    return _narrow(acc, out_dtype)
+
+
+def grad_scatter(grads, cu, cp_size):
+    """Writer w puts the rows owner o owns into slot [o][w] (two-chunk layout).
+
+    grads: list over writers of global [T, ...] arrays.  Returns
+    slots[o][w] = grads[w][g_o(:)], i.e. partition(grads[w])[o].
+    """
+    W = cp_size
+    T = grads[0].shape[0]
+    slots = [[None] * W for _ in range(W)]
+    for w in range(W):
+        for o in range(W):
+            slots[o][w] = grads[w][rank_rows(cu, T, W, DUAL_CHUNK_SWAP, o)]
+    return slots
+
+
+def grad_return(grads, cu, cp_size, in_dtype, out_dtype):
+    """Scatter, then each owner sums its W writer slots in order 0..W-1.
+
+    Returns (slots, out) with out[o] = sum_w slots[o][w].
+    """
+    slots = grad_scatter(grads, cu, cp_size)
+    out = [slot_sum(slots[o], in_dtype, out_dtype) for o in range(cp_size)]
+    return slots, out
+
+
+def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype):
+    """No slots: out[o][i] = sum over w (in order) of grads[w][g_o(i)]."""
+    W = cp_size
+    T = grads[0].shape[0]
+    out = []
+    for o in range(W):
+        rows = rank_rows(cu, T, W, DUAL_CHUNK_SWAP, o)
+        acc = _widen(grads[0][rows], in_dtype).astype(np.float32, copy=True)
+        for w in range(1, W):
+            acc = (acc + _widen(grads[w][rows], in_dtype)).astype(np.float32)
+        out.append(_narrow(acc, out_dtype))
+    return out
+
+
+def epochs_after(cp_size, epoch):
+    """Epoch table after every writer has published `epoch` to every owner."""
+    return np.full((cp_size, cp_size), epoch, dtype=np.uint32)

@@ -1,0 +1,314 @@
+"""Checks that pin the CPU oracle to facts fixed outside of it.
+
+Each check takes the oracle module as its argument so the same check can be run
+against a deliberately broken copy (see test_oracle_mutations.py) to show it
+catches that mistake.  None of these checks retypes an oracle formula: they use
+hand-worked tables from the pages' rules (tests/golden), closed forms,
+brute-force characterisations and library routines.
+"""
+import json
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "cu_8_16_24.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- hand-worked tables
+def check_handworked_dcs(o):
+    g = golden()
+    cu = np.array(g["cu_seqlens"], dtype=np.int32)
+    for w_str, tab in g["dual_chunk_swap"].items():
+        if not w_str.isdigit():
+            continue
+        W = int(w_str)
+        for r in range(W):
+            rows = o.rank_rows(cu, 48, W, o.DUAL_CHUNK_SWAP, r)
+            assert rows.tolist() == tab["rows"][r], (W, r, rows.tolist())
+        local, n_local = o.local_cu_seqlens(cu, 48, W, o.DUAL_CHUNK_SWAP)
+        assert local.tolist() == tab["local_cu"], (W, local.tolist())
+        assert n_local.tolist() == tab["n_local"]
+
+
+def check_handworked_pc(o):
+    g = golden()
+    cu = np.array(g["cu_seqlens"], dtype=np.int32)
+    for w_str, tab in g["packed_contiguous"].items():
+        W = int(w_str)
+        for r in range(W):
+            rows = o.rank_rows(cu, 48, W, o.PACKED_CONTIGUOUS, r)
+            assert rows.tolist() == tab["rows"][r]
+        local, n_local = o.local_cu_seqlens(cu, 48, W, o.PACKED_CONTIGUOUS)
+        assert local.tolist() == tab["local_cu"], (W, local.tolist())
+        assert n_local.tolist() == tab["n_local"], (W, n_local.tolist())
+
+
+def check_handworked_rejections(o):
+    g = golden()
+    cu = g["cu_seqlens"]
+    for W in g["dual_chunk_swap"]["rejected_cp_sizes"]:
+        assert "doc_not_divisible" in o.cu_violations(cu, 48, W, o.DUAL_CHUNK_SWAP)
+    for W in (1, 2, 4):
+        assert o.cu_violations(cu, 48, W, o.DUAL_CHUNK_SWAP) == set()
+    assert "total_not_divisible" in o.cu_violations(cu, 48, 5, o.PACKED_CONTIGUOUS)
+    assert o.cu_violations([1, 8, 48], 48, 1, o.PACKED_CONTIGUOUS) == {"first_not_zero"}
+    assert o.cu_violations([0, 30, 24, 48], 48, 2, o.PACKED_CONTIGUOUS) == {"decreasing"}
+    assert o.cu_violations([0, 8, 24, 40], 48, 2, o.PACKED_CONTIGUOUS) == {"last_not_total"}
+
+
+def check_integer_grad_return(o):
+    """G_w[t,h,d] = (w+1)(t+1) makes every sum exact: out = (t+1) W(W+1)/2."""
+    g = golden()
+    cu = np.array(g["cu_seqlens"], dtype=np.int32)
+    T, H, D = 48, 2, 8
+    t = np.arange(T, dtype=np.float32)[:, None, None]
+    for W in (1, 2, 4):
+        grads = [np.broadcast_to((w + 1) * (t + 1), (T, H, D)).astype(np.float32) for w in range(W)]
+        for fn in ("grad_return", "grad_return_fused"):
+            res = getattr(o, fn)(grads, cu, W, "f32", "f32")
+            out = res[1] if fn == "grad_return" else res
+            for owner in range(W):
+                rows = np.array(g["dual_chunk_swap"][str(W)]["rows"][owner]) if str(W) in g["dual_chunk_swap"] \
+                    else np.arange(T)
+                want = (rows + 1) * (W * (W + 1) // 2)
+                assert out[owner].shape == (T // W, H, D)
+                assert (out[owner] == want[:, None, None].astype(np.float32)).all(), (fn, W, owner)
+        if W == 2:
+            out = o.grad_return(grads, cu, W, "f32", "f32")[1]
+            assert out[0][:5, 0, 0].tolist() == g["integer_grad_return_w2"]["owner0_first"]
+            assert out[1][:5, 0, 0].tolist() == g["integer_grad_return_w2"]["owner1_first"]
+        # the same integers are exact in bf16
+        gb = [o.f32_to_bf16_rne(x) for x in grads]
+        out_b = o.grad_return_fused(gb, cu, W, "bf16", "bf16")
+        for owner in range(W):
+            rows = o.rank_rows(cu, T, W, o.DUAL_CHUNK_SWAP, owner)
+            want = ((rows + 1) * (W * (W + 1) // 2)).astype(np.float32)
+            assert (o.bf16_to_f32(out_b[owner][:, 0, 0]) == want).all()
+
+
+# ---------------------------------------------------------------- order and seed
+def check_sum_order(o):
+    """(1e8 + 1) - 1e8 + 1 = 1 in fp32 only when slots are added 0,1,2,3 in turn."""
+    vals = [1e8, 1.0, -1e8, 1.0]
+    slots = [np.full((5,), v, dtype=np.float32) for v in vals]
+    out = o.slot_sum(slots, "f32", "f32")
+    assert (out == np.float32(1.0)).all(), out
+    # a different order (3,2,1,0) would give 1 - 1e8 + 1 + 1e8 = 0, and (0,2,1,3) gives 2
+    rev = o.slot_sum(slots[::-1], "f32", "f32")
+    assert (rev == np.float32(0.0)).all(), rev
+    # the same order through the fused path (writers hold constant rows)
+    cu = np.array([0, 8], dtype=np.int32)
+    grads = [np.full((8, 1, 1), v, dtype=np.float32) for v in vals]
+    fused = o.grad_return_fused(grads, cu, 4, "f32", "f32")
+    for owner in range(4):
+        assert (fused[owner] == np.float32(1.0)).all()
+
+
+def check_negative_zero_seed(o):
+    """All slots -0.0 must give -0.0: the accumulator starts from slot 0, not +0."""
+    for W in (1, 2, 4):
+        slots = [np.full((3,), -0.0, dtype=np.float32) for _ in range(W)]
+        out = o.slot_sum(slots, "f32", "f32")
+        assert (out.view(np.uint32) == np.uint32(0x80000000)).all(), (W, out.view(np.uint32))
+        out_b = o.slot_sum([o.f32_to_bf16_rne(s) for s in slots], "bf16", "bf16")
+        assert (out_b == np.uint16(0x8000)).all()
+
+
+# ---------------------------------------------------------------- bf16
+def check_bf16_rne_against_torch(o, exhaustive=False):
+    """fp32 -> bf16 must agree with torch's CPU cast (round-to-nearest-even)."""
+    import torch
+
+    hi = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    lows = np.array([0x0000, 0x0001, 0x3FFF, 0x7FFF, 0x8000, 0x8001, 0xBFFF, 0xC000, 0xFFFF],
+                    dtype=np.uint32)
+    rng = np.random.default_rng(1234)
+    lows = np.concatenate([lows, rng.integers(0, 1 << 16, size=7, dtype=np.uint32)])
+    chunks = [(hi[:, None] | lows[None, :]).ravel()]
+    chunks.append(rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32))
+    if exhaustive:
+        chunks = [np.arange(s, s + (1 << 26), dtype=np.uint64).astype(np.uint32)
+                  for s in range(0, 1 << 32, 1 << 26)]
+    for bits in chunks:
+        f = bits.view(np.float32)
+        ours = o.f32_to_bf16_rne(f)
+        ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        nan = np.isnan(f)
+        assert (ours[~nan] == ref[~nan]).all()
+        # NaN: quiet, sign kept
+        assert ((ours[nan] & 0x7FC0) == 0x7FC0).all()
+        assert ((ours[nan] >> 15) == (bits[nan] >> 31)).all()
+
+
+def check_bf16_widen_exact(o):
+    u = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = o.bf16_to_f32(u)
+    import torch
+
+    ref = torch.from_numpy(u.view(np.int16).copy()).view(torch.bfloat16).to(torch.float32).numpy()
+    same = (f.view(np.uint32) == ref.view(np.uint32)) | (np.isnan(f) & np.isnan(ref))
+    assert same.all()
+
+
+# ---------------------------------------------------------------- special cases
+def check_w1_identity(o, x=None):
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((30, 3, 4)).astype(np.float32)
+    for pol, cu in ((o.DUAL_CHUNK_SWAP, [0, 4, 10, 30]), (o.PACKED_CONTIGUOUS, [0, 7, 30])):
+        parts = o.partition(x, np.array(cu), 1, pol)
+        assert parts.shape == (1, 30, 3, 4)
+        assert (parts[0] == x).all()
+
+
+def check_single_document_native_layout(o):
+    """One document: rank r holds [r c, (r+1) c) then [(2W-1-r) c, (2W-r) c), c = T/2W."""
+    for W in (1, 2, 3, 4, 8):
+        T = 2 * W * 5
+        cu = np.array([0, T], dtype=np.int32)
+        c = T // (2 * W)
+        for r in range(W):
+            want = list(range(r * c, (r + 1) * c)) + list(range((2 * W - 1 - r) * c, (2 * W - r) * c))
+            assert o.rank_rows(cu, T, W, o.DUAL_CHUNK_SWAP, r).tolist() == want
+
+
+def check_pc_is_reshape(o):
+    rng = np.random.default_rng(6)
+    for W in (1, 2, 4, 8):
+        T = 8 * 9
+        x = rng.standard_normal((T, 2, 3)).astype(np.float32)
+        cu = np.array([0, 5, 5, 40, T], dtype=np.int32)
+        parts = o.partition(x, cu, W, o.PACKED_CONTIGUOUS)
+        assert (parts == x.reshape(W, T // W, 2, 3)).all()
+
+
+# ---------------------------------------------------------------- brute force
+def brute_owner_rows(cu, T, W):
+    """Owner of every token by scanning documents and chunks; rows listed in global order.
+
+    Token t in document b at offset j falls in chunk k = j // (L_b / 2W); chunk k
+    belongs to rank k if k < W, else to rank 2W-1-k.  Under the stated local order
+    (document-major, the lower chunk first, tokens ascending) a rank's local rows
+    are its tokens in ascending global order.
+    """
+    owners = []
+    for t in range(T):
+        b = 0
+        while not (cu[b] <= t < cu[b + 1]):
+            b += 1
+        L = cu[b + 1] - cu[b]
+        c = L // (2 * W)
+        k = (t - cu[b]) // c
+        owners.append(k if k < W else 2 * W - 1 - k)
+    return [[t for t in range(T) if owners[t] == r] for r in range(W)]
+
+
+def check_brute_force_grad_return(o, seed=0):
+    rng = np.random.default_rng(seed)
+    for W, lengths in ((2, [4, 0, 8, 12]), (3, [6, 12]), (4, [8, 16, 8])):
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        T = int(cu[-1])
+        H, D = 2, 3
+        grads = [(rng.standard_normal((T, H, D)) * 10.0 ** int(rng.integers(-3, 3))).astype(np.float32)
+                 for _ in range(W)]
+        owner_rows = brute_owner_rows(cu, T, W)
+        slots, out = o.grad_return(grads, cu, W, "f32", "f32")
+        fused = o.grad_return_fused(grads, cu, W, "f32", "f32")
+        for owner in range(W):
+            assert o.rank_rows(cu, T, W, o.DUAL_CHUNK_SWAP, owner).tolist() == owner_rows[owner]
+            for i, t in enumerate(owner_rows[owner]):
+                for w in range(W):
+                    assert (slots[owner][w][i] == grads[w][t]).all()
+                for h in range(H):
+                    for d in range(D):
+                        acc = np.float32(grads[0][t, h, d])
+                        for w in range(1, W):
+                            acc = np.float32(acc + np.float32(grads[w][t, h, d]))
+                        assert out[owner][i, h, d].view(np.uint32) == acc.view(np.uint32)
+                        assert fused[owner][i, h, d].view(np.uint32) == acc.view(np.uint32)
+
+
+# ---------------------------------------------------------------- invariants
+def check_invariants(o, cu, T, W, policy, x):
+    cu = np.asarray(cu, dtype=np.int32)
+    B = len(cu) - 1
+    n = T // W
+    parts = o.partition(x, cu, W, policy)
+    assert parts.shape == (W, n) + x.shape[1:]
+    back = o.gather(parts, cu, W, policy)
+    assert back.tobytes() == x.tobytes()
+    all_rows = np.concatenate([o.rank_rows(cu, T, W, policy, r) for r in range(W)])
+    assert sorted(all_rows.tolist()) == list(range(T))           # each token owned once
+    for r in range(W):
+        rows = o.rank_rows(cu, T, W, policy, r)
+        assert (parts[r] == x[rows]).all()
+        counts = np.array([((rows >= cu[b]) & (rows < cu[b + 1])).sum() for b in range(B)])
+        if policy == o.DUAL_CHUNK_SWAP:
+            assert (counts == (cu[1:] - cu[:-1]) // W).all()         # L_b / W per rank
+    per_doc = np.zeros(B, dtype=np.int64)
+    for r in range(W):
+        rows = o.rank_rows(cu, T, W, policy, r)
+        per_doc += np.array([((rows >= cu[b]) & (rows < cu[b + 1])).sum() for b in range(B)],
+                            dtype=np.int64)
+    assert (per_doc == cu[1:] - cu[:-1]).all()                       # document counts kept
+    local, n_local = o.local_cu_seqlens(cu, T, W, policy)
+    for r in range(W):
+        lc = local[r]
+        assert lc[0] == 0 and (np.diff(lc) >= 0).all() and lc[-1] == n
+        k = n_local[r]
+        assert lc[k] == n and (lc[k:] == n).all()
+        if policy == o.DUAL_CHUNK_SWAP:
+            assert (lc == cu // W).all()
+        else:
+            clipped = np.clip(cu.astype(np.int64) - r * n, 0, n)
+            compact = np.unique(np.concatenate([[0], clipped, [n]]))
+            assert lc[:k + 1].tolist() == compact.tolist()
+            # the local segments are exactly the runs of each document inside the slice
+            rows = o.rank_rows(cu, T, W, policy, r)
+            doc_of = np.searchsorted(cu, rows, side="right") - 1
+            starts = sorted({0, n} | {i for i in range(1, n) if doc_of[i] != doc_of[i - 1]})
+            assert lc[:k + 1].tolist() == starts
+    if policy == o.DUAL_CHUNK_SWAP and W > 0:
+        # causal work per rank (keys seen by each query token) is balanced
+        work = []
+        for r in range(W):
+            rows = o.rank_rows(cu, T, W, policy, r)
+            doc_of = np.searchsorted(cu, rows, side="right") - 1
+            work.append(int((rows - cu[doc_of] + 1).sum()))
+        assert len(set(work)) == 1, work
+
+
+def check_fused_equals_unfused(o, seed=3):
+    rng = np.random.default_rng(seed)
+    for W, dt in ((2, "f32"), (4, "bf16"), (8, "bf16"), (3, "f32")):
+        lengths = [2 * W * int(k) for k in rng.integers(0, 4, size=5)]
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        T = int(cu[-1])
+        g32 = [rng.standard_normal((T, 2, 4)).astype(np.float32) for _ in range(W)]
+        grads = g32 if dt == "f32" else [o.f32_to_bf16_rne(g) for g in g32]
+        for out_dt in (("f32",) if dt == "f32" else ("bf16", "f32")):
+            _, out = o.grad_return(grads, cu, W, dt, out_dt)
+            fused = o.grad_return_fused(grads, cu, W, dt, out_dt)
+            for owner in range(W):
+                assert out[owner].tobytes() == fused[owner].tobytes()
+
+
+ALL_CHECKS = [
+    check_handworked_dcs,
+    check_handworked_pc,
+    check_handworked_rejections,
+    check_integer_grad_return,
+    check_sum_order,
+    check_negative_zero_seed,
+    check_bf16_rne_against_torch,
+    check_bf16_widen_exact,
+    check_w1_identity,
+    check_single_document_native_layout,
+    check_pc_is_reshape,
+    check_brute_force_grad_return,
+    check_fused_equals_unfused,
+]

@@ -1,0 +1,224 @@
+"""Plant plausible mistakes in a private copy of the CPU oracle and check that the
+pins catch every one of them (a dropped term, a wrong index, a transposed
+operand, a reversed order, a wrong rounding)."""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+import pins
+
+ORACLE_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "oracle", "cp_oracle.py")
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("cp_oracle_mutant", ORACLE_PATH)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _dcs_swapped_chunks(o):
+    def dcs_rank_rows(cu, cp_size, rank):
+        W = cp_size
+        pieces = [np.zeros(0, dtype=np.int64)]
+        for b in range(len(cu) - 1):
+            chunks = np.split(np.arange(int(cu[b]), int(cu[b + 1])), 2 * W)
+            pieces += [chunks[2 * W - 1 - rank], chunks[rank]]
+        return np.concatenate(pieces)
+    return dcs_rank_rows
+
+
+def _dcs_wrong_mirror(o):
+    def dcs_rank_rows(cu, cp_size, rank):
+        W = cp_size
+        pieces = [np.zeros(0, dtype=np.int64)]
+        for b in range(len(cu) - 1):
+            chunks = np.split(np.arange(int(cu[b]), int(cu[b + 1])), 2 * W)
+            pieces += [chunks[rank], chunks[W + rank]]
+        return np.concatenate(pieces)
+    return dcs_rank_rows
+
+
+def _pc_keep_empty(o):
+    orig = o.local_cu_seqlens
+
+    def local_cu_seqlens(cu, total_tokens, cp_size, policy):
+        if policy != o.PACKED_CONTIGUOUS:
+            return orig(cu, total_tokens, cp_size, policy)
+        W, B = cp_size, len(cu) - 1
+        n = total_tokens // W
+        local = np.zeros((W, B + 1), dtype=np.int32)
+        n_local = np.zeros(W, dtype=np.int32)
+        for r in range(W):
+            inner = [int(v) - r * n for v in cu if r * n < int(v) < (r + 1) * n]  # duplicates kept
+            row = [0] + inner + [n]
+            n_local[r] = len(row) - 1
+            local[r] = (row + [n] * (B + 1))[:B + 1]
+        return local, n_local
+    return local_cu_seqlens
+
+
+def _pc_pad_zero(o):
+    orig = o.local_cu_seqlens
+
+    def local_cu_seqlens(cu, total_tokens, cp_size, policy):
+        local, n_local = orig(cu, total_tokens, cp_size, policy)
+        if policy == o.PACKED_CONTIGUOUS:
+            for r in range(cp_size):
+                local[r, n_local[r] + 1:] = 0
+        return local, n_local
+    return local_cu_seqlens
+
+
+def _dcs_local_cu_halved(o):
+    orig = o.local_cu_seqlens
+
+    def local_cu_seqlens(cu, total_tokens, cp_size, policy):
+        local, n_local = orig(cu, total_tokens, cp_size, policy)
+        if policy == o.DUAL_CHUNK_SWAP:
+            local = (np.asarray(cu, dtype=np.int32)[None, :] // (2 * cp_size)).repeat(cp_size, 0)
+        return local, n_local
+    return local_cu_seqlens
+
+
+def _sum_reversed(o):
+    def slot_sum(slots, in_dtype, out_dtype):
+        acc = o._widen(slots[-1], in_dtype).astype(np.float32, copy=True)
+        for w in range(len(slots) - 2, -1, -1):
+            acc = (acc + o._widen(slots[w], in_dtype)).astype(np.float32)
+        return o._narrow(acc, out_dtype)
+    return slot_sum
+
+
+def _sum_zero_seed(o):
+    def slot_sum(slots, in_dtype, out_dtype):
+        acc = np.zeros(slots[0].shape, dtype=np.float32)
+        for s in slots:
+            acc = (acc + o._widen(s, in_dtype)).astype(np.float32)
+        return o._narrow(acc, out_dtype)
+    return slot_sum
+
+
+def _sum_drops_last(o):
+    def slot_sum(slots, in_dtype, out_dtype):
+        acc = o._widen(slots[0], in_dtype).astype(np.float32, copy=True)
+        for w in range(1, len(slots) - 1):
+            acc = (acc + o._widen(slots[w], in_dtype)).astype(np.float32)
+        return o._narrow(acc, out_dtype)
+    return slot_sum
+
+
+def _bf16_truncate(o):
+    def f32_to_bf16_rne(f32):
+        return (np.ascontiguousarray(f32, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return f32_to_bf16_rne
+
+
+def _bf16_half_up(o):
+    def f32_to_bf16_rne(f32):
+        f32 = np.ascontiguousarray(f32, dtype=np.float32)
+        u = f32.view(np.uint32).astype(np.uint64)
+        r = ((u + np.uint64(0x8000)) >> np.uint64(16)).astype(np.uint32)
+        q = ((u >> np.uint64(16)) | np.uint64(0x40)).astype(np.uint32)
+        return np.where(np.isnan(f32), q, r).astype(np.uint16)
+    return f32_to_bf16_rne
+
+
+def _scatter_transposed(o):
+    def grad_scatter(grads, cu, cp_size):
+        W = cp_size
+        T = grads[0].shape[0]
+        slots = [[None] * W for _ in range(W)]
+        for w in range(W):
+            for own in range(W):
+                slots[own][w] = grads[own][o.rank_rows(cu, T, W, o.DUAL_CHUNK_SWAP, w)]
+        return slots
+    return grad_scatter
+
+
+def _fused_reversed(o):
+    def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype):
+        W = cp_size
+        T = grads[0].shape[0]
+        out = []
+        for own in range(W):
+            rows = o.rank_rows(cu, T, W, o.DUAL_CHUNK_SWAP, own)
+            acc = o._widen(grads[W - 1][rows], in_dtype).astype(np.float32, copy=True)
+            for w in range(W - 2, -1, -1):
+                acc = (acc + o._widen(grads[w][rows], in_dtype)).astype(np.float32)
+            out.append(o._narrow(acc, out_dtype))
+        return out
+    return grad_return_fused
+
+
+def _no_decreasing_check(o):
+    orig = o.cu_violations
+
+    def cu_violations(cu, total_tokens, cp_size, policy):
+        return orig(cu, total_tokens, cp_size, policy) - {"decreasing"}
+    return cu_violations
+
+
+def _pc_off_by_one(o):
+    def pc_rank_rows(total_tokens, cp_size, rank):
+        n = total_tokens // cp_size
+        return (np.arange(rank * n, (rank + 1) * n, dtype=np.int64) + 1) % max(total_tokens, 1)
+    return pc_rank_rows
+
+
+MUTATIONS = {
+    "dcs_swapped_chunks": ("dcs_rank_rows", _dcs_swapped_chunks),
+    "dcs_wrong_mirror": ("dcs_rank_rows", _dcs_wrong_mirror),
+    "pc_keep_empty_docs": ("local_cu_seqlens", _pc_keep_empty),
+    "pc_pad_with_zero": ("local_cu_seqlens", _pc_pad_zero),
+    "dcs_local_cu_halved": ("local_cu_seqlens", _dcs_local_cu_halved),
+    "sum_reversed": ("slot_sum", _sum_reversed),
+    "sum_zero_seed": ("slot_sum", _sum_zero_seed),
+    "sum_drops_last_slot": ("slot_sum", _sum_drops_last),
+    "bf16_truncate": ("f32_to_bf16_rne", _bf16_truncate),
+    "bf16_round_half_up": ("f32_to_bf16_rne", _bf16_half_up),
+    "scatter_transposed": ("grad_scatter", _scatter_transposed),
+    "fused_reversed": ("grad_return_fused", _fused_reversed),
+    "no_decreasing_check": ("cu_violations", _no_decreasing_check),
+    "pc_off_by_one": ("pc_rank_rows", _pc_off_by_one),
+}
+
+INVARIANT_CASES = [
+    (2, "dual_chunk_swap", [0, 4, 4, 16, 24]),
+    (3, "packed_contiguous", [0, 5, 5, 17, 30]),
+    (4, "packed_contiguous", [0, 3, 9, 9, 20, 24]),
+]
+
+
+def run_all_pins(o):
+    failures = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(o)
+        except (AssertionError, ValueError, IndexError) as e:  # noqa: PERF203
+            failures.append((check.__name__, repr(e)[:80]))
+    for W, pol, cu in INVARIANT_CASES:
+        cu = np.array(cu, dtype=np.int32)
+        T = int(cu[-1])
+        x = np.random.default_rng(T).standard_normal((T, 2, 2)).astype(np.float32)
+        try:
+            pins.check_invariants(o, cu, T, W, pol, x)
+        except (AssertionError, ValueError, IndexError) as e:
+            failures.append(("invariants", repr(e)[:80]))
+    return failures
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert run_all_pins(fresh_oracle()) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    o = fresh_oracle()
+    attr, make = MUTATIONS[name]
+    setattr(o, attr, make(o))
+    failures = run_all_pins(o)
+    assert failures, f"planted mistake {name} passed every pin"

@@ -1,0 +1,85 @@
+"""The CPU oracle against facts fixed outside of it (hand-worked tables, closed
+forms, brute force, torch's bf16 cast, invariants)."""
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import pins
+from oracle import cp_oracle as o
+
+
+@pytest.mark.parametrize("check", pins.ALL_CHECKS, ids=lambda c: c.__name__)
+def test_pin(check):
+    check(o)
+
+
+@st.composite
+def dcs_case(draw):
+    W = draw(st.sampled_from([1, 2, 3, 4, 8]))
+    ks = draw(st.lists(st.integers(0, 4), min_size=0, max_size=6))
+    lengths = [2 * W * k for k in ks]
+    return W, lengths
+
+
+@st.composite
+def pc_case(draw):
+    W = draw(st.sampled_from([1, 2, 3, 4, 8]))
+    lengths = draw(st.lists(st.integers(0, 23), min_size=1, max_size=8))
+    T = sum(lengths)
+    pad = (-T) % W
+    lengths[-1] += pad
+    return W, lengths
+
+
+def _x(T, seed):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((T, 2, 3)).astype(np.float32)
+
+
+@settings(max_examples=60, deadline=None, derandomize=True)
+@given(dcs_case())
+def test_invariants_dcs(case):
+    W, lengths = case
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    pins.check_invariants(o, cu, T, W, o.DUAL_CHUNK_SWAP, _x(T, T))
+
+
+@settings(max_examples=60, deadline=None, derandomize=True)
+@given(pc_case())
+def test_invariants_pc(case):
+    W, lengths = case
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    pins.check_invariants(o, cu, T, W, o.PACKED_CONTIGUOUS, _x(T, T + 1))
+
+
+@settings(max_examples=40, deadline=None, derandomize=True)
+@given(dcs_case(), st.integers(0, 2**31 - 1))
+def test_brute_force_random(case, seed):
+    W, lengths = case
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    rows = pins.brute_owner_rows(cu, T, W) if T else [[] for _ in range(W)]
+    for r in range(W):
+        assert o.rank_rows(cu, T, W, o.DUAL_CHUNK_SWAP, r).tolist() == rows[r]
+
+
+def test_empty_input():
+    cu = np.array([0], dtype=np.int32)
+    for pol in o.POLICIES:
+        x = np.zeros((0, 2, 3), dtype=np.float32)
+        parts = o.partition(x, cu, 4, pol)
+        assert parts.shape == (4, 0, 2, 3)
+        local, n_local = o.local_cu_seqlens(cu, 0, 4, pol)
+        assert local.shape == (4, 1) and (local == 0).all()
+
+
+def test_epochs_after():
+    e = o.epochs_after(4, 7)
+    assert e.shape == (4, 4) and (e == 7).all()
+
+
+@pytest.mark.slow
+def test_bf16_rne_exhaustive():
+    pins.check_bf16_rne_against_torch(o, exhaustive=True)
