@@ -1,0 +1,312 @@
+/*
+ * cpthd.h - C ABI of libcpthd, the MI355X (gfx950) library for the THD
+ * context-parallel token layout and the owner gradient return.
+ *
+ * Tensors are packed THD: all documents concatenated along tokens, shape
+ * [T, H, D], row-major, so one token ("row") is H*D elements.  Document
+ * boundaries are int32 cu_seqlens[B+1] (cu[0] = 0, cu[B] = T).  W is the CP
+ * size (number of ranks).  On one GPU the W ranks are emulated by W buffers
+ * (slots) in the same HBM.
+ *
+ * Sources (web pages, by title and section):
+ *  [PC]  "[PyTorch] Add experimental packed-contiguous THD all-gather CP"
+ *        (TransformerEngine PR 3221): sections "Conversation" (commit
+ *        messages), "Why", "Scope and constraints".
+ *  [GR]  "Add stream-ordered CP gradient return primitive"
+ *        (TransformerEngine PR 3235): sections "Description", "Changes",
+ *        "Sequence Diagram", "Validation", and the author's reply on CP size.
+ *  [LL]  "Low Latency Communication Kernels with NVSHMEM" (GPU MODE lecture
+ *        87 notes): exercise list (1 KB - 16 MB sum sweep).
+ *  [MM]  "Kernel-level compute-communication overlapping for CP linear
+ *        attention kernels via nvshmem" (cuLA issue 15): replies on buffer
+ *        ownership (buffers allocated outside the module, lifetime owned by
+ *        the caller).
+ *
+ * Conventions common to every entry point
+ *  - Every data pointer is a device pointer of the CURRENT HIP device,
+ *    allocated by the caller ([MM]; [GR] "Description": peer tensor views are
+ *    supplied by the caller).  The library allocates no device memory and
+ *    keeps no state between calls (cp_profile_* aside).
+ *  - Host pointer tables (const void* const*) are read only during the call.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronizes, except cp_meta_status and
+ *    cp_profile_read, which say so.  ([GR] "Description": stream-ordered.)
+ *  - Host-side validation runs first.  On any error nothing is launched and
+ *    the status is returned: fail-closed ([GR] reply on CP size: a
+ *    fail-closed validation boundary; [PC] "Scope and constraints": FP8 and
+ *    unvalidated combinations are rejected).
+ *  - Checks that depend on device data (the cu_seqlens values) are made on
+ *    the device by cp_build_meta, which records them in the meta header.
+ *    Every later kernel reads the header first and does nothing (writes no
+ *    output byte) when the metadata is invalid or does not match the call;
+ *    the mismatch is recorded as a sticky CP_CALL_* flag, and
+ *    cp_meta_status reports both.
+ *  - Outputs must not overlap inputs or each other (CP_ERR_ALIAS); [GR]
+ *    "Description" (self-alias assertions on the rank-self slots).
+ */
+#ifndef CPTHD_H
+#define CPTHD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t; spelled out so this header needs no HIP header. */
+typedef struct ihipStream_t* cp_stream_t;
+
+/* ------------------------------------------------------------ status codes */
+enum cp_status {
+  CP_OK = 0,
+  CP_ERR_ARG = 1,         /* bad scalar argument or NULL pointer             */
+  CP_ERR_UNSUPPORTED = 2, /* dtype / mode not supported (FP8, grad-return
+                             under packed-contiguous, ...)                   */
+  CP_ERR_SHAPE = 3,       /* sizes inconsistent (T % W under PC, buffer too
+                             small, ...)                                     */
+  CP_ERR_DEVICE = 4,      /* a pointer is not device memory of the current
+                             device                                          */
+  CP_ERR_ALIAS = 5,       /* an output overlaps an input or another output   */
+  CP_ERR_HIP = 6,         /* a HIP runtime call failed                       */
+  CP_ERR_TIMEOUT = 7,     /* device-reported: an epoch wait hit its limit    */
+  CP_ERR_META = 8         /* device-reported: invalid cu_seqlens, or a call
+                             that did not match its metadata                 */
+};
+
+/* ownership policies ([PC] "Why" and commit messages) */
+enum cp_policy {
+  CP_POLICY_DUAL_CHUNK_SWAP = 0,   /* per-document 2W chunks, rank r owns r and 2W-1-r */
+  CP_POLICY_PACKED_CONTIGUOUS = 1  /* rank r owns tokens [rT/W, (r+1)T/W)              */
+};
+
+/* element types; FP8 is recognised and rejected ([PC] "Scope and constraints") */
+enum cp_dtype {
+  CP_F32 = 0,
+  CP_BF16 = 1,
+  CP_F16 = 2,
+  CP_FP8_E4M3 = 3,
+  CP_FP8_E5M2 = 4
+};
+
+#define CP_ALL_RANKS (-1)
+#define CP_MAX_CP_SIZE 64
+
+/* ------------------------------------------------------------ metadata */
+/*
+ * Device metadata built by cp_build_meta in a caller-allocated buffer of
+ * cp_meta_bytes(B, W) bytes:
+ *   offset 0                         cp_meta_header (64 bytes)
+ *   offset 64                        int32 cu_seqlens[B+1]   (copy of the input)
+ *   offset 64 + 4(B+1)               int32 local_cu[W][B+1]  (per-rank cu_seqlens)
+ *   offset 64 + 4(B+1)(W+1)          int32 n_local[W]        (documents per rank)
+ *
+ * local_cu (the per-rank sequence metadata of [PC] "Conversation"):
+ *   dual-chunk-swap:    local_cu[r][b] = cu[b] / W for every r; n_local[r] = B.
+ *                        (A rank's rows are document-major; inside a document,
+ *                        chunk r precedes chunk 2W-1-r.)
+ *   packed-contiguous:  the ascending set {0} + {cu[b] - r*T/W : r*T/W < cu[b] <
+ *                        (r+1)*T/W} + {T/W}, i.e. the documents clipped at the
+ *                        rank's slice, without empty segments; n_local[r] = its
+ *                        length - 1; the entries after it are T/W.
+ */
+#define CP_META_MAGIC 0x48545043u /* "CPTH" */
+
+/* cp_meta_header.flags: set by cp_build_meta (device-side validation) */
+#define CP_META_FIRST_NOT_ZERO    0x0001 /* cu[0] != 0                                   */
+#define CP_META_DECREASING        0x0002 /* cu[b+1] < cu[b] for some b                   */
+#define CP_META_LAST_NOT_TOTAL    0x0004 /* cu[B] != total_tokens                        */
+#define CP_META_DOC_NOT_DIVISIBLE 0x0008 /* dual-chunk-swap: some L_b % (2W) != 0        */
+#define CP_META_BUILD_MASK        0x00FF
+/* cp_meta_header.flags: sticky errors OR-ed in by later calls' kernels */
+#define CP_CALL_BAD_MAGIC         0x0100 /* meta was never built                         */
+#define CP_CALL_TOKENS_MISMATCH   0x0200 /* total_tokens differs from the meta's          */
+#define CP_CALL_CP_SIZE_MISMATCH  0x0400 /* cp_size differs from the meta's               */
+#define CP_CALL_POLICY_MISMATCH   0x0800 /* grad return needs dual-chunk-swap metadata    */
+#define CP_CALL_USED_INVALID_META 0x1000 /* a kernel met invalid metadata and did nothing */
+
+typedef struct cp_meta_header {
+  uint32_t magic;             /* CP_META_MAGIC once built                        */
+  int32_t flags;              /* CP_META_* | CP_CALL_*                           */
+  int32_t policy;             /* enum cp_policy                                  */
+  int32_t cp_size;            /* W                                               */
+  int32_t num_docs;           /* B                                               */
+  int32_t reserved0;
+  int64_t total_tokens;       /* T                                               */
+  int64_t local_tokens;       /* T / W                                           */
+  uint64_t wait_timeout_ranks;/* bit o set: owner o's last epoch wait timed out  */
+  int32_t reserved[4];
+} cp_meta_header;
+
+/* Bytes the caller must allocate for the metadata of B documents and W ranks
+ * (a multiple of 256).  Returns 0 for B < 0 or W outside [1, CP_MAX_CP_SIZE]. */
+size_t cp_meta_bytes(int32_t num_docs, int32_t cp_size);
+
+/*
+ * cp_build_meta - validate cu_seqlens and build the per-rank metadata.
+ * Source: [PC] "Why" (dual-chunk-swap divides every sequence into 2*cp_size
+ * chunks; packed-contiguous uses the whole buffer as the sharding unit, cp_size
+ * equal chunks) and "Conversation" (document boundaries kept through sequence
+ * metadata; packed metadata is one chunk per rank); [GR] author's reply (owner
+ * o receives chunks o and 2N-1-o, sized from cp_size).
+ *
+ *   cu_seqlens    device int32[num_docs+1]
+ *   num_docs      B >= 0
+ *   total_tokens  T, 0 <= T < 2^31
+ *   cp_size       W in [1, 64]
+ *   policy        enum cp_policy
+ *   meta          device buffer of at least meta_bytes >= cp_meta_bytes(B, W)
+ * Host errors: CP_ERR_ARG (range, NULL), CP_ERR_SHAPE (packed-contiguous with
+ * T % W != 0; meta_bytes too small), CP_ERR_DEVICE, CP_ERR_ALIAS (meta overlaps
+ * cu_seqlens), CP_ERR_HIP.  Data errors (cu[0] != 0, decreasing cu, cu[B] != T,
+ * dual-chunk-swap document not divisible by 2W) are written to the header
+ * flags on the device; read them with cp_meta_status.
+ */
+int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tokens,
+                  int32_t cp_size, int32_t policy, void* meta, size_t meta_bytes,
+                  cp_stream_t stream);
+
+/*
+ * cp_meta_status - synchronize `stream`, then read the header flags.
+ * Returns CP_OK when no flag is set and no epoch wait timed out; CP_ERR_META
+ * when a CP_META_* or CP_CALL_* flag is set; CP_ERR_TIMEOUT when only
+ * wait_timeout_ranks is non-zero; CP_ERR_ARG/CP_ERR_DEVICE/CP_ERR_HIP on a bad
+ * call.  *flags_out (may be NULL) receives the flags word, *timeouts_out (may be
+ * NULL) the wait_timeout_ranks mask.
+ */
+int cp_meta_status(const void* meta, cp_stream_t stream, int32_t* flags_out,
+                   uint64_t* timeouts_out);
+
+/* ------------------------------------------------------------ token layout */
+/*
+ * cp_partition_thd - split a global THD tensor into the W per-rank layouts.
+ * Source: [PC] "Why" and commit messages (per-document dual-chunk-swap; one
+ * contiguous chunk per rank for packed-contiguous); [GR] author's reply
+ * (ownership rule).  parts[r][i] = x[g_r(i)], where g_r lists rank r's global
+ * tokens in local order (documented at the metadata above).  A bit copy.
+ *
+ *   x            device [T, H, D] of `dtype`            (input)
+ *   parts        device [W, T/W, H, D] of `dtype`       (output)
+ *   total_tokens T (must equal the meta's), heads H >= 1, head_dim D >= 1
+ *   dtype        CP_F32 / CP_BF16 / CP_F16 (FP8 -> CP_ERR_UNSUPPORTED)
+ *   meta         built by cp_build_meta (either policy)
+ * Errors: CP_ERR_ARG, CP_ERR_UNSUPPORTED, CP_ERR_DEVICE, CP_ERR_ALIAS
+ * (parts overlaps x or meta), CP_ERR_HIP; metadata mismatch is recorded in the
+ * meta flags and the kernel writes nothing.
+ */
+int cp_partition_thd(const void* x, void* parts, int64_t total_tokens, int32_t heads,
+                     int32_t head_dim, int32_t dtype, const void* meta, cp_stream_t stream);
+
+/*
+ * cp_gather_thd - inverse of cp_partition_thd: x[g_r(i)] = parts[r][i]
+ * (the key/value reorder after an all-gather, [PC] commit messages: the
+ * rank-major packed-contiguous layout needs no reorder, dual-chunk-swap does).
+ * Same arguments, roles of x and parts swapped (parts input, x output).
+ */
+int cp_gather_thd(const void* parts, void* x, int64_t total_tokens, int32_t heads,
+                  int32_t head_dim, int32_t dtype, const void* meta, cp_stream_t stream);
+
+/* ------------------------------------------------------------ gradient return */
+/*
+ * cp_grad_return - owner gradient return: scatter, epoch publish, epoch wait,
+ * fixed-order slot sum.
+ * Source: [GR] "Description" (scatter global dK/dV into owner buffers in the
+ * native two-chunk CP layout; publish writer epochs; wait for all writers;
+ * accumulate the writer slots into the owner's dK/dV; the caller supplies the
+ * peer views) and "Sequence Diagram" (slot index [owner][writer rank]; wait
+ * until every epoch slot >= epoch; accumulate slots 0..cp_size-1).
+ *
+ *   rank         CP_ALL_RANKS: emulate all W ranks in stream order on `stream`.
+ *                0..W-1: the part of rank `rank` only (scatter its own
+ *                gradient to every owner, publish its epoch to every owner,
+ *                wait for its own W epochs, sum its own slots).  The W ranks'
+ *                calls MUST be made on W different streams: on one stream the
+ *                first rank's wait precedes the other writers' scatter and
+ *                ends in CP_ERR_TIMEOUT.
+ *   cp_size      W, must equal the meta's; the meta must be dual-chunk-swap
+ *   n_tensors    number of gradient tensors per rank (2 for dK, dV), >= 1
+ *   grads        host table [n_tensors][W] of device [T, H, D] `in_dtype`:
+ *                writer w's global gradient of tensor t
+ *   slots        host table [n_tensors][W owner][W writer] of device
+ *                [T/W, H, D] `in_dtype`: the owner's receive slots
+ *   out          host table [n_tensors][W owner] of device [T/W, H, D]
+ *                `out_dtype`: overwritten with the sum (not accumulated into)
+ *   in_dtype/out_dtype  (CP_F32, CP_F32), (CP_BF16, CP_BF16), (CP_BF16, CP_F32)
+ *   epochs       device uint32 [W owner][W writer], or NULL in CP_ALL_RANKS
+ *                mode (then ordering is stream order alone).  Required when
+ *                rank >= 0.  Writers store `epoch` with release semantics;
+ *                owners wait until every entry of their row is >= epoch.
+ *   epoch        must exceed every value already in `epochs` (the caller owns
+ *                the counter; there is no hidden per-buffer epoch state).
+ *   wait_timeout_us  bound on the device-side wait (<= 0: 2 seconds).  On
+ *                timeout the owner's bit in meta wait_timeout_ranks is set and
+ *                the owner's sum writes nothing (fail-closed).
+ * Sum: out = ((s_0 + s_1) + s_2) + ... + s_{W-1} in fp32, s_w = widened slot w,
+ * accumulator seeded with s_0, then rounded once to out_dtype (bf16:
+ * round-to-nearest-even).
+ * In per-rank mode the call reads grads[t][rank], writes slots[t][o][rank] for
+ * every o, reads slots[t][rank][*] and writes out[t][rank]; only those table
+ * entries must be valid.
+ * Errors: CP_ERR_ARG, CP_ERR_UNSUPPORTED (dtype pair), CP_ERR_DEVICE,
+ * CP_ERR_ALIAS, CP_ERR_HIP; device-side mismatch or timeout as above.
+ */
+int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors,
+                   const void* const* grads, void* const* slots, void* const* out,
+                   int64_t total_tokens, int32_t heads, int32_t head_dim,
+                   int32_t in_dtype, int32_t out_dtype, const void* meta,
+                   uint32_t* epochs, uint32_t epoch, int64_t wait_timeout_us,
+                   cp_stream_t stream);
+
+/*
+ * cp_grad_return_fused - the same result as cp_grad_return with no slots:
+ * out[t][o][i] = sum over w = 0..W-1 (in that order, fp32, seeded with w = 0)
+ * of grads[t][w][g_o(i)], rounded once to out_dtype.  Bitwise identical to the
+ * unfused path.  Source: [GR] "Description" (scatter and accumulate, composed
+ * into one pass; each owner pulls its two chunks from every writer's view).
+ *
+ *   rank         CP_ALL_RANKS: every owner; 0..W-1: owner `rank` only (it reads
+ *                all W writers' views, which must be complete in stream order)
+ *   other arguments as cp_grad_return; only grads[t][*] and out[t][o] used.
+ */
+int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
+                         const void* const* grads, void* const* out, int64_t total_tokens,
+                         int32_t heads, int32_t head_dim, int32_t in_dtype,
+                         int32_t out_dtype, const void* meta, cp_stream_t stream);
+
+/*
+ * cp_slot_sum - out[k] = ((s_0[k] + s_1[k]) + ...) + s_{W-1}[k] in fp32, for
+ * flat buffers: the owner-side reduction of [GR] "Sequence Diagram" on its own,
+ * as used by the small-message sweep of [LL] exercise list (1 KB - 16 MB).
+ *   num_slots    W in [1, 64]
+ *   slots        host table [W] of device buffers of n_elems `in_dtype`
+ *   out          device buffer of n_elems `out_dtype`
+ *   dtype pairs  as cp_grad_return
+ */
+int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t n_elems,
+                int32_t in_dtype, int32_t out_dtype, cp_stream_t stream);
+
+/* ------------------------------------------------------------ utilities */
+/* Static text for a status code (never NULL). */
+const char* cp_status_string(int status);
+
+/* Library version, as 10000*major + 100*minor + patch. */
+int cp_version(void);
+
+/*
+ * Per-kernel timing with HIP events on the launch stream, for benchmarks.
+ * cp_profile_enable(1) starts recording an event pair around every kernel the
+ * library launches (capacity 4096 launches; later ones are not recorded);
+ * cp_profile_enable(0) stops.  cp_profile_read synchronizes the recorded
+ * events, and for up to `capacity` distinct kernels writes its name (NUL-
+ * terminated, at most 127 chars) into names[k*128], its launch count into
+ * counts[k] and the summed milliseconds into total_ms[k]; it returns the
+ * number of distinct kernels (or a negative cp_status) and clears the record.
+ */
+int cp_profile_enable(int enable);
+int cp_profile_read(char* names, int64_t* counts, double* total_ms, int capacity);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPTHD_H */

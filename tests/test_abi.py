@@ -1,0 +1,137 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, the binding's constants equal the header's, and the host-side
+argument checks that run before any HIP call reject bad input."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpthd.h")
+
+
+def _header():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", _header(), flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(cp_\w+)\s*\(", text, flags=re.M)))
+
+
+def header_constants():
+    text = re.sub(r"/\*.*?\*/", "", _header(), flags=re.S)
+    consts = {}
+    for name, val in re.findall(r"#define\s+(CP_\w+)\s+\(?(-?0x[0-9A-Fa-f]+|-?\d+)u?\)?", text):
+        consts[name] = int(val, 0)
+    for body in re.findall(r"enum\s+\w+\s*\{(.*?)\}", text, flags=re.S):
+        for name, val in re.findall(r"(CP_\w+)\s*=\s*(\d+)", body):
+            consts[name] = int(val)
+    return consts
+
+
+@pytest.fixture(scope="module")
+def cp():
+    from thd_token_layout_amd import cpthd
+    return cpthd
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for name in ["cp_build_meta", "cp_partition_thd", "cp_gather_thd", "cp_grad_return",
+                 "cp_grad_return_fused", "cp_slot_sum", "cp_meta_status", "cp_meta_bytes"]:
+        assert name in fns, fns
+
+
+def test_every_declared_symbol_is_exported(cp):
+    lib = ctypes.CDLL(cp.LIB_PATH)
+    missing = [f for f in declared_functions() if not hasattr(lib, f)]
+    assert not missing, missing
+    assert sorted(cp.EXPORTED) == declared_functions()
+
+
+def test_constants_match_header(cp):
+    consts = header_constants()
+    assert len(consts) > 20
+    for name, val in consts.items():
+        assert getattr(cp, name) == val, name
+
+
+def test_meta_bytes_closed_form(cp):
+    for B in (0, 1, 3, 115, 1000):
+        for W in (1, 2, 4, 8, 64):
+            raw = 64 + 4 * (B + 1) * (W + 1) + 4 * W
+            assert cp.cp_meta_bytes(B, W) == (raw + 255) // 256 * 256
+    assert cp.cp_meta_bytes(-1, 4) == 0
+    assert cp.cp_meta_bytes(3, 0) == 0
+    assert cp.cp_meta_bytes(3, 65) == 0
+
+
+def test_status_strings(cp):
+    for s in range(9):
+        assert cp.cp_status_string(s) and cp.cp_status_string(s) != "unknown status"
+    assert cp.cp_status_string(99) == "unknown status"
+    assert cp.cp_version() >= 100
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails host-side first
+
+
+def test_host_checks_before_any_hip_call(cp):
+    lib = cp.lib
+    # build_meta: W range, policy, PC divisibility, meta size, NULLs
+    assert lib.cp_build_meta(FAKE, 3, 48, 0, 0, FAKE, 4096, None) == cp.CP_ERR_ARG
+    assert lib.cp_build_meta(FAKE, 3, 48, 65, 0, FAKE, 4096, None) == cp.CP_ERR_ARG
+    assert lib.cp_build_meta(FAKE, 3, 48, 2, 7, FAKE, 4096, None) == cp.CP_ERR_ARG
+    assert lib.cp_build_meta(FAKE, 3, 50, 4, 1, FAKE, 4096, None) == cp.CP_ERR_SHAPE
+    assert lib.cp_build_meta(FAKE, 3, 48, 2, 0, FAKE, 16, None) == cp.CP_ERR_SHAPE
+    assert lib.cp_build_meta(None, 3, 48, 2, 0, FAKE, 4096, None) == cp.CP_ERR_ARG
+    assert lib.cp_build_meta(FAKE, 3, -1, 2, 0, FAKE, 4096, None) == cp.CP_ERR_ARG
+    # partition / gather: FP8 rejected, unknown dtype, NULLs, sizes
+    for fn in (lib.cp_partition_thd, lib.cp_gather_thd):
+        assert fn(FAKE, FAKE, 48, 2, 8, cp.CP_FP8_E4M3, FAKE, None) == cp.CP_ERR_UNSUPPORTED
+        assert fn(FAKE, FAKE, 48, 2, 8, cp.CP_FP8_E5M2, FAKE, None) == cp.CP_ERR_UNSUPPORTED
+        assert fn(FAKE, FAKE, 48, 2, 8, 42, FAKE, None) == cp.CP_ERR_ARG
+        assert fn(None, FAKE, 48, 2, 8, cp.CP_F32, FAKE, None) == cp.CP_ERR_ARG
+        assert fn(FAKE, FAKE, 48, 0, 8, cp.CP_F32, FAKE, None) == cp.CP_ERR_ARG
+        assert fn(FAKE, FAKE, 48, 2, 8, cp.CP_F32, None, None) == cp.CP_ERR_ARG
+    # grad return: dtype pairs, rank range, divisibility, per-rank mode needs epochs
+    tab = (ctypes.c_void_p * 64)(*([0x10000] * 64))
+    gr = lib.cp_grad_return
+    assert gr(-1, 2, 2, tab, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_BF16, FAKE, None, 0, 0, None) \
+        == cp.CP_ERR_UNSUPPORTED
+    assert gr(-1, 2, 2, tab, tab, tab, 48, 2, 8, cp.CP_FP8_E4M3, cp.CP_F32, FAKE, None, 0, 0, None) \
+        == cp.CP_ERR_UNSUPPORTED
+    assert gr(2, 2, 2, tab, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0, None) \
+        == cp.CP_ERR_ARG
+    assert gr(-1, 4, 2, tab, tab, tab, 20, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0, None) \
+        == cp.CP_ERR_SHAPE
+    assert gr(0, 2, 2, tab, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0, None) \
+        == cp.CP_ERR_ARG
+    assert gr(-1, 2, 0, tab, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0, None) \
+        == cp.CP_ERR_ARG
+    nulls = (ctypes.c_void_p * 64)()
+    assert gr(-1, 2, 2, nulls, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0, None) \
+        == cp.CP_ERR_ARG
+    fu = lib.cp_grad_return_fused
+    assert fu(-1, 2, 2, tab, tab, 48, 2, 8, cp.CP_F16, cp.CP_F16, FAKE, None) == cp.CP_ERR_UNSUPPORTED
+    assert fu(-1, 65, 2, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None) == cp.CP_ERR_ARG
+    assert fu(-1, 2, 2, nulls, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None) == cp.CP_ERR_ARG
+    ss = lib.cp_slot_sum
+    assert ss(0, tab, FAKE, 10, cp.CP_F32, cp.CP_F32, None) == cp.CP_ERR_ARG
+    assert ss(65, tab, FAKE, 10, cp.CP_F32, cp.CP_F32, None) == cp.CP_ERR_ARG
+    assert ss(2, tab, FAKE, 10, cp.CP_F32, cp.CP_BF16, None) == cp.CP_ERR_UNSUPPORTED
+    assert ss(2, nulls, FAKE, 10, cp.CP_F32, cp.CP_F32, None) == cp.CP_ERR_ARG
+
+
+def test_library_has_no_oracle_dependency():
+    """The product path must not route through the CPU oracle."""
+    pkg = os.path.join(ROOT, "thd_token_layout_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
+                assert "cp_oracle" not in text, f

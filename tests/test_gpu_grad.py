@@ -1,0 +1,330 @@
+"""GPU parity of the owner gradient return (scatter, epochs, fixed-order slot sum),
+the fused scatter+sum and the small-message slot sum against the CPU oracle:
+bit-exact at oracle-sized shapes, sampled rows plus fused == unfused at the full
+S=262144 / S=131072 shapes, order and sign pins, per-rank protocol mode on
+separate streams with a delayed writer and NaN-poisoned slots, and the
+host-forced epoch timeout."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, O, WL, bits_equal, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+TAG = {torch.float32: "f32", torch.bfloat16: "bf16"}
+
+
+@pytest.fixture(scope="module")
+def cp():
+    from thd_token_layout_amd import cpthd
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return cpthd
+
+
+def make_meta(cp, cu_np, T, W):
+    cu = torch.from_numpy(np.asarray(cu_np, dtype=np.int32)).to(DEV)
+    return cp.cp_build_meta(cu, T, W, cp.CP_POLICY_DUAL_CHUNK_SWAP, check=True)
+
+
+def alloc(grads, W, out_dtype, fill=None):
+    n_t = len(grads)
+    T, H, D = grads[0][0].shape
+    n = T // W
+    mk = (lambda dt: torch.full((n, H, D), fill, dtype=dt, device=DEV)) if fill is not None else \
+        (lambda dt: torch.empty((n, H, D), dtype=dt, device=DEV))
+    slots = [[[mk(grads[0][0].dtype) for _ in range(W)] for _ in range(W)] for _ in range(n_t)]
+    out = [[mk(out_dtype) for _ in range(W)] for _ in range(n_t)]
+    return slots, out
+
+
+def oracle_full(grads, cu, W, out_tag):
+    """Oracle results for every tensor: (slots[t][o][w], out[t][o])."""
+    res = []
+    for gt in grads:
+        gn = [to_np(g) for g in gt]
+        res.append(O.grad_return(gn, np.asarray(cu), W, TAG[gt[0].dtype], out_tag))
+    return res
+
+
+def run_and_check_full(cp, grads, cu, W, out_dtype, epochs=None, epoch=0):
+    T = grads[0][0].shape[0]
+    meta = make_meta(cp, cu, T, W)
+    slots, out = alloc(grads, W, out_dtype)
+    cp.cp_grad_return(grads, slots, out, meta, epochs=epochs, epoch=epoch)
+    fused = [[torch.empty_like(o) for o in row] for row in out]
+    cp.cp_grad_return_fused(grads, fused, meta)
+    st = cp.cp_meta_status(meta)
+    assert st[0] == cp.CP_OK, st
+    ref = oracle_full(grads, cu, W, TAG[out_dtype])
+    for t in range(len(grads)):
+        ref_slots, ref_out = ref[t]
+        for o in range(W):
+            for w in range(W):
+                assert bits_equal(to_np(slots[t][o][w]), ref_slots[o][w]), (t, o, w)
+            assert bits_equal(to_np(out[t][o]), ref_out[o]), (t, o)
+            assert bits_equal(to_np(fused[t][o]), ref_out[o]), (t, o)
+    return meta
+
+
+# ------------------------------------------------------------------ tiny case (C1)
+def test_tiny_grad_return(cp):
+    w = WL.WORKLOADS["tiny_w2"]
+    say("case tiny_w2 grad return")
+    cu = WL.cu_seqlens(w)
+    vals = WL.random_tensors(w, 4, device=DEV)  # writers 0,1 x {dK, dV}
+    grads = [[vals[0], vals[1]], [vals[2], vals[3]]]
+    epochs = torch.zeros((2, 2), dtype=torch.int32, device=DEV)
+    run_and_check_full(cp, grads, cu, 2, torch.float32, epochs=epochs, epoch=5)
+    assert (epochs.cpu().numpy().view(np.uint32) == O.epochs_after(2, 5)).all()
+    # exact-integer pin through the GPU: G_w[t] = (w+1)(t+1)
+    t = torch.arange(48, dtype=torch.float32, device=DEV)[:, None, None]
+    gi = [[((wr + 1) * (t + 1)).expand(48, 2, 8).contiguous() for wr in range(2)]]
+    meta = make_meta(cp, cu, 48, 2)
+    slots, out = alloc(gi, 2, torch.float32)
+    cp.cp_grad_return(gi, slots, out, meta)
+    g = __import__("pins").golden()["integer_grad_return_w2"]
+    assert out[0][0][:5, 0, 0].cpu().tolist() == g["owner0_first"]
+    assert out[0][1][:5, 0, 0].cpu().tolist() == g["owner1_first"]
+
+
+@pytest.mark.parametrize("W,in_dt,out_dt", [
+    (2, torch.float32, torch.float32), (3, torch.float32, torch.float32),
+    (4, torch.float32, torch.float32), (4, torch.bfloat16, torch.bfloat16),
+    (4, torch.bfloat16, torch.float32), (8, torch.bfloat16, torch.bfloat16),
+    (8, torch.float32, torch.float32), (12, torch.float32, torch.float32),
+    (16, torch.bfloat16, torch.bfloat16)])
+def test_random_documents(cp, W, in_dt, out_dt):
+    say(f"case random docs W={W} {in_dt}->{out_dt}")
+    rng = np.random.default_rng(W)
+    lengths = (rng.integers(0, 6, size=7) * 2 * W).tolist()
+    lengths[-1] += 2 * W * 4
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    gen = torch.Generator(device=DEV).manual_seed(W)
+    grads = [[(torch.randn((T, 3, 40), generator=gen, device=DEV) * 1e-3).to(in_dt) for _ in range(W)]
+             for _ in range(2)]
+    run_and_check_full(cp, grads, cu, W, out_dt)
+
+
+def test_order_and_negative_zero(cp):
+    say("case order pin")
+    cu = np.array([0, 64], dtype=np.int32)
+    vals = [1e8, 1.0, -1e8, 1.0]
+    grads = [[torch.full((64, 1, 8), v, device=DEV) for v in vals]]
+    meta = make_meta(cp, cu, 64, 4)
+    slots, out = alloc(grads, 4, torch.float32)
+    cp.cp_grad_return(grads, slots, out, meta)
+    fused = [[torch.empty_like(o) for o in out[0]]]
+    cp.cp_grad_return_fused(grads, fused, meta)
+    for o in range(4):
+        assert (out[0][o] == 1.0).all() and (fused[0][o] == 1.0).all()
+    ss = torch.empty(1000, device=DEV)
+    cp.cp_slot_sum([torch.full((1000,), v, device=DEV) for v in vals], ss)
+    assert (ss == 1.0).all()
+    # -0.0 survives: the accumulator is seeded with slot 0
+    nz = [[torch.full((64, 1, 8), -0.0, device=DEV) for _ in range(4)]]
+    cp.cp_grad_return(nz, slots, out, meta)
+    cp.cp_grad_return_fused(nz, fused, meta)
+    for o in range(4):
+        assert (out[0][o].view(torch.int32) == -2**31).all()
+        assert (fused[0][o].view(torch.int32) == -2**31).all()
+
+
+def test_bf16_rounding_specials(cp):
+    """fp32 sums that land on bf16 ties, NaN, inf, denormals: device RNE == oracle RNE."""
+    say("case bf16 specials")
+    bits = np.array([0x3F808000, 0x3F818000, 0x3F80FFFF, 0x7F7FFFFF, 0x00008000, 0x00018000,
+                     0x80008000, 0x7FC00001, 0xFFA00000, 0x7F800000, 0xFF800000, 0x00000001,
+                     0x3F7FFFFF, 0x477FE000, 0xC77FE000, 0x7F7F8000], dtype=np.uint32)
+    f = bits.view(np.float32)
+    n = 1024
+    s0 = np.resize(f, n).astype(np.float32)
+    s1 = np.zeros(n, dtype=np.float32)  # x + 0 = x except -0
+    slots = [torch.from_numpy(s0).to(DEV), torch.from_numpy(s1).to(DEV)]
+    for out_dt, tag in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+        out = torch.empty(n, dtype=out_dt, device=DEV)
+        cp.cp_slot_sum(slots, out)
+        ref = O.slot_sum([s0, s1], "f32", tag)
+        got = to_np(out)
+        if tag == "f32":
+            nan = np.isnan(ref)
+            assert bits_equal(got[~nan], ref[~nan]) and np.isnan(got[nan]).all()
+        else:
+            assert bits_equal(got, ref)
+
+
+@pytest.mark.parametrize("n,W,in_dt,out_dt,offset", [
+    (1, 8, torch.float32, torch.float32, 0), (7, 3, torch.float32, torch.float32, 0),
+    (1000003, 8, torch.float32, torch.float32, 0), (4099, 5, torch.bfloat16, torch.bfloat16, 0),
+    (4099, 5, torch.bfloat16, torch.float32, 0), (777, 4, torch.float32, torch.float32, 1),
+    (777, 4, torch.bfloat16, torch.bfloat16, 3), (65536, 64, torch.float32, torch.float32, 0)])
+def test_slot_sum_tails_and_alignment(cp, n, W, in_dt, out_dt, offset):
+    gen = torch.Generator(device=DEV).manual_seed(n + W)
+    bufs = [torch.randn(n + offset, generator=gen, device=DEV).to(in_dt) for _ in range(W)]
+    slots = [b[offset:] for b in bufs]
+    outb = torch.empty(n + offset, dtype=out_dt, device=DEV)
+    out = outb[offset:]
+    cp.cp_slot_sum(slots, out)
+    ref = O.slot_sum([to_np(s) for s in slots], TAG[in_dt], TAG[out_dt])
+    assert bits_equal(to_np(out), ref)
+
+
+def test_small_message_sweep(cp):
+    """W=8 fp32 slots of 1 KiB .. 16 MiB summed into one (every size, full compare)."""
+    w = WL.WORKLOADS["sweep_w8"]
+    for nbytes in WL.SWEEP_BYTES:
+        n = nbytes // 4
+        slots = WL.random_tensors(w, 8, shape=(n,), device=DEV, seed_offset=nbytes)
+        out = torch.empty(n, device=DEV)
+        cp.cp_slot_sum(slots, out)
+        ref = O.slot_sum([to_np(s) for s in slots], "f32", "f32")
+        assert bits_equal(to_np(out), ref), nbytes
+
+
+# ------------------------------------------------------------------ full-size shapes
+def sampled_check(cp, grads, slots, out, cu, W, out_dtype, n_samples=256, seed=0):
+    """Oracle map + oracle sum on sampled owner rows (full shapes are too big to copy whole)."""
+    T = grads[0][0].shape[0]
+    n = T // W
+    rng = np.random.default_rng(seed)
+    for t in range(len(grads)):
+        for o in range(W):
+            rows = O.rank_rows(np.asarray(cu), T, W, O.DUAL_CHUNK_SWAP, o)
+            idx = np.unique(np.concatenate([rng.integers(0, n, size=n_samples), [0, n // 2 - 1,
+                                                                                 n // 2, n - 1]]))
+            gidx = torch.from_numpy(rows[idx]).to(DEV)
+            lidx = torch.from_numpy(idx).to(DEV)
+            src = [to_np(grads[t][w].index_select(0, gidx)) for w in range(W)]
+            ref = O.slot_sum(src, TAG[grads[t][0].dtype], TAG[out_dtype])
+            assert bits_equal(to_np(out[t][o].index_select(0, lidx)), ref), (t, o)
+            if slots is not None:
+                for w in range(W):
+                    assert bits_equal(to_np(slots[t][o][w].index_select(0, lidx)), src[w]), (t, o, w)
+
+
+def test_grad_return_s256k_w4(cp):
+    w = WL.WORKLOADS["grad_s256k_w4"]
+    say("case grad_s256k_w4 (full size)")
+    cu = WL.cu_seqlens(w)
+    W = w.cp_size
+    vals = WL.random_tensors(w, 2 * W, device=DEV)
+    grads = [vals[:W], vals[W:]]  # dK, dV of writers 0..3
+    meta = make_meta(cp, cu, w.total_tokens, W)
+    slots, out = alloc(grads, W, torch.float32)
+    epochs = torch.zeros((W, W), dtype=torch.int32, device=DEV)
+    cp.cp_grad_return(grads, slots, out, meta, epochs=epochs, epoch=1)
+    assert cp.cp_meta_status(meta)[0] == cp.CP_OK
+    sampled_check(cp, grads, slots, out, cu, W, torch.float32)
+    del slots
+    torch.cuda.empty_cache()
+    fused = [[torch.empty_like(o) for o in row] for row in out]
+    cp.cp_grad_return_fused(grads, fused, meta)
+    torch.cuda.synchronize()
+    for t in range(2):
+        for o in range(W):
+            assert torch.equal(fused[t][o].view(torch.int32), out[t][o].view(torch.int32)), (t, o)
+    assert (epochs == 1).all()
+
+
+def test_fused_s128k_w8(cp):
+    w = WL.WORKLOADS["fused_s128k_w8"]
+    say("case fused_s128k_w8 (full size)")
+    cu = WL.cu_seqlens(w)
+    W = w.cp_size
+    vals = WL.random_tensors(w, 2 * W, device=DEV)
+    grads = [vals[:W], vals[W:]]
+    meta = make_meta(cp, cu, w.total_tokens, W)
+    n = w.total_tokens // W
+    fused = [[torch.empty((n, w.heads, w.head_dim), dtype=torch.bfloat16, device=DEV) for _ in range(W)]
+             for _ in range(2)]
+    cp.cp_grad_return_fused(grads, fused, meta)
+    sampled_check(cp, grads, None, fused, cu, W, torch.bfloat16)
+    slots, out = alloc(grads, W, torch.bfloat16)
+    cp.cp_grad_return(grads, slots, out, meta)
+    torch.cuda.synchronize()
+    for t in range(2):
+        for o in range(W):
+            assert torch.equal(fused[t][o].view(torch.int16), out[t][o].view(torch.int16)), (t, o)
+
+
+# ------------------------------------------------------------------ per-rank protocol mode
+@pytest.mark.parametrize("W", [2, 4])
+def test_per_rank_streams_with_delayed_writer(cp, W):
+    """Each rank on its own stream; one writer is delayed; slots start as NaN.  The
+    owners must wait for every epoch, so the result equals the oracle and holds no NaN."""
+    say(f"case per-rank W={W}")
+    rng = np.random.default_rng(40 + W)
+    lengths = (rng.integers(1, 5, size=5) * 2 * W * 16).tolist()
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    gen = torch.Generator(device=DEV).manual_seed(W)
+    grads = [[torch.randn((T, 4, 64), generator=gen, device=DEV) for _ in range(W)] for _ in range(2)]
+    meta = make_meta(cp, cu, T, W)
+    slots, out = alloc(grads, W, torch.float32, fill=float("nan"))
+    epochs = torch.zeros((W, W), dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(W)]
+    delayed = W - 1
+    for r in range(W):
+        with torch.cuda.stream(streams[r]):
+            if r == delayed:
+                torch.cuda._sleep(50_000_000)  # ~20 ms of device spinning before this writer starts
+            cp.cp_grad_return(grads, slots, out, meta, rank=r, epochs=epochs, epoch=3,
+                              wait_timeout_us=5_000_000, stream=streams[r])
+    torch.cuda.synchronize()
+    st, flags, timeouts = cp.cp_meta_status(meta)
+    assert st == cp.CP_OK and timeouts == 0, (st, hex(flags), timeouts)
+    ref = oracle_full(grads, cu, W, "f32")
+    for t in range(2):
+        for o in range(W):
+            got = to_np(out[t][o])
+            assert not np.isnan(got).any()
+            assert bits_equal(got, ref[t][1][o]), (t, o)
+    assert (epochs == 3).all()
+
+
+def test_epoch_timeout_is_reported_not_hung(cp):
+    """Per-rank calls on ONE stream: rank 0 waits for rank 1's epoch, which is queued
+    behind it.  The device wait gives up after 2 ms, rank 0's sum writes nothing and
+    the timeout is reported; rank 1 then completes normally."""
+    say("case epoch timeout")
+    W = 2
+    cu = np.array([0, 64], dtype=np.int32)
+    grads = [[torch.randn((64, 1, 8), device=DEV) for _ in range(W)]]
+    meta = make_meta(cp, cu, 64, W)
+    slots, out = alloc(grads, W, torch.float32, fill=-7.0)
+    epochs = torch.zeros((W, W), dtype=torch.int32, device=DEV)
+    for r in range(W):
+        cp.cp_grad_return(grads, slots, out, meta, rank=r, epochs=epochs, epoch=1,
+                          wait_timeout_us=2000)
+    st, flags, timeouts = cp.cp_meta_status(meta)
+    assert st == cp.CP_ERR_TIMEOUT and timeouts == 0b01, (st, hex(flags), timeouts)
+    assert (out[0][0] == -7.0).all()           # fail-closed: owner 0 wrote nothing
+    ref = O.grad_return([to_np(g) for g in grads[0]], cu, W, "f32", "f32")[1]
+    assert bits_equal(to_np(out[0][1]), ref[1])
+    # a later, correctly ordered call clears the verdict
+    cp.cp_grad_return(grads, slots, out, meta, epochs=epochs, epoch=2)
+    st, flags, timeouts = cp.cp_meta_status(meta)
+    assert st == cp.CP_OK and timeouts == 0
+    assert bits_equal(to_np(out[0][0]), ref[0])
+
+
+def test_grad_return_rejects_mismatch(cp):
+    cu = np.array([0, 64], dtype=np.int32)
+    grads = [[torch.randn((64, 1, 8), device=DEV) for _ in range(2)]]
+    pc = cp.cp_build_meta(torch.from_numpy(cu).to(DEV), 64, 2, cp.CP_POLICY_PACKED_CONTIGUOUS, check=True)
+    slots, out = alloc(grads, 2, torch.float32, fill=3.0)
+    cp.cp_grad_return(grads, slots, out, pc)
+    st, flags, _ = cp.cp_meta_status(pc)
+    assert st == cp.CP_ERR_META and flags & cp.CP_CALL_POLICY_MISMATCH
+    assert (out[0][0] == 3.0).all() and (slots[0][0][1] == 3.0).all()
+    m4 = make_meta(cp, cu, 64, 4)
+    fused = [[torch.full((32, 1, 8), 3.0, device=DEV) for _ in range(2)]]
+    cp.cp_grad_return_fused(grads, fused, m4)  # W=2 call on W=4 metadata
+    st, flags, _ = cp.cp_meta_status(m4)
+    assert st == cp.CP_ERR_META and flags & cp.CP_CALL_CP_SIZE_MISMATCH
+    assert (fused[0][0] == 3.0).all()
+    with pytest.raises(cp.CpError) as e:  # output aliasing an input
+        cp.cp_grad_return_fused(grads, [[grads[0][0][:32], grads[0][1][32:]]], make_meta(cp, cu, 64, 2))
+    assert e.value.status == cp.CP_ERR_ALIAS

@@ -1,0 +1,245 @@
+"""GPU parity of the metadata builder, THD partition and inverse gather against the
+CPU oracle: bit-exact, on the tiny hand-worked case, the packed-document
+workloads at full size, the S=262144 shapes (full compare of one tensor plus
+round trips), and edge cases (empty input and documents, W=1 and W=64, ragged
+and unaligned rows, invalid and mismatched metadata)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, O, WL, bits_equal, policy_name, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cp():
+    from thd_token_layout_amd import cpthd
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return cpthd
+
+
+def build(cp, cu_np, T, W, policy, check=True):
+    cu = torch.from_numpy(np.asarray(cu_np, dtype=np.int32)).to(DEV)
+    return cp.cp_build_meta(cu, T, W, policy, check=check)
+
+
+def check_meta_against_oracle(cp, meta, cu_np, T, W, pol):
+    local, n_local = cp.read_local_cu(meta)
+    ref_local, ref_n = O.local_cu_seqlens(np.asarray(cu_np), T, W, pol)
+    assert bits_equal(local.numpy(), ref_local), (local, ref_local)
+    assert bits_equal(n_local.numpy(), ref_n), (n_local, ref_n)
+
+
+def check_layout(cp, x, cu_np, W, pol_code, full=True, sample_rows=4096, seed=0):
+    """partition vs oracle, gather vs oracle, round trip; returns parts."""
+    T = x.shape[0]
+    pol = policy_name(pol_code)
+    meta = build(cp, cu_np, T, W, pol_code)
+    check_meta_against_oracle(cp, meta, cu_np, T, W, pol)
+    parts = cp.cp_partition_thd(x, meta)
+    back = cp.cp_gather_thd(parts, meta)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16) if x.dtype != torch.float32 else back.view(torch.int32),
+                       x.view(torch.int16) if x.dtype != torch.float32 else x.view(torch.int32))
+    xn = to_np(x)
+    if full:
+        ref = O.partition(xn, np.asarray(cu_np), W, pol)
+        assert bits_equal(to_np(parts), ref)
+        ref_back = O.gather(ref, np.asarray(cu_np), W, pol)
+        assert bits_equal(to_np(back), ref_back)
+    else:
+        rng = np.random.default_rng(seed)
+        n = T // W
+        for r in range(W):
+            rows = O.rank_rows(np.asarray(cu_np), T, W, pol, r)
+            idx = np.unique(np.concatenate([rng.integers(0, n, size=sample_rows), [0, n - 1]]))
+            got = to_np(parts[r][torch.from_numpy(idx).to(DEV)])
+            assert bits_equal(got, xn[rows[idx]]), (r,)
+    meta_status = cp.cp_meta_status(meta)
+    assert meta_status[0] == cp.CP_OK, meta_status
+    return parts
+
+
+# ------------------------------------------------------------------ tiny hand-worked case
+def test_tiny_dcs_and_pc(cp):
+    w = WL.WORKLOADS["tiny_w2"]
+    say("case tiny_w2")
+    cu = WL.cu_seqlens(w)
+    (x,) = WL.random_tensors(w, 1)
+    x = x.to(DEV)
+    for W in (1, 2, 4):
+        check_layout(cp, x, cu, W, cp.CP_POLICY_DUAL_CHUNK_SWAP)
+        check_layout(cp, x, cu, W, cp.CP_POLICY_PACKED_CONTIGUOUS)
+    check_layout(cp, x, cu, 3, cp.CP_POLICY_PACKED_CONTIGUOUS)
+    # the hand-worked ownership table, through the GPU: x[t] = t
+    xi = torch.arange(48, dtype=torch.float32, device=DEV)[:, None, None].expand(48, 2, 8).contiguous()
+    g = __import__("pins").golden()
+    for W in (2, 4):
+        parts = cp.cp_partition_thd(xi, build(cp, cu, 48, W, cp.CP_POLICY_DUAL_CHUNK_SWAP))
+        got = parts[:, :, 0, 0].cpu().numpy().astype(int).tolist()
+        assert got == g["dual_chunk_swap"][str(W)]["rows"]
+
+
+@pytest.mark.parametrize("name", ["dcs_t32k_w4", "pc_t64k_w4"])
+def test_packed_documents_full_size(cp, name):
+    w = WL.WORKLOADS[name]
+    say(f"case {name}")
+    cu = WL.cu_seqlens(w)
+    pol = cp.POLICY[w.policy]
+    for x in WL.random_tensors(w, w.n_tensors, device=DEV):  # Q, K, V
+        check_layout(cp, x, cu, w.cp_size, pol)
+
+
+@pytest.mark.parametrize("name", ["dcs_s256k_w4", "pc_s256k_w4", "dcs1_s256k_w4"])
+def test_s256k_shapes(cp, name):
+    w = WL.WORKLOADS[name]
+    say(f"case {name}")
+    cu = WL.cu_seqlens(w)
+    pol = cp.POLICY[w.policy]
+    xs = WL.random_tensors(w, w.n_tensors, device=DEV)
+    for k, x in enumerate(xs):
+        check_layout(cp, x, cu, w.cp_size, pol, full=(k == 0), seed=k)
+        torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ edge cases
+def test_empty_input(cp):
+    say("case empty")
+    for pol in (0, 1):
+        cu = torch.zeros(1, dtype=torch.int32, device=DEV)
+        meta = cp.cp_build_meta(cu, 0, 4, pol, check=True)
+        x = torch.empty((0, 2, 8), dtype=torch.bfloat16, device=DEV)
+        parts = cp.cp_partition_thd(x, meta)
+        assert parts.shape == (4, 0, 2, 8)
+        back = cp.cp_gather_thd(parts, meta)
+        assert back.shape == (0, 2, 8)
+        local, n_local = cp.read_local_cu(meta)
+        assert (local == 0).all() and (n_local == 0).all()
+
+
+@pytest.mark.parametrize("W,lengths", [(2, [0, 4, 0, 8, 0]), (4, [8, 0, 0, 16, 8]),
+                                       (3, [0, 6, 12, 0])])
+def test_empty_documents_dcs(cp, W, lengths):
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    x = torch.randn((T, 3, 16), device=DEV)
+    check_layout(cp, x, cu, W, cp.CP_POLICY_DUAL_CHUNK_SWAP)
+
+
+@pytest.mark.parametrize("W,lengths", [(2, [0, 5, 0, 7, 0]), (4, [3, 0, 0, 13, 0]),
+                                       (8, [1, 2, 3, 4, 5, 6, 7, 4]), (5, [25])])
+def test_empty_and_odd_documents_pc(cp, W, lengths):
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    x = torch.randn((T, 2, 8), device=DEV)
+    check_layout(cp, x, cu, W, cp.CP_POLICY_PACKED_CONTIGUOUS)
+
+
+def test_w64_and_many_documents(cp):
+    say("case W=64")
+    rng = np.random.default_rng(11)
+    W = 64
+    lengths = (rng.integers(0, 4, size=40) * 2 * W).tolist()
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    x = torch.randn((T, 1, 64), device=DEV).to(torch.bfloat16)
+    check_layout(cp, x, cu, W, cp.CP_POLICY_DUAL_CHUNK_SWAP)
+    check_layout(cp, x, cu, W, cp.CP_POLICY_PACKED_CONTIGUOUS)
+    # many documents: B large relative to the block size of the metadata builder
+    lengths = (rng.integers(1, 3, size=3000) * 8).tolist()
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    x = torch.randn((T, 2, 8), device=DEV)
+    check_layout(cp, x, cu, 4, cp.CP_POLICY_DUAL_CHUNK_SWAP)
+    check_layout(cp, x, cu, 4, cp.CP_POLICY_PACKED_CONTIGUOUS)
+
+
+@pytest.mark.parametrize("H,D,dtype", [(3, 5, torch.bfloat16),     # 30 B rows: 2-byte units
+                                       (1, 6, torch.float32),      # 24 B rows: 8-byte units
+                                       (3, 3, torch.float32),      # 36 B rows: 4-byte units
+                                       (8, 136, torch.bfloat16),   # 2176 B: ragged lane tail
+                                       (40, 128, torch.float32),   # 20 KiB rows: several passes
+                                       (1, 8, torch.float16)])
+def test_ragged_rows(cp, H, D, dtype):
+    cu = np.array([0, 16, 24, 64, 64, 128], dtype=np.int32)
+    x = torch.randn((128, H, D), device=DEV).to(dtype)
+    check_layout(cp, x, cu, 4, cp.CP_POLICY_DUAL_CHUNK_SWAP)
+    check_layout(cp, x, cu, 4, cp.CP_POLICY_PACKED_CONTIGUOUS)
+
+
+def test_unaligned_base_pointers(cp):
+    cu = np.array([0, 32, 64], dtype=np.int32)
+    flat = torch.randn(64 * 2 * 8 + 1, device=DEV).to(torch.bfloat16)
+    x = flat[1:].view(64, 2, 8)  # data_ptr is 2 bytes past a 256-byte boundary
+    assert x.data_ptr() % 16 == 2
+    out_flat = torch.zeros(64 * 2 * 8 + 3, device=DEV, dtype=torch.bfloat16)
+    parts = out_flat[3:].view(4, 16, 2, 8)
+    meta = build(cp, cu, 64, 4, cp.CP_POLICY_DUAL_CHUNK_SWAP)
+    cp.cp_partition_thd(x, meta, parts=parts)
+    ref = O.partition(to_np(x), cu, 4, O.DUAL_CHUNK_SWAP)
+    assert bits_equal(to_np(parts), ref)
+    back_flat = torch.zeros(64 * 2 * 8 + 5, device=DEV, dtype=torch.bfloat16)
+    back = back_flat[5:].view(64, 2, 8)
+    cp.cp_gather_thd(parts, meta, x=back)
+    assert bits_equal(to_np(back), to_np(x))
+
+
+# ------------------------------------------------------------------ invalid / mismatched metadata
+FLAG_NAMES = {"first_not_zero": 0x1, "decreasing": 0x2, "last_not_total": 0x4,
+              "doc_not_divisible": 0x8}
+
+
+@pytest.mark.parametrize("cu,T,W,pol", [
+    ([0, 8, 24, 48], 48, 8, 0),           # 8 % 16 != 0 (hand-worked rejection)
+    ([1, 8, 48], 48, 1, 1),
+    ([0, 30, 24, 48], 48, 2, 1),
+    ([0, 8, 24, 40], 48, 2, 0),
+    ([2, 30, 20, 40], 48, 2, 0),
+])
+def test_invalid_cu_is_flagged_and_nothing_written(cp, cu, T, W, pol):
+    meta = build(cp, cu, T, W, pol, check=False)
+    st, flags, _ = cp.cp_meta_status(meta)
+    want = 0
+    for name in O.cu_violations(cu, T, W, policy_name(pol)):
+        want |= FLAG_NAMES[name]
+    assert st == cp.CP_ERR_META and (flags & cp.CP_META_BUILD_MASK) == want, (hex(flags), want)
+    x = torch.randn((T, 2, 8), device=DEV)
+    parts = torch.full((T,), 7.0, device=DEV).view(W, T // W, 1, 1).expand(W, T // W, 2, 8).contiguous() \
+        if T % W == 0 else None
+    if parts is not None:
+        before = parts.clone()
+        cp.cp_partition_thd(x, meta, parts=parts)
+        torch.cuda.synchronize()
+        assert torch.equal(parts, before)
+        st, flags, _ = cp.cp_meta_status(meta)
+        assert flags & cp.CP_CALL_USED_INVALID_META
+
+
+def test_meta_mismatch_and_host_errors(cp):
+    cu = np.array([0, 16, 32], dtype=np.int32)
+    meta = build(cp, cu, 32, 2, cp.CP_POLICY_DUAL_CHUNK_SWAP)
+    x = torch.randn((48, 2, 8), device=DEV)  # 48 tokens, meta says 32
+    parts = torch.zeros((2, 24, 2, 8), device=DEV)
+    cp.cp_partition_thd(x, meta, parts=parts)
+    st, flags, _ = cp.cp_meta_status(meta)
+    assert st == cp.CP_ERR_META and flags & cp.CP_CALL_TOKENS_MISMATCH
+    assert torch.count_nonzero(parts) == 0
+    # host pointer -> CP_ERR_DEVICE; overlapping output -> CP_ERR_ALIAS; FP8 -> unsupported
+    meta = build(cp, cu, 32, 2, cp.CP_POLICY_DUAL_CHUNK_SWAP)
+    xh = torch.randn((32, 2, 8))
+    with pytest.raises(cp.CpError) as e:
+        cp.cp_partition_thd(xh, meta, parts=torch.zeros((2, 16, 2, 8), device=DEV))
+    assert e.value.status == cp.CP_ERR_DEVICE
+    buf = torch.randn((64, 2, 8), device=DEV)
+    with pytest.raises(cp.CpError) as e:
+        cp.cp_partition_thd(buf[:32], meta, parts=buf[16:48].view(2, 16, 2, 8))
+    assert e.value.status == cp.CP_ERR_ALIAS
+    if hasattr(torch, "float8_e4m3fn"):
+        x8 = torch.zeros((32, 2, 8), device=DEV).to(torch.float8_e4m3fn)
+        with pytest.raises(cp.CpError) as e:
+            cp.cp_partition_thd(x8, meta, parts=torch.zeros((2, 16, 2, 8), device=DEV).to(torch.float8_e4m3fn))
+        assert e.value.status == cp.CP_ERR_UNSUPPORTED
+    with pytest.raises(cp.CpError) as e:
+        cp.cp_build_meta(torch.tensor([0, 5, 10], dtype=torch.int32, device=DEV), 10, 4, 1)
+    assert e.value.status == cp.CP_ERR_SHAPE

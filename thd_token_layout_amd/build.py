@@ -1,0 +1,82 @@
+"""Build libcpthd.so (HIP kernels for gfx950 + the C-ABI layer) in-tree.
+
+    python -m thd_token_layout_amd.build          # or: python thd_token_layout_amd/build.py
+
+Compiles every time it is called.  Output: thd_token_layout_amd/libcpthd.so.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libcpthd.so")
+
+ARCH = "gfx950"
+HIP_SOURCES = ["meta.hip", "permute.hip", "reduce.hip"]
+HOST_SOURCES = ["abi.cpp"]
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+# Device code: gfx950 only; packed-fp32 instructions disabled; no fast-math,
+# denormals kept (the fixed-order fp32 sums must match IEEE single precision).
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero", "-ffp-contract=off"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    jobs = []
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        cmd = [cc, *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        jobs.append((src, cmd))
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        cmd = [cc, *COMMON, "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, src), "-o", obj]
+        jobs.append((src, cmd))
+        objs.append(obj)
+    procs = []
+    for src, cmd in jobs:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+    failed = []
+    for src, cmd, p in procs:
+        out, _ = p.communicate()
+        text = out.decode(errors="replace")
+        if p.returncode != 0:
+            failed.append(src)
+            sys.stderr.write(f"--- {src} failed:\n{' '.join(cmd)}\n{text}\n")
+        elif verbose and text.strip():
+            sys.stderr.write(text)
+    if failed:
+        raise RuntimeError(f"compilation failed: {failed}")
+    tmp = LIB + ".tmp"
+    link = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,285 @@
+"""Python binding of libcpthd (C ABI in include/cpthd.h).
+
+Argument marshalling only: torch tensors are turned into device pointers and
+the current HIP stream, the C entry point of the same name is called (ctypes
+releases the GIL during the call), and a non-zero status raises CpError.  Every
+step of the computation runs in the HIP kernels of libcpthd.so; importing this
+module raises ImportError when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcpthd.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"libcpthd.so not found at {_LIB_PATH}: build it with "
+        "`python -m thd_token_layout_amd.build` (hipcc, gfx950)")
+lib = ctypes.CDLL(_LIB_PATH)
+LIB_PATH = _LIB_PATH
+
+# ---------------------------------------------------------------- constants (cpthd.h)
+CP_OK, CP_ERR_ARG, CP_ERR_UNSUPPORTED, CP_ERR_SHAPE, CP_ERR_DEVICE = 0, 1, 2, 3, 4
+CP_ERR_ALIAS, CP_ERR_HIP, CP_ERR_TIMEOUT, CP_ERR_META = 5, 6, 7, 8
+CP_POLICY_DUAL_CHUNK_SWAP, CP_POLICY_PACKED_CONTIGUOUS = 0, 1
+CP_F32, CP_BF16, CP_F16, CP_FP8_E4M3, CP_FP8_E5M2 = 0, 1, 2, 3, 4
+CP_ALL_RANKS = -1
+CP_MAX_CP_SIZE = 64
+CP_META_MAGIC = 0x48545043
+CP_META_FIRST_NOT_ZERO = 0x0001
+CP_META_DECREASING = 0x0002
+CP_META_LAST_NOT_TOTAL = 0x0004
+CP_META_DOC_NOT_DIVISIBLE = 0x0008
+CP_META_BUILD_MASK = 0x00FF
+CP_CALL_BAD_MAGIC = 0x0100
+CP_CALL_TOKENS_MISMATCH = 0x0200
+CP_CALL_CP_SIZE_MISMATCH = 0x0400
+CP_CALL_POLICY_MISMATCH = 0x0800
+CP_CALL_USED_INVALID_META = 0x1000
+
+POLICY = {"dual_chunk_swap": CP_POLICY_DUAL_CHUNK_SWAP,
+          "packed_contiguous": CP_POLICY_PACKED_CONTIGUOUS}
+
+_c = ctypes
+_vp = _c.c_void_p
+_i32, _i64, _u32, _u64, _sz = _c.c_int32, _c.c_int64, _c.c_uint32, _c.c_uint64, _c.c_size_t
+
+lib.cp_meta_bytes.restype = _sz
+lib.cp_meta_bytes.argtypes = [_i32, _i32]
+lib.cp_build_meta.restype = _c.c_int
+lib.cp_build_meta.argtypes = [_vp, _i32, _i64, _i32, _i32, _vp, _sz, _vp]
+lib.cp_meta_status.restype = _c.c_int
+lib.cp_meta_status.argtypes = [_vp, _vp, _c.POINTER(_i32), _c.POINTER(_u64)]
+lib.cp_partition_thd.restype = _c.c_int
+lib.cp_partition_thd.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]
+lib.cp_gather_thd.restype = _c.c_int
+lib.cp_gather_thd.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]
+lib.cp_grad_return.restype = _c.c_int
+lib.cp_grad_return.argtypes = [_i32, _i32, _i32, _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_vp),
+                               _i64, _i32, _i32, _i32, _i32, _vp, _vp, _u32, _i64, _vp]
+lib.cp_grad_return_fused.restype = _c.c_int
+lib.cp_grad_return_fused.argtypes = [_i32, _i32, _i32, _c.POINTER(_vp), _c.POINTER(_vp), _i64, _i32,
+                                     _i32, _i32, _i32, _vp, _vp]
+lib.cp_slot_sum.restype = _c.c_int
+lib.cp_slot_sum.argtypes = [_i32, _c.POINTER(_vp), _vp, _i64, _i32, _i32, _vp]
+lib.cp_status_string.restype = _c.c_char_p
+lib.cp_status_string.argtypes = [_c.c_int]
+lib.cp_version.restype = _c.c_int
+lib.cp_version.argtypes = []
+lib.cp_profile_enable.restype = _c.c_int
+lib.cp_profile_enable.argtypes = [_c.c_int]
+lib.cp_profile_read.restype = _c.c_int
+lib.cp_profile_read.argtypes = [_c.c_char_p, _c.POINTER(_i64), _c.POINTER(_c.c_double), _c.c_int]
+
+
+class CpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {cp_status_string(status)} (status {status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != CP_OK:
+        raise CpError(status, where)
+
+
+def cp_status_string(status: int) -> str:
+    return lib.cp_status_string(int(status)).decode()
+
+
+def cp_version() -> int:
+    return lib.cp_version()
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    table = {torch.float32: CP_F32, torch.bfloat16: CP_BF16, torch.float16: CP_F16}
+    fp8 = {getattr(torch, "float8_e4m3fn", None): CP_FP8_E4M3,
+           getattr(torch, "float8_e5m2", None): CP_FP8_E5M2}
+    if dt in table:
+        return table[dt]
+    if dt in fp8:
+        return fp8[dt]
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libcpthd must be contiguous")
+    return t.data_ptr()
+
+
+def _table(rows) -> "ctypes.Array":
+    flat = [_ptr(t) for t in rows]
+    return (_vp * len(flat))(*flat)
+
+
+@dataclass
+class Meta:
+    """Device metadata buffer plus the host-side parameters it was built from."""
+    buf: torch.Tensor        # uint8 device tensor of cp_meta_bytes(B, W) bytes
+    cp_size: int
+    policy: int
+    num_docs: int
+    total_tokens: int
+
+    @property
+    def local_tokens(self) -> int:
+        return self.total_tokens // self.cp_size
+
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+
+def cp_meta_bytes(num_docs: int, cp_size: int) -> int:
+    return lib.cp_meta_bytes(num_docs, cp_size)
+
+
+def cp_build_meta(cu_seqlens: torch.Tensor, total_tokens: int, cp_size: int, policy,
+                  meta: Optional[torch.Tensor] = None, stream=None, check: bool = False) -> Meta:
+    """Validate cu_seqlens on the device and build per-rank metadata.
+
+    With check=True the stream is synchronized and a data error raises CpError.
+    """
+    if isinstance(policy, str):
+        policy = POLICY[policy]
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    B = cu_seqlens.numel() - 1
+    nbytes = cp_meta_bytes(B, cp_size)
+    if meta is None:
+        meta = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=cu_seqlens.device)
+    st = lib.cp_build_meta(_ptr(cu_seqlens), B, int(total_tokens), int(cp_size), int(policy),
+                           _ptr(meta), meta.numel(), _stream(stream))
+    _check(st, "cp_build_meta")
+    m = Meta(meta, int(cp_size), int(policy), B, int(total_tokens))
+    if check:
+        status, flags, _ = cp_meta_status(m, stream)
+        if status != CP_OK:
+            raise CpError(status, f"cp_build_meta: invalid cu_seqlens (flags 0x{flags:x})")
+    return m
+
+
+def cp_meta_status(meta, stream=None):
+    """Synchronize and return (status, flags, wait_timeout_ranks)."""
+    buf = meta.buf if isinstance(meta, Meta) else meta
+    flags = _i32(0)
+    timeouts = _u64(0)
+    st = lib.cp_meta_status(_ptr(buf), _stream(stream), ctypes.byref(flags), ctypes.byref(timeouts))
+    if st not in (CP_OK, CP_ERR_META, CP_ERR_TIMEOUT):
+        raise CpError(st, "cp_meta_status")
+    return st, flags.value, timeouts.value
+
+
+def read_local_cu(meta: Meta):
+    """(local_cu [W, B+1], n_local [W]) copied from the device metadata (synchronizes)."""
+    B, W = meta.num_docs, meta.cp_size
+    words = meta.buf[: 64 + 4 * (B + 1) * (W + 1) + 4 * W].cpu().view(torch.int32)
+    base = 16 + (B + 1)
+    local = words[base: base + W * (B + 1)].reshape(W, B + 1).clone()
+    n_local = words[base + W * (B + 1): base + W * (B + 1) + W].clone()
+    return local, n_local
+
+
+def cp_partition_thd(x: torch.Tensor, meta: Meta, parts: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    T, H, D = x.shape
+    if parts is None:
+        parts = torch.empty((meta.cp_size, T // meta.cp_size, H, D), dtype=x.dtype, device=x.device)
+    st = lib.cp_partition_thd(_ptr(x), _ptr(parts), T, H, D, dtype_code(x.dtype), meta.ptr(),
+                              _stream(stream))
+    _check(st, "cp_partition_thd")
+    return parts
+
+
+def cp_gather_thd(parts: torch.Tensor, meta: Meta, x: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    W, n, H, D = parts.shape
+    T = W * n
+    if x is None:
+        x = torch.empty((T, H, D), dtype=parts.dtype, device=parts.device)
+    st = lib.cp_gather_thd(_ptr(parts), _ptr(x), T, H, D, dtype_code(parts.dtype), meta.ptr(),
+                           _stream(stream))
+    _check(st, "cp_gather_thd")
+    return x
+
+
+def _flat2(tab: Sequence[Sequence[Optional[torch.Tensor]]]):
+    return [t for row in tab for t in row]
+
+
+def _flat3(tab):
+    return [t for a in tab for b in a for t in b]
+
+
+def cp_grad_return(grads: Sequence[Sequence[torch.Tensor]], slots, out, meta: Meta,
+                   rank: int = CP_ALL_RANKS, epochs: Optional[torch.Tensor] = None,
+                   epoch: int = 0, wait_timeout_us: int = 0, stream=None) -> None:
+    """grads[t][w] [T,H,D]; slots[t][o][w] [T/W,H,D]; out[t][o] [T/W,H,D] (overwritten)."""
+    n_tensors = len(grads)
+    W = meta.cp_size
+    ref = next(g for g in _flat2(grads) if g is not None)
+    T, H, D = ref.shape
+    out_ref = next(o for o in _flat2(out) if o is not None)
+    st = lib.cp_grad_return(int(rank), W, n_tensors, _table(_flat2(grads)), _table(_flat3(slots)),
+                            _table(_flat2(out)), T, H, D, dtype_code(ref.dtype),
+                            dtype_code(out_ref.dtype), meta.ptr(), _ptr(epochs), int(epoch),
+                            int(wait_timeout_us), _stream(stream))
+    _check(st, "cp_grad_return")
+
+
+def cp_grad_return_fused(grads, out, meta: Meta, rank: int = CP_ALL_RANKS, stream=None) -> None:
+    n_tensors = len(grads)
+    W = meta.cp_size
+    ref = next(g for g in _flat2(grads) if g is not None)
+    T, H, D = ref.shape
+    out_ref = next(o for o in _flat2(out) if o is not None)
+    st = lib.cp_grad_return_fused(int(rank), W, n_tensors, _table(_flat2(grads)), _table(_flat2(out)),
+                                  T, H, D, dtype_code(ref.dtype), dtype_code(out_ref.dtype),
+                                  meta.ptr(), _stream(stream))
+    _check(st, "cp_grad_return_fused")
+
+
+def cp_slot_sum(slots: Sequence[torch.Tensor], out: torch.Tensor, stream=None) -> torch.Tensor:
+    st = lib.cp_slot_sum(len(slots), _table(slots), _ptr(out), out.numel(),
+                         dtype_code(slots[0].dtype), dtype_code(out.dtype), _stream(stream))
+    _check(st, "cp_slot_sum")
+    return out
+
+
+def cp_profile_enable(enable: bool = True) -> None:
+    _check(lib.cp_profile_enable(1 if enable else 0), "cp_profile_enable")
+
+
+def cp_profile_read(capacity: int = 64):
+    """{kernel name: (launches, total ms)} recorded since the last read (synchronizes)."""
+    names = ctypes.create_string_buffer(128 * capacity)
+    counts = (_i64 * capacity)()
+    ms = (ctypes.c_double * capacity)()
+    k = lib.cp_profile_read(names, counts, ms, capacity)
+    if k < 0:
+        raise CpError(-k, "cp_profile_read")
+    res = {}
+    for i in range(min(k, capacity)):
+        nm = names.raw[128 * i: 128 * (i + 1)].split(b"\0", 1)[0].decode()
+        res[nm] = (int(counts[i]), float(ms[i]))
+    return res
+
+
+EXPORTED = ["cp_meta_bytes", "cp_build_meta", "cp_meta_status", "cp_partition_thd", "cp_gather_thd",
+            "cp_grad_return", "cp_grad_return_fused", "cp_slot_sum", "cp_status_string", "cp_version",
+            "cp_profile_enable", "cp_profile_read"]

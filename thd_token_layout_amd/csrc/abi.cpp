@@ -1,0 +1,553 @@
+// C-ABI entry points of libcpthd: host-side validation, then stream-ordered
+// launches.  Validation order: scalar arguments and NULL checks first (no HIP
+// call), then device membership of every pointer, then byte-range overlap of
+// outputs against inputs and each other, then the launches.  Nothing is
+// launched when any check fails ("Add stream-ordered CP gradient return
+// primitive", author's reply: a fail-closed validation boundary; section
+// "Description": device guards on every tensor and self-alias assertions).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "cpthd.h"
+#include "cpthd_internal.h"
+
+namespace cpthd {
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Every output against every input and every other output.
+int check_alias(const std::vector<Range>& outs, const std::vector<Range>& ins) {
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return CP_ERR_ALIAS;
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlap(outs[i], outs[j])) return CP_ERR_ALIAS;
+  }
+  return CP_OK;
+}
+
+int current_device(int* dev) {
+  if (hipGetDevice(dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return CP_ERR_HIP;
+  }
+  return CP_OK;
+}
+
+// The pointer must be device memory owned by device `dev`.
+int check_device_ptr(const void* p, int dev) {
+  if (p == nullptr) return CP_ERR_ARG;
+  hipPointerAttribute_t attr;
+  memset(&attr, 0, sizeof(attr));
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return CP_ERR_DEVICE;
+  }
+  if (attr.type != hipMemoryTypeDevice || attr.device != dev) return CP_ERR_DEVICE;
+  return CP_OK;
+}
+
+bool valid_layout_dtype(int32_t dt) { return dt == CP_F32 || dt == CP_BF16 || dt == CP_F16; }
+bool is_fp8(int32_t dt) { return dt == CP_FP8_E4M3 || dt == CP_FP8_E5M2; }
+
+// (in, out) pairs of the gradient return and the slot sum.
+int check_sum_dtypes(int32_t in, int32_t out) {
+  if (is_fp8(in) || is_fp8(out)) return CP_ERR_UNSUPPORTED;
+  if (in == CP_F32 && out == CP_F32) return CP_OK;
+  if (in == CP_BF16 && out == CP_BF16) return CP_OK;
+  if (in == CP_BF16 && out == CP_F32) return CP_OK;
+  if (valid_layout_dtype(in) && valid_layout_dtype(out)) return CP_ERR_UNSUPPORTED;
+  return CP_ERR_ARG;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? CP_OK : CP_ERR_HIP; }
+
+// ---------------------------------------------------------------- timing hooks
+struct ProfileRecord {
+  std::string name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mutex;
+bool g_prof_enabled = false;
+std::vector<ProfileRecord> g_prof_records;
+std::vector<hipEvent_t> g_prof_free;
+std::string g_prof_pending_name;
+hipEvent_t g_prof_pending_start = nullptr;
+constexpr size_t kProfCapacity = 4096;
+
+hipEvent_t take_event() {
+  if (!g_prof_free.empty()) {
+    hipEvent_t e = g_prof_free.back();
+    g_prof_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return e;
+}
+
+std::mutex g_cu_mutex;
+std::map<int, int> g_cu_count;
+
+}  // namespace
+
+void profile_before(const char* name, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_prof_mutex);
+  if (!g_prof_enabled || g_prof_records.size() >= kProfCapacity) return;
+  hipEvent_t e = take_event();
+  if (e == nullptr) return;
+  if (hipEventRecord(e, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    g_prof_free.push_back(e);
+    return;
+  }
+  g_prof_pending_name = name;
+  g_prof_pending_start = e;
+}
+
+void profile_after(hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_prof_mutex);
+  if (g_prof_pending_start == nullptr) return;
+  hipEvent_t e = take_event();
+  if (e != nullptr && hipEventRecord(e, stream) == hipSuccess) {
+    g_prof_records.push_back(ProfileRecord{g_prof_pending_name, g_prof_pending_start, e});
+  } else {
+    (void)hipGetLastError();
+    g_prof_free.push_back(g_prof_pending_start);
+    if (e != nullptr) g_prof_free.push_back(e);
+  }
+  g_prof_pending_start = nullptr;
+}
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  std::lock_guard<std::mutex> lock(g_cu_mutex);
+  auto it = g_cu_count.find(dev);
+  if (it != g_cu_count.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = 1;
+  }
+  g_cu_count[dev] = n;
+  return n;
+}
+
+}  // namespace cpthd
+
+using namespace cpthd;
+
+extern "C" {
+
+size_t cp_meta_bytes(int32_t num_docs, int32_t cp_size) {
+  if (num_docs < 0 || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return 0;
+  const size_t bytes = 64 + 4 * (size_t)(num_docs + 1) * (size_t)(cp_size + 1) + 4 * (size_t)cp_size;
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tokens,
+                  int32_t cp_size, int32_t policy, void* meta, size_t meta_bytes,
+                  cp_stream_t stream) {
+  if (cu_seqlens == nullptr || meta == nullptr) return CP_ERR_ARG;
+  if (num_docs < 0 || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return CP_ERR_ARG;
+  if (total_tokens < 0 || total_tokens > INT32_MAX) return CP_ERR_ARG;
+  if (policy != CP_POLICY_DUAL_CHUNK_SWAP && policy != CP_POLICY_PACKED_CONTIGUOUS) return CP_ERR_ARG;
+  if (policy == CP_POLICY_PACKED_CONTIGUOUS && total_tokens % cp_size != 0) return CP_ERR_SHAPE;
+  if (meta_bytes < cp_meta_bytes(num_docs, cp_size)) return CP_ERR_SHAPE;
+  int dev, st;
+  if ((st = current_device(&dev)) != CP_OK) return st;
+  if ((st = check_device_ptr(cu_seqlens, dev)) != CP_OK) return st;
+  if ((st = check_device_ptr(meta, dev)) != CP_OK) return st;
+  if ((st = check_alias({range_of(meta, (int64_t)meta_bytes)},
+                        {range_of(cu_seqlens, 4 * (int64_t)(num_docs + 1))})) != CP_OK)
+    return st;
+  return hip_status(launch_build_meta(cu_seqlens, num_docs, total_tokens, cp_size, policy, meta,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cp_meta_status(const void* meta, cp_stream_t stream, int32_t* flags_out,
+                   uint64_t* timeouts_out) {
+  if (meta == nullptr) return CP_ERR_ARG;
+  int dev, st;
+  if ((st = current_device(&dev)) != CP_OK) return st;
+  if ((st = check_device_ptr(meta, dev)) != CP_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) {
+    (void)hipGetLastError();
+    return CP_ERR_HIP;
+  }
+  cp_meta_header h;
+  if (hipMemcpy(&h, meta, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) {
+    (void)hipGetLastError();
+    return CP_ERR_HIP;
+  }
+  int32_t flags = h.flags;
+  if (h.magic != CP_META_MAGIC) flags |= CP_CALL_BAD_MAGIC;
+  if (flags_out) *flags_out = flags;
+  if (timeouts_out) *timeouts_out = h.wait_timeout_ranks;
+  if (flags != 0) return CP_ERR_META;
+  if (h.wait_timeout_ranks != 0) return CP_ERR_TIMEOUT;
+  return CP_OK;
+}
+
+static int layout_call(const void* in, void* out, int64_t total_tokens, int32_t heads,
+                       int32_t head_dim, int32_t dtype, const void* meta, cp_stream_t stream,
+                       bool to_local) {
+  if (is_fp8(dtype)) return CP_ERR_UNSUPPORTED;
+  if (!valid_layout_dtype(dtype)) return CP_ERR_ARG;
+  if (in == nullptr || out == nullptr || meta == nullptr) return CP_ERR_ARG;
+  if (total_tokens < 0 || total_tokens > INT32_MAX || heads < 1 || head_dim < 1) return CP_ERR_ARG;
+  const int64_t row_bytes = (int64_t)heads * head_dim * dtype_bytes(dtype);
+  const int64_t bytes = total_tokens * row_bytes;
+  int dev, st;
+  if ((st = current_device(&dev)) != CP_OK) return st;
+  if ((st = check_device_ptr(in, dev)) != CP_OK) return st;
+  if ((st = check_device_ptr(out, dev)) != CP_OK) return st;
+  if ((st = check_device_ptr(meta, dev)) != CP_OK) return st;
+  if ((st = check_alias({range_of(out, bytes)},
+                        {range_of(in, bytes), range_of(meta, sizeof(cp_meta_header))})) != CP_OK)
+    return st;
+  if (total_tokens == 0) return CP_OK;
+  PermuteArgs a;
+  memset(&a, 0, sizeof(a));
+  a.meta = const_cast<cp_meta_header*>(static_cast<const cp_meta_header*>(meta));
+  a.global = static_cast<char*>(to_local ? const_cast<void*>(in) : out);
+  a.local.p[0] = static_cast<char*>(to_local ? out : const_cast<void*>(in));
+  a.local_table = false;
+  a.to_local = to_local;
+  a.total_tokens = total_tokens;
+  a.row_bytes = row_bytes;
+  a.expect_cp_size = -1;
+  a.expect_policy = -1;
+  return hip_status(launch_permute(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cp_partition_thd(const void* x, void* parts, int64_t total_tokens, int32_t heads,
+                     int32_t head_dim, int32_t dtype, const void* meta, cp_stream_t stream) {
+  return layout_call(x, parts, total_tokens, heads, head_dim, dtype, meta, stream, true);
+}
+
+int cp_gather_thd(const void* parts, void* x, int64_t total_tokens, int32_t heads,
+                  int32_t head_dim, int32_t dtype, const void* meta, cp_stream_t stream) {
+  return layout_call(parts, x, total_tokens, heads, head_dim, dtype, meta, stream, false);
+}
+
+// Common scalar checks of the gradient-return family.
+static int grad_scalar_checks(int32_t rank, int32_t cp_size, int32_t n_tensors, int64_t total_tokens,
+                              int32_t heads, int32_t head_dim, int32_t in_dtype, int32_t out_dtype,
+                              const void* meta) {
+  int st;
+  if ((st = check_sum_dtypes(in_dtype, out_dtype)) != CP_OK) return st;
+  if (cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return CP_ERR_ARG;
+  if (rank != CP_ALL_RANKS && (rank < 0 || rank >= cp_size)) return CP_ERR_ARG;
+  if (n_tensors < 1) return CP_ERR_ARG;
+  if (total_tokens < 0 || total_tokens > INT32_MAX || heads < 1 || head_dim < 1) return CP_ERR_ARG;
+  if (total_tokens % (2 * (int64_t)cp_size) != 0) return CP_ERR_SHAPE;
+  if (meta == nullptr) return CP_ERR_ARG;
+  return CP_OK;
+}
+
+int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void* const* grads,
+                   void* const* slots, void* const* out, int64_t total_tokens, int32_t heads,
+                   int32_t head_dim, int32_t in_dtype, int32_t out_dtype, const void* meta,
+                   uint32_t* epochs, uint32_t epoch, int64_t wait_timeout_us,
+                   cp_stream_t stream) {
+  int st;
+  if ((st = grad_scalar_checks(rank, cp_size, n_tensors, total_tokens, heads, head_dim, in_dtype,
+                               out_dtype, meta)) != CP_OK)
+    return st;
+  if (grads == nullptr || slots == nullptr || out == nullptr) return CP_ERR_ARG;
+  const bool all = rank == CP_ALL_RANKS;
+  if (!all && epochs == nullptr) return CP_ERR_ARG;
+  const int W = cp_size;
+  const int64_t n = total_tokens / W;
+  const int64_t row_elems = (int64_t)heads * head_dim;
+  const int64_t in_row = row_elems * dtype_bytes(in_dtype);
+  const int64_t out_row = row_elems * dtype_bytes(out_dtype);
+  auto G = [&](int t, int w) { return grads[(size_t)t * W + w]; };
+  auto S = [&](int t, int o, int w) { return slots[((size_t)t * W + o) * W + w]; };
+  auto O = [&](int t, int o) { return out[(size_t)t * W + o]; };
+  const int w_lo = all ? 0 : rank, w_hi = all ? W : rank + 1;  // writers this call acts for
+  const int o_lo = w_lo, o_hi = w_hi;                           // owners this call sums for
+
+  // NULL checks on every table entry this call touches.
+  for (int t = 0; t < n_tensors; ++t) {
+    for (int w = w_lo; w < w_hi; ++w) {
+      if (G(t, w) == nullptr) return CP_ERR_ARG;
+      for (int o = 0; o < W; ++o)
+        if (S(t, o, w) == nullptr) return CP_ERR_ARG;
+    }
+    for (int o = o_lo; o < o_hi; ++o) {
+      if (O(t, o) == nullptr) return CP_ERR_ARG;
+      for (int w = 0; w < W; ++w)
+        if (S(t, o, w) == nullptr) return CP_ERR_ARG;
+    }
+  }
+  int dev;
+  if ((st = current_device(&dev)) != CP_OK) return st;
+  if ((st = check_device_ptr(meta, dev)) != CP_OK) return st;
+  if (epochs && (st = check_device_ptr(epochs, dev)) != CP_OK) return st;
+  std::vector<Range> ins, outs;
+  ins.push_back(range_of(meta, sizeof(cp_meta_header)));
+  for (int t = 0; t < n_tensors; ++t) {
+    for (int w = w_lo; w < w_hi; ++w) {
+      if ((st = check_device_ptr(G(t, w), dev)) != CP_OK) return st;
+      ins.push_back(range_of(G(t, w), total_tokens * in_row));
+      for (int o = 0; o < W; ++o) {
+        if ((st = check_device_ptr(S(t, o, w), dev)) != CP_OK) return st;
+        outs.push_back(range_of(S(t, o, w), n * in_row));
+      }
+    }
+    for (int o = o_lo; o < o_hi; ++o) {
+      if ((st = check_device_ptr(O(t, o), dev)) != CP_OK) return st;
+      outs.push_back(range_of(O(t, o), n * out_row));
+      for (int w = 0; w < W; ++w) {
+        if (w >= w_lo && w < w_hi) continue;  // already listed as an output of this call
+        if ((st = check_device_ptr(S(t, o, w), dev)) != CP_OK) return st;
+        ins.push_back(range_of(S(t, o, w), n * in_row));
+      }
+    }
+  }
+  if (epochs) {
+    outs.push_back(range_of(epochs, 4 * (int64_t)W * W));
+  }
+  if ((st = check_alias(outs, ins)) != CP_OK) return st;
+  if (total_tokens == 0) return CP_OK;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  cp_meta_header* h = const_cast<cp_meta_header*>(static_cast<const cp_meta_header*>(meta));
+  // 1. scatter: writer w's global gradient -> slot [o][w] of every owner o
+  for (int t = 0; t < n_tensors; ++t) {
+    for (int w = w_lo; w < w_hi; ++w) {
+      PermuteArgs a;
+      memset(&a, 0, sizeof(a));
+      a.meta = h;
+      a.global = static_cast<char*>(const_cast<void*>(G(t, w)));
+      for (int o = 0; o < W; ++o) a.local.p[o] = static_cast<char*>(S(t, o, w));
+      a.local_table = true;
+      a.to_local = true;
+      a.total_tokens = total_tokens;
+      a.row_bytes = in_row;
+      a.expect_cp_size = W;
+      a.expect_policy = CP_POLICY_DUAL_CHUNK_SWAP;
+      if ((st = hip_status(launch_permute(a, s))) != CP_OK) return st;
+    }
+  }
+  // 2-3. publish this call's writer epochs, wait for this call's owners
+  if (epochs) {
+    int rate_khz = 0;
+    if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        rate_khz <= 0) {
+      (void)hipGetLastError();
+      rate_khz = 100000;
+    }
+    const int64_t us = wait_timeout_us > 0 ? wait_timeout_us : 2000000;
+    const int64_t ticks = us * (int64_t)rate_khz / 1000;
+    if ((st = hip_status(launch_epoch_publish(epochs, W, all ? -1 : rank, epoch, s))) != CP_OK)
+      return st;
+    if ((st = hip_status(launch_epoch_wait(epochs, W, all ? -1 : rank, epoch, ticks, h, s))) != CP_OK)
+      return st;
+  }
+  // 4. owner o: out = slot 0 + slot 1 + ... + slot W-1
+  for (int t = 0; t < n_tensors; ++t) {
+    for (int o = o_lo; o < o_hi; ++o) {
+      SlotSumArgs a;
+      memset(&a, 0, sizeof(a));
+      for (int w = 0; w < W; ++w) a.in.p[w] = static_cast<const char*>(S(t, o, w));
+      a.out = static_cast<char*>(O(t, o));
+      a.num_slots = W;
+      a.n_elems = n * row_elems;
+      a.in_dtype = in_dtype;
+      a.out_dtype = out_dtype;
+      a.gate_meta = h;
+      a.gate_T = total_tokens;
+      a.owner = epochs ? o : -1;
+      if ((st = hip_status(launch_slot_sum(a, s))) != CP_OK) return st;
+    }
+  }
+  return CP_OK;
+}
+
+int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
+                         const void* const* grads, void* const* out, int64_t total_tokens,
+                         int32_t heads, int32_t head_dim, int32_t in_dtype, int32_t out_dtype,
+                         const void* meta, cp_stream_t stream) {
+  int st;
+  if ((st = grad_scalar_checks(rank, cp_size, n_tensors, total_tokens, heads, head_dim, in_dtype,
+                               out_dtype, meta)) != CP_OK)
+    return st;
+  if (grads == nullptr || out == nullptr) return CP_ERR_ARG;
+  const int W = cp_size;
+  const bool all = rank == CP_ALL_RANKS;
+  const int o_lo = all ? 0 : rank, o_hi = all ? W : rank + 1;
+  const int64_t n = total_tokens / W;
+  const int64_t row_elems = (int64_t)heads * head_dim;
+  const int64_t in_row = row_elems * dtype_bytes(in_dtype);
+  const int64_t out_row = row_elems * dtype_bytes(out_dtype);
+  for (int t = 0; t < n_tensors; ++t) {
+    for (int w = 0; w < W; ++w)
+      if (grads[(size_t)t * W + w] == nullptr) return CP_ERR_ARG;
+    for (int o = o_lo; o < o_hi; ++o)
+      if (out[(size_t)t * W + o] == nullptr) return CP_ERR_ARG;
+  }
+  int dev;
+  if ((st = current_device(&dev)) != CP_OK) return st;
+  if ((st = check_device_ptr(meta, dev)) != CP_OK) return st;
+  std::vector<Range> ins, outs;
+  ins.push_back(range_of(meta, sizeof(cp_meta_header)));
+  for (int t = 0; t < n_tensors; ++t) {
+    for (int w = 0; w < W; ++w) {
+      const void* g = grads[(size_t)t * W + w];
+      if ((st = check_device_ptr(g, dev)) != CP_OK) return st;
+      ins.push_back(range_of(g, total_tokens * in_row));
+    }
+    for (int o = o_lo; o < o_hi; ++o) {
+      void* p = out[(size_t)t * W + o];
+      if ((st = check_device_ptr(p, dev)) != CP_OK) return st;
+      outs.push_back(range_of(p, n * out_row));
+    }
+  }
+  if ((st = check_alias(outs, ins)) != CP_OK) return st;
+  if (total_tokens == 0) return CP_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (int t = 0; t < n_tensors; ++t) {
+    FusedArgs a;
+    memset(&a, 0, sizeof(a));
+    a.meta = const_cast<cp_meta_header*>(static_cast<const cp_meta_header*>(meta));
+    for (int w = 0; w < W; ++w) a.grads.p[w] = static_cast<const char*>(grads[(size_t)t * W + w]);
+    for (int o = o_lo; o < o_hi; ++o) a.out.p[o] = static_cast<char*>(out[(size_t)t * W + o]);
+    a.cp_size = W;
+    a.owner_begin = o_lo;
+    a.owner_end = o_hi;
+    a.total_tokens = total_tokens;
+    a.row_elems = row_elems;
+    a.in_dtype = in_dtype;
+    a.out_dtype = out_dtype;
+    if ((st = hip_status(launch_fused(a, s))) != CP_OK) return st;
+  }
+  return CP_OK;
+}
+
+int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t n_elems,
+                int32_t in_dtype, int32_t out_dtype, cp_stream_t stream) {
+  int st;
+  if ((st = check_sum_dtypes(in_dtype, out_dtype)) != CP_OK) return st;
+  if (num_slots < 1 || num_slots > CP_MAX_CP_SIZE || n_elems < 0) return CP_ERR_ARG;
+  if (slots == nullptr || out == nullptr) return CP_ERR_ARG;
+  for (int w = 0; w < num_slots; ++w)
+    if (slots[w] == nullptr) return CP_ERR_ARG;
+  int dev;
+  if ((st = current_device(&dev)) != CP_OK) return st;
+  std::vector<Range> ins;
+  for (int w = 0; w < num_slots; ++w) {
+    if ((st = check_device_ptr(slots[w], dev)) != CP_OK) return st;
+    ins.push_back(range_of(slots[w], n_elems * dtype_bytes(in_dtype)));
+  }
+  if ((st = check_device_ptr(out, dev)) != CP_OK) return st;
+  if ((st = check_alias({range_of(out, n_elems * dtype_bytes(out_dtype))}, ins)) != CP_OK) return st;
+  SlotSumArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int w = 0; w < num_slots; ++w) a.in.p[w] = static_cast<const char*>(slots[w]);
+  a.out = static_cast<char*>(out);
+  a.num_slots = num_slots;
+  a.n_elems = n_elems;
+  a.in_dtype = in_dtype;
+  a.out_dtype = out_dtype;
+  a.gate_meta = nullptr;
+  a.owner = -1;
+  return hip_status(launch_slot_sum(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char* cp_status_string(int status) {
+  switch (status) {
+    case CP_OK: return "ok";
+    case CP_ERR_ARG: return "invalid argument";
+    case CP_ERR_UNSUPPORTED: return "unsupported dtype or mode";
+    case CP_ERR_SHAPE: return "inconsistent sizes";
+    case CP_ERR_DEVICE: return "pointer is not device memory of the current device";
+    case CP_ERR_ALIAS: return "output overlaps an input or another output";
+    case CP_ERR_HIP: return "HIP runtime error";
+    case CP_ERR_TIMEOUT: return "epoch wait timed out";
+    case CP_ERR_META: return "invalid metadata or call/metadata mismatch";
+    default: return "unknown status";
+  }
+}
+
+int cp_version(void) { return 100; }
+
+int cp_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lock(g_prof_mutex);
+  g_prof_enabled = enable != 0;
+  return CP_OK;
+}
+
+int cp_profile_read(char* names, int64_t* counts, double* total_ms, int capacity) {
+  std::vector<ProfileRecord> recs;
+  {
+    std::lock_guard<std::mutex> lock(g_prof_mutex);
+    recs.swap(g_prof_records);
+  }
+  std::vector<std::string> order;
+  std::map<std::string, std::pair<int64_t, double>> agg;
+  int status = CP_OK;
+  for (ProfileRecord& r : recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+      (void)hipGetLastError();
+      status = CP_ERR_HIP;
+    }
+    if (agg.find(r.name) == agg.end()) order.push_back(r.name);
+    auto& slot = agg[r.name];
+    slot.first += 1;
+    slot.second += ms;
+  }
+  {
+    std::lock_guard<std::mutex> lock(g_prof_mutex);
+    for (ProfileRecord& r : recs) {
+      g_prof_free.push_back(r.start);
+      g_prof_free.push_back(r.stop);
+    }
+  }
+  if (status != CP_OK) return -status;
+  int k = 0;
+  for (const std::string& nm : order) {
+    if (k >= capacity) break;
+    if (names) {
+      strncpy(names + (size_t)k * 128, nm.c_str(), 127);
+      names[(size_t)k * 128 + 127] = '\0';
+    }
+    if (counts) counts[k] = agg[nm].first;
+    if (total_ms) total_ms[k] = agg[nm].second;
+    ++k;
+  }
+  return (int)order.size();
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// Internal interface between the C-ABI layer (abi.cpp) and the HIP kernels.
+// Host code only sees launch functions; kernels live in the .hip files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cpthd.h"
+
+namespace cpthd {
+
+constexpr int kMaxRanks = CP_MAX_CP_SIZE;
+constexpr int kBlock = 256;           // threads per workgroup: 4 wave64s
+constexpr int kWavesPerBlock = kBlock / 64;
+
+// Byte offsets inside the metadata buffer (layout documented in cpthd.h).
+__host__ __device__ inline int64_t meta_cu_offset() { return 64; }
+__host__ __device__ inline int64_t meta_local_cu_offset(int32_t B) { return 64 + 4 * (int64_t)(B + 1); }
+__host__ __device__ inline int64_t meta_n_local_offset(int32_t B, int32_t W) {
+  return 64 + 4 * (int64_t)(B + 1) * (W + 1);
+}
+
+// Fixed-capacity pointer table passed by value in the kernel arguments.
+struct RankPtrs {
+  char* p[kMaxRanks];
+};
+struct ConstRankPtrs {
+  const char* p[kMaxRanks];
+};
+
+// Bytes per element of a cp_dtype (0 for unsupported).
+inline int dtype_bytes(int32_t dt) {
+  switch (dt) {
+    case CP_F32: return 4;
+    case CP_BF16: return 2;
+    case CP_F16: return 2;
+    default: return 0;
+  }
+}
+
+// ---------------------------------------------------------------- metadata
+hipError_t launch_build_meta(const int32_t* cu, int32_t B, int64_t T, int32_t W, int32_t policy,
+                             void* meta, hipStream_t stream);
+
+// ---------------------------------------------------------------- row permutation
+// One launch moves all T rows between the global layout and the per-rank
+// layout.  `global` is x ([T, row]); the local side is either one contiguous
+// [W, T/W, row] buffer (local_table == false, local.p[0] = base) or one
+// [T/W, row] buffer per rank (local_table == true).  to_local: partition /
+// scatter (global -> local); otherwise gather (local -> global).
+struct PermuteArgs {
+  cp_meta_header* meta;
+  char* global;
+  RankPtrs local;
+  bool local_table;
+  bool to_local;
+  int64_t total_tokens;
+  int64_t row_bytes;
+  int32_t expect_cp_size;   // -1: any
+  int32_t expect_policy;    // -1: any
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- reductions
+// out[k] = sum_w in[w][k] in fp32, w = 0..W-1 in order, seeded with in[0].
+struct SlotSumArgs {
+  ConstRankPtrs in;
+  char* out;
+  int32_t num_slots;
+  int64_t n_elems;
+  int32_t in_dtype;
+  int32_t out_dtype;
+  // Optional fail-closed gate (gradient return): when gate_meta is set the
+  // kernel writes nothing unless the meta is valid dual-chunk-swap metadata
+  // for gate_T tokens and num_slots ranks, and, when owner >= 0, bit `owner`
+  // of meta->wait_timeout_ranks is clear.
+  cp_meta_header* gate_meta;
+  int64_t gate_T;
+  int32_t owner;
+};
+hipError_t launch_slot_sum(const SlotSumArgs& a, hipStream_t stream);
+
+// Fused scatter+sum: out[o][i] = sum_w grads[w][g_o(i)] for owners o in
+// [owner_begin, owner_end).
+struct FusedArgs {
+  cp_meta_header* meta;
+  ConstRankPtrs grads;  // [W] writer views, [T, row]
+  RankPtrs out;         // [W] owner outputs, [T/W, row] (entries outside the owner range unused)
+  int32_t cp_size;
+  int32_t owner_begin;
+  int32_t owner_end;
+  int64_t total_tokens;
+  int64_t row_elems;
+  int32_t in_dtype;
+  int32_t out_dtype;
+};
+hipError_t launch_fused(const FusedArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- epochs
+// Writer `writer` (or every writer when writer < 0) stores `epoch` into
+// epochs[o][writer] for every owner o, with release ordering.
+hipError_t launch_epoch_publish(uint32_t* epochs, int32_t W, int32_t writer, uint32_t epoch,
+                                hipStream_t stream);
+// Owner `owner` (or every owner when owner < 0) waits until epochs[o][w] >=
+// epoch for all w, or until timeout_ticks of the device wall clock pass; then
+// records the owners still pending in meta->wait_timeout_ranks.
+hipError_t launch_epoch_wait(const uint32_t* epochs, int32_t W, int32_t owner, uint32_t epoch,
+                             int64_t timeout_ticks, cp_meta_header* meta, hipStream_t stream);
+
+// ---------------------------------------------------------------- timing hooks
+// Called by every launch function around its kernel launch.
+void profile_before(const char* name, hipStream_t stream);
+void profile_after(hipStream_t stream);
+
+// Number of compute units of the current device (cached).
+int device_cu_count();
+
+}  // namespace cpthd

@@ -1,0 +1,244 @@
+// Row-permutation copy engine: THD partition, inverse gather and the
+// gradient-return scatter.
+//
+// Ownership ("[PyTorch] Add experimental packed-contiguous THD all-gather CP",
+// sections "Why" and commit messages; "Add stream-ordered CP gradient return
+// primitive", author's reply): under dual-chunk-swap every document b of
+// length L_b is cut into 2W chunks of c_b = L_b/(2W) tokens and rank r holds
+// chunk r then chunk 2W-1-r, document after document; under packed-contiguous
+// rank r holds tokens [r n, (r+1) n), n = T/W.  So local row i of rank r, in
+// document b (local_cu[b] <= i < local_cu[b+1], local_cu = cu/W), offset
+// j = i - local_cu[b], is global row
+//     cu[b] + r c_b + j                   if j <  c_b
+//     cu[b] + (2W-1-r) c_b + (j - c_b)    if j >= c_b.
+//
+// Design (gfx950): pure data movement, HBM-bound.  Each wave64 owns groups of
+// G consecutive local rows (grid-stride over groups, grid sized to the
+// resident capacity so every wave does the same amount of work).  The row map
+// is computed once per group in wave-uniform (scalar) code: a binary search
+// over the per-rank document table, then an incremental cursor for the rest of
+// the group.  Each lane then moves 16-byte units of the G rows (VPL units per
+// row, up to G*VPL loads in flight per lane) with non-temporal loads and
+// stores, fully coalesced (a wave touches 1 KiB contiguous per instruction).
+#include "cpthd_internal.h"
+
+#include <mutex>
+
+namespace cpthd {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename U>
+__device__ __forceinline__ U load_nt(const U* p) {
+  return __builtin_nontemporal_load(p);
+}
+template <typename U>
+__device__ __forceinline__ void store_nt(U* p, U v) {
+  __builtin_nontemporal_store(v, p);
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Wave-uniform cursor over the flat local row index p = r*n + i.
+struct Cursor {
+  int32_t r;        // rank
+  int64_t i;        // local row inside the rank
+  int32_t b;        // document (dual-chunk-swap only)
+  int64_t lstart;   // local_cu[b]
+  int64_t lend;     // local_cu[b+1]
+  int64_t gstart;   // cu[b]
+  int64_t c;        // chunk length of document b
+};
+
+__device__ __forceinline__ void load_doc(Cursor& k, const int32_t* cu, const int32_t* lcu) {
+  k.lstart = lcu[k.b];
+  k.lend = lcu[k.b + 1];
+  k.gstart = cu[k.b];
+  k.c = (k.lend - k.lstart) >> 1;
+}
+
+__device__ __forceinline__ void seek(Cursor& k, int64_t p, int64_t n, int32_t B, bool dcs,
+                                     const int32_t* cu, const int32_t* lcu) {
+  k.r = (int32_t)(p / n);
+  k.i = p - (int64_t)k.r * n;
+  if (!dcs) return;
+  int lo = 0, hi = B - 1;  // largest b with lcu[b] <= i (lcu[0] = 0 <= i)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)lcu[mid] <= k.i) lo = mid; else hi = mid - 1;
+  }
+  k.b = lo;
+  load_doc(k, cu, lcu);
+}
+
+__device__ __forceinline__ void advance(Cursor& k, int64_t n, bool dcs, const int32_t* cu,
+                                        const int32_t* lcu) {
+  ++k.i;
+  if (k.i == n) {
+    ++k.r;
+    k.i = 0;
+    if (dcs) { k.b = 0; load_doc(k, cu, lcu); }
+  }
+  if (dcs) {
+    while (k.i >= k.lend) { ++k.b; load_doc(k, cu, lcu); }
+  }
+}
+
+__device__ __forceinline__ int64_t global_row(const Cursor& k, int32_t W, int64_t n, bool dcs) {
+  if (!dcs) return (int64_t)k.r * n + k.i;
+  const int64_t j = k.i - k.lstart;
+  return j < k.c ? k.gstart + (int64_t)k.r * k.c + j
+                 : k.gstart + (int64_t)(2 * W - 1 - k.r) * k.c + (j - k.c);
+}
+
+// Reads the metadata header; returns false (and records why) when the call
+// must not touch any output.
+__device__ __forceinline__ bool meta_ok(cp_meta_header* h, int64_t T, int32_t expect_W,
+                                        int32_t expect_policy) {
+  int code = 0;
+  if (h->magic != CP_META_MAGIC) code = CP_CALL_BAD_MAGIC;
+  else if (h->flags & CP_META_BUILD_MASK) code = CP_CALL_USED_INVALID_META;
+  else if (h->total_tokens != T) code = CP_CALL_TOKENS_MISMATCH;
+  else if (expect_W >= 0 && h->cp_size != expect_W) code = CP_CALL_CP_SIZE_MISMATCH;
+  else if (expect_policy >= 0 && h->policy != expect_policy) code = CP_CALL_POLICY_MISMATCH;
+  if (code != 0 && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&h->flags, code);
+  return code == 0;
+}
+
+template <typename U, int VPL, int G>
+__global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
+  cp_meta_header* h = a.meta;
+  if (!meta_ok(h, a.total_tokens, a.expect_cp_size, a.expect_policy)) return;
+
+  const int64_t T = a.total_tokens;
+  const int32_t W = h->cp_size;
+  const int32_t B = h->num_docs;
+  const int64_t n = h->local_tokens;
+  const bool dcs = h->policy == CP_POLICY_DUAL_CHUNK_SWAP;
+  const int32_t* cu = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(h) + 64);
+  const int32_t* lcu = cu + (B + 1);  // local_cu[0][*] = cu / W
+  const int64_t upr = a.row_bytes / (int64_t)sizeof(U);  // units per row
+
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  const int64_t ngroups = (T + G - 1) / G;
+
+  for (int64_t grp = wave; grp < ngroups; grp += nwaves) {
+    const int64_t p0 = grp * G;
+    Cursor k;
+    seek(k, p0, n, B, dcs, cu, lcu);
+    const U* src[G];
+    U* dst[G];
+    bool ok[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      ok[g] = p0 + g < T;
+      src[g] = nullptr;
+      dst[g] = nullptr;
+      if (ok[g]) {
+        char* gptr = a.global + global_row(k, W, n, dcs) * a.row_bytes;
+        char* lptr = a.local_table ? a.local.p[k.r] + k.i * a.row_bytes
+                                   : a.local.p[0] + ((int64_t)k.r * n + k.i) * a.row_bytes;
+        src[g] = reinterpret_cast<const U*>(a.to_local ? gptr : lptr);
+        dst[g] = reinterpret_cast<U*>(a.to_local ? lptr : gptr);
+        if (g + 1 < G && p0 + g + 1 < T) advance(k, n, dcs, cu, lcu);
+      }
+    }
+    for (int64_t cb = 0; cb < upr; cb += 64 * VPL) {
+      U buf[G][VPL];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int m = 0; m < VPL; ++m) {
+          const int64_t col = cb + lane + 64 * m;
+          if (ok[g] && col < upr) buf[g][m] = load_nt(src[g] + col);
+        }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int m = 0; m < VPL; ++m) {
+          const int64_t col = cb + lane + 64 * m;
+          if (ok[g] && col < upr) store_nt(dst[g] + col, buf[g][m]);
+        }
+    }
+  }
+}
+
+typedef void (*PermuteKernel)(PermuteArgs);
+
+struct Variant {
+  PermuteKernel fn;
+  int group;
+  const char* name;
+  int max_blocks_per_cu;  // cached occupancy, 0 = unknown
+};
+
+template <typename U, int VPL>
+constexpr int group_for() {
+  return VPL <= 1 ? 8 : VPL <= 2 ? 4 : VPL <= 5 ? 2 : 1;
+}
+
+#define CP_VARIANT(U, VPL, UNAME)                                                         \
+  Variant{permute_rows_kernel<U, VPL, group_for<U, VPL>()>, group_for<U, VPL>(),          \
+          "permute_rows<" UNAME "," #VPL ">", 0}
+
+#define CP_VARIANTS_FOR(U, UNAME)                                                        \
+  { CP_VARIANT(U, 1, UNAME), CP_VARIANT(U, 2, UNAME), CP_VARIANT(U, 4, UNAME),            \
+    CP_VARIANT(U, 5, UNAME), CP_VARIANT(U, 8, UNAME), CP_VARIANT(U, 10, UNAME),           \
+    CP_VARIANT(U, 16, UNAME) }
+
+constexpr int kVpl[7] = {1, 2, 4, 5, 8, 10, 16};
+
+Variant g_variants[4][7] = {
+    CP_VARIANTS_FOR(u32x4, "16B"),
+    CP_VARIANTS_FOR(u32x2, "8B"),
+    CP_VARIANTS_FOR(unsigned int, "4B"),
+    CP_VARIANTS_FOR(unsigned short, "2B"),
+};
+std::mutex g_occ_mutex;
+
+}  // namespace
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
+  if (a.total_tokens == 0 || a.row_bytes == 0) return hipSuccess;
+  // Widest unit that divides the row size and every base address.
+  uintptr_t align_bits = (uintptr_t)a.global | (uintptr_t)a.row_bytes;
+  const int nlocal = a.local_table ? kMaxRanks : 1;
+  for (int k = 0; k < nlocal; ++k) align_bits |= (uintptr_t)a.local.p[k];
+  int ui;
+  int usize;
+  if ((align_bits & 15) == 0) { ui = 0; usize = 16; }
+  else if ((align_bits & 7) == 0) { ui = 1; usize = 8; }
+  else if ((align_bits & 3) == 0) { ui = 2; usize = 4; }
+  else if ((align_bits & 1) == 0) { ui = 3; usize = 2; }
+  else return hipErrorInvalidValue;  // rows of 2- or 4-byte elements are always even
+  const int64_t upr = a.row_bytes / usize;
+  const int64_t need = (upr + 63) / 64;
+  int vi = 6;
+  for (int k = 0; k < 7; ++k)
+    if (kVpl[k] >= need) { vi = k; break; }
+  Variant& v = g_variants[ui][vi];
+  {
+    std::lock_guard<std::mutex> lock(g_occ_mutex);
+    if (v.max_blocks_per_cu == 0) {
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, v.fn, kBlock, 0) != hipSuccess || nb < 1)
+        nb = 1;
+      v.max_blocks_per_cu = nb;
+    }
+  }
+  const int64_t groups = (a.total_tokens + v.group - 1) / v.group;
+  const int64_t want = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t cap = (int64_t)device_cu_count() * v.max_blocks_per_cu;
+  const int blocks = (int)(want < cap ? want : cap);
+  profile_before(v.name, stream);
+  hipLaunchKernelGGL(v.fn, dim3(blocks), dim3(kBlock), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  profile_after(stream);
+  return e;
+}
+
+}  // namespace cpthd
