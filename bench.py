@@ -1,0 +1,331 @@
+"""Benchmark: the THD context-parallel layout + gradient-return hot path at S=262144.
+
+One step = one pass of every stage of the path over one batch of synthetic
+input already resident in HBM:
+  * metadata for the three token layouts (cp_build_meta),
+  * dual-chunk-swap partition + inverse gather of Q, K, V [262144, 20, 128] bf16
+    (packed documents, log-uniform lengths in [256, 8192], W = 4),
+  * packed-contiguous partition + inverse gather of the same Q, K, V
+    (documents of U{1..4096} tokens, W = 4),
+  * owner gradient return, W = 4: 4 writers x {dK, dV} [262144, 20, 128] fp32
+    scattered into 4 x 4 owner slots (two-chunk layout), epochs published and
+    awaited, slots summed in fixed order into each owner's dK/dV,
+  * fused scatter+sum gradient return on the same gradients,
+  * the W = 8 fp32 slot-sum sweep, 1 KiB .. 16 MiB per slot.
+
+Prints one JSON line: whole-step algorithmic HBM bytes / step time in GB/s,
+the roofline of the dominant kernel (HIP events on its launch stream over the
+timed region) and the CPU oracle's rate on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, AMD public specification
+METRIC = "HBM GB/s & % of peak: THD CP partition/gather + dK/dV grad-return, S=262144"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Step:
+    """Buffers and calls of one step; every op records its algorithmic bytes."""
+
+    def __init__(self, cp, WL, torch, S: int, device: str):
+        self.cp, self.torch = cp, torch
+        dev = device
+        self.ops = []  # (name, bytes, callable)
+        w_dcs = WL.WORKLOADS["dcs_s256k_w4"]
+        w_pc = WL.WORKLOADS["pc_s256k_w4"]
+        w_gr = WL.WORKLOADS["grad_s256k_w4"]
+        w_sw = WL.WORKLOADS["sweep_w8"]
+        if S != w_dcs.total_tokens:
+            w_dcs, w_pc, w_gr = (WL.scaled(w, total_tokens=S) for w in (w_dcs, w_pc, w_gr))
+        self.S = S
+        self.workloads = (w_dcs, w_pc, w_gr)
+        W = w_dcs.cp_size
+        H, D = w_dcs.heads, w_dcs.head_dim
+        # ---- layout inputs (same Q,K,V under both policies: matched inputs)
+        cu_dcs = torch.from_numpy(WL.cu_seqlens(w_dcs)).to(dev)
+        cu_pc = torch.from_numpy(WL.cu_seqlens(w_pc)).to(dev)
+        cu_gr = torch.from_numpy(WL.cu_seqlens(w_gr)).to(dev)
+        self.num_docs = (cu_dcs.numel() - 1, cu_pc.numel() - 1)
+        self.qkv = WL.random_tensors(w_dcs, 3, device=dev)
+        self.parts = [torch.empty((W, S // W, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+        self.back = [torch.empty_like(x) for x in self.qkv]
+        self.meta_dcs = cp.cp_build_meta(cu_dcs, S, W, cp.CP_POLICY_DUAL_CHUNK_SWAP, check=True)
+        self.meta_pc = cp.cp_build_meta(cu_pc, S, W, cp.CP_POLICY_PACKED_CONTIGUOUS, check=True)
+        self.meta_gr = cp.cp_build_meta(cu_gr, S, W, cp.CP_POLICY_DUAL_CHUNK_SWAP, check=True)
+        row_bf16 = H * D * 2
+        # ---- gradient return inputs
+        Wg = w_gr.cp_size
+        n = S // Wg
+        vals = WL.random_tensors(w_gr, 2 * Wg, device=dev)
+        self.grads = [vals[:Wg], vals[Wg:]]
+        row_f32 = w_gr.heads * w_gr.head_dim * 4
+        self.slots = [[[torch.empty((n, w_gr.heads, w_gr.head_dim), device=dev) for _ in range(Wg)]
+                       for _ in range(Wg)] for _ in range(2)]
+        self.out = [[torch.empty((n, w_gr.heads, w_gr.head_dim), device=dev) for _ in range(Wg)]
+                    for _ in range(2)]
+        self.fused = [[torch.empty_like(o) for o in row] for row in self.out]
+        self.epochs = torch.zeros((Wg, Wg), dtype=torch.int32, device=dev)
+        self.epoch = 0
+        # ---- sweep
+        self.sweep = []
+        for nbytes in WL.SWEEP_BYTES:
+            k = nbytes // 4
+            slots = WL.random_tensors(w_sw, 8, shape=(k,), device=dev, seed_offset=nbytes)
+            self.sweep.append((nbytes, slots, torch.empty(k, device=dev)))
+
+        metas = [(cu_dcs, cp.CP_POLICY_DUAL_CHUNK_SWAP, self.meta_dcs),
+                 (cu_pc, cp.CP_POLICY_PACKED_CONTIGUOUS, self.meta_pc),
+                 (cu_gr, cp.CP_POLICY_DUAL_CHUNK_SWAP, self.meta_gr)]
+
+        def build_metas():
+            for cu, pol, m in metas:
+                cp.cp_build_meta(cu, S, m.cp_size, pol, meta=m.buf)
+
+        meta_bytes = sum(4 * (cu.numel()) + 4 * (cu.numel()) * (W + 1) + 4 * W for cu, _, _ in metas)
+        self.ops.append(("build_meta x3", meta_bytes, build_metas))
+        for pname, meta in (("dual_chunk_swap", self.meta_dcs), ("packed_contiguous", self.meta_pc)):
+            self.ops.append((f"partition_{pname} QKV", 3 * 2 * S * row_bf16,
+                             lambda meta=meta: [cp.cp_partition_thd(x, meta, parts=p)
+                                                for x, p in zip(self.qkv, self.parts)]))
+            self.ops.append((f"gather_{pname} QKV", 3 * 2 * S * row_bf16,
+                             lambda meta=meta: [cp.cp_gather_thd(p, meta, x=b)
+                                                for p, b in zip(self.parts, self.back)]))
+
+        def grad_return():
+            self.epoch += 1
+            cp.cp_grad_return(self.grads, self.slots, self.out, self.meta_gr, epochs=self.epochs,
+                              epoch=self.epoch)
+
+        self.ops.append(("grad_return dK,dV", 2 * (3 * Wg + 1) * S * row_f32, grad_return))
+        self.ops.append(("grad_return_fused dK,dV", 2 * (Wg + 1) * S * row_f32,
+                         lambda: cp.cp_grad_return_fused(self.grads, self.fused, self.meta_gr)))
+        self.ops.append(("slot_sum sweep W=8 1KiB..16MiB", sum(9 * nb for nb, _, _ in self.sweep),
+                         lambda: [cp.cp_slot_sum(s, o) for _, s, o in self.sweep]))
+        # per-launch algorithmic bytes of each kernel, by the kernel's role in its op
+        self.kernel_bytes = {
+            "scatter": 2 * S * row_f32,                 # one writer, one tensor: read T rows, write T rows
+            "owner_sum": (Wg + 1) * n * row_f32,        # one owner, one tensor: read W slots, write 1
+            "layout": 2 * S * row_bf16,                 # one tensor: read T rows, write T rows
+            "fused": (Wg + 1) * S * row_f32,            # one tensor, all owners
+        }
+
+    @property
+    def step_bytes(self) -> int:
+        return sum(b for _, b, _ in self.ops)
+
+    def run(self):
+        for _, _, fn in self.ops:
+            fn()
+
+
+def attribute_kernels(step: Step, cp, torch):
+    """Run each op once with timing hooks on and map kernel name -> bytes per launch."""
+    per_kernel = {}
+    torch.cuda.synchronize()
+    cp.cp_profile_enable(True)
+    for name, nbytes, fn in step.ops:
+        fn()
+        prof = cp.cp_profile_read()
+        for kname, (count, _) in prof.items():
+            if name.startswith("grad_return dK"):
+                role = "scatter" if kname.startswith("permute_rows") else \
+                    "owner_sum" if kname.startswith("slot_sum") else None
+                b = step.kernel_bytes[role] if role else 0
+            elif name.startswith("grad_return_fused"):
+                b = step.kernel_bytes["fused"]
+            elif name.startswith(("partition", "gather")):
+                b = step.kernel_bytes["layout"]
+            elif name.startswith("slot_sum sweep"):
+                b = nbytes / count
+            else:
+                b = 0
+            per_kernel.setdefault(kname, []).append((count, b))
+    cp.cp_profile_enable(False)
+    # bytes per step per kernel name
+    return {k: sum(c * b for c, b in v) for k, v in per_kernel.items()}, \
+        {k: sum(c for c, _ in v) for k, v in per_kernel.items()}
+
+
+def cpu_baseline(S_sample: int, WL):
+    """The CPU oracle, as it stands, on the same step at S_sample tokens."""
+    import numpy as np
+    import torch
+
+    from oracle import cp_oracle as O
+
+    w_dcs, w_pc, w_gr = (WL.scaled(WL.WORKLOADS[n], total_tokens=S_sample)
+                         for n in ("dcs_s256k_w4", "pc_s256k_w4", "grad_s256k_w4"))
+    cu_dcs, cu_pc, cu_gr = WL.cu_seqlens(w_dcs), WL.cu_seqlens(w_pc), WL.cu_seqlens(w_gr)
+    qkv = [t.view(torch.int16).numpy().view(np.uint16) for t in WL.random_tensors(w_dcs, 3)]
+    Wg = w_gr.cp_size
+    vals = [t.numpy() for t in WL.random_tensors(w_gr, 2 * Wg)]
+    grads = [vals[:Wg], vals[Wg:]]
+    sweep_sizes = [nb for nb in WL.SWEEP_BYTES if nb <= (1 << 24)]
+    rng = np.random.default_rng(6)
+    sweep = [[rng.standard_normal(nb // 4).astype(np.float32) for _ in range(8)] for nb in sweep_sizes]
+    row_bf16 = w_dcs.heads * w_dcs.head_dim * 2
+    row_f32 = w_gr.heads * w_gr.head_dim * 4
+    nbytes = 0
+    t0 = time.perf_counter()
+    for cu, pol, W in ((cu_dcs, O.DUAL_CHUNK_SWAP, w_dcs.cp_size), (cu_pc, O.PACKED_CONTIGUOUS, w_pc.cp_size)):
+        O.local_cu_seqlens(cu, S_sample, W, pol)
+        for x in qkv:
+            parts = O.partition(x, cu, W, pol)
+            O.gather(parts, cu, W, pol)
+            nbytes += 2 * 2 * S_sample * row_bf16
+    for gt in grads:
+        O.grad_return(gt, cu_gr, Wg, "f32", "f32")
+        nbytes += (3 * Wg + 1) * S_sample * row_f32
+        O.grad_return_fused(gt, cu_gr, Wg, "f32", "f32")
+        nbytes += (Wg + 1) * S_sample * row_f32
+    for nb, s in zip(sweep_sizes, sweep):
+        O.slot_sum(s, "f32", "f32")
+        nbytes += 9 * nb
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full step (metadata, DCS and PC partition+gather of Q,K,V, unfused and "
+                      f"fused dK/dV gradient return, W=8 sweep) at S={S_sample} instead of 262144, "
+                      f"same heads, head_dim, cp_size, dtypes and distributions; numpy, one thread; "
+                      f"{nbytes / 1e9:.2f} GB algorithmic in {dt:.1f} s"}
+
+
+def sweep_latency(step: Step, cp, torch, reps: int = 200):
+    """Per-call latency (host validation + launch + kernel) of the W=8 slot sum."""
+    res = []
+    for nbytes, slots, out in step.sweep:
+        for _ in range(5):
+            cp.cp_slot_sum(slots, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            cp.cp_slot_sum(slots, out)
+        e1.record()
+        torch.cuda.synchronize()
+        per_call_us = e0.elapsed_time(e1) * 1000.0 / reps
+        cp.cp_profile_enable(True)
+        for _ in range(20):
+            cp.cp_slot_sum(slots, out)
+        prof = cp.cp_profile_read()
+        cp.cp_profile_enable(False)
+        kcount = sum(c for c, _ in prof.values())
+        kms = sum(m for _, m in prof.values())
+        res.append({"bytes_per_slot": nbytes, "us_per_call": round(per_call_us, 2),
+                    "kernel_us": round(kms * 1000.0 / max(kcount, 1), 2)})
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=262144, help="S (default 262144)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep-latency", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the W context-parallel ranks are emulated as slot "
+              "buffers in one GPU's HBM, and no multi-GPU path is built; run with --gpus 1.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from thd_token_layout_amd import cpthd as cp
+    from thd_token_layout_amd import workloads as WL
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"[bench] building inputs S={args.tokens}")
+    step = Step(cp, WL, torch, args.tokens, dev)
+    torch.cuda.synchronize()
+    log("[bench] attributing kernels")
+    kbytes, kcount = attribute_kernels(step, cp, torch)
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    cp.cp_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.run()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    cp.cp_profile_enable(False)
+    prof = cp.cp_profile_read(capacity=256)
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    step_bytes = step.step_bytes
+    value = step_bytes / (ms_per_step / 1000.0) / 1e9
+    log(f"[bench] {ms_per_step:.3f} ms/step, {value:.1f} GB/s")
+
+    kernels = []
+    for name, (count, total_ms) in prof.items():
+        b = kbytes.get(name, 0) * args.steps
+        kernels.append({"kernel": name, "launches": count, "avg_us": round(total_ms * 1000 / count, 2),
+                        "total_ms": round(total_ms, 3),
+                        "gbs": round(b / (total_ms / 1000.0) / 1e9, 1) if total_ms > 0 and b else None,
+                        "bytes_per_launch": int(b / count) if count else 0})
+    kernels.sort(key=lambda k: -k["total_ms"])
+    dom = kernels[0]
+    achieved = dom["gbs"] or 0.0
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": dom["kernel"], "bytes_per_launch": dom["bytes_per_launch"],
+                "avg_launch_us": dom["avg_us"]}
+
+    sweep = None if args.no_sweep_latency else sweep_latency(step, cp, torch)
+    w_dcs, w_pc, w_gr = step.workloads
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"THD CP layout + gradient return at S={args.tokens}: DCS and packed-contiguous "
+                        f"partition+gather of Q,K,V [S,20,128] bf16 (W=4), dK/dV gradient return "
+                        f"unfused and fused (W=4, [S,20,128] fp32), W=8 fp32 slot-sum sweep",
+            "S": args.tokens, "cp_size": 4, "heads": 20, "head_dim": 128,
+            "layout_dtype": "bf16", "grad_dtype": "f32", "accumulate": "f32",
+            "docs_dcs": step.num_docs[0], "docs_pc": step.num_docs[1],
+            "step_bytes": step_bytes,
+        },
+        "roofline": roofline,
+        "kernels": kernels,
+        "ops": [{"op": n, "bytes": b} for n, b, _ in step.ops],
+        "sweep_latency": sweep,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline at S={args.cpu_sample_tokens}")
+        result["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens, WL)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

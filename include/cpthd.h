@@ -92,6 +92,14 @@ enum cp_dtype {
 #define CP_ALL_RANKS (-1)
 #define CP_MAX_CP_SIZE 64
 
+/* phases of cp_grad_return ([GR] "Sequence Diagram": scatter, epoch publish,
+ * epoch wait, accumulate); CP_PHASE_ALL runs the four in that order */
+#define CP_PHASE_SCATTER 0x1
+#define CP_PHASE_PUBLISH 0x2
+#define CP_PHASE_WAIT    0x4
+#define CP_PHASE_SUM     0x8
+#define CP_PHASE_ALL     0xF
+
 /* ------------------------------------------------------------ metadata */
 /*
  * Device metadata built by cp_build_meta in a caller-allocated buffer of
@@ -190,6 +198,7 @@ int cp_meta_status(const void* meta, cp_stream_t stream, int32_t* flags_out,
  *   total_tokens T (must equal the meta's), heads H >= 1, head_dim D >= 1
  *   dtype        CP_F32 / CP_BF16 / CP_F16 (FP8 -> CP_ERR_UNSUPPORTED)
  *   meta         built by cp_build_meta (either policy)
+ * total_tokens == 0 is a no-op after the scalar checks (x, parts may be NULL).
  * Errors: CP_ERR_ARG, CP_ERR_UNSUPPORTED, CP_ERR_DEVICE, CP_ERR_ALIAS
  * (parts overlaps x or meta), CP_ERR_HIP; metadata mismatch is recorded in the
  * meta flags and the kernel writes nothing.
@@ -219,10 +228,11 @@ int cp_gather_thd(const void* parts, void* x, int64_t total_tokens, int32_t head
  *   rank         CP_ALL_RANKS: emulate all W ranks in stream order on `stream`.
  *                0..W-1: the part of rank `rank` only (scatter its own
  *                gradient to every owner, publish its epoch to every owner,
- *                wait for its own W epochs, sum its own slots).  The W ranks'
- *                calls MUST be made on W different streams: on one stream the
- *                first rank's wait precedes the other writers' scatter and
- *                ends in CP_ERR_TIMEOUT.
+ *                wait for its own W epochs, sum its own slots).  With
+ *                CP_PHASE_ALL the W ranks' calls MUST run concurrently, on W
+ *                streams that map to distinct hardware queues: a wait that
+ *                precedes another writer's publish in the same queue ends in
+ *                CP_ERR_TIMEOUT (see `phases` for the split that avoids it).
  *   cp_size      W, must equal the meta's; the meta must be dual-chunk-swap
  *   n_tensors    number of gradient tensors per rank (2 for dK, dV), >= 1
  *   grads        host table [n_tensors][W] of device [T, H, D] `in_dtype`:
@@ -231,10 +241,17 @@ int cp_gather_thd(const void* parts, void* x, int64_t total_tokens, int32_t head
  *                [T/W, H, D] `in_dtype`: the owner's receive slots
  *   out          host table [n_tensors][W owner] of device [T/W, H, D]
  *                `out_dtype`: overwritten with the sum (not accumulated into)
- *   in_dtype/out_dtype  (CP_F32, CP_F32), (CP_BF16, CP_BF16), (CP_BF16, CP_F32)
- *   epochs       device uint32 [W owner][W writer], or NULL in CP_ALL_RANKS
- *                mode (then ordering is stream order alone).  Required when
- *                rank >= 0.  Writers store `epoch` with release semantics;
+ *   in_dtype/out_dtype  (CP_F32, CP_F32), (CP_F32, CP_BF16), (CP_BF16, CP_BF16),
+ *                (CP_BF16, CP_F32)
+ *   phases       CP_PHASE_* mask; phases run in the order scatter, publish,
+ *                wait, sum.  CP_PHASE_ALL is the whole protocol.  A caller that
+ *                drives several emulated ranks from one process may enqueue
+ *                every rank's SCATTER|PUBLISH half before any rank's WAIT|SUM
+ *                half, so that ranks sharing a hardware queue cannot block
+ *                each other.
+ *   epochs       device uint32 [W owner][W writer].  Required when rank >= 0.
+ *                In CP_ALL_RANKS mode it may be NULL: the publish and wait
+ *                phases are then skipped and ordering is stream order alone.  Writers store `epoch` with release semantics;
  *                owners wait until every entry of their row is >= epoch.
  *   epoch        must exceed every value already in `epochs` (the caller owns
  *                the counter; there is no hidden per-buffer epoch state).
@@ -247,6 +264,7 @@ int cp_gather_thd(const void* parts, void* x, int64_t total_tokens, int32_t head
  * In per-rank mode the call reads grads[t][rank], writes slots[t][o][rank] for
  * every o, reads slots[t][rank][*] and writes out[t][rank]; only those table
  * entries must be valid.
+ * total_tokens == 0 is a no-op after the scalar checks (pointers may be NULL).
  * Errors: CP_ERR_ARG, CP_ERR_UNSUPPORTED (dtype pair), CP_ERR_DEVICE,
  * CP_ERR_ALIAS, CP_ERR_HIP; device-side mismatch or timeout as above.
  */
@@ -255,7 +273,7 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors,
                    int64_t total_tokens, int32_t heads, int32_t head_dim,
                    int32_t in_dtype, int32_t out_dtype, const void* meta,
                    uint32_t* epochs, uint32_t epoch, int64_t wait_timeout_us,
-                   cp_stream_t stream);
+                   int32_t phases, cp_stream_t stream);
 
 /*
  * cp_grad_return_fused - the same result as cp_grad_return with no slots:
@@ -281,6 +299,7 @@ int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
  *   slots        host table [W] of device buffers of n_elems `in_dtype`
  *   out          device buffer of n_elems `out_dtype`
  *   dtype pairs  as cp_grad_return
+ * n_elems == 0 is a no-op (pointers may then be NULL).
  */
 int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t n_elems,
                 int32_t in_dtype, int32_t out_dtype, cp_stream_t stream);
@@ -295,7 +314,7 @@ int cp_version(void);
 /*
  * Per-kernel timing with HIP events on the launch stream, for benchmarks.
  * cp_profile_enable(1) starts recording an event pair around every kernel the
- * library launches (capacity 4096 launches; later ones are not recorded);
+ * library launches (capacity 65536 launches; later ones are not recorded);
  * cp_profile_enable(0) stops.  cp_profile_read synchronizes the recorded
  * events, and for up to `capacity` distinct kernels writes its name (NUL-
  * terminated, at most 127 chars) into names[k*128], its launch count into

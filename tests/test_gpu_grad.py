@@ -249,30 +249,21 @@ def test_fused_s128k_w8(cp):
 
 
 # ------------------------------------------------------------------ per-rank protocol mode
-@pytest.mark.parametrize("W", [2, 4])
-def test_per_rank_streams_with_delayed_writer(cp, W):
-    """Each rank on its own stream; one writer is delayed; slots start as NaN.  The
-    owners must wait for every epoch, so the result equals the oracle and holds no NaN."""
-    say(f"case per-rank W={W}")
-    rng = np.random.default_rng(40 + W)
+def per_rank_case(cp, W, seed):
+    rng = np.random.default_rng(seed)
     lengths = (rng.integers(1, 5, size=5) * 2 * W * 16).tolist()
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     T = int(cu[-1])
-    gen = torch.Generator(device=DEV).manual_seed(W)
+    gen = torch.Generator(device=DEV).manual_seed(seed)
     grads = [[torch.randn((T, 4, 64), generator=gen, device=DEV) for _ in range(W)] for _ in range(2)]
     meta = make_meta(cp, cu, T, W)
     slots, out = alloc(grads, W, torch.float32, fill=float("nan"))
     epochs = torch.zeros((W, W), dtype=torch.int32, device=DEV)
     torch.cuda.synchronize()
-    streams = [torch.cuda.Stream() for _ in range(W)]
-    delayed = W - 1
-    for r in range(W):
-        with torch.cuda.stream(streams[r]):
-            if r == delayed:
-                torch.cuda._sleep(50_000_000)  # ~20 ms of device spinning before this writer starts
-            cp.cp_grad_return(grads, slots, out, meta, rank=r, epochs=epochs, epoch=3,
-                              wait_timeout_us=5_000_000, stream=streams[r])
-    torch.cuda.synchronize()
+    return cu, grads, meta, slots, out, epochs
+
+
+def check_per_rank_result(cp, meta, cu, grads, out, epochs, W, epoch):
     st, flags, timeouts = cp.cp_meta_status(meta)
     assert st == cp.CP_OK and timeouts == 0, (st, hex(flags), timeouts)
     ref = oracle_full(grads, cu, W, "f32")
@@ -281,7 +272,48 @@ def test_per_rank_streams_with_delayed_writer(cp, W):
             got = to_np(out[t][o])
             assert not np.isnan(got).any()
             assert bits_equal(got, ref[t][1][o]), (t, o)
-    assert (epochs == 3).all()
+    assert (epochs == epoch).all()
+
+
+def test_per_rank_streams_with_delayed_writer(cp):
+    """W=2 ranks, each the whole protocol on its own stream; writer 1 is delayed and
+    the slots start as NaN.  Owner 0 must wait for writer 1's epoch, so the result
+    equals the oracle and holds no NaN."""
+    W = 2
+    say(f"case per-rank full protocol W={W}")
+    cu, grads, meta, slots, out, epochs = per_rank_case(cp, W, 42)
+    streams = [torch.cuda.Stream() for _ in range(W)]
+    for r in range(W):
+        with torch.cuda.stream(streams[r]):
+            if r == W - 1:
+                torch.cuda._sleep(50_000_000)  # device-side spin before this writer starts
+            cp.cp_grad_return(grads, slots, out, meta, rank=r, epochs=epochs, epoch=3,
+                              wait_timeout_us=5_000_000, stream=streams[r])
+    torch.cuda.synchronize()
+    check_per_rank_result(cp, meta, cu, grads, out, epochs, W, 3)
+
+
+@pytest.mark.parametrize("W", [4, 8])
+def test_per_rank_split_phases_with_delayed_writer(cp, W):
+    """W ranks on W streams, each enqueueing its writer half (scatter, publish) and
+    then its owner half (wait, sum).  Writers' halves are all enqueued before any
+    owner half, so ranks whose streams share a hardware queue cannot block each
+    other; the delayed last writer still forces every other owner to wait."""
+    say(f"case per-rank split phases W={W}")
+    cu, grads, meta, slots, out, epochs = per_rank_case(cp, W, 40 + W)
+    streams = [torch.cuda.Stream() for _ in range(W)]
+    for r in range(W):
+        with torch.cuda.stream(streams[r]):
+            if r == W - 1:
+                torch.cuda._sleep(50_000_000)
+            cp.cp_grad_return(grads, slots, out, meta, rank=r, epochs=epochs, epoch=9,
+                              phases=cp.CP_PHASE_SCATTER | cp.CP_PHASE_PUBLISH, stream=streams[r])
+    for r in range(W):
+        cp.cp_grad_return(grads, slots, out, meta, rank=r, epochs=epochs, epoch=9,
+                          wait_timeout_us=5_000_000, phases=cp.CP_PHASE_WAIT | cp.CP_PHASE_SUM,
+                          stream=streams[r])
+    torch.cuda.synchronize()
+    check_per_rank_result(cp, meta, cu, grads, out, epochs, W, 9)
 
 
 def test_epoch_timeout_is_reported_not_hung(cp):

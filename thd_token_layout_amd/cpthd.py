@@ -30,6 +30,8 @@ CP_POLICY_DUAL_CHUNK_SWAP, CP_POLICY_PACKED_CONTIGUOUS = 0, 1
 CP_F32, CP_BF16, CP_F16, CP_FP8_E4M3, CP_FP8_E5M2 = 0, 1, 2, 3, 4
 CP_ALL_RANKS = -1
 CP_MAX_CP_SIZE = 64
+CP_PHASE_SCATTER, CP_PHASE_PUBLISH, CP_PHASE_WAIT, CP_PHASE_SUM = 0x1, 0x2, 0x4, 0x8
+CP_PHASE_ALL = 0xF
 CP_META_MAGIC = 0x48545043
 CP_META_FIRST_NOT_ZERO = 0x0001
 CP_META_DECREASING = 0x0002
@@ -61,7 +63,7 @@ lib.cp_gather_thd.restype = _c.c_int
 lib.cp_gather_thd.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]
 lib.cp_grad_return.restype = _c.c_int
 lib.cp_grad_return.argtypes = [_i32, _i32, _i32, _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_vp),
-                               _i64, _i32, _i32, _i32, _i32, _vp, _vp, _u32, _i64, _vp]
+                               _i64, _i32, _i32, _i32, _i32, _vp, _vp, _u32, _i64, _i32, _vp]
 lib.cp_grad_return_fused.restype = _c.c_int
 lib.cp_grad_return_fused.argtypes = [_i32, _i32, _i32, _c.POINTER(_vp), _c.POINTER(_vp), _i64, _i32,
                                      _i32, _i32, _i32, _vp, _vp]
@@ -118,6 +120,8 @@ def _stream(stream) -> int:
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     if t is None:
         return None
+    if t.numel() == 0:
+        return t.data_ptr() or None
     if not t.is_contiguous():
         raise ValueError("tensors passed to libcpthd must be contiguous")
     return t.data_ptr()
@@ -228,23 +232,24 @@ def _flat3(tab):
 
 def cp_grad_return(grads: Sequence[Sequence[torch.Tensor]], slots, out, meta: Meta,
                    rank: int = CP_ALL_RANKS, epochs: Optional[torch.Tensor] = None,
-                   epoch: int = 0, wait_timeout_us: int = 0, stream=None) -> None:
+                   epoch: int = 0, wait_timeout_us: int = 0, phases: int = CP_PHASE_ALL,
+                   stream=None) -> None:
     """grads[t][w] [T,H,D]; slots[t][o][w] [T/W,H,D]; out[t][o] [T/W,H,D] (overwritten)."""
     n_tensors = len(grads)
-    W = meta.cp_size
+    W = len(grads[0])
     ref = next(g for g in _flat2(grads) if g is not None)
     T, H, D = ref.shape
     out_ref = next(o for o in _flat2(out) if o is not None)
     st = lib.cp_grad_return(int(rank), W, n_tensors, _table(_flat2(grads)), _table(_flat3(slots)),
                             _table(_flat2(out)), T, H, D, dtype_code(ref.dtype),
                             dtype_code(out_ref.dtype), meta.ptr(), _ptr(epochs), int(epoch),
-                            int(wait_timeout_us), _stream(stream))
+                            int(wait_timeout_us), int(phases), _stream(stream))
     _check(st, "cp_grad_return")
 
 
 def cp_grad_return_fused(grads, out, meta: Meta, rank: int = CP_ALL_RANKS, stream=None) -> None:
     n_tensors = len(grads)
-    W = meta.cp_size
+    W = len(grads[0])
     ref = next(g for g in _flat2(grads) if g is not None)
     T, H, D = ref.shape
     out_ref = next(o for o in _flat2(out) if o is not None)

@@ -74,6 +74,7 @@ bool is_fp8(int32_t dt) { return dt == CP_FP8_E4M3 || dt == CP_FP8_E5M2; }
 int check_sum_dtypes(int32_t in, int32_t out) {
   if (is_fp8(in) || is_fp8(out)) return CP_ERR_UNSUPPORTED;
   if (in == CP_F32 && out == CP_F32) return CP_OK;
+  if (in == CP_F32 && out == CP_BF16) return CP_OK;
   if (in == CP_BF16 && out == CP_BF16) return CP_OK;
   if (in == CP_BF16 && out == CP_F32) return CP_OK;
   if (valid_layout_dtype(in) && valid_layout_dtype(out)) return CP_ERR_UNSUPPORTED;
@@ -93,7 +94,7 @@ std::vector<ProfileRecord> g_prof_records;
 std::vector<hipEvent_t> g_prof_free;
 std::string g_prof_pending_name;
 hipEvent_t g_prof_pending_start = nullptr;
-constexpr size_t kProfCapacity = 4096;
+constexpr size_t kProfCapacity = 1 << 16;
 
 hipEvent_t take_event() {
   if (!g_prof_free.empty()) {
@@ -222,8 +223,9 @@ static int layout_call(const void* in, void* out, int64_t total_tokens, int32_t 
                        bool to_local) {
   if (is_fp8(dtype)) return CP_ERR_UNSUPPORTED;
   if (!valid_layout_dtype(dtype)) return CP_ERR_ARG;
-  if (in == nullptr || out == nullptr || meta == nullptr) return CP_ERR_ARG;
   if (total_tokens < 0 || total_tokens > INT32_MAX || heads < 1 || head_dim < 1) return CP_ERR_ARG;
+  if (total_tokens == 0) return CP_OK;  // nothing to move; empty tensors may have NULL data
+  if (in == nullptr || out == nullptr || meta == nullptr) return CP_ERR_ARG;
   const int64_t row_bytes = (int64_t)heads * head_dim * dtype_bytes(dtype);
   const int64_t bytes = total_tokens * row_bytes;
   int dev, st;
@@ -234,7 +236,6 @@ static int layout_call(const void* in, void* out, int64_t total_tokens, int32_t 
   if ((st = check_alias({range_of(out, bytes)},
                         {range_of(in, bytes), range_of(meta, sizeof(cp_meta_header))})) != CP_OK)
     return st;
-  if (total_tokens == 0) return CP_OK;
   PermuteArgs a;
   memset(&a, 0, sizeof(a));
   a.meta = const_cast<cp_meta_header*>(static_cast<const cp_meta_header*>(meta));
@@ -270,7 +271,7 @@ static int grad_scalar_checks(int32_t rank, int32_t cp_size, int32_t n_tensors, 
   if (n_tensors < 1) return CP_ERR_ARG;
   if (total_tokens < 0 || total_tokens > INT32_MAX || heads < 1 || head_dim < 1) return CP_ERR_ARG;
   if (total_tokens % (2 * (int64_t)cp_size) != 0) return CP_ERR_SHAPE;
-  if (meta == nullptr) return CP_ERR_ARG;
+  if (total_tokens > 0 && meta == nullptr) return CP_ERR_ARG;
   return CP_OK;
 }
 
@@ -278,14 +279,16 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
                    void* const* slots, void* const* out, int64_t total_tokens, int32_t heads,
                    int32_t head_dim, int32_t in_dtype, int32_t out_dtype, const void* meta,
                    uint32_t* epochs, uint32_t epoch, int64_t wait_timeout_us,
-                   cp_stream_t stream) {
+                   int32_t phases, cp_stream_t stream) {
   int st;
   if ((st = grad_scalar_checks(rank, cp_size, n_tensors, total_tokens, heads, head_dim, in_dtype,
                                out_dtype, meta)) != CP_OK)
     return st;
-  if (grads == nullptr || slots == nullptr || out == nullptr) return CP_ERR_ARG;
+  if (phases <= 0 || (phases & ~CP_PHASE_ALL) != 0) return CP_ERR_ARG;
   const bool all = rank == CP_ALL_RANKS;
   if (!all && epochs == nullptr) return CP_ERR_ARG;
+  if (total_tokens == 0) return CP_OK;  // nothing to move; empty tensors may have NULL data
+  if (grads == nullptr || slots == nullptr || out == nullptr) return CP_ERR_ARG;
   const int W = cp_size;
   const int64_t n = total_tokens / W;
   const int64_t row_elems = (int64_t)heads * head_dim;
@@ -339,12 +342,11 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
     outs.push_back(range_of(epochs, 4 * (int64_t)W * W));
   }
   if ((st = check_alias(outs, ins)) != CP_OK) return st;
-  if (total_tokens == 0) return CP_OK;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   cp_meta_header* h = const_cast<cp_meta_header*>(static_cast<const cp_meta_header*>(meta));
   // 1. scatter: writer w's global gradient -> slot [o][w] of every owner o
-  for (int t = 0; t < n_tensors; ++t) {
+  for (int t = 0; t < n_tensors && (phases & CP_PHASE_SCATTER); ++t) {
     for (int w = w_lo; w < w_hi; ++w) {
       PermuteArgs a;
       memset(&a, 0, sizeof(a));
@@ -361,7 +363,7 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
     }
   }
   // 2-3. publish this call's writer epochs, wait for this call's owners
-  if (epochs) {
+  if (epochs && (phases & (CP_PHASE_PUBLISH | CP_PHASE_WAIT))) {
     int rate_khz = 0;
     if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
         rate_khz <= 0) {
@@ -370,13 +372,15 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
     }
     const int64_t us = wait_timeout_us > 0 ? wait_timeout_us : 2000000;
     const int64_t ticks = us * (int64_t)rate_khz / 1000;
-    if ((st = hip_status(launch_epoch_publish(epochs, W, all ? -1 : rank, epoch, s))) != CP_OK)
+    if ((phases & CP_PHASE_PUBLISH) &&
+        (st = hip_status(launch_epoch_publish(epochs, W, all ? -1 : rank, epoch, s))) != CP_OK)
       return st;
-    if ((st = hip_status(launch_epoch_wait(epochs, W, all ? -1 : rank, epoch, ticks, h, s))) != CP_OK)
+    if ((phases & CP_PHASE_WAIT) &&
+        (st = hip_status(launch_epoch_wait(epochs, W, all ? -1 : rank, epoch, ticks, h, s))) != CP_OK)
       return st;
   }
   // 4. owner o: out = slot 0 + slot 1 + ... + slot W-1
-  for (int t = 0; t < n_tensors; ++t) {
+  for (int t = 0; t < n_tensors && (phases & CP_PHASE_SUM); ++t) {
     for (int o = o_lo; o < o_hi; ++o) {
       SlotSumArgs a;
       memset(&a, 0, sizeof(a));
@@ -403,6 +407,7 @@ int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
   if ((st = grad_scalar_checks(rank, cp_size, n_tensors, total_tokens, heads, head_dim, in_dtype,
                                out_dtype, meta)) != CP_OK)
     return st;
+  if (total_tokens == 0) return CP_OK;  // nothing to move; empty tensors may have NULL data
   if (grads == nullptr || out == nullptr) return CP_ERR_ARG;
   const int W = cp_size;
   const bool all = rank == CP_ALL_RANKS;
@@ -435,7 +440,6 @@ int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
     }
   }
   if ((st = check_alias(outs, ins)) != CP_OK) return st;
-  if (total_tokens == 0) return CP_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   for (int t = 0; t < n_tensors; ++t) {
     FusedArgs a;
@@ -460,6 +464,7 @@ int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t 
   int st;
   if ((st = check_sum_dtypes(in_dtype, out_dtype)) != CP_OK) return st;
   if (num_slots < 1 || num_slots > CP_MAX_CP_SIZE || n_elems < 0) return CP_ERR_ARG;
+  if (n_elems == 0) return CP_OK;
   if (slots == nullptr || out == nullptr) return CP_ERR_ARG;
   for (int w = 0; w < num_slots; ++w)
     if (slots[w] == nullptr) return CP_ERR_ARG;

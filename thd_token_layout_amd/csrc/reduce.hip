@@ -328,6 +328,10 @@ SumTable<CP_F32, CP_F32> g_sum_ff = {{CP_SUM_ROW(CP_F32, CP_F32, false, ""),
                                       CP_SUM_ROW(CP_F32, CP_F32, true, "")},
                                      {{0}},
                                      {CP_SUM_NAMES("f32,f32", "s"), CP_SUM_NAMES("f32,f32", "v")}};
+SumTable<CP_F32, CP_BF16> g_sum_fb = {{CP_SUM_ROW(CP_F32, CP_BF16, false, ""),
+                                       CP_SUM_ROW(CP_F32, CP_BF16, true, "")},
+                                      {{0}},
+                                      {CP_SUM_NAMES("f32,bf16", "s"), CP_SUM_NAMES("f32,bf16", "v")}};
 SumTable<CP_BF16, CP_BF16> g_sum_bb = {{CP_SUM_ROW(CP_BF16, CP_BF16, false, ""),
                                         CP_SUM_ROW(CP_BF16, CP_BF16, true, "")},
                                        {{0}},
@@ -355,6 +359,10 @@ FusedTable<CP_F32, CP_F32> g_fused_ff = {{CP_FUSED_ROW(CP_F32, CP_F32, false),
                                           CP_FUSED_ROW(CP_F32, CP_F32, true)},
                                          {{0}},
                                          {CP_FUSED_NAMES("f32,f32", "s"), CP_FUSED_NAMES("f32,f32", "v")}};
+FusedTable<CP_F32, CP_BF16> g_fused_fb = {{CP_FUSED_ROW(CP_F32, CP_BF16, false),
+                                          CP_FUSED_ROW(CP_F32, CP_BF16, true)},
+                                         {{0}},
+                                         {CP_FUSED_NAMES("f32,bf16", "s"), CP_FUSED_NAMES("f32,bf16", "v")}};
 FusedTable<CP_BF16, CP_BF16> g_fused_bb = {{CP_FUSED_ROW(CP_BF16, CP_BF16, false),
                                             CP_FUSED_ROW(CP_BF16, CP_BF16, true)},
                                            {{0}},
@@ -410,6 +418,7 @@ hipError_t launch_slot_sum(const SlotSumArgs& a, hipStream_t stream) {
   bool vec = aligned16(a.out);
   for (int w = 0; w < a.num_slots; ++w) vec = vec && aligned16(a.in.p[w]);
   if (a.in_dtype == CP_F32 && a.out_dtype == CP_F32) return run_sum(g_sum_ff, a, vec, a.num_slots, a.n_elems, stream);
+  if (a.in_dtype == CP_F32 && a.out_dtype == CP_BF16) return run_sum(g_sum_fb, a, vec, a.num_slots, a.n_elems, stream);
   if (a.in_dtype == CP_BF16 && a.out_dtype == CP_BF16) return run_sum(g_sum_bb, a, vec, a.num_slots, a.n_elems, stream);
   if (a.in_dtype == CP_BF16 && a.out_dtype == CP_F32) return run_sum(g_sum_bf, a, vec, a.num_slots, a.n_elems, stream);
   return hipErrorInvalidValue;
@@ -423,6 +432,7 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
   for (int w = 0; w < a.cp_size; ++w) vec = vec && aligned16(a.grads.p[w]);
   for (int o = a.owner_begin; o < a.owner_end; ++o) vec = vec && aligned16(a.out.p[o]);
   if (a.in_dtype == CP_F32 && a.out_dtype == CP_F32) return run_fused(g_fused_ff, a, vec, stream);
+  if (a.in_dtype == CP_F32 && a.out_dtype == CP_BF16) return run_fused(g_fused_fb, a, vec, stream);
   if (a.in_dtype == CP_BF16 && a.out_dtype == CP_BF16) return run_fused(g_fused_bb, a, vec, stream);
   if (a.in_dtype == CP_BF16 && a.out_dtype == CP_F32) return run_fused(g_fused_bf, a, vec, stream);
   return hipErrorInvalidValue;
