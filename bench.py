@@ -159,8 +159,8 @@ def attribute_kernels(step: Step, cp, torch):
         {k: sum(c for c, _ in v) for k, v in per_kernel.items()}
 
 
-def cpu_baseline(S_sample: int, WL):
-    """The CPU oracle, as it stands, on the same step at S_sample tokens."""
+def cpu_baseline(S_sample: int, WL, passes: int = 2):
+    """The CPU oracle, as it stands, on the same step at S_sample tokens, `passes` times."""
     import numpy as np
     import torch
 
@@ -180,26 +180,28 @@ def cpu_baseline(S_sample: int, WL):
     row_f32 = w_gr.heads * w_gr.head_dim * 4
     nbytes = 0
     t0 = time.perf_counter()
-    for cu, pol, W in ((cu_dcs, O.DUAL_CHUNK_SWAP, w_dcs.cp_size), (cu_pc, O.PACKED_CONTIGUOUS, w_pc.cp_size)):
-        O.local_cu_seqlens(cu, S_sample, W, pol)
-        for x in qkv:
-            parts = O.partition(x, cu, W, pol)
-            O.gather(parts, cu, W, pol)
-            nbytes += 2 * 2 * S_sample * row_bf16
-    for gt in grads:
-        O.grad_return(gt, cu_gr, Wg, "f32", "f32")
-        nbytes += (3 * Wg + 1) * S_sample * row_f32
-        O.grad_return_fused(gt, cu_gr, Wg, "f32", "f32")
-        nbytes += (Wg + 1) * S_sample * row_f32
-    for nb, s in zip(sweep_sizes, sweep):
-        O.slot_sum(s, "f32", "f32")
-        nbytes += 9 * nb
+    for _ in range(passes):
+        for cu, pol, W in ((cu_dcs, O.DUAL_CHUNK_SWAP, w_dcs.cp_size),
+                           (cu_pc, O.PACKED_CONTIGUOUS, w_pc.cp_size)):
+            O.local_cu_seqlens(cu, S_sample, W, pol)
+            for x in qkv:
+                parts = O.partition(x, cu, W, pol)
+                O.gather(parts, cu, W, pol)
+                nbytes += 2 * 2 * S_sample * row_bf16
+        for gt in grads:
+            O.grad_return(gt, cu_gr, Wg, "f32", "f32")
+            nbytes += (3 * Wg + 1) * S_sample * row_f32
+            O.grad_return_fused(gt, cu_gr, Wg, "f32", "f32")
+            nbytes += (Wg + 1) * S_sample * row_f32
+        for nb, s in zip(sweep_sizes, sweep):
+            O.slot_sum(s, "f32", "f32")
+            nbytes += 9 * nb
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the full step (metadata, DCS and PC partition+gather of Q,K,V, unfused and "
-                      f"fused dK/dV gradient return, W=8 sweep) at S={S_sample} instead of 262144, "
-                      f"same heads, head_dim, cp_size, dtypes and distributions; numpy, one thread; "
-                      f"{nbytes / 1e9:.2f} GB algorithmic in {dt:.1f} s"}
+            "sample": f"{passes} passes of the full step (metadata, DCS and PC partition+gather of "
+                      f"Q,K,V, unfused and fused dK/dV gradient return, W=8 sweep) at S={S_sample} "
+                      f"instead of 262144, same heads, head_dim, cp_size, dtypes and distributions; "
+                      f"numpy, one thread; {nbytes / 1e9:.2f} GB algorithmic in {dt:.1f} s"}
 
 
 def sweep_latency(step: Step, cp, torch, reps: int = 200):
@@ -234,9 +236,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tokens", type=int, default=262144, help="S (default 262144)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep-latency", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="run one plain 1 GiB device copy (torch copy_) first, as the reference "
+                         "dispatch for scaling hardware traffic counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the W context-parallel ranks are emulated as slot "
@@ -251,6 +256,14 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.calibration_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 1 GiB read + 1 GiB written")
+        del a, b
     log(f"[bench] building inputs S={args.tokens}")
     step = Step(cp, WL, torch, args.tokens, dev)
     torch.cuda.synchronize()

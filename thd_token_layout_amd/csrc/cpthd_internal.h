@@ -12,6 +12,9 @@ namespace cpthd {
 constexpr int kMaxRanks = CP_MAX_CP_SIZE;
 constexpr int kBlock = 256;           // threads per workgroup: 4 wave64s
 constexpr int kWavesPerBlock = kBlock / 64;
+// Largest grid launched; kernels loop (grid-stride) over work beyond it.  Keeps
+// blocks * kBlock well inside the 32-bit grid size.
+constexpr int64_t kMaxGrid = int64_t(1) << 22;
 
 // Byte offsets inside the metadata buffer (layout documented in cpthd.h).
 __host__ __device__ inline int64_t meta_cu_offset() { return 64; }

@@ -12,17 +12,19 @@
 //     cu[b] + r c_b + j                   if j <  c_b
 //     cu[b] + (2W-1-r) c_b + (j - c_b)    if j >= c_b.
 //
-// Design (gfx950): pure data movement, HBM-bound.  Each wave64 owns groups of
-// G consecutive local rows (grid-stride over groups, grid sized to the
-// resident capacity so every wave does the same amount of work).  The row map
-// is computed once per group in wave-uniform (scalar) code: a binary search
-// over the per-rank document table, then an incremental cursor for the rest of
-// the group.  Each lane then moves 16-byte units of the G rows (VPL units per
-// row, up to G*VPL loads in flight per lane) with non-temporal loads and
-// stores, fully coalesced (a wave touches 1 KiB contiguous per instruction).
+// Design (gfx950): pure data movement, HBM-bound.  A workgroup (4 waves) owns
+// a tile of consecutive local rows (8-20 KiB); the launch covers every tile
+// (a full grid, not a persistent one:
+// measured on MI355X, concurrently running workgroups then stream one
+// contiguous window of HBM and a copy reaches ~5.8 TB/s, against ~4.7 TB/s for
+// a resident-capacity grid-stride loop).  The row map is computed once per
+// group in wave-uniform (scalar) code: a binary search over the per-rank
+// document table, then an incremental cursor for the rest of the group.  Each
+// lane then moves 16-byte units of the G rows (VPL units per row, up to G*VPL
+// loads in flight per lane) with non-temporal loads and stores, fully
+// coalesced (a wave touches 1 KiB contiguous per instruction).
 #include "cpthd_internal.h"
 
-#include <mutex>
 
 namespace cpthd {
 namespace {
@@ -107,8 +109,14 @@ __device__ __forceinline__ bool meta_ok(cp_meta_header* h, int64_t T, int32_t ex
   return code == 0;
 }
 
-template <typename U, int VPL, int G>
+// One workgroup = 4 waves = a tile of (4 / WPR) * G consecutive local rows.
+// Waves are grouped WPR to a row: wave w takes rows [p_tile + (w / WPR) G, +G)
+// and, inside each row, the column chunks c = w % WPR, c + WPR, ... of 64*VPL
+// units each, so every lane has up to G*VPL loads in flight.
+template <typename U, int VPL, int G, int WPR>
 __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
+  static_assert(kWavesPerBlock % WPR == 0, "WPR must divide the waves of a workgroup");
+  constexpr int kRowsPerTile = (kWavesPerBlock / WPR) * G;
   cp_meta_header* h = a.meta;
   if (!meta_ok(h, a.total_tokens, a.expect_cp_size, a.expect_policy)) return;
 
@@ -122,12 +130,14 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
   const int64_t upr = a.row_bytes / (int64_t)sizeof(U);  // units per row
 
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-  const int64_t ngroups = (T + G - 1) / G;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int row_slot = wave / WPR;
+  const int chunk = wave % WPR;
+  const int64_t ntiles = (T + kRowsPerTile - 1) / kRowsPerTile;
 
-  for (int64_t grp = wave; grp < ngroups; grp += nwaves) {
-    const int64_t p0 = grp * G;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t p0 = tile * kRowsPerTile + (int64_t)row_slot * G;
+    if (p0 >= T) continue;
     Cursor k;
     seek(k, p0, n, B, dcs, cu, lcu);
     const U* src[G];
@@ -147,7 +157,7 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
         if (g + 1 < G && p0 + g + 1 < T) advance(k, n, dcs, cu, lcu);
       }
     }
-    for (int64_t cb = 0; cb < upr; cb += 64 * VPL) {
+    for (int64_t cb = (int64_t)chunk * 64 * VPL; cb < upr; cb += (int64_t)WPR * 64 * VPL) {
       U buf[G][VPL];
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -171,26 +181,27 @@ typedef void (*PermuteKernel)(PermuteArgs);
 
 struct Variant {
   PermuteKernel fn;
-  int group;
+  int rows_per_tile;
   const char* name;
-  int max_blocks_per_cu;  // cached occupancy, 0 = unknown
 };
 
-template <typename U, int VPL>
-constexpr int group_for() {
-  return VPL <= 1 ? 8 : VPL <= 2 ? 4 : VPL <= 5 ? 2 : 1;
-}
+#define CP_VARIANT(U, UNAME, VPL, G, WPR)                                                  \
+  Variant{permute_rows_kernel<U, VPL, G, WPR>, (kWavesPerBlock / WPR) * G,                 \
+          "permute_rows<" UNAME "," #VPL "x" #G "/" #WPR ">"}
 
-#define CP_VARIANT(U, VPL, UNAME)                                                         \
-  Variant{permute_rows_kernel<U, VPL, group_for<U, VPL>()>, group_for<U, VPL>(),          \
-          "permute_rows<" UNAME "," #VPL ">", 0}
-
-#define CP_VARIANTS_FOR(U, UNAME)                                                        \
-  { CP_VARIANT(U, 1, UNAME), CP_VARIANT(U, 2, UNAME), CP_VARIANT(U, 4, UNAME),            \
-    CP_VARIANT(U, 5, UNAME), CP_VARIANT(U, 8, UNAME), CP_VARIANT(U, 10, UNAME),           \
-    CP_VARIANT(U, 16, UNAME) }
-
-constexpr int kVpl[7] = {1, 2, 4, 5, 8, 10, 16};
+// Shapes by units per row (upr), from a sweep of tile shapes on MI355X
+// (partition, gather and scatter of 2, 5, 8 and 10 KiB rows): a workgroup
+// tile of 8-20 KiB with 4-8 loads in flight per lane streamed best; longer
+// tiles or more loads per lane lost 5-10%.
+#define CP_VARIANTS_FOR(U, UNAME)                                                           \
+  {CP_VARIANT(U, UNAME, 1, 4, 1),  /* upr <=   64: 4 rows per wave            */           \
+   CP_VARIANT(U, UNAME, 2, 4, 1),  /* upr <=  128: 4 rows per wave            */           \
+   CP_VARIANT(U, UNAME, 4, 1, 1),  /* upr <=  256: 1 row per wave             */           \
+   CP_VARIANT(U, UNAME, 5, 1, 1),  /* upr <=  320: 1 row per wave, 5 loads    */           \
+   CP_VARIANT(U, UNAME, 4, 1, 2),  /* upr <=  512: 2 waves per row            */           \
+   CP_VARIANT(U, UNAME, 4, 1, 2),  /* upr <=  640: 2 waves per row, 2 passes  */           \
+   CP_VARIANT(U, UNAME, 4, 1, 4)}  /* longer rows: 1 row per tile, 16 KiB passes */
+constexpr int64_t kUprLimit[7] = {64, 128, 256, 320, 512, 640, INT64_MAX};
 
 Variant g_variants[4][7] = {
     CP_VARIANTS_FOR(u32x4, "16B"),
@@ -198,7 +209,6 @@ Variant g_variants[4][7] = {
     CP_VARIANTS_FOR(unsigned int, "4B"),
     CP_VARIANTS_FOR(unsigned short, "2B"),
 };
-std::mutex g_occ_mutex;
 
 }  // namespace
 
@@ -216,24 +226,12 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   else if ((align_bits & 1) == 0) { ui = 3; usize = 2; }
   else return hipErrorInvalidValue;  // rows of 2- or 4-byte elements are always even
   const int64_t upr = a.row_bytes / usize;
-  const int64_t need = (upr + 63) / 64;
   int vi = 6;
   for (int k = 0; k < 7; ++k)
-    if (kVpl[k] >= need) { vi = k; break; }
-  Variant& v = g_variants[ui][vi];
-  {
-    std::lock_guard<std::mutex> lock(g_occ_mutex);
-    if (v.max_blocks_per_cu == 0) {
-      int nb = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, v.fn, kBlock, 0) != hipSuccess || nb < 1)
-        nb = 1;
-      v.max_blocks_per_cu = nb;
-    }
-  }
-  const int64_t groups = (a.total_tokens + v.group - 1) / v.group;
-  const int64_t want = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int64_t cap = (int64_t)device_cu_count() * v.max_blocks_per_cu;
-  const int blocks = (int)(want < cap ? want : cap);
+    if (upr <= kUprLimit[k]) { vi = k; break; }
+  const Variant& v = g_variants[ui][vi];
+  const int64_t tiles = (a.total_tokens + v.rows_per_tile - 1) / v.rows_per_tile;
+  const int blocks = (int)(tiles < kMaxGrid ? tiles : kMaxGrid);  // grid-stride beyond kMaxGrid
   profile_before(v.name, stream);
   hipLaunchKernelGGL(v.fn, dim3(blocks), dim3(kBlock), 0, stream, a);
   hipError_t e = hipGetLastError();

@@ -16,9 +16,13 @@
 // Design: HBM-bound streaming.  A thread handles units of 8 elements (16 B of
 // bf16, 32 B of fp32 per slot), issues the loads of a batch of WB slots before
 // adding them in order, and writes 16-byte vectors with non-temporal stores.
+// Launches cover all work with one small contiguous tile per workgroup (a full
+// grid rather than a resident-capacity persistent loop, which streams HBM less
+// contiguously and measured slower on MI355X).
 #include "cpthd_internal.h"
 
-#include <mutex>
+#include <string>
+
 
 namespace cpthd {
 namespace {
@@ -97,37 +101,48 @@ __device__ __forceinline__ void store_elem(char* base, int64_t k, float f) {
   else reinterpret_cast<unsigned short*>(base)[k] = (unsigned short)f32_to_bf16_bits(f);
 }
 
-// Sum one 8-element unit over slots 0..W-1 in order: batches of WB loads in
-// flight, then the adds of that batch in slot order.  `in` is the kernel
-// argument table (uniform), `off` a byte offset applied to every slot.
-template <int IN, int WB>
-__device__ __forceinline__ void sum_unit(F8& acc, const ConstRankPtrs& in, int W, int64_t off,
-                                         int64_t unit) {
+// Sum UPT 8-element units over slots 0..W-1 in order.  The loads of a batch
+// of WB slots (for all UPT units) are issued before that batch's adds, which
+// then run in slot order.  `in` is the kernel argument table (uniform), off[u]
+// a byte offset applied to every slot for unit u, ok[u] masks units past the end.
+template <int IN, int WB, int UPT>
+__device__ __forceinline__ void sum_units(F8 (&acc)[UPT], const ConstRankPtrs& in, int W,
+                                          const int64_t (&off)[UPT], const int64_t (&unit)[UPT],
+                                          const bool (&ok)[UPT]) {
   {
-    F8 x[WB];
+    F8 x[UPT][WB];
 #pragma unroll
-    for (int w = 0; w < WB; ++w)
-      if (w < W) load_unit<IN>(x[w], in.p[w] + off, unit);
+    for (int u = 0; u < UPT; ++u)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc.v[e] = x[0].v[e];
+      for (int w = 0; w < WB; ++w)
+        if (ok[u] && w < W) load_unit<IN>(x[u][w], in.p[w] + off[u], unit[u]);
 #pragma unroll
-    for (int w = 1; w < WB; ++w)
-      if (w < W) {
+    for (int u = 0; u < UPT; ++u) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc.v[e] = acc.v[e] + x[w].v[e];
-      }
+      for (int e = 0; e < 8; ++e) acc[u].v[e] = x[u][0].v[e];
+#pragma unroll
+      for (int w = 1; w < WB; ++w)
+        if (w < W) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[u].v[e] = acc[u].v[e] + x[u][w].v[e];
+        }
+    }
   }
   for (int w0 = WB; w0 < W; w0 += WB) {
-    F8 x[WB];
+    F8 x[UPT][WB];
 #pragma unroll
-    for (int w = 0; w < WB; ++w)
-      if (w0 + w < W) load_unit<IN>(x[w], in.p[w0 + w] + off, unit);
+    for (int u = 0; u < UPT; ++u)
 #pragma unroll
-    for (int w = 0; w < WB; ++w)
-      if (w0 + w < W) {
+      for (int w = 0; w < WB; ++w)
+        if (ok[u] && w0 + w < W) load_unit<IN>(x[u][w], in.p[w0 + w] + off[u], unit[u]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc.v[e] = acc.v[e] + x[w].v[e];
-      }
+    for (int u = 0; u < UPT; ++u)
+#pragma unroll
+      for (int w = 0; w < WB; ++w)
+        if (w0 + w < W) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[u].v[e] = acc[u].v[e] + x[u][w].v[e];
+        }
   }
 }
 
@@ -143,7 +158,9 @@ __device__ __forceinline__ bool grad_meta_ok(cp_meta_header* h, int64_t T, int32
 }
 
 // ---- slot sum ----------------------------------------------------------------
-template <int IN, int OUT, int WB, bool VEC>
+// A workgroup owns a tile of kBlock*UPT consecutive 8-element units; thread t
+// takes units t, t + kBlock, ... of the tile (coalesced per load instruction).
+template <int IN, int OUT, int WB, bool VEC, int UPT>
 __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
   if (a.gate_meta != nullptr) {
     cp_meta_header* h = a.gate_meta;
@@ -151,18 +168,29 @@ __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
     if (a.owner >= 0 && ((h->wait_timeout_ranks >> a.owner) & 1ull)) return;
   }
   const int W = a.num_slots;
-  const int64_t gtid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  const int64_t gstride = (int64_t)gridDim.x * kBlock;
   int64_t done = 0;
   if constexpr (VEC) {
     const int64_t nunits = a.n_elems / 8;
-    for (int64_t u = gtid; u < nunits; u += gstride) {
-      F8 acc;
-      sum_unit<IN, WB>(acc, a.in, W, 0, u);
-      store_unit<OUT>(a.out, u, acc);
+    const int64_t ntiles = (nunits + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+      int64_t unit[UPT], off[UPT];
+      bool ok[UPT];
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        unit[u] = tile * kBlock * UPT + (int64_t)u * kBlock + threadIdx.x;
+        ok[u] = unit[u] < nunits;
+        off[u] = 0;
+      }
+      F8 acc[UPT];
+      sum_units<IN, WB, UPT>(acc, a.in, W, off, unit, ok);
+#pragma unroll
+      for (int u = 0; u < UPT; ++u)
+        if (ok[u]) store_unit<OUT>(a.out, unit[u], acc[u]);
     }
     done = nunits * 8;
   }
+  const int64_t gtid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int64_t gstride = (int64_t)gridDim.x * kBlock;
   for (int64_t k = done + gtid; k < a.n_elems; k += gstride) {
     float acc = load_elem<IN>(a.in.p[0], k);
     for (int w = 1; w < W; ++w) acc = acc + load_elem<IN>(a.in.p[w], k);
@@ -202,8 +230,12 @@ __device__ __forceinline__ int64_t owner_row_to_global(int32_t o, int64_t i, int
                  : k.gstart + (int64_t)(2 * W - 1 - o) * k.c + (j - k.c);
 }
 
-template <int IN, int OUT, int WB, bool VEC>
+// A workgroup owns (4 / WPR) output rows; WPR waves share a row, each taking
+// column passes of 64*UPL units (8 elements each) so a lane has UPL*W loads in
+// flight per pass.
+template <int IN, int OUT, int WB, bool VEC, int WPR, int UPL>
 __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
+  constexpr int kRowsPerTile = kWavesPerBlock / WPR;
   cp_meta_header* h = a.meta;
   if (!grad_meta_ok(h, a.total_tokens, a.cp_size)) return;
   const int32_t W = a.cp_size;
@@ -215,11 +247,15 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
   const int out_bytes = OUT == CP_F32 ? 4 : 2;
 
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int row_slot = wave / WPR;
+  const int chunk = wave % WPR;
   const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * n;
+  const int64_t ntiles = (rows + kRowsPerTile - 1) / kRowsPerTile;
 
-  for (int64_t q = wave; q < rows; q += nwaves) {
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t q = tile * kRowsPerTile + row_slot;
+    if (q >= rows) continue;
     const int32_t o = a.owner_begin + (int32_t)(q / n);
     const int64_t i = q - (int64_t)(o - a.owner_begin) * n;
     const int64_t g = owner_row_to_global(o, i, W, B, cu, lcu);
@@ -227,18 +263,89 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
     char* row_dst = a.out.p[o] + i * a.row_elems * out_bytes;
     if constexpr (VEC) {
       const int64_t units = a.row_elems / 8;
-      for (int64_t u = lane; u < units; u += 64) {
-        F8 acc;
-        sum_unit<IN, WB>(acc, a.grads, W, src_off, u);
-        store_unit<OUT>(row_dst, u, acc);
+      for (int64_t cb = (int64_t)chunk * 64 * UPL; cb < units; cb += (int64_t)WPR * 64 * UPL) {
+        int64_t unit[UPL], off[UPL];
+        bool ok[UPL];
+#pragma unroll
+        for (int m = 0; m < UPL; ++m) {
+          unit[m] = cb + lane + 64 * m;
+          ok[m] = unit[m] < units;
+          off[m] = src_off;
+        }
+        F8 acc[UPL];
+        sum_units<IN, WB, UPL>(acc, a.grads, W, off, unit, ok);
+#pragma unroll
+        for (int m = 0; m < UPL; ++m)
+          if (ok[m]) store_unit<OUT>(row_dst, unit[m], acc[m]);
       }
-    } else {
+    } else if (chunk == 0) {
       for (int64_t k = lane; k < a.row_elems; k += 64) {
         float acc = load_elem<IN>(a.grads.p[0] + src_off, k);
         for (int w = 1; w < W; ++w) acc = acc + load_elem<IN>(a.grads.p[w] + src_off, k);
         store_elem<OUT>(row_dst, k, acc);
       }
     }
+  }
+}
+
+// Flat-tile variant: a workgroup owns `rows_per_tile` consecutive output rows
+// (at most kMaxTileRows).  The first rows_per_tile threads look up their row's
+// source offset and destination and share them through LDS; the workgroup then
+// walks the tile's rows*units 8-element units as one flat range, NP units per
+// thread and pass, so every pass keeps all four waves busy whatever the row
+// length.  row = unit / units_per_row uses a multiply-high by `upr_magic` =
+// ceil(2^32 / units_per_row), exact for unit * units_per_row < 2^32.
+constexpr int kMaxTileRows = 16;
+
+template <int IN, int OUT, int WB, int NP>
+__global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, int rows_per_tile,
+                                                            uint32_t upr_magic) {
+  __shared__ int64_t s_src[kMaxTileRows];
+  __shared__ char* s_dst[kMaxTileRows];
+  cp_meta_header* h = a.meta;
+  if (!grad_meta_ok(h, a.total_tokens, a.cp_size)) return;
+  const int32_t W = a.cp_size;
+  const int32_t B = h->num_docs;
+  const int64_t n = h->local_tokens;
+  const int32_t* cu = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(h) + 64);
+  const int32_t* lcu = cu + (B + 1);
+  const int in_bytes = IN == CP_F32 ? 4 : 2;
+  const int out_bytes = OUT == CP_F32 ? 4 : 2;
+  const int64_t upr = a.row_elems / 8;
+  const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * n;
+  const int64_t ntiles = (rows + rows_per_tile - 1) / rows_per_tile;
+
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t q0 = tile * rows_per_tile;
+    const int nrows = (int)(rows - q0 < rows_per_tile ? rows - q0 : rows_per_tile);
+    if ((int)threadIdx.x < nrows) {
+      const int64_t q = q0 + threadIdx.x;
+      const int32_t o = a.owner_begin + (int32_t)(q / n);
+      const int64_t i = q - (int64_t)(o - a.owner_begin) * n;
+      s_src[threadIdx.x] = owner_row_to_global(o, i, W, B, cu, lcu) * a.row_elems * in_bytes;
+      s_dst[threadIdx.x] = a.out.p[o] + i * a.row_elems * out_bytes;
+    }
+    __syncthreads();
+    const int64_t total = (int64_t)nrows * upr;
+    for (int64_t p0 = 0; p0 < total; p0 += (int64_t)kBlock * NP) {
+      int64_t unit[NP], off[NP];
+      int row[NP];
+      bool ok[NP];
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        const uint32_t f = (uint32_t)(p0 + (int64_t)m * kBlock + threadIdx.x);
+        ok[m] = (int64_t)f < total;
+        row[m] = ok[m] ? (int)__umulhi(f, upr_magic) : 0;
+        unit[m] = (int64_t)f - (int64_t)row[m] * upr;
+        off[m] = s_src[row[m]];
+      }
+      F8 acc[NP];
+      sum_units<IN, WB, NP>(acc, a.grads, W, off, unit, ok);
+#pragma unroll
+      for (int m = 0; m < NP; ++m)
+        if (ok[m]) store_unit<OUT>(s_dst[row[m]], unit[m], acc[m]);
+    }
+    __syncthreads();  // s_src / s_dst are rewritten by the next tile
   }
 }
 
@@ -295,120 +402,108 @@ epoch_wait_kernel(const uint32_t* epochs, int32_t W, int32_t owner, uint32_t epo
 }
 
 // ---- dispatch -------------------------------------------------------------------
-template <typename K>
-int occupancy(K fn, int* cache, std::mutex& m) {
-  std::lock_guard<std::mutex> lock(m);
-  if (*cache == 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kBlock, 0) != hipSuccess || nb < 1) nb = 1;
-    *cache = nb;
-  }
-  return *cache;
-}
-
-std::mutex g_mutex;
-
-
-template <int IN, int OUT>
-struct SumTable {
-  void (*fn[2][4])(SlotSumArgs);
-  int occ[2][4];
-  const char* name[2][4];
-};
-
-#define CP_SUM_ROW(IN, OUT, VEC, TAG)                                                        \
-  {slot_sum_kernel<IN, OUT, 1, VEC>, slot_sum_kernel<IN, OUT, 2, VEC>,                      \
-   slot_sum_kernel<IN, OUT, 4, VEC>, slot_sum_kernel<IN, OUT, 8, VEC>}
-
-#define CP_SUM_NAMES(TAG, VEC)                                                               \
-  {"slot_sum<" TAG ",1," VEC ">", "slot_sum<" TAG ",2," VEC ">", "slot_sum<" TAG ",4," VEC ">", \
-   "slot_sum<" TAG ",8," VEC ">"}
-
-SumTable<CP_F32, CP_F32> g_sum_ff = {{CP_SUM_ROW(CP_F32, CP_F32, false, ""),
-                                      CP_SUM_ROW(CP_F32, CP_F32, true, "")},
-                                     {{0}},
-                                     {CP_SUM_NAMES("f32,f32", "s"), CP_SUM_NAMES("f32,f32", "v")}};
-SumTable<CP_F32, CP_BF16> g_sum_fb = {{CP_SUM_ROW(CP_F32, CP_BF16, false, ""),
-                                       CP_SUM_ROW(CP_F32, CP_BF16, true, "")},
-                                      {{0}},
-                                      {CP_SUM_NAMES("f32,bf16", "s"), CP_SUM_NAMES("f32,bf16", "v")}};
-SumTable<CP_BF16, CP_BF16> g_sum_bb = {{CP_SUM_ROW(CP_BF16, CP_BF16, false, ""),
-                                        CP_SUM_ROW(CP_BF16, CP_BF16, true, "")},
-                                       {{0}},
-                                       {CP_SUM_NAMES("bf16,bf16", "s"), CP_SUM_NAMES("bf16,bf16", "v")}};
-SumTable<CP_BF16, CP_F32> g_sum_bf = {{CP_SUM_ROW(CP_BF16, CP_F32, false, ""),
-                                       CP_SUM_ROW(CP_BF16, CP_F32, true, "")},
-                                      {{0}},
-                                      {CP_SUM_NAMES("bf16,f32", "s"), CP_SUM_NAMES("bf16,f32", "v")}};
-
-template <int IN, int OUT>
-struct FusedTable {
-  void (*fn[2][4])(FusedArgs);
-  int occ[2][4];
-  const char* name[2][4];
-};
-
-#define CP_FUSED_ROW(IN, OUT, VEC)                                                           \
-  {fused_kernel<IN, OUT, 1, VEC>, fused_kernel<IN, OUT, 2, VEC>, fused_kernel<IN, OUT, 4, VEC>, \
-   fused_kernel<IN, OUT, 8, VEC>}
-#define CP_FUSED_NAMES(TAG, VEC)                                                             \
-  {"fused_grad_return<" TAG ",1," VEC ">", "fused_grad_return<" TAG ",2," VEC ">",            \
-   "fused_grad_return<" TAG ",4," VEC ">", "fused_grad_return<" TAG ",8," VEC ">"}
-
-FusedTable<CP_F32, CP_F32> g_fused_ff = {{CP_FUSED_ROW(CP_F32, CP_F32, false),
-                                          CP_FUSED_ROW(CP_F32, CP_F32, true)},
-                                         {{0}},
-                                         {CP_FUSED_NAMES("f32,f32", "s"), CP_FUSED_NAMES("f32,f32", "v")}};
-FusedTable<CP_F32, CP_BF16> g_fused_fb = {{CP_FUSED_ROW(CP_F32, CP_BF16, false),
-                                          CP_FUSED_ROW(CP_F32, CP_BF16, true)},
-                                         {{0}},
-                                         {CP_FUSED_NAMES("f32,bf16", "s"), CP_FUSED_NAMES("f32,bf16", "v")}};
-FusedTable<CP_BF16, CP_BF16> g_fused_bb = {{CP_FUSED_ROW(CP_BF16, CP_BF16, false),
-                                            CP_FUSED_ROW(CP_BF16, CP_BF16, true)},
-                                           {{0}},
-                                           {CP_FUSED_NAMES("bf16,bf16", "s"),
-                                            CP_FUSED_NAMES("bf16,bf16", "v")}};
-FusedTable<CP_BF16, CP_F32> g_fused_bf = {{CP_FUSED_ROW(CP_BF16, CP_F32, false),
-                                           CP_FUSED_ROW(CP_BF16, CP_F32, true)},
-                                          {{0}},
-                                          {CP_FUSED_NAMES("bf16,f32", "s"),
-                                           CP_FUSED_NAMES("bf16,f32", "v")}};
-
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
-template <typename Table, typename Args>
-hipError_t run_sum(Table& tab, const Args& ka, bool vec, int W, int64_t n_elems, hipStream_t stream) {
-  const int v = vec ? 1 : 0;
-  const int wi = W <= 1 ? 0 : W <= 2 ? 1 : W <= 4 ? 2 : 3;
-  const int occ = occupancy(tab.fn[v][wi], &tab.occ[v][wi], g_mutex);
-  const int64_t work = vec ? (n_elems / 8 + (n_elems % 8)) : n_elems;
-  int64_t want = (work + kBlock - 1) / kBlock;
-  const int64_t cap = (int64_t)device_cu_count() * occ;
-  if (want > cap) want = cap;
-  if (want < 1) want = 1;
-  profile_before(tab.name[v][wi], stream);
-  hipLaunchKernelGGL(tab.fn[v][wi], dim3((unsigned)want), dim3(kBlock), 0, stream, ka);
+const char* dtype_tag(int dt) { return dt == CP_F32 ? "f32" : "bf16"; }
+
+// Tile shapes (units of 8 elements per thread / per lane, waves per row).
+// Chosen from a sweep on MI355X; see the kernels' comments.
+// At most 8 slots x 8 floats of loaded data per thread and pass: more raises
+// register use enough to lower occupancy (a W=8 bf16 sum with 2 units per
+// thread measured 25% slower).
+constexpr int sum_upt(int in_dtype, int wb) { return wb <= 2 ? 4 : wb <= 4 ? 2 : 1; }
+constexpr int fused_upl(int in_dtype, int wb) { return wb <= 2 ? 2 : 1; }
+constexpr int kFusedWpr = 4;
+// Flat fused tiles: ~20 KiB of output rows per workgroup, NP units per thread
+// and pass (best of a sweep of 1-8 rows x 1-2 units on the S=262144 and
+// S=131072 shapes).
+constexpr int64_t kFusedTileBytes = 20480;
+constexpr int fused_np(int wb) { return wb <= 4 ? 2 : 1; }
+
+template <int IN, int OUT, int WB>
+hipError_t launch_sum_wb(const SlotSumArgs& a, bool vec, hipStream_t stream) {
+  constexpr int UPT = sum_upt(IN, WB);
+  static const std::string names[2] = {
+      std::string("slot_sum<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," + std::to_string(WB) + ",s>",
+      std::string("slot_sum<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," + std::to_string(WB) + ",v" +
+          std::to_string(UPT) + ">"};
+  int64_t blocks;
+  if (vec) {
+    const int64_t units = a.n_elems / 8;
+    blocks = (units + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
+    const int64_t tail = a.n_elems - units * 8;
+    if (blocks == 0 && tail > 0) blocks = 1;
+  } else {
+    blocks = (a.n_elems + kBlock - 1) / kBlock;
+  }
+  if (blocks > kMaxGrid) blocks = kMaxGrid;
+  if (blocks < 1) blocks = 1;
+  profile_before(names[vec ? 1 : 0].c_str(), stream);
+  if (vec)
+    hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, true, UPT>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, false, 1>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                       stream, a);
   hipError_t e = hipGetLastError();
   profile_after(stream);
   return e;
 }
 
-template <typename Table>
-hipError_t run_fused(Table& tab, const FusedArgs& a, bool vec, hipStream_t stream) {
-  const int v = vec ? 1 : 0;
-  const int W = a.cp_size;
-  const int wi = W <= 1 ? 0 : W <= 2 ? 1 : W <= 4 ? 2 : 3;
-  const int occ = occupancy(tab.fn[v][wi], &tab.occ[v][wi], g_mutex);
-  const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * (a.total_tokens / W);
-  int64_t want = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int64_t cap = (int64_t)device_cu_count() * occ;
-  if (want > cap) want = cap;
-  if (want < 1) want = 1;
-  profile_before(tab.name[v][wi], stream);
-  hipLaunchKernelGGL(tab.fn[v][wi], dim3((unsigned)want), dim3(kBlock), 0, stream, a);
+template <int IN, int OUT>
+hipError_t launch_sum_typed(const SlotSumArgs& a, bool vec, hipStream_t stream) {
+  const int W = a.num_slots;
+  if (W <= 1) return launch_sum_wb<IN, OUT, 1>(a, vec, stream);
+  if (W <= 2) return launch_sum_wb<IN, OUT, 2>(a, vec, stream);
+  if (W <= 4) return launch_sum_wb<IN, OUT, 4>(a, vec, stream);
+  return launch_sum_wb<IN, OUT, 8>(a, vec, stream);
+}
+
+template <int IN, int OUT, int WB>
+hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
+  constexpr int NP = fused_np(WB);
+  static const std::string names[3] = {
+      std::string("fused_grad_return<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," + std::to_string(WB) + ",s>",
+      std::string("fused_grad_return<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," + std::to_string(WB) +
+          ",flat" + std::to_string(NP) + ">",
+      std::string("fused_grad_return<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," + std::to_string(WB) +
+          ",v" + std::to_string(fused_upl(IN, WB)) + "/" + std::to_string(kFusedWpr) + ">"};
+  const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * (a.total_tokens / a.cp_size);
+  const int64_t upr = a.row_elems / 8;
+  const int64_t out_row = a.row_elems * (OUT == CP_F32 ? 4 : 2);
+  int64_t rpt = kFusedTileBytes / out_row;
+  rpt = rpt < 1 ? 1 : (rpt > kMaxTileRows ? kMaxTileRows : rpt);
+  // flat tiles need unit * units_per_row < 2^32 for the multiply-high row split
+  const bool flat = vec && upr * upr * rpt < (int64_t(1) << 32);
+  const int kind = !vec ? 0 : flat ? 1 : 2;
+  const int64_t rows_per_block = kind == 1 ? rpt : kind == 2 ? kWavesPerBlock / kFusedWpr : kWavesPerBlock;
+  int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+  if (blocks > kMaxGrid) blocks = kMaxGrid;
+  if (blocks < 1) blocks = 1;
+  profile_before(names[kind].c_str(), stream);
+  if (kind == 1) {
+    const uint32_t magic = (uint32_t)(((uint64_t(1) << 32) + (uint64_t)upr - 1) / (uint64_t)upr);
+    hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, NP>), dim3((unsigned)blocks), dim3(kBlock), 0, stream,
+                       a, (int)rpt, magic);
+  } else if (kind == 2) {
+    hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, true, kFusedWpr, fused_upl(IN, WB)>), dim3((unsigned)blocks),
+                       dim3(kBlock), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, false, 1, 1>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                       stream, a);
+  }
   hipError_t e = hipGetLastError();
   profile_after(stream);
   return e;
+}
+
+template <int IN, int OUT>
+hipError_t launch_fused_typed(const FusedArgs& a, bool vec, hipStream_t stream) {
+  const int W = a.cp_size;
+  if (W <= 1) return launch_fused_wb<IN, OUT, 1>(a, vec, stream);
+  if (W <= 2) return launch_fused_wb<IN, OUT, 2>(a, vec, stream);
+  if (W <= 4) return launch_fused_wb<IN, OUT, 4>(a, vec, stream);
+  return launch_fused_wb<IN, OUT, 8>(a, vec, stream);
 }
 
 }  // namespace
@@ -417,10 +512,10 @@ hipError_t launch_slot_sum(const SlotSumArgs& a, hipStream_t stream) {
   if (a.n_elems == 0) return hipSuccess;
   bool vec = aligned16(a.out);
   for (int w = 0; w < a.num_slots; ++w) vec = vec && aligned16(a.in.p[w]);
-  if (a.in_dtype == CP_F32 && a.out_dtype == CP_F32) return run_sum(g_sum_ff, a, vec, a.num_slots, a.n_elems, stream);
-  if (a.in_dtype == CP_F32 && a.out_dtype == CP_BF16) return run_sum(g_sum_fb, a, vec, a.num_slots, a.n_elems, stream);
-  if (a.in_dtype == CP_BF16 && a.out_dtype == CP_BF16) return run_sum(g_sum_bb, a, vec, a.num_slots, a.n_elems, stream);
-  if (a.in_dtype == CP_BF16 && a.out_dtype == CP_F32) return run_sum(g_sum_bf, a, vec, a.num_slots, a.n_elems, stream);
+  if (a.in_dtype == CP_F32 && a.out_dtype == CP_F32) return launch_sum_typed<CP_F32, CP_F32>(a, vec, stream);
+  if (a.in_dtype == CP_F32 && a.out_dtype == CP_BF16) return launch_sum_typed<CP_F32, CP_BF16>(a, vec, stream);
+  if (a.in_dtype == CP_BF16 && a.out_dtype == CP_BF16) return launch_sum_typed<CP_BF16, CP_BF16>(a, vec, stream);
+  if (a.in_dtype == CP_BF16 && a.out_dtype == CP_F32) return launch_sum_typed<CP_BF16, CP_F32>(a, vec, stream);
   return hipErrorInvalidValue;
 }
 
@@ -431,10 +526,10 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
   bool vec = a.row_elems % 8 == 0 && (a.row_elems * in_b) % 16 == 0 && (a.row_elems * out_b) % 16 == 0;
   for (int w = 0; w < a.cp_size; ++w) vec = vec && aligned16(a.grads.p[w]);
   for (int o = a.owner_begin; o < a.owner_end; ++o) vec = vec && aligned16(a.out.p[o]);
-  if (a.in_dtype == CP_F32 && a.out_dtype == CP_F32) return run_fused(g_fused_ff, a, vec, stream);
-  if (a.in_dtype == CP_F32 && a.out_dtype == CP_BF16) return run_fused(g_fused_fb, a, vec, stream);
-  if (a.in_dtype == CP_BF16 && a.out_dtype == CP_BF16) return run_fused(g_fused_bb, a, vec, stream);
-  if (a.in_dtype == CP_BF16 && a.out_dtype == CP_F32) return run_fused(g_fused_bf, a, vec, stream);
+  if (a.in_dtype == CP_F32 && a.out_dtype == CP_F32) return launch_fused_typed<CP_F32, CP_F32>(a, vec, stream);
+  if (a.in_dtype == CP_F32 && a.out_dtype == CP_BF16) return launch_fused_typed<CP_F32, CP_BF16>(a, vec, stream);
+  if (a.in_dtype == CP_BF16 && a.out_dtype == CP_BF16) return launch_fused_typed<CP_BF16, CP_BF16>(a, vec, stream);
+  if (a.in_dtype == CP_BF16 && a.out_dtype == CP_F32) return launch_fused_typed<CP_BF16, CP_F32>(a, vec, stream);
   return hipErrorInvalidValue;
 }
 
