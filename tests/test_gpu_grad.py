@@ -107,6 +107,23 @@ def test_random_documents(cp, W, in_dt, out_dt):
     run_and_check_full(cp, grads, cu, W, out_dt)
 
 
+@pytest.mark.parametrize("W,H,D,in_dt,out_dt", [
+    (4, 4, 128, torch.float32, torch.float32), (4, 8, 128, torch.float32, torch.bfloat16),
+    (8, 4, 128, torch.bfloat16, torch.bfloat16), (4, 4, 128, torch.bfloat16, torch.float32),
+    (2, 2, 256, torch.float32, torch.float32), (3, 12, 128, torch.float32, torch.float32)])
+def test_vector_paths_full_compare(cp, W, H, D, in_dt, out_dt):
+    """Rows of whole 512-element groups take the vectorized fused / slot-sum paths."""
+    say(f"case vector paths W={W} [{H},{D}] {in_dt}->{out_dt}")
+    rng = np.random.default_rng(100 + W)
+    lengths = (rng.integers(1, 4, size=5) * 2 * W * 8).tolist()
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    gen = torch.Generator(device=DEV).manual_seed(W + H)
+    grads = [[(torch.randn((T, H, D), generator=gen, device=DEV) * 1e-3).to(in_dt) for _ in range(W)]
+             for _ in range(2)]
+    run_and_check_full(cp, grads, cu, W, out_dt)
+
+
 def test_order_and_negative_zero(cp):
     say("case order pin")
     cu = np.array([0, 64], dtype=np.int32)

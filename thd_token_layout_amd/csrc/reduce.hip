@@ -28,6 +28,7 @@ namespace cpthd {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -43,49 +44,84 @@ __device__ __forceinline__ unsigned int f32_to_bf16_bits(float f) {
 }
 
 // ---- 8-element units -------------------------------------------------------
+// Element layout of unit u.  Contiguous (bf16 -> bf16): elements [8u, 8u+8),
+// one 16-byte access per lane.  Split (whenever fp32 data is involved): units
+// come in groups of 64, and unit u = 64g + l holds the pieces
+// [512g + 4l, +4) and [512g + 256 + 4l, +4), so each load or store instruction
+// of a wave covers one contiguous span of 64 pieces (16 B per lane for fp32,
+// 8 B for bf16).  With 32 contiguous bytes per lane instead, every store
+// instruction half-filled each cache line: measured 8-10% extra HBM write
+// traffic.  The split layout needs whole groups: 512 elements.
 struct F8 {
   float v[8];
 };
 
-template <int IN>  // IN: CP_F32 or CP_BF16
+template <int IN, int OUT>
+constexpr bool split_layout() { return IN == CP_F32 || OUT == CP_F32; }
+template <int IN, int OUT>
+constexpr int64_t unit_group_elems() { return split_layout<IN, OUT>() ? 512 : 8; }
+
+__device__ __forceinline__ int64_t split_piece(int64_t unit) { return (unit >> 6) * 128 + (unit & 63); }
+
+__device__ __forceinline__ void bf16x4_to_f32(float* v, u32x2 w) {
+  v[0] = bf16_bits_to_f32(w.x & 0xFFFFu);
+  v[1] = bf16_bits_to_f32(w.x >> 16);
+  v[2] = bf16_bits_to_f32(w.y & 0xFFFFu);
+  v[3] = bf16_bits_to_f32(w.y >> 16);
+}
+
+__device__ __forceinline__ void f32x4_from(float* v, u32x4 a) {
+  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+  v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+}
+
+template <int IN, bool SPLIT>
 __device__ __forceinline__ void load_unit(F8& x, const char* base, int64_t unit) {
-  if constexpr (IN == CP_F32) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(base) + 2 * unit;
-    const u32x4 a = __builtin_nontemporal_load(p);
-    const u32x4 b = __builtin_nontemporal_load(p + 1);
-    x.v[0] = __uint_as_float(a.x); x.v[1] = __uint_as_float(a.y);
-    x.v[2] = __uint_as_float(a.z); x.v[3] = __uint_as_float(a.w);
-    x.v[4] = __uint_as_float(b.x); x.v[5] = __uint_as_float(b.y);
-    x.v[6] = __uint_as_float(b.z); x.v[7] = __uint_as_float(b.w);
-  } else {
-    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + unit);
-    const unsigned int w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x.v[2 * k] = bf16_bits_to_f32(w[k] & 0xFFFFu);
-      x.v[2 * k + 1] = bf16_bits_to_f32(w[k] >> 16);
+  if constexpr (SPLIT) {
+    const int64_t p0 = split_piece(unit);
+    if constexpr (IN == CP_F32) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(base);
+      f32x4_from(x.v, __builtin_nontemporal_load(p + p0));
+      f32x4_from(x.v + 4, __builtin_nontemporal_load(p + p0 + 64));
+    } else {
+      const u32x2* p = reinterpret_cast<const u32x2*>(base);
+      bf16x4_to_f32(x.v, __builtin_nontemporal_load(p + p0));
+      bf16x4_to_f32(x.v + 4, __builtin_nontemporal_load(p + p0 + 64));
     }
+  } else {
+    static_assert(IN == CP_BF16, "the contiguous layout is bf16 only");
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + unit);
+    bf16x4_to_f32(x.v, u32x2{a.x, a.y});
+    bf16x4_to_f32(x.v + 4, u32x2{a.z, a.w});
   }
 }
 
-template <int OUT>
+__device__ __forceinline__ u32x4 f32x4_bits(const float* v) {
+  return u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+               __float_as_uint(v[3])};
+}
+__device__ __forceinline__ u32x2 bf16x4_bits(const float* v) {
+  return u32x2{f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+               f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
+}
+
+template <int OUT, bool SPLIT>
 __device__ __forceinline__ void store_unit(char* base, int64_t unit, const F8& x) {
-  if constexpr (OUT == CP_F32) {
-    u32x4* p = reinterpret_cast<u32x4*>(base) + 2 * unit;
-    u32x4 a, b;
-    a.x = __float_as_uint(x.v[0]); a.y = __float_as_uint(x.v[1]);
-    a.z = __float_as_uint(x.v[2]); a.w = __float_as_uint(x.v[3]);
-    b.x = __float_as_uint(x.v[4]); b.y = __float_as_uint(x.v[5]);
-    b.z = __float_as_uint(x.v[6]); b.w = __float_as_uint(x.v[7]);
-    __builtin_nontemporal_store(a, p);
-    __builtin_nontemporal_store(b, p + 1);
+  if constexpr (SPLIT) {
+    const int64_t p0 = split_piece(unit);
+    if constexpr (OUT == CP_F32) {
+      u32x4* p = reinterpret_cast<u32x4*>(base);
+      __builtin_nontemporal_store(f32x4_bits(x.v), p + p0);
+      __builtin_nontemporal_store(f32x4_bits(x.v + 4), p + p0 + 64);
+    } else {
+      u32x2* p = reinterpret_cast<u32x2*>(base);
+      __builtin_nontemporal_store(bf16x4_bits(x.v), p + p0);
+      __builtin_nontemporal_store(bf16x4_bits(x.v + 4), p + p0 + 64);
+    }
   } else {
-    u32x4 a;
-    a.x = f32_to_bf16_bits(x.v[0]) | (f32_to_bf16_bits(x.v[1]) << 16);
-    a.y = f32_to_bf16_bits(x.v[2]) | (f32_to_bf16_bits(x.v[3]) << 16);
-    a.z = f32_to_bf16_bits(x.v[4]) | (f32_to_bf16_bits(x.v[5]) << 16);
-    a.w = f32_to_bf16_bits(x.v[6]) | (f32_to_bf16_bits(x.v[7]) << 16);
-    __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(base) + unit);
+    static_assert(OUT == CP_BF16, "the contiguous layout is bf16 only");
+    const u32x2 lo = bf16x4_bits(x.v), hi = bf16x4_bits(x.v + 4);
+    __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y}, reinterpret_cast<u32x4*>(base) + unit);
   }
 }
 
@@ -105,7 +141,7 @@ __device__ __forceinline__ void store_elem(char* base, int64_t k, float f) {
 // of WB slots (for all UPT units) are issued before that batch's adds, which
 // then run in slot order.  `in` is the kernel argument table (uniform), off[u]
 // a byte offset applied to every slot for unit u, ok[u] masks units past the end.
-template <int IN, int WB, int UPT>
+template <int IN, bool SPLIT, int WB, int UPT>
 __device__ __forceinline__ void sum_units(F8 (&acc)[UPT], const ConstRankPtrs& in, int W,
                                           const int64_t (&off)[UPT], const int64_t (&unit)[UPT],
                                           const bool (&ok)[UPT]) {
@@ -115,7 +151,7 @@ __device__ __forceinline__ void sum_units(F8 (&acc)[UPT], const ConstRankPtrs& i
     for (int u = 0; u < UPT; ++u)
 #pragma unroll
       for (int w = 0; w < WB; ++w)
-        if (ok[u] && w < W) load_unit<IN>(x[u][w], in.p[w] + off[u], unit[u]);
+        if (ok[u] && w < W) load_unit<IN, SPLIT>(x[u][w], in.p[w] + off[u], unit[u]);
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
 #pragma unroll
@@ -134,7 +170,7 @@ __device__ __forceinline__ void sum_units(F8 (&acc)[UPT], const ConstRankPtrs& i
     for (int u = 0; u < UPT; ++u)
 #pragma unroll
       for (int w = 0; w < WB; ++w)
-        if (ok[u] && w0 + w < W) load_unit<IN>(x[u][w], in.p[w0 + w] + off[u], unit[u]);
+        if (ok[u] && w0 + w < W) load_unit<IN, SPLIT>(x[u][w], in.p[w0 + w] + off[u], unit[u]);
 #pragma unroll
     for (int u = 0; u < UPT; ++u)
 #pragma unroll
@@ -168,9 +204,10 @@ __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
     if (a.owner >= 0 && ((h->wait_timeout_ranks >> a.owner) & 1ull)) return;
   }
   const int W = a.num_slots;
+  constexpr bool SPLIT = split_layout<IN, OUT>();
   int64_t done = 0;
   if constexpr (VEC) {
-    const int64_t nunits = a.n_elems / 8;
+    const int64_t nunits = a.n_elems / unit_group_elems<IN, OUT>() * (unit_group_elems<IN, OUT>() / 8);
     const int64_t ntiles = (nunits + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
       int64_t unit[UPT], off[UPT];
@@ -182,10 +219,10 @@ __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
         off[u] = 0;
       }
       F8 acc[UPT];
-      sum_units<IN, WB, UPT>(acc, a.in, W, off, unit, ok);
+      sum_units<IN, SPLIT, WB, UPT>(acc, a.in, W, off, unit, ok);
 #pragma unroll
       for (int u = 0; u < UPT; ++u)
-        if (ok[u]) store_unit<OUT>(a.out, unit[u], acc[u]);
+        if (ok[u]) store_unit<OUT, SPLIT>(a.out, unit[u], acc[u]);
     }
     done = nunits * 8;
   }
@@ -273,10 +310,10 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
           off[m] = src_off;
         }
         F8 acc[UPL];
-        sum_units<IN, WB, UPL>(acc, a.grads, W, off, unit, ok);
+        sum_units<IN, split_layout<IN, OUT>(), WB, UPL>(acc, a.grads, W, off, unit, ok);
 #pragma unroll
         for (int m = 0; m < UPL; ++m)
-          if (ok[m]) store_unit<OUT>(row_dst, unit[m], acc[m]);
+          if (ok[m]) store_unit<OUT, split_layout<IN, OUT>()>(row_dst, unit[m], acc[m]);
       }
     } else if (chunk == 0) {
       for (int64_t k = lane; k < a.row_elems; k += 64) {
@@ -340,10 +377,10 @@ __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, int row
         off[m] = s_src[row[m]];
       }
       F8 acc[NP];
-      sum_units<IN, WB, NP>(acc, a.grads, W, off, unit, ok);
+      sum_units<IN, split_layout<IN, OUT>(), WB, NP>(acc, a.grads, W, off, unit, ok);
 #pragma unroll
       for (int m = 0; m < NP; ++m)
-        if (ok[m]) store_unit<OUT>(s_dst[row[m]], unit[m], acc[m]);
+        if (ok[m]) store_unit<OUT, split_layout<IN, OUT>()>(s_dst[row[m]], unit[m], acc[m]);
     }
     __syncthreads();  // s_src / s_dst are rewritten by the next tile
   }
@@ -429,9 +466,10 @@ hipError_t launch_sum_wb(const SlotSumArgs& a, bool vec, hipStream_t stream) {
           std::to_string(UPT) + ">"};
   int64_t blocks;
   if (vec) {
-    const int64_t units = a.n_elems / 8;
+    constexpr int64_t G = unit_group_elems<IN, OUT>();
+    const int64_t units = a.n_elems / G * (G / 8);
     blocks = (units + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
-    const int64_t tail = a.n_elems - units * 8;
+    const int64_t tail = a.n_elems - units * 8;  // elements left to the scalar loop
     if (blocks == 0 && tail > 0) blocks = 1;
   } else {
     blocks = (a.n_elems + kBlock - 1) / kBlock;
@@ -462,6 +500,7 @@ hipError_t launch_sum_typed(const SlotSumArgs& a, bool vec, hipStream_t stream) 
 template <int IN, int OUT, int WB>
 hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
   constexpr int NP = fused_np(WB);
+  vec = vec && a.row_elems % unit_group_elems<IN, OUT>() == 0;  // whole unit groups per row
   static const std::string names[3] = {
       std::string("fused_grad_return<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," + std::to_string(WB) + ",s>",
       std::string("fused_grad_return<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," + std::to_string(WB) +
