@@ -159,6 +159,30 @@ def attribute_kernels(step: Step, cp, torch):
         {k: sum(c for c, _ in v) for k, v in per_kernel.items()}
 
 
+def counted_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter runs.
+
+    None when there is no record for this kernel or when any source the record
+    was measured with has changed since (the counters would then be stale).
+    """
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic_s262144.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel") != kernel:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return int(round(rec["traffic_bytes_per_launch"]))
+
+
 def cpu_baseline(S_sample: int, WL, passes: int = 2):
     """The CPU oracle, as it stands, on the same step at S_sample tokens, `passes` times."""
     import numpy as np
@@ -299,8 +323,11 @@ def main():
     kernels.sort(key=lambda k: -k["total_ms"])
     dom = kernels[0]
     achieved = dom["gbs"] or 0.0
+    traffic = counted_traffic(dom["kernel"])
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled "
+                                "by a 1 GiB copy; profiles/traffic_s262144.md)",
                 "kernel": dom["kernel"], "bytes_per_launch": dom["bytes_per_launch"],
                 "avg_launch_us": dom["avg_us"]}
 
