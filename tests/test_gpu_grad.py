@@ -333,6 +333,39 @@ def test_per_rank_split_phases_with_delayed_writer(cp, W):
     check_per_rank_result(cp, meta, cu, grads, out, epochs, W, 9)
 
 
+def test_wait_blocks_until_host_releases_epoch(cp):
+    """Rank 0 of W=2 runs alone: writer 1's slot data is already in place but its epoch
+    is withheld.  While rank 0's device wait spins, its output still holds the poison
+    (read back through a copy on another stream); once the host writes the epoch, the
+    wait ends, the sum runs and equals the oracle, and no timeout is reported."""
+    say("case host-released epoch")
+    W = 2
+    cu = np.array([0, 64, 128], dtype=np.int32)
+    grads = [[torch.randn((128, 2, 64), device=DEV) for _ in range(W)]]
+    meta = make_meta(cp, cu, 128, W)
+    slots, out = alloc(grads, W, torch.float32, fill=float("nan"))
+    # writer 1's scatter, done beforehand; its epoch is not published
+    ref_slots, ref_out = O.grad_return([to_np(g) for g in grads[0]], cu, W, "f32", "f32")
+    slots[0][0][1].copy_(torch.from_numpy(ref_slots[0][1]))
+    epochs = torch.zeros((W, W), dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+    main, side = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(main):
+        cp.cp_grad_return(grads, slots, out, meta, rank=0, epochs=epochs, epoch=4,
+                          wait_timeout_us=10_000_000, stream=main)
+    import time
+    time.sleep(0.2)
+    with torch.cuda.stream(side):
+        probe = out[0][0].to("cpu")  # copy on the side stream while rank 0 waits
+        assert torch.isnan(probe).all(), "the owner summed before every epoch was published"
+        release = torch.full((1,), 4, dtype=torch.int32).pin_memory()
+        epochs[0, 1:2].copy_(release, non_blocking=True)
+    torch.cuda.synchronize()
+    st, flags, timeouts = cp.cp_meta_status(meta)
+    assert st == cp.CP_OK and timeouts == 0, (st, hex(flags), timeouts)
+    assert bits_equal(to_np(out[0][0]), ref_out[0])
+
+
 def test_epoch_timeout_is_reported_not_hung(cp):
     """Per-rank calls on ONE stream: rank 0 waits for rank 1's epoch, which is queued
     behind it.  The device wait gives up after 2 ms, rank 0's sum writes nothing and
@@ -352,7 +385,7 @@ def test_epoch_timeout_is_reported_not_hung(cp):
     assert (out[0][0] == -7.0).all()           # fail-closed: owner 0 wrote nothing
     ref = O.grad_return([to_np(g) for g in grads[0]], cu, W, "f32", "f32")[1]
     assert bits_equal(to_np(out[0][1]), ref[1])
-    # a later, correctly ordered call clears the verdict
+    # a later, correctly ordered call clears the timeout mask
     cp.cp_grad_return(grads, slots, out, meta, epochs=epochs, epoch=2)
     st, flags, timeouts = cp.cp_meta_status(meta)
     assert st == cp.CP_OK and timeouts == 0

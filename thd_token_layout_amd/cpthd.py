@@ -98,19 +98,29 @@ def cp_version() -> int:
     return lib.cp_version()
 
 
+_DTYPES = {torch.float32: CP_F32, torch.bfloat16: CP_BF16, torch.float16: CP_F16}
+for _name, _code in (("float8_e4m3fn", CP_FP8_E4M3), ("float8_e5m2", CP_FP8_E5M2)):
+    if hasattr(torch, _name):
+        _DTYPES[getattr(torch, _name)] = _code
+
+
 def dtype_code(dt: torch.dtype) -> int:
-    table = {torch.float32: CP_F32, torch.bfloat16: CP_BF16, torch.float16: CP_F16}
-    fp8 = {getattr(torch, "float8_e4m3fn", None): CP_FP8_E4M3,
-           getattr(torch, "float8_e5m2", None): CP_FP8_E5M2}
-    if dt in table:
-        return table[dt]
-    if dt in fp8:
-        return fp8[dt]
-    raise TypeError(f"unsupported dtype {dt}")
+    try:
+        return _DTYPES[dt]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {dt}") from None
 
 
-def _stream(stream) -> int:
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, like: Optional[torch.Tensor] = None) -> int:
+    """The HIP stream handle: `stream` if given, else torch's current stream."""
     if stream is None:
+        if _raw_stream is not None:
+            dev = like.device.index if like is not None and like.device.index is not None \
+                else torch.cuda.current_device()
+            return _raw_stream(dev)
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, int):
         return stream
@@ -168,7 +178,7 @@ def cp_build_meta(cu_seqlens: torch.Tensor, total_tokens: int, cp_size: int, pol
     if meta is None:
         meta = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=cu_seqlens.device)
     st = lib.cp_build_meta(_ptr(cu_seqlens), B, int(total_tokens), int(cp_size), int(policy),
-                           _ptr(meta), meta.numel(), _stream(stream))
+                           _ptr(meta), meta.numel(), _stream(stream, cu_seqlens))
     _check(st, "cp_build_meta")
     m = Meta(meta, int(cp_size), int(policy), B, int(total_tokens))
     if check:
@@ -183,7 +193,7 @@ def cp_meta_status(meta, stream=None):
     buf = meta.buf if isinstance(meta, Meta) else meta
     flags = _i32(0)
     timeouts = _u64(0)
-    st = lib.cp_meta_status(_ptr(buf), _stream(stream), ctypes.byref(flags), ctypes.byref(timeouts))
+    st = lib.cp_meta_status(_ptr(buf), _stream(stream, buf), ctypes.byref(flags), ctypes.byref(timeouts))
     if st not in (CP_OK, CP_ERR_META, CP_ERR_TIMEOUT):
         raise CpError(st, "cp_meta_status")
     return st, flags.value, timeouts.value
@@ -205,7 +215,7 @@ def cp_partition_thd(x: torch.Tensor, meta: Meta, parts: Optional[torch.Tensor] 
     if parts is None:
         parts = torch.empty((meta.cp_size, T // meta.cp_size, H, D), dtype=x.dtype, device=x.device)
     st = lib.cp_partition_thd(_ptr(x), _ptr(parts), T, H, D, dtype_code(x.dtype), meta.ptr(),
-                              _stream(stream))
+                              _stream(stream, x))
     _check(st, "cp_partition_thd")
     return parts
 
@@ -217,7 +227,7 @@ def cp_gather_thd(parts: torch.Tensor, meta: Meta, x: Optional[torch.Tensor] = N
     if x is None:
         x = torch.empty((T, H, D), dtype=parts.dtype, device=parts.device)
     st = lib.cp_gather_thd(_ptr(parts), _ptr(x), T, H, D, dtype_code(parts.dtype), meta.ptr(),
-                           _stream(stream))
+                           _stream(stream, parts))
     _check(st, "cp_gather_thd")
     return x
 
@@ -243,7 +253,7 @@ def cp_grad_return(grads: Sequence[Sequence[torch.Tensor]], slots, out, meta: Me
     st = lib.cp_grad_return(int(rank), W, n_tensors, _table(_flat2(grads)), _table(_flat3(slots)),
                             _table(_flat2(out)), T, H, D, dtype_code(ref.dtype),
                             dtype_code(out_ref.dtype), meta.ptr(), _ptr(epochs), int(epoch),
-                            int(wait_timeout_us), int(phases), _stream(stream))
+                            int(wait_timeout_us), int(phases), _stream(stream, ref))
     _check(st, "cp_grad_return")
 
 
@@ -255,13 +265,13 @@ def cp_grad_return_fused(grads, out, meta: Meta, rank: int = CP_ALL_RANKS, strea
     out_ref = next(o for o in _flat2(out) if o is not None)
     st = lib.cp_grad_return_fused(int(rank), W, n_tensors, _table(_flat2(grads)), _table(_flat2(out)),
                                   T, H, D, dtype_code(ref.dtype), dtype_code(out_ref.dtype),
-                                  meta.ptr(), _stream(stream))
+                                  meta.ptr(), _stream(stream, ref))
     _check(st, "cp_grad_return_fused")
 
 
 def cp_slot_sum(slots: Sequence[torch.Tensor], out: torch.Tensor, stream=None) -> torch.Tensor:
     st = lib.cp_slot_sum(len(slots), _table(slots), _ptr(out), out.numel(),
-                         dtype_code(slots[0].dtype), dtype_code(out.dtype), _stream(stream))
+                         dtype_code(slots[0].dtype), dtype_code(out.dtype), _stream(stream, out))
     _check(st, "cp_slot_sum")
     return out
 
