@@ -124,10 +124,35 @@ def pc_rank_rows(total_tokens, cp_size, rank):
 
 
 def rank_rows(cu, total_tokens, cp_size, policy, rank):
+    """Global token index of every local row of `rank` under `policy` (validated cu)."""
     _require_valid(cu, total_tokens, cp_size, policy)
     if policy == DUAL_CHUNK_SWAP:
         return dcs_rank_rows(cu, cp_size, rank)
     return pc_rank_rows(total_tokens, cp_size, rank)
+
+
+def rank_row(cu, total_tokens, cp_size, policy, rank, i):
+    """Global token of local row i of `rank`, one row at a time (for sampled checks).
+
+    Walks the documents in order, counting the rows each one leaves on the rank
+    (its two chunks under dual-chunk-swap), until the document holding local
+    row i is reached; inside it, the first chunk-length rows come from chunk
+    `rank` and the rest from chunk 2W-1-rank.  Packed-contiguous: r*T/W + i.
+    Input validity is the caller's job (call cu_violations first).
+    """
+    W = cp_size
+    if policy == PACKED_CONTIGUOUS:
+        return rank * (total_tokens // W) + i
+    seen = 0
+    for b in range(len(cu) - 1):
+        L = int(cu[b + 1]) - int(cu[b])
+        c = L // (2 * W)
+        if i < seen + 2 * c:
+            j = i - seen
+            chunk = rank if j < c else 2 * W - 1 - rank
+            return int(cu[b]) + chunk * c + (j % c if c else 0)
+        seen += 2 * c
+    raise IndexError(i)
 
 
 # --------------------------------------------------------------------------
@@ -176,7 +201,11 @@ def local_cu_seqlens(cu, total_tokens, cp_size, policy):
 # Partition and inverse gather of a packed [T, H, D] tensor (bit copies).
 # --------------------------------------------------------------------------
 def partition(x, cu, cp_size, policy):
-    """parts[r][i] = x[g_r(i)]; returns an array [W, T/W, ...] of x's dtype."""
+    """parts[r][i] = x[g_r(i)]; returns an array [W, T/W, ...] of x's dtype.
+
+    "[PyTorch] Add experimental packed-contiguous THD all-gather CP", "Why":
+    each rank's share of the packed buffer under the chosen policy.
+    """
     T = x.shape[0]
     W = cp_size
     parts = np.empty((W, T // W) + x.shape[1:], dtype=x.dtype)
@@ -186,7 +215,11 @@ def partition(x, cu, cp_size, policy):
 
 
 def gather(parts, cu, cp_size, policy):
-    """Inverse of partition: x[g_r(i)] = parts[r][i]."""
+    """Inverse of partition: x[g_r(i)] = parts[r][i].
+
+    Same page, commit messages: after the all-gather the dual-chunk-swap
+    layout needs a reorder back to global order (packed-contiguous does not).
+    """
     W = cp_size
     T = parts.shape[0] * parts.shape[1]
     x = np.empty((T,) + parts.shape[2:], dtype=parts.dtype)
@@ -210,7 +243,12 @@ def bf16_to_f32(u16):
 
 
 def f32_to_bf16_rne(f32):
-    """Round fp32 to bf16, nearest-even, on the bit pattern; NaN -> quiet NaN."""
+    """Round fp32 to bf16, nearest-even, on the bit pattern; NaN -> quiet NaN.
+
+    The pages fix no rounding for the bf16 output; this is the stated reading
+    (IEEE default rounding, as torch's cast): add 0x7FFF plus the lowest kept
+    bit, keep the high 16 bits.
+    """
     f32 = np.ascontiguousarray(f32, dtype=np.float32)
     u = f32.view(np.uint32).astype(np.uint64)
     lsb = (u >> np.uint64(16)) & np.uint64(1)
@@ -289,5 +327,9 @@ def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype):
 
 
 def epochs_after(cp_size, epoch):
-    """Epoch table after every writer has published `epoch` to every owner."""
+    """Epoch table after every writer has published `epoch` to every owner.
+
+    "Add stream-ordered CP gradient return primitive", "Sequence Diagram": each
+    writer writes its epoch into every owner's [owner][writer] entry.
+    """
     return np.full((cp_size, cp_size), epoch, dtype=np.uint32)

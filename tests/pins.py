@@ -282,6 +282,23 @@ def check_invariants(o, cu, T, W, policy, x):
         assert len(set(work)) == 1, work
 
 
+def check_rank_row_matches_rank_rows(o):
+    """The one-row form agrees with the full-array form, row by row."""
+    rng = np.random.default_rng(9)
+    for W in (1, 2, 3, 4, 8):
+        for pol in o.POLICIES:
+            if pol == o.DUAL_CHUNK_SWAP:
+                lengths = [2 * W * int(k) for k in rng.integers(0, 4, size=6)]
+            else:
+                lengths = [int(k) for k in rng.integers(0, 9, size=6)]
+                lengths[-1] += (-sum(lengths)) % W
+            cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+            T = int(cu[-1])
+            for r in range(W):
+                rows = o.rank_rows(cu, T, W, pol, r)
+                assert [o.rank_row(cu, T, W, pol, r, i) for i in range(len(rows))] == rows.tolist()
+
+
 def check_fused_equals_unfused(o, seed=3):
     rng = np.random.default_rng(seed)
     for W, dt in ((2, "f32"), (4, "bf16"), (8, "bf16"), (3, "f32")):
@@ -310,5 +327,6 @@ ALL_CHECKS = [
     check_single_document_native_layout,
     check_pc_is_reshape,
     check_brute_force_grad_return,
+    check_rank_row_matches_rank_rows,
     check_fused_equals_unfused,
 ]

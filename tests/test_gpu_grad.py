@@ -244,6 +244,31 @@ def test_grad_return_s256k_w4(cp):
     assert (epochs == 1).all()
 
 
+def test_fused_more_rows_than_the_grid(cp):
+    """68M output rows of 4 fp32 (scalar fused path, one row per wave): more than the
+    largest grid launched, so the grid-stride loop runs; sampled rows vs the oracle."""
+    say("case fused 68M rows (grid-stride)")
+    W = 2
+    lengths = [1 << 26, (1 << 20) + 4, 12]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    gen = torch.Generator(device=DEV).manual_seed(68)
+    grads = [[torch.randn((T, 1, 4), generator=gen, device=DEV) for _ in range(W)]]
+    meta = make_meta(cp, cu, T, W)
+    n = T // W
+    out = [[torch.empty((n, 1, 4), device=DEV) for _ in range(W)]]
+    cp.cp_grad_return_fused(grads, out, meta)
+    rng = np.random.default_rng(6)
+    for o in range(W):
+        idx = np.unique(np.concatenate([rng.integers(0, n, size=300), [0, n - 1]]))
+        g = torch.tensor([O.rank_row(cu, T, W, O.DUAL_CHUNK_SWAP, o, int(i)) for i in idx], device=DEV)
+        src = [to_np(grads[0][w].index_select(0, g)) for w in range(W)]
+        ref = O.slot_sum(src, "f32", "f32")
+        assert bits_equal(to_np(out[0][o].index_select(0, torch.from_numpy(idx).to(DEV))), ref), o
+    del grads, out
+    torch.cuda.empty_cache()
+
+
 def test_fused_s128k_w8(cp):
     w = WL.WORKLOADS["fused_s128k_w8"]
     say("case fused_s128k_w8 (full size)")
