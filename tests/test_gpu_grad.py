@@ -110,7 +110,9 @@ def test_random_documents(cp, W, in_dt, out_dt):
 @pytest.mark.parametrize("W,H,D,in_dt,out_dt", [
     (4, 4, 128, torch.float32, torch.float32), (4, 8, 128, torch.float32, torch.bfloat16),
     (8, 4, 128, torch.bfloat16, torch.bfloat16), (4, 4, 128, torch.bfloat16, torch.float32),
-    (2, 2, 256, torch.float32, torch.float32), (3, 12, 128, torch.float32, torch.float32)])
+    (2, 2, 256, torch.float32, torch.float32), (3, 12, 128, torch.float32, torch.float32),
+    (4, 16, 128, torch.float32, torch.float32), (2, 20, 128, torch.float32, torch.bfloat16),
+    (4, 16, 128, torch.bfloat16, torch.bfloat16), (3, 24, 128, torch.bfloat16, torch.float32)])
 def test_vector_paths_full_compare(cp, W, H, D, in_dt, out_dt):
     """Rows of whole 512-element groups take the vectorized fused / slot-sum paths."""
     say(f"case vector paths W={W} [{H},{D}] {in_dt}->{out_dt}")

@@ -451,9 +451,10 @@ const char* dtype_tag(int dt) { return dt == CP_F32 ? "f32" : "bf16"; }
 constexpr int sum_upt(int in_dtype, int wb) { return wb <= 2 ? 4 : wb <= 4 ? 2 : 1; }
 constexpr int fused_upl(int in_dtype, int wb) { return wb <= 2 ? 2 : 1; }
 constexpr int kFusedWpr = 4;
-// Flat fused tiles: ~20 KiB of output rows per workgroup, NP units per thread
-// and pass (best of a sweep of 1-8 rows x 1-2 units on the S=262144 and
-// S=131072 shapes).
+// Fused shapes, from a sweep on the S=262144 (W=4 fp32) and S=131072 (W=8
+// bf16) shapes: for W <= 4 a wave per row with 4 units per lane and pass
+// (6.07 TB/s against 5.8-6.0 for flat tiles); otherwise flat tiles of ~20 KiB
+// of output rows, NP units per thread and pass.
 constexpr int64_t kFusedTileBytes = 20480;
 constexpr int fused_np(int wb) { return wb <= 4 ? 2 : 1; }
 
@@ -501,21 +502,26 @@ template <int IN, int OUT, int WB>
 hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
   constexpr int NP = fused_np(WB);
   vec = vec && a.row_elems % unit_group_elems<IN, OUT>() == 0;  // whole unit groups per row
-  static const std::string names[3] = {
-      std::string("fused_grad_return<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," + std::to_string(WB) + ",s>",
-      std::string("fused_grad_return<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," + std::to_string(WB) +
-          ",flat" + std::to_string(NP) + ">",
-      std::string("fused_grad_return<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," + std::to_string(WB) +
-          ",v" + std::to_string(fused_upl(IN, WB)) + "/" + std::to_string(kFusedWpr) + ">"};
+  const std::string tag = std::string("fused_grad_return<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," +
+                          std::to_string(WB) + ",";
+  static const std::string names[4] = {tag + "s>", tag + "flat" + std::to_string(NP) + ">", tag + "v4/1>",
+                                       tag + "v" + std::to_string(fused_upl(IN, WB)) + "/" +
+                                           std::to_string(kFusedWpr) + ">"};
   const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * (a.total_tokens / a.cp_size);
   const int64_t upr = a.row_elems / 8;
   const int64_t out_row = a.row_elems * (OUT == CP_F32 ? 4 : 2);
   int64_t rpt = kFusedTileBytes / out_row;
   rpt = rpt < 1 ? 1 : (rpt > kMaxTileRows ? kMaxTileRows : rpt);
-  // flat tiles need unit * units_per_row < 2^32 for the multiply-high row split
-  const bool flat = vec && upr * upr * rpt < (int64_t(1) << 32);
-  const int kind = !vec ? 0 : flat ? 1 : 2;
-  const int64_t rows_per_block = kind == 1 ? rpt : kind == 2 ? kWavesPerBlock / kFusedWpr : kWavesPerBlock;
+  // kind 0: scalar; 1: flat tiles; 2: wave per row, 4 units per lane (W <= 4 and
+  // rows of >= 256 units); 3: 4 waves per row (very long rows).  The flat split
+  // needs unit * units_per_row < 2^32.
+  int kind = 0;
+  if (vec) {
+    if (WB <= 4 && upr >= 256) kind = 2;
+    else if (upr * upr * rpt < (int64_t(1) << 32)) kind = 1;
+    else kind = 3;
+  }
+  const int64_t rows_per_block = kind == 1 ? rpt : kind == 3 ? kWavesPerBlock / kFusedWpr : kWavesPerBlock;
   int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
   if (blocks > kMaxGrid) blocks = kMaxGrid;
   if (blocks < 1) blocks = 1;
@@ -525,6 +531,9 @@ hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
     hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, NP>), dim3((unsigned)blocks), dim3(kBlock), 0, stream,
                        a, (int)rpt, magic);
   } else if (kind == 2) {
+    hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, true, 1, 4>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                       stream, a);
+  } else if (kind == 3) {
     hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, true, kFusedWpr, fused_upl(IN, WB)>), dim3((unsigned)blocks),
                        dim3(kBlock), 0, stream, a);
   } else {
