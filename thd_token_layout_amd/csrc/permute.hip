@@ -95,6 +95,59 @@ __device__ __forceinline__ int64_t global_row(const Cursor& k, int32_t W, int64_
                  : k.gstart + (int64_t)(2 * W - 1 - k.r) * k.c + (j - k.c);
 }
 
+// Wave-uniform cursor in global order (used when the global side is the
+// destination, so the writes are sequential): global row t lies in document b
+// at offset off = t - cu[b], in chunk k = off / c_b at position j; chunk k
+// belongs to rank k (k < W) or 2W-1-k, and sits at local row
+// local_cu[b] + j (first chunk of the rank) or local_cu[b] + c_b + j.
+struct GCursor {
+  int64_t t;
+  int32_t b;
+  int64_t dstart;  // cu[b]
+  int64_t lstart;  // local_cu[b]
+  int64_t c;       // chunk length of document b
+  int32_t k;       // chunk index in [0, 2W)
+  int64_t j;       // position inside the chunk
+};
+
+__device__ __forceinline__ void gload_doc(GCursor& g, const int32_t* cu, const int32_t* lcu) {
+  g.dstart = cu[g.b];
+  g.lstart = lcu[g.b];
+  g.c = (lcu[g.b + 1] - lcu[g.b]) >> 1;
+}
+
+__device__ __forceinline__ void gseek(GCursor& g, int64_t t, int32_t B, const int32_t* cu,
+                                      const int32_t* lcu) {
+  g.t = t;
+  int lo = 0, hi = B - 1;  // largest b with cu[b] <= t: the non-empty document holding t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  g.b = lo;
+  gload_doc(g, cu, lcu);
+  const int64_t off = t - g.dstart;
+  g.k = (int32_t)(off / g.c);
+  g.j = off - (int64_t)g.k * g.c;
+}
+
+__device__ __forceinline__ void gadvance(GCursor& g, int32_t W, const int32_t* cu, const int32_t* lcu) {
+  ++g.t;
+  if (++g.j == g.c) {
+    g.j = 0;
+    if (++g.k == 2 * W) {
+      g.k = 0;
+      do { ++g.b; gload_doc(g, cu, lcu); } while (g.c == 0);
+    }
+  }
+}
+
+// Local position (rank, row) of the cursor's global row.
+__device__ __forceinline__ void glocal(const GCursor& g, int32_t W, int32_t* r, int64_t* i) {
+  if (g.k < W) { *r = g.k; *i = g.lstart + g.j; }
+  else { *r = 2 * W - 1 - g.k; *i = g.lstart + g.c + g.j; }
+}
+
 // Reads the metadata header; returns false (and records why) when the call
 // must not touch any output.
 __device__ __forceinline__ bool meta_ok(cp_meta_header* h, int64_t T, int32_t expect_W,
@@ -113,7 +166,7 @@ __device__ __forceinline__ bool meta_ok(cp_meta_header* h, int64_t T, int32_t ex
 // Waves are grouped WPR to a row: wave w takes rows [p_tile + (w / WPR) G, +G)
 // and, inside each row, the column chunks c = w % WPR, c + WPR, ... of 64*VPL
 // units each, so every lane has up to G*VPL loads in flight.
-template <typename U, int VPL, int G, int WPR>
+template <typename U, int VPL, int G, int WPR, bool GORDER>
 __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
   static_assert(kWavesPerBlock % WPR == 0, "WPR must divide the waves of a workgroup");
   constexpr int kRowsPerTile = (kWavesPerBlock / WPR) * G;
@@ -138,23 +191,53 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int64_t p0 = tile * kRowsPerTile + (int64_t)row_slot * G;
     if (p0 >= T) continue;
-    Cursor k;
-    seek(k, p0, n, B, dcs, cu, lcu);
     const U* src[G];
     U* dst[G];
     bool ok[G];
+    if constexpr (GORDER) {
+      // p0 indexes global rows; rows are visited in global order.
+      GCursor gc;
+      int64_t pcr = 0, pci = 0;  // packed-contiguous: rank and local row
+      if (dcs) gseek(gc, p0, B, cu, lcu);
+      else { pcr = p0 / n; pci = p0 - pcr * n; }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      ok[g] = p0 + g < T;
-      src[g] = nullptr;
-      dst[g] = nullptr;
-      if (ok[g]) {
-        char* gptr = a.global + global_row(k, W, n, dcs) * a.row_bytes;
-        char* lptr = a.local_table ? a.local.p[k.r] + k.i * a.row_bytes
-                                   : a.local.p[0] + ((int64_t)k.r * n + k.i) * a.row_bytes;
-        src[g] = reinterpret_cast<const U*>(a.to_local ? gptr : lptr);
-        dst[g] = reinterpret_cast<U*>(a.to_local ? lptr : gptr);
-        if (g + 1 < G && p0 + g + 1 < T) advance(k, n, dcs, cu, lcu);
+      for (int g = 0; g < G; ++g) {
+        ok[g] = p0 + g < T;
+        src[g] = nullptr;
+        dst[g] = nullptr;
+        if (ok[g]) {
+          int32_t r;
+          int64_t i;
+          if (dcs) glocal(gc, W, &r, &i);
+          else { r = (int32_t)pcr; i = pci; }
+          char* gptr = a.global + (p0 + g) * a.row_bytes;
+          char* lptr = a.local_table ? a.local.p[r] + i * a.row_bytes
+                                     : a.local.p[0] + ((int64_t)r * n + i) * a.row_bytes;
+          src[g] = reinterpret_cast<const U*>(a.to_local ? gptr : lptr);
+          dst[g] = reinterpret_cast<U*>(a.to_local ? lptr : gptr);
+          if (g + 1 < G && p0 + g + 1 < T) {
+            if (dcs) gadvance(gc, W, cu, lcu);
+            else if (++pci == n) { pci = 0; ++pcr; }
+          }
+        }
+      }
+    } else {
+      // p0 indexes local rows (flat r*n + i); rows are visited in local order.
+      Cursor k;
+      seek(k, p0, n, B, dcs, cu, lcu);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        ok[g] = p0 + g < T;
+        src[g] = nullptr;
+        dst[g] = nullptr;
+        if (ok[g]) {
+          char* gptr = a.global + global_row(k, W, n, dcs) * a.row_bytes;
+          char* lptr = a.local_table ? a.local.p[k.r] + k.i * a.row_bytes
+                                     : a.local.p[0] + ((int64_t)k.r * n + k.i) * a.row_bytes;
+          src[g] = reinterpret_cast<const U*>(a.to_local ? gptr : lptr);
+          dst[g] = reinterpret_cast<U*>(a.to_local ? lptr : gptr);
+          if (g + 1 < G && p0 + g + 1 < T) advance(k, n, dcs, cu, lcu);
+        }
       }
     }
     for (int64_t cb = (int64_t)chunk * 64 * VPL; cb < upr; cb += (int64_t)WPR * 64 * VPL) {
@@ -180,14 +263,16 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
 typedef void (*PermuteKernel)(PermuteArgs);
 
 struct Variant {
-  PermuteKernel fn;
+  PermuteKernel fn[2];  // [0]: local order (partition, scatter); [1]: global order (gather)
   int rows_per_tile;
-  const char* name;
+  const char* name[2];
 };
 
 #define CP_VARIANT(U, UNAME, VPL, G, WPR)                                                  \
-  Variant{permute_rows_kernel<U, VPL, G, WPR>, (kWavesPerBlock / WPR) * G,                 \
-          "permute_rows<" UNAME "," #VPL "x" #G "/" #WPR ">"}
+  Variant{{permute_rows_kernel<U, VPL, G, WPR, false>, permute_rows_kernel<U, VPL, G, WPR, true>}, \
+          (kWavesPerBlock / WPR) * G,                                                        \
+          {"permute_rows<" UNAME "," #VPL "x" #G "/" #WPR ">",                               \
+           "permute_rows<" UNAME "," #VPL "x" #G "/" #WPR ",g>"}}
 
 // Shapes by units per row (upr), from a sweep of tile shapes on MI355X
 // (partition, gather and scatter of 2, 5, 8 and 10 KiB rows): a workgroup
@@ -232,8 +317,11 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   const Variant& v = g_variants[ui][vi];
   const int64_t tiles = (a.total_tokens + v.rows_per_tile - 1) / v.rows_per_tile;
   const int blocks = (int)(tiles < kMaxGrid ? tiles : kMaxGrid);  // grid-stride beyond kMaxGrid
-  profile_before(v.name, stream);
-  hipLaunchKernelGGL(v.fn, dim3(blocks), dim3(kBlock), 0, stream, a);
+  // Visit rows in the order of the side being written: a gather writes the
+  // global layout, partition and scatter write the per-rank layout.
+  const int order = a.to_local ? 0 : 1;
+  profile_before(v.name[order], stream);
+  hipLaunchKernelGGL(v.fn[order], dim3(blocks), dim3(kBlock), 0, stream, a);
   hipError_t e = hipGetLastError();
   profile_after(stream);
   return e;
