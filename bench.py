@@ -98,11 +98,9 @@ class Step:
         self.ops.append(("build_meta x3", meta_bytes, build_metas))
         for pname, meta in (("dual_chunk_swap", self.meta_dcs), ("packed_contiguous", self.meta_pc)):
             self.ops.append((f"partition_{pname} QKV", 3 * 2 * S * row_bf16,
-                             lambda meta=meta: [cp.cp_partition_thd(x, meta, parts=p)
-                                                for x, p in zip(self.qkv, self.parts)]))
+                             lambda meta=meta: cp.cp_partition_thd_multi(self.qkv, meta, parts=self.parts)))
             self.ops.append((f"gather_{pname} QKV", 3 * 2 * S * row_bf16,
-                             lambda meta=meta: [cp.cp_gather_thd(p, meta, x=b)
-                                                for p, b in zip(self.parts, self.back)]))
+                             lambda meta=meta: cp.cp_gather_thd_multi(self.parts, meta, xs=self.back)))
 
         def grad_return():
             self.epoch += 1
@@ -118,7 +116,6 @@ class Step:
         self.kernel_bytes = {
             "scatter": 2 * S * row_f32,                 # one writer, one tensor: read T rows, write T rows
             "owner_sum": (Wg + 1) * n * row_f32,        # one owner, one tensor: read W slots, write 1
-            "layout": 2 * S * row_bf16,                 # one tensor: read T rows, write T rows
             "fused": (Wg + 1) * S * row_f32,            # one tensor, all owners
         }
 
@@ -147,7 +144,7 @@ def attribute_kernels(step: Step, cp, torch):
             elif name.startswith("grad_return_fused"):
                 b = step.kernel_bytes["fused"]
             elif name.startswith(("partition", "gather")):
-                b = step.kernel_bytes["layout"]
+                b = nbytes / count  # Q, K, V: one launch each, or one launch for all three
             elif name.startswith("slot_sum sweep"):
                 b = nbytes / count
             else:
@@ -228,6 +225,82 @@ def cpu_baseline(S_sample: int, WL, passes: int = 2):
                       f"numpy, one thread; {nbytes / 1e9:.2f} GB algorithmic in {dt:.1f} s"}
 
 
+def per_config(cp, WL, torch, dev, reps: int = 10):
+    """Each workload's ops timed on their own: median of `reps` HIP-event timings,
+    each preceded by a 1 GiB write that flushes the 256 MB last-level cache."""
+    import statistics
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    results = []
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        fn()  # warm
+        for _ in range(reps):
+            flush.fill_(1.0)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1000.0)
+        return statistics.median(ts)
+
+    def add(cfg, op, nbytes, us):
+        results.append({"config": cfg, "op": op, "bytes": nbytes, "median_us": round(us, 1),
+                        "gbs": round(nbytes / us / 1e3, 1), "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+
+    for name in ("dcs_t32k_w4", "pc_t64k_w4", "dcs_s256k_w4", "pc_s256k_w4", "dcs1_s256k_w4"):
+        w = WL.WORKLOADS[name]
+        cu = torch.from_numpy(WL.cu_seqlens(w)).to(dev)
+        meta = cp.cp_build_meta(cu, w.total_tokens, w.cp_size, cp.POLICY[w.policy], check=True)
+        xs = WL.random_tensors(w, w.n_tensors, device=dev)
+        parts = [torch.empty((w.cp_size, w.total_tokens // w.cp_size, w.heads, w.head_dim),
+                             dtype=x.dtype, device=dev) for x in xs]
+        back = [torch.empty_like(x) for x in xs]
+        nbytes = sum(2 * x.numel() * x.element_size() for x in xs)
+        add(name, "partition Q,K,V (multi-tensor call)", nbytes,
+            timed(lambda: cp.cp_partition_thd_multi(xs, meta, parts=parts)))
+        add(name, "gather Q,K,V (multi-tensor call)", nbytes,
+            timed(lambda: cp.cp_gather_thd_multi(parts, meta, xs=back)))
+        add(name, "partition Q,K,V (three single-tensor calls)", nbytes,
+            timed(lambda: [cp.cp_partition_thd(x, meta, parts=p) for x, p in zip(xs, parts)]))
+        add(name, "metadata", 0, timed(lambda: cp.cp_build_meta(cu, w.total_tokens, w.cp_size,
+                                                                  cp.POLICY[w.policy], meta=meta.buf)))
+        del xs, parts, back
+        torch.cuda.empty_cache()
+    for name in ("grad_s256k_w4", "fused_s128k_w8"):
+        w = WL.WORKLOADS[name]
+        W, S = w.cp_size, w.total_tokens
+        n = S // W
+        cu = torch.from_numpy(WL.cu_seqlens(w)).to(dev)
+        meta = cp.cp_build_meta(cu, S, W, cp.CP_POLICY_DUAL_CHUNK_SWAP, check=True)
+        vals = WL.random_tensors(w, 2 * W, device=dev)
+        grads = [vals[:W], vals[W:]]
+        dt = grads[0][0].dtype
+        row_in = w.heads * w.head_dim * grads[0][0].element_size()
+        out = [[torch.empty((n, w.heads, w.head_dim), dtype=dt, device=dev) for _ in range(W)]
+               for _ in range(2)]
+        add(name, "fused grad return dK,dV", 2 * (W + 1) * S * row_in,
+            timed(lambda: cp.cp_grad_return_fused(grads, out, meta)))
+        slots = [[[torch.empty((n, w.heads, w.head_dim), dtype=dt, device=dev) for _ in range(W)]
+                  for _ in range(W)] for _ in range(2)]
+        epochs = torch.zeros((W, W), dtype=torch.int32, device=dev)
+        state = {"e": 0}
+
+        def unfused():
+            state["e"] += 1
+            cp.cp_grad_return(grads, slots, out, meta, epochs=epochs, epoch=state["e"])
+
+        add(name, "grad return dK,dV (scatter, epochs, owner sums)", 2 * (3 * W + 1) * S * row_in,
+            timed(unfused))
+        del vals, grads, out, slots
+        torch.cuda.empty_cache()
+    del flush
+    torch.cuda.empty_cache()
+    return results
+
+
 def sweep_latency(step: Step, cp, torch, reps: int = 200):
     """Per-call latency (host validation + launch + kernel) of the W=8 slot sum."""
     res = []
@@ -263,6 +336,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep-latency", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload measurements (each config's ops timed alone)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run one plain 1 GiB device copy (torch copy_) first, as the reference "
                          "dispatch for scaling hardware traffic counters")
@@ -332,7 +407,14 @@ def main():
                 "avg_launch_us": dom["avg_us"]}
 
     sweep = None if args.no_sweep_latency else sweep_latency(step, cp, torch)
-    w_dcs, w_pc, w_gr = step.workloads
+    num_docs = step.num_docs
+    ops = [{"op": n, "bytes": b} for n, b, _ in step.ops]
+    configs = None
+    if not args.no_configs:
+        del step  # free the step's buffers (~70 GB) before the per-workload runs
+        torch.cuda.empty_cache()
+        log("[bench] per-config measurements")
+        configs = per_config(cp, WL, torch, dev)
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -352,13 +434,14 @@ def main():
                         f"unfused and fused (W=4, [S,20,128] fp32), W=8 fp32 slot-sum sweep",
             "S": args.tokens, "cp_size": 4, "heads": 20, "head_dim": 128,
             "layout_dtype": "bf16", "grad_dtype": "f32", "accumulate": "f32",
-            "docs_dcs": step.num_docs[0], "docs_pc": step.num_docs[1],
+            "docs_dcs": num_docs[0], "docs_pc": num_docs[1],
             "step_bytes": step_bytes,
         },
         "roofline": roofline,
         "kernels": kernels,
-        "ops": [{"op": n, "bytes": b} for n, b, _ in step.ops],
+        "ops": ops,
         "sweep_latency": sweep,
+        "per_config": configs,
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:

@@ -215,6 +215,23 @@ int cp_partition_thd(const void* x, void* parts, int64_t total_tokens, int32_t h
 int cp_gather_thd(const void* parts, void* x, int64_t total_tokens, int32_t heads,
                   int32_t head_dim, int32_t dtype, const void* meta, cp_stream_t stream);
 
+/*
+ * cp_partition_thd_multi / cp_gather_thd_multi - the same operations on
+ * n_tensors tensors of one shape in one launch (the pages partition Q, K and
+ * V together: [PC] "Why").  xs[t] and parts[t] (host tables of n_tensors
+ * device pointers) are tensor t's x [T, H, D] and parts [W, T/W, H, D];
+ * 1 <= n_tensors <= 8.  Every output must be disjoint from every input and
+ * from every other output.  Errors as cp_partition_thd.  (The library runs
+ * small tensors in one launch and tensors of >= 1 GiB of traffic each in one
+ * launch per tensor, whichever streams faster.)
+ */
+int cp_partition_thd_multi(int32_t n_tensors, const void* const* xs, void* const* parts,
+                           int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                           const void* meta, cp_stream_t stream);
+int cp_gather_thd_multi(int32_t n_tensors, const void* const* parts, void* const* xs,
+                        int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                        const void* meta, cp_stream_t stream);
+
 /* ------------------------------------------------------------ gradient return */
 /*
  * cp_grad_return - owner gradient return: scatter, epoch publish, epoch wait,

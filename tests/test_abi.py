@@ -97,6 +97,13 @@ def test_host_checks_before_any_hip_call(cp):
         assert fn(None, FAKE, 48, 2, 8, cp.CP_F32, FAKE, None) == cp.CP_ERR_ARG
         assert fn(FAKE, FAKE, 48, 0, 8, cp.CP_F32, FAKE, None) == cp.CP_ERR_ARG
         assert fn(FAKE, FAKE, 48, 2, 8, cp.CP_F32, None, None) == cp.CP_ERR_ARG
+    tab3 = (ctypes.c_void_p * 8)(*([0x10000] * 8))
+    for fn in (lib.cp_partition_thd_multi, lib.cp_gather_thd_multi):
+        assert fn(0, tab3, tab3, 48, 2, 8, cp.CP_BF16, FAKE, None) == cp.CP_ERR_ARG
+        assert fn(9, tab3, tab3, 48, 2, 8, cp.CP_BF16, FAKE, None) == cp.CP_ERR_ARG
+        assert fn(3, tab3, tab3, 48, 2, 8, cp.CP_FP8_E4M3, FAKE, None) == cp.CP_ERR_UNSUPPORTED
+        assert fn(3, None, tab3, 48, 2, 8, cp.CP_BF16, FAKE, None) == cp.CP_ERR_ARG
+        assert fn(3, None, None, 0, 2, 8, cp.CP_BF16, None, None) == cp.CP_OK
     # grad return: dtype pairs, rank range, divisibility, per-rank mode needs epochs
     tab = (ctypes.c_void_p * 64)(*([0x10000] * 64))
     gr = lib.cp_grad_return

@@ -91,6 +91,30 @@ def test_packed_documents_full_size(cp, name):
         check_layout(cp, x, cu, w.cp_size, pol)
 
 
+@pytest.mark.parametrize("name", ["dcs_t32k_w4", "pc_t64k_w4"])
+def test_multi_tensor_calls(cp, name):
+    """Q, K, V in one launch: every tensor equals the oracle's partition, the
+    gather restores each, and outputs overlapping each other are rejected."""
+    w = WL.WORKLOADS[name]
+    say(f"case {name} multi-tensor")
+    cu = WL.cu_seqlens(w)
+    pol = cp.POLICY[w.policy]
+    xs = WL.random_tensors(w, w.n_tensors, device=DEV)
+    meta = build(cp, cu, w.total_tokens, w.cp_size, pol)
+    parts = cp.cp_partition_thd_multi(xs, meta)
+    backs = cp.cp_gather_thd_multi(parts, meta)
+    for x, p, b in zip(xs, parts, backs):
+        assert bits_equal(to_np(p), O.partition(to_np(x), cu, w.cp_size, policy_name(pol)))
+        assert bits_equal(to_np(b), to_np(x))
+    big = torch.empty((2 * w.total_tokens, w.heads, w.head_dim), dtype=xs[0].dtype, device=DEV)
+    shaped = (w.cp_size, w.total_tokens // w.cp_size, w.heads, w.head_dim)
+    overlapping = [big[: w.total_tokens].view(shaped), big[w.total_tokens // 2: 3 * w.total_tokens // 2].view(shaped),
+                   parts[2]]
+    with pytest.raises(cp.CpError) as e:
+        cp.cp_partition_thd_multi(xs, meta, parts=overlapping)
+    assert e.value.status == cp.CP_ERR_ALIAS
+
+
 @pytest.mark.parametrize("name", ["dcs_s256k_w4", "pc_s256k_w4", "dcs1_s256k_w4"])
 def test_s256k_shapes(cp, name):
     w = WL.WORKLOADS[name]

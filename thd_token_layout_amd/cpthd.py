@@ -61,6 +61,12 @@ lib.cp_partition_thd.restype = _c.c_int
 lib.cp_partition_thd.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]
 lib.cp_gather_thd.restype = _c.c_int
 lib.cp_gather_thd.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]
+lib.cp_partition_thd_multi.restype = _c.c_int
+lib.cp_partition_thd_multi.argtypes = [_i32, _c.POINTER(_vp), _c.POINTER(_vp), _i64, _i32, _i32, _i32,
+                                       _vp, _vp]
+lib.cp_gather_thd_multi.restype = _c.c_int
+lib.cp_gather_thd_multi.argtypes = [_i32, _c.POINTER(_vp), _c.POINTER(_vp), _i64, _i32, _i32, _i32,
+                                    _vp, _vp]
 lib.cp_grad_return.restype = _c.c_int
 lib.cp_grad_return.argtypes = [_i32, _i32, _i32, _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_vp),
                                _i64, _i32, _i32, _i32, _i32, _vp, _vp, _u32, _i64, _i32, _vp]
@@ -232,6 +238,32 @@ def cp_gather_thd(parts: torch.Tensor, meta: Meta, x: Optional[torch.Tensor] = N
     return x
 
 
+def cp_partition_thd_multi(xs: Sequence[torch.Tensor], meta: Meta,
+                           parts: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    """Partition several tensors of one shape (e.g. Q, K, V) in one launch."""
+    T, H, D = xs[0].shape
+    if parts is None:
+        parts = [torch.empty((meta.cp_size, T // meta.cp_size, H, D), dtype=x.dtype, device=x.device)
+                 for x in xs]
+    st = lib.cp_partition_thd_multi(len(xs), _table(xs), _table(parts), T, H, D, dtype_code(xs[0].dtype),
+                                    meta.ptr(), _stream(stream, xs[0]))
+    _check(st, "cp_partition_thd_multi")
+    return list(parts)
+
+
+def cp_gather_thd_multi(parts: Sequence[torch.Tensor], meta: Meta,
+                        xs: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    """Inverse of cp_partition_thd_multi."""
+    W, n, H, D = parts[0].shape
+    T = W * n
+    if xs is None:
+        xs = [torch.empty((T, H, D), dtype=p.dtype, device=p.device) for p in parts]
+    st = lib.cp_gather_thd_multi(len(parts), _table(parts), _table(xs), T, H, D,
+                                 dtype_code(parts[0].dtype), meta.ptr(), _stream(stream, parts[0]))
+    _check(st, "cp_gather_thd_multi")
+    return list(xs)
+
+
 def _flat2(tab: Sequence[Sequence[Optional[torch.Tensor]]]):
     return [t for row in tab for t in row]
 
@@ -296,5 +328,6 @@ def cp_profile_read(capacity: int = 64):
 
 
 EXPORTED = ["cp_meta_bytes", "cp_build_meta", "cp_meta_status", "cp_partition_thd", "cp_gather_thd",
+            "cp_partition_thd_multi", "cp_gather_thd_multi",
             "cp_grad_return", "cp_grad_return_fused", "cp_slot_sum", "cp_status_string", "cp_version",
             "cp_profile_enable", "cp_profile_read"]

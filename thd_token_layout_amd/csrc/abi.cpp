@@ -218,29 +218,38 @@ int cp_meta_status(const void* meta, cp_stream_t stream, int32_t* flags_out,
   return CP_OK;
 }
 
-static int layout_call(const void* in, void* out, int64_t total_tokens, int32_t heads,
-                       int32_t head_dim, int32_t dtype, const void* meta, cp_stream_t stream,
-                       bool to_local) {
+static int layout_call(int32_t n_tensors, const void* const* ins, void* const* outs,
+                       int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                       const void* meta, cp_stream_t stream, bool to_local) {
   if (is_fp8(dtype)) return CP_ERR_UNSUPPORTED;
   if (!valid_layout_dtype(dtype)) return CP_ERR_ARG;
+  if (n_tensors < 1 || n_tensors > kMaxLayoutTensors) return CP_ERR_ARG;
   if (total_tokens < 0 || total_tokens > INT32_MAX || heads < 1 || head_dim < 1) return CP_ERR_ARG;
   if (total_tokens == 0) return CP_OK;  // nothing to move; empty tensors may have NULL data
-  if (in == nullptr || out == nullptr || meta == nullptr) return CP_ERR_ARG;
+  if (ins == nullptr || outs == nullptr || meta == nullptr) return CP_ERR_ARG;
+  for (int t = 0; t < n_tensors; ++t)
+    if (ins[t] == nullptr || outs[t] == nullptr) return CP_ERR_ARG;
   const int64_t row_bytes = (int64_t)heads * head_dim * dtype_bytes(dtype);
   const int64_t bytes = total_tokens * row_bytes;
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
-  if ((st = check_device_ptr(in, dev)) != CP_OK) return st;
-  if ((st = check_device_ptr(out, dev)) != CP_OK) return st;
   if ((st = check_device_ptr(meta, dev)) != CP_OK) return st;
-  if ((st = check_alias({range_of(out, bytes)},
-                        {range_of(in, bytes), range_of(meta, sizeof(cp_meta_header))})) != CP_OK)
-    return st;
+  std::vector<Range> in_ranges{range_of(meta, sizeof(cp_meta_header))}, out_ranges;
+  for (int t = 0; t < n_tensors; ++t) {
+    if ((st = check_device_ptr(ins[t], dev)) != CP_OK) return st;
+    if ((st = check_device_ptr(outs[t], dev)) != CP_OK) return st;
+    in_ranges.push_back(range_of(ins[t], bytes));
+    out_ranges.push_back(range_of(outs[t], bytes));
+  }
+  if ((st = check_alias(out_ranges, in_ranges)) != CP_OK) return st;
   PermuteArgs a;
   memset(&a, 0, sizeof(a));
   a.meta = const_cast<cp_meta_header*>(static_cast<const cp_meta_header*>(meta));
-  a.global = static_cast<char*>(to_local ? const_cast<void*>(in) : out);
-  a.local.p[0] = static_cast<char*>(to_local ? out : const_cast<void*>(in));
+  a.n_tensors = n_tensors;
+  for (int t = 0; t < n_tensors; ++t) {
+    a.global[t] = static_cast<char*>(to_local ? const_cast<void*>(ins[t]) : outs[t]);
+    a.local[t] = static_cast<char*>(to_local ? outs[t] : const_cast<void*>(ins[t]));
+  }
   a.local_table = false;
   a.to_local = to_local;
   a.total_tokens = total_tokens;
@@ -252,12 +261,24 @@ static int layout_call(const void* in, void* out, int64_t total_tokens, int32_t 
 
 int cp_partition_thd(const void* x, void* parts, int64_t total_tokens, int32_t heads,
                      int32_t head_dim, int32_t dtype, const void* meta, cp_stream_t stream) {
-  return layout_call(x, parts, total_tokens, heads, head_dim, dtype, meta, stream, true);
+  return layout_call(1, &x, &parts, total_tokens, heads, head_dim, dtype, meta, stream, true);
 }
 
 int cp_gather_thd(const void* parts, void* x, int64_t total_tokens, int32_t heads,
                   int32_t head_dim, int32_t dtype, const void* meta, cp_stream_t stream) {
-  return layout_call(parts, x, total_tokens, heads, head_dim, dtype, meta, stream, false);
+  return layout_call(1, &parts, &x, total_tokens, heads, head_dim, dtype, meta, stream, false);
+}
+
+int cp_partition_thd_multi(int32_t n_tensors, const void* const* xs, void* const* parts,
+                           int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                           const void* meta, cp_stream_t stream) {
+  return layout_call(n_tensors, xs, parts, total_tokens, heads, head_dim, dtype, meta, stream, true);
+}
+
+int cp_gather_thd_multi(int32_t n_tensors, const void* const* parts, void* const* xs,
+                        int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                        const void* meta, cp_stream_t stream) {
+  return layout_call(n_tensors, parts, xs, total_tokens, heads, head_dim, dtype, meta, stream, false);
 }
 
 // Common scalar checks of the gradient-return family.
@@ -351,8 +372,9 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
       PermuteArgs a;
       memset(&a, 0, sizeof(a));
       a.meta = h;
-      a.global = static_cast<char*>(const_cast<void*>(G(t, w)));
-      for (int o = 0; o < W; ++o) a.local.p[o] = static_cast<char*>(S(t, o, w));
+      a.n_tensors = 1;
+      a.global[0] = static_cast<char*>(const_cast<void*>(G(t, w)));
+      for (int o = 0; o < W; ++o) a.table.p[o] = static_cast<char*>(S(t, o, w));
       a.local_table = true;
       a.to_local = true;
       a.total_tokens = total_tokens;

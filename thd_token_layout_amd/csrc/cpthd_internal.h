@@ -46,15 +46,19 @@ hipError_t launch_build_meta(const int32_t* cu, int32_t B, int64_t T, int32_t W,
                              void* meta, hipStream_t stream);
 
 // ---------------------------------------------------------------- row permutation
-// One launch moves all T rows between the global layout and the per-rank
-// layout.  `global` is x ([T, row]); the local side is either one contiguous
-// [W, T/W, row] buffer (local_table == false, local.p[0] = base) or one
-// [T/W, row] buffer per rank (local_table == true).  to_local: partition /
-// scatter (global -> local); otherwise gather (local -> global).
+// One launch moves all T rows of n_tensors tensors (same T, row size and
+// layout) between the global layout and the per-rank layout.  global[t] is
+// tensor t's x ([T, row]); the local side is either one contiguous
+// [W, T/W, row] buffer per tensor (local_table == false, local[t]) or, for a
+// single tensor, one [T/W, row] buffer per rank (local_table == true, table).
+// to_local: partition / scatter (global -> local); otherwise gather.
+constexpr int kMaxLayoutTensors = 8;
 struct PermuteArgs {
   cp_meta_header* meta;
-  char* global;
-  RankPtrs local;
+  int32_t n_tensors;
+  char* global[kMaxLayoutTensors];
+  char* local[kMaxLayoutTensors];
+  RankPtrs table;
   bool local_table;
   bool to_local;
   int64_t total_tokens;

@@ -188,9 +188,12 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
   const int chunk = wave % WPR;
   const int64_t ntiles = (T + kRowsPerTile - 1) / kRowsPerTile;
 
+  const int tsr = blockIdx.y;  // tensor of this workgroup's tiles
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int64_t p0 = tile * kRowsPerTile + (int64_t)row_slot * G;
     if (p0 >= T) continue;
+    char* const gbase = a.global[tsr];
+    char* const lbase = a.local[tsr];
     const U* src[G];
     U* dst[G];
     bool ok[G];
@@ -210,9 +213,9 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
           int64_t i;
           if (dcs) glocal(gc, W, &r, &i);
           else { r = (int32_t)pcr; i = pci; }
-          char* gptr = a.global + (p0 + g) * a.row_bytes;
-          char* lptr = a.local_table ? a.local.p[r] + i * a.row_bytes
-                                     : a.local.p[0] + ((int64_t)r * n + i) * a.row_bytes;
+          char* gptr = gbase + (p0 + g) * a.row_bytes;
+          char* lptr = a.local_table ? a.table.p[r] + i * a.row_bytes
+                                     : lbase + ((int64_t)r * n + i) * a.row_bytes;
           src[g] = reinterpret_cast<const U*>(a.to_local ? gptr : lptr);
           dst[g] = reinterpret_cast<U*>(a.to_local ? lptr : gptr);
           if (g + 1 < G && p0 + g + 1 < T) {
@@ -231,9 +234,9 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
         src[g] = nullptr;
         dst[g] = nullptr;
         if (ok[g]) {
-          char* gptr = a.global + global_row(k, W, n, dcs) * a.row_bytes;
-          char* lptr = a.local_table ? a.local.p[k.r] + k.i * a.row_bytes
-                                     : a.local.p[0] + ((int64_t)k.r * n + k.i) * a.row_bytes;
+          char* gptr = gbase + global_row(k, W, n, dcs) * a.row_bytes;
+          char* lptr = a.local_table ? a.table.p[k.r] + k.i * a.row_bytes
+                                     : lbase + ((int64_t)k.r * n + k.i) * a.row_bytes;
           src[g] = reinterpret_cast<const U*>(a.to_local ? gptr : lptr);
           dst[g] = reinterpret_cast<U*>(a.to_local ? lptr : gptr);
           if (g + 1 < G && p0 + g + 1 < T) advance(k, n, dcs, cu, lcu);
@@ -298,11 +301,13 @@ Variant g_variants[4][7] = {
 }  // namespace
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
-  if (a.total_tokens == 0 || a.row_bytes == 0) return hipSuccess;
+  if (a.total_tokens == 0 || a.row_bytes == 0 || a.n_tensors < 1) return hipSuccess;
+  if (a.n_tensors > kMaxLayoutTensors || (a.local_table && a.n_tensors != 1)) return hipErrorInvalidValue;
   // Widest unit that divides the row size and every base address.
-  uintptr_t align_bits = (uintptr_t)a.global | (uintptr_t)a.row_bytes;
-  const int nlocal = a.local_table ? kMaxRanks : 1;
-  for (int k = 0; k < nlocal; ++k) align_bits |= (uintptr_t)a.local.p[k];
+  uintptr_t align_bits = (uintptr_t)a.row_bytes;
+  for (int t = 0; t < a.n_tensors; ++t) align_bits |= (uintptr_t)a.global[t] | (uintptr_t)a.local[t];
+  if (a.local_table)
+    for (int k = 0; k < kMaxRanks; ++k) align_bits |= (uintptr_t)a.table.p[k];
   int ui;
   int usize;
   if ((align_bits & 15) == 0) { ui = 0; usize = 16; }
@@ -320,8 +325,27 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   // Visit rows in the order of the side being written: a gather writes the
   // global layout, partition and scatter write the per-rank layout.
   const int order = a.to_local ? 0 : 1;
+  // Several tensors: one launch (a tensor per grid row) when each tensor is
+  // small, one launch per tensor when each moves >= 1 GiB.  Measured on
+  // MI355X: Q,K,V of 32768 x 8 x 128 bf16 run 19% faster in one launch, of
+  // 262144 x 20 x 128 bf16 4% slower.
+  const bool per_tensor = a.n_tensors > 1 && 2 * a.total_tokens * a.row_bytes >= (int64_t(1) << 30);
+  if (per_tensor) {
+    for (int t = 0; t < a.n_tensors; ++t) {
+      PermuteArgs b = a;
+      b.n_tensors = 1;
+      b.global[0] = a.global[t];
+      b.local[0] = a.local[t];
+      profile_before(v.name[order], stream);
+      hipLaunchKernelGGL(v.fn[order], dim3(blocks, 1), dim3(kBlock), 0, stream, b);
+      hipError_t e = hipGetLastError();
+      profile_after(stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   profile_before(v.name[order], stream);
-  hipLaunchKernelGGL(v.fn[order], dim3(blocks), dim3(kBlock), 0, stream, a);
+  hipLaunchKernelGGL(v.fn[order], dim3(blocks, a.n_tensors), dim3(kBlock), 0, stream, a);
   hipError_t e = hipGetLastError();
   profile_after(stream);
   return e;
