@@ -325,18 +325,18 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
   }
 }
 
-// Flat-tile variant: a workgroup owns `rows_per_tile` consecutive output rows
-// (at most kMaxTileRows).  The first rows_per_tile threads look up their row's
-// source offset and destination and share them through LDS; the workgroup then
-// walks the tile's rows*units 8-element units as one flat range, NP units per
-// thread and pass, so every pass keeps all four waves busy whatever the row
-// length.  row = unit / units_per_row uses a multiply-high by `upr_magic` =
-// ceil(2^32 / units_per_row), exact for unit * units_per_row < 2^32.
+// Flat-tile variant: the owners' output rows are one flat range of
+// rows * units_per_row 8-element units, and a workgroup owns kBlock*NP
+// consecutive units of it (a tile may start and end inside a row), so every
+// thread does exactly NP units in one pass, as in the slot sum.  The first
+// threads look up the source offset and destination of the <= kMaxTileRows
+// rows the tile touches and share them through LDS.  The row of a unit is
+// found with a multiply-high by `upr_magic` = ceil(2^32 / units_per_row),
+// exact while the in-tile offset times units_per_row stays below 2^32.
 constexpr int kMaxTileRows = 16;
 
 template <int IN, int OUT, int WB, int NP>
-__global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, int rows_per_tile,
-                                                            uint32_t upr_magic) {
+__global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_t upr_magic) {
   __shared__ int64_t s_src[kMaxTileRows];
   __shared__ char* s_dst[kMaxTileRows];
   cp_meta_header* h = a.meta;
@@ -350,38 +350,40 @@ __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, int row
   const int out_bytes = OUT == CP_F32 ? 4 : 2;
   const int64_t upr = a.row_elems / 8;
   const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * n;
-  const int64_t ntiles = (rows + rows_per_tile - 1) / rows_per_tile;
+  const int64_t total = rows * upr;
+  constexpr int64_t kTileUnits = (int64_t)kBlock * NP;
+  const int64_t ntiles = (total + kTileUnits - 1) / kTileUnits;
 
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t q0 = tile * rows_per_tile;
-    const int nrows = (int)(rows - q0 < rows_per_tile ? rows - q0 : rows_per_tile);
+    const int64_t u0 = tile * kTileUnits;
+    const int64_t row0 = u0 / upr;
+    const int64_t u_end = u0 + kTileUnits < total ? u0 + kTileUnits : total;
+    const int nrows = (int)((u_end - 1) / upr - row0 + 1);
     if ((int)threadIdx.x < nrows) {
-      const int64_t q = q0 + threadIdx.x;
+      const int64_t q = row0 + threadIdx.x;
       const int32_t o = a.owner_begin + (int32_t)(q / n);
       const int64_t i = q - (int64_t)(o - a.owner_begin) * n;
       s_src[threadIdx.x] = owner_row_to_global(o, i, W, B, cu, lcu) * a.row_elems * in_bytes;
       s_dst[threadIdx.x] = a.out.p[o] + i * a.row_elems * out_bytes;
     }
     __syncthreads();
-    const int64_t total = (int64_t)nrows * upr;
-    for (int64_t p0 = 0; p0 < total; p0 += (int64_t)kBlock * NP) {
-      int64_t unit[NP], off[NP];
-      int row[NP];
-      bool ok[NP];
+    const int64_t base = u0 - row0 * upr;  // offset of the tile's first unit inside row0
+    int64_t unit[NP], off[NP];
+    int row[NP];
+    bool ok[NP];
 #pragma unroll
-      for (int m = 0; m < NP; ++m) {
-        const uint32_t f = (uint32_t)(p0 + (int64_t)m * kBlock + threadIdx.x);
-        ok[m] = (int64_t)f < total;
-        row[m] = ok[m] ? (int)__umulhi(f, upr_magic) : 0;
-        unit[m] = (int64_t)f - (int64_t)row[m] * upr;
-        off[m] = s_src[row[m]];
-      }
-      F8 acc[NP];
-      sum_units<IN, split_layout<IN, OUT>(), WB, NP>(acc, a.grads, W, off, unit, ok);
-#pragma unroll
-      for (int m = 0; m < NP; ++m)
-        if (ok[m]) store_unit<OUT, split_layout<IN, OUT>()>(s_dst[row[m]], unit[m], acc[m]);
+    for (int m = 0; m < NP; ++m) {
+      const uint32_t f = (uint32_t)(base + (int64_t)m * kBlock + threadIdx.x);
+      ok[m] = u0 + (int64_t)m * kBlock + threadIdx.x < u_end;
+      row[m] = ok[m] ? (int)__umulhi(f, upr_magic) : 0;
+      unit[m] = (int64_t)f - (int64_t)row[m] * upr;
+      off[m] = s_src[row[m]];
     }
+    F8 acc[NP];
+    sum_units<IN, split_layout<IN, OUT>(), WB, NP>(acc, a.grads, W, off, unit, ok);
+#pragma unroll
+    for (int m = 0; m < NP; ++m)
+      if (ok[m]) store_unit<OUT, split_layout<IN, OUT>()>(s_dst[row[m]], unit[m], acc[m]);
     __syncthreads();  // s_src / s_dst are rewritten by the next tile
   }
 }
@@ -452,11 +454,8 @@ constexpr int sum_upt(int in_dtype, int wb) { return wb <= 2 ? 4 : wb <= 4 ? 2 :
 constexpr int fused_upl(int in_dtype, int wb) { return wb <= 2 ? 2 : 1; }
 constexpr int kFusedWpr = 4;
 // Fused shapes, from a sweep on the S=262144 (W=4 fp32) and S=131072 (W=8
-// bf16) shapes: for W <= 4 a wave per row with 4 units per lane and pass
-// (6.07 TB/s against 5.8-6.0 for flat tiles); otherwise flat tiles of ~20 KiB
-// of output rows, NP units per thread and pass.
-constexpr int64_t kFusedTileBytes = 20480;
-constexpr int fused_np(int wb) { return wb <= 4 ? 2 : 1; }
+// bf16) shapes: flat unit tiles, 2 units per thread for W <= 4 (6.20 TB/s,
+// against 6.05 for a wave per row), 1 unit per thread above.
 
 template <int IN, int OUT, int WB>
 hipError_t launch_sum_wb(const SlotSumArgs& a, bool vec, hipStream_t stream) {
@@ -500,39 +499,39 @@ hipError_t launch_sum_typed(const SlotSumArgs& a, bool vec, hipStream_t stream) 
 
 template <int IN, int OUT, int WB>
 hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
-  constexpr int NP = fused_np(WB);
-  vec = vec && a.row_elems % unit_group_elems<IN, OUT>() == 0;  // whole unit groups per row
   const std::string tag = std::string("fused_grad_return<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," +
                           std::to_string(WB) + ",";
-  static const std::string names[4] = {tag + "s>", tag + "flat" + std::to_string(NP) + ">", tag + "v4/1>",
+  static const std::string names[4] = {tag + "s>", tag + "flat1>", tag + "flat2>",
                                        tag + "v" + std::to_string(fused_upl(IN, WB)) + "/" +
                                            std::to_string(kFusedWpr) + ">"};
+  vec = vec && a.row_elems % unit_group_elems<IN, OUT>() == 0;  // whole unit groups per row
   const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * (a.total_tokens / a.cp_size);
   const int64_t upr = a.row_elems / 8;
-  const int64_t out_row = a.row_elems * (OUT == CP_F32 ? 4 : 2);
-  int64_t rpt = kFusedTileBytes / out_row;
-  rpt = rpt < 1 ? 1 : (rpt > kMaxTileRows ? kMaxTileRows : rpt);
-  // kind 0: scalar; 1: flat tiles; 2: wave per row, 4 units per lane (W <= 4 and
-  // rows of >= 256 units); 3: 4 waves per row (very long rows).  The flat split
-  // needs unit * units_per_row < 2^32.
-  int kind = 0;
-  if (vec) {
-    if (WB <= 4 && upr >= 256) kind = 2;
-    else if (upr * upr * rpt < (int64_t(1) << 32)) kind = 1;
-    else kind = 3;
+  const int np = a.cp_size <= 4 ? 2 : 1;
+  const int64_t tile_units = (int64_t)kBlock * np;
+  // Flat unit tiles need the rows a tile touches to fit kMaxTileRows and
+  // (tile units + units_per_row) * units_per_row < 2^32 for the row split.
+  const bool flat_ok = upr > 0 && tile_units / upr + 2 <= kMaxTileRows &&
+                       (tile_units + upr) * upr < (int64_t(1) << 32);
+  // kind 0: scalar; 1, 2: flat unit tiles with NP = 1, 2; 3: 4 waves per row (very long rows)
+  const int kind = !vec ? 0 : !flat_ok ? 3 : np;
+  int64_t blocks;
+  if (kind == 1 || kind == 2) {
+    blocks = (rows * upr + tile_units - 1) / tile_units;
+  } else {
+    const int64_t rows_per_block = kind == 3 ? kWavesPerBlock / kFusedWpr : kWavesPerBlock;
+    blocks = (rows + rows_per_block - 1) / rows_per_block;
   }
-  const int64_t rows_per_block = kind == 1 ? rpt : kind == 3 ? kWavesPerBlock / kFusedWpr : kWavesPerBlock;
-  int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
   if (blocks > kMaxGrid) blocks = kMaxGrid;
   if (blocks < 1) blocks = 1;
+  const uint32_t magic = upr > 0 ? (uint32_t)(((uint64_t(1) << 32) + (uint64_t)upr - 1) / (uint64_t)upr) : 0;
   profile_before(names[kind].c_str(), stream);
   if (kind == 1) {
-    const uint32_t magic = (uint32_t)(((uint64_t(1) << 32) + (uint64_t)upr - 1) / (uint64_t)upr);
-    hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, NP>), dim3((unsigned)blocks), dim3(kBlock), 0, stream,
-                       a, (int)rpt, magic);
+    hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, 1>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, a,
+                       magic);
   } else if (kind == 2) {
-    hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, true, 1, 4>), dim3((unsigned)blocks), dim3(kBlock), 0,
-                       stream, a);
+    hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, 2>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, a,
+                       magic);
   } else if (kind == 3) {
     hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, true, kFusedWpr, fused_upl(IN, WB)>), dim3((unsigned)blocks),
                        dim3(kBlock), 0, stream, a);
@@ -545,13 +544,14 @@ hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
   return e;
 }
 
+// Writers are summed in batches of at most 4 (W = 8 bf16 measured 6.08 TB/s
+// with two batches of 4, 5.03 TB/s with one batch of 8: register pressure).
 template <int IN, int OUT>
 hipError_t launch_fused_typed(const FusedArgs& a, bool vec, hipStream_t stream) {
   const int W = a.cp_size;
   if (W <= 1) return launch_fused_wb<IN, OUT, 1>(a, vec, stream);
   if (W <= 2) return launch_fused_wb<IN, OUT, 2>(a, vec, stream);
-  if (W <= 4) return launch_fused_wb<IN, OUT, 4>(a, vec, stream);
-  return launch_fused_wb<IN, OUT, 8>(a, vec, stream);
+  return launch_fused_wb<IN, OUT, 4>(a, vec, stream);
 }
 
 }  // namespace
