@@ -1,0 +1,68 @@
+// Device helpers shared by the kernels: the metadata check every kernel runs
+// first, and the dual-chunk-swap row map.
+//
+// Ownership ("[PyTorch] Add experimental packed-contiguous THD all-gather CP",
+// section "Why"; "Add stream-ordered CP gradient return primitive", author's
+// reply): every document b of length L_b is cut into 2W chunks of
+// c_b = L_b / (2W) tokens; rank r holds chunk r then chunk 2W-1-r, document
+// after document, so its local boundaries are local_cu = cu / W.  Local row i
+// of rank r, in document b (local_cu[b] <= i < local_cu[b+1]) at offset
+// j = i - local_cu[b], is global row
+//     cu[b] + r c_b + j                 if j <  c_b
+//     cu[b] + (2W-1-r) c_b + (j - c_b)  if j >= c_b.
+#pragma once
+
+#include "cpthd_internal.h"
+
+namespace cpthd {
+
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// The header words every kernel reads (scalar loads).
+__device__ __forceinline__ const int32_t* meta_cu(const cp_meta_header* h) {
+  return reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(h) + meta_cu_offset());
+}
+// local_cu of rank 0; under dual-chunk-swap every rank's local_cu is cu / W.
+__device__ __forceinline__ const int32_t* meta_local_cu0(const cp_meta_header* h) {
+  return meta_cu(h) + (h->num_docs + 1);
+}
+
+// Returns false, and records why in the sticky call flags, when a kernel must
+// not write any output: metadata never built, built from invalid cu_seqlens,
+// or built for another token count, CP size (expect_W >= 0) or policy
+// (expect_policy >= 0).  Every workgroup evaluates the same header, so all
+// of them take the same decision; one thread records it.
+__device__ __forceinline__ bool meta_ok(cp_meta_header* h, int64_t T, int32_t expect_W,
+                                        int32_t expect_policy) {
+  int code = 0;
+  if (h->magic != CP_META_MAGIC) code = CP_CALL_BAD_MAGIC;
+  else if (h->flags & CP_META_BUILD_MASK) code = CP_CALL_USED_INVALID_META;
+  else if (h->total_tokens != T) code = CP_CALL_TOKENS_MISMATCH;
+  else if (expect_W >= 0 && h->cp_size != expect_W) code = CP_CALL_CP_SIZE_MISMATCH;
+  else if (expect_policy >= 0 && h->policy != expect_policy) code = CP_CALL_POLICY_MISMATCH;
+  if (code != 0 && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) atomicOr(&h->flags, code);
+  return code == 0;
+}
+
+// Largest b in [0, B) with bound[b] <= v, for a nondecreasing bound[] with
+// bound[0] <= v < bound[B]: the non-empty document holding position v.
+__device__ __forceinline__ int find_doc(const int32_t* bound, int32_t B, int64_t v) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)bound[mid] <= v) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Global row of local row i of rank r under dual-chunk-swap.
+__device__ __forceinline__ int64_t dcs_global_row(int32_t r, int64_t i, int32_t W, int32_t B,
+                                                  const int32_t* cu, const int32_t* lcu) {
+  const int b = find_doc(lcu, B, i);
+  const int64_t lstart = lcu[b];
+  const int64_t c = (lcu[b + 1] - lstart) >> 1;
+  const int64_t j = i - lstart;
+  return j < c ? cu[b] + (int64_t)r * c + j : cu[b] + (int64_t)(2 * W - 1 - r) * c + (j - c);
+}
+
+}  // namespace cpthd

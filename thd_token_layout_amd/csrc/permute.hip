@@ -1,16 +1,9 @@
 // Row-permutation copy engine: THD partition, inverse gather and the
 // gradient-return scatter.
 //
-// Ownership ("[PyTorch] Add experimental packed-contiguous THD all-gather CP",
-// sections "Why" and commit messages; "Add stream-ordered CP gradient return
-// primitive", author's reply): under dual-chunk-swap every document b of
-// length L_b is cut into 2W chunks of c_b = L_b/(2W) tokens and rank r holds
-// chunk r then chunk 2W-1-r, document after document; under packed-contiguous
-// rank r holds tokens [r n, (r+1) n), n = T/W.  So local row i of rank r, in
-// document b (local_cu[b] <= i < local_cu[b+1], local_cu = cu/W), offset
-// j = i - local_cu[b], is global row
-//     cu[b] + r c_b + j                   if j <  c_b
-//     cu[b] + (2W-1-r) c_b + (j - c_b)    if j >= c_b.
+// The row map (ownership rule and its formula) is in device_common.h: under
+// dual-chunk-swap rank r holds chunk r then chunk 2W-1-r of every document;
+// under packed-contiguous rank r holds tokens [r n, (r+1) n), n = T/W.
 //
 // Design (gfx950): pure data movement, HBM-bound.  A workgroup (4 waves) owns
 // a tile of consecutive local rows (8-20 KiB); the launch covers every tile
@@ -23,7 +16,7 @@
 // lane then moves 16-byte units of the G rows (VPL units per row, up to G*VPL
 // loads in flight per lane) with non-temporal loads and stores, fully
 // coalesced (a wave touches 1 KiB contiguous per instruction).
-#include "cpthd_internal.h"
+#include "device_common.h"
 
 
 namespace cpthd {
@@ -40,8 +33,6 @@ template <typename U>
 __device__ __forceinline__ void store_nt(U* p, U v) {
   __builtin_nontemporal_store(v, p);
 }
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Wave-uniform cursor over the flat local row index p = r*n + i.
 struct Cursor {
@@ -66,12 +57,7 @@ __device__ __forceinline__ void seek(Cursor& k, int64_t p, int64_t n, int32_t B,
   k.r = (int32_t)(p / n);
   k.i = p - (int64_t)k.r * n;
   if (!dcs) return;
-  int lo = 0, hi = B - 1;  // largest b with lcu[b] <= i (lcu[0] = 0 <= i)
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)lcu[mid] <= k.i) lo = mid; else hi = mid - 1;
-  }
-  k.b = lo;
+  k.b = find_doc(lcu, B, k.i);
   load_doc(k, cu, lcu);
 }
 
@@ -119,12 +105,7 @@ __device__ __forceinline__ void gload_doc(GCursor& g, const int32_t* cu, const i
 __device__ __forceinline__ void gseek(GCursor& g, int64_t t, int32_t B, const int32_t* cu,
                                       const int32_t* lcu) {
   g.t = t;
-  int lo = 0, hi = B - 1;  // largest b with cu[b] <= t: the non-empty document holding t
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  g.b = lo;
+  g.b = find_doc(cu, B, t);
   gload_doc(g, cu, lcu);
   const int64_t off = t - g.dstart;
   g.k = (int32_t)(off / g.c);
@@ -148,20 +129,6 @@ __device__ __forceinline__ void glocal(const GCursor& g, int32_t W, int32_t* r, 
   else { *r = 2 * W - 1 - g.k; *i = g.lstart + g.c + g.j; }
 }
 
-// Reads the metadata header; returns false (and records why) when the call
-// must not touch any output.
-__device__ __forceinline__ bool meta_ok(cp_meta_header* h, int64_t T, int32_t expect_W,
-                                        int32_t expect_policy) {
-  int code = 0;
-  if (h->magic != CP_META_MAGIC) code = CP_CALL_BAD_MAGIC;
-  else if (h->flags & CP_META_BUILD_MASK) code = CP_CALL_USED_INVALID_META;
-  else if (h->total_tokens != T) code = CP_CALL_TOKENS_MISMATCH;
-  else if (expect_W >= 0 && h->cp_size != expect_W) code = CP_CALL_CP_SIZE_MISMATCH;
-  else if (expect_policy >= 0 && h->policy != expect_policy) code = CP_CALL_POLICY_MISMATCH;
-  if (code != 0 && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&h->flags, code);
-  return code == 0;
-}
-
 // One workgroup = 4 waves = a tile of (4 / WPR) * G consecutive local rows.
 // Waves are grouped WPR to a row: wave w takes rows [p_tile + (w / WPR) G, +G)
 // and, inside each row, the column chunks c = w % WPR, c + WPR, ... of 64*VPL
@@ -178,12 +145,12 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
   const int32_t B = h->num_docs;
   const int64_t n = h->local_tokens;
   const bool dcs = h->policy == CP_POLICY_DUAL_CHUNK_SWAP;
-  const int32_t* cu = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(h) + 64);
-  const int32_t* lcu = cu + (B + 1);  // local_cu[0][*] = cu / W
+  const int32_t* cu = meta_cu(h);
+  const int32_t* lcu = meta_local_cu0(h);
   const int64_t upr = a.row_bytes / (int64_t)sizeof(U);  // units per row
 
   const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
+  const int wave = wave_uniform(threadIdx.x >> 6);
   const int row_slot = wave / WPR;
   const int chunk = wave % WPR;
   const int64_t ntiles = (T + kRowsPerTile - 1) / kRowsPerTile;

@@ -13,13 +13,14 @@
 // an agent-scope release store, the wait is a bounded spin with agent-scope
 // acquire loads (gfx950 has one L2 per XCD, so plain loads could stay stale).
 //
-// Design: HBM-bound streaming.  A thread handles units of 8 elements (16 B of
-// bf16, 32 B of fp32 per slot), issues the loads of a batch of WB slots before
-// adding them in order, and writes 16-byte vectors with non-temporal stores.
+// Design: HBM-bound streaming.  A thread handles units of 8 elements (laid out
+// so that every wave instruction touches one contiguous span, see below),
+// issues the loads of a batch of WB slots before adding them in order, and
+// writes with non-temporal stores.
 // Launches cover all work with one small contiguous tile per workgroup (a full
 // grid rather than a resident-capacity persistent loop, which streams HBM less
 // contiguously and measured slower on MI355X).
-#include "cpthd_internal.h"
+#include "device_common.h"
 
 #include <string>
 
@@ -29,8 +30,6 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ float bf16_bits_to_f32(unsigned int bits16) {
   return __uint_as_float(bits16 << 16);
@@ -182,15 +181,9 @@ __device__ __forceinline__ void sum_units(F8 (&acc)[UPT], const ConstRankPtrs& i
   }
 }
 
+// Gradient-return kernels need valid dual-chunk-swap metadata for W ranks.
 __device__ __forceinline__ bool grad_meta_ok(cp_meta_header* h, int64_t T, int32_t W) {
-  int code = 0;
-  if (h->magic != CP_META_MAGIC) code = CP_CALL_BAD_MAGIC;
-  else if (h->flags & CP_META_BUILD_MASK) code = CP_CALL_USED_INVALID_META;
-  else if (h->total_tokens != T) code = CP_CALL_TOKENS_MISMATCH;
-  else if (h->cp_size != W) code = CP_CALL_CP_SIZE_MISMATCH;
-  else if (h->policy != CP_POLICY_DUAL_CHUNK_SWAP) code = CP_CALL_POLICY_MISMATCH;
-  if (code != 0 && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&h->flags, code);
-  return code == 0;
+  return meta_ok(h, T, W, CP_POLICY_DUAL_CHUNK_SWAP);
 }
 
 // ---- slot sum ----------------------------------------------------------------
@@ -236,36 +229,7 @@ __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
 }
 
 // ---- fused scatter + sum ---------------------------------------------------
-// Same row map as the permutation engine, restricted to dual-chunk-swap.
-struct DocCursor {
-  int32_t r;
-  int64_t i, lstart, lend, gstart, c;
-  int32_t b;
-};
-
-__device__ __forceinline__ void doc_load(DocCursor& k, const int32_t* cu, const int32_t* lcu) {
-  k.lstart = lcu[k.b];
-  k.lend = lcu[k.b + 1];
-  k.gstart = cu[k.b];
-  k.c = (k.lend - k.lstart) >> 1;
-}
-
-__device__ __forceinline__ int64_t owner_row_to_global(int32_t o, int64_t i, int32_t W, int32_t B,
-                                                       const int32_t* cu, const int32_t* lcu) {
-  DocCursor k;
-  k.r = o;
-  k.i = i;
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)lcu[mid] <= i) lo = mid; else hi = mid - 1;
-  }
-  k.b = lo;
-  doc_load(k, cu, lcu);
-  const int64_t j = i - k.lstart;
-  return j < k.c ? k.gstart + (int64_t)o * k.c + j
-                 : k.gstart + (int64_t)(2 * W - 1 - o) * k.c + (j - k.c);
-}
+// Owner o's local row i reads global row dcs_global_row(o, i) of every writer.
 
 // A workgroup owns (4 / WPR) output rows; WPR waves share a row, each taking
 // column passes of 64*UPL units (8 elements each) so a lane has UPL*W loads in
@@ -278,13 +242,13 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
   const int32_t W = a.cp_size;
   const int32_t B = h->num_docs;
   const int64_t n = h->local_tokens;
-  const int32_t* cu = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(h) + 64);
-  const int32_t* lcu = cu + (B + 1);
+  const int32_t* cu = meta_cu(h);
+  const int32_t* lcu = meta_local_cu0(h);
   const int in_bytes = IN == CP_F32 ? 4 : 2;
   const int out_bytes = OUT == CP_F32 ? 4 : 2;
 
   const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
+  const int wave = wave_uniform(threadIdx.x >> 6);
   const int row_slot = wave / WPR;
   const int chunk = wave % WPR;
   const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * n;
@@ -295,7 +259,7 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
     if (q >= rows) continue;
     const int32_t o = a.owner_begin + (int32_t)(q / n);
     const int64_t i = q - (int64_t)(o - a.owner_begin) * n;
-    const int64_t g = owner_row_to_global(o, i, W, B, cu, lcu);
+    const int64_t g = dcs_global_row(o, i, W, B, cu, lcu);
     const int64_t src_off = g * a.row_elems * in_bytes;  // same row in every writer's view
     char* row_dst = a.out.p[o] + i * a.row_elems * out_bytes;
     if constexpr (VEC) {
@@ -344,8 +308,8 @@ __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_
   const int32_t W = a.cp_size;
   const int32_t B = h->num_docs;
   const int64_t n = h->local_tokens;
-  const int32_t* cu = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(h) + 64);
-  const int32_t* lcu = cu + (B + 1);
+  const int32_t* cu = meta_cu(h);
+  const int32_t* lcu = meta_local_cu0(h);
   const int in_bytes = IN == CP_F32 ? 4 : 2;
   const int out_bytes = OUT == CP_F32 ? 4 : 2;
   const int64_t upr = a.row_elems / 8;
@@ -363,7 +327,7 @@ __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_
       const int64_t q = row0 + threadIdx.x;
       const int32_t o = a.owner_begin + (int32_t)(q / n);
       const int64_t i = q - (int64_t)(o - a.owner_begin) * n;
-      s_src[threadIdx.x] = owner_row_to_global(o, i, W, B, cu, lcu) * a.row_elems * in_bytes;
+      s_src[threadIdx.x] = dcs_global_row(o, i, W, B, cu, lcu) * a.row_elems * in_bytes;
       s_dst[threadIdx.x] = a.out.p[o] + i * a.row_elems * out_bytes;
     }
     __syncthreads();
