@@ -34,9 +34,14 @@ Readings where the pages are silent (the design notes list them all):
   * packed-contiguous local cu_seqlens are the sorted set of boundaries that
     fall inside the rank's slice, plus 0 and the slice length, padded with
     the slice length up to num_docs+1 entries;
-  * the owner's output is overwritten with the sum (not accumulated into);
-  * the fp32 accumulator is seeded with slot 0 (so -0.0 survives) and slots
-    are added in writer order 0..W-1;
+  * by default the owner's output is overwritten with the sum; in the
+    accumulate mode (the sequence diagram's "accumulate ... to dk" taken
+    literally) the fp32 accumulator starts from the owner's current gradient
+    and every slot is added to it in writer order;
+  * otherwise the fp32 accumulator is seeded with slot 0 (so -0.0 survives)
+    and slots are added in writer order 0..W-1;
+  * the gradient return follows the metadata's policy: under packed-contiguous
+    owner o's rows are its contiguous slice, as in the partition;
   * fp32 -> bf16 is round-to-nearest-even on the bit pattern; NaN stays a
     quiet NaN with its sign; denormals are kept.
 
@@ -279,48 +284,69 @@ def _narrow(acc, dtype):
 # --------------------------------------------------------------------------
 # Owner gradient return (PR 3235 "Description" and "Sequence Diagram").
 # --------------------------------------------------------------------------
-def slot_sum(slots, in_dtype, out_dtype):
-    """Sum W slot arrays in fp32, slot 0 first, one add per further slot."""
-    acc = _widen(slots[0], in_dtype).astype(np.float32, copy=True)
-    for w in range(1, len(slots)):
-        acc = (acc + _widen(slots[w], in_dtype)).astype(np.float32)
+def slot_sum(slots, in_dtype, out_dtype, into=None):
+    """Sum W slot arrays in fp32, one add per slot, in writer order.
+
+    Without `into` the accumulator is slot 0 and slots 1..W-1 are added.  With
+    `into` (the owner's current gradient, in out_dtype) the accumulator starts
+    from it and slots 0..W-1 are all added: "accumulate grad_key_return
+    [0..cp_size-1] to dk" of the sequence diagram, one slot at a time.
+    """
+    if into is None:
+        acc = _widen(slots[0], in_dtype).astype(np.float32, copy=True)
+        rest = slots[1:]
+    else:
+        acc = _widen(into, out_dtype).astype(np.float32, copy=True)
+        rest = slots
+    for s in rest:
+        acc = (acc + _widen(s, in_dtype)).astype(np.float32)
     return _narrow(acc, out_dtype)
 
 
-def grad_scatter(grads, cu, cp_size):
-    """Writer w puts the rows owner o owns into slot [o][w] (two-chunk layout).
+def grad_scatter(grads, cu, cp_size, policy=DUAL_CHUNK_SWAP):
+    """Writer w puts the rows owner o owns into slot [o][w].
 
     grads: list over writers of global [T, ...] arrays.  Returns
-    slots[o][w] = grads[w][g_o(:)], i.e. partition(grads[w])[o].
+    slots[o][w] = grads[w][g_o(:)], i.e. partition(grads[w])[o]: the two-chunk
+    layout under DualChunkSwap, the owner's contiguous slice under
+    packed-contiguous.
     """
     W = cp_size
     T = grads[0].shape[0]
     slots = [[None] * W for _ in range(W)]
     for w in range(W):
         for o in range(W):
-            slots[o][w] = grads[w][rank_rows(cu, T, W, DUAL_CHUNK_SWAP, o)]
+            slots[o][w] = grads[w][rank_rows(cu, T, W, policy, o)]
     return slots
 
 
-def grad_return(grads, cu, cp_size, in_dtype, out_dtype):
+def grad_return(grads, cu, cp_size, in_dtype, out_dtype, policy=DUAL_CHUNK_SWAP, into=None):
     """Scatter, then each owner sums its W writer slots in order 0..W-1.
 
-    Returns (slots, out) with out[o] = sum_w slots[o][w].
+    Returns (slots, out) with out[o] = sum_w slots[o][w]; with `into` (a list
+    over owners of their current gradients) out[o] = into[o] + slot 0 + ... .
     """
-    slots = grad_scatter(grads, cu, cp_size)
-    out = [slot_sum(slots[o], in_dtype, out_dtype) for o in range(cp_size)]
+    slots = grad_scatter(grads, cu, cp_size, policy)
+    out = [slot_sum(slots[o], in_dtype, out_dtype, None if into is None else into[o])
+           for o in range(cp_size)]
     return slots, out
 
 
-def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype):
-    """No slots: out[o][i] = sum over w (in order) of grads[w][g_o(i)]."""
+def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=DUAL_CHUNK_SWAP, into=None):
+    """No slots: out[o][i] = sum over w (in order) of grads[w][g_o(i)]
+    (after into[o][i] when accumulating)."""
     W = cp_size
     T = grads[0].shape[0]
     out = []
     for o in range(W):
-        rows = rank_rows(cu, T, W, DUAL_CHUNK_SWAP, o)
-        acc = _widen(grads[0][rows], in_dtype).astype(np.float32, copy=True)
-        for w in range(1, W):
+        rows = rank_rows(cu, T, W, policy, o)
+        if into is None:
+            acc = _widen(grads[0][rows], in_dtype).astype(np.float32, copy=True)
+            first = 1
+        else:
+            acc = _widen(into[o], out_dtype).astype(np.float32, copy=True)
+            first = 0
+        for w in range(first, W):
             acc = (acc + _widen(grads[w][rows], in_dtype)).astype(np.float32)
         out.append(_narrow(acc, out_dtype))
     return out

@@ -314,6 +314,96 @@ def check_fused_equals_unfused(o, seed=3):
                 assert out[owner].tobytes() == fused[owner].tobytes()
 
 
+# ---------------------------------------------------------------- accumulate mode, packed-contiguous owners
+def check_accumulate_order(o):
+    """Accumulating into 1e8 the slots (1, -1e8, 1) one at a time gives 1 in fp32.
+
+    Adding the slot sum to the old value in one step would give 0 (1 - 1e8 + 1
+    rounds to -1e8), and leaving the old value out would give -1e8.
+    """
+    slots = [np.full((5,), v, dtype=np.float32) for v in (1.0, -1e8, 1.0)]
+    into = np.full((5,), 1e8, dtype=np.float32)
+    assert (o.slot_sum(slots, "f32", "f32", into=into) == np.float32(1.0)).all()
+    assert (into == np.float32(1e8)).all()  # the caller's array is not modified
+    cu = np.array([0, 6], dtype=np.int32)
+    grads = [np.full((6, 1, 1), v, dtype=np.float32) for v in (1.0, -1e8, 1.0)]
+    for pol in (o.DUAL_CHUNK_SWAP, o.PACKED_CONTIGUOUS):
+        into_o = [np.full((2, 1, 1), 1e8, dtype=np.float32) for _ in range(3)]
+        fused = o.grad_return_fused(grads, cu, 3, "f32", "f32", policy=pol, into=into_o)
+        _, out = o.grad_return(grads, cu, 3, "f32", "f32", policy=pol, into=into_o)
+        for owner in range(3):
+            assert (fused[owner] == np.float32(1.0)).all() and (out[owner] == np.float32(1.0)).all()
+
+
+def check_accumulate_integer(o):
+    """Old gradient 100(t+1) plus writers (w+1)(t+1): out = (t+1)(100 + W(W+1)/2), exact."""
+    g = golden()
+    cu = np.array(g["cu_seqlens"], dtype=np.int32)
+    T, H, D = 48, 2, 4
+    t = np.arange(T, dtype=np.float32)[:, None, None]
+    for W in (1, 2, 4):
+        grads = [np.broadcast_to((w + 1) * (t + 1), (T, H, D)).astype(np.float32) for w in range(W)]
+        for pol in (o.DUAL_CHUNK_SWAP, o.PACKED_CONTIGUOUS):
+            table = g[pol].get(str(W))
+            rows = [np.array(table["rows"][r]) if table else np.arange(T) for r in range(W)]
+            into = [np.broadcast_to(100 * (rows[r] + 1.0)[:, None, None], (T // W, H, D)).astype(np.float32)
+                    for r in range(W)]
+            want = [((rows[r] + 1) * (100 + W * (W + 1) // 2)).astype(np.float32)[:, None, None] for r in range(W)]
+            _, out = o.grad_return(grads, cu, W, "f32", "f32", policy=pol, into=into)
+            fused = o.grad_return_fused(grads, cu, W, "f32", "f32", policy=pol, into=into)
+            # bf16 writers (the integers are exact in bf16) into an fp32 gradient
+            gb = [o.f32_to_bf16_rne(x) for x in grads]
+            fused_b = o.grad_return_fused(gb, cu, W, "bf16", "f32", policy=pol, into=into)
+            for r in range(W):
+                for res in (out, fused, fused_b):
+                    assert (res[r] == want[r]).all(), (pol, W, r)
+    # bf16 into bf16: T = 8, W = 2, sums stay below 256 (exact in bf16)
+    cu8 = np.array([0, 8], dtype=np.int32)
+    t8 = np.arange(8, dtype=np.float32)[:, None, None]
+    grads = [o.f32_to_bf16_rne(np.broadcast_to((w + 1) * (t8 + 1), (8, 1, 2)).astype(np.float32)) for w in range(2)]
+    for pol in (o.DUAL_CHUNK_SWAP, o.PACKED_CONTIGUOUS):
+        rows = [o.rank_rows(cu8, 8, 2, pol, r) for r in range(2)]
+        into = [o.f32_to_bf16_rne(np.broadcast_to(4.0 * (rows[r] + 1)[:, None, None], (4, 1, 2)).astype(np.float32))
+                for r in range(2)]
+        res = o.grad_return_fused(grads, cu8, 2, "bf16", "bf16", policy=pol, into=into)
+        for r in range(2):
+            assert (o.bf16_to_f32(res[r][:, 0, 0]) == 7.0 * (rows[r] + 1)).all()
+
+
+def check_accumulate_signed_zero(o):
+    """-0 into -0 slots stays -0; +0 into -0 slots gives +0 (IEEE: +0 + -0 = +0)."""
+    for W in (1, 3):
+        slots = [np.full((3,), -0.0, dtype=np.float32) for _ in range(W)]
+        neg = o.slot_sum(slots, "f32", "f32", into=np.full((3,), -0.0, dtype=np.float32))
+        pos = o.slot_sum(slots, "f32", "f32", into=np.zeros((3,), dtype=np.float32))
+        assert (neg.view(np.uint32) == np.uint32(0x80000000)).all()
+        assert (pos.view(np.uint32) == np.uint32(0)).all()
+
+
+def check_pc_grad_return_is_reshape(o, seed=5):
+    """Under packed-contiguous, owner o's slot from writer w is rows [o n, (o+1) n) of G_w."""
+    rng = np.random.default_rng(seed)
+    for W, lengths in ((2, [3, 0, 9]), (3, [5, 1, 6]), (4, [16])):
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        T = int(cu[-1])
+        n = T // W
+        grads = [rng.standard_normal((T, 2, 3)).astype(np.float32) for _ in range(W)]
+        slots, out = o.grad_return(grads, cu, W, "f32", "f32", policy=o.PACKED_CONTIGUOUS)
+        fused = o.grad_return_fused(grads, cu, W, "f32", "f32", policy=o.PACKED_CONTIGUOUS)
+        for owner in range(W):
+            for w in range(W):
+                assert (slots[owner][w] == grads[w].reshape(W, n, 2, 3)[owner]).all()
+            # per element, brute force: the writers' values at global token owner*n + i, in order
+            for i in range(n):
+                for h in range(2):
+                    for d in range(3):
+                        acc = np.float32(grads[0][owner * n + i, h, d])
+                        for w in range(1, W):
+                            acc = np.float32(acc + grads[w][owner * n + i, h, d])
+                        assert out[owner][i, h, d].view(np.uint32) == acc.view(np.uint32)
+                        assert fused[owner][i, h, d].view(np.uint32) == acc.view(np.uint32)
+
+
 ALL_CHECKS = [
     check_handworked_dcs,
     check_handworked_pc,
@@ -329,4 +419,8 @@ ALL_CHECKS = [
     check_brute_force_grad_return,
     check_rank_row_matches_rank_rows,
     check_fused_equals_unfused,
+    check_accumulate_order,
+    check_accumulate_integer,
+    check_accumulate_signed_zero,
+    check_pc_grad_return_is_reshape,
 ]

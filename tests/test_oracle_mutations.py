@@ -85,7 +85,8 @@ def _dcs_local_cu_halved(o):
 
 
 def _sum_reversed(o):
-    def slot_sum(slots, in_dtype, out_dtype):
+    def slot_sum(slots, in_dtype, out_dtype, into=None):
+        slots = list(slots) if into is None else [into] + list(slots)
         acc = o._widen(slots[-1], in_dtype).astype(np.float32, copy=True)
         for w in range(len(slots) - 2, -1, -1):
             acc = (acc + o._widen(slots[w], in_dtype)).astype(np.float32)
@@ -94,8 +95,10 @@ def _sum_reversed(o):
 
 
 def _sum_zero_seed(o):
-    def slot_sum(slots, in_dtype, out_dtype):
+    def slot_sum(slots, in_dtype, out_dtype, into=None):
         acc = np.zeros(slots[0].shape, dtype=np.float32)
+        if into is not None:
+            acc = (acc + o._widen(into, out_dtype)).astype(np.float32)
         for s in slots:
             acc = (acc + o._widen(s, in_dtype)).astype(np.float32)
         return o._narrow(acc, out_dtype)
@@ -103,8 +106,10 @@ def _sum_zero_seed(o):
 
 
 def _sum_drops_last(o):
-    def slot_sum(slots, in_dtype, out_dtype):
+    def slot_sum(slots, in_dtype, out_dtype, into=None):
         acc = o._widen(slots[0], in_dtype).astype(np.float32, copy=True)
+        if into is not None:
+            acc = (o._widen(into, out_dtype) + acc).astype(np.float32)
         for w in range(1, len(slots) - 1):
             acc = (acc + o._widen(slots[w], in_dtype)).astype(np.float32)
         return o._narrow(acc, out_dtype)
@@ -128,27 +133,29 @@ def _bf16_half_up(o):
 
 
 def _scatter_transposed(o):
-    def grad_scatter(grads, cu, cp_size):
+    def grad_scatter(grads, cu, cp_size, policy=o.DUAL_CHUNK_SWAP):
         W = cp_size
         T = grads[0].shape[0]
         slots = [[None] * W for _ in range(W)]
         for w in range(W):
             for own in range(W):
-                slots[own][w] = grads[own][o.rank_rows(cu, T, W, o.DUAL_CHUNK_SWAP, w)]
+                slots[own][w] = grads[own][o.rank_rows(cu, T, W, policy, w)]
         return slots
     return grad_scatter
 
 
 def _fused_reversed(o):
-    def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype):
+    def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=o.DUAL_CHUNK_SWAP, into=None):
         W = cp_size
         T = grads[0].shape[0]
         out = []
         for own in range(W):
-            rows = o.rank_rows(cu, T, W, o.DUAL_CHUNK_SWAP, own)
+            rows = o.rank_rows(cu, T, W, policy, own)
             acc = o._widen(grads[W - 1][rows], in_dtype).astype(np.float32, copy=True)
             for w in range(W - 2, -1, -1):
                 acc = (acc + o._widen(grads[w][rows], in_dtype)).astype(np.float32)
+            if into is not None:
+                acc = (acc + o._widen(into[own], out_dtype)).astype(np.float32)
             out.append(o._narrow(acc, out_dtype))
         return out
     return grad_return_fused
@@ -169,6 +176,42 @@ def _pc_off_by_one(o):
     return pc_rank_rows
 
 
+def _acc_added_once(o):
+    orig = o.slot_sum
+
+    def slot_sum(slots, in_dtype, out_dtype, into=None):
+        if into is None:
+            return orig(slots, in_dtype, out_dtype)
+        total = orig(slots, in_dtype, "f32")
+        acc = (o._widen(into, out_dtype) + total).astype(np.float32)
+        return o._narrow(acc, out_dtype)
+    return slot_sum
+
+
+def _acc_ignored(o):
+    orig = o.grad_return_fused
+
+    def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=o.DUAL_CHUNK_SWAP, into=None):
+        return orig(grads, cu, cp_size, in_dtype, out_dtype, policy)
+    return grad_return_fused
+
+
+def _grad_policy_ignored(o):
+    orig = o.grad_scatter
+
+    def grad_scatter(grads, cu, cp_size, policy=o.DUAL_CHUNK_SWAP):
+        return orig(grads, cu, cp_size, o.DUAL_CHUNK_SWAP)
+    return grad_scatter
+
+
+def _fused_policy_ignored(o):
+    orig = o.grad_return_fused
+
+    def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=o.DUAL_CHUNK_SWAP, into=None):
+        return orig(grads, cu, cp_size, in_dtype, out_dtype, o.DUAL_CHUNK_SWAP, into)
+    return grad_return_fused
+
+
 MUTATIONS = {
     "dcs_swapped_chunks": ("dcs_rank_rows", _dcs_swapped_chunks),
     "dcs_wrong_mirror": ("dcs_rank_rows", _dcs_wrong_mirror),
@@ -184,6 +227,10 @@ MUTATIONS = {
     "fused_reversed": ("grad_return_fused", _fused_reversed),
     "no_decreasing_check": ("cu_violations", _no_decreasing_check),
     "pc_off_by_one": ("pc_rank_rows", _pc_off_by_one),
+    "accumulate_added_once": ("slot_sum", _acc_added_once),
+    "accumulate_ignored": ("grad_return_fused", _acc_ignored),
+    "grad_scatter_ignores_policy": ("grad_scatter", _grad_policy_ignored),
+    "fused_ignores_policy": ("grad_return_fused", _fused_policy_ignored),
 }
 
 INVARIANT_CASES = [
