@@ -294,6 +294,20 @@ def per_config(cp, WL, torch, dev, reps: int = 10):
 
         add(name, "grad return dK,dV (scatter, epochs, owner sums)", 2 * (3 * W + 1) * S * row_in,
             timed(unfused))
+        # accumulate mode: the owner's gradient is read as well (one more row per output row)
+        add(name, "fused grad return dK,dV, accumulate", 2 * (W + 2) * S * row_in,
+            timed(lambda: cp.cp_grad_return_fused(grads, out, meta, accumulate=True)))
+        # the same tensors under packed-contiguous ownership (owner o: tokens [o S/W, (o+1) S/W))
+        meta_pc = cp.cp_build_meta(cu, S, W, cp.CP_POLICY_PACKED_CONTIGUOUS, check=True)
+        add(name, "fused grad return dK,dV, packed-contiguous owners", 2 * (W + 1) * S * row_in,
+            timed(lambda: cp.cp_grad_return_fused(grads, out, meta_pc)))
+
+        def unfused_pc():
+            state["e"] += 1
+            cp.cp_grad_return(grads, slots, out, meta_pc, epochs=epochs, epoch=state["e"])
+
+        add(name, "grad return dK,dV, packed-contiguous owners", 2 * (3 * W + 1) * S * row_in,
+            timed(unfused_pc))
         del vals, grads, out, slots
         torch.cuda.empty_cache()
     del flush

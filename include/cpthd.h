@@ -100,6 +100,15 @@ enum cp_dtype {
 #define CP_PHASE_SUM     0x8
 #define CP_PHASE_ALL     0xF
 
+/* Accumulate mode of the owner-side sum, accepted in `phases` of cp_grad_return
+ * and in `flags` of cp_grad_return_fused and cp_slot_sum.  [GR] "Sequence
+ * Diagram" accumulates the writer slots 0..cp_size-1 "to dk"; read literally,
+ * one slot at a time into the owner's gradient:
+ *     out = (((out + s_0) + s_1) + ...) + s_{W-1}
+ * in fp32 (out widened first), rounded once to out_dtype.  Without the flag
+ * out is overwritten with ((s_0 + s_1) + ...) + s_{W-1}. */
+#define CP_SUM_ACCUMULATE 0x10
+
 /* ------------------------------------------------------------ metadata */
 /*
  * Device metadata built by cp_build_meta in a caller-allocated buffer of
@@ -130,7 +139,7 @@ enum cp_dtype {
 #define CP_CALL_BAD_MAGIC         0x0100 /* meta was never built                         */
 #define CP_CALL_TOKENS_MISMATCH   0x0200 /* total_tokens differs from the meta's          */
 #define CP_CALL_CP_SIZE_MISMATCH  0x0400 /* cp_size differs from the meta's               */
-#define CP_CALL_POLICY_MISMATCH   0x0800 /* grad return needs dual-chunk-swap metadata    */
+#define CP_CALL_POLICY_MISMATCH   0x0800 /* call needs the other policy (none does today) */
 #define CP_CALL_USED_INVALID_META 0x1000 /* a kernel met invalid metadata and did nothing */
 
 typedef struct cp_meta_header {
@@ -250,17 +259,22 @@ int cp_gather_thd_multi(int32_t n_tensors, const void* const* parts, void* const
  *                streams that map to distinct hardware queues: a wait that
  *                precedes another writer's publish in the same queue ends in
  *                CP_ERR_TIMEOUT (see `phases` for the split that avoids it).
- *   cp_size      W, must equal the meta's; the meta must be dual-chunk-swap
+ *   cp_size      W, must equal the meta's.  Either policy: owner o's rows
+ *                are those the partition gives rank o (the two-chunk layout
+ *                under dual-chunk-swap, tokens [o T/W, (o+1) T/W) under
+ *                packed-contiguous).
  *   n_tensors    number of gradient tensors per rank (2 for dK, dV), >= 1
  *   grads        host table [n_tensors][W] of device [T, H, D] `in_dtype`:
  *                writer w's global gradient of tensor t
  *   slots        host table [n_tensors][W owner][W writer] of device
  *                [T/W, H, D] `in_dtype`: the owner's receive slots
  *   out          host table [n_tensors][W owner] of device [T/W, H, D]
- *                `out_dtype`: overwritten with the sum (not accumulated into)
+ *                `out_dtype`: overwritten with the sum, or accumulated into
+ *                with CP_SUM_ACCUMULATE
  *   in_dtype/out_dtype  (CP_F32, CP_F32), (CP_F32, CP_BF16), (CP_BF16, CP_BF16),
  *                (CP_BF16, CP_F32)
- *   phases       CP_PHASE_* mask; phases run in the order scatter, publish,
+ *   phases       CP_PHASE_* mask (at least one phase), optionally with
+ *                CP_SUM_ACCUMULATE; phases run in the order scatter, publish,
  *                wait, sum.  CP_PHASE_ALL is the whole protocol.  A caller that
  *                drives several emulated ranks from one process may enqueue
  *                every rank's SCATTER|PUBLISH half before any rank's WAIT|SUM
@@ -276,14 +290,16 @@ int cp_gather_thd_multi(int32_t n_tensors, const void* const* parts, void* const
  *                timeout the owner's bit in meta wait_timeout_ranks is set and
  *                the owner's sum writes nothing (fail-closed).
  * Sum: out = ((s_0 + s_1) + s_2) + ... + s_{W-1} in fp32, s_w = widened slot w,
- * accumulator seeded with s_0, then rounded once to out_dtype (bf16:
+ * accumulator seeded with s_0 (with CP_SUM_ACCUMULATE: seeded with the widened
+ * out, then s_0 ... s_{W-1} added), then rounded once to out_dtype (bf16:
  * round-to-nearest-even).
  * In per-rank mode the call reads grads[t][rank], writes slots[t][o][rank] for
  * every o, reads slots[t][rank][*] and writes out[t][rank]; only those table
  * entries must be valid.
  * total_tokens == 0 is a no-op after the scalar checks (pointers may be NULL).
- * Errors: CP_ERR_ARG, CP_ERR_UNSUPPORTED (dtype pair), CP_ERR_DEVICE,
- * CP_ERR_ALIAS, CP_ERR_HIP; device-side mismatch or timeout as above.
+ * Errors: CP_ERR_ARG, CP_ERR_UNSUPPORTED (dtype pair), CP_ERR_SHAPE (T not a
+ * multiple of W), CP_ERR_DEVICE, CP_ERR_ALIAS, CP_ERR_HIP; device-side
+ * mismatch or timeout as above.
  */
 int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors,
                    const void* const* grads, void* const* slots, void* const* out,
@@ -301,12 +317,14 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors,
  *
  *   rank         CP_ALL_RANKS: every owner; 0..W-1: owner `rank` only (it reads
  *                all W writers' views, which must be complete in stream order)
+ *   flags        0 or CP_SUM_ACCUMULATE (seed the sum with the current out)
  *   other arguments as cp_grad_return; only grads[t][*] and out[t][o] used.
  */
 int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
                          const void* const* grads, void* const* out, int64_t total_tokens,
                          int32_t heads, int32_t head_dim, int32_t in_dtype,
-                         int32_t out_dtype, const void* meta, cp_stream_t stream);
+                         int32_t out_dtype, const void* meta, int32_t flags,
+                         cp_stream_t stream);
 
 /*
  * cp_slot_sum - out[k] = ((s_0[k] + s_1[k]) + ...) + s_{W-1}[k] in fp32, for
@@ -316,10 +334,11 @@ int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
  *   slots        host table [W] of device buffers of n_elems `in_dtype`
  *   out          device buffer of n_elems `out_dtype`
  *   dtype pairs  as cp_grad_return
+ *   flags        0 or CP_SUM_ACCUMULATE (out = ((out + s_0) + ...) + s_{W-1})
  * n_elems == 0 is a no-op (pointers may then be NULL).
  */
 int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t n_elems,
-                int32_t in_dtype, int32_t out_dtype, cp_stream_t stream);
+                int32_t in_dtype, int32_t out_dtype, int32_t flags, cp_stream_t stream);
 
 /* ------------------------------------------------------------ utilities */
 /* Static text for a status code (never NULL). */

@@ -113,32 +113,36 @@ def test_host_checks_before_any_hip_call(cp):
         == cp.CP_ERR_UNSUPPORTED
     assert gr(2, 2, 2, tab, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0, 15, None) \
         == cp.CP_ERR_ARG
-    assert gr(-1, 4, 2, tab, tab, tab, 20, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0, 15, None) \
+    assert gr(-1, 4, 2, tab, tab, tab, 22, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0, 15, None) \
         == cp.CP_ERR_SHAPE
     assert gr(0, 2, 2, tab, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0, 15, None) \
         == cp.CP_ERR_ARG
     assert gr(-1, 2, 0, tab, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0, 15, None) \
         == cp.CP_ERR_ARG
-    for bad_phases in (0, 0x10, -1):
+    for bad_phases in (0, cp.CP_SUM_ACCUMULATE, 0x20 | cp.CP_PHASE_ALL, -1):
         assert gr(-1, 2, 2, tab, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0,
                   bad_phases, None) == cp.CP_ERR_ARG
     # empty input is a no-op before any pointer is looked at
     assert gr(-1, 2, 2, None, None, None, 0, 2, 8, cp.CP_F32, cp.CP_F32, None, None, 0, 0, 15, None) \
         == cp.CP_OK
     assert lib.cp_partition_thd(None, None, 0, 2, 8, cp.CP_BF16, None, None) == cp.CP_OK
-    assert lib.cp_slot_sum(4, None, None, 0, cp.CP_F32, cp.CP_F32, None) == cp.CP_OK
+    assert lib.cp_slot_sum(4, None, None, 0, cp.CP_F32, cp.CP_F32, 0, None) == cp.CP_OK
+    assert lib.cp_slot_sum(4, None, None, 0, cp.CP_F32, cp.CP_F32, cp.CP_SUM_ACCUMULATE, None) == cp.CP_OK
     nulls = (ctypes.c_void_p * 64)()
     assert gr(-1, 2, 2, nulls, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0, 15, None) \
         == cp.CP_ERR_ARG
     fu = lib.cp_grad_return_fused
-    assert fu(-1, 2, 2, tab, tab, 48, 2, 8, cp.CP_F16, cp.CP_F16, FAKE, None) == cp.CP_ERR_UNSUPPORTED
-    assert fu(-1, 65, 2, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None) == cp.CP_ERR_ARG
-    assert fu(-1, 2, 2, nulls, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None) == cp.CP_ERR_ARG
+    assert fu(-1, 2, 2, tab, tab, 48, 2, 8, cp.CP_F16, cp.CP_F16, FAKE, 0, None) == cp.CP_ERR_UNSUPPORTED
+    assert fu(-1, 65, 2, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, 0, None) == cp.CP_ERR_ARG
+    assert fu(-1, 2, 2, nulls, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, 0, None) == cp.CP_ERR_ARG
+    assert fu(-1, 2, 2, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, 0x20, None) == cp.CP_ERR_ARG
+    assert fu(-1, 4, 2, tab, tab, 22, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, 0, None) == cp.CP_ERR_SHAPE
     ss = lib.cp_slot_sum
-    assert ss(0, tab, FAKE, 10, cp.CP_F32, cp.CP_F32, None) == cp.CP_ERR_ARG
-    assert ss(65, tab, FAKE, 10, cp.CP_F32, cp.CP_F32, None) == cp.CP_ERR_ARG
-    assert ss(2, tab, FAKE, 10, cp.CP_F32, cp.CP_F16, None) == cp.CP_ERR_UNSUPPORTED
-    assert ss(2, nulls, FAKE, 10, cp.CP_F32, cp.CP_F32, None) == cp.CP_ERR_ARG
+    assert ss(0, tab, FAKE, 10, cp.CP_F32, cp.CP_F32, 0, None) == cp.CP_ERR_ARG
+    assert ss(65, tab, FAKE, 10, cp.CP_F32, cp.CP_F32, 0, None) == cp.CP_ERR_ARG
+    assert ss(2, tab, FAKE, 10, cp.CP_F32, cp.CP_F16, 0, None) == cp.CP_ERR_UNSUPPORTED
+    assert ss(2, nulls, FAKE, 10, cp.CP_F32, cp.CP_F32, 0, None) == cp.CP_ERR_ARG
+    assert ss(2, tab, FAKE, 10, cp.CP_F32, cp.CP_F32, 0x20, None) == cp.CP_ERR_ARG
 
 
 def test_library_has_no_oracle_dependency():

@@ -422,11 +422,11 @@ def test_epoch_timeout_is_reported_not_hung(cp):
 def test_grad_return_rejects_mismatch(cp):
     cu = np.array([0, 64], dtype=np.int32)
     grads = [[torch.randn((64, 1, 8), device=DEV) for _ in range(2)]]
-    pc = cp.cp_build_meta(torch.from_numpy(cu).to(DEV), 64, 2, cp.CP_POLICY_PACKED_CONTIGUOUS, check=True)
+    m128 = make_meta(cp, np.array([0, 128], dtype=np.int32), 128, 2)  # built for another token count
     slots, out = alloc(grads, 2, torch.float32, fill=3.0)
-    cp.cp_grad_return(grads, slots, out, pc)
-    st, flags, _ = cp.cp_meta_status(pc)
-    assert st == cp.CP_ERR_META and flags & cp.CP_CALL_POLICY_MISMATCH
+    cp.cp_grad_return(grads, slots, out, m128)
+    st, flags, _ = cp.cp_meta_status(m128)
+    assert st == cp.CP_ERR_META and flags & cp.CP_CALL_TOKENS_MISMATCH
     assert (out[0][0] == 3.0).all() and (slots[0][0][1] == 3.0).all()
     m4 = make_meta(cp, cu, 64, 4)
     fused = [[torch.full((32, 1, 8), 3.0, device=DEV) for _ in range(2)]]

@@ -32,6 +32,7 @@ CP_ALL_RANKS = -1
 CP_MAX_CP_SIZE = 64
 CP_PHASE_SCATTER, CP_PHASE_PUBLISH, CP_PHASE_WAIT, CP_PHASE_SUM = 0x1, 0x2, 0x4, 0x8
 CP_PHASE_ALL = 0xF
+CP_SUM_ACCUMULATE = 0x10
 CP_META_MAGIC = 0x48545043
 CP_META_FIRST_NOT_ZERO = 0x0001
 CP_META_DECREASING = 0x0002
@@ -72,9 +73,9 @@ lib.cp_grad_return.argtypes = [_i32, _i32, _i32, _c.POINTER(_vp), _c.POINTER(_vp
                                _i64, _i32, _i32, _i32, _i32, _vp, _vp, _u32, _i64, _i32, _vp]
 lib.cp_grad_return_fused.restype = _c.c_int
 lib.cp_grad_return_fused.argtypes = [_i32, _i32, _i32, _c.POINTER(_vp), _c.POINTER(_vp), _i64, _i32,
-                                     _i32, _i32, _i32, _vp, _vp]
+                                     _i32, _i32, _i32, _vp, _i32, _vp]
 lib.cp_slot_sum.restype = _c.c_int
-lib.cp_slot_sum.argtypes = [_i32, _c.POINTER(_vp), _vp, _i64, _i32, _i32, _vp]
+lib.cp_slot_sum.argtypes = [_i32, _c.POINTER(_vp), _vp, _i64, _i32, _i32, _i32, _vp]
 lib.cp_status_string.restype = _c.c_char_p
 lib.cp_status_string.argtypes = [_c.c_int]
 lib.cp_version.restype = _c.c_int
@@ -275,8 +276,9 @@ def _flat3(tab):
 def cp_grad_return(grads: Sequence[Sequence[torch.Tensor]], slots, out, meta: Meta,
                    rank: int = CP_ALL_RANKS, epochs: Optional[torch.Tensor] = None,
                    epoch: int = 0, wait_timeout_us: int = 0, phases: int = CP_PHASE_ALL,
-                   stream=None) -> None:
-    """grads[t][w] [T,H,D]; slots[t][o][w] [T/W,H,D]; out[t][o] [T/W,H,D] (overwritten)."""
+                   accumulate: bool = False, stream=None) -> None:
+    """grads[t][w] [T,H,D]; slots[t][o][w] [T/W,H,D]; out[t][o] [T/W,H,D] (overwritten, or
+    accumulated into when `accumulate`)."""
     n_tensors = len(grads)
     W = len(grads[0])
     ref = next(g for g in _flat2(grads) if g is not None)
@@ -285,11 +287,13 @@ def cp_grad_return(grads: Sequence[Sequence[torch.Tensor]], slots, out, meta: Me
     st = lib.cp_grad_return(int(rank), W, n_tensors, _table(_flat2(grads)), _table(_flat3(slots)),
                             _table(_flat2(out)), T, H, D, dtype_code(ref.dtype),
                             dtype_code(out_ref.dtype), meta.ptr(), _ptr(epochs), int(epoch),
-                            int(wait_timeout_us), int(phases), _stream(stream, ref))
+                            int(wait_timeout_us), int(phases) | (CP_SUM_ACCUMULATE if accumulate else 0),
+                            _stream(stream, ref))
     _check(st, "cp_grad_return")
 
 
-def cp_grad_return_fused(grads, out, meta: Meta, rank: int = CP_ALL_RANKS, stream=None) -> None:
+def cp_grad_return_fused(grads, out, meta: Meta, rank: int = CP_ALL_RANKS, accumulate: bool = False,
+                         stream=None) -> None:
     n_tensors = len(grads)
     W = len(grads[0])
     ref = next(g for g in _flat2(grads) if g is not None)
@@ -297,13 +301,15 @@ def cp_grad_return_fused(grads, out, meta: Meta, rank: int = CP_ALL_RANKS, strea
     out_ref = next(o for o in _flat2(out) if o is not None)
     st = lib.cp_grad_return_fused(int(rank), W, n_tensors, _table(_flat2(grads)), _table(_flat2(out)),
                                   T, H, D, dtype_code(ref.dtype), dtype_code(out_ref.dtype),
-                                  meta.ptr(), _stream(stream, ref))
+                                  meta.ptr(), CP_SUM_ACCUMULATE if accumulate else 0, _stream(stream, ref))
     _check(st, "cp_grad_return_fused")
 
 
-def cp_slot_sum(slots: Sequence[torch.Tensor], out: torch.Tensor, stream=None) -> torch.Tensor:
+def cp_slot_sum(slots: Sequence[torch.Tensor], out: torch.Tensor, accumulate: bool = False,
+                stream=None) -> torch.Tensor:
     st = lib.cp_slot_sum(len(slots), _table(slots), _ptr(out), out.numel(),
-                         dtype_code(slots[0].dtype), dtype_code(out.dtype), _stream(stream, out))
+                         dtype_code(slots[0].dtype), dtype_code(out.dtype),
+                         CP_SUM_ACCUMULATE if accumulate else 0, _stream(stream, out))
     _check(st, "cp_slot_sum")
     return out
 

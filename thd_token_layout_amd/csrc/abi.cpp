@@ -291,7 +291,9 @@ static int grad_scalar_checks(int32_t rank, int32_t cp_size, int32_t n_tensors, 
   if (rank != CP_ALL_RANKS && (rank < 0 || rank >= cp_size)) return CP_ERR_ARG;
   if (n_tensors < 1) return CP_ERR_ARG;
   if (total_tokens < 0 || total_tokens > INT32_MAX || heads < 1 || head_dim < 1) return CP_ERR_ARG;
-  if (total_tokens % (2 * (int64_t)cp_size) != 0) return CP_ERR_SHAPE;
+  // T % W under either policy; dual-chunk-swap metadata also guarantees T % 2W
+  // (every document is a multiple of 2W), which the kernels check on the device.
+  if (total_tokens % (int64_t)cp_size != 0) return CP_ERR_SHAPE;
   if (total_tokens > 0 && meta == nullptr) return CP_ERR_ARG;
   return CP_OK;
 }
@@ -305,7 +307,7 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
   if ((st = grad_scalar_checks(rank, cp_size, n_tensors, total_tokens, heads, head_dim, in_dtype,
                                out_dtype, meta)) != CP_OK)
     return st;
-  if (phases <= 0 || (phases & ~CP_PHASE_ALL) != 0) return CP_ERR_ARG;
+  if ((phases & CP_PHASE_ALL) == 0 || (phases & ~(CP_PHASE_ALL | CP_SUM_ACCUMULATE)) != 0) return CP_ERR_ARG;
   const bool all = rank == CP_ALL_RANKS;
   if (!all && epochs == nullptr) return CP_ERR_ARG;
   if (total_tokens == 0) return CP_OK;  // nothing to move; empty tensors may have NULL data
@@ -380,7 +382,7 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
       a.total_tokens = total_tokens;
       a.row_bytes = in_row;
       a.expect_cp_size = W;
-      a.expect_policy = CP_POLICY_DUAL_CHUNK_SWAP;
+      a.expect_policy = -1;  // the owner's rows follow the metadata's policy
       if ((st = hip_status(launch_permute(a, s))) != CP_OK) return st;
     }
   }
@@ -401,7 +403,7 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
         (st = hip_status(launch_epoch_wait(epochs, W, all ? -1 : rank, epoch, ticks, h, s))) != CP_OK)
       return st;
   }
-  // 4. owner o: out = slot 0 + slot 1 + ... + slot W-1
+  // 4. owner o: out = slot 0 + slot 1 + ... + slot W-1 (after out itself when accumulating)
   for (int t = 0; t < n_tensors && (phases & CP_PHASE_SUM); ++t) {
     for (int o = o_lo; o < o_hi; ++o) {
       SlotSumArgs a;
@@ -415,6 +417,7 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
       a.gate_meta = h;
       a.gate_T = total_tokens;
       a.owner = epochs ? o : -1;
+      a.accumulate = (phases & CP_SUM_ACCUMULATE) != 0;
       if ((st = hip_status(launch_slot_sum(a, s))) != CP_OK) return st;
     }
   }
@@ -424,11 +427,12 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
 int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
                          const void* const* grads, void* const* out, int64_t total_tokens,
                          int32_t heads, int32_t head_dim, int32_t in_dtype, int32_t out_dtype,
-                         const void* meta, cp_stream_t stream) {
+                         const void* meta, int32_t flags, cp_stream_t stream) {
   int st;
   if ((st = grad_scalar_checks(rank, cp_size, n_tensors, total_tokens, heads, head_dim, in_dtype,
                                out_dtype, meta)) != CP_OK)
     return st;
+  if ((flags & ~CP_SUM_ACCUMULATE) != 0) return CP_ERR_ARG;
   if (total_tokens == 0) return CP_OK;  // nothing to move; empty tensors may have NULL data
   if (grads == nullptr || out == nullptr) return CP_ERR_ARG;
   const int W = cp_size;
@@ -476,16 +480,18 @@ int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
     a.row_elems = row_elems;
     a.in_dtype = in_dtype;
     a.out_dtype = out_dtype;
+    a.accumulate = (flags & CP_SUM_ACCUMULATE) != 0;
     if ((st = hip_status(launch_fused(a, s))) != CP_OK) return st;
   }
   return CP_OK;
 }
 
 int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t n_elems,
-                int32_t in_dtype, int32_t out_dtype, cp_stream_t stream) {
+                int32_t in_dtype, int32_t out_dtype, int32_t flags, cp_stream_t stream) {
   int st;
   if ((st = check_sum_dtypes(in_dtype, out_dtype)) != CP_OK) return st;
   if (num_slots < 1 || num_slots > CP_MAX_CP_SIZE || n_elems < 0) return CP_ERR_ARG;
+  if ((flags & ~CP_SUM_ACCUMULATE) != 0) return CP_ERR_ARG;
   if (n_elems == 0) return CP_OK;
   if (slots == nullptr || out == nullptr) return CP_ERR_ARG;
   for (int w = 0; w < num_slots; ++w)
@@ -509,6 +515,7 @@ int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t 
   a.out_dtype = out_dtype;
   a.gate_meta = nullptr;
   a.owner = -1;
+  a.accumulate = (flags & CP_SUM_ACCUMULATE) != 0;
   return hip_status(launch_slot_sum(a, reinterpret_cast<hipStream_t>(stream)));
 }
 

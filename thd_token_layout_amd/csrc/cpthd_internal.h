@@ -78,12 +78,13 @@ struct SlotSumArgs {
   int32_t in_dtype;
   int32_t out_dtype;
   // Optional fail-closed gate (gradient return): when gate_meta is set the
-  // kernel writes nothing unless the meta is valid dual-chunk-swap metadata
-  // for gate_T tokens and num_slots ranks, and, when owner >= 0, bit `owner`
-  // of meta->wait_timeout_ranks is clear.
+  // kernel writes nothing unless the meta is valid metadata for gate_T tokens
+  // and num_slots ranks, and, when owner >= 0, bit `owner` of
+  // meta->wait_timeout_ranks is clear.
   cp_meta_header* gate_meta;
   int64_t gate_T;
   int32_t owner;
+  int32_t accumulate;  // nonzero: out = ((out + s_0) + s_1) + ... (out read first)
 };
 hipError_t launch_slot_sum(const SlotSumArgs& a, hipStream_t stream);
 
@@ -100,6 +101,7 @@ struct FusedArgs {
   int64_t row_elems;
   int32_t in_dtype;
   int32_t out_dtype;
+  int32_t accumulate;  // nonzero: the owner's current out seeds the sum
 };
 hipError_t launch_fused(const FusedArgs& a, hipStream_t stream);
 

@@ -65,4 +65,12 @@ __device__ __forceinline__ int64_t dcs_global_row(int32_t r, int64_t i, int32_t 
   return j < c ? cu[b] + (int64_t)r * c + j : cu[b] + (int64_t)(2 * W - 1 - r) * c + (j - c);
 }
 
+// Global row of owner r's local row i under the metadata's policy: the
+// dual-chunk-swap map above, or r n + i under packed-contiguous (n = T / W).
+__device__ __forceinline__ int64_t owner_global_row(int32_t policy, int32_t r, int64_t i, int64_t n,
+                                                    int32_t W, int32_t B, const int32_t* cu,
+                                                    const int32_t* lcu) {
+  return policy == CP_POLICY_DUAL_CHUNK_SWAP ? dcs_global_row(r, i, W, B, cu, lcu) : (int64_t)r * n + i;
+}
+
 }  // namespace cpthd

@@ -140,7 +140,9 @@ __device__ __forceinline__ void store_elem(char* base, int64_t k, float f) {
 // of WB slots (for all UPT units) are issued before that batch's adds, which
 // then run in slot order.  `in` is the kernel argument table (uniform), off[u]
 // a byte offset applied to every slot for unit u, ok[u] masks units past the end.
-template <int IN, bool SPLIT, int WB, int UPT>
+// Without ACC the accumulator is seeded with slot 0; with ACC the caller has
+// seeded it (with the owner's current values) and every slot is added.
+template <int IN, bool SPLIT, int WB, int UPT, bool ACC>
 __device__ __forceinline__ void sum_units(F8 (&acc)[UPT], const ConstRankPtrs& in, int W,
                                           const int64_t (&off)[UPT], const int64_t (&unit)[UPT],
                                           const bool (&ok)[UPT]) {
@@ -153,8 +155,13 @@ __device__ __forceinline__ void sum_units(F8 (&acc)[UPT], const ConstRankPtrs& i
         if (ok[u] && w < W) load_unit<IN, SPLIT>(x[u][w], in.p[w] + off[u], unit[u]);
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
+      if constexpr (ACC) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[u].v[e] = x[u][0].v[e];
+        for (int e = 0; e < 8; ++e) acc[u].v[e] = acc[u].v[e] + x[u][0].v[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[u].v[e] = x[u][0].v[e];
+      }
 #pragma unroll
       for (int w = 1; w < WB; ++w)
         if (w < W) {
@@ -181,15 +188,25 @@ __device__ __forceinline__ void sum_units(F8 (&acc)[UPT], const ConstRankPtrs& i
   }
 }
 
-// Gradient-return kernels need valid dual-chunk-swap metadata for W ranks.
+// Seed of the accumulate mode: the owner's current values, widened to fp32.
+template <int OUT, bool SPLIT, int UPT>
+__device__ __forceinline__ void seed_units(F8 (&acc)[UPT], const char* out, const int64_t (&unit)[UPT],
+                                           const bool (&ok)[UPT]) {
+#pragma unroll
+  for (int u = 0; u < UPT; ++u)
+    if (ok[u]) load_unit<OUT, SPLIT>(acc[u], out, unit[u]);
+}
+
+// Gradient-return kernels need metadata built for W ranks and T tokens (either
+// policy: the owner's rows are those the partition gives it).
 __device__ __forceinline__ bool grad_meta_ok(cp_meta_header* h, int64_t T, int32_t W) {
-  return meta_ok(h, T, W, CP_POLICY_DUAL_CHUNK_SWAP);
+  return meta_ok(h, T, W, -1);
 }
 
 // ---- slot sum ----------------------------------------------------------------
 // A workgroup owns a tile of kBlock*UPT consecutive 8-element units; thread t
 // takes units t, t + kBlock, ... of the tile (coalesced per load instruction).
-template <int IN, int OUT, int WB, bool VEC, int UPT>
+template <int IN, int OUT, int WB, bool VEC, int UPT, bool ACC>
 __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
   if (a.gate_meta != nullptr) {
     cp_meta_header* h = a.gate_meta;
@@ -212,7 +229,8 @@ __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
         off[u] = 0;
       }
       F8 acc[UPT];
-      sum_units<IN, SPLIT, WB, UPT>(acc, a.in, W, off, unit, ok);
+      if constexpr (ACC) seed_units<OUT, SPLIT, UPT>(acc, a.out, unit, ok);
+      sum_units<IN, SPLIT, WB, UPT, ACC>(acc, a.in, W, off, unit, ok);
 #pragma unroll
       for (int u = 0; u < UPT; ++u)
         if (ok[u]) store_unit<OUT, SPLIT>(a.out, unit[u], acc[u]);
@@ -222,19 +240,19 @@ __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
   const int64_t gtid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   const int64_t gstride = (int64_t)gridDim.x * kBlock;
   for (int64_t k = done + gtid; k < a.n_elems; k += gstride) {
-    float acc = load_elem<IN>(a.in.p[0], k);
+    float acc = ACC ? load_elem<OUT>(a.out, k) + load_elem<IN>(a.in.p[0], k) : load_elem<IN>(a.in.p[0], k);
     for (int w = 1; w < W; ++w) acc = acc + load_elem<IN>(a.in.p[w], k);
     store_elem<OUT>(a.out, k, acc);
   }
 }
 
 // ---- fused scatter + sum ---------------------------------------------------
-// Owner o's local row i reads global row dcs_global_row(o, i) of every writer.
+// Owner o's local row i reads global row owner_global_row(o, i) of every writer.
 
 // A workgroup owns (4 / WPR) output rows; WPR waves share a row, each taking
 // column passes of 64*UPL units (8 elements each) so a lane has UPL*W loads in
 // flight per pass.
-template <int IN, int OUT, int WB, bool VEC, int WPR, int UPL>
+template <int IN, int OUT, int WB, bool VEC, int WPR, int UPL, bool ACC>
 __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
   constexpr int kRowsPerTile = kWavesPerBlock / WPR;
   cp_meta_header* h = a.meta;
@@ -259,7 +277,7 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
     if (q >= rows) continue;
     const int32_t o = a.owner_begin + (int32_t)(q / n);
     const int64_t i = q - (int64_t)(o - a.owner_begin) * n;
-    const int64_t g = dcs_global_row(o, i, W, B, cu, lcu);
+    const int64_t g = owner_global_row(h->policy, o, i, n, W, B, cu, lcu);
     const int64_t src_off = g * a.row_elems * in_bytes;  // same row in every writer's view
     char* row_dst = a.out.p[o] + i * a.row_elems * out_bytes;
     if constexpr (VEC) {
@@ -274,14 +292,16 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
           off[m] = src_off;
         }
         F8 acc[UPL];
-        sum_units<IN, split_layout<IN, OUT>(), WB, UPL>(acc, a.grads, W, off, unit, ok);
+        if constexpr (ACC) seed_units<OUT, split_layout<IN, OUT>(), UPL>(acc, row_dst, unit, ok);
+        sum_units<IN, split_layout<IN, OUT>(), WB, UPL, ACC>(acc, a.grads, W, off, unit, ok);
 #pragma unroll
         for (int m = 0; m < UPL; ++m)
           if (ok[m]) store_unit<OUT, split_layout<IN, OUT>()>(row_dst, unit[m], acc[m]);
       }
     } else if (chunk == 0) {
       for (int64_t k = lane; k < a.row_elems; k += 64) {
-        float acc = load_elem<IN>(a.grads.p[0] + src_off, k);
+        float acc = ACC ? load_elem<OUT>(row_dst, k) + load_elem<IN>(a.grads.p[0] + src_off, k)
+                        : load_elem<IN>(a.grads.p[0] + src_off, k);
         for (int w = 1; w < W; ++w) acc = acc + load_elem<IN>(a.grads.p[w] + src_off, k);
         store_elem<OUT>(row_dst, k, acc);
       }
@@ -299,7 +319,7 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
 // exact while the in-tile offset times units_per_row stays below 2^32.
 constexpr int kMaxTileRows = 16;
 
-template <int IN, int OUT, int WB, int NP>
+template <int IN, int OUT, int WB, int NP, bool ACC>
 __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_t upr_magic) {
   __shared__ int64_t s_src[kMaxTileRows];
   __shared__ char* s_dst[kMaxTileRows];
@@ -327,7 +347,7 @@ __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_
       const int64_t q = row0 + threadIdx.x;
       const int32_t o = a.owner_begin + (int32_t)(q / n);
       const int64_t i = q - (int64_t)(o - a.owner_begin) * n;
-      s_src[threadIdx.x] = dcs_global_row(o, i, W, B, cu, lcu) * a.row_elems * in_bytes;
+      s_src[threadIdx.x] = owner_global_row(h->policy, o, i, n, W, B, cu, lcu) * a.row_elems * in_bytes;
       s_dst[threadIdx.x] = a.out.p[o] + i * a.row_elems * out_bytes;
     }
     __syncthreads();
@@ -344,7 +364,12 @@ __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_
       off[m] = s_src[row[m]];
     }
     F8 acc[NP];
-    sum_units<IN, split_layout<IN, OUT>(), WB, NP>(acc, a.grads, W, off, unit, ok);
+    if constexpr (ACC) {
+#pragma unroll
+      for (int m = 0; m < NP; ++m)
+        if (ok[m]) load_unit<OUT, split_layout<IN, OUT>()>(acc[m], s_dst[row[m]], unit[m]);
+    }
+    sum_units<IN, split_layout<IN, OUT>(), WB, NP, ACC>(acc, a.grads, W, off, unit, ok);
 #pragma unroll
     for (int m = 0; m < NP; ++m)
       if (ok[m]) store_unit<OUT, split_layout<IN, OUT>()>(s_dst[row[m]], unit[m], acc[m]);
@@ -421,13 +446,12 @@ constexpr int kFusedWpr = 4;
 // bf16) shapes: flat unit tiles, 2 units per thread for W <= 4 (6.20 TB/s,
 // against 6.05 for a wave per row), 1 unit per thread above.
 
-template <int IN, int OUT, int WB>
+template <int IN, int OUT, int WB, bool ACC>
 hipError_t launch_sum_wb(const SlotSumArgs& a, bool vec, hipStream_t stream) {
   constexpr int UPT = sum_upt(IN, WB);
-  static const std::string names[2] = {
-      std::string("slot_sum<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," + std::to_string(WB) + ",s>",
-      std::string("slot_sum<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," + std::to_string(WB) + ",v" +
-          std::to_string(UPT) + ">"};
+  const std::string tag = std::string(ACC ? "slot_sum_acc<" : "slot_sum<") + dtype_tag(IN) + "," +
+                          dtype_tag(OUT) + "," + std::to_string(WB) + ",";
+  static const std::string names[2] = {tag + "s>", tag + "v" + std::to_string(UPT) + ">"};
   int64_t blocks;
   if (vec) {
     constexpr int64_t G = unit_group_elems<IN, OUT>();
@@ -442,29 +466,35 @@ hipError_t launch_sum_wb(const SlotSumArgs& a, bool vec, hipStream_t stream) {
   if (blocks < 1) blocks = 1;
   profile_before(names[vec ? 1 : 0].c_str(), stream);
   if (vec)
-    hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, true, UPT>), dim3((unsigned)blocks), dim3(kBlock), 0,
+    hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, true, UPT, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0,
                        stream, a);
   else
-    hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, false, 1>), dim3((unsigned)blocks), dim3(kBlock), 0,
+    hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, false, 1, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0,
                        stream, a);
   hipError_t e = hipGetLastError();
   profile_after(stream);
   return e;
 }
 
-template <int IN, int OUT>
-hipError_t launch_sum_typed(const SlotSumArgs& a, bool vec, hipStream_t stream) {
+template <int IN, int OUT, bool ACC>
+hipError_t launch_sum_acc(const SlotSumArgs& a, bool vec, hipStream_t stream) {
   const int W = a.num_slots;
-  if (W <= 1) return launch_sum_wb<IN, OUT, 1>(a, vec, stream);
-  if (W <= 2) return launch_sum_wb<IN, OUT, 2>(a, vec, stream);
-  if (W <= 4) return launch_sum_wb<IN, OUT, 4>(a, vec, stream);
-  return launch_sum_wb<IN, OUT, 8>(a, vec, stream);
+  if (W <= 1) return launch_sum_wb<IN, OUT, 1, ACC>(a, vec, stream);
+  if (W <= 2) return launch_sum_wb<IN, OUT, 2, ACC>(a, vec, stream);
+  if (W <= 4) return launch_sum_wb<IN, OUT, 4, ACC>(a, vec, stream);
+  return launch_sum_wb<IN, OUT, 8, ACC>(a, vec, stream);
 }
 
-template <int IN, int OUT, int WB>
+template <int IN, int OUT>
+hipError_t launch_sum_typed(const SlotSumArgs& a, bool vec, hipStream_t stream) {
+  return a.accumulate ? launch_sum_acc<IN, OUT, true>(a, vec, stream)
+                      : launch_sum_acc<IN, OUT, false>(a, vec, stream);
+}
+
+template <int IN, int OUT, int WB, bool ACC>
 hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
-  const std::string tag = std::string("fused_grad_return<") + dtype_tag(IN) + "," + dtype_tag(OUT) + "," +
-                          std::to_string(WB) + ",";
+  const std::string tag = std::string(ACC ? "fused_grad_return_acc<" : "fused_grad_return<") + dtype_tag(IN) +
+                          "," + dtype_tag(OUT) + "," + std::to_string(WB) + ",";
   static const std::string names[4] = {tag + "s>", tag + "flat1>", tag + "flat2>",
                                        tag + "v" + std::to_string(fused_upl(IN, WB)) + "/" +
                                            std::to_string(kFusedWpr) + ">"};
@@ -491,16 +521,16 @@ hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
   const uint32_t magic = upr > 0 ? (uint32_t)(((uint64_t(1) << 32) + (uint64_t)upr - 1) / (uint64_t)upr) : 0;
   profile_before(names[kind].c_str(), stream);
   if (kind == 1) {
-    hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, 1>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, a,
-                       magic);
+    hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, 1, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0, stream,
+                       a, magic);
   } else if (kind == 2) {
-    hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, 2>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, a,
-                       magic);
+    hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, 2, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0, stream,
+                       a, magic);
   } else if (kind == 3) {
-    hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, true, kFusedWpr, fused_upl(IN, WB)>), dim3((unsigned)blocks),
-                       dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, true, kFusedWpr, fused_upl(IN, WB), ACC>),
+                       dim3((unsigned)blocks), dim3(kBlock), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, false, 1, 1>), dim3((unsigned)blocks), dim3(kBlock), 0,
+    hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, false, 1, 1, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0,
                        stream, a);
   }
   hipError_t e = hipGetLastError();
@@ -510,12 +540,18 @@ hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
 
 // Writers are summed in batches of at most 4 (W = 8 bf16 measured 6.08 TB/s
 // with two batches of 4, 5.03 TB/s with one batch of 8: register pressure).
+template <int IN, int OUT, bool ACC>
+hipError_t launch_fused_acc(const FusedArgs& a, bool vec, hipStream_t stream) {
+  const int W = a.cp_size;
+  if (W <= 1) return launch_fused_wb<IN, OUT, 1, ACC>(a, vec, stream);
+  if (W <= 2) return launch_fused_wb<IN, OUT, 2, ACC>(a, vec, stream);
+  return launch_fused_wb<IN, OUT, 4, ACC>(a, vec, stream);
+}
+
 template <int IN, int OUT>
 hipError_t launch_fused_typed(const FusedArgs& a, bool vec, hipStream_t stream) {
-  const int W = a.cp_size;
-  if (W <= 1) return launch_fused_wb<IN, OUT, 1>(a, vec, stream);
-  if (W <= 2) return launch_fused_wb<IN, OUT, 2>(a, vec, stream);
-  return launch_fused_wb<IN, OUT, 4>(a, vec, stream);
+  return a.accumulate ? launch_fused_acc<IN, OUT, true>(a, vec, stream)
+                      : launch_fused_acc<IN, OUT, false>(a, vec, stream);
 }
 
 }  // namespace
