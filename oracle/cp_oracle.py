@@ -43,7 +43,13 @@ Readings where the pages are silent (the design notes list them all):
   * the gradient return follows the metadata's policy: under packed-contiguous
     owner o's rows are its contiguous slice, as in the partition;
   * fp32 -> bf16 is round-to-nearest-even on the bit pattern; NaN stays a
-    quiet NaN with its sign; denormals are kept.
+    quiet NaN with its sign; denormals are kept;
+  * attention after the all-gather is causal inside each document (token t
+    sees token s when they share a document and s <= t), keys in global
+    order; a dual-chunk-swap rank runs step 0 on chunk r and step 1 on chunk
+    2W-1-r of every document, each against the document's prefix up to the
+    chunk's end; a packed-contiguous rank runs one step in which every local
+    segment sees its document from the first token on.
 
 bf16 tensors are represented here as numpy uint16 bit patterns.
 """
@@ -200,6 +206,96 @@ def local_cu_seqlens(cu, total_tokens, cp_size, policy):
             row = ordered + [n] * (B + 1 - len(ordered))
             local[r, :] = row
     return local, n_local
+
+
+# --------------------------------------------------------------------------
+# Attention steps after the all-gather (PR 3221 "Why": the per-document
+# partition runs two attention steps per rank, packed-contiguous one;
+# "Scope and constraints": THD self-attention, all-gather CP, a full causal
+# mask, no inter-sequence padding; document isolation kept by the metadata).
+# --------------------------------------------------------------------------
+def attention_steps(cu, total_tokens, cp_size, policy, rank):
+    """Query and key ranges of every attention step of `rank`.
+
+    Keys and values are the all-gathered buffer in global token order (the
+    gather output).  Token t attends to token s when both lie in the same
+    document and s <= t.  Returns a list of steps; a step is a list of segments
+    (q_start, q_len, kv_start, kv_len): local query rows [q_start, q_start+q_len)
+    whose keys are global rows [kv_start, kv_start+kv_len), the queries being
+    the last q_len tokens of that key range (the causal mask aligned at the
+    bottom right).
+
+    DualChunkSwap: step 0 holds chunk `rank` of every document, step 1 chunk
+    2W-1-rank; chunk k of a document with chunk length c attends to the
+    document's first (k+1) c tokens.  Packed-contiguous: one step; every local
+    segment (a document clipped to the rank's slice) attends from its
+    document's first token up to its own last token.
+    """
+    _require_valid(cu, total_tokens, cp_size, policy)
+    W = cp_size
+    B = len(cu) - 1
+    if policy == DUAL_CHUNK_SWAP:
+        steps = []
+        for step, chunk in ((0, rank), (1, 2 * W - 1 - rank)):
+            segs = []
+            first_local = 0  # local row of the document's first row on this rank
+            for b in range(B):
+                c = (int(cu[b + 1]) - int(cu[b])) // (2 * W)
+                segs.append((first_local + step * c, c, int(cu[b]), (chunk + 1) * c))
+                first_local += 2 * c
+            steps.append(segs)
+        return steps
+    n = total_tokens // W
+    local, n_local = local_cu_seqlens(cu, total_tokens, cp_size, policy)
+    segs = []
+    for j in range(int(n_local[rank])):
+        q0, q1 = int(local[rank, j]), int(local[rank, j + 1])
+        a = rank * n + q0  # global token of the segment's first query
+        d = max(b for b in range(B) if int(cu[b]) <= a < int(cu[b + 1]))
+        segs.append((q0, q1 - q0, int(cu[d]), a + (q1 - q0) - int(cu[d])))
+    return [segs]
+
+
+def attention_meta(cu, total_tokens, cp_size, policy):
+    """The steps of every rank in the packed per-step form an attention call
+    takes (two step records per rank; under packed-contiguous the second is
+    empty).  For rank r, step s, with m segments:
+
+      num_segments, max_seqlen_q, max_seqlen_kv, total_q, total_kv
+      cu_seqlens_q[B+1]   0 then the running sum of q_len (padded with the total)
+      cu_seqlens_kv[B+1]  the same for kv_len
+      q_offsets[B+1]      q_start of each segment, then T/W (padded with T/W)
+      kv_offsets[B+1]     kv_start of each segment, then T (padded with T)
+
+    Returned as a dict of int32 arrays of shape [W, 2] (scalars) and
+    [W, 2, B+1] (tables).
+    """
+    W = cp_size
+    B = len(cu) - 1
+    n = total_tokens // W
+    out = {k: np.zeros((W, 2), dtype=np.int32)
+           for k in ("num_segments", "max_seqlen_q", "max_seqlen_kv", "total_q", "total_kv")}
+    for k in ("cu_seqlens_q", "cu_seqlens_kv", "q_offsets", "kv_offsets"):
+        out[k] = np.zeros((W, 2, B + 1), dtype=np.int32)
+    for r in range(W):
+        steps = attention_steps(cu, total_tokens, cp_size, policy, r)
+        for s in range(2):
+            segs = steps[s] if s < len(steps) else []
+            m = len(segs)
+            q_len = [g[1] for g in segs]
+            kv_len = [g[3] for g in segs]
+            cq = [0] + [int(v) for v in np.cumsum(q_len)]
+            ck = [0] + [int(v) for v in np.cumsum(kv_len)]
+            out["num_segments"][r, s] = m
+            out["max_seqlen_q"][r, s] = max(q_len, default=0)
+            out["max_seqlen_kv"][r, s] = max(kv_len, default=0)
+            out["total_q"][r, s] = cq[-1]
+            out["total_kv"][r, s] = ck[-1]
+            out["cu_seqlens_q"][r, s] = cq + [cq[-1]] * (B - m)
+            out["cu_seqlens_kv"][r, s] = ck + [ck[-1]] * (B - m)
+            out["q_offsets"][r, s] = [g[0] for g in segs] + [n] * (B + 1 - m)
+            out["kv_offsets"][r, s] = [g[2] for g in segs] + [total_tokens] * (B + 1 - m)
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -404,6 +404,96 @@ def check_pc_grad_return_is_reshape(o, seed=5):
                         assert fused[owner][i, h, d].view(np.uint32) == acc.view(np.uint32)
 
 
+# ---------------------------------------------------------------- attention steps
+def check_attention_handworked(o):
+    g = golden()
+    cu = np.array(g["cu_seqlens"], dtype=np.int32)
+    for pol, table in (("dual_chunk_swap", g["attention_steps"]["dual_chunk_swap"]),
+                       ("packed_contiguous", g["attention_steps"]["packed_contiguous"])):
+        for W, ranks in table.items():
+            for r, steps in enumerate(ranks):
+                got = o.attention_steps(cu, 48, int(W), pol, r)
+                assert [[list(seg) for seg in st] for st in got] == steps, (pol, W, r)
+
+
+def brute_attention_pairs(cu, T):
+    """Every (query token, key token) pair of causal document-isolated self-attention."""
+    doc = np.zeros(T, dtype=np.int64)
+    for b in range(len(cu) - 1):
+        doc[int(cu[b]):int(cu[b + 1])] = b
+    return {(t, s) for t in range(T) for s in range(t + 1) if doc[s] == doc[t]}
+
+
+def check_attention_pairs(o, cu, T, W, pol):
+    """The steps' pairs, with queries mapped to global tokens by the partition, are
+    exactly the causal in-document pairs of the rank's tokens, each produced once,
+    and every local row is a query of exactly one step."""
+    want_all = brute_attention_pairs(cu, T)
+    for r in range(W):
+        rows = o.rank_rows(cu, T, W, pol, r)
+        mine = set(rows.tolist())
+        want = {(t, s) for (t, s) in want_all if t in mine}
+        got, seen_rows = [], []
+        for step in o.attention_steps(cu, T, W, pol, r):
+            for q0, ql, k0, kl in step:
+                assert 0 <= ql <= kl, (W, pol, r)
+                for i in range(ql):
+                    t = int(rows[q0 + i])
+                    seen_rows.append(q0 + i)
+                    got += [(t, s) for s in range(k0, k0 + kl - ql + i + 1)]
+        assert sorted(seen_rows) == list(range(len(rows))), (W, pol, r)
+        assert len(got) == len(set(got)) and set(got) == want, (W, pol, r)
+
+
+def check_attention_brute_force(o):
+    cases = [(2, "dual_chunk_swap", [4, 0, 8, 12]), (3, "dual_chunk_swap", [6, 12]),
+             (2, "packed_contiguous", [3, 0, 9, 1, 7]), (3, "packed_contiguous", [5, 1, 6, 0, 3]),
+             (4, "packed_contiguous", [16]), (4, "packed_contiguous", [1, 1, 1, 13]),
+             (1, "dual_chunk_swap", [2, 4]), (1, "packed_contiguous", [3, 2])]
+    for W, pol, lengths in cases:
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        check_attention_pairs(o, cu, int(cu[-1]), W, pol)
+
+
+def check_attention_meta_closed_forms(o):
+    """Packed per-step tables against closed forms: dual-chunk-swap cu_q = cu/(2W),
+    cu_kv = (k+1) cu/(2W), q_offsets = cu/W (+ the chunk length in step 1),
+    kv_offsets = cu; packed-contiguous cu_q = q_offsets = the local cu, cu_kv = the
+    local cu shifted by the look-back to the first document's start."""
+    cu = np.array([0, 12, 12, 36, 60, 96], dtype=np.int32)
+    T, B = 96, 5
+    for W in (1, 2, 3):
+        m = o.attention_meta(cu, T, W, o.DUAL_CHUNK_SWAP)
+        n = T // W
+        for r in range(W):
+            for s, k in ((0, r), (1, 2 * W - 1 - r)):
+                assert (m["num_segments"][r, s] == B)
+                assert (m["cu_seqlens_q"][r, s] == cu // (2 * W)).all()
+                assert (m["cu_seqlens_kv"][r, s] == (k + 1) * (cu // (2 * W))).all()
+                qo = cu[:-1] // W + s * (np.diff(cu) // (2 * W))
+                assert (m["q_offsets"][r, s] == np.append(qo, n)).all()
+                assert (m["kv_offsets"][r, s] == np.append(cu[:-1], T)).all()
+                assert m["max_seqlen_q"][r, s] == np.diff(cu).max() // (2 * W)
+                assert m["max_seqlen_kv"][r, s] == (k + 1) * (np.diff(cu).max() // (2 * W))
+    cu = np.array([0, 5, 5, 17, 18, 30], dtype=np.int32)
+    T = 30
+    for W in (1, 2, 3, 5):
+        n = T // W
+        m = o.attention_meta(cu, T, W, o.PACKED_CONTIGUOUS)
+        local, n_local = o.local_cu_seqlens(cu, T, W, o.PACKED_CONTIGUOUS)
+        for r in range(W):
+            d0 = int(np.searchsorted(cu, r * n, side="right")) - 1  # document of the first token
+            back = r * n - int(cu[d0])
+            assert m["num_segments"][r, 0] == n_local[r] and m["num_segments"][r, 1] == 0
+            assert (m["cu_seqlens_q"][r, 0] == local[r]).all() and (m["q_offsets"][r, 0] == local[r]).all()
+            kv = local[r] + back
+            kv[0] = 0
+            assert (m["cu_seqlens_kv"][r, 0] == kv).all()
+            assert m["kv_offsets"][r, 0][0] == cu[d0]
+            assert (m["cu_seqlens_q"][r, 1] == 0).all() and (m["q_offsets"][r, 1] == n).all()
+            assert (m["kv_offsets"][r, 1] == T).all()
+
+
 ALL_CHECKS = [
     check_handworked_dcs,
     check_handworked_pc,
@@ -423,4 +513,7 @@ ALL_CHECKS = [
     check_accumulate_integer,
     check_accumulate_signed_zero,
     check_pc_grad_return_is_reshape,
+    check_attention_handworked,
+    check_attention_brute_force,
+    check_attention_meta_closed_forms,
 ]

@@ -212,6 +212,47 @@ def _fused_policy_ignored(o):
     return grad_return_fused
 
 
+def _attn_kv_one_chunk_short(o):
+    orig = o.attention_steps
+
+    def attention_steps(cu, total_tokens, cp_size, policy, rank):
+        steps = orig(cu, total_tokens, cp_size, policy, rank)
+        if policy != o.DUAL_CHUNK_SWAP:
+            return steps
+        return [[(q0, ql, k0, kl - ql) for q0, ql, k0, kl in st] for st in steps]
+    return attention_steps
+
+
+def _attn_pc_no_lookback(o):
+    orig = o.attention_steps
+
+    def attention_steps(cu, total_tokens, cp_size, policy, rank):
+        steps = orig(cu, total_tokens, cp_size, policy, rank)
+        if policy != o.PACKED_CONTIGUOUS:
+            return steps
+        n = total_tokens // cp_size
+        return [[(q0, ql, rank * n + q0, ql) for q0, ql, k0, kl in st] for st in steps]
+    return attention_steps
+
+
+def _attn_steps_swapped(o):
+    orig = o.attention_steps
+
+    def attention_steps(cu, total_tokens, cp_size, policy, rank):
+        return orig(cu, total_tokens, cp_size, policy, rank)[::-1]
+    return attention_steps
+
+
+def _attn_offsets_packed(o):
+    orig = o.attention_meta
+
+    def attention_meta(cu, total_tokens, cp_size, policy):
+        m = orig(cu, total_tokens, cp_size, policy)
+        m["q_offsets"] = m["cu_seqlens_q"].copy()
+        return m
+    return attention_meta
+
+
 MUTATIONS = {
     "dcs_swapped_chunks": ("dcs_rank_rows", _dcs_swapped_chunks),
     "dcs_wrong_mirror": ("dcs_rank_rows", _dcs_wrong_mirror),
@@ -231,6 +272,10 @@ MUTATIONS = {
     "accumulate_ignored": ("grad_return_fused", _acc_ignored),
     "grad_scatter_ignores_policy": ("grad_scatter", _grad_policy_ignored),
     "fused_ignores_policy": ("grad_return_fused", _fused_policy_ignored),
+    "attention_kv_one_chunk_short": ("attention_steps", _attn_kv_one_chunk_short),
+    "attention_pc_no_lookback": ("attention_steps", _attn_pc_no_lookback),
+    "attention_steps_swapped": ("attention_steps", _attn_steps_swapped),
+    "attention_offsets_packed": ("attention_meta", _attn_offsets_packed),
 }
 
 INVARIANT_CASES = [

@@ -65,6 +65,22 @@ def test_brute_force_random(case, seed):
         assert o.rank_rows(cu, T, W, o.DUAL_CHUNK_SWAP, r).tolist() == rows[r]
 
 
+@settings(max_examples=40, deadline=None, derandomize=True)
+@given(dcs_case())
+def test_attention_pairs_dcs(case):
+    W, lengths = case
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    pins.check_attention_pairs(o, cu, int(cu[-1]), W, o.DUAL_CHUNK_SWAP)
+
+
+@settings(max_examples=40, deadline=None, derandomize=True)
+@given(pc_case())
+def test_attention_pairs_pc(case):
+    W, lengths = case
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    pins.check_attention_pairs(o, cu, int(cu[-1]), W, o.PACKED_CONTIGUOUS)
+
+
 def test_empty_input():
     cu = np.array([0], dtype=np.int32)
     for pol in o.POLICIES:
