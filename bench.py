@@ -2,7 +2,8 @@
 
 One step = one pass of every stage of the path over one batch of synthetic
 input already resident in HBM:
-  * metadata for the three token layouts (cp_build_meta),
+  * metadata for the three token layouts (cp_build_meta) and the attention-step
+    tables of both layout policies (cp_build_attn_meta),
   * dual-chunk-swap partition + inverse gather of Q, K, V [262144, 20, 128] bf16
     (packed documents, log-uniform lengths in [256, 8192], W = 4),
   * packed-contiguous partition + inverse gather of the same Q, K, V
@@ -96,6 +97,11 @@ class Step:
 
         meta_bytes = sum(4 * (cu.numel()) + 4 * (cu.numel()) * (W + 1) + 4 * W for cu, _, _ in metas)
         self.ops.append(("build_meta x3", meta_bytes, build_metas))
+        # attention-step tables of both layout policies (written bytes; < 20 KB)
+        attn = [(m, cp.cp_build_attn_meta(m)) for m in (self.meta_dcs, self.meta_pc)]
+        attn_bytes = sum(2 * m.cp_size * (32 + 16 * (m.num_docs + 1)) for m, _ in attn)
+        self.ops.append(("build_attn_meta x2", attn_bytes,
+                         lambda: [cp.cp_build_attn_meta(m, attn=a) for m, a in attn]))
         for pname, meta in (("dual_chunk_swap", self.meta_dcs), ("packed_contiguous", self.meta_pc)):
             self.ops.append((f"partition_{pname} QKV", 3 * 2 * S * row_bf16,
                              lambda meta=meta: cp.cp_partition_thd_multi(self.qkv, meta, parts=self.parts)))
@@ -205,6 +211,7 @@ def cpu_baseline(S_sample: int, WL, passes: int = 2):
         for cu, pol, W in ((cu_dcs, O.DUAL_CHUNK_SWAP, w_dcs.cp_size),
                            (cu_pc, O.PACKED_CONTIGUOUS, w_pc.cp_size)):
             O.local_cu_seqlens(cu, S_sample, W, pol)
+            O.attention_meta(cu, S_sample, W, pol)
             for x in qkv:
                 parts = O.partition(x, cu, W, pol)
                 O.gather(parts, cu, W, pol)
@@ -219,7 +226,8 @@ def cpu_baseline(S_sample: int, WL, passes: int = 2):
             nbytes += 9 * nb
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} passes of the full step (metadata, DCS and PC partition+gather of "
+            "sample": f"{passes} passes of the full step (metadata and attention-step tables, DCS and "
+                      f"PC partition+gather of "
                       f"Q,K,V, unfused and fused dK/dV gradient return, W=8 sweep) at S={S_sample} "
                       f"instead of 262144, same heads, head_dim, cp_size, dtypes and distributions; "
                       f"numpy, one thread; {nbytes / 1e9:.2f} GB algorithmic in {dt:.1f} s"}
@@ -267,6 +275,8 @@ def per_config(cp, WL, torch, dev, reps: int = 10):
             timed(lambda: [cp.cp_partition_thd(x, meta, parts=p) for x, p in zip(xs, parts)]))
         add(name, "metadata", 0, timed(lambda: cp.cp_build_meta(cu, w.total_tokens, w.cp_size,
                                                                   cp.POLICY[w.policy], meta=meta.buf)))
+        attn = cp.cp_build_attn_meta(meta)
+        add(name, "attention-step metadata", 0, timed(lambda: cp.cp_build_attn_meta(meta, attn=attn)))
         del xs, parts, back
         torch.cuda.empty_cache()
     for name in ("grad_s256k_w4", "fused_s128k_w8"):

@@ -141,6 +141,7 @@ enum cp_dtype {
 #define CP_CALL_CP_SIZE_MISMATCH  0x0400 /* cp_size differs from the meta's               */
 #define CP_CALL_POLICY_MISMATCH   0x0800 /* call needs the other policy (none does today) */
 #define CP_CALL_USED_INVALID_META 0x1000 /* a kernel met invalid metadata and did nothing */
+#define CP_CALL_DOCS_MISMATCH     0x2000 /* num_docs differs from the meta's              */
 
 typedef struct cp_meta_header {
   uint32_t magic;             /* CP_META_MAGIC once built                        */
@@ -193,6 +194,78 @@ int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tok
  */
 int cp_meta_status(const void* meta, cp_stream_t stream, int32_t* flags_out,
                    uint64_t* timeouts_out);
+
+/* ------------------------------------------------------------ attention steps */
+/*
+ * Per-rank attention-step metadata for all-gather CP: which local query rows
+ * attend to which rows of the all-gathered key/value buffer (global token
+ * order: the output of cp_gather_thd).  Source: [PC] "Why" (the per-document
+ * partition performs two attention steps per rank, packed-contiguous one) and
+ * "Scope and constraints" (THD self-attention, all-gather CP, full causal mask,
+ * no inter-sequence padding); commit messages (document boundaries retained
+ * through sequence metadata; packed metadata simplified to one chunk and one
+ * attention step per rank).  Attention is causal inside each document: token t
+ * sees token s when they share a document and s <= t.
+ *
+ *   dual-chunk-swap, rank r: step 0 = chunk r of every document, step 1 =
+ *     chunk 2W-1-r; chunk k of document b (chunk length c_b = L_b / 2W) sees
+ *     the document's first (k+1) c_b tokens.  B segments per step (empty
+ *     documents give empty segments).
+ *   packed-contiguous, rank r: one step (the second record is empty); every
+ *     local segment (a document clipped to the rank's slice, as in local_cu)
+ *     sees its document from the first token up to the segment's last token.
+ * In every segment the queries are the LAST q_len tokens of its key range (the
+ * causal mask aligned at the bottom right of the q_len x kv_len block).
+ *
+ * Layout (cp_attn_meta_bytes(B, W) bytes, caller-allocated, device memory):
+ *   offset 0    cp_attn_header (64 bytes)
+ *   offset 64   2W step records, rank-major (rank r step s at index 2r + s),
+ *               each 32 + 16(B+1) bytes:
+ *     int32 num_segments   m (B under dual-chunk-swap; n_local[r] or 0 under
+ *                          packed-contiguous)
+ *     int32 max_seqlen_q, max_seqlen_kv   longest segment (0 if m = 0)
+ *     int32 total_q, total_kv             sums of the segment lengths
+ *     int32 reserved[3]
+ *     int32 cu_seqlens_q[B+1]   0, q_len_0, q_len_0 + q_len_1, ...; entries
+ *                               after m repeat total_q
+ *     int32 cu_seqlens_kv[B+1]  the same for kv_len (entries after m: total_kv)
+ *     int32 q_offsets[B+1]      q_start of segment j in the rank's [T/W] local
+ *                               buffer; entries from m on hold T/W
+ *     int32 kv_offsets[B+1]     kv_start of segment j in the gathered [T]
+ *                               buffer; entries from m on hold T
+ */
+#define CP_ATTN_MAGIC 0x54414350u /* "PCAT" */
+
+typedef struct cp_attn_header {
+  uint32_t magic;             /* CP_ATTN_MAGIC when built from valid metadata, else 0 */
+  int32_t policy;
+  int32_t cp_size;            /* W                                                    */
+  int32_t num_docs;           /* B                                                    */
+  int32_t num_steps;          /* 2 (dual-chunk-swap) or 1 (packed-contiguous)         */
+  int32_t reserved0;
+  int64_t total_tokens;       /* T                                                    */
+  int64_t local_tokens;       /* T / W                                                */
+  int32_t reserved[6];
+} cp_attn_header;
+
+/* Bytes of the attention-step metadata of B documents and W ranks (a multiple
+ * of 256); 0 for B < 0 or W outside [1, CP_MAX_CP_SIZE]. */
+size_t cp_attn_meta_bytes(int32_t num_docs, int32_t cp_size);
+
+/*
+ * cp_build_attn_meta - fill the attention-step metadata of every rank from
+ * metadata built by cp_build_meta (either policy).
+ *   meta        device metadata of num_docs documents and cp_size ranks
+ *   attn        device buffer of attn_bytes >= cp_attn_meta_bytes(B, W) bytes;
+ *               must not overlap meta
+ * Host errors: CP_ERR_ARG (NULL, ranges), CP_ERR_SHAPE (attn_bytes too small),
+ * CP_ERR_DEVICE, CP_ERR_ALIAS, CP_ERR_HIP.  On the device, invalid metadata or
+ * a num_docs / cp_size that differs from the meta's sets the meta's sticky
+ * CP_CALL_* flag (read with cp_meta_status), and the attention header's magic
+ * is written as 0 with no step record written (fail-closed).
+ */
+int cp_build_attn_meta(const void* meta, int32_t num_docs, int32_t cp_size, void* attn,
+                       size_t attn_bytes, cp_stream_t stream);
 
 /* ------------------------------------------------------------ token layout */
 /*

@@ -69,6 +69,16 @@ def test_meta_bytes_closed_form(cp):
     assert cp.cp_meta_bytes(3, 65) == 0
 
 
+def test_attn_meta_bytes_closed_form(cp):
+    for B in (0, 1, 3, 115, 1000):
+        for W in (1, 2, 4, 8, 64):
+            raw = 64 + 2 * W * (32 + 16 * (B + 1))
+            assert cp.cp_attn_meta_bytes(B, W) == (raw + 255) // 256 * 256
+    assert cp.cp_attn_meta_bytes(-1, 4) == 0
+    assert cp.cp_attn_meta_bytes(3, 0) == 0
+    assert cp.cp_attn_meta_bytes(3, 65) == 0
+
+
 def test_status_strings(cp):
     for s in range(9):
         assert cp.cp_status_string(s) and cp.cp_status_string(s) != "unknown status"
@@ -89,6 +99,14 @@ def test_host_checks_before_any_hip_call(cp):
     assert lib.cp_build_meta(FAKE, 3, 48, 2, 0, FAKE, 16, None) == cp.CP_ERR_SHAPE
     assert lib.cp_build_meta(None, 3, 48, 2, 0, FAKE, 4096, None) == cp.CP_ERR_ARG
     assert lib.cp_build_meta(FAKE, 3, -1, 2, 0, FAKE, 4096, None) == cp.CP_ERR_ARG
+    # attention steps: NULLs, ranges, buffer size
+    am = lib.cp_build_attn_meta
+    assert am(None, 3, 2, FAKE, 4096, None) == cp.CP_ERR_ARG
+    assert am(FAKE, 3, 2, None, 4096, None) == cp.CP_ERR_ARG
+    assert am(FAKE, -1, 2, FAKE, 4096, None) == cp.CP_ERR_ARG
+    assert am(FAKE, 3, 0, FAKE, 4096, None) == cp.CP_ERR_ARG
+    assert am(FAKE, 3, 65, FAKE, 4096, None) == cp.CP_ERR_ARG
+    assert am(FAKE, 3, 2, FAKE, cp.cp_attn_meta_bytes(3, 2) - 1, None) == cp.CP_ERR_SHAPE
     # partition / gather: FP8 rejected, unknown dtype, NULLs, sizes
     for fn in (lib.cp_partition_thd, lib.cp_gather_thd):
         assert fn(FAKE, FAKE, 48, 2, 8, cp.CP_FP8_E4M3, FAKE, None) == cp.CP_ERR_UNSUPPORTED

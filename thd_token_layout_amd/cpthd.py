@@ -44,6 +44,8 @@ CP_CALL_TOKENS_MISMATCH = 0x0200
 CP_CALL_CP_SIZE_MISMATCH = 0x0400
 CP_CALL_POLICY_MISMATCH = 0x0800
 CP_CALL_USED_INVALID_META = 0x1000
+CP_CALL_DOCS_MISMATCH = 0x2000
+CP_ATTN_MAGIC = 0x54414350
 
 POLICY = {"dual_chunk_swap": CP_POLICY_DUAL_CHUNK_SWAP,
           "packed_contiguous": CP_POLICY_PACKED_CONTIGUOUS}
@@ -76,6 +78,10 @@ lib.cp_grad_return_fused.argtypes = [_i32, _i32, _i32, _c.POINTER(_vp), _c.POINT
                                      _i32, _i32, _i32, _vp, _i32, _vp]
 lib.cp_slot_sum.restype = _c.c_int
 lib.cp_slot_sum.argtypes = [_i32, _c.POINTER(_vp), _vp, _i64, _i32, _i32, _i32, _vp]
+lib.cp_attn_meta_bytes.restype = _sz
+lib.cp_attn_meta_bytes.argtypes = [_i32, _i32]
+lib.cp_build_attn_meta.restype = _c.c_int
+lib.cp_build_attn_meta.argtypes = [_vp, _i32, _i32, _vp, _sz, _vp]
 lib.cp_status_string.restype = _c.c_char_p
 lib.cp_status_string.argtypes = [_c.c_int]
 lib.cp_version.restype = _c.c_int
@@ -216,6 +222,39 @@ def read_local_cu(meta: Meta):
     return local, n_local
 
 
+def cp_attn_meta_bytes(num_docs: int, cp_size: int) -> int:
+    return lib.cp_attn_meta_bytes(num_docs, cp_size)
+
+
+def cp_build_attn_meta(meta: Meta, attn: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Per-rank attention-step tables (uint8 device buffer) from built metadata."""
+    nbytes = cp_attn_meta_bytes(meta.num_docs, meta.cp_size)
+    if attn is None:
+        attn = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=meta.buf.device)
+    st = lib.cp_build_attn_meta(meta.ptr(), meta.num_docs, meta.cp_size, _ptr(attn), attn.numel(),
+                                _stream(stream, meta.buf))
+    _check(st, "cp_build_attn_meta")
+    return attn
+
+
+ATTN_SCALARS = ("num_segments", "max_seqlen_q", "max_seqlen_kv", "total_q", "total_kv")
+ATTN_TABLES = ("cu_seqlens_q", "cu_seqlens_kv", "q_offsets", "kv_offsets")
+
+
+def read_attn_meta(attn: torch.Tensor, num_docs: int, cp_size: int):
+    """Copy the attention-step tables to the host (synchronizes): (magic, dict of int32
+    tensors [W, 2] for the scalars and [W, 2, B+1] for the tables)."""
+    B, W = num_docs, cp_size
+    rec = 8 + 4 * (B + 1)  # int32 words per step record
+    words = attn[: 64 + 4 * 2 * W * rec].cpu().view(torch.int32)
+    magic = int(words[0].item()) & 0xFFFFFFFF
+    recs = words[16: 16 + 2 * W * rec].reshape(W, 2, rec)
+    out = {k: recs[:, :, i].clone() for i, k in enumerate(ATTN_SCALARS)}
+    for i, k in enumerate(ATTN_TABLES):
+        out[k] = recs[:, :, 8 + i * (B + 1): 8 + (i + 1) * (B + 1)].clone()
+    return magic, out
+
+
 def cp_partition_thd(x: torch.Tensor, meta: Meta, parts: Optional[torch.Tensor] = None,
                      stream=None) -> torch.Tensor:
     T, H, D = x.shape
@@ -333,7 +372,8 @@ def cp_profile_read(capacity: int = 64):
     return res
 
 
-EXPORTED = ["cp_meta_bytes", "cp_build_meta", "cp_meta_status", "cp_partition_thd", "cp_gather_thd",
+EXPORTED = ["cp_meta_bytes", "cp_build_meta", "cp_meta_status", "cp_attn_meta_bytes", "cp_build_attn_meta",
+            "cp_partition_thd", "cp_gather_thd",
             "cp_partition_thd_multi", "cp_gather_thd_multi",
             "cp_grad_return", "cp_grad_return_fused", "cp_slot_sum", "cp_status_string", "cp_version",
             "cp_profile_enable", "cp_profile_read"]

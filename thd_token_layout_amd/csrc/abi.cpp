@@ -193,6 +193,27 @@ int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tok
                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t cp_attn_meta_bytes(int32_t num_docs, int32_t cp_size) {
+  if (num_docs < 0 || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return 0;
+  const size_t bytes = 64 + 2 * (size_t)cp_size * (size_t)attn_record_bytes(num_docs);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int cp_build_attn_meta(const void* meta, int32_t num_docs, int32_t cp_size, void* attn,
+                       size_t attn_bytes, cp_stream_t stream) {
+  if (meta == nullptr || attn == nullptr) return CP_ERR_ARG;
+  if (num_docs < 0 || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return CP_ERR_ARG;
+  if (attn_bytes < cp_attn_meta_bytes(num_docs, cp_size)) return CP_ERR_SHAPE;
+  int dev, st;
+  if ((st = current_device(&dev)) != CP_OK) return st;
+  if ((st = check_device_ptr(meta, dev)) != CP_OK) return st;
+  if ((st = check_device_ptr(attn, dev)) != CP_OK) return st;
+  if ((st = check_alias({range_of(attn, (int64_t)attn_bytes)},
+                        {range_of(meta, (int64_t)cp_meta_bytes(num_docs, cp_size))})) != CP_OK)
+    return st;
+  return hip_status(launch_build_attn_meta(meta, num_docs, cp_size, attn, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int cp_meta_status(const void* meta, cp_stream_t stream, int32_t* flags_out,
                    uint64_t* timeouts_out) {
   if (meta == nullptr) return CP_ERR_ARG;

@@ -45,6 +45,14 @@ inline int dtype_bytes(int32_t dt) {
 hipError_t launch_build_meta(const int32_t* cu, int32_t B, int64_t T, int32_t W, int32_t policy,
                              void* meta, hipStream_t stream);
 
+// Attention-step records (layout documented in cpthd.h): 64-byte header, then
+// 2W records of 32 + 16(B+1) bytes.
+__host__ __device__ inline int64_t attn_record_bytes(int32_t B) { return 32 + 16 * (int64_t)(B + 1); }
+__host__ __device__ inline int64_t attn_record_offset(int32_t B, int32_t index) {
+  return 64 + (int64_t)index * attn_record_bytes(B);
+}
+hipError_t launch_build_attn_meta(const void* meta, int32_t B, int32_t W, void* attn, hipStream_t stream);
+
 // ---------------------------------------------------------------- row permutation
 // One launch moves all T rows of n_tensors tensors (same T, row size and
 // layout) between the global layout and the per-rank layout.  global[t] is

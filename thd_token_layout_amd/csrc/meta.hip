@@ -9,7 +9,16 @@
 // inside the slice (first occurrence only, so empty documents vanish), shifted,
 // between 0 and T/W.  The compaction is a wavefront ballot + popcount prefix,
 // combined across the block's four waves through LDS.
-#include "cpthd_internal.h"
+//
+// cp_build_attn_meta kernel: the query / key ranges of every rank's attention
+// steps after the all-gather (same PR, "Why": two steps per rank under the
+// per-document partition, one under packed-contiguous; "Scope and
+// constraints": causal THD self-attention).  Chunk k of a document with chunk
+// length c sees the document's first (k+1) c keys; a packed-contiguous segment
+// sees its document from the first token on.  Every table entry has a closed
+// form in cu, the rank's local cu and the look-back from the rank's first
+// token to its document's start, so a thread per entry fills the tables.
+#include "device_common.h"
 
 namespace cpthd {
 namespace {
@@ -102,7 +111,143 @@ build_meta_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t T, int32_t 
   }
 }
 
+// Maximum over the workgroup (every thread gets it).
+__device__ int32_t block_max(int32_t v) {
+  __shared__ int32_t s_max[kWavesPerBlock];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int32_t m = s_max[0];
+#pragma unroll
+  for (int k = 1; k < kWavesPerBlock; ++k) m = max(m, s_max[k]);
+  __syncthreads();  // s_max may be reused by the next call
+  return m;
+}
+
+// One workgroup per (rank, step): blockIdx.x = 2 rank + step.
+__global__ void __launch_bounds__(kBlock)
+build_attn_meta_kernel(cp_meta_header* h, int32_t B, int32_t W, char* __restrict__ attn) {
+  const int tid = threadIdx.x;
+  bool ok = meta_ok(h, h->total_tokens, W, -1);
+  if (ok && h->num_docs != B) {
+    ok = false;
+    if (blockIdx.x == 0 && tid == 0) atomicOr(&h->flags, CP_CALL_DOCS_MISMATCH);
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    cp_attn_header* a = reinterpret_cast<cp_attn_header*>(attn);
+    a->policy = ok ? h->policy : -1;
+    a->cp_size = W;
+    a->num_docs = B;
+    a->num_steps = ok ? (h->policy == CP_POLICY_DUAL_CHUNK_SWAP ? 2 : 1) : 0;
+    a->reserved0 = 0;
+    a->total_tokens = ok ? h->total_tokens : 0;
+    a->local_tokens = ok ? h->local_tokens : 0;
+    for (int k = 0; k < 6; ++k) a->reserved[k] = 0;
+    a->magic = ok ? CP_ATTN_MAGIC : 0u;
+  }
+  if (!ok) return;
+
+  const int32_t r = blockIdx.x >> 1;
+  const int32_t step = blockIdx.x & 1;
+  const int32_t T = (int32_t)h->total_tokens;
+  const int32_t n = (int32_t)h->local_tokens;
+  const int32_t* cu = meta_cu(h);
+  int32_t* scal = reinterpret_cast<int32_t*>(attn + attn_record_offset(B, blockIdx.x));
+  int32_t* cuq = scal + 8;
+  int32_t* cukv = cuq + (B + 1);
+  int32_t* qoff = cukv + (B + 1);
+  int32_t* kvoff = qoff + (B + 1);
+
+  if (h->policy == CP_POLICY_DUAL_CHUNK_SWAP) {
+    const int32_t k = step == 0 ? r : 2 * W - 1 - r;  // the step's chunk index
+    const int32_t two_w = 2 * W;
+    int32_t max_c = 0;
+    for (int j = tid; j <= B; j += kBlock) {
+      const int32_t v = cu[j];
+      const int32_t before = v / two_w;  // chunk length summed over documents 0..j-1
+      cuq[j] = before;
+      cukv[j] = (k + 1) * before;
+      if (j < B) {
+        const int32_t c = (cu[j + 1] - v) / two_w;
+        qoff[j] = v / W + step * c;
+        kvoff[j] = v;
+        max_c = max(max_c, c);
+      } else {
+        qoff[j] = n;
+        kvoff[j] = T;
+      }
+    }
+    max_c = block_max(max_c);
+    if (tid == 0) {
+      const int32_t total_c = cu[B] / two_w;
+      scal[0] = B;
+      scal[1] = max_c;
+      scal[2] = (k + 1) * max_c;
+      scal[3] = total_c;
+      scal[4] = (k + 1) * total_c;
+      scal[5] = scal[6] = scal[7] = 0;
+    }
+    return;
+  }
+
+  // packed-contiguous: one step; the second record of a rank is empty.
+  if (step == 1) {
+    for (int j = tid; j <= B; j += kBlock) {
+      cuq[j] = 0;
+      cukv[j] = 0;
+      qoff[j] = n;
+      kvoff[j] = T;
+    }
+    if (tid < 8) scal[tid] = 0;
+    return;
+  }
+  const int32_t* lcu = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(h) +
+                                                        meta_local_cu_offset(B)) + (int64_t)r * (B + 1);
+  const int32_t m = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(h) +
+                                                     meta_n_local_offset(B, W))[r];
+  const int32_t first = r * n;  // the rank's first global token
+  int32_t doc_start = 0, back = 0;
+  if (m > 0) {
+    doc_start = cu[find_doc(cu, B, first)];
+    back = first - doc_start;  // keys of the first segment before the rank's slice
+  }
+  int32_t max_q = 0, max_kv = 0;
+  for (int j = tid; j <= B; j += kBlock) {
+    const int32_t l = lcu[j];  // padded with n after entry m
+    cuq[j] = l;
+    qoff[j] = l;
+    cukv[j] = j == 0 ? 0 : l + back;
+    kvoff[j] = j >= m ? T : (j == 0 ? doc_start : first + l);
+    if (j < m) {
+      const int32_t q_len = lcu[j + 1] - l;
+      max_q = max(max_q, q_len);
+      max_kv = max(max_kv, j == 0 ? q_len + back : q_len);
+    }
+  }
+  max_q = block_max(max_q);
+  max_kv = block_max(max_kv);
+  if (tid == 0) {
+    scal[0] = m;
+    scal[1] = max_q;
+    scal[2] = max_kv;
+    scal[3] = m > 0 ? n : 0;
+    scal[4] = m > 0 ? n + back : 0;
+    scal[5] = scal[6] = scal[7] = 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_build_attn_meta(const void* meta, int32_t B, int32_t W, void* attn, hipStream_t stream) {
+  profile_before("build_attn_meta", stream);
+  hipLaunchKernelGGL(build_attn_meta_kernel, dim3(2 * W), dim3(kBlock), 0, stream,
+                     const_cast<cp_meta_header*>(static_cast<const cp_meta_header*>(meta)), B, W,
+                     static_cast<char*>(attn));
+  hipError_t e = hipGetLastError();
+  profile_after(stream);
+  return e;
+}
 
 hipError_t launch_build_meta(const int32_t* cu, int32_t B, int64_t T, int32_t W, int32_t policy,
                              void* meta, hipStream_t stream) {
