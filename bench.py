@@ -144,7 +144,7 @@ def attribute_kernels(step: Step, cp, torch):
         prof = cp.cp_profile_read()
         for kname, (count, _) in prof.items():
             if name.startswith("grad_return dK"):
-                role = "scatter" if kname.startswith("permute_rows") else \
+                role = "scatter" if kname.startswith("permute") else \
                     "owner_sum" if kname.startswith("slot_sum") else None
                 b = step.kernel_bytes[role] if role else 0
             elif name.startswith("grad_return_fused"):

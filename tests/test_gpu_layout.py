@@ -236,6 +236,63 @@ def test_more_tiles_than_the_grid(cp):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("pol,lengths", [
+    (1, [7, 0, 93, 20]), (1, [120]),          # packed-contiguous: 8 KiB unit tiles
+    (0, [120]), (0, [8]),                     # one document: 12 KiB unit tiles
+    (0, [16, 0, 8]),                          # several documents: row tiles
+])
+@pytest.mark.parametrize("units", [55, 65, 100, 333, 1280])
+def test_unit_tiles_ragged(cp, pol, lengths, units):
+    """Rows of 16-byte units whose count does not divide the unit tile, so tiles
+    start and end inside rows and the last tile is partial; one tensor and three
+    tensors per call; every output against the oracle."""
+    W = 4
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    say(f"case unit tiles pol={pol} T={T} row={16 * units} B")
+    gen = torch.Generator(device=DEV).manual_seed(units + T)
+    xs = [torch.randint(-2**15, 2**15, (T, 1, 8 * units), dtype=torch.int16, device=DEV,
+                        generator=gen).view(torch.bfloat16) for _ in range(3)]
+    check_layout(cp, xs[0], cu, W, pol)
+    meta = build(cp, cu, T, W, pol)
+    parts = cp.cp_partition_thd_multi(xs, meta)
+    backs = cp.cp_gather_thd_multi(parts, meta)
+    for x, p, bk in zip(xs, parts, backs):
+        assert bits_equal(to_np(p), O.partition(to_np(x), cu, W, policy_name(pol)))
+        assert bits_equal(to_np(bk), to_np(x))
+
+
+def test_unit_tiles_more_than_the_grid(cp):
+    """2^31 + 4096 units of 16 bytes (32 GiB per buffer) under packed-contiguous
+    metadata: more unit tiles than the largest grid launched, so the unit-tile
+    kernel's grid-stride loop runs.  Rows hold their own index, so every sampled
+    row of the partition and of the gather is checked against the oracle's map."""
+    T, W, words = (1 << 25) + 64, 4, 128  # rows of 1 KiB = 128 int64 words
+    say(f"case unit tiles beyond the grid: T={T}, 1 KiB rows")
+    x = torch.empty((T, 1, 512), dtype=torch.bfloat16, device=DEV)
+    torch.add(torch.arange(T, dtype=torch.int64, device=DEV)[:, None] * words,
+              torch.arange(words, dtype=torch.int64, device=DEV)[None, :], out=x.view(torch.int64).view(T, words))
+    cu = np.array([0, 1000, T], dtype=np.int32)
+    meta = build(cp, cu, T, W, cp.CP_POLICY_PACKED_CONTIGUOUS)
+    parts = cp.cp_partition_thd(x, meta)
+    x.zero_()
+    cp.cp_gather_thd(parts, meta, x=x)
+    n = T // W
+    rng = np.random.default_rng(11)
+    cols = np.arange(words, dtype=np.int64)
+    for r in range(W):
+        idx = np.unique(np.concatenate([rng.integers(0, n, size=200), [0, n - 1]]))
+        got = parts[r][torch.from_numpy(idx).to(DEV)].view(torch.int64).view(-1, words).cpu().numpy()
+        g = np.array([O.rank_row(cu, T, W, O.PACKED_CONTIGUOUS, r, int(i)) for i in idx], dtype=np.int64)
+        assert (got == g[:, None] * words + cols[None, :]).all(), r
+    idx = np.unique(np.concatenate([rng.integers(0, T, size=800), [0, T - 1]]))
+    got = x[torch.from_numpy(idx).to(DEV)].view(torch.int64).view(-1, words).cpu().numpy()
+    assert (got == idx[:, None].astype(np.int64) * words + cols[None, :]).all()
+    assert cp.cp_meta_status(meta)[0] == cp.CP_OK
+    del x, parts
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ invalid / mismatched metadata
 FLAG_NAMES = {"first_not_zero": 0x1, "decreasing": 0x2, "last_not_total": 0x4,
               "doc_not_divisible": 0x8}

@@ -13,6 +13,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "cpthd.h"
@@ -24,6 +25,38 @@ namespace {
 struct Range {
   uintptr_t lo, hi;
 };
+
+// What the host knows of the metadata it built, by buffer address.  It only
+// picks the permutation engine's tile shape: every kernel reads and validates
+// the metadata itself on the device, so a stale record (a buffer rebuilt by
+// other means, or memory reused) can cost speed but never change a result.
+struct MetaRecord {
+  int32_t policy, num_docs, cp_size;
+  int64_t total_tokens;
+};
+std::mutex g_records_mu;
+std::unordered_map<const void*, MetaRecord> g_records;
+constexpr size_t kMaxRecords = 4096;
+
+void remember_meta(const void* meta, const MetaRecord& r) {
+  std::lock_guard<std::mutex> lock(g_records_mu);
+  if (g_records.size() >= kMaxRecords && g_records.find(meta) == g_records.end()) g_records.clear();
+  g_records[meta] = r;
+}
+
+// Fill the tile-shape hints of `a` from the record of `meta` when it matches
+// the call's token count (and CP size, when the call has one).
+void hint_from_record(const void* meta, int64_t total_tokens, int32_t cp_size, PermuteArgs* a) {
+  a->hint_policy = -1;
+  a->hint_docs = -1;
+  std::lock_guard<std::mutex> lock(g_records_mu);
+  auto it = g_records.find(meta);
+  if (it == g_records.end()) return;
+  const MetaRecord& r = it->second;
+  if (r.total_tokens != total_tokens || (cp_size > 0 && r.cp_size != cp_size)) return;
+  a->hint_policy = r.policy;
+  a->hint_docs = r.num_docs;
+}
 
 Range range_of(const void* p, int64_t bytes) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(p);
@@ -189,8 +222,11 @@ int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tok
   if ((st = check_alias({range_of(meta, (int64_t)meta_bytes)},
                         {range_of(cu_seqlens, 4 * (int64_t)(num_docs + 1))})) != CP_OK)
     return st;
-  return hip_status(launch_build_meta(cu_seqlens, num_docs, total_tokens, cp_size, policy, meta,
-                                      reinterpret_cast<hipStream_t>(stream)));
+  if ((st = hip_status(launch_build_meta(cu_seqlens, num_docs, total_tokens, cp_size, policy, meta,
+                                         reinterpret_cast<hipStream_t>(stream)))) != CP_OK)
+    return st;
+  remember_meta(meta, MetaRecord{policy, num_docs, cp_size, total_tokens});
+  return CP_OK;
 }
 
 size_t cp_attn_meta_bytes(int32_t num_docs, int32_t cp_size) {
@@ -277,6 +313,7 @@ static int layout_call(int32_t n_tensors, const void* const* ins, void* const* o
   a.row_bytes = row_bytes;
   a.expect_cp_size = -1;
   a.expect_policy = -1;
+  hint_from_record(meta, total_tokens, -1, &a);
   return hip_status(launch_permute(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -404,6 +441,7 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
       a.row_bytes = in_row;
       a.expect_cp_size = W;
       a.expect_policy = -1;  // the owner's rows follow the metadata's policy
+      hint_from_record(meta, total_tokens, W, &a);
       if ((st = hip_status(launch_permute(a, s))) != CP_OK) return st;
     }
   }

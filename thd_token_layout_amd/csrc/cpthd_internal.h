@@ -73,6 +73,11 @@ struct PermuteArgs {
   int64_t row_bytes;
   int32_t expect_cp_size;   // -1: any
   int32_t expect_policy;    // -1: any
+  // Host-side record of the metadata (policy and document count when the host
+  // built it at this address; -1: unknown).  Chooses the tile shape only: the
+  // kernels read the metadata itself on the device.
+  int32_t hint_policy;
+  int32_t hint_docs;
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 

@@ -230,6 +230,94 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
   }
 }
 
+// Unit-granular variant: the rows x units space of the side being written is
+// cut into tiles of kBlock*NP consecutive 16-byte units (a tile may start and
+// end inside a row), so the tile size no longer depends on the row length.  The
+// first threads of the workgroup look up the source and destination of the
+// <= kFlatMaxRows rows a tile touches and share them through LDS; the row of a
+// unit is a multiply-high by `upr_magic` = ceil(2^32 / units_per_row), exact
+// while (tile units + units_per_row) * units_per_row < 2^32.  The lookups sit
+// on the workgroup's critical path, so this pays off only where a row lookup is
+// a few instructions: packed-contiguous metadata and single-document
+// dual-chunk-swap metadata (measured on MI355X: +4..13% over the row tiles
+// there, 10..40% slower with ~100 documents).
+constexpr int kFlatMaxRows = 16;
+
+template <int NP, bool GORDER>
+__global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uint32_t upr_magic) {
+  __shared__ const u32x4* s_src[kFlatMaxRows];
+  __shared__ u32x4* s_dst[kFlatMaxRows];
+  cp_meta_header* h = a.meta;
+  if (!meta_ok(h, a.total_tokens, a.expect_cp_size, a.expect_policy)) return;
+
+  const int64_t T = a.total_tokens;
+  const int32_t W = h->cp_size;
+  const int32_t B = h->num_docs;
+  const int64_t n = h->local_tokens;
+  const bool dcs = h->policy == CP_POLICY_DUAL_CHUNK_SWAP;
+  const int32_t* cu = meta_cu(h);
+  const int32_t* lcu = meta_local_cu0(h);
+  const int64_t upr = a.row_bytes / 16;
+  const int64_t total = T * upr;
+  constexpr int64_t kTileUnits = (int64_t)kBlock * NP;
+  const int64_t ntiles = (total + kTileUnits - 1) / kTileUnits;
+  const int tsr = blockIdx.y;
+  char* const gbase = a.global[tsr];
+  char* const lbase = a.local[tsr];
+
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t u0 = tile * kTileUnits;
+    const int64_t row0 = u0 / upr;
+    const int64_t u_end = u0 + kTileUnits < total ? u0 + kTileUnits : total;
+    const int nrows = (int)((u_end - 1) / upr - row0 + 1);
+    if ((int)threadIdx.x < nrows) {
+      // row p of the written side: a global row (gather) or a flat local row r*n + i
+      const int64_t p = row0 + threadIdx.x;
+      int32_t r;
+      int64_t i, g;
+      if constexpr (GORDER) {
+        g = p;
+        if (dcs) {
+          GCursor gc;
+          gseek(gc, p, B, cu, lcu);
+          glocal(gc, W, &r, &i);
+        } else {
+          r = (int32_t)(p / n);
+          i = p - (int64_t)r * n;
+        }
+      } else {
+        Cursor k;
+        seek(k, p, n, B, dcs, cu, lcu);
+        r = k.r;
+        i = k.i;
+        g = global_row(k, W, n, dcs);
+      }
+      char* gptr = gbase + g * a.row_bytes;
+      char* lptr = a.local_table ? a.table.p[r] + i * a.row_bytes : lbase + ((int64_t)r * n + i) * a.row_bytes;
+      s_src[threadIdx.x] = reinterpret_cast<const u32x4*>(a.to_local ? gptr : lptr);
+      s_dst[threadIdx.x] = reinterpret_cast<u32x4*>(a.to_local ? lptr : gptr);
+    }
+    __syncthreads();
+    const int64_t base = u0 - row0 * upr;  // offset of the tile's first unit inside row0
+    u32x4 v[NP];
+    int row[NP];
+    int64_t col[NP];
+    bool ok[NP];
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+      const uint32_t f = (uint32_t)(base + (int64_t)m * kBlock + threadIdx.x);
+      ok[m] = u0 + (int64_t)m * kBlock + threadIdx.x < u_end;
+      row[m] = ok[m] ? (int)__umulhi(f, upr_magic) : 0;
+      col[m] = (int64_t)f - (int64_t)row[m] * upr;
+      if (ok[m]) v[m] = load_nt(s_src[row[m]] + col[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < NP; ++m)
+      if (ok[m]) store_nt(s_dst[row[m]] + col[m], v[m]);
+    __syncthreads();  // s_src / s_dst are rewritten by the next tile
+  }
+}
+
 typedef void (*PermuteKernel)(PermuteArgs);
 
 struct Variant {
@@ -265,6 +353,25 @@ Variant g_variants[4][7] = {
     CP_VARIANTS_FOR(unsigned short, "2B"),
 };
 
+// Flat tiles (see permute_flat_kernel): NP units per thread, by the policy and
+// document count the host recorded when it built the metadata.  Swept on
+// MI355X over 2, 5, 8 and 10 KiB rows: packed-contiguous streams best with 2
+// units per thread (8 KiB tiles), single-document dual-chunk-swap with 3.
+// 0: keep the row tiles.
+int flat_units_per_thread(const PermuteArgs& a, int64_t upr) {
+  int np = 0;
+  if (a.hint_policy == CP_POLICY_PACKED_CONTIGUOUS) np = 2;
+  else if (a.hint_policy == CP_POLICY_DUAL_CHUNK_SWAP && a.hint_docs == 1) np = 3;
+  if (np == 0 || upr <= 0) return 0;
+  const int64_t tile_units = (int64_t)kBlock * np;
+  if (tile_units / upr + 2 > kFlatMaxRows) return 0;            // short rows: row tiles
+  if ((tile_units + upr) * upr >= (int64_t(1) << 32)) return 0;  // row split would not be exact
+  return np;
+}
+
+const char* const kFlatNames[2][2] = {{"permute_flat<16B,2>", "permute_flat<16B,2,g>"},
+                                      {"permute_flat<16B,3>", "permute_flat<16B,3,g>"}};
+
 }  // namespace
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
@@ -287,11 +394,23 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   for (int k = 0; k < 7; ++k)
     if (upr <= kUprLimit[k]) { vi = k; break; }
   const Variant& v = g_variants[ui][vi];
-  const int64_t tiles = (a.total_tokens + v.rows_per_tile - 1) / v.rows_per_tile;
-  const int blocks = (int)(tiles < kMaxGrid ? tiles : kMaxGrid);  // grid-stride beyond kMaxGrid
   // Visit rows in the order of the side being written: a gather writes the
   // global layout, partition and scatter write the per-rank layout.
   const int order = a.to_local ? 0 : 1;
+  const int np = ui == 0 ? flat_units_per_thread(a, upr) : 0;
+  PermuteKernel row_fn = v.fn[order];
+  void (*flat_fn)(PermuteArgs, uint32_t) = nullptr;
+  const char* name = v.name[order];
+  int64_t tiles = (a.total_tokens + v.rows_per_tile - 1) / v.rows_per_tile;
+  uint32_t magic = 0;
+  if (np != 0) {
+    flat_fn = np == 2 ? (order ? permute_flat_kernel<2, true> : permute_flat_kernel<2, false>)
+                      : (order ? permute_flat_kernel<3, true> : permute_flat_kernel<3, false>);
+    name = kFlatNames[np - 2][order];
+    tiles = (a.total_tokens * upr + (int64_t)kBlock * np - 1) / ((int64_t)kBlock * np);
+    magic = (uint32_t)(((uint64_t(1) << 32) + (uint64_t)upr - 1) / (uint64_t)upr);
+  }
+  const int blocks = (int)(tiles < kMaxGrid ? tiles : kMaxGrid);  // grid-stride beyond kMaxGrid
   // Several tensors: one launch (a tensor per grid row) when each tensor is
   // small, one launch per tensor when each moves >= 1 GiB.  Measured on
   // MI355X: Q,K,V of 32768 x 8 x 128 bf16 run 19% faster in one launch, of
@@ -303,16 +422,18 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
       b.n_tensors = 1;
       b.global[0] = a.global[t];
       b.local[0] = a.local[t];
-      profile_before(v.name[order], stream);
-      hipLaunchKernelGGL(v.fn[order], dim3(blocks, 1), dim3(kBlock), 0, stream, b);
+      profile_before(name, stream);
+      if (flat_fn) hipLaunchKernelGGL(flat_fn, dim3(blocks, 1), dim3(kBlock), 0, stream, b, magic);
+      else hipLaunchKernelGGL(row_fn, dim3(blocks, 1), dim3(kBlock), 0, stream, b);
       hipError_t e = hipGetLastError();
       profile_after(stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
   }
-  profile_before(v.name[order], stream);
-  hipLaunchKernelGGL(v.fn[order], dim3(blocks, a.n_tensors), dim3(kBlock), 0, stream, a);
+  profile_before(name, stream);
+  if (flat_fn) hipLaunchKernelGGL(flat_fn, dim3(blocks, a.n_tensors), dim3(kBlock), 0, stream, a, magic);
+  else hipLaunchKernelGGL(row_fn, dim3(blocks, a.n_tensors), dim3(kBlock), 0, stream, a);
   hipError_t e = hipGetLastError();
   profile_after(stream);
   return e;
