@@ -239,7 +239,8 @@ def test_more_tiles_than_the_grid(cp):
 @pytest.mark.parametrize("pol,lengths", [
     (1, [7, 0, 93, 20]), (1, [120]),          # packed-contiguous: 8 KiB unit tiles
     (0, [120]), (0, [8]),                     # one document: 12 KiB unit tiles
-    (0, [16, 0, 8]),                          # several documents: row tiles
+    (0, [16, 0, 8, 0, 40, 8, 0, 24]),         # a few documents: 12 KiB unit tiles
+    (0, [8] * 17),                            # more than 16 documents: row tiles
 ])
 @pytest.mark.parametrize("units", [55, 65, 100, 333, 1280])
 def test_unit_tiles_ragged(cp, pol, lengths, units):

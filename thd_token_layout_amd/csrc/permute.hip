@@ -238,9 +238,10 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
 // unit is a multiply-high by `upr_magic` = ceil(2^32 / units_per_row), exact
 // while (tile units + units_per_row) * units_per_row < 2^32.  The lookups sit
 // on the workgroup's critical path, so this pays off only where a row lookup is
-// a few instructions: packed-contiguous metadata and single-document
-// dual-chunk-swap metadata (measured on MI355X: +4..13% over the row tiles
-// there, 10..40% slower with ~100 documents).
+// a few instructions: packed-contiguous metadata and dual-chunk-swap metadata
+// of at most 16 documents (a binary search of <= 4 steps).  Measured on MI355X:
+// +4..13% over the row tiles there, about even at 32 documents, 5..10% slower
+// at 64-128.
 constexpr int kFlatMaxRows = 16;
 
 template <int NP, bool GORDER>
@@ -356,12 +357,13 @@ Variant g_variants[4][7] = {
 // Flat tiles (see permute_flat_kernel): NP units per thread, by the policy and
 // document count the host recorded when it built the metadata.  Swept on
 // MI355X over 2, 5, 8 and 10 KiB rows: packed-contiguous streams best with 2
-// units per thread (8 KiB tiles), single-document dual-chunk-swap with 3.
+// units per thread (8 KiB tiles), dual-chunk-swap with few documents with 3.
 // 0: keep the row tiles.
+constexpr int kFlatMaxDocs = 16;
 int flat_units_per_thread(const PermuteArgs& a, int64_t upr) {
   int np = 0;
   if (a.hint_policy == CP_POLICY_PACKED_CONTIGUOUS) np = 2;
-  else if (a.hint_policy == CP_POLICY_DUAL_CHUNK_SWAP && a.hint_docs == 1) np = 3;
+  else if (a.hint_policy == CP_POLICY_DUAL_CHUNK_SWAP && a.hint_docs >= 1 && a.hint_docs <= kFlatMaxDocs) np = 3;
   if (np == 0 || upr <= 0) return 0;
   const int64_t tile_units = (int64_t)kBlock * np;
   if (tile_units / upr + 2 > kFlatMaxRows) return 0;            // short rows: row tiles
