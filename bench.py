@@ -325,8 +325,32 @@ def per_config(cp, WL, torch, dev, reps: int = 10):
     return results
 
 
+def graph_us_per_call(cp, torch, slots, out, calls: int = 100, replays: int = 5):
+    """The same call captured `calls` times back to back in one HIP graph and replayed:
+    per-call time without host work or per-launch submission."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        cp.cp_slot_sum(slots, out)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            cp.cp_slot_sum(slots, out)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / (calls * replays)
+
+
 def sweep_latency(step: Step, cp, torch, reps: int = 200):
-    """Per-call latency (host validation + launch + kernel) of the W=8 slot sum."""
+    """Per-call latency of the W=8 slot sum: eager (host validation + launch + kernel),
+    the kernel alone (HIP events around each launch), and replayed from a HIP graph."""
     res = []
     for nbytes, slots, out in step.sweep:
         for _ in range(5):
@@ -347,7 +371,8 @@ def sweep_latency(step: Step, cp, torch, reps: int = 200):
         kcount = sum(c for c, _ in prof.values())
         kms = sum(m for _, m in prof.values())
         res.append({"bytes_per_slot": nbytes, "us_per_call": round(per_call_us, 2),
-                    "kernel_us": round(kms * 1000.0 / max(kcount, 1), 2)})
+                    "kernel_us": round(kms * 1000.0 / max(kcount, 1), 2),
+                    "graph_us_per_call": round(graph_us_per_call(cp, torch, slots, out), 2)})
     return res
 
 
