@@ -240,7 +240,8 @@ def test_more_tiles_than_the_grid(cp):
     (1, [7, 0, 93, 20]), (1, [120]),          # packed-contiguous: 8 KiB unit tiles
     (0, [120]), (0, [8]),                     # one document: 12 KiB unit tiles
     (0, [16, 0, 8, 0, 40, 8, 0, 24]),         # a few documents: 12 KiB unit tiles
-    (0, [8] * 17),                            # more than 16 documents: row tiles
+    (0, [8, 0, 16] * 13),                     # 39 documents: unit tiles, tables staged in LDS
+    (0, [8] * 65),                            # more than 64 documents: row tiles
 ])
 @pytest.mark.parametrize("units", [55, 65, 100, 333, 1280])
 def test_unit_tiles_ragged(cp, pol, lengths, units):
@@ -261,6 +262,31 @@ def test_unit_tiles_ragged(cp, pol, lengths, units):
     for x, p, bk in zip(xs, parts, backs):
         assert bits_equal(to_np(p), O.partition(to_np(x), cu, W, policy_name(pol)))
         assert bits_equal(to_np(bk), to_np(x))
+
+
+def test_stale_host_record_changes_no_result(cp):
+    """The host's record of a metadata buffer only picks the tile shape.  Overwrite a
+    buffer built for 3 documents with metadata of 100 documents (a plain device copy,
+    which the host does not see): the unit-tile kernel then finds more documents than
+    it can stage and searches the metadata itself; the result still equals the oracle."""
+    say("case stale host record")
+    W, T = 4, 800
+    cu_small = np.array([0, 200, 200, 800], dtype=np.int32)
+    cu_big = np.arange(0, T + 1, 8, dtype=np.int32)  # 100 documents of 8 tokens
+    x = torch.randint(-2**15, 2**15, (T, 1, 520), dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    for pol in (cp.CP_POLICY_DUAL_CHUNK_SWAP, cp.CP_POLICY_PACKED_CONTIGUOUS):
+        big = build(cp, cu_big, T, W, pol)
+        buf = torch.zeros(big.buf.numel(), dtype=torch.uint8, device=DEV)
+        small = cp.cp_build_meta(torch.from_numpy(cu_small).to(DEV), T, W, cp.CP_POLICY_DUAL_CHUNK_SWAP,
+                                 meta=buf, check=True)
+        buf.copy_(big.buf)  # the record still says: dual-chunk-swap, 3 documents
+        stale = cp.Meta(buf, W, pol, len(cu_big) - 1, T)
+        parts = cp.cp_partition_thd(x, stale)
+        back = cp.cp_gather_thd(parts, stale)
+        assert bits_equal(to_np(parts), O.partition(to_np(x), cu_big, W, policy_name(pol))), pol
+        assert bits_equal(to_np(back), to_np(x)), pol
+        assert cp.cp_meta_status(stale)[0] == cp.CP_OK
+        del small
 
 
 def test_unit_tiles_more_than_the_grid(cp):

@@ -237,17 +237,21 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
 // <= kFlatMaxRows rows a tile touches and share them through LDS; the row of a
 // unit is a multiply-high by `upr_magic` = ceil(2^32 / units_per_row), exact
 // while (tile units + units_per_row) * units_per_row < 2^32.  The lookups sit
-// on the workgroup's critical path, so this pays off only where a row lookup is
-// a few instructions: packed-contiguous metadata and dual-chunk-swap metadata
-// of at most 16 documents (a binary search of <= 4 steps).  Measured on MI355X:
-// +4..13% over the row tiles there, about even at 32 documents, 5..10% slower
-// at 64-128.
+// on the workgroup's critical path (one barrier per tile), so under
+// dual-chunk-swap the document tables (<= kFlatMaxDocs documents) are first
+// staged in LDS with one coalesced load and searched there.  Measured on
+// MI355X against the row tiles: +4..13% for packed-contiguous and
+// single-document metadata, +3..5% at 32-64 documents, slower from ~128
+// documents (the staging then costs more than it saves).
 constexpr int kFlatMaxRows = 16;
+constexpr int kFlatMaxDocs = 64;
 
 template <int NP, bool GORDER>
 __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uint32_t upr_magic) {
   __shared__ const u32x4* s_src[kFlatMaxRows];
   __shared__ u32x4* s_dst[kFlatMaxRows];
+  __shared__ int32_t s_cu[kFlatMaxDocs + 1];
+  __shared__ int32_t s_lcu[kFlatMaxDocs + 1];
   cp_meta_header* h = a.meta;
   if (!meta_ok(h, a.total_tokens, a.expect_cp_size, a.expect_policy)) return;
 
@@ -256,8 +260,18 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
   const int32_t B = h->num_docs;
   const int64_t n = h->local_tokens;
   const bool dcs = h->policy == CP_POLICY_DUAL_CHUNK_SWAP;
-  const int32_t* cu = meta_cu(h);
-  const int32_t* lcu = meta_local_cu0(h);
+  // Document tables: staged in LDS when small enough, else read from the metadata.
+  const bool staged = dcs && B <= kFlatMaxDocs;
+  if (staged) {
+    const int32_t* mcu = meta_cu(h);
+    const int32_t* mlcu = meta_local_cu0(h);
+    for (int k = threadIdx.x; k <= B; k += kBlock) {
+      s_cu[k] = mcu[k];
+      s_lcu[k] = mlcu[k];
+    }
+  }
+  const int32_t* cu = staged ? s_cu : meta_cu(h);
+  const int32_t* lcu = staged ? s_lcu : meta_local_cu0(h);
   const int64_t upr = a.row_bytes / 16;
   const int64_t total = T * upr;
   constexpr int64_t kTileUnits = (int64_t)kBlock * NP;
@@ -271,6 +285,7 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
     const int64_t row0 = u0 / upr;
     const int64_t u_end = u0 + kTileUnits < total ? u0 + kTileUnits : total;
     const int nrows = (int)((u_end - 1) / upr - row0 + 1);
+    __syncthreads();  // staged tables written; the previous tile's s_src / s_dst consumed
     if ((int)threadIdx.x < nrows) {
       // row p of the written side: a global row (gather) or a flat local row r*n + i
       const int64_t p = row0 + threadIdx.x;
@@ -315,7 +330,6 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
 #pragma unroll
     for (int m = 0; m < NP; ++m)
       if (ok[m]) store_nt(s_dst[row[m]] + col[m], v[m]);
-    __syncthreads();  // s_src / s_dst are rewritten by the next tile
   }
 }
 
@@ -357,9 +371,8 @@ Variant g_variants[4][7] = {
 // Flat tiles (see permute_flat_kernel): NP units per thread, by the policy and
 // document count the host recorded when it built the metadata.  Swept on
 // MI355X over 2, 5, 8 and 10 KiB rows: packed-contiguous streams best with 2
-// units per thread (8 KiB tiles), dual-chunk-swap with few documents with 3.
+// units per thread (8 KiB tiles), dual-chunk-swap with <= 64 documents with 3.
 // 0: keep the row tiles.
-constexpr int kFlatMaxDocs = 16;
 int flat_units_per_thread(const PermuteArgs& a, int64_t upr) {
   int np = 0;
   if (a.hint_policy == CP_POLICY_PACKED_CONTIGUOUS) np = 2;
