@@ -437,3 +437,39 @@ def test_grad_return_rejects_mismatch(cp):
     with pytest.raises(cp.CpError) as e:  # output aliasing an input
         cp.cp_grad_return_fused(grads, [[grads[0][0][:32], grads[0][1][32:]]], make_meta(cp, cu, 64, 2))
     assert e.value.status == cp.CP_ERR_ALIAS
+
+
+# ------------------------------------------------------------------ largest sizes
+def test_largest_sizes(cp):
+    """Fused gradient return at T = 2^31 - 8 tokens (W = 2, rows of 4 fp32) and a
+    slot sum over 2^31 + 5 elements: every offset past 2^31 elements is computed in
+    64 bits.  Sampled rows / elements against the oracle's map and sum."""
+    T, W = (1 << 31) - 8, 2
+    say(f"case largest sizes: fused T={T}, slot sum n={(1 << 31) + 5}")
+    cu = np.array([0, T], dtype=np.int32)
+    gen = torch.Generator(device=DEV).manual_seed(2)
+    grads = [[torch.randn((T, 1, 4), generator=gen, device=DEV) for _ in range(W)]]
+    meta = make_meta(cp, cu, T, W)
+    n = T // W
+    out = [[torch.empty((n, 1, 4), device=DEV) for _ in range(W)]]
+    cp.cp_grad_return_fused(grads, out, meta)
+    rng = np.random.default_rng(9)
+    for o in range(W):
+        idx = np.unique(np.concatenate([rng.integers(0, n, size=300), [0, n - 1]]))
+        g = torch.tensor([O.rank_row(cu, T, W, O.DUAL_CHUNK_SWAP, o, int(i)) for i in idx], device=DEV)
+        src = [to_np(grads[0][w].index_select(0, g)) for w in range(W)]
+        ref = O.slot_sum(src, "f32", "f32")
+        assert bits_equal(to_np(out[0][o].index_select(0, torch.from_numpy(idx).to(DEV))), ref), o
+    assert cp.cp_meta_status(meta)[0] == cp.CP_OK
+    del grads, out
+    torch.cuda.empty_cache()
+    m = (1 << 31) + 5
+    slots = [torch.randn(m, generator=gen, device=DEV) for _ in range(2)]
+    res = torch.empty(m, device=DEV)
+    cp.cp_slot_sum(slots, res)
+    idx = np.unique(np.concatenate([rng.integers(0, m, size=2000), [0, (1 << 31) - 1, 1 << 31, m - 1]]))
+    ti = torch.from_numpy(idx).to(DEV)
+    ref = O.slot_sum([to_np(s.index_select(0, ti)) for s in slots], "f32", "f32")
+    assert bits_equal(to_np(res.index_select(0, ti)), ref)
+    del slots, res
+    torch.cuda.empty_cache()

@@ -378,3 +378,43 @@ def test_meta_mismatch_and_host_errors(cp):
     with pytest.raises(cp.CpError) as e:
         cp.cp_build_meta(torch.tensor([0, 5, 10], dtype=torch.int32, device=DEV), 10, 4, 1)
     assert e.value.status == cp.CP_ERR_SHAPE
+
+
+# ------------------------------------------------------------------ largest token count
+def test_largest_token_count(cp):
+    """T = 2^31 - 8 tokens (the largest multiple of 2W = 8 the ABI accepts), rows of
+    16 bytes holding their own index: partition and gather under both policies,
+    the attention-step tables, every index kept in 64 bits where it must be.
+    Sampled rows against the oracle's one-row map."""
+    T, W = (1 << 31) - 8, 4
+    say(f"case largest token count T={T}")
+    x = torch.empty((T, 1, 2), dtype=torch.int64, device=DEV)
+    x[:, 0, 0] = torch.arange(T, dtype=torch.int64, device=DEV)
+    x[:, 0, 1] = -x[:, 0, 0]
+    xf = x.view(torch.float32).view(T, 1, 4)  # 16-byte rows
+    rng = np.random.default_rng(31)
+    n = T // W
+    for pol, cu in ((cp.CP_POLICY_DUAL_CHUNK_SWAP, np.array([0, T], dtype=np.int32)),
+                    (cp.CP_POLICY_PACKED_CONTIGUOUS, np.array([0, 1000, T - 8, T], dtype=np.int32))):
+        meta = build(cp, cu, T, W, pol)
+        parts = cp.cp_partition_thd(xf, meta)
+        for r in range(W):
+            idx = np.unique(np.concatenate([rng.integers(0, n, size=200), [0, n - 1]]))
+            got = parts[r][torch.from_numpy(idx).to(DEV)].view(torch.int64).view(-1, 2).cpu().numpy()
+            g = np.array([O.rank_row(cu, T, W, policy_name(pol), r, int(i)) for i in idx], dtype=np.int64)
+            assert (got[:, 0] == g).all() and (got[:, 1] == -g).all(), (pol, r)
+        back = torch.zeros_like(xf)
+        cp.cp_gather_thd(parts, meta, x=back)
+        del parts
+        idx = np.unique(np.concatenate([rng.integers(0, T, size=500), [0, T - 1]]))
+        got = back[torch.from_numpy(idx).to(DEV)].view(torch.int64).view(-1, 2).cpu().numpy()
+        assert (got[:, 0] == idx).all() and (got[:, 1] == -idx).all(), pol
+        del back
+        magic, tables = cp.read_attn_meta(cp.cp_build_attn_meta(meta), len(cu) - 1, W)
+        assert magic == cp.CP_ATTN_MAGIC
+        for k, v in O.attention_meta(cu, T, W, policy_name(pol)).items():
+            assert np.array_equal(tables[k].numpy(), v), (pol, k)
+        assert cp.cp_meta_status(meta)[0] == cp.CP_OK
+        torch.cuda.empty_cache()
+    del x, xf
+    torch.cuda.empty_cache()
