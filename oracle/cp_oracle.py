@@ -394,8 +394,9 @@ def slot_sum(slots, in_dtype, out_dtype, into=None):
     else:
         acc = _widen(into, out_dtype).astype(np.float32, copy=True)
         rest = slots
-    for s in rest:
-        acc = (acc + _widen(s, in_dtype)).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):  # IEEE: overflow -> inf, inf - inf -> NaN
+        for s in rest:
+            acc = (acc + _widen(s, in_dtype)).astype(np.float32)
     return _narrow(acc, out_dtype)
 
 
@@ -442,8 +443,9 @@ def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=DUAL_CHUNK
         else:
             acc = _widen(into[o], out_dtype).astype(np.float32, copy=True)
             first = 0
-        for w in range(first, W):
-            acc = (acc + _widen(grads[w][rows], in_dtype)).astype(np.float32)
+        with np.errstate(over="ignore", invalid="ignore"):
+            for w in range(first, W):
+                acc = (acc + _widen(grads[w][rows], in_dtype)).astype(np.float32)
         out.append(_narrow(acc, out_dtype))
     return out
 
