@@ -25,8 +25,11 @@
  * Conventions common to every entry point
  *  - Every data pointer is a device pointer of the CURRENT HIP device,
  *    allocated by the caller ([MM]; [GR] "Description": peer tensor views are
- *    supplied by the caller).  The library allocates no device memory and
- *    keeps no state between calls (cp_profile_* aside).
+ *    supplied by the caller).  The library allocates no device memory.  The
+ *    only host state kept between calls is the timing record of cp_profile_*
+ *    and, per metadata buffer built by cp_build_meta, its policy and sizes,
+ *    used to choose kernel tile shapes only (every kernel reads the metadata
+ *    itself, so a buffer rewritten by other means still gives exact results).
  *  - Host pointer tables (const void* const*) are read only during the call.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream) and never synchronizes, except cp_meta_status and
@@ -61,8 +64,8 @@ typedef struct ihipStream_t* cp_stream_t;
 enum cp_status {
   CP_OK = 0,
   CP_ERR_ARG = 1,         /* bad scalar argument or NULL pointer             */
-  CP_ERR_UNSUPPORTED = 2, /* dtype / mode not supported (FP8, grad-return
-                             under packed-contiguous, ...)                   */
+  CP_ERR_UNSUPPORTED = 2, /* dtype / mode not supported (FP8, a gradient
+                             dtype pair other than the four listed)          */
   CP_ERR_SHAPE = 3,       /* sizes inconsistent (T % W under PC, buffer too
                              small, ...)                                     */
   CP_ERR_DEVICE = 4,      /* a pointer is not device memory of the current
@@ -139,7 +142,7 @@ enum cp_dtype {
 #define CP_CALL_BAD_MAGIC         0x0100 /* meta was never built                         */
 #define CP_CALL_TOKENS_MISMATCH   0x0200 /* total_tokens differs from the meta's          */
 #define CP_CALL_CP_SIZE_MISMATCH  0x0400 /* cp_size differs from the meta's               */
-#define CP_CALL_POLICY_MISMATCH   0x0800 /* call needs the other policy (none does today) */
+#define CP_CALL_POLICY_MISMATCH   0x0800 /* reserved: a call bound to the other policy     */
 #define CP_CALL_USED_INVALID_META 0x1000 /* a kernel met invalid metadata and did nothing */
 #define CP_CALL_DOCS_MISMATCH     0x2000 /* num_docs differs from the meta's              */
 
