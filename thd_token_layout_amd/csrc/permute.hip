@@ -5,17 +5,20 @@
 // dual-chunk-swap rank r holds chunk r then chunk 2W-1-r of every document;
 // under packed-contiguous rank r holds tokens [r n, (r+1) n), n = T/W.
 //
-// Design (gfx950): pure data movement, HBM-bound.  A workgroup (4 waves) owns
-// a tile of consecutive local rows (8-20 KiB); the launch covers every tile
-// (a full grid, not a persistent one:
-// measured on MI355X, concurrently running workgroups then stream one
-// contiguous window of HBM and a copy reaches ~5.8 TB/s, against ~4.7 TB/s for
-// a resident-capacity grid-stride loop).  The row map is computed once per
-// group in wave-uniform (scalar) code: a binary search over the per-rank
-// document table, then an incremental cursor for the rest of the group.  Each
-// lane then moves 16-byte units of the G rows (VPL units per row, up to G*VPL
-// loads in flight per lane) with non-temporal loads and stores, fully
-// coalesced (a wave touches 1 KiB contiguous per instruction).
+// Design (gfx950): pure data movement, HBM-bound.  Two tilings, both with a
+// full grid (one tile per workgroup; measured on MI355X, concurrently running
+// workgroups then stream one contiguous window of HBM, while a resident-
+// capacity grid-stride loop, or several tiles per workgroup, streamed 5-20%
+// slower):
+//  - row tiles (permute_rows_kernel): a workgroup (4 waves) owns 8-20 KiB of
+//    consecutive local rows; the row map is computed once per group in
+//    wave-uniform (scalar) code, a binary search over the per-rank document
+//    table and then an incremental cursor, so each wave runs independently;
+//  - unit tiles (permute_flat_kernel): a workgroup owns a fixed number of
+//    16-byte units whatever the row length, with the touched rows looked up
+//    into LDS; used where that lookup is cheap (see there).
+// Lanes move 16-byte units with non-temporal loads and stores, fully coalesced
+// (a wave touches 1 KiB contiguous per instruction).
 #include "device_common.h"
 
 

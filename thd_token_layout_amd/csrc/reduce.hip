@@ -8,6 +8,10 @@
 // accumulator starts as slot 0 (widened exactly) and each further slot is added
 // once, in writer order; the result is rounded once to the output type
 // (bf16: round-to-nearest-even on the bit pattern, NaN kept quiet with its sign).
+// In the accumulate mode the accumulator starts from the owner's current value
+// (widened) and slots 0..cp_size-1 are all added, one at a time, in order.
+// The owner's rows follow the metadata's policy (two-chunk layout under
+// dual-chunk-swap, the contiguous slice under packed-contiguous).
 //
 // On one GPU the writers' and owners' streams share one HBM; an epoch store is
 // an agent-scope release store, the wait is a bounded spin with agent-scope
