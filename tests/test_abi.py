@@ -95,6 +95,10 @@ def test_host_checks_before_any_hip_call(cp):
     assert lib.cp_build_meta(FAKE, 3, 48, 0, 0, FAKE, 4096, None) == cp.CP_ERR_ARG
     assert lib.cp_build_meta(FAKE, 3, 48, 65, 0, FAKE, 4096, None) == cp.CP_ERR_ARG
     assert lib.cp_build_meta(FAKE, 3, 48, 2, 7, FAKE, 4096, None) == cp.CP_ERR_ARG
+    # the retired whole-buffer "super sequence" selector has no policy value of its own
+    # (its layout is dual-chunk-swap with cu = [0, T]); a third selector is rejected
+    assert lib.cp_build_meta(FAKE, 3, 48, 2, 2, FAKE, 4096, None) == cp.CP_ERR_ARG
+    assert set(cp.POLICY) == {"dual_chunk_swap", "packed_contiguous"}
     assert lib.cp_build_meta(FAKE, 3, 50, 4, 1, FAKE, 4096, None) == cp.CP_ERR_SHAPE
     assert lib.cp_build_meta(FAKE, 3, 48, 2, 0, FAKE, 16, None) == cp.CP_ERR_SHAPE
     assert lib.cp_build_meta(None, 3, 48, 2, 0, FAKE, 4096, None) == cp.CP_ERR_ARG
