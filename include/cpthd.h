@@ -46,6 +46,11 @@
  *    cp_meta_status reports both.
  *  - Outputs must not overlap inputs or each other (CP_ERR_ALIAS); [GR]
  *    "Description" (self-alias assertions on the rank-self slots).
+ *  - Every buffer must be device memory of the current device (else
+ *    CP_ERR_DEVICE) and, as far as the runtime reports allocation extents,
+ *    lie inside one allocation for the byte count the call's sizes imply
+ *    (else CP_ERR_SHAPE: the buffer is smaller than the sizes say).  Sizes
+ *    whose byte counts would exceed 2^62 give CP_ERR_ARG.
  */
 #ifndef CPTHD_H
 #define CPTHD_H

@@ -103,6 +103,11 @@ def test_host_checks_before_any_hip_call(cp):
     assert lib.cp_build_meta(FAKE, 3, 48, 2, 0, FAKE, 16, None) == cp.CP_ERR_SHAPE
     assert lib.cp_build_meta(None, 3, 48, 2, 0, FAKE, 4096, None) == cp.CP_ERR_ARG
     assert lib.cp_build_meta(FAKE, 3, -1, 2, 0, FAKE, 4096, None) == cp.CP_ERR_ARG
+    # byte counts that would overflow are rejected before any pointer is looked at
+    assert lib.cp_partition_thd(FAKE, FAKE, (1 << 31) - 8, 1 << 30, 1 << 30, cp.CP_BF16, FAKE, None) \
+        == cp.CP_ERR_ARG
+    assert lib.cp_slot_sum(2, (ctypes.c_void_p * 2)(0x10000, 0x20000), FAKE, 1 << 62, cp.CP_F32, cp.CP_F32,
+                           0, None) == cp.CP_ERR_ARG
     # attention steps: NULLs, ranges, buffer size
     am = lib.cp_build_attn_meta
     assert am(None, 3, 2, FAKE, 4096, None) == cp.CP_ERR_ARG
@@ -141,6 +146,8 @@ def test_host_checks_before_any_hip_call(cp):
         == cp.CP_ERR_ARG
     assert gr(-1, 2, 0, tab, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0, 15, None) \
         == cp.CP_ERR_ARG
+    assert gr(-1, 2, 2, tab, tab, tab, 48, 1 << 30, 1 << 30, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0, 15,
+              None) == cp.CP_ERR_ARG
     for bad_phases in (0, cp.CP_SUM_ACCUMULATE, 0x20 | cp.CP_PHASE_ALL, -1):
         assert gr(-1, 2, 2, tab, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, None, 0, 0,
                   bad_phases, None) == cp.CP_ERR_ARG

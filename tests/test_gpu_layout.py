@@ -3,6 +3,8 @@ CPU oracle: bit-exact, on the tiny hand-worked case, the packed-document
 workloads at full size, the S=262144 shapes (full compare of one tensor plus
 round trips), and edge cases (empty input and documents, W=1 and W=64, ragged
 and unaligned rows, invalid and mismatched metadata)."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -262,6 +264,29 @@ def test_unit_tiles_ragged(cp, pol, lengths, units):
     for x, p, bk in zip(xs, parts, backs):
         assert bits_equal(to_np(p), O.partition(to_np(x), cu, W, policy_name(pol)))
         assert bits_equal(to_np(bk), to_np(x))
+
+
+def test_buffers_smaller_than_the_sizes_are_rejected(cp):
+    """A call whose sizes run past the end of a buffer's allocation is refused on the
+    host (CP_ERR_SHAPE) before anything is launched."""
+    say("case buffers past their allocation")
+    torch.cuda.empty_cache()
+    x = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    parts = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    meta = build(cp, np.array([0, 64], dtype=np.int32), 64, 4, cp.CP_POLICY_DUAL_CHUNK_SWAP)
+    T = (1 << 31) - 8  # 2^31 rows of 512 bytes: 1 TiB, more than the device holds
+    st = cp.lib.cp_partition_thd(x.data_ptr(), parts.data_ptr(), T, 1, 256, cp.CP_BF16, meta.ptr(), None)
+    assert st == cp.CP_ERR_SHAPE
+    st = cp.lib.cp_slot_sum(2, (ctypes.c_void_p * 2)(x.data_ptr(), parts.data_ptr()), parts.data_ptr(),
+                            1 << 38, cp.CP_F32, cp.CP_F32, 0, None)
+    assert st == cp.CP_ERR_SHAPE
+    grads = (ctypes.c_void_p * 2)(x.data_ptr(), x.data_ptr())
+    outs = (ctypes.c_void_p * 2)(parts.data_ptr(), parts.data_ptr())
+    st = cp.lib.cp_grad_return_fused(-1, 2, 1, grads, outs, T - 2040, 1, 256, cp.CP_F32, cp.CP_F32,
+                                     meta.ptr(), 0, None)
+    assert st == cp.CP_ERR_SHAPE
+    torch.cuda.synchronize()
+    assert (x == 0).all() and (parts == 0).all()  # nothing was launched
 
 
 def test_stale_host_record_changes_no_result(cp):

@@ -87,8 +87,12 @@ int current_device(int* dev) {
   return CP_OK;
 }
 
-// The pointer must be device memory owned by device `dev`.
-int check_device_ptr(const void* p, int dev) {
+// [p, p + bytes) must be device memory of device `dev` (CP_ERR_DEVICE) and lie
+// inside one allocation (CP_ERR_SHAPE: the buffer is smaller than the call's
+// sizes say), so that no kernel can touch memory outside what the caller
+// passed.  When the runtime cannot report the allocation's extent, the
+// membership check alone applies.
+int check_device_buf(const void* p, int64_t bytes, int dev) {
   if (p == nullptr) return CP_ERR_ARG;
   hipPointerAttribute_t attr;
   memset(&attr, 0, sizeof(attr));
@@ -97,7 +101,23 @@ int check_device_ptr(const void* p, int dev) {
     return CP_ERR_DEVICE;
   }
   if (attr.type != hipMemoryTypeDevice || attr.device != dev) return CP_ERR_DEVICE;
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+    (void)hipGetLastError();
+    return CP_OK;
+  }
+  const uintptr_t end = reinterpret_cast<uintptr_t>(base) + size;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  if (a < reinterpret_cast<uintptr_t>(base) || bytes < 0 || (uint64_t)bytes > end - a) return CP_ERR_SHAPE;
   return CP_OK;
+}
+
+// rows * row_bytes, or -1 when it would exceed 2^62 bytes.
+int64_t checked_bytes(int64_t rows, int64_t row_bytes) {
+  if (rows < 0 || row_bytes < 0) return -1;
+  if (row_bytes != 0 && rows > (int64_t(1) << 62) / row_bytes) return -1;
+  return rows * row_bytes;
 }
 
 bool valid_layout_dtype(int32_t dt) { return dt == CP_F32 || dt == CP_BF16 || dt == CP_F16; }
@@ -217,8 +237,8 @@ int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tok
   if (meta_bytes < cp_meta_bytes(num_docs, cp_size)) return CP_ERR_SHAPE;
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
-  if ((st = check_device_ptr(cu_seqlens, dev)) != CP_OK) return st;
-  if ((st = check_device_ptr(meta, dev)) != CP_OK) return st;
+  if ((st = check_device_buf(cu_seqlens, 4 * (int64_t)(num_docs + 1), dev)) != CP_OK) return st;
+  if ((st = check_device_buf(meta, (int64_t)cp_meta_bytes(num_docs, cp_size), dev)) != CP_OK) return st;
   if ((st = check_alias({range_of(meta, (int64_t)meta_bytes)},
                         {range_of(cu_seqlens, 4 * (int64_t)(num_docs + 1))})) != CP_OK)
     return st;
@@ -242,8 +262,8 @@ int cp_build_attn_meta(const void* meta, int32_t num_docs, int32_t cp_size, void
   if (attn_bytes < cp_attn_meta_bytes(num_docs, cp_size)) return CP_ERR_SHAPE;
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
-  if ((st = check_device_ptr(meta, dev)) != CP_OK) return st;
-  if ((st = check_device_ptr(attn, dev)) != CP_OK) return st;
+  if ((st = check_device_buf(meta, (int64_t)cp_meta_bytes(num_docs, cp_size), dev)) != CP_OK) return st;
+  if ((st = check_device_buf(attn, (int64_t)cp_attn_meta_bytes(num_docs, cp_size), dev)) != CP_OK) return st;
   if ((st = check_alias({range_of(attn, (int64_t)attn_bytes)},
                         {range_of(meta, (int64_t)cp_meta_bytes(num_docs, cp_size))})) != CP_OK)
     return st;
@@ -255,7 +275,7 @@ int cp_meta_status(const void* meta, cp_stream_t stream, int32_t* flags_out,
   if (meta == nullptr) return CP_ERR_ARG;
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
-  if ((st = check_device_ptr(meta, dev)) != CP_OK) return st;
+  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev)) != CP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (hipStreamSynchronize(s) != hipSuccess) {
     (void)hipGetLastError();
@@ -286,15 +306,16 @@ static int layout_call(int32_t n_tensors, const void* const* ins, void* const* o
   if (ins == nullptr || outs == nullptr || meta == nullptr) return CP_ERR_ARG;
   for (int t = 0; t < n_tensors; ++t)
     if (ins[t] == nullptr || outs[t] == nullptr) return CP_ERR_ARG;
-  const int64_t row_bytes = (int64_t)heads * head_dim * dtype_bytes(dtype);
-  const int64_t bytes = total_tokens * row_bytes;
+  const int64_t row_bytes = checked_bytes((int64_t)heads * head_dim, dtype_bytes(dtype));
+  const int64_t bytes = checked_bytes(total_tokens, row_bytes);
+  if (row_bytes < 0 || bytes < 0) return CP_ERR_ARG;
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
-  if ((st = check_device_ptr(meta, dev)) != CP_OK) return st;
+  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev)) != CP_OK) return st;
   std::vector<Range> in_ranges{range_of(meta, sizeof(cp_meta_header))}, out_ranges;
   for (int t = 0; t < n_tensors; ++t) {
-    if ((st = check_device_ptr(ins[t], dev)) != CP_OK) return st;
-    if ((st = check_device_ptr(outs[t], dev)) != CP_OK) return st;
+    if ((st = check_device_buf(ins[t], bytes, dev)) != CP_OK) return st;
+    if ((st = check_device_buf(outs[t], bytes, dev)) != CP_OK) return st;
     in_ranges.push_back(range_of(ins[t], bytes));
     out_ranges.push_back(range_of(outs[t], bytes));
   }
@@ -353,6 +374,9 @@ static int grad_scalar_checks(int32_t rank, int32_t cp_size, int32_t n_tensors, 
   // (every document is a multiple of 2W), which the kernels check on the device.
   if (total_tokens % (int64_t)cp_size != 0) return CP_ERR_SHAPE;
   if (total_tokens > 0 && meta == nullptr) return CP_ERR_ARG;
+  // every buffer size fits comfortably in 64 bits
+  const int64_t row_elems = (int64_t)heads * head_dim;
+  if (checked_bytes(total_tokens, checked_bytes(row_elems, 4)) < 0) return CP_ERR_ARG;
   return CP_OK;
 }
 
@@ -396,25 +420,25 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
   }
   int dev;
   if ((st = current_device(&dev)) != CP_OK) return st;
-  if ((st = check_device_ptr(meta, dev)) != CP_OK) return st;
-  if (epochs && (st = check_device_ptr(epochs, dev)) != CP_OK) return st;
+  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev)) != CP_OK) return st;
+  if (epochs && (st = check_device_buf(epochs, 4 * (int64_t)W * W, dev)) != CP_OK) return st;
   std::vector<Range> ins, outs;
   ins.push_back(range_of(meta, sizeof(cp_meta_header)));
   for (int t = 0; t < n_tensors; ++t) {
     for (int w = w_lo; w < w_hi; ++w) {
-      if ((st = check_device_ptr(G(t, w), dev)) != CP_OK) return st;
+      if ((st = check_device_buf(G(t, w), total_tokens * in_row, dev)) != CP_OK) return st;
       ins.push_back(range_of(G(t, w), total_tokens * in_row));
       for (int o = 0; o < W; ++o) {
-        if ((st = check_device_ptr(S(t, o, w), dev)) != CP_OK) return st;
+        if ((st = check_device_buf(S(t, o, w), n * in_row, dev)) != CP_OK) return st;
         outs.push_back(range_of(S(t, o, w), n * in_row));
       }
     }
     for (int o = o_lo; o < o_hi; ++o) {
-      if ((st = check_device_ptr(O(t, o), dev)) != CP_OK) return st;
+      if ((st = check_device_buf(O(t, o), n * out_row, dev)) != CP_OK) return st;
       outs.push_back(range_of(O(t, o), n * out_row));
       for (int w = 0; w < W; ++w) {
         if (w >= w_lo && w < w_hi) continue;  // already listed as an output of this call
-        if ((st = check_device_ptr(S(t, o, w), dev)) != CP_OK) return st;
+        if ((st = check_device_buf(S(t, o, w), n * in_row, dev)) != CP_OK) return st;
         ins.push_back(range_of(S(t, o, w), n * in_row));
       }
     }
@@ -509,18 +533,18 @@ int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
   }
   int dev;
   if ((st = current_device(&dev)) != CP_OK) return st;
-  if ((st = check_device_ptr(meta, dev)) != CP_OK) return st;
+  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev)) != CP_OK) return st;
   std::vector<Range> ins, outs;
   ins.push_back(range_of(meta, sizeof(cp_meta_header)));
   for (int t = 0; t < n_tensors; ++t) {
     for (int w = 0; w < W; ++w) {
       const void* g = grads[(size_t)t * W + w];
-      if ((st = check_device_ptr(g, dev)) != CP_OK) return st;
+      if ((st = check_device_buf(g, total_tokens * in_row, dev)) != CP_OK) return st;
       ins.push_back(range_of(g, total_tokens * in_row));
     }
     for (int o = o_lo; o < o_hi; ++o) {
       void* p = out[(size_t)t * W + o];
-      if ((st = check_device_ptr(p, dev)) != CP_OK) return st;
+      if ((st = check_device_buf(p, n * out_row, dev)) != CP_OK) return st;
       outs.push_back(range_of(p, n * out_row));
     }
   }
@@ -550,6 +574,7 @@ int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t 
   int st;
   if ((st = check_sum_dtypes(in_dtype, out_dtype)) != CP_OK) return st;
   if (num_slots < 1 || num_slots > CP_MAX_CP_SIZE || n_elems < 0) return CP_ERR_ARG;
+  if (checked_bytes(n_elems, 4) < 0) return CP_ERR_ARG;
   if ((flags & ~CP_SUM_ACCUMULATE) != 0) return CP_ERR_ARG;
   if (n_elems == 0) return CP_OK;
   if (slots == nullptr || out == nullptr) return CP_ERR_ARG;
@@ -559,10 +584,10 @@ int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t 
   if ((st = current_device(&dev)) != CP_OK) return st;
   std::vector<Range> ins;
   for (int w = 0; w < num_slots; ++w) {
-    if ((st = check_device_ptr(slots[w], dev)) != CP_OK) return st;
+    if ((st = check_device_buf(slots[w], n_elems * dtype_bytes(in_dtype), dev)) != CP_OK) return st;
     ins.push_back(range_of(slots[w], n_elems * dtype_bytes(in_dtype)));
   }
-  if ((st = check_device_ptr(out, dev)) != CP_OK) return st;
+  if ((st = check_device_buf(out, n_elems * dtype_bytes(out_dtype), dev)) != CP_OK) return st;
   if ((st = check_alias({range_of(out, n_elems * dtype_bytes(out_dtype))}, ins)) != CP_OK) return st;
   SlotSumArgs a;
   memset(&a, 0, sizeof(a));
