@@ -387,6 +387,9 @@ def main():
     ap.add_argument("--no-sweep-latency", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload measurements (each config's ops timed alone)")
+    ap.add_argument("--only-configs", action="store_true",
+                    help="run only the per-workload measurements and print them as one JSON line "
+                         "(for profiling them on their own; not the benchmark line)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run one plain 1 GiB device copy (torch copy_) first, as the reference "
                          "dispatch for scaling hardware traffic counters")
@@ -412,6 +415,10 @@ def main():
         torch.cuda.synchronize()
         log("[bench] calibration copy: 1 GiB read + 1 GiB written")
         del a, b
+    if args.only_configs:
+        log("[bench] per-config measurements only")
+        print(json.dumps({"per_config": per_config(cp, WL, torch, dev)}), flush=True)
+        return
     log(f"[bench] building inputs S={args.tokens}")
     step = Step(cp, WL, torch, args.tokens, dev)
     torch.cuda.synchronize()
