@@ -186,7 +186,7 @@ def counted_traffic(kernel: str):
     return int(round(rec["traffic_bytes_per_launch"]))
 
 
-def cpu_baseline(S_sample: int, WL, passes: int = 2):
+def cpu_baseline(S_sample: int, WL, passes: int = 3):
     """The CPU oracle, as it stands, on the same step at S_sample tokens, `passes` times."""
     import numpy as np
     import torch
