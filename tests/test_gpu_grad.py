@@ -360,6 +360,36 @@ def test_per_rank_split_phases_with_delayed_writer(cp, W):
     check_per_rank_result(cp, meta, cu, grads, out, epochs, W, 9)
 
 
+def test_repeated_calls_reuse_slots_and_epochs(cp):
+    """Twelve gradient returns in a row on the same slots and epoch table (epoch
+    1, 2, ...), per-rank split phases on 4 streams with the last writer delayed
+    every time and new gradients each time: an owner that stopped waiting early
+    would sum the previous call's slots, so every call's output must equal the
+    oracle for that call's gradients."""
+    W = 4
+    say(f"case repeated per-rank calls W={W}")
+    cu, grads, meta, slots, out, epochs = per_rank_case(cp, W, 77)
+    streams = [torch.cuda.Stream() for _ in range(W)]
+    gen = torch.Generator(device=DEV).manual_seed(77)
+    for epoch in range(1, 13):
+        for t in range(2):
+            for w in range(W):
+                grads[t][w].copy_(torch.randn(grads[t][w].shape, generator=gen, device=DEV))
+        torch.cuda.synchronize()
+        for r in range(W):
+            with torch.cuda.stream(streams[r]):
+                if r == W - 1:
+                    torch.cuda._sleep(20_000_000)
+                cp.cp_grad_return(grads, slots, out, meta, rank=r, epochs=epochs, epoch=epoch,
+                                  phases=cp.CP_PHASE_SCATTER | cp.CP_PHASE_PUBLISH, stream=streams[r])
+        for r in range(W):
+            cp.cp_grad_return(grads, slots, out, meta, rank=r, epochs=epochs, epoch=epoch,
+                              wait_timeout_us=5_000_000, phases=cp.CP_PHASE_WAIT | cp.CP_PHASE_SUM,
+                              stream=streams[r])
+        torch.cuda.synchronize()
+        check_per_rank_result(cp, meta, cu, grads, out, epochs, W, epoch)
+
+
 def test_wait_blocks_until_host_releases_epoch(cp):
     """Rank 0 of W=2 runs alone: writer 1's slot data is already in place but its epoch
     is withheld.  While rank 0's device wait spins, its output still holds the poison
