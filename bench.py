@@ -348,7 +348,7 @@ def graph_us_per_call(cp, torch, slots, out, calls: int = 100, replays: int = 5)
     return e0.elapsed_time(e1) * 1000.0 / (calls * replays)
 
 
-def sweep_latency(step: Step, cp, torch, reps: int = 200):
+def sweep_latency(step: Step, cp, torch, reps: int = 1000):
     """Per-call latency of the W=8 slot sum: eager (host validation + launch + kernel),
     the kernel alone (HIP events around each launch), and replayed from a HIP graph."""
     res = []
