@@ -81,6 +81,41 @@ def test_attention_pairs_pc(case):
     pins.check_attention_pairs(o, cu, int(cu[-1]), W, o.PACKED_CONTIGUOUS)
 
 
+@settings(max_examples=40, deadline=None, derandomize=True)
+@given(st.integers(1, 8), st.integers(1, 50), st.integers(0, 2**31 - 1), st.booleans())
+def test_accumulate_exact_integers(W, n, seed, bf16_out):
+    """Small integers are exact in fp32 (and bf16 up to 256): accumulating slots into
+    an existing gradient must give the plain integer sum, whatever the order."""
+    rng = np.random.default_rng(seed)
+    slots = [rng.integers(-20, 21, size=n).astype(np.float32) for _ in range(W)]
+    into = rng.integers(-50, 51, size=n).astype(np.float32)
+    want = into.astype(np.int64) + sum(x.astype(np.int64) for x in slots)
+    if bf16_out:
+        got = o.bf16_to_f32(o.slot_sum(slots, "f32", "bf16", into=o.f32_to_bf16_rne(into)))
+    else:
+        got = o.slot_sum(slots, "f32", "f32", into=into)
+    assert (got == want.astype(np.float32)).all()
+
+
+@settings(max_examples=40, deadline=None, derandomize=True)
+@given(pc_case(), st.integers(0, 2**31 - 1))
+def test_pc_grad_return_random(case, seed):
+    """Packed-contiguous owners: every slot is the writer's contiguous slice and the
+    integer-valued sums are exact, for random documents and cp sizes."""
+    W, lengths = case
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    rng = np.random.default_rng(seed)
+    grads = [rng.integers(-9, 10, size=(T, 2)).astype(np.float32) for _ in range(W)]
+    slots, out = o.grad_return(grads, cu, W, "f32", "f32", policy=o.PACKED_CONTIGUOUS)
+    n = T // W
+    total = sum(g.astype(np.int64) for g in grads)
+    for owner in range(W):
+        for w in range(W):
+            assert (slots[owner][w] == grads[w][owner * n:(owner + 1) * n]).all()
+        assert (out[owner] == total[owner * n:(owner + 1) * n].astype(np.float32)).all()
+
+
 def test_empty_input():
     cu = np.array([0], dtype=np.int32)
     for pol in o.POLICIES:
