@@ -437,6 +437,8 @@ int cp_version(void);
  * terminated, at most 127 chars) into names[k*128], its launch count into
  * counts[k] and the summed milliseconds into total_ms[k]; it returns the
  * number of distinct kernels (or a negative cp_status) and clears the record.
+ * Meant for one calling thread: launches issued from several threads at once
+ * while recording is on may be attributed to the wrong kernel name.
  */
 int cp_profile_enable(int enable);
 int cp_profile_read(char* names, int64_t* counts, double* total_ms, int capacity);
