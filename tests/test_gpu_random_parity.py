@@ -3,6 +3,8 @@ lengths with empty documents, row shapes including unaligned ones, dtypes,
 tensor counts, accumulate mode) run through every entry point of the C ABI and
 compared bit-exactly with the CPU oracle.  Each case prints its parameters
 before it runs."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -14,7 +16,8 @@ pytestmark = pytest.mark.gpu
 POL = {0: O.DUAL_CHUNK_SWAP, 1: O.PACKED_CONTIGUOUS}
 TAG = {torch.float32: "f32", torch.bfloat16: "bf16"}
 ROWS = [(1, 1), (1, 3), (2, 8), (3, 5), (1, 64), (4, 32), (8, 17), (2, 128), (1, 520), (5, 128)]
-N_CASES = 160
+# 160 cases by default; CPTHD_RANDOM_CASES raises the count for a longer run.
+N_CASES = int(os.environ.get("CPTHD_RANDOM_CASES", "160"))
 
 
 @pytest.fixture(scope="module")
