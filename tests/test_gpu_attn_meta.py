@@ -108,3 +108,54 @@ def test_fail_closed(cp):
     with pytest.raises(cp.CpError) as e:
         cp.cp_build_attn_meta(good, attn=buf[128:])
     assert e.value.status == cp.CP_ERR_ALIAS
+
+
+def _attention(q, k, v, mask):
+    """Plain fp32 softmax attention: q [Tq,H,D], k/v [Tk,H,D], mask [Tq,Tk] (True = attend)."""
+    qh = q.permute(1, 0, 2).contiguous()
+    kh = k.permute(1, 2, 0).contiguous()
+    vh = v.permute(1, 0, 2).contiguous()
+    s = torch.matmul(qh, kh) / float(q.shape[-1]) ** 0.5
+    s = s.masked_fill(~mask[None], float("-inf"))
+    return torch.matmul(torch.softmax(s, dim=-1), vh).permute(1, 0, 2)
+
+
+@pytest.mark.parametrize("policy,lengths,W", [
+    (0, [16, 48, 32, 64], 2), (0, [64, 16, 0, 48], 4),
+    (1, [5, 40, 3, 0, 70, 10], 4), (1, [100, 7, 21], 2), (1, [128], 4)])
+def test_tables_drive_document_causal_attention(cp, policy, lengths, W):
+    """Attention run per rank and per step from the GPU-built tables (queries: the
+    rank's local rows of each segment; keys/values: the gathered global buffer;
+    causal mask aligned at the bottom right of each segment) and gathered back
+    equals attention over the whole packed buffer with the causal in-document mask."""
+    say(f"case attention through the tables, policy={policy} W={W}")
+    cu_np = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T, B, H, D = int(cu_np[-1]), len(lengths), 2, 16
+    meta = cp.cp_build_meta(torch.from_numpy(cu_np).to(DEV), T, W, policy, check=True)
+    magic, tab = cp.read_attn_meta(cp.cp_build_attn_meta(meta), B, W)
+    assert magic == cp.CP_ATTN_MAGIC
+    gen = torch.Generator(device=DEV).manual_seed(T + W)
+    q, k, v = (torch.randn((T, H, D), generator=gen, device=DEV) for _ in range(3))
+    doc = torch.repeat_interleave(torch.arange(B, device=DEV), torch.tensor(lengths, device=DEV))
+    pos = torch.arange(T, device=DEV)
+    full_mask = (doc[:, None] == doc[None, :]) & (pos[None, :] <= pos[:, None])
+    want = _attention(q, k, v, full_mask)
+    q_local = cp.cp_partition_thd(q, meta)  # [W, T/W, H, D]
+    out_local = torch.full_like(q_local, float("nan"))
+    for r in range(W):
+        for step in range(2):
+            m = int(tab["num_segments"][r, step])
+            cq, qo = tab["cu_seqlens_q"][r, step], tab["q_offsets"][r, step]
+            ck, ko = tab["cu_seqlens_kv"][r, step], tab["kv_offsets"][r, step]
+            for j in range(m):
+                ql, kl = int(cq[j + 1] - cq[j]), int(ck[j + 1] - ck[j])
+                q0, k0 = int(qo[j]), int(ko[j])
+                if ql == 0:
+                    continue
+                i = torch.arange(ql, device=DEV)[:, None]
+                kk = torch.arange(kl, device=DEV)[None, :]
+                mask = kk <= (kl - ql) + i
+                out_local[r, q0:q0 + ql] = _attention(q_local[r, q0:q0 + ql], k[k0:k0 + kl], v[k0:k0 + kl], mask)
+    got = cp.cp_gather_thd(out_local, meta)
+    assert not torch.isnan(got).any()
+    assert torch.allclose(got, want, atol=1e-5, rtol=1e-5), (got - want).abs().max().item()
