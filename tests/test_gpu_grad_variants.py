@@ -229,3 +229,18 @@ def test_s256k_w4_packed_contiguous_and_accumulate(cp):
             assert bits_equal(to_np(out[t][o].index_select(0, lidx)), ref), (t, o)
     del grads, out, fused
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n_tensors", [1, 3, 5])
+def test_any_number_of_gradient_tensors(cp, n_tensors):
+    """The gradient return takes any number of tensors per rank (dK, dV, ... ): one
+    table row per tensor, every one bit-exact against the oracle."""
+    say(f"case {n_tensors} gradient tensors per rank")
+    W, H, D = 4, 2, 128
+    cu = documents("dcs", W, seed=n_tensors, unit=8)
+    T = int(cu[-1])
+    gen = torch.Generator(device=DEV).manual_seed(500 + n_tensors)
+    grads = [[randn((T, H, D), torch.float32, gen) for _ in range(W)] for _ in range(n_tensors)]
+    into = [[randn((T // W, H, D), torch.bfloat16, gen) for _ in range(W)] for _ in range(n_tensors)]
+    slots, out, fused = run_variants(cp, grads, into, cu, W, "dcs", accumulate=False)
+    check_against_oracle(grads, into, cu, W, "dcs", False, slots, out, fused)
