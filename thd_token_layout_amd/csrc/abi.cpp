@@ -163,8 +163,6 @@ hipEvent_t take_event() {
   return e;
 }
 
-std::mutex g_cu_mutex;
-std::map<int, int> g_cu_count;
 
 }  // namespace
 
@@ -196,23 +194,6 @@ void profile_after(hipStream_t stream) {
   g_prof_pending_start = nullptr;
 }
 
-int device_cu_count() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) {
-    (void)hipGetLastError();
-    return 1;
-  }
-  std::lock_guard<std::mutex> lock(g_cu_mutex);
-  auto it = g_cu_count.find(dev);
-  if (it != g_cu_count.end()) return it->second;
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
-    (void)hipGetLastError();
-    n = 1;
-  }
-  g_cu_count[dev] = n;
-  return n;
-}
 
 }  // namespace cpthd
 
@@ -618,7 +599,7 @@ const char* cp_status_string(int status) {
   }
 }
 
-int cp_version(void) { return 100; }
+int cp_version(void) { return 200; }
 
 int cp_profile_enable(int enable) {
   std::lock_guard<std::mutex> lock(g_prof_mutex);

@@ -134,7 +134,4 @@ hipError_t launch_epoch_wait(const uint32_t* epochs, int32_t W, int32_t owner, u
 void profile_before(const char* name, hipStream_t stream);
 void profile_after(hipStream_t stream);
 
-// Number of compute units of the current device (cached).
-int device_cu_count();
-
 }  // namespace cpthd
