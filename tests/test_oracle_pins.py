@@ -134,3 +134,44 @@ def test_epochs_after():
 @pytest.mark.slow
 def test_bf16_rne_exhaustive():
     pins.check_bf16_rne_against_torch(o, exhaustive=True)
+
+
+def _compositions(total, parts_max=None):
+    """Every ordered list of positive integers summing to `total`."""
+    if total == 0:
+        yield []
+        return
+    for first in range(1, total + 1):
+        for rest in _compositions(total - first):
+            yield [first] + rest
+
+
+def test_exhaustive_small_layouts():
+    """Every document split of every small T (packed-contiguous: T <= 9; dual-chunk-
+    swap: up to 5 chunk-lengths per rank), for W = 1..4: partition invariants, the
+    brute-force owners, and the attention pairs against the brute-force mask."""
+    count = 0
+    for W in (1, 2, 3, 4):
+        for T in range(0, 10):
+            if T % W:
+                continue
+            for lengths in _compositions(T):
+                cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+                x = np.arange(T * 2, dtype=np.float32).reshape(T, 1, 2)
+                pins.check_invariants(o, cu, T, W, o.PACKED_CONTIGUOUS, x)
+                pins.check_attention_pairs(o, cu, T, W, o.PACKED_CONTIGUOUS)
+                count += 1
+        for units in range(0, 6):  # total length in multiples of 2W
+            for chunks in _compositions(units):
+                lengths = [2 * W * c for c in chunks]
+                cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+                T = int(cu[-1])
+                x = np.arange(T * 2, dtype=np.float32).reshape(T, 1, 2)
+                pins.check_invariants(o, cu, T, W, o.DUAL_CHUNK_SWAP, x)
+                pins.check_attention_pairs(o, cu, T, W, o.DUAL_CHUNK_SWAP)
+                if T:
+                    rows = pins.brute_owner_rows(cu, T, W)
+                    for r in range(W):
+                        assert o.rank_rows(cu, T, W, o.DUAL_CHUNK_SWAP, r).tolist() == rows[r]
+                count += 1
+    assert count > 500
