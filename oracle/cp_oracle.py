@@ -24,7 +24,8 @@ Sources (the pages; see their titles):
     [owner][writer], publish an epoch, owners wait for all epochs and then
     accumulate slots 0..cp_size-1.
   * "Low Latency Communication Kernels with NVSHMEM" (GPU MODE lecture 87
-    notes), exercise list: the 1 KB - 16 MB sum sweep.
+    notes), exercise list: the 1 KB - 16 MB sum sweep, and the all-reduce
+    algorithms chosen by message size (one-shot against ring).
 
 Readings where the pages are silent (the design notes list them all):
   * a DualChunkSwap rank stores its tokens document-major, and inside a
@@ -49,7 +50,12 @@ Readings where the pages are silent (the design notes list them all):
     order; a dual-chunk-swap rank runs step 0 on chunk r and step 1 on chunk
     2W-1-r of every document, each against the document's prefix up to the
     chunk's end; a packed-contiguous rank runs one step in which every local
-    segment sees its document from the first token on.
+    segment sees its document from the first token on;
+  * the all-reduce algorithms take their textbook forms: one-shot = every
+    rank sums all W buffers in rank order, fp32, one rounding; ring = a
+    reduce-scatter then an all-gather of W-1 steps each, passing to rank r+1,
+    over W chunks of a 64-element-aligned length; ring partials travel in the
+    buffer type (a bf16 ring rounds after every add).
 
 bf16 tensors are represented here as numpy uint16 bit patterns.
 """
@@ -457,3 +463,74 @@ def epochs_after(cp_size, epoch):
     writer writes its epoch into every owner's [owner][writer] entry.
     """
     return np.full((cp_size, cp_size), epoch, dtype=np.uint32)
+
+
+# --------------------------------------------------------------------------
+# All-reduce of W rank buffers: one-shot and ring ("Low Latency Communication
+# Kernels with NVSHMEM", the menu of all-reduce algorithms chosen by message
+# size, and exercises 2-3: the 1 KB - 16 MB latency sweep, one-shot against
+# ring).  The pages name the two algorithms without spelling them out; the
+# textbook forms are taken:
+#   * one-shot: every rank reads all W buffers and sums them itself, in rank
+#     order 0..W-1, in fp32, rounding once to the buffer type;
+#   * ring: the buffer is cut into W chunks; a reduce-scatter of W-1 steps in
+#     which rank r passes one partial chunk to rank r+1 (mod W), which adds its
+#     own contribution, then an all-gather of W-1 steps in which rank r passes
+#     one complete chunk to rank r+1.  Partials travel in the buffer type, so a
+#     bf16 ring rounds after every add.
+# Buffers are one-dimensional arrays of n elements (f32, or bf16 as uint16).
+# --------------------------------------------------------------------------
+RING_CHUNK_ALIGN = 64  # elements
+
+
+def ring_chunks(n, cp_size):
+    """Chunk k of the ring is [min(k*q, n), min((k+1)*q, n)), q = n/W rounded
+    up to a multiple of 64 elements (chunk starts stay 256-byte aligned for
+    fp32); trailing chunks may be empty for small n."""
+    q = -(-n // (RING_CHUNK_ALIGN * cp_size)) * RING_CHUNK_ALIGN
+    return [(min(k * q, n), min((k + 1) * q, n)) for k in range(cp_size)]
+
+
+def allreduce_one_shot(inputs, dtype):
+    """Every rank's result: sum of inputs[0..W-1] in rank order, fp32, one rounding."""
+    W = len(inputs)
+    acc = _widen(inputs[0], dtype).astype(np.float32, copy=True)
+    with np.errstate(over="ignore", invalid="ignore"):
+        for w in range(1, W):
+            acc = (acc + _widen(inputs[w], dtype)).astype(np.float32)
+    res = _narrow(acc, dtype)
+    return [res.copy() for _ in range(W)]
+
+
+def allreduce_ring(inputs, dtype):
+    """The ring, simulated step by step with one working buffer per rank.
+
+    Every step is a round of messages: each rank sends one chunk of its
+    working buffer (as it stood before the step) to rank r+1, which stores
+    it, after adding its own input chunk during the reduce-scatter.  In
+    reduce-scatter step s rank r receives chunk (r-1-s) mod W; after W-1
+    steps rank r holds chunk (r+1) mod W complete.  In all-gather step s
+    rank r receives chunk (r-s) mod W, complete.
+    """
+    W = len(inputs)
+    n = inputs[0].shape[0]
+    chunks = ring_chunks(n, W)
+    buf = [np.array(x, copy=True) for x in inputs]
+    for s in range(W - 1):  # reduce-scatter
+        msgs = []
+        for r in range(W):
+            src = (r - 1) % W
+            a, b = chunks[(r - 1 - s) % W]
+            msgs.append((r, a, b, buf[src][a:b].copy()))
+        for r, a, b, m in msgs:
+            with np.errstate(over="ignore", invalid="ignore"):
+                acc = (_widen(m, dtype) + _widen(inputs[r][a:b], dtype)).astype(np.float32)
+            buf[r][a:b] = _narrow(acc, dtype)
+    for s in range(W - 1):  # all-gather
+        msgs = []
+        for r in range(W):
+            a, b = chunks[(r - s) % W]
+            msgs.append((r, a, b, buf[(r - 1) % W][a:b].copy()))
+        for r, a, b, m in msgs:
+            buf[r][a:b] = m
+    return buf

@@ -494,6 +494,138 @@ def check_attention_meta_closed_forms(o):
             assert (m["kv_offsets"][r, 1] == T).all()
 
 
+# ---------------------------------------------------------------- all-reduce (one-shot, ring)
+def check_ring_chunks(o):
+    # hand-worked: 64-element granules, W chunks covering [0, n), empties at the end
+    assert o.ring_chunks(300, 8) == [(0, 64), (64, 128), (128, 192), (192, 256), (256, 300),
+                                     (300, 300), (300, 300), (300, 300)]
+    assert o.ring_chunks(1, 4) == [(0, 1), (1, 1), (1, 1), (1, 1)]
+    assert o.ring_chunks(0, 3) == [(0, 0), (0, 0), (0, 0)]
+    assert o.ring_chunks(4194304, 8)[1] == (524288, 1048576)   # 16 MiB of fp32, 8 ranks
+    assert o.ring_chunks(1000, 1) == [(0, 1000)]
+    for n in (0, 1, 63, 64, 65, 511, 512, 4097, 100000):
+        for W in (1, 2, 3, 7, 8, 16):
+            ch = o.ring_chunks(n, W)
+            assert len(ch) == W and ch[0][0] == 0 and ch[-1][1] == n
+            assert all(ch[k][1] == ch[k + 1][0] for k in range(W - 1))
+            lens = [b - a for a, b in ch]
+            full = [L for L in lens if L > 0]
+            assert lens[:len(full)] == full           # empty chunks only at the end
+            if len(full) <= 1:
+                assert n <= 64 or W == 1
+            else:
+                # equal chunks but the last; their length is the smallest
+                # multiple of 64 with which W chunks cover n
+                q = full[0]
+                assert all(L == q for L in full[:-1]) and 0 < full[-1] <= q
+                assert q % 64 == 0 and W * q >= n and W * (q - 64) < n
+
+
+def check_allreduce_integer(o):
+    # integer-valued fp32 data: every partial sum is exact, so both algorithms
+    # give the exact integer sum on every rank, whatever the order
+    rng = np.random.default_rng(11)
+    for W in (1, 2, 3, 5, 8):
+        for n in (0, 1, 64, 65, 300, 1030):
+            ints = rng.integers(-1000, 1000, size=(W, n))
+            xs = [r.astype(np.float32) for r in ints]
+            exact = ints.sum(axis=0).astype(np.float64)
+            for res in (o.allreduce_one_shot(xs, "f32"), o.allreduce_ring(xs, "f32")):
+                assert len(res) == W
+                for r in range(W):
+                    assert np.array_equal(res[r].astype(np.float64), exact), (W, n, r)
+
+
+def _pattern(W, n, where):
+    """Rank buffers of n fp32 elements where, inside chunk k, rank (k + j) % W
+    holds where[j]."""
+    xs = [np.zeros(n, dtype=np.float32) for _ in range(W)]
+    q = n // W
+    for k in range(W):
+        for j, v in enumerate(where):
+            xs[(k + j) % W][k * q:(k + 1) * q] = v
+    return xs
+
+
+def check_allreduce_order_handworked(o):
+    # W = 4, n = 256: four chunks of 64.  2**24 + 1 is a tie in fp32 and rounds
+    # to 2**24, while 2**24 + 2 is exact, so the order of adds shows in the result.
+    big = np.float32(2 ** 24)
+    # pattern A: inside chunk k, rank k holds 2^24, ranks k+2 and k+3 hold 1.
+    # Ring order k, k+1, k+2, k+3 adds the ones after 2^24: 2^24 in every chunk.
+    # Rank order 0..3 adds both ones first in chunks 2 and 3: 2^24 + 2 there.
+    xs = _pattern(4, 256, [big, 0, 1, 1])
+    ring = o.allreduce_ring(xs, "f32")
+    one = o.allreduce_one_shot(xs, "f32")
+    want_ring = [2 ** 24] * 4
+    want_one = [2 ** 24, 2 ** 24, 2 ** 24 + 2, 2 ** 24 + 2]
+    # pattern B: ranks k and k+1 hold 1, rank k+2 holds 2^24.  Ring order gives
+    # 2 + 2^24 everywhere; a ring run the other way (k, k-1, ...) would give 2^24.
+    xsb = _pattern(4, 256, [1, 1, big, 0])
+    ringb = o.allreduce_ring(xsb, "f32")
+    oneb = o.allreduce_one_shot(xsb, "f32")
+    want_ringb = [2 ** 24 + 2] * 4
+    want_oneb = [2 ** 24 + 2, 2 ** 24 + 2, 2 ** 24, 2 ** 24]
+    for r in range(4):
+        for k in range(4):
+            sl = slice(64 * k, 64 * (k + 1))
+            assert (ring[r][sl] == want_ring[k]).all(), ("A ring", r, k)
+            assert (one[r][sl] == want_one[k]).all(), ("A one-shot", r, k)
+            assert (ringb[r][sl] == want_ringb[k]).all(), ("B ring", r, k)
+            assert (oneb[r][sl] == want_oneb[k]).all(), ("B one-shot", r, k)
+
+
+def check_allreduce_bf16_rounding(o):
+    # bf16 keeps 8 significant bits: 256 + 1 = 257 is a tie and rounds to 256
+    # (0x4380); 258 is exact (0x4381).  Inside chunk k rank k holds 256 and the
+    # others 1 (0x3F80).  The ring rounds after each add: 256 every time.  The
+    # one-shot adds in fp32 and rounds once: 258.
+    W, n = 3, 192
+    xs = [np.full(n, 0x3F80, dtype=np.uint16) for _ in range(W)]
+    for k in range(W):
+        xs[k][64 * k:64 * (k + 1)] = 0x4380
+    ring = o.allreduce_ring(xs, "bf16")
+    one = o.allreduce_one_shot(xs, "bf16")
+    for r in range(W):
+        assert ring[r].dtype == np.uint16 and (ring[r] == 0x4380).all(), r
+        assert one[r].dtype == np.uint16 and (one[r] == 0x4381).all(), r
+
+
+def check_allreduce_rotated_sums(o, seed=12):
+    # closed form of the ring: chunk k is summed in rank order k, k+1, ..., k-1
+    # (mod W), rounding to the buffer type after each add; every rank ends with
+    # the same bits.  The one-shot equals the owner slot sum of the W buffers.
+    rng = np.random.default_rng(seed)
+    for W, n in ((2, 130), (3, 1000), (5, 777), (8, 4096), (4, 3)):
+        xs = [rng.standard_normal(n).astype(np.float32) for _ in range(W)]
+        xb = [o.f32_to_bf16_rne(x) for x in xs]
+        for data, dt in ((xs, "f32"), (xb, "bf16")):
+            ring = o.allreduce_ring(data, dt)
+            one = o.allreduce_one_shot(data, dt)
+            want = np.empty_like(data[0])
+            q = -(-n // (64 * W)) * 64
+            for k in range(W):
+                a, b = min(k * q, n), min((k + 1) * q, n)
+                acc = data[k][a:b]
+                for j in range(1, W):
+                    x = data[(k + j) % W][a:b]
+                    if dt == "f32":
+                        acc = (acc + x).astype(np.float32)
+                    else:
+                        acc = o.f32_to_bf16_rne(o.bf16_to_f32(acc) + o.bf16_to_f32(x))
+                want[a:b] = acc
+            ref_one = o.slot_sum(data, dt, dt)
+            for r in range(W):
+                assert np.array_equal(ring[r].view(np.uint8), want.view(np.uint8)), (W, n, dt, r)
+                assert np.array_equal(one[r].view(np.uint8), ref_one.view(np.uint8)), (W, n, dt, r)
+
+
+def check_allreduce_w1(o):
+    x = np.random.default_rng(4).standard_normal(100).astype(np.float32)
+    for res in (o.allreduce_ring([x], "f32"), o.allreduce_one_shot([x], "f32")):
+        assert len(res) == 1 and np.array_equal(res[0], x)
+
+
 ALL_CHECKS = [
     check_handworked_dcs,
     check_handworked_pc,
@@ -516,4 +648,10 @@ ALL_CHECKS = [
     check_attention_handworked,
     check_attention_brute_force,
     check_attention_meta_closed_forms,
+    check_ring_chunks,
+    check_allreduce_integer,
+    check_allreduce_order_handworked,
+    check_allreduce_bf16_rounding,
+    check_allreduce_rotated_sums,
+    check_allreduce_w1,
 ]

@@ -253,6 +253,73 @@ def _attn_offsets_packed(o):
     return attention_meta
 
 
+def _ring_variant(o, direction=1, rs_shift=1, round_once=False, ag_steps=None):
+    """A ring with one planted change: messages sent to rank r - 1 instead of
+    r + 1, the wrong chunk index in the reduce-scatter, bf16 partials kept in
+    fp32 until the end, or an all-gather step dropped."""
+    def allreduce_ring(inputs, dtype):
+        W = len(inputs)
+        n = inputs[0].shape[0]
+        ch = o.ring_chunks(n, W)
+        wide = [o.bf16_to_f32(x) if dtype == "bf16" else x.copy() for x in inputs]
+        buf = [x.copy() for x in wide]
+        for s in range(W - 1):
+            msgs = []
+            for r in range(W):
+                a, b = ch[(r - direction * (rs_shift + s)) % W]
+                msgs.append((r, a, b, buf[(r - direction) % W][a:b].copy()))
+            for r, a, b, m in msgs:
+                acc = (m + wide[r][a:b]).astype(np.float32)
+                if dtype == "bf16" and not round_once:
+                    acc = o.bf16_to_f32(o.f32_to_bf16_rne(acc))
+                buf[r][a:b] = acc
+        for s in range(W - 1 if ag_steps is None else ag_steps(W)):
+            msgs = []
+            for r in range(W):
+                a, b = ch[(r - direction * s) % W]
+                msgs.append((r, a, b, buf[(r - direction) % W][a:b].copy()))
+            for r, a, b, m in msgs:
+                buf[r][a:b] = m
+        return [o.f32_to_bf16_rne(x) if dtype == "bf16" else x for x in buf]
+    return allreduce_ring
+
+
+def _ring_reversed(o):
+    return _ring_variant(o, direction=-1)
+
+
+def _ring_rs_chunk_shifted(o):
+    return _ring_variant(o, rs_shift=0)
+
+
+def _ring_bf16_rounds_once(o):
+    return _ring_variant(o, round_once=True)
+
+
+def _ring_short_allgather(o):
+    return _ring_variant(o, ag_steps=lambda W: max(W - 2, 0))
+
+
+def _ring_rank_order(o):
+    def allreduce_ring(inputs, dtype):
+        return o.allreduce_one_shot(inputs, dtype)
+    return allreduce_ring
+
+
+def _ring_chunks_unaligned(o):
+    def ring_chunks(n, cp_size):
+        q = -(-n // cp_size)
+        return [(min(k * q, n), min((k + 1) * q, n)) for k in range(cp_size)]
+    return ring_chunks
+
+
+def _one_shot_reversed(o):
+    def allreduce_one_shot(inputs, dtype):
+        res = o.slot_sum(inputs[::-1], dtype, dtype)
+        return [res.copy() for _ in inputs]
+    return allreduce_one_shot
+
+
 MUTATIONS = {
     "dcs_swapped_chunks": ("dcs_rank_rows", _dcs_swapped_chunks),
     "dcs_wrong_mirror": ("dcs_rank_rows", _dcs_wrong_mirror),
@@ -276,6 +343,13 @@ MUTATIONS = {
     "attention_pc_no_lookback": ("attention_steps", _attn_pc_no_lookback),
     "attention_steps_swapped": ("attention_steps", _attn_steps_swapped),
     "attention_offsets_packed": ("attention_meta", _attn_offsets_packed),
+    "ring_reversed": ("allreduce_ring", _ring_reversed),
+    "ring_rs_chunk_shifted": ("allreduce_ring", _ring_rs_chunk_shifted),
+    "ring_bf16_rounds_once": ("allreduce_ring", _ring_bf16_rounds_once),
+    "ring_short_allgather": ("allreduce_ring", _ring_short_allgather),
+    "ring_in_rank_order": ("allreduce_ring", _ring_rank_order),
+    "ring_chunks_unaligned": ("ring_chunks", _ring_chunks_unaligned),
+    "one_shot_reversed": ("allreduce_one_shot", _one_shot_reversed),
 }
 
 INVARIANT_CASES = [
