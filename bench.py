@@ -325,18 +325,18 @@ def per_config(cp, WL, torch, dev, reps: int = 10):
     return results
 
 
-def graph_us_per_call(cp, torch, slots, out, calls: int = 100, replays: int = 5):
-    """The same call captured `calls` times back to back in one HIP graph and replayed:
+def graph_us_per_call(torch, fn, calls: int = 100, replays: int = 5):
+    """`fn` captured `calls` times back to back in one HIP graph and replayed:
     per-call time without host work or per-launch submission."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        cp.cp_slot_sum(slots, out)
+        fn()
     torch.cuda.current_stream().wait_stream(side)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for _ in range(calls):
-            cp.cp_slot_sum(slots, out)
+            fn()
     graph.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -345,7 +345,31 @@ def graph_us_per_call(cp, torch, slots, out, calls: int = 100, replays: int = 5)
         graph.replay()
     e1.record()
     torch.cuda.synchronize()
+    del graph
     return e0.elapsed_time(e1) * 1000.0 / (calls * replays)
+
+
+def eager_us_per_call(torch, fn, reps: int):
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / reps
+
+
+def kernel_us_per_call(cp, fn, calls: int = 20):
+    """Summed duration of the kernels one call launches (HIP events around each launch)."""
+    cp.cp_profile_enable(True)
+    for _ in range(calls):
+        fn()
+    prof = cp.cp_profile_read()
+    cp.cp_profile_enable(False)
+    return sum(m for _, m in prof.values()) * 1000.0 / calls, sum(c for c, _ in prof.values()) // calls
 
 
 def sweep_latency(step: Step, cp, torch, reps: int = 1000):
@@ -353,27 +377,40 @@ def sweep_latency(step: Step, cp, torch, reps: int = 1000):
     the kernel alone (HIP events around each launch), and replayed from a HIP graph."""
     res = []
     for nbytes, slots, out in step.sweep:
-        for _ in range(5):
+        def call():
             cp.cp_slot_sum(slots, out)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            cp.cp_slot_sum(slots, out)
-        e1.record()
-        torch.cuda.synchronize()
-        per_call_us = e0.elapsed_time(e1) * 1000.0 / reps
-        cp.cp_profile_enable(True)
-        for _ in range(20):
-            cp.cp_slot_sum(slots, out)
-        prof = cp.cp_profile_read()
-        cp.cp_profile_enable(False)
-        kcount = sum(c for c, _ in prof.values())
-        kms = sum(m for _, m in prof.values())
-        res.append({"bytes_per_slot": nbytes, "us_per_call": round(per_call_us, 2),
-                    "kernel_us": round(kms * 1000.0 / max(kcount, 1), 2),
-                    "graph_us_per_call": round(graph_us_per_call(cp, torch, slots, out), 2)})
+        kus, _ = kernel_us_per_call(cp, call)
+        res.append({"bytes_per_slot": nbytes, "us_per_call": round(eager_us_per_call(torch, call, reps), 2),
+                    "kernel_us": round(kus, 2),
+                    "graph_us_per_call": round(graph_us_per_call(torch, call), 2)})
     return res
+
+
+def allreduce_sweep(step: Step, cp, torch):
+    """All-reduce of W=8 fp32 rank buffers of 1 KiB ... 16 MiB, every rank emulated on this
+    GPU: one-shot (one launch, each rank reads all 8 buffers) against ring (14 launches:
+    7 reduce-scatter and 7 all-gather steps).  Per call: eager latency, summed kernel time,
+    and time replayed from a HIP graph; algorithmic bytes over all 8 ranks (one-shot 72 x
+    size, ring 35 x size) over the kernel time."""
+    W = 8
+    res = []
+    for nbytes, slots, _ in step.sweep:
+        outs = [torch.empty_like(slots[0]) for _ in range(W)]
+        row = {"bytes_per_rank": nbytes}
+        for algo, factor in (("one_shot", W * (W + 1)), ("ring", 5 * (W - 1))):
+            def call(algo=algo):
+                cp.cp_allreduce(slots, outs, algo=algo)
+            kus, launches = kernel_us_per_call(cp, call)
+            row[algo] = {"us_per_call": round(eager_us_per_call(torch, call, 200), 2),
+                         "kernel_us": round(kus, 2), "launches": launches,
+                         "graph_us_per_call": round(graph_us_per_call(torch, call, calls=20), 2),
+                         "kernel_gbs": round(factor * nbytes / (kus * 1e-6) / 1e9, 1) if kus > 0 else None}
+        res.append(row)
+        del outs
+    faster = [r["bytes_per_rank"] for r in res
+              if r["ring"]["graph_us_per_call"] < r["one_shot"]["graph_us_per_call"]]
+    return {"cp_size": W, "dtype": "f32", "sizes": res,
+            "ring_faster_from_bytes": min(faster) if faster else None}
 
 
 def main():
@@ -385,6 +422,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep-latency", action="store_true")
+    ap.add_argument("--no-allreduce", action="store_true",
+                    help="skip the one-shot / ring all-reduce sweep")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload measurements (each config's ops timed alone)")
     ap.add_argument("--only-configs", action="store_true",
@@ -463,6 +502,9 @@ def main():
                 "avg_launch_us": dom["avg_us"]}
 
     sweep = None if args.no_sweep_latency else sweep_latency(step, cp, torch)
+    if not args.no_allreduce:
+        log("[bench] all-reduce sweep (one-shot, ring)")
+    allreduce = None if args.no_allreduce else allreduce_sweep(step, cp, torch)
     num_docs = step.num_docs
     ops = [{"op": n, "bytes": b} for n, b, _ in step.ops]
     configs = None
@@ -497,6 +539,7 @@ def main():
         "kernels": kernels,
         "ops": ops,
         "sweep_latency": sweep,
+        "allreduce_sweep": allreduce,
         "per_config": configs,
         "device": torch.cuda.get_device_name(0),
     }

@@ -16,7 +16,8 @@
  *        (TransformerEngine PR 3235): sections "Description", "Changes",
  *        "Sequence Diagram", "Validation", and the author's reply on CP size.
  *  [LL]  "Low Latency Communication Kernels with NVSHMEM" (GPU MODE lecture
- *        87 notes): exercise list (1 KB - 16 MB sum sweep).
+ *        87 notes): exercise list (1 KB - 16 MB sum sweep; one-shot against
+ *        ring all-reduce) and the all-reduce algorithms chosen by message size.
  *  [MM]  "Kernel-level compute-communication overlapping for CP linear
  *        attention kernels via nvshmem" (cuLA issue 15): replies on buffer
  *        ownership (buffers allocated outside the module, lifetime owned by
@@ -420,6 +421,39 @@ int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
  */
 int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t n_elems,
                 int32_t in_dtype, int32_t out_dtype, int32_t flags, cp_stream_t stream);
+
+/* ------------------------------------------------------------ all-reduce */
+#define CP_ALLREDUCE_ONE_SHOT 0
+#define CP_ALLREDUCE_RING     1
+
+/*
+ * cp_allreduce - all W ranks, emulated by W buffers on this device, end with
+ * the sum of all W inputs: out[r][k] = in[0][k] + ... + in[W-1][k] for every
+ * rank r.  The two algorithms of [LL] (the all-reduce menu by message size;
+ * exercises 2-3, one-shot against ring over 1 KB - 16 MB):
+ *   CP_ALLREDUCE_ONE_SHOT  one launch: every rank reads all W inputs and sums
+ *       them in rank order 0..W-1 in fp32 (seeded with in[0]), rounding once
+ *       to dtype.  Every rank's out holds the same bits as cp_slot_sum.
+ *   CP_ALLREDUCE_RING      the buffer is cut into W chunks of q elements,
+ *       q = 64 * ceil(n_elems / (64 W)) (chunk c = [c q, (c+1) q) clipped to
+ *       n_elems; trailing chunks may be empty).  Reduce-scatter: W-1 steps;
+ *       in step s rank r takes chunk (r-1-s) mod W from rank r-1 (rank r-1's
+ *       input at s = 0, its out after) and writes that plus its own input
+ *       chunk, added in fp32 and rounded to dtype, into out[r].  Chunk c is
+ *       thus summed in rank order c, c+1, ..., c-1 (mod W), rounded after
+ *       every add.  All-gather: W-1 steps; in step s rank r copies chunk
+ *       (r-s) mod W from out[r-1].  2(W-1) launches, stream-ordered; W = 1 is
+ *       one copy.  out[r] is the rank's working buffer throughout.
+ *   algo         CP_ALLREDUCE_ONE_SHOT or CP_ALLREDUCE_RING (else CP_ERR_ARG)
+ *   cp_size      W in [1, 64]
+ *   in, out      host tables [W] of device buffers of n_elems `dtype` each;
+ *                outputs must not overlap any input or each other
+ *                (CP_ERR_ALIAS); inputs may share memory and are not written
+ *   dtype        CP_F32 or CP_BF16 (CP_F16 and FP8: CP_ERR_UNSUPPORTED)
+ * n_elems == 0 is a no-op (pointers may then be NULL).
+ */
+int cp_allreduce(int32_t algo, int32_t cp_size, const void* const* in, void* const* out,
+                 int64_t n_elems, int32_t dtype, cp_stream_t stream);
 
 /* ------------------------------------------------------------ utilities */
 /* Static text for a status code (never NULL). */

@@ -46,6 +46,9 @@ int main(void) {
          "fused rejects an unsupported dtype pair");
   expect(cp_slot_sum(4, NULL, NULL, 0, CP_F32, CP_F32, 0, NULL) == CP_OK, "empty slot sum");
   expect(cp_build_attn_meta(fake, 3, 2, fake, 16, NULL) == CP_ERR_SHAPE, "attention buffer too small");
+  expect(cp_allreduce(CP_ALLREDUCE_RING, 8, table, otable, 256, CP_F16, NULL) == CP_ERR_UNSUPPORTED,
+         "all-reduce rejects fp16");
+  expect(cp_allreduce(CP_ALLREDUCE_ONE_SHOT, 8, NULL, NULL, 0, CP_F32, NULL) == CP_OK, "empty all-reduce");
 
   if (failures == 0) printf("c consumer ok\n");
   return failures == 0 ? 0 : 1;

@@ -41,7 +41,8 @@ def cp():
 def test_header_declares_the_boundary():
     fns = declared_functions()
     for name in ["cp_build_meta", "cp_partition_thd", "cp_gather_thd", "cp_grad_return",
-                 "cp_grad_return_fused", "cp_slot_sum", "cp_meta_status", "cp_meta_bytes"]:
+                 "cp_grad_return_fused", "cp_slot_sum", "cp_meta_status", "cp_meta_bytes",
+                 "cp_allreduce"]:
         assert name in fns, fns
 
 
@@ -172,6 +173,22 @@ def test_host_checks_before_any_hip_call(cp):
     assert ss(2, tab, FAKE, 10, cp.CP_F32, cp.CP_F16, 0, None) == cp.CP_ERR_UNSUPPORTED
     assert ss(2, nulls, FAKE, 10, cp.CP_F32, cp.CP_F32, 0, None) == cp.CP_ERR_ARG
     assert ss(2, tab, FAKE, 10, cp.CP_F32, cp.CP_F32, 0x20, None) == cp.CP_ERR_ARG
+    # all-reduce: algorithm, dtype, rank count, NULLs, sizes; empty is a no-op
+    ar = lib.cp_allreduce
+    assert ar(2, 2, tab, tab, 10, cp.CP_F32, None) == cp.CP_ERR_ARG
+    assert ar(-1, 2, tab, tab, 10, cp.CP_F32, None) == cp.CP_ERR_ARG
+    for algo in (cp.CP_ALLREDUCE_ONE_SHOT, cp.CP_ALLREDUCE_RING):
+        assert ar(algo, 2, tab, tab, 10, cp.CP_F16, None) == cp.CP_ERR_UNSUPPORTED
+        assert ar(algo, 2, tab, tab, 10, cp.CP_FP8_E5M2, None) == cp.CP_ERR_UNSUPPORTED
+        assert ar(algo, 2, tab, tab, 10, 42, None) == cp.CP_ERR_ARG
+        assert ar(algo, 0, tab, tab, 10, cp.CP_F32, None) == cp.CP_ERR_ARG
+        assert ar(algo, 65, tab, tab, 10, cp.CP_F32, None) == cp.CP_ERR_ARG
+        assert ar(algo, 2, tab, tab, -1, cp.CP_F32, None) == cp.CP_ERR_ARG
+        assert ar(algo, 2, tab, tab, 1 << 62, cp.CP_F32, None) == cp.CP_ERR_ARG
+        assert ar(algo, 2, nulls, tab, 10, cp.CP_F32, None) == cp.CP_ERR_ARG
+        assert ar(algo, 2, tab, nulls, 10, cp.CP_BF16, None) == cp.CP_ERR_ARG
+        assert ar(algo, 2, None, tab, 10, cp.CP_F32, None) == cp.CP_ERR_ARG
+        assert ar(algo, 8, None, None, 0, cp.CP_F32, None) == cp.CP_OK
 
 
 def test_library_has_no_oracle_dependency():

@@ -1,0 +1,191 @@
+"""GPU parity of the all-reduce of W rank buffers (one-shot and ring), through the
+C ABI, bit-exact against the CPU oracle: every rank's output, for every rank
+count, size (empty and short chunks, ragged tails, unaligned views), dtype and
+the W = 8, 1 KiB - 16 MiB sizes of the latency sweep; special values; errors
+the host rejects; and both algorithms captured in a HIP graph and replayed."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, O, bits_equal, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+TAG = {torch.float32: "f32", torch.bfloat16: "bf16"}
+REF = {"one_shot": O.allreduce_one_shot, "ring": O.allreduce_ring}
+
+
+@pytest.fixture(scope="module")
+def cp():
+    from thd_token_layout_amd import cpthd
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return cpthd
+
+
+def rank_inputs(W, n, dtype, seed, offset=0):
+    """W input views of n elements (offset elements into their allocation)."""
+    gen = torch.Generator(device=DEV).manual_seed(seed)
+    full = [torch.randn(n + offset, generator=gen, device=DEV).to(dtype) for _ in range(W)]
+    return [f[offset:] for f in full]
+
+
+def nan_outputs(W, n, dtype, offset=0):
+    return [torch.full((n + offset,), float("nan"), dtype=dtype, device=DEV)[offset:] for _ in range(W)]
+
+
+def check(cp, algo, xs, outs):
+    ref = REF[algo]([to_np(x) for x in xs], TAG[xs[0].dtype])
+    for r, o in enumerate(outs):
+        assert bits_equal(to_np(o), ref[r]), (algo, r)
+
+
+@pytest.mark.parametrize("algo", ["one_shot", "ring"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("W,n", [(1, 1000), (2, 1), (2, 130), (3, 64), (3, 65), (4, 511), (4, 512),
+                                 (5, 4099), (8, 256), (8, 300), (8, 4096), (8, 100003), (16, 1 << 16),
+                                 (7, 3 * 512 * 7 + 5), (64, 70000)])
+def test_allreduce_matches_oracle(cp, algo, dtype, W, n):
+    say(f"case allreduce {algo} W={W} n={n} {dtype}")
+    xs = rank_inputs(W, n, dtype, seed=W * 1000 + n)
+    outs = nan_outputs(W, n, dtype)
+    cp.cp_allreduce(xs, outs, algo=algo)
+    torch.cuda.synchronize()
+    check(cp, algo, xs, outs)
+
+
+@pytest.mark.parametrize("algo", ["one_shot", "ring"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_unaligned_views(cp, algo, dtype, offset):
+    """Views that start off a 16-byte boundary take the element path."""
+    W, n = 4, 2000 + offset
+    say(f"case allreduce unaligned {algo} {dtype} offset={offset}")
+    xs = rank_inputs(W, n, dtype, seed=offset, offset=offset)
+    outs = nan_outputs(W, n, dtype, offset=(offset + 1) % 4)
+    cp.cp_allreduce(xs, outs, algo=algo)
+    torch.cuda.synchronize()
+    check(cp, algo, xs, outs)
+
+
+@pytest.mark.parametrize("algo", ["one_shot", "ring"])
+@pytest.mark.parametrize("size", [1024 << k for k in range(15)])
+def test_sweep_sizes(cp, algo, size):
+    """W = 8 fp32 buffers of 1 KiB ... 16 MiB, as timed by the benchmark."""
+    W, n = 8, size // 4
+    say(f"case allreduce sweep {algo} bytes={size}")
+    xs = rank_inputs(W, n, torch.float32, seed=size)
+    outs = nan_outputs(W, n, torch.float32)
+    cp.cp_allreduce(xs, outs, algo=algo)
+    torch.cuda.synchronize()
+    check(cp, algo, xs, outs)
+
+
+@pytest.mark.parametrize("algo", ["one_shot", "ring"])
+def test_special_values(cp, algo):
+    """Signed zeros, infinities, NaN, overflow to inf, denormals; NaN results are
+    compared as NaN (payloads of two NaNs meeting are not fixed by IEEE)."""
+    W, n = 4, 1024
+    say(f"case allreduce special values {algo}")
+    vals = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 3.0e38, -3.0e38, 1e-45, -1e-45, 1.0], dtype=np.float32)
+    rng = np.random.default_rng(9)
+    host = [vals[rng.integers(0, len(vals), size=n)] for _ in range(W)]
+    host[0][:64] = -0.0
+    host[1][:64] = -0.0
+    host[2][:64] = -0.0
+    host[3][:64] = -0.0
+    xs = [torch.from_numpy(h).to(DEV) for h in host]
+    outs = nan_outputs(W, n, torch.float32)
+    cp.cp_allreduce(xs, outs, algo=algo)
+    torch.cuda.synchronize()
+    ref = REF[algo](host, "f32")
+    for r in range(W):
+        got = to_np(outs[r])
+        nan = np.isnan(ref[r])
+        assert (np.isnan(got) == nan).all()
+        assert bits_equal(got[~nan], ref[r][~nan]), r
+        assert (got[:64].view(np.uint32) == 0x80000000).all()  # -0 + -0 + ... stays -0
+
+
+def test_shared_input_buffer(cp):
+    """Inputs may share memory (they are only read)."""
+    say("case allreduce shared input")
+    x = rank_inputs(1, 5000, torch.float32, seed=3)[0]
+    xs = [x, x, x]
+    for algo in ("one_shot", "ring"):
+        outs = nan_outputs(3, 5000, torch.float32)
+        cp.cp_allreduce(xs, outs, algo=algo)
+        torch.cuda.synchronize()
+        check(cp, algo, xs, outs)
+
+
+def test_repeated_calls_overwrite(cp):
+    """A second call with new inputs and fewer elements gives that call's result."""
+    say("case allreduce repeated calls")
+    W = 8
+    outs = nan_outputs(W, 10000, torch.float32)
+    for algo in ("one_shot", "ring"):
+        for n, seed in ((10000, 1), (6001, 2)):
+            xs = rank_inputs(W, n, torch.float32, seed=seed)
+            view = [o[:n] for o in outs]
+            cp.cp_allreduce(xs, view, algo=algo)
+            torch.cuda.synchronize()
+            check(cp, algo, xs, view)
+
+
+def test_errors_rejected_before_launch(cp):
+    say("case allreduce errors")
+    lib = cp.lib
+    W, n = 4, 1000
+    xs = rank_inputs(W, n, torch.float32, seed=5)
+    outs = nan_outputs(W, n, torch.float32)
+    tab = lambda ts: (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])  # noqa: E731
+    for algo in (cp.CP_ALLREDUCE_ONE_SHOT, cp.CP_ALLREDUCE_RING):
+        # an output that is an input, or two outputs that overlap
+        assert lib.cp_allreduce(algo, W, tab(xs), tab([xs[1]] + outs[1:]), n, cp.CP_F32, None) == cp.CP_ERR_ALIAS
+        assert lib.cp_allreduce(algo, W, tab(xs), tab([outs[0], outs[0][10:]] + outs[2:]), n - 10,
+                                cp.CP_F32, None) == cp.CP_ERR_ALIAS
+        # sizes that run past the end of the buffers' allocations (2^36 elements:
+        # more than any allocation on the device)
+        assert lib.cp_allreduce(algo, W, tab(xs), tab(outs), 1 << 36, cp.CP_F32, None) == cp.CP_ERR_SHAPE
+        # host memory
+        host = torch.empty(n)
+        assert lib.cp_allreduce(algo, W, tab(xs), tab(outs[:3] + [host]), n, cp.CP_F32, None) == cp.CP_ERR_DEVICE
+    torch.cuda.synchronize()
+    assert all(torch.isnan(o).all() for o in outs), "a rejected call wrote an output"
+    with pytest.raises(ValueError):
+        cp.cp_allreduce(xs, outs[:3])
+
+
+@pytest.mark.parametrize("algo", ["one_shot", "ring"])
+def test_graph_capture_replays(cp, algo):
+    """Both algorithms record only kernel launches: captured once, replayed with
+    new inputs written eagerly between replays, every replay is exact."""
+    W, n = 8, 70000
+    say(f"case allreduce graph {algo}")
+    xs = [torch.empty(n, device=DEV) for _ in range(W)]
+    outs = [torch.empty(n, device=DEV) for _ in range(W)]
+    gen = torch.Generator(device=DEV).manual_seed(17)
+
+    def fresh():
+        for x in xs:
+            x.copy_(torch.randn(n, generator=gen, device=DEV))
+
+    fresh()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        cp.cp_allreduce(xs, outs, algo=algo)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cp.cp_allreduce(xs, outs, algo=algo)
+    for replay in range(3):
+        fresh()
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        check(cp, algo, xs, outs)

@@ -46,6 +46,7 @@ CP_CALL_POLICY_MISMATCH = 0x0800
 CP_CALL_USED_INVALID_META = 0x1000
 CP_CALL_DOCS_MISMATCH = 0x2000
 CP_ATTN_MAGIC = 0x54414350
+CP_ALLREDUCE_ONE_SHOT, CP_ALLREDUCE_RING = 0, 1
 
 POLICY = {"dual_chunk_swap": CP_POLICY_DUAL_CHUNK_SWAP,
           "packed_contiguous": CP_POLICY_PACKED_CONTIGUOUS}
@@ -78,6 +79,8 @@ lib.cp_grad_return_fused.argtypes = [_i32, _i32, _i32, _c.POINTER(_vp), _c.POINT
                                      _i32, _i32, _i32, _vp, _i32, _vp]
 lib.cp_slot_sum.restype = _c.c_int
 lib.cp_slot_sum.argtypes = [_i32, _c.POINTER(_vp), _vp, _i64, _i32, _i32, _i32, _vp]
+lib.cp_allreduce.restype = _c.c_int
+lib.cp_allreduce.argtypes = [_i32, _i32, _c.POINTER(_vp), _c.POINTER(_vp), _i64, _i32, _vp]
 lib.cp_attn_meta_bytes.restype = _sz
 lib.cp_attn_meta_bytes.argtypes = [_i32, _i32]
 lib.cp_build_attn_meta.restype = _c.c_int
@@ -353,6 +356,23 @@ def cp_slot_sum(slots: Sequence[torch.Tensor], out: torch.Tensor, accumulate: bo
     return out
 
 
+ALLREDUCE_ALGOS = {"one_shot": CP_ALLREDUCE_ONE_SHOT, "ring": CP_ALLREDUCE_RING}
+
+
+def cp_allreduce(inputs: Sequence[torch.Tensor], outs: Optional[Sequence[torch.Tensor]] = None,
+                 algo: str = "one_shot", stream=None) -> List[torch.Tensor]:
+    """Every rank's out = the sum of all W inputs (W rank buffers on this device)."""
+    if outs is None:
+        outs = [torch.empty_like(x) for x in inputs]
+    if len(outs) != len(inputs) or any(t.dtype != inputs[0].dtype or t.numel() != inputs[0].numel()
+                                       for t in list(inputs) + list(outs)):
+        raise ValueError("cp_allreduce: W inputs and W outputs of one dtype and size")
+    st = lib.cp_allreduce(ALLREDUCE_ALGOS[algo], len(inputs), _table(inputs), _table(outs),
+                          inputs[0].numel(), dtype_code(inputs[0].dtype), _stream(stream, inputs[0]))
+    _check(st, "cp_allreduce")
+    return list(outs)
+
+
 def cp_profile_enable(enable: bool = True) -> None:
     _check(lib.cp_profile_enable(1 if enable else 0), "cp_profile_enable")
 
@@ -375,5 +395,6 @@ def cp_profile_read(capacity: int = 64):
 EXPORTED = ["cp_meta_bytes", "cp_build_meta", "cp_meta_status", "cp_attn_meta_bytes", "cp_build_attn_meta",
             "cp_partition_thd", "cp_gather_thd",
             "cp_partition_thd_multi", "cp_gather_thd_multi",
-            "cp_grad_return", "cp_grad_return_fused", "cp_slot_sum", "cp_status_string", "cp_version",
+            "cp_grad_return", "cp_grad_return_fused", "cp_slot_sum", "cp_allreduce",
+            "cp_status_string", "cp_version",
             "cp_profile_enable", "cp_profile_read"]

@@ -584,6 +584,49 @@ int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t 
   return hip_status(launch_slot_sum(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int cp_allreduce(int32_t algo, int32_t cp_size, const void* const* in, void* const* out,
+                 int64_t n_elems, int32_t dtype, cp_stream_t stream) {
+  if (algo != CP_ALLREDUCE_ONE_SHOT && algo != CP_ALLREDUCE_RING) return CP_ERR_ARG;
+  if (is_fp8(dtype) || dtype == CP_F16) return CP_ERR_UNSUPPORTED;
+  if (dtype != CP_F32 && dtype != CP_BF16) return CP_ERR_ARG;
+  if (cp_size < 1 || cp_size > CP_MAX_CP_SIZE || n_elems < 0) return CP_ERR_ARG;
+  const int64_t bytes = checked_bytes(n_elems, dtype_bytes(dtype));
+  if (bytes < 0) return CP_ERR_ARG;
+  if (n_elems == 0) return CP_OK;
+  if (in == nullptr || out == nullptr) return CP_ERR_ARG;
+  for (int r = 0; r < cp_size; ++r)
+    if (in[r] == nullptr || out[r] == nullptr) return CP_ERR_ARG;
+  int dev, st;
+  if ((st = current_device(&dev)) != CP_OK) return st;
+  std::vector<Range> ins, outs;
+  for (int r = 0; r < cp_size; ++r) {
+    if ((st = check_device_buf(in[r], bytes, dev)) != CP_OK) return st;
+    if ((st = check_device_buf(out[r], bytes, dev)) != CP_OK) return st;
+    ins.push_back(range_of(in[r], bytes));
+    outs.push_back(range_of(out[r], bytes));
+  }
+  if ((st = check_alias(outs, ins)) != CP_OK) return st;
+  AllreduceArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int r = 0; r < cp_size; ++r) {
+    a.in.p[r] = static_cast<const char*>(in[r]);
+    a.out.p[r] = static_cast<char*>(out[r]);
+  }
+  a.cp_size = cp_size;
+  a.n_elems = n_elems;
+  a.dtype = dtype;
+  const int64_t granule = 64 * (int64_t)cp_size;
+  a.chunk = (n_elems + granule - 1) / granule * 64;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (algo == CP_ALLREDUCE_ONE_SHOT) return hip_status(launch_allreduce_one_shot(a, s));
+  if (cp_size == 1) return hip_status(launch_ring_gather_step(a, 0, true, s));
+  for (int step = 0; step < cp_size - 1; ++step)
+    if ((st = hip_status(launch_ring_reduce_step(a, step, s))) != CP_OK) return st;
+  for (int step = 0; step < cp_size - 1; ++step)
+    if ((st = hip_status(launch_ring_gather_step(a, step, false, s))) != CP_OK) return st;
+  return CP_OK;
+}
+
 const char* cp_status_string(int status) {
   switch (status) {
     case CP_OK: return "ok";
@@ -599,7 +642,7 @@ const char* cp_status_string(int status) {
   }
 }
 
-int cp_version(void) { return 200; }
+int cp_version(void) { return 300; }
 
 int cp_profile_enable(int enable) {
   std::lock_guard<std::mutex> lock(g_prof_mutex);

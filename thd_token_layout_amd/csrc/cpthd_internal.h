@@ -118,6 +118,29 @@ struct FusedArgs {
 };
 hipError_t launch_fused(const FusedArgs& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- all-reduce
+// W rank buffers of n elements (f32 or bf16), every rank's out = the sum of
+// all W inputs.  One-shot: one launch, rank r reads all inputs and sums them
+// in rank order.  Ring: W chunks of `chunk` elements (the last ones possibly
+// short or empty); a reduce-scatter step s has rank r add its own input to
+// chunk (r-1-s) mod W received from rank r-1; an all-gather step s has rank r
+// copy chunk (r-s) mod W from rank r-1.
+struct AllreduceArgs {
+  ConstRankPtrs in;   // [W] inputs, n elements each
+  RankPtrs out;       // [W] outputs, n elements each (ring: the working buffers)
+  int32_t cp_size;
+  int64_t n_elems;
+  int64_t chunk;      // ring chunk length in elements (a multiple of 64)
+  int32_t dtype;      // CP_F32 or CP_BF16, inputs and outputs alike
+};
+hipError_t launch_allreduce_one_shot(const AllreduceArgs& a, hipStream_t stream);
+// Reduce-scatter step `step` (0..W-2) of the ring for all ranks in one launch.
+hipError_t launch_ring_reduce_step(const AllreduceArgs& a, int32_t step, hipStream_t stream);
+// All-gather step `step` (0..W-2) for all ranks; with from_input (W = 1 only)
+// every rank copies its own input instead.
+hipError_t launch_ring_gather_step(const AllreduceArgs& a, int32_t step, bool from_input,
+                                   hipStream_t stream);
+
 // ---------------------------------------------------------------- epochs
 // Writer `writer` (or every writer when writer < 0) stores `epoch` into
 // epochs[o][writer] for every owner o, with release ordering.

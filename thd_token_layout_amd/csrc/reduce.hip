@@ -27,6 +27,7 @@
 #include "device_common.h"
 
 #include <string>
+#include <type_traits>
 
 
 namespace cpthd {
@@ -433,6 +434,147 @@ epoch_wait_kernel(const uint32_t* epochs, int32_t W, int32_t owner, uint32_t epo
   }
 }
 
+// ---- all-reduce: one-shot and ring ---------------------------------------------
+// All W ranks' buffers sit in this device's HBM; each launch does one step of
+// the algorithm for every rank, ranks in blockIdx.y (dispatch runs rank by
+// rank, as W devices would each do their own share).
+
+// One-shot: rank r's workgroups sum all W inputs in rank order (seeded with
+// input 0, one fp32 add per further input) and write out[r].
+template <int T, int WB, bool VEC, int UPT>
+__global__ void __launch_bounds__(kBlock) allreduce_one_shot_kernel(AllreduceArgs a) {
+  const int W = a.cp_size;
+  char* const out = a.out.p[blockIdx.y];
+  constexpr bool SPLIT = split_layout<T, T>();
+  int64_t done = 0;
+  if constexpr (VEC) {
+    constexpr int64_t G = unit_group_elems<T, T>();
+    const int64_t nunits = a.n_elems / G * (G / 8);
+    const int64_t ntiles = (nunits + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+      int64_t unit[UPT], off[UPT];
+      bool ok[UPT];
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        unit[u] = tile * kBlock * UPT + (int64_t)u * kBlock + threadIdx.x;
+        ok[u] = unit[u] < nunits;
+        off[u] = 0;
+      }
+      F8 acc[UPT];
+      sum_units<T, SPLIT, WB, UPT, false>(acc, a.in, W, off, unit, ok);
+#pragma unroll
+      for (int u = 0; u < UPT; ++u)
+        if (ok[u]) store_unit<T, SPLIT>(out, unit[u], acc[u]);
+    }
+    done = nunits * 8;
+  }
+  const int64_t gstride = (int64_t)gridDim.x * kBlock;
+  for (int64_t k = done + (int64_t)blockIdx.x * kBlock + threadIdx.x; k < a.n_elems; k += gstride) {
+    float acc = load_elem<T>(a.in.p[0], k);
+    for (int w = 1; w < W; ++w) acc = acc + load_elem<T>(a.in.p[w], k);
+    store_elem<T>(out, k, acc);
+  }
+}
+
+// Chunk c of the ring: [lo, hi) elements.
+__device__ __forceinline__ void ring_chunk(const AllreduceArgs& a, int c, int64_t& lo, int64_t& hi) {
+  lo = (int64_t)c * a.chunk;
+  hi = lo + a.chunk;
+  if (lo > a.n_elems) lo = a.n_elems;
+  if (hi > a.n_elems) hi = a.n_elems;
+}
+
+// Ring reduce-scatter step: rank r receives chunk c = (r-1-step) mod W from
+// rank r-1 (its input at step 0, its working buffer after) and stores
+// received + own input, rounded to the buffer type.
+template <int T, bool VEC, int UPT>
+__global__ void __launch_bounds__(kBlock) ring_reduce_step_kernel(AllreduceArgs a, int32_t step) {
+  const int W = a.cp_size;
+  const int r = blockIdx.y;
+  const int prev = r == 0 ? W - 1 : r - 1;
+  const int c = ((r - 1 - step) % W + W) % W;
+  int64_t lo, hi;
+  ring_chunk(a, c, lo, hi);
+  const int64_t len = hi - lo;
+  constexpr int64_t eb = T == CP_F32 ? 4 : 2;
+  const char* const recv = (step == 0 ? a.in.p[prev] : a.out.p[prev]) + lo * eb;
+  const char* const own = a.in.p[r] + lo * eb;
+  char* const dst = a.out.p[r] + lo * eb;
+  constexpr bool SPLIT = split_layout<T, T>();
+  int64_t done = 0;
+  if constexpr (VEC) {
+    constexpr int64_t G = unit_group_elems<T, T>();
+    const int64_t nunits = len / G * (G / 8);
+    const int64_t ntiles = (nunits + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+      F8 x[UPT], y[UPT];
+      int64_t unit[UPT];
+      bool ok[UPT];
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        unit[u] = tile * kBlock * UPT + (int64_t)u * kBlock + threadIdx.x;
+        ok[u] = unit[u] < nunits;
+        if (ok[u]) {
+          load_unit<T, SPLIT>(x[u], recv, unit[u]);
+          load_unit<T, SPLIT>(y[u], own, unit[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UPT; ++u)
+        if (ok[u]) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[u].v[e] = x[u].v[e] + y[u].v[e];
+          store_unit<T, SPLIT>(dst, unit[u], x[u]);
+        }
+    }
+    done = nunits * 8;
+  }
+  const int64_t gstride = (int64_t)gridDim.x * kBlock;
+  for (int64_t k = done + (int64_t)blockIdx.x * kBlock + threadIdx.x; k < len; k += gstride)
+    store_elem<T>(dst, k, load_elem<T>(recv, k) + load_elem<T>(own, k));
+}
+
+// Ring all-gather step: rank r copies chunk c = (r-step) mod W from rank
+// r-1's working buffer, bit for bit.  FROM_IN (one rank): copy the input.
+template <int EB, bool VEC, bool FROM_IN>
+__global__ void __launch_bounds__(kBlock) ring_gather_step_kernel(AllreduceArgs a, int32_t step) {
+  const int W = a.cp_size;
+  const int r = blockIdx.y;
+  const int prev = r == 0 ? W - 1 : r - 1;
+  const int c = ((r - step) % W + W) % W;
+  int64_t lo, hi;
+  ring_chunk(a, c, lo, hi);
+  const char* const src = (FROM_IN ? a.in.p[r] : a.out.p[prev]) + lo * EB;
+  char* const dst = a.out.p[r] + lo * EB;
+  const int64_t len = hi - lo;
+  int64_t done = 0;
+  if constexpr (VEC) {
+    constexpr int kUpt = 4;  // 16-byte units per thread and tile
+    const int64_t n16 = len * EB / 16;
+    const int64_t ntiles = (n16 + (int64_t)kBlock * kUpt - 1) / ((int64_t)kBlock * kUpt);
+    const u32x4* s16 = reinterpret_cast<const u32x4*>(src);
+    u32x4* d16 = reinterpret_cast<u32x4*>(dst);
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+      u32x4 v[kUpt];
+      int64_t unit[kUpt];
+#pragma unroll
+      for (int u = 0; u < kUpt; ++u) {
+        unit[u] = tile * kBlock * kUpt + (int64_t)u * kBlock + threadIdx.x;
+        if (unit[u] < n16) v[u] = __builtin_nontemporal_load(s16 + unit[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kUpt; ++u)
+        if (unit[u] < n16) __builtin_nontemporal_store(v[u], d16 + unit[u]);
+    }
+    done = n16 * 16 / EB;
+  }
+  typedef typename std::conditional<EB == 4, unsigned int, unsigned short>::type E;
+  const E* se = reinterpret_cast<const E*>(src);
+  E* de = reinterpret_cast<E*>(dst);
+  const int64_t gstride = (int64_t)gridDim.x * kBlock;
+  for (int64_t k = done + (int64_t)blockIdx.x * kBlock + threadIdx.x; k < len; k += gstride) de[k] = se[k];
+}
+
 // ---- dispatch -------------------------------------------------------------------
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
@@ -558,6 +700,97 @@ hipError_t launch_fused_typed(const FusedArgs& a, bool vec, hipStream_t stream) 
                       : launch_fused_acc<IN, OUT, false>(a, vec, stream);
 }
 
+
+// ---- all-reduce launches --------------------------------------------------------
+template <int T, int WB>
+hipError_t launch_one_shot_wb(const AllreduceArgs& a, bool vec, hipStream_t stream) {
+  constexpr int UPT = sum_upt(T, WB);
+  static const std::string names[2] = {
+      std::string("allreduce_one_shot<") + dtype_tag(T) + "," + std::to_string(WB) + ",s>",
+      std::string("allreduce_one_shot<") + dtype_tag(T) + "," + std::to_string(WB) + ",v" +
+          std::to_string(UPT) + ">"};
+  int64_t blocks;
+  if (vec) {
+    constexpr int64_t G = unit_group_elems<T, T>();
+    blocks = (a.n_elems / G * (G / 8) + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
+  } else {
+    blocks = (a.n_elems + kBlock - 1) / kBlock;
+  }
+  if (blocks > kMaxGrid) blocks = kMaxGrid;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks, (unsigned)a.cp_size);
+  profile_before(names[vec ? 1 : 0].c_str(), stream);
+  if (vec)
+    hipLaunchKernelGGL((allreduce_one_shot_kernel<T, WB, true, UPT>), grid, dim3(kBlock), 0, stream, a);
+  else
+    hipLaunchKernelGGL((allreduce_one_shot_kernel<T, WB, false, 1>), grid, dim3(kBlock), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  profile_after(stream);
+  return e;
+}
+
+template <int T>
+hipError_t launch_one_shot_typed(const AllreduceArgs& a, bool vec, hipStream_t stream) {
+  const int W = a.cp_size;
+  if (W <= 1) return launch_one_shot_wb<T, 1>(a, vec, stream);
+  if (W <= 2) return launch_one_shot_wb<T, 2>(a, vec, stream);
+  if (W <= 4) return launch_one_shot_wb<T, 4>(a, vec, stream);
+  return launch_one_shot_wb<T, 8>(a, vec, stream);
+}
+
+bool allreduce_aligned(const AllreduceArgs& a) {
+  bool vec = true;
+  for (int w = 0; w < a.cp_size; ++w) vec = vec && aligned16(a.in.p[w]) && aligned16(a.out.p[w]);
+  return vec;
+}
+
+constexpr int kRingUpt = 2;  // 8-element units per thread in a reduce-scatter step
+
+template <int T>
+hipError_t launch_ring_reduce_typed(const AllreduceArgs& a, int32_t step, bool vec, hipStream_t stream) {
+  static const std::string names[2] = {std::string("ring_reduce_step<") + dtype_tag(T) + ",s>",
+                                       std::string("ring_reduce_step<") + dtype_tag(T) + ",v>"};
+  const int64_t len = a.chunk < a.n_elems ? a.chunk : a.n_elems;  // longest chunk
+  int64_t blocks;
+  if (vec) {
+    constexpr int64_t G = unit_group_elems<T, T>();
+    blocks = (len / G * (G / 8) + (int64_t)kBlock * kRingUpt - 1) / ((int64_t)kBlock * kRingUpt);
+  } else {
+    blocks = (len + kBlock - 1) / kBlock;
+  }
+  if (blocks > kMaxGrid) blocks = kMaxGrid;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks, (unsigned)a.cp_size);
+  profile_before(names[vec ? 1 : 0].c_str(), stream);
+  if (vec)
+    hipLaunchKernelGGL((ring_reduce_step_kernel<T, true, kRingUpt>), grid, dim3(kBlock), 0, stream, a, step);
+  else
+    hipLaunchKernelGGL((ring_reduce_step_kernel<T, false, 1>), grid, dim3(kBlock), 0, stream, a, step);
+  hipError_t e = hipGetLastError();
+  profile_after(stream);
+  return e;
+}
+
+template <int EB, bool FROM_IN>
+hipError_t launch_ring_gather_typed(const AllreduceArgs& a, int32_t step, bool vec, hipStream_t stream) {
+  static const std::string names[2] = {std::string("ring_gather_step<") + std::to_string(EB) + "B,s>",
+                                       std::string("ring_gather_step<") + std::to_string(EB) + "B,v>"};
+  const int64_t len = a.chunk < a.n_elems ? a.chunk : a.n_elems;
+  int64_t blocks = vec ? (len * EB / 16 + (int64_t)kBlock * 4 - 1) / ((int64_t)kBlock * 4)
+                       : (len + kBlock - 1) / kBlock;
+  if (blocks > kMaxGrid) blocks = kMaxGrid;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks, (unsigned)a.cp_size);
+  profile_before(names[vec ? 1 : 0].c_str(), stream);
+  if (vec)
+    hipLaunchKernelGGL((ring_gather_step_kernel<EB, true, FROM_IN>), grid, dim3(kBlock), 0, stream, a, step);
+  else
+    hipLaunchKernelGGL((ring_gather_step_kernel<EB, false, FROM_IN>), grid, dim3(kBlock), 0, stream, a, step);
+  hipError_t e = hipGetLastError();
+  profile_after(stream);
+  return e;
+}
+
 }  // namespace
 
 hipError_t launch_slot_sum(const SlotSumArgs& a, hipStream_t stream) {
@@ -582,6 +815,35 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
   if (a.in_dtype == CP_F32 && a.out_dtype == CP_BF16) return launch_fused_typed<CP_F32, CP_BF16>(a, vec, stream);
   if (a.in_dtype == CP_BF16 && a.out_dtype == CP_BF16) return launch_fused_typed<CP_BF16, CP_BF16>(a, vec, stream);
   if (a.in_dtype == CP_BF16 && a.out_dtype == CP_F32) return launch_fused_typed<CP_BF16, CP_F32>(a, vec, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_allreduce_one_shot(const AllreduceArgs& a, hipStream_t stream) {
+  if (a.n_elems == 0) return hipSuccess;
+  const bool vec = allreduce_aligned(a);
+  if (a.dtype == CP_F32) return launch_one_shot_typed<CP_F32>(a, vec, stream);
+  if (a.dtype == CP_BF16) return launch_one_shot_typed<CP_BF16>(a, vec, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_ring_reduce_step(const AllreduceArgs& a, int32_t step, hipStream_t stream) {
+  if (a.n_elems == 0) return hipSuccess;
+  const bool vec = allreduce_aligned(a);
+  if (a.dtype == CP_F32) return launch_ring_reduce_typed<CP_F32>(a, step, vec, stream);
+  if (a.dtype == CP_BF16) return launch_ring_reduce_typed<CP_BF16>(a, step, vec, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_ring_gather_step(const AllreduceArgs& a, int32_t step, bool from_input,
+                                   hipStream_t stream) {
+  if (a.n_elems == 0) return hipSuccess;
+  const bool vec = allreduce_aligned(a);
+  if (a.dtype == CP_F32)
+    return from_input ? launch_ring_gather_typed<4, true>(a, step, vec, stream)
+                      : launch_ring_gather_typed<4, false>(a, step, vec, stream);
+  if (a.dtype == CP_BF16)
+    return from_input ? launch_ring_gather_typed<2, true>(a, step, vec, stream)
+                      : launch_ring_gather_typed<2, false>(a, step, vec, stream);
   return hipErrorInvalidValue;
 }
 
