@@ -92,8 +92,28 @@ int current_device(int* dev) {
 // sizes say), so that no kernel can touch memory outside what the caller
 // passed.  When the runtime cannot report the allocation's extent, the
 // membership check alone applies.
-int check_device_buf(const void* p, int64_t bytes, int dev) {
+//
+// Buffers of one call often lie in one allocation (rank slices of one tensor,
+// small tensors that the caching allocator put in one segment), and the two
+// runtime lookups per buffer are most of a small call's host time; `cache`
+// keeps the allocations already checked during the current call, so a buffer
+// inside one of them is checked against its extent without a lookup.  A cache
+// lives for one call only (an allocation can be freed between calls).
+struct AllocCache {
+  static constexpr int kCap = 16;
+  uintptr_t base[kCap];
+  uintptr_t end[kCap];
+  int n = 0;
+};
+
+int check_device_buf(const void* p, int64_t bytes, int dev, AllocCache* cache) {
   if (p == nullptr) return CP_ERR_ARG;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  if (cache != nullptr) {
+    for (int i = 0; i < cache->n; ++i)
+      if (a >= cache->base[i] && a < cache->end[i])
+        return bytes >= 0 && (uint64_t)bytes <= cache->end[i] - a ? CP_OK : CP_ERR_SHAPE;
+  }
   hipPointerAttribute_t attr;
   memset(&attr, 0, sizeof(attr));
   if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
@@ -108,8 +128,12 @@ int check_device_buf(const void* p, int64_t bytes, int dev) {
     return CP_OK;
   }
   const uintptr_t end = reinterpret_cast<uintptr_t>(base) + size;
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
   if (a < reinterpret_cast<uintptr_t>(base) || bytes < 0 || (uint64_t)bytes > end - a) return CP_ERR_SHAPE;
+  if (cache != nullptr && cache->n < AllocCache::kCap) {
+    cache->base[cache->n] = reinterpret_cast<uintptr_t>(base);
+    cache->end[cache->n] = end;
+    ++cache->n;
+  }
   return CP_OK;
 }
 
@@ -218,8 +242,9 @@ int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tok
   if (meta_bytes < cp_meta_bytes(num_docs, cp_size)) return CP_ERR_SHAPE;
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
-  if ((st = check_device_buf(cu_seqlens, 4 * (int64_t)(num_docs + 1), dev)) != CP_OK) return st;
-  if ((st = check_device_buf(meta, (int64_t)cp_meta_bytes(num_docs, cp_size), dev)) != CP_OK) return st;
+  AllocCache cache;
+  if ((st = check_device_buf(cu_seqlens, 4 * (int64_t)(num_docs + 1), dev, &cache)) != CP_OK) return st;
+  if ((st = check_device_buf(meta, (int64_t)cp_meta_bytes(num_docs, cp_size), dev, &cache)) != CP_OK) return st;
   if ((st = check_alias({range_of(meta, (int64_t)meta_bytes)},
                         {range_of(cu_seqlens, 4 * (int64_t)(num_docs + 1))})) != CP_OK)
     return st;
@@ -243,8 +268,9 @@ int cp_build_attn_meta(const void* meta, int32_t num_docs, int32_t cp_size, void
   if (attn_bytes < cp_attn_meta_bytes(num_docs, cp_size)) return CP_ERR_SHAPE;
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
-  if ((st = check_device_buf(meta, (int64_t)cp_meta_bytes(num_docs, cp_size), dev)) != CP_OK) return st;
-  if ((st = check_device_buf(attn, (int64_t)cp_attn_meta_bytes(num_docs, cp_size), dev)) != CP_OK) return st;
+  AllocCache cache;
+  if ((st = check_device_buf(meta, (int64_t)cp_meta_bytes(num_docs, cp_size), dev, &cache)) != CP_OK) return st;
+  if ((st = check_device_buf(attn, (int64_t)cp_attn_meta_bytes(num_docs, cp_size), dev, &cache)) != CP_OK) return st;
   if ((st = check_alias({range_of(attn, (int64_t)attn_bytes)},
                         {range_of(meta, (int64_t)cp_meta_bytes(num_docs, cp_size))})) != CP_OK)
     return st;
@@ -256,7 +282,8 @@ int cp_meta_status(const void* meta, cp_stream_t stream, int32_t* flags_out,
   if (meta == nullptr) return CP_ERR_ARG;
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
-  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev)) != CP_OK) return st;
+  AllocCache cache;
+  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev, &cache)) != CP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (hipStreamSynchronize(s) != hipSuccess) {
     (void)hipGetLastError();
@@ -292,11 +319,12 @@ static int layout_call(int32_t n_tensors, const void* const* ins, void* const* o
   if (row_bytes < 0 || bytes < 0) return CP_ERR_ARG;
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
-  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev)) != CP_OK) return st;
+  AllocCache cache;
+  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev, &cache)) != CP_OK) return st;
   std::vector<Range> in_ranges{range_of(meta, sizeof(cp_meta_header))}, out_ranges;
   for (int t = 0; t < n_tensors; ++t) {
-    if ((st = check_device_buf(ins[t], bytes, dev)) != CP_OK) return st;
-    if ((st = check_device_buf(outs[t], bytes, dev)) != CP_OK) return st;
+    if ((st = check_device_buf(ins[t], bytes, dev, &cache)) != CP_OK) return st;
+    if ((st = check_device_buf(outs[t], bytes, dev, &cache)) != CP_OK) return st;
     in_ranges.push_back(range_of(ins[t], bytes));
     out_ranges.push_back(range_of(outs[t], bytes));
   }
@@ -401,25 +429,26 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
   }
   int dev;
   if ((st = current_device(&dev)) != CP_OK) return st;
-  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev)) != CP_OK) return st;
-  if (epochs && (st = check_device_buf(epochs, 4 * (int64_t)W * W, dev)) != CP_OK) return st;
+  AllocCache cache;
+  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev, &cache)) != CP_OK) return st;
+  if (epochs && (st = check_device_buf(epochs, 4 * (int64_t)W * W, dev, &cache)) != CP_OK) return st;
   std::vector<Range> ins, outs;
   ins.push_back(range_of(meta, sizeof(cp_meta_header)));
   for (int t = 0; t < n_tensors; ++t) {
     for (int w = w_lo; w < w_hi; ++w) {
-      if ((st = check_device_buf(G(t, w), total_tokens * in_row, dev)) != CP_OK) return st;
+      if ((st = check_device_buf(G(t, w), total_tokens * in_row, dev, &cache)) != CP_OK) return st;
       ins.push_back(range_of(G(t, w), total_tokens * in_row));
       for (int o = 0; o < W; ++o) {
-        if ((st = check_device_buf(S(t, o, w), n * in_row, dev)) != CP_OK) return st;
+        if ((st = check_device_buf(S(t, o, w), n * in_row, dev, &cache)) != CP_OK) return st;
         outs.push_back(range_of(S(t, o, w), n * in_row));
       }
     }
     for (int o = o_lo; o < o_hi; ++o) {
-      if ((st = check_device_buf(O(t, o), n * out_row, dev)) != CP_OK) return st;
+      if ((st = check_device_buf(O(t, o), n * out_row, dev, &cache)) != CP_OK) return st;
       outs.push_back(range_of(O(t, o), n * out_row));
       for (int w = 0; w < W; ++w) {
         if (w >= w_lo && w < w_hi) continue;  // already listed as an output of this call
-        if ((st = check_device_buf(S(t, o, w), n * in_row, dev)) != CP_OK) return st;
+        if ((st = check_device_buf(S(t, o, w), n * in_row, dev, &cache)) != CP_OK) return st;
         ins.push_back(range_of(S(t, o, w), n * in_row));
       }
     }
@@ -514,18 +543,19 @@ int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
   }
   int dev;
   if ((st = current_device(&dev)) != CP_OK) return st;
-  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev)) != CP_OK) return st;
+  AllocCache cache;
+  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev, &cache)) != CP_OK) return st;
   std::vector<Range> ins, outs;
   ins.push_back(range_of(meta, sizeof(cp_meta_header)));
   for (int t = 0; t < n_tensors; ++t) {
     for (int w = 0; w < W; ++w) {
       const void* g = grads[(size_t)t * W + w];
-      if ((st = check_device_buf(g, total_tokens * in_row, dev)) != CP_OK) return st;
+      if ((st = check_device_buf(g, total_tokens * in_row, dev, &cache)) != CP_OK) return st;
       ins.push_back(range_of(g, total_tokens * in_row));
     }
     for (int o = o_lo; o < o_hi; ++o) {
       void* p = out[(size_t)t * W + o];
-      if ((st = check_device_buf(p, n * out_row, dev)) != CP_OK) return st;
+      if ((st = check_device_buf(p, n * out_row, dev, &cache)) != CP_OK) return st;
       outs.push_back(range_of(p, n * out_row));
     }
   }
@@ -563,12 +593,13 @@ int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t 
     if (slots[w] == nullptr) return CP_ERR_ARG;
   int dev;
   if ((st = current_device(&dev)) != CP_OK) return st;
+  AllocCache cache;
   std::vector<Range> ins;
   for (int w = 0; w < num_slots; ++w) {
-    if ((st = check_device_buf(slots[w], n_elems * dtype_bytes(in_dtype), dev)) != CP_OK) return st;
+    if ((st = check_device_buf(slots[w], n_elems * dtype_bytes(in_dtype), dev, &cache)) != CP_OK) return st;
     ins.push_back(range_of(slots[w], n_elems * dtype_bytes(in_dtype)));
   }
-  if ((st = check_device_buf(out, n_elems * dtype_bytes(out_dtype), dev)) != CP_OK) return st;
+  if ((st = check_device_buf(out, n_elems * dtype_bytes(out_dtype), dev, &cache)) != CP_OK) return st;
   if ((st = check_alias({range_of(out, n_elems * dtype_bytes(out_dtype))}, ins)) != CP_OK) return st;
   SlotSumArgs a;
   memset(&a, 0, sizeof(a));
@@ -598,10 +629,11 @@ int cp_allreduce(int32_t algo, int32_t cp_size, const void* const* in, void* con
     if (in[r] == nullptr || out[r] == nullptr) return CP_ERR_ARG;
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
+  AllocCache cache;
   std::vector<Range> ins, outs;
   for (int r = 0; r < cp_size; ++r) {
-    if ((st = check_device_buf(in[r], bytes, dev)) != CP_OK) return st;
-    if ((st = check_device_buf(out[r], bytes, dev)) != CP_OK) return st;
+    if ((st = check_device_buf(in[r], bytes, dev, &cache)) != CP_OK) return st;
+    if ((st = check_device_buf(out[r], bytes, dev, &cache)) != CP_OK) return st;
     ins.push_back(range_of(in[r], bytes));
     outs.push_back(range_of(out[r], bytes));
   }
