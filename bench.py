@@ -38,6 +38,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def sweep_buffers(WL, torch, dev):
+    """[(bytes per slot, 8 fp32 slots, output)] for 1 KiB ... 16 MiB per slot."""
+    w_sw = WL.WORKLOADS["sweep_w8"]
+    res = []
+    for nbytes in WL.SWEEP_BYTES:
+        k = nbytes // 4
+        slots = WL.random_tensors(w_sw, 8, shape=(k,), device=dev, seed_offset=nbytes)
+        res.append((nbytes, slots, torch.empty(k, device=dev)))
+    return res
+
+
 class Step:
     """Buffers and calls of one step; every op records its algorithmic bytes."""
 
@@ -48,7 +59,6 @@ class Step:
         w_dcs = WL.WORKLOADS["dcs_s256k_w4"]
         w_pc = WL.WORKLOADS["pc_s256k_w4"]
         w_gr = WL.WORKLOADS["grad_s256k_w4"]
-        w_sw = WL.WORKLOADS["sweep_w8"]
         if S != w_dcs.total_tokens:
             w_dcs, w_pc, w_gr = (WL.scaled(w, total_tokens=S) for w in (w_dcs, w_pc, w_gr))
         self.S = S
@@ -81,11 +91,7 @@ class Step:
         self.epochs = torch.zeros((Wg, Wg), dtype=torch.int32, device=dev)
         self.epoch = 0
         # ---- sweep
-        self.sweep = []
-        for nbytes in WL.SWEEP_BYTES:
-            k = nbytes // 4
-            slots = WL.random_tensors(w_sw, 8, shape=(k,), device=dev, seed_offset=nbytes)
-            self.sweep.append((nbytes, slots, torch.empty(k, device=dev)))
+        self.sweep = sweep_buffers(WL, torch, dev)
 
         metas = [(cu_dcs, cp.CP_POLICY_DUAL_CHUNK_SWAP, self.meta_dcs),
                  (cu_pc, cp.CP_POLICY_PACKED_CONTIGUOUS, self.meta_pc),
@@ -362,6 +368,20 @@ def eager_us_per_call(torch, fn, reps: int):
     return e0.elapsed_time(e1) * 1000.0 / reps
 
 
+def c_abi_call(cp, torch, name, *args):
+    """A call of the C entry point `name` with its arguments marshalled once (ctypes),
+    on torch's current stream: the eager cost of the C ABI without the binding's
+    per-call marshalling."""
+    import ctypes
+
+    fn = getattr(cp.lib, name)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    st = fn(*args, stream)
+    if st != 0:
+        raise RuntimeError(f"{name}: status {st}")
+    return lambda: fn(*args, stream)
+
+
 def kernel_us_per_call(cp, fn, calls: int = 20):
     """Summed duration of the kernels one call launches (HIP events around each launch)."""
     cp.cp_profile_enable(True)
@@ -373,35 +393,50 @@ def kernel_us_per_call(cp, fn, calls: int = 20):
 
 
 def sweep_latency(step: Step, cp, torch, reps: int = 1000):
-    """Per-call latency of the W=8 slot sum: eager (host validation + launch + kernel),
-    the kernel alone (HIP events around each launch), and replayed from a HIP graph."""
+    """Per-call latency of the W=8 slot sum: eager through the Python binding (marshalling +
+    host validation + launch + kernel), eager through the C ABI with arguments marshalled
+    once, the kernel alone (HIP events around each launch), and replayed from a HIP graph."""
+    res = []
+    import ctypes
+
     res = []
     for nbytes, slots, out in step.sweep:
         def call():
             cp.cp_slot_sum(slots, out)
+        raw = c_abi_call(cp, torch, "cp_slot_sum", len(slots),
+                         (ctypes.c_void_p * len(slots))(*[t.data_ptr() for t in slots]),
+                         ctypes.c_void_p(out.data_ptr()), out.numel(), cp.CP_F32, cp.CP_F32, 0)
         kus, _ = kernel_us_per_call(cp, call)
         res.append({"bytes_per_slot": nbytes, "us_per_call": round(eager_us_per_call(torch, call, reps), 2),
+                    "c_abi_us_per_call": round(eager_us_per_call(torch, raw, reps), 2),
                     "kernel_us": round(kus, 2),
                     "graph_us_per_call": round(graph_us_per_call(torch, call), 2)})
     return res
 
 
-def allreduce_sweep(step: Step, cp, torch):
+def allreduce_sweep(sweep, cp, torch):
     """All-reduce of W=8 fp32 rank buffers of 1 KiB ... 16 MiB, every rank emulated on this
     GPU: one-shot (one launch, each rank reads all 8 buffers) against ring (14 launches:
-    7 reduce-scatter and 7 all-gather steps).  Per call: eager latency, summed kernel time,
-    and time replayed from a HIP graph; algorithmic bytes over all 8 ranks (one-shot 72 x
-    size, ring 35 x size) over the kernel time."""
+    7 reduce-scatter and 7 all-gather steps).  Per call: eager latency (through the binding
+    and through the C ABI), summed kernel time, and time replayed from a HIP graph;
+    algorithmic bytes over all 8 ranks (one-shot 72 x size, ring 35 x size) over the
+    kernel time."""
+    import ctypes
+
     W = 8
     res = []
-    for nbytes, slots, _ in step.sweep:
+    for nbytes, slots, _ in sweep:
         outs = [torch.empty_like(slots[0]) for _ in range(W)]
         row = {"bytes_per_rank": nbytes}
         for algo, factor in (("one_shot", W * (W + 1)), ("ring", 5 * (W - 1))):
             def call(algo=algo):
                 cp.cp_allreduce(slots, outs, algo=algo)
+            raw = c_abi_call(cp, torch, "cp_allreduce", cp.ALLREDUCE_ALGOS[algo], W,
+                             (ctypes.c_void_p * W)(*[t.data_ptr() for t in slots]),
+                             (ctypes.c_void_p * W)(*[t.data_ptr() for t in outs]), slots[0].numel(), cp.CP_F32)
             kus, launches = kernel_us_per_call(cp, call)
             row[algo] = {"us_per_call": round(eager_us_per_call(torch, call, 200), 2),
+                         "c_abi_us_per_call": round(eager_us_per_call(torch, raw, 200), 2),
                          "kernel_us": round(kus, 2), "launches": launches,
                          "graph_us_per_call": round(graph_us_per_call(torch, call, calls=20), 2),
                          "kernel_gbs": round(factor * nbytes / (kus * 1e-6) / 1e9, 1) if kus > 0 else None}
@@ -429,6 +464,9 @@ def main():
     ap.add_argument("--only-configs", action="store_true",
                     help="run only the per-workload measurements and print them as one JSON line "
                          "(for profiling them on their own; not the benchmark line)")
+    ap.add_argument("--only-allreduce", action="store_true",
+                    help="run only the one-shot / ring all-reduce sweep and print it as one JSON line "
+                         "(for profiling it on its own; not the benchmark line)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run one plain 1 GiB device copy (torch copy_) first, as the reference "
                          "dispatch for scaling hardware traffic counters")
@@ -454,6 +492,11 @@ def main():
         torch.cuda.synchronize()
         log("[bench] calibration copy: 1 GiB read + 1 GiB written")
         del a, b
+    if args.only_allreduce:
+        log("[bench] all-reduce sweep only")
+        print(json.dumps({"allreduce_sweep": allreduce_sweep(sweep_buffers(WL, torch, dev), cp, torch)}),
+              flush=True)
+        return
     if args.only_configs:
         log("[bench] per-config measurements only")
         print(json.dumps({"per_config": per_config(cp, WL, torch, dev)}), flush=True)
@@ -504,7 +547,7 @@ def main():
     sweep = None if args.no_sweep_latency else sweep_latency(step, cp, torch)
     if not args.no_allreduce:
         log("[bench] all-reduce sweep (one-shot, ring)")
-    allreduce = None if args.no_allreduce else allreduce_sweep(step, cp, torch)
+    allreduce = None if args.no_allreduce else allreduce_sweep(step.sweep, cp, torch)
     num_docs = step.num_docs
     ops = [{"op": n, "bytes": b} for n, b, _ in step.ops]
     configs = None
