@@ -82,6 +82,23 @@ def test_sweep_sizes(cp, algo, size):
     check(cp, algo, xs, outs)
 
 
+@pytest.mark.parametrize("seed", range(48))
+def test_random_configurations(cp, seed):
+    """Seeded random rank counts, sizes, dtypes, algorithms and view offsets."""
+    rng = np.random.default_rng(5000 + seed)
+    W = int(rng.choice([1, 2, 3, 4, 6, 8, 11, 16, 32]))
+    n = int(rng.choice([int(rng.integers(0, 200)), int(rng.integers(200, 5000)), int(rng.integers(5000, 300000))]))
+    dtype = [torch.float32, torch.bfloat16][int(rng.integers(0, 2))]
+    algo = ["one_shot", "ring"][int(rng.integers(0, 2))]
+    off_in, off_out = (int(v) for v in rng.choice([0, 0, 0, 1, 3], size=2))
+    say(f"case allreduce random seed={seed}: {algo} W={W} n={n} {dtype} offsets={off_in},{off_out}")
+    xs = rank_inputs(W, n, dtype, seed=seed, offset=off_in)
+    outs = nan_outputs(W, n, dtype, offset=off_out)
+    cp.cp_allreduce(xs, outs, algo=algo)
+    torch.cuda.synchronize()
+    check(cp, algo, xs, outs)
+
+
 @pytest.mark.parametrize("algo", ["one_shot", "ring"])
 def test_special_values(cp, algo):
     """Signed zeros, infinities, NaN, overflow to inf, denormals; NaN results are
