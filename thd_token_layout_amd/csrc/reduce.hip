@@ -435,6 +435,12 @@ epoch_wait_kernel(const uint32_t* epochs, int32_t W, int32_t owner, uint32_t epo
 }
 
 // ---- all-reduce: one-shot and ring ---------------------------------------------
+// "Low Latency Communication Kernels with NVSHMEM": the all-reduce algorithms
+// picked by message size and the exercise comparing a one-shot all-reduce
+// with a ring over 1 KB - 16 MB.  One-shot: every rank sums all W buffers
+// itself.  Ring: a reduce-scatter then an all-gather, W-1 steps each, every
+// rank passing one chunk to rank r+1 per step; partials travel in the buffer
+// type, so a bf16 ring rounds after each add.
 // All W ranks' buffers sit in this device's HBM; each launch does one step of
 // the algorithm for every rank, ranks in blockIdx.y (dispatch runs rank by
 // rank, as W devices would each do their own share).
