@@ -591,8 +591,8 @@ const char* dtype_tag(int dt) { return dt == CP_F32 ? "f32" : "bf16"; }
 // At most 8 slots x 8 floats of loaded data per thread and pass: more raises
 // register use enough to lower occupancy (a W=8 bf16 sum with 2 units per
 // thread measured 25% slower).
-constexpr int sum_upt(int in_dtype, int wb) { return wb <= 2 ? 4 : wb <= 4 ? 2 : 1; }
-constexpr int fused_upl(int in_dtype, int wb) { return wb <= 2 ? 2 : 1; }
+constexpr int sum_upt(int wb) { return wb <= 2 ? 4 : wb <= 4 ? 2 : 1; }
+constexpr int fused_upl(int wb) { return wb <= 2 ? 2 : 1; }
 constexpr int kFusedWpr = 4;
 // Fused shapes, from a sweep on the S=262144 (W=4 fp32) and S=131072 (W=8
 // bf16) shapes: flat unit tiles, 2 units per thread for W <= 4 (6.20 TB/s,
@@ -600,7 +600,7 @@ constexpr int kFusedWpr = 4;
 
 template <int IN, int OUT, int WB, bool ACC>
 hipError_t launch_sum_wb(const SlotSumArgs& a, bool vec, hipStream_t stream) {
-  constexpr int UPT = sum_upt(IN, WB);
+  constexpr int UPT = sum_upt(WB);
   const std::string tag = std::string(ACC ? "slot_sum_acc<" : "slot_sum<") + dtype_tag(IN) + "," +
                           dtype_tag(OUT) + "," + std::to_string(WB) + ",";
   static const std::string names[2] = {tag + "s>", tag + "v" + std::to_string(UPT) + ">"};
@@ -648,7 +648,7 @@ hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
   const std::string tag = std::string(ACC ? "fused_grad_return_acc<" : "fused_grad_return<") + dtype_tag(IN) +
                           "," + dtype_tag(OUT) + "," + std::to_string(WB) + ",";
   static const std::string names[4] = {tag + "s>", tag + "flat1>", tag + "flat2>",
-                                       tag + "v" + std::to_string(fused_upl(IN, WB)) + "/" +
+                                       tag + "v" + std::to_string(fused_upl(WB)) + "/" +
                                            std::to_string(kFusedWpr) + ">"};
   vec = vec && a.row_elems % unit_group_elems<IN, OUT>() == 0;  // whole unit groups per row
   const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * (a.total_tokens / a.cp_size);
@@ -679,7 +679,7 @@ hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
     hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, 2, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0, stream,
                        a, magic);
   } else if (kind == 3) {
-    hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, true, kFusedWpr, fused_upl(IN, WB), ACC>),
+    hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, true, kFusedWpr, fused_upl(WB), ACC>),
                        dim3((unsigned)blocks), dim3(kBlock), 0, stream, a);
   } else {
     hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, false, 1, 1, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0,
@@ -710,7 +710,7 @@ hipError_t launch_fused_typed(const FusedArgs& a, bool vec, hipStream_t stream) 
 // ---- all-reduce launches --------------------------------------------------------
 template <int T, int WB>
 hipError_t launch_one_shot_wb(const AllreduceArgs& a, bool vec, hipStream_t stream) {
-  constexpr int UPT = sum_upt(T, WB);
+  constexpr int UPT = sum_upt(WB);
   static const std::string names[2] = {
       std::string("allreduce_one_shot<") + dtype_tag(T) + "," + std::to_string(WB) + ",s>",
       std::string("allreduce_one_shot<") + dtype_tag(T) + "," + std::to_string(WB) + ",v" +
