@@ -359,16 +359,27 @@ def cp_slot_sum(slots: Sequence[torch.Tensor], out: torch.Tensor, accumulate: bo
 ALLREDUCE_ALGOS = {"one_shot": CP_ALLREDUCE_ONE_SHOT, "ring": CP_ALLREDUCE_RING}
 
 
+def _uniform_table(ts, dtype, n: int) -> "ctypes.Array":
+    """Pointer table of contiguous tensors that all have `dtype` and `n` elements."""
+    ptrs = []
+    for t in ts:
+        if t.dtype != dtype or t.numel() != n or not t.is_contiguous():
+            raise ValueError("cp_allreduce: W contiguous inputs and W outputs of one dtype and size")
+        ptrs.append(t.data_ptr() or None)
+    return (_vp * len(ptrs))(*ptrs)
+
+
 def cp_allreduce(inputs: Sequence[torch.Tensor], outs: Optional[Sequence[torch.Tensor]] = None,
                  algo: str = "one_shot", stream=None) -> List[torch.Tensor]:
     """Every rank's out = the sum of all W inputs (W rank buffers on this device)."""
     if outs is None:
         outs = [torch.empty_like(x) for x in inputs]
-    if len(outs) != len(inputs) or any(t.dtype != inputs[0].dtype or t.numel() != inputs[0].numel()
-                                       for t in list(inputs) + list(outs)):
-        raise ValueError("cp_allreduce: W inputs and W outputs of one dtype and size")
-    st = lib.cp_allreduce(ALLREDUCE_ALGOS[algo], len(inputs), _table(inputs), _table(outs),
-                          inputs[0].numel(), dtype_code(inputs[0].dtype), _stream(stream, inputs[0]))
+    if len(outs) != len(inputs):
+        raise ValueError("cp_allreduce: as many outputs as inputs")
+    x0 = inputs[0]
+    dt, n = x0.dtype, x0.numel()
+    st = lib.cp_allreduce(ALLREDUCE_ALGOS[algo], len(inputs), _uniform_table(inputs, dt, n),
+                          _uniform_table(outs, dt, n), n, dtype_code(dt), _stream(stream, x0))
     _check(st, "cp_allreduce")
     return list(outs)
 
