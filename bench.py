@@ -417,8 +417,9 @@ def sweep_latency(step: Step, cp, torch, reps: int = 1000):
 def allreduce_sweep(sweep, cp, torch):
     """All-reduce of W=8 fp32 rank buffers of 1 KiB ... 16 MiB, every rank emulated on this
     GPU: one-shot (one launch, each rank reads all 8 buffers) against ring (14 launches:
-    7 reduce-scatter and 7 all-gather steps).  Per call: eager latency (through the binding
-    and through the C ABI), summed kernel time, and time replayed from a HIP graph;
+    7 reduce-scatter and 7 all-gather steps) and the same ring in one launch with
+    in-kernel signals.  Per call: eager latency (through the binding and through the
+    C ABI), summed kernel time, and (launch-per-step forms) time replayed from a HIP graph;
     algorithmic bytes over all 8 ranks (one-shot 72 x size, ring 35 x size) over the
     kernel time."""
     import ctypes
@@ -440,8 +441,34 @@ def allreduce_sweep(sweep, cp, torch):
                          "kernel_us": round(kus, 2), "launches": launches,
                          "graph_us_per_call": round(graph_us_per_call(torch, call, calls=20), 2),
                          "kernel_gbs": round(factor * nbytes / (kus * 1e-6) / 1e9, 1) if kus > 0 else None}
+        # the ring in one launch (in-kernel signals): every call needs a new epoch, so it
+        # is timed eagerly only (a captured call would replay a stale epoch)
+        sig = torch.zeros(cp.cp_allreduce_signal_bytes(W), dtype=torch.uint8, device=slots[0].device)
+        epoch = [0]
+
+        def call_sig():
+            epoch[0] += 1
+            cp.cp_allreduce_signal(slots, sig, epoch[0], outs=outs)
+
+        fn = cp.lib.cp_allreduce_signal
+        tin = (ctypes.c_void_p * W)(*[t.data_ptr() for t in slots])
+        tout = (ctypes.c_void_p * W)(*[t.data_ptr() for t in outs])
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+        def raw_sig():
+            epoch[0] += 1
+            fn(W, tin, tout, slots[0].numel(), cp.CP_F32, ctypes.c_void_p(sig.data_ptr()), sig.numel(),
+               epoch[0], 0, stream)
+
+        kus, launches = kernel_us_per_call(cp, call_sig)
+        row["ring_one_launch"] = {"us_per_call": round(eager_us_per_call(torch, call_sig, 200), 2),
+                                  "c_abi_us_per_call": round(eager_us_per_call(torch, raw_sig, 200), 2),
+                                  "kernel_us": round(kus, 2), "launches": launches,
+                                  "kernel_gbs": round(5 * (W - 1) * nbytes / (kus * 1e-6) / 1e9, 1) if kus > 0 else None}
+        if cp.cp_allreduce_signal_status(sig, W, epoch[0]) != cp.CP_OK:
+            raise RuntimeError("one-launch ring reported a stale epoch or a timeout")
         res.append(row)
-        del outs
+        del outs, sig
     faster = [r["bytes_per_rank"] for r in res
               if r["ring"]["graph_us_per_call"] < r["one_shot"]["graph_us_per_call"]]
     return {"cp_size": W, "dtype": "f32", "sizes": res,

@@ -455,6 +455,54 @@ int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t 
 int cp_allreduce(int32_t algo, int32_t cp_size, const void* const* in, void* const* out,
                  int64_t n_elems, int32_t dtype, cp_stream_t stream);
 
+/*
+ * The ring of cp_allreduce in ONE launch: the persistent, in-kernel-signalling
+ * form that [LL] sets against one launch per communication step (launch
+ * overhead removed; the steps of a collective run inside one kernel).  Rank r
+ * of tile t waits, before each of its 2(W-1) steps but the first, until rank
+ * r-1 of the same tile has published the previous step through a device flag.
+ * Same chunks, same order, same rounding as CP_ALLREDUCE_RING: the results are
+ * the same bits.  Each rank gets about sqrt(q / 2048) workgroups (q = chunk
+ * length in elements), at most 16, and all ranks together at most half of
+ * what the device holds at once, so every workgroup a wait depends on is
+ * running (an unmet wait ends in a reported timeout, never a hang).  On one
+ * MI355X each hop costs about as much as a kernel boundary replayed from a
+ * HIP graph (agent-scope release and acquire act on whole L2 caches): this
+ * form pays off against eager per-step launches for small messages only.
+ *
+ * cp_allreduce_signal_bytes - bytes of the signal buffer for W ranks (0 for W
+ * outside [1, 64]).  Layout (uint64 words): [0] the largest epoch in which a
+ * wait timed out, [1] the largest epoch found stale, then the flags
+ * [W][256] = (epoch << 8) + steps finished.
+ *
+ * cp_allreduce_signal
+ *   cp_size, in, out, n_elems, dtype   as cp_allreduce
+ *   signals        device buffer of at least cp_allreduce_signal_bytes(W)
+ *                  bytes (signals_bytes), caller-owned, zero-filled once before
+ *                  its first use; it must not overlap any input or output
+ *   epoch          in [1, 2^55), larger than the epoch of every earlier call on
+ *                  this buffer (so no clearing is needed between calls); a call
+ *                  whose epoch is not larger finds flags at or above its own
+ *                  base, records its epoch in word [1] and stops, leaving
+ *                  `out` undefined (later calls need a still larger epoch)
+ *   wait_timeout_us  limit of each wait (<= 0: 2 s); a wait that runs out
+ *                  records the epoch in word [0] and every workgroup stops,
+ *                  leaving `out` undefined - the kernel never hangs
+ * Returns CP_ERR_UNSUPPORTED when W workgroups exceed half the resident capacity.
+ * W = 1 is one copy (no signalling).  Calls that share a signal buffer must
+ * not overlap in time.
+ *
+ * cp_allreduce_signal_status - synchronize `stream`, then report the call of
+ * `epoch` (or a later call on the same buffer): CP_ERR_ARG if an epoch was
+ * stale, CP_ERR_TIMEOUT if a wait ran out, else CP_OK.  Not for HIP graphs:
+ * a replayed call would reuse its recorded epoch, which is then stale.
+ */
+size_t cp_allreduce_signal_bytes(int32_t cp_size);
+int cp_allreduce_signal(int32_t cp_size, const void* const* in, void* const* out, int64_t n_elems,
+                        int32_t dtype, void* signals, size_t signals_bytes, uint64_t epoch,
+                        int64_t wait_timeout_us, cp_stream_t stream);
+int cp_allreduce_signal_status(const void* signals, int32_t cp_size, uint64_t epoch, cp_stream_t stream);
+
 /* ------------------------------------------------------------ utilities */
 /* Static text for a status code (never NULL). */
 const char* cp_status_string(int status);

@@ -189,6 +189,20 @@ def test_host_checks_before_any_hip_call(cp):
         assert ar(algo, 2, tab, nulls, 10, cp.CP_BF16, None) == cp.CP_ERR_ARG
         assert ar(algo, 2, None, tab, 10, cp.CP_F32, None) == cp.CP_ERR_ARG
         assert ar(algo, 8, None, None, 0, cp.CP_F32, None) == cp.CP_OK
+    # the ring in one launch: signal buffer size, epoch range, dtype; empty is a no-op
+    sg = lib.cp_allreduce_signal
+    assert cp.cp_allreduce_signal_bytes(4) >= 8 * (2 + 4 * 256) and cp.cp_allreduce_signal_bytes(4) % 256 == 0
+    assert cp.cp_allreduce_signal_bytes(0) == 0 and cp.cp_allreduce_signal_bytes(65) == 0
+    nb = cp.cp_allreduce_signal_bytes(2)
+    assert sg(2, tab, tab, 10, cp.CP_F32, FAKE, nb, 0, 0, None) == cp.CP_ERR_ARG
+    assert sg(2, tab, tab, 10, cp.CP_F32, FAKE, nb, 1 << 55, 0, None) == cp.CP_ERR_ARG
+    assert sg(2, tab, tab, 10, cp.CP_F16, FAKE, nb, 1, 0, None) == cp.CP_ERR_UNSUPPORTED
+    assert sg(2, tab, tab, 10, cp.CP_F32, FAKE, nb - 1, 1, 0, None) == cp.CP_ERR_SHAPE
+    assert sg(2, tab, tab, 10, cp.CP_F32, None, nb, 1, 0, None) == cp.CP_ERR_ARG
+    assert sg(0, tab, tab, 10, cp.CP_F32, FAKE, nb, 1, 0, None) == cp.CP_ERR_ARG
+    assert sg(2, None, None, 0, cp.CP_F32, None, 0, 1, 0, None) == cp.CP_OK
+    assert lib.cp_allreduce_signal_status(None, 2, 1, None) == cp.CP_ERR_ARG
+    assert lib.cp_allreduce_signal_status(FAKE, 2, 0, None) == cp.CP_ERR_ARG
 
 
 def test_library_has_no_oracle_dependency():

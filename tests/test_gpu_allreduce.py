@@ -206,3 +206,99 @@ def test_graph_capture_replays(cp, algo):
         graph.replay()
         torch.cuda.synchronize()
         check(cp, algo, xs, outs)
+
+
+# ------------------------------------------------------------------ the ring in one launch
+def signal_buffer(cp, W):
+    return torch.zeros(cp.cp_allreduce_signal_bytes(W), dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("W,n", [(1, 1000), (2, 1), (2, 130), (3, 65), (4, 512), (5, 4099), (8, 256),
+                                 (8, 100003), (8, 1 << 22), (16, 1 << 16), (64, 70000)])
+def test_signal_ring_matches_oracle(cp, dtype, W, n):
+    """Same bits as the launch-per-step ring (the oracle's ring)."""
+    say(f"case allreduce one-launch ring W={W} n={n} {dtype}")
+    xs = rank_inputs(W, n, dtype, seed=W * 7 + n)
+    outs = nan_outputs(W, n, dtype)
+    sig = signal_buffer(cp, W)
+    cp.cp_allreduce_signal(xs, sig, epoch=1, outs=outs, wait_timeout_us=500000)
+    assert cp.cp_allreduce_signal_status(sig, W, 1) == cp.CP_OK
+    check(cp, "ring", xs, outs)
+
+
+@pytest.mark.parametrize("offset", [1, 3])
+def test_signal_ring_unaligned(cp, offset):
+    W, n = 4, 5000 + offset
+    say(f"case allreduce one-launch ring unaligned offset={offset}")
+    xs = rank_inputs(W, n, torch.float32, seed=offset, offset=offset)
+    outs = nan_outputs(W, n, torch.float32)
+    sig = signal_buffer(cp, W)
+    cp.cp_allreduce_signal(xs, sig, epoch=3, outs=outs, wait_timeout_us=500000)
+    assert cp.cp_allreduce_signal_status(sig, W, 3) == cp.CP_OK
+    check(cp, "ring", xs, outs)
+
+
+def test_signal_ring_repeated_calls_and_stale_epoch(cp):
+    """One signal buffer, calls with rising epochs and new inputs: each exact.  A
+    call that repeats an epoch finds its flags stale, stops, and is reported."""
+    W, n = 8, 300000
+    say("case allreduce one-launch ring repeated calls")
+    sig = signal_buffer(cp, W)
+    outs = nan_outputs(W, n, torch.float32)
+    for epoch in (1, 2, 7, 8, 1000):
+        xs = rank_inputs(W, n, torch.float32, seed=epoch)
+        cp.cp_allreduce_signal(xs, sig, epoch=epoch, outs=outs, wait_timeout_us=500000)
+        assert cp.cp_allreduce_signal_status(sig, W, epoch) == cp.CP_OK, epoch
+        check(cp, "ring", xs, outs)
+    for o in outs:
+        o.fill_(float("nan"))
+    cp.cp_allreduce_signal(xs, sig, epoch=1000, outs=outs, wait_timeout_us=500000)
+    assert cp.cp_allreduce_signal_status(sig, W, 1000) == cp.CP_ERR_ARG
+    assert all(torch.isnan(o).all() for o in outs), "a stale call wrote an output"
+    cp.cp_allreduce_signal(xs, sig, epoch=1001, outs=outs, wait_timeout_us=500000)
+    assert cp.cp_allreduce_signal_status(sig, W, 1001) == cp.CP_OK
+    check(cp, "ring", xs, outs)
+
+
+def test_signal_ring_short_wait_limit_ends(cp):
+    """A 1 us wait limit on 16 MiB per rank: the call ends (no hang) and reports
+    either success with exact results or a timeout."""
+    W, n = 8, 1 << 22
+    say("case allreduce one-launch ring 1 us wait limit")
+    xs = rank_inputs(W, n, torch.float32, seed=11)
+    outs = nan_outputs(W, n, torch.float32)
+    sig = signal_buffer(cp, W)
+    cp.cp_allreduce_signal(xs, sig, epoch=5, outs=outs, wait_timeout_us=1)
+    st = cp.cp_allreduce_signal_status(sig, W, 5)
+    say(f"status with a 1 us wait limit: {cp.cp_status_string(st)}")
+    assert st in (cp.CP_OK, cp.CP_ERR_TIMEOUT)
+    if st == cp.CP_OK:
+        check(cp, "ring", xs, outs)
+    cp.cp_allreduce_signal(xs, sig, epoch=6, outs=outs, wait_timeout_us=500000)
+    assert cp.cp_allreduce_signal_status(sig, W, 6) == cp.CP_OK
+    check(cp, "ring", xs, outs)
+
+
+def test_signal_ring_errors(cp):
+    say("case allreduce one-launch ring errors")
+    lib = cp.lib
+    W, n = 4, 1000
+    xs = rank_inputs(W, n, torch.float32, seed=5)
+    outs = nan_outputs(W, n, torch.float32)
+    sig = signal_buffer(cp, W)
+    nb = sig.numel()
+    tab = lambda ts: (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])  # noqa: E731
+    call = lambda i, o, s, sb, e, dt=cp.CP_F32: lib.cp_allreduce_signal(W, tab(i), tab(o), n, dt, s, sb, e, 0, None)  # noqa: E731
+    assert call(xs, outs, sig.data_ptr(), nb, 0) == cp.CP_ERR_ARG                    # epoch 0
+    assert call(xs, outs, sig.data_ptr(), nb, 1 << 55) == cp.CP_ERR_ARG              # epoch too large
+    assert call(xs, outs, sig.data_ptr(), nb - 1, 1) == cp.CP_ERR_SHAPE              # buffer too small
+    assert call(xs, outs, None, nb, 1) == cp.CP_ERR_ARG
+    assert call(xs, outs, sig.data_ptr(), nb, 1, cp.CP_F16) == cp.CP_ERR_UNSUPPORTED
+    assert call(xs, outs, outs[2].data_ptr(), nb, 1) in (cp.CP_ERR_ALIAS, cp.CP_ERR_SHAPE)  # signals on an output
+    assert call(xs, [xs[0]] + outs[1:], sig.data_ptr(), nb, 1) == cp.CP_ERR_ALIAS
+    torch.cuda.synchronize()
+    assert all(torch.isnan(o).all() for o in outs), "a rejected call wrote an output"
+    assert (sig == 0).all()
+    assert cp.cp_allreduce_signal_bytes(0) == 0 and cp.cp_allreduce_signal_bytes(65) == 0
+    assert lib.cp_allreduce_signal(W, None, None, 0, cp.CP_F32, None, 0, 1, 0, None) == cp.CP_OK  # empty

@@ -81,6 +81,13 @@ lib.cp_slot_sum.restype = _c.c_int
 lib.cp_slot_sum.argtypes = [_i32, _c.POINTER(_vp), _vp, _i64, _i32, _i32, _i32, _vp]
 lib.cp_allreduce.restype = _c.c_int
 lib.cp_allreduce.argtypes = [_i32, _i32, _c.POINTER(_vp), _c.POINTER(_vp), _i64, _i32, _vp]
+lib.cp_allreduce_signal_bytes.restype = _sz
+lib.cp_allreduce_signal_bytes.argtypes = [_i32]
+lib.cp_allreduce_signal.restype = _c.c_int
+lib.cp_allreduce_signal.argtypes = [_i32, _c.POINTER(_vp), _c.POINTER(_vp), _i64, _i32, _vp, _sz, _u64,
+                                    _i64, _vp]
+lib.cp_allreduce_signal_status.restype = _c.c_int
+lib.cp_allreduce_signal_status.argtypes = [_vp, _i32, _u64, _vp]
 lib.cp_attn_meta_bytes.restype = _sz
 lib.cp_attn_meta_bytes.argtypes = [_i32, _i32]
 lib.cp_build_attn_meta.restype = _c.c_int
@@ -384,6 +391,34 @@ def cp_allreduce(inputs: Sequence[torch.Tensor], outs: Optional[Sequence[torch.T
     return list(outs)
 
 
+def cp_allreduce_signal_bytes(cp_size: int) -> int:
+    return lib.cp_allreduce_signal_bytes(cp_size)
+
+
+def cp_allreduce_signal(inputs: Sequence[torch.Tensor], signals: torch.Tensor, epoch: int,
+                        outs: Optional[Sequence[torch.Tensor]] = None, wait_timeout_us: int = 0,
+                        stream=None) -> List[torch.Tensor]:
+    """The ring all-reduce in one launch, ranks signalling each hop through `signals`
+    (a zero-filled device buffer of cp_allreduce_signal_bytes(W) bytes; `epoch` must
+    exceed that of every earlier call on it)."""
+    if outs is None:
+        outs = [torch.empty_like(x) for x in inputs]
+    if len(outs) != len(inputs):
+        raise ValueError("cp_allreduce_signal: as many outputs as inputs")
+    x0 = inputs[0]
+    dt, n = x0.dtype, x0.numel()
+    st = lib.cp_allreduce_signal(len(inputs), _uniform_table(inputs, dt, n), _uniform_table(outs, dt, n), n,
+                                 dtype_code(dt), _ptr(signals), signals.numel() * signals.element_size(),
+                                 int(epoch), int(wait_timeout_us), _stream(stream, x0))
+    _check(st, "cp_allreduce_signal")
+    return list(outs)
+
+
+def cp_allreduce_signal_status(signals: torch.Tensor, cp_size: int, epoch: int, stream=None) -> int:
+    """Synchronize, then CP_OK / CP_ERR_ARG (stale epoch) / CP_ERR_TIMEOUT for the call of `epoch`."""
+    return lib.cp_allreduce_signal_status(_ptr(signals), cp_size, int(epoch), _stream(stream, signals))
+
+
 def cp_profile_enable(enable: bool = True) -> None:
     _check(lib.cp_profile_enable(1 if enable else 0), "cp_profile_enable")
 
@@ -407,5 +442,6 @@ EXPORTED = ["cp_meta_bytes", "cp_build_meta", "cp_meta_status", "cp_attn_meta_by
             "cp_partition_thd", "cp_gather_thd",
             "cp_partition_thd_multi", "cp_gather_thd_multi",
             "cp_grad_return", "cp_grad_return_fused", "cp_slot_sum", "cp_allreduce",
+            "cp_allreduce_signal_bytes", "cp_allreduce_signal", "cp_allreduce_signal_status",
             "cp_status_string", "cp_version",
             "cp_profile_enable", "cp_profile_read"]

@@ -160,6 +160,19 @@ int check_sum_dtypes(int32_t in, int32_t out) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? CP_OK : CP_ERR_HIP; }
 
+// A wait limit in device wall-clock ticks: wait_timeout_us <= 0 means 2 s;
+// limits above one hour are held at one hour (no overflow in the conversion).
+int64_t wait_ticks(int dev, int64_t wait_timeout_us) {
+  int rate_khz = 0;
+  if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || rate_khz <= 0) {
+    (void)hipGetLastError();
+    rate_khz = 100000;
+  }
+  int64_t us = wait_timeout_us > 0 ? wait_timeout_us : 2000000;
+  if (us > int64_t(3600) * 1000000) us = int64_t(3600) * 1000000;
+  return us * (int64_t)rate_khz / 1000;
+}
+
 // ---------------------------------------------------------------- timing hooks
 struct ProfileRecord {
   std::string name;
@@ -481,14 +494,7 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
   }
   // 2-3. publish this call's writer epochs, wait for this call's owners
   if (epochs && (phases & (CP_PHASE_PUBLISH | CP_PHASE_WAIT))) {
-    int rate_khz = 0;
-    if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
-        rate_khz <= 0) {
-      (void)hipGetLastError();
-      rate_khz = 100000;
-    }
-    const int64_t us = wait_timeout_us > 0 ? wait_timeout_us : 2000000;
-    const int64_t ticks = us * (int64_t)rate_khz / 1000;
+    const int64_t ticks = wait_ticks(dev, wait_timeout_us);
     if ((phases & CP_PHASE_PUBLISH) &&
         (st = hip_status(launch_epoch_publish(epochs, W, all ? -1 : rank, epoch, s))) != CP_OK)
       return st;
@@ -656,6 +662,84 @@ int cp_allreduce(int32_t algo, int32_t cp_size, const void* const* in, void* con
     if ((st = hip_status(launch_ring_reduce_step(a, step, s))) != CP_OK) return st;
   for (int step = 0; step < cp_size - 1; ++step)
     if ((st = hip_status(launch_ring_gather_step(a, step, false, s))) != CP_OK) return st;
+  return CP_OK;
+}
+
+size_t cp_allreduce_signal_bytes(int32_t cp_size) {
+  if (cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return 0;
+  const size_t bytes = 8 * (size_t)signal_words(cp_size);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int cp_allreduce_signal(int32_t cp_size, const void* const* in, void* const* out, int64_t n_elems,
+                        int32_t dtype, void* signals, size_t signals_bytes, uint64_t epoch,
+                        int64_t wait_timeout_us, cp_stream_t stream) {
+  if (is_fp8(dtype) || dtype == CP_F16) return CP_ERR_UNSUPPORTED;
+  if (dtype != CP_F32 && dtype != CP_BF16) return CP_ERR_ARG;
+  if (cp_size < 1 || cp_size > CP_MAX_CP_SIZE || n_elems < 0) return CP_ERR_ARG;
+  if (epoch == 0 || epoch >= (uint64_t(1) << 55)) return CP_ERR_ARG;
+  const int64_t bytes = checked_bytes(n_elems, dtype_bytes(dtype));
+  if (bytes < 0) return CP_ERR_ARG;
+  if (n_elems == 0) return CP_OK;
+  if (in == nullptr || out == nullptr || signals == nullptr) return CP_ERR_ARG;
+  for (int r = 0; r < cp_size; ++r)
+    if (in[r] == nullptr || out[r] == nullptr) return CP_ERR_ARG;
+  const size_t sig_bytes = cp_allreduce_signal_bytes(cp_size);
+  if (signals_bytes < sig_bytes) return CP_ERR_SHAPE;
+  int dev, st;
+  if ((st = current_device(&dev)) != CP_OK) return st;
+  AllocCache cache;
+  std::vector<Range> ins, outs;
+  for (int r = 0; r < cp_size; ++r) {
+    if ((st = check_device_buf(in[r], bytes, dev, &cache)) != CP_OK) return st;
+    if ((st = check_device_buf(out[r], bytes, dev, &cache)) != CP_OK) return st;
+    ins.push_back(range_of(in[r], bytes));
+    outs.push_back(range_of(out[r], bytes));
+  }
+  if ((st = check_device_buf(signals, (int64_t)sig_bytes, dev, &cache)) != CP_OK) return st;
+  outs.push_back(range_of(signals, (int64_t)sig_bytes));
+  if ((st = check_alias(outs, ins)) != CP_OK) return st;
+  AllreduceArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int r = 0; r < cp_size; ++r) {
+    a.in.p[r] = static_cast<const char*>(in[r]);
+    a.out.p[r] = static_cast<char*>(out[r]);
+  }
+  a.cp_size = cp_size;
+  a.n_elems = n_elems;
+  a.dtype = dtype;
+  const int64_t granule = 64 * (int64_t)cp_size;
+  a.chunk = (n_elems + granule - 1) / granule * 64;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (cp_size == 1) return hip_status(launch_ring_gather_step(a, 0, true, s));
+  RingSignalArgs g;
+  memset(&g, 0, sizeof(g));
+  const int tiles = ring_signal_tiles(a, &g.tile_elems);
+  if (tiles < 1) return CP_ERR_UNSUPPORTED;  // not even one workgroup per rank can be resident
+  g.signals = static_cast<uint64_t*>(signals);
+  g.epoch = epoch;
+  g.timeout_ticks = wait_ticks(dev, wait_timeout_us);
+  return hip_status(launch_ring_signal(a, g, tiles, s));
+}
+
+int cp_allreduce_signal_status(const void* signals, int32_t cp_size, uint64_t epoch, cp_stream_t stream) {
+  if (signals == nullptr || cp_size < 1 || cp_size > CP_MAX_CP_SIZE || epoch == 0) return CP_ERR_ARG;
+  int dev, st;
+  if ((st = current_device(&dev)) != CP_OK) return st;
+  AllocCache cache;
+  if ((st = check_device_buf(signals, (int64_t)cp_allreduce_signal_bytes(cp_size), dev, &cache)) != CP_OK)
+    return st;
+  if (hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)) != hipSuccess) {
+    (void)hipGetLastError();
+    return CP_ERR_HIP;
+  }
+  uint64_t words[2] = {0, 0};
+  if (hipMemcpy(words, signals, sizeof(words), hipMemcpyDeviceToHost) != hipSuccess) {
+    (void)hipGetLastError();
+    return CP_ERR_HIP;
+  }
+  if (words[1] >= epoch) return CP_ERR_ARG;
+  if (words[0] >= epoch) return CP_ERR_TIMEOUT;
   return CP_OK;
 }
 

@@ -132,6 +132,7 @@ struct AllreduceArgs {
   int64_t n_elems;
   int64_t chunk;      // ring chunk length in elements (a multiple of 64)
   int32_t dtype;      // CP_F32 or CP_BF16, inputs and outputs alike
+  int32_t vec;        // all pointers 16-byte aligned (set by the launch functions)
 };
 hipError_t launch_allreduce_one_shot(const AllreduceArgs& a, hipStream_t stream);
 // Reduce-scatter step `step` (0..W-2) of the ring for all ranks in one launch.
@@ -140,6 +141,24 @@ hipError_t launch_ring_reduce_step(const AllreduceArgs& a, int32_t step, hipStre
 // every rank copies its own input instead.
 hipError_t launch_ring_gather_step(const AllreduceArgs& a, int32_t step, bool from_input,
                                    hipStream_t stream);
+
+// The ring in one launch.  Workgroup (rank r, tile t) runs rank r's 2(W-1)
+// steps on tile t of each chunk and signals every finished step through a
+// device flag; before a step it waits for rank r-1's flag of the same tile.
+// signals (uint64 words): [0] largest epoch in which a wait timed out, [1]
+// largest epoch found stale (not above the flags left by an earlier call),
+// [2 + r * kSignalTiles + t] = (epoch << 8) + steps finished by (r, t).
+constexpr int kSignalTiles = 256;
+inline int64_t signal_words(int32_t W) { return 2 + (int64_t)W * kSignalTiles; }
+struct RingSignalArgs {
+  uint64_t* signals;
+  uint64_t epoch;
+  int64_t timeout_ticks;  // per wait, device wall-clock ticks
+  int64_t tile_elems;     // elements per tile, a multiple of 512
+};
+// Tiles per rank, from co-residency on the current device and the chunk length.
+int ring_signal_tiles(const AllreduceArgs& a, int64_t* tile_elems);
+hipError_t launch_ring_signal(const AllreduceArgs& a, const RingSignalArgs& g, int tiles, hipStream_t stream);
 
 // ---------------------------------------------------------------- epochs
 // Writer `writer` (or every writer when writer < 0) stores `epoch` into

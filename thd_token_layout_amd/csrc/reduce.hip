@@ -581,6 +581,148 @@ __global__ void __launch_bounds__(kBlock) ring_gather_step_kernel(AllreduceArgs 
   for (int64_t k = done + (int64_t)blockIdx.x * kBlock + threadIdx.x; k < len; k += gstride) de[k] = se[k];
 }
 
+
+// The ring in one launch (the persistent, in-kernel-signalling form of the
+// pages' design): workgroup (t, r) is rank r's share of tile t of every chunk.
+// It runs rank r's W-1 reduce-scatter and W-1 all-gather steps in order; before
+// step k > 0 one lane waits until rank r-1's workgroup of the same tile has
+// finished k steps, and after each step the workgroup publishes k+1.  Every
+// dependency of the ring is within one tile, so tiles proceed independently.
+// Data written in a step is made visible at agent scope by the flag store with
+// release after a workgroup barrier; the waiter polls with relaxed loads and
+// acquires once.  Waits are bounded by the device wall clock; a timeout, or a
+// stale epoch (a flag already at or above this call's base), is recorded in the
+// status words and every workgroup stops.  The grid is sized to at most half of
+// what can be resident at once, so every workgroup a wait depends on runs; a
+// cooperative launch would guarantee that too but costs ~20 us on this chip,
+// which is more than the whole ring of a small message.
+__device__ __forceinline__ void atomic_max_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int T>
+__global__ void __launch_bounds__(kBlock) ring_signal_kernel(AllreduceArgs a, RingSignalArgs g) {
+  const int W = a.cp_size;
+  const int r = blockIdx.y;
+  const int t = blockIdx.x;
+  const int prev = r == 0 ? W - 1 : r - 1;
+  uint64_t* const words = g.signals;
+  uint64_t* const mine = g.signals + 2 + (int64_t)r * kSignalTiles + t;
+  const uint64_t* const theirs = g.signals + 2 + (int64_t)prev * kSignalTiles + t;
+  const uint64_t base = g.epoch << 8;
+  __shared__ int s_go;
+  if (threadIdx.x == 0) {
+    const uint64_t v = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_go = v < base;
+    if (!s_go) atomic_max_u64(&words[1], g.epoch);
+  }
+  __syncthreads();
+  if (!s_go) return;
+  constexpr int64_t eb = T == CP_F32 ? 4 : 2;
+  constexpr bool SPLIT = split_layout<T, T>();
+  constexpr int64_t G = unit_group_elems<T, T>();
+  // The four buffers this workgroup touches, read once from the argument tables
+  // (indexing the tables inside the loop would copy them to scratch memory).
+  const char* const in_prev = a.in.p[prev];
+  const char* const in_mine = a.in.p[r];
+  const char* const out_prev = a.out.p[prev];
+  char* const out_mine = a.out.p[r];
+  const int64_t n = a.n_elems, chunk = a.chunk;
+  const bool vec = a.vec != 0;
+  const int steps = 2 * (W - 1);
+  for (int k = 0; k < steps; ++k) {
+    if (k > 0) {
+      if (threadIdx.x == 0) {
+        int ok = 1;
+        const int64_t start = wall_clock64();
+        while (__hip_atomic_load(theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < base + (uint64_t)k) {
+          if (__hip_atomic_load(&words[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= g.epoch ||
+              __hip_atomic_load(&words[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= g.epoch) {
+            ok = 0;  // another workgroup has stopped the call
+            break;
+          }
+          if (wall_clock64() - start > g.timeout_ticks) {
+            atomic_max_u64(&words[0], g.epoch);
+            ok = 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        // One acquire for the workgroup: the cache invalidation it implies is
+        // cache-wide, and the barrier orders every wave's loads after it.
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_go = ok;
+      }
+      __syncthreads();
+      if (!s_go) return;
+    }
+    const bool reduce = k < W - 1;
+    const int s = reduce ? k : k - (W - 1);
+    const int c = reduce ? ((r - 1 - s) % W + W) % W : ((r - s) % W + W) % W;
+    const int64_t lo = (int64_t)c * chunk < n ? (int64_t)c * chunk : n;
+    const int64_t hi = lo + chunk < n ? lo + chunk : n;
+    int64_t tlo = lo + (int64_t)t * g.tile_elems;
+    if (tlo > hi) tlo = hi;
+    int64_t thi = tlo + g.tile_elems;
+    if (thi > hi) thi = hi;
+    const int64_t len = thi - tlo;
+    char* const dst = out_mine + tlo * eb;
+    if (reduce) {
+      const char* const recv = (s == 0 ? in_prev : out_prev) + tlo * eb;
+      const char* const own = in_mine + tlo * eb;
+      const int64_t nunits = vec ? len / G * (G / 8) : 0;
+      constexpr int kU = 4;  // units in flight per thread
+      for (int64_t u0 = threadIdx.x; u0 < nunits; u0 += kBlock * kU) {
+        F8 x[kU], y[kU];
+#pragma unroll
+        for (int m = 0; m < kU; ++m) {
+          const int64_t u = u0 + (int64_t)m * kBlock;
+          if (u < nunits) {
+            load_unit<T, SPLIT>(x[m], recv, u);
+            load_unit<T, SPLIT>(y[m], own, u);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < kU; ++m) {
+          const int64_t u = u0 + (int64_t)m * kBlock;
+          if (u < nunits) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[m].v[e] = x[m].v[e] + y[m].v[e];
+            store_unit<T, SPLIT>(dst, u, x[m]);
+          }
+        }
+      }
+      for (int64_t q = nunits * 8 + threadIdx.x; q < len; q += kBlock)
+        store_elem<T>(dst, q, load_elem<T>(recv, q) + load_elem<T>(own, q));
+    } else {
+      const char* const src = out_prev + tlo * eb;
+      const int64_t n16 = vec ? len * eb / 16 : 0;
+      constexpr int kC = 8;  // 16-byte units in flight per thread
+      for (int64_t u0 = threadIdx.x; u0 < n16; u0 += kBlock * kC) {
+        u32x4 v[kC];
+#pragma unroll
+        for (int m = 0; m < kC; ++m) {
+          const int64_t u = u0 + (int64_t)m * kBlock;
+          if (u < n16) v[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + u);
+        }
+#pragma unroll
+        for (int m = 0; m < kC; ++m) {
+          const int64_t u = u0 + (int64_t)m * kBlock;
+          if (u < n16) __builtin_nontemporal_store(v[m], reinterpret_cast<u32x4*>(dst) + u);
+        }
+      }
+      typedef typename std::conditional<eb == 4, unsigned int, unsigned short>::type E;
+      for (int64_t q = n16 * 16 / eb + threadIdx.x; q < len; q += kBlock)
+        reinterpret_cast<E*>(dst)[q] = reinterpret_cast<const E*>(src)[q];
+    }
+    // The barrier completes every wave's stores into this XCD's L2; lane 0's
+    // agent-scope release then writes the L2 back before the flag is stored.
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_store(mine, base + (uint64_t)(k + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // ---- dispatch -------------------------------------------------------------------
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
@@ -797,6 +939,24 @@ hipError_t launch_ring_gather_typed(const AllreduceArgs& a, int32_t step, bool v
   return e;
 }
 
+
+template <int T>
+int ring_signal_resident_blocks() {
+  // Workgroups of this kernel that fit on the device at once.
+  static int cached = 0;
+  if (cached > 0) return cached;
+  int per_cu = 0, cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ring_signal_kernel<T>),
+                                                   kBlock, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  cached = per_cu * cus;
+  return cached;
+}
+
 }  // namespace
 
 hipError_t launch_slot_sum(const SlotSumArgs& a, hipStream_t stream) {
@@ -851,6 +1011,49 @@ hipError_t launch_ring_gather_step(const AllreduceArgs& a, int32_t step, bool fr
     return from_input ? launch_ring_gather_typed<2, true>(a, step, vec, stream)
                       : launch_ring_gather_typed<2, false>(a, step, vec, stream);
   return hipErrorInvalidValue;
+}
+
+int ring_signal_tiles(const AllreduceArgs& a, int64_t* tile_elems) {
+  const int resident = a.dtype == CP_F32 ? ring_signal_resident_blocks<CP_F32>()
+                                         : ring_signal_resident_blocks<CP_BF16>();
+  int cap = resident / 2 / a.cp_size;  // at most half of the resident capacity
+  if (cap > kSignalTiles) cap = kSignalTiles;
+  if (cap < 1) return 0;
+  const int64_t q = a.chunk < a.n_elems ? a.chunk : a.n_elems;
+  // About sqrt(q / 2048) tiles, at most 16: every agent-scope release and
+  // acquire acts on a whole L2, so more workgroups per hop cost more than they
+  // stream (W = 8 fp32, measured best: 1 tile up to 64 KiB per rank, 2 at
+  // 256 KiB, 4 at 1 MiB, 8 at 4 MiB, 16 at 16 MiB).
+  int tiles = 1;
+  while (tiles < 16 && (int64_t)(tiles + 1) * (tiles + 1) * 2048 <= q) ++tiles;
+  if (tiles > cap) tiles = cap;
+  int64_t te = (q + tiles - 1) / tiles;
+  te = (te + 511) / 512 * 512;
+  if (te < 512) te = 512;
+  *tile_elems = te;
+  return (int)((q + te - 1) / te);
+}
+
+hipError_t launch_ring_signal(const AllreduceArgs& a, const RingSignalArgs& g, int tiles, hipStream_t stream) {
+  if (a.n_elems == 0) return hipSuccess;
+  const dim3 grid((unsigned)tiles, (unsigned)a.cp_size);
+  AllreduceArgs args = a;
+  args.vec = allreduce_aligned(a) ? 1 : 0;
+  RingSignalArgs sig = g;
+  void* params[2] = {&args, &sig};
+  static const std::string names[2] = {"ring_signal<f32>", "ring_signal<bf16>"};
+  profile_before(names[a.dtype == CP_F32 ? 0 : 1].c_str(), stream);
+  hipError_t e;
+  if (a.dtype == CP_F32)
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&ring_signal_kernel<CP_F32>), grid, dim3(kBlock), params, 0,
+                        stream);
+  else
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&ring_signal_kernel<CP_BF16>), grid, dim3(kBlock), params, 0,
+                        stream);
+  if (e == hipSuccess) e = hipGetLastError();
+  else (void)hipGetLastError();
+  profile_after(stream);
+  return e;
 }
 
 hipError_t launch_epoch_publish(uint32_t* epochs, int32_t W, int32_t writer, uint32_t epoch,
