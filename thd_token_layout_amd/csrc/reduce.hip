@@ -26,6 +26,7 @@
 // contiguously and measured slower on MI355X).
 #include "device_common.h"
 
+#include <atomic>
 #include <string>
 #include <type_traits>
 
@@ -942,19 +943,27 @@ hipError_t launch_ring_gather_typed(const AllreduceArgs& a, int32_t step, bool v
 
 template <int T>
 int ring_signal_resident_blocks() {
-  // Workgroups of this kernel that fit on the device at once.
-  static int cached = 0;
-  if (cached > 0) return cached;
-  int per_cu = 0, cus = 0, dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ring_signal_kernel<T>),
+  // Workgroups of this kernel that fit on the current device at once, kept per
+  // device (the first 64 device indices; others are queried every time).
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (dev >= 0 && dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ring_signal_kernel<T>),
                                                    kBlock, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
-  cached = per_cu * cus;
-  return cached;
+  if (dev >= 0 && dev < 64) cached[dev].store(per_cu * cus, std::memory_order_relaxed);
+  return per_cu * cus;
 }
 
 }  // namespace
