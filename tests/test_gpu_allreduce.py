@@ -84,22 +84,29 @@ def test_sweep_sizes(cp, algo, size):
 
 @pytest.mark.parametrize("seed", range(48))
 def test_random_configurations(cp, seed):
-    """Seeded random rank counts, sizes, dtypes, algorithms and view offsets."""
+    """Seeded random rank counts, sizes, dtypes, algorithms (one-shot, ring, ring in one
+    launch) and view offsets."""
     rng = np.random.default_rng(5000 + seed)
     W = int(rng.choice([1, 2, 3, 4, 6, 8, 11, 16, 32]))
     n = int(rng.choice([int(rng.integers(0, 200)), int(rng.integers(200, 5000)), int(rng.integers(5000, 300000))]))
     dtype = [torch.float32, torch.bfloat16][int(rng.integers(0, 2))]
-    algo = ["one_shot", "ring"][int(rng.integers(0, 2))]
+    algo = ["one_shot", "ring", "ring_one_launch"][int(rng.integers(0, 3))]
     off_in, off_out = (int(v) for v in rng.choice([0, 0, 0, 1, 3], size=2))
     say(f"case allreduce random seed={seed}: {algo} W={W} n={n} {dtype} offsets={off_in},{off_out}")
     xs = rank_inputs(W, n, dtype, seed=seed, offset=off_in)
     outs = nan_outputs(W, n, dtype, offset=off_out)
-    cp.cp_allreduce(xs, outs, algo=algo)
+    if algo == "ring_one_launch":
+        sig = torch.zeros(cp.cp_allreduce_signal_bytes(W), dtype=torch.uint8, device=DEV)
+        cp.cp_allreduce_signal(xs, sig, epoch=seed + 1, outs=outs, wait_timeout_us=500000)
+        assert cp.cp_allreduce_signal_status(sig, W, seed + 1) == cp.CP_OK
+        algo = "ring"  # same result as the launch-per-step ring
+    else:
+        cp.cp_allreduce(xs, outs, algo=algo)
     torch.cuda.synchronize()
     check(cp, algo, xs, outs)
 
 
-@pytest.mark.parametrize("algo", ["one_shot", "ring"])
+@pytest.mark.parametrize("algo", ["one_shot", "ring", "ring_one_launch"])
 def test_special_values(cp, algo):
     """Signed zeros, infinities, NaN, overflow to inf, denormals; NaN results are
     compared as NaN (payloads of two NaNs meeting are not fixed by IEEE)."""
@@ -114,7 +121,13 @@ def test_special_values(cp, algo):
     host[3][:64] = -0.0
     xs = [torch.from_numpy(h).to(DEV) for h in host]
     outs = nan_outputs(W, n, torch.float32)
-    cp.cp_allreduce(xs, outs, algo=algo)
+    if algo == "ring_one_launch":
+        sig = torch.zeros(cp.cp_allreduce_signal_bytes(W), dtype=torch.uint8, device=DEV)
+        cp.cp_allreduce_signal(xs, sig, epoch=1, outs=outs, wait_timeout_us=500000)
+        assert cp.cp_allreduce_signal_status(sig, W, 1) == cp.CP_OK
+        algo = "ring"
+    else:
+        cp.cp_allreduce(xs, outs, algo=algo)
     torch.cuda.synchronize()
     ref = REF[algo](host, "f32")
     for r in range(W):
