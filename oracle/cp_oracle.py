@@ -55,7 +55,9 @@ Readings where the pages are silent (the design notes list them all):
     rank sums all W buffers in rank order, fp32, one rounding; ring = a
     reduce-scatter then an all-gather of W-1 steps each, passing to rank r+1,
     over W chunks of a 64-element-aligned length; ring partials travel in the
-    buffer type (a bf16 ring rounds after every add).
+    buffer type (a bf16 ring rounds after every add); the two-shot (not named by
+    the pages; the direct two-step algorithm between the two) reduces chunk c at
+    rank c in rank order, then every rank copies every reduced chunk.
 
 bf16 tensors are represented here as numpy uint16 bit patterns.
 """
@@ -534,3 +536,31 @@ def allreduce_ring(inputs, dtype):
         for r, a, b, m in msgs:
             buf[r][a:b] = m
     return buf
+
+
+def allreduce_two_shot(inputs, dtype):
+    """Two-shot all-reduce: a reduce-scatter in which rank c sums chunk c of all W
+    buffers itself (rank order, fp32, one rounding), then an all-gather in which every
+    rank copies each other rank's reduced chunk.  Chunks as in the ring.
+
+    The pages name one-shot and ring; this is the direct two-step algorithm that sits
+    between them on a fully connected topology (each byte crosses a link twice, in two
+    dependent steps), taken in its textbook form.
+    """
+    W = len(inputs)
+    n = inputs[0].shape[0]
+    chunks = ring_chunks(n, W)
+    reduced = []
+    for c in range(W):  # reduce-scatter: owner c pulls chunk c from every rank
+        a, b = chunks[c]
+        acc = _widen(inputs[0][a:b], dtype).astype(np.float32, copy=True)
+        with np.errstate(over="ignore", invalid="ignore"):
+            for w in range(1, W):
+                acc = (acc + _widen(inputs[w][a:b], dtype)).astype(np.float32)
+        reduced.append(_narrow(acc, dtype))
+    out = [np.empty_like(inputs[0]) for _ in range(W)]
+    for r in range(W):  # all-gather: rank r pulls every owner's chunk
+        for c in range(W):
+            a, b = chunks[c]
+            out[r][a:b] = reduced[c]
+    return out

@@ -530,7 +530,8 @@ def check_allreduce_integer(o):
             ints = rng.integers(-1000, 1000, size=(W, n))
             xs = [r.astype(np.float32) for r in ints]
             exact = ints.sum(axis=0).astype(np.float64)
-            for res in (o.allreduce_one_shot(xs, "f32"), o.allreduce_ring(xs, "f32")):
+            for res in (o.allreduce_one_shot(xs, "f32"), o.allreduce_ring(xs, "f32"),
+                        o.allreduce_two_shot(xs, "f32")):
                 assert len(res) == W
                 for r in range(W):
                     assert np.array_equal(res[r].astype(np.float64), exact), (W, n, r)
@@ -566,9 +567,14 @@ def check_allreduce_order_handworked(o):
     oneb = o.allreduce_one_shot(xsb, "f32")
     want_ringb = [2 ** 24 + 2] * 4
     want_oneb = [2 ** 24 + 2, 2 ** 24 + 2, 2 ** 24, 2 ** 24]
+    # the two-shot sums every chunk in rank order, like the one-shot
+    two = o.allreduce_two_shot(xs, "f32")
+    twob = o.allreduce_two_shot(xsb, "f32")
     for r in range(4):
         for k in range(4):
             sl = slice(64 * k, 64 * (k + 1))
+            assert (two[r][sl] == want_one[k]).all(), ("A two-shot", r, k)
+            assert (twob[r][sl] == want_oneb[k]).all(), ("B two-shot", r, k)
             assert (ring[r][sl] == want_ring[k]).all(), ("A ring", r, k)
             assert (one[r][sl] == want_one[k]).all(), ("A one-shot", r, k)
             assert (ringb[r][sl] == want_ringb[k]).all(), ("B ring", r, k)
@@ -586,15 +592,18 @@ def check_allreduce_bf16_rounding(o):
         xs[k][64 * k:64 * (k + 1)] = 0x4380
     ring = o.allreduce_ring(xs, "bf16")
     one = o.allreduce_one_shot(xs, "bf16")
+    two = o.allreduce_two_shot(xs, "bf16")
     for r in range(W):
         assert ring[r].dtype == np.uint16 and (ring[r] == 0x4380).all(), r
         assert one[r].dtype == np.uint16 and (one[r] == 0x4381).all(), r
+        assert two[r].dtype == np.uint16 and (two[r] == 0x4381).all(), r
 
 
 def check_allreduce_rotated_sums(o, seed=12):
     # closed form of the ring: chunk k is summed in rank order k, k+1, ..., k-1
     # (mod W), rounding to the buffer type after each add; every rank ends with
-    # the same bits.  The one-shot equals the owner slot sum of the W buffers.
+    # the same bits.  The one-shot and the two-shot equal the owner slot sum of
+    # the W buffers.
     rng = np.random.default_rng(seed)
     for W, n in ((2, 130), (3, 1000), (5, 777), (8, 4096), (4, 3)):
         xs = [rng.standard_normal(n).astype(np.float32) for _ in range(W)]
@@ -615,14 +624,32 @@ def check_allreduce_rotated_sums(o, seed=12):
                         acc = o.f32_to_bf16_rne(o.bf16_to_f32(acc) + o.bf16_to_f32(x))
                 want[a:b] = acc
             ref_one = o.slot_sum(data, dt, dt)
+            two = o.allreduce_two_shot(data, dt)
             for r in range(W):
                 assert np.array_equal(ring[r].view(np.uint8), want.view(np.uint8)), (W, n, dt, r)
                 assert np.array_equal(one[r].view(np.uint8), ref_one.view(np.uint8)), (W, n, dt, r)
+                assert np.array_equal(two[r].view(np.uint8), ref_one.view(np.uint8)), (W, n, dt, r)
+
+
+def check_two_shot_chunk_owners(o):
+    # every rank's chunk c must come from owner c's sum: give each rank's buffer a
+    # different constant per chunk and check chunk c holds sum_w (1000 w + c)
+    W, n = 5, 1000
+    ch = o.ring_chunks(n, W)
+    xs = [np.zeros(n, dtype=np.float32) for _ in range(W)]
+    for w in range(W):
+        for c, (a, b) in enumerate(ch):
+            xs[w][a:b] = 1000 * w + c
+    res = o.allreduce_two_shot(xs, "f32")
+    for r in range(W):
+        for c, (a, b) in enumerate(ch):
+            assert (res[r][a:b] == 1000 * W * (W - 1) / 2 + W * c).all(), (r, c)
 
 
 def check_allreduce_w1(o):
     x = np.random.default_rng(4).standard_normal(100).astype(np.float32)
-    for res in (o.allreduce_ring([x], "f32"), o.allreduce_one_shot([x], "f32")):
+    for res in (o.allreduce_ring([x], "f32"), o.allreduce_one_shot([x], "f32"),
+                o.allreduce_two_shot([x], "f32")):
         assert len(res) == 1 and np.array_equal(res[0], x)
 
 
@@ -654,4 +681,5 @@ ALL_CHECKS = [
     check_allreduce_bf16_rounding,
     check_allreduce_rotated_sums,
     check_allreduce_w1,
+    check_two_shot_chunk_owners,
 ]

@@ -313,6 +313,34 @@ def _ring_chunks_unaligned(o):
     return ring_chunks
 
 
+def _two_shot_wrong_owner(o):
+    def allreduce_two_shot(inputs, dtype):
+        W = len(inputs)
+        n = inputs[0].shape[0]
+        ch = o.ring_chunks(n, W)
+        out = [np.empty_like(inputs[0]) for _ in range(W)]
+        for c, (a, b) in enumerate(ch):
+            src = ch[(c + 1) % W]  # owner c reduces the next chunk's rows
+            m = min(b - a, src[1] - src[0])
+            red = o.slot_sum([x[src[0]:src[0] + m] for x in inputs], dtype, dtype)
+            for r in range(W):
+                out[r][a:b] = 0
+                out[r][a:a + m] = red
+        return out
+    return allreduce_two_shot
+
+
+def _two_shot_no_gather(o):
+    def allreduce_two_shot(inputs, dtype):
+        W = len(inputs)
+        ch = o.ring_chunks(inputs[0].shape[0], W)
+        out = [x.copy() for x in inputs]
+        for c, (a, b) in enumerate(ch):
+            out[c][a:b] = o.slot_sum([x[a:b] for x in inputs], dtype, dtype)  # owners only
+        return out
+    return allreduce_two_shot
+
+
 def _one_shot_reversed(o):
     def allreduce_one_shot(inputs, dtype):
         res = o.slot_sum(inputs[::-1], dtype, dtype)
@@ -350,6 +378,8 @@ MUTATIONS = {
     "ring_in_rank_order": ("allreduce_ring", _ring_rank_order),
     "ring_chunks_unaligned": ("ring_chunks", _ring_chunks_unaligned),
     "one_shot_reversed": ("allreduce_one_shot", _one_shot_reversed),
+    "two_shot_wrong_owner": ("allreduce_two_shot", _two_shot_wrong_owner),
+    "two_shot_no_gather": ("allreduce_two_shot", _two_shot_no_gather),
 }
 
 INVARIANT_CASES = [
