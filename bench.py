@@ -417,11 +417,11 @@ def sweep_latency(step: Step, cp, torch, reps: int = 1000):
 def allreduce_sweep(sweep, cp, torch):
     """All-reduce of W=8 fp32 rank buffers of 1 KiB ... 16 MiB, every rank emulated on this
     GPU: one-shot (one launch, each rank reads all 8 buffers) against ring (14 launches:
-    7 reduce-scatter and 7 all-gather steps) and the same ring in one launch with
-    in-kernel signals.  Per call: eager latency (through the binding and through the
+    7 reduce-scatter and 7 all-gather steps), two-shot (2 launches) and the ring in one
+    launch with in-kernel signals.  Per call: eager latency (through the binding and through the
     C ABI), summed kernel time, and (launch-per-step forms) time replayed from a HIP graph;
-    algorithmic bytes over all 8 ranks (one-shot 72 x size, ring 35 x size) over the
-    kernel time."""
+    algorithmic bytes over all 8 ranks (one-shot 72 x size, ring 35 x size, two-shot
+    23 x size) over the kernel time."""
     import ctypes
 
     W = 8
@@ -429,7 +429,7 @@ def allreduce_sweep(sweep, cp, torch):
     for nbytes, slots, _ in sweep:
         outs = [torch.empty_like(slots[0]) for _ in range(W)]
         row = {"bytes_per_rank": nbytes}
-        for algo, factor in (("one_shot", W * (W + 1)), ("ring", 5 * (W - 1))):
+        for algo, factor in (("one_shot", W * (W + 1)), ("ring", 5 * (W - 1)), ("two_shot", 3 * W - 1)):
             def call(algo=algo):
                 cp.cp_allreduce(slots, outs, algo=algo)
             raw = c_abi_call(cp, torch, "cp_allreduce", cp.ALLREDUCE_ALGOS[algo], W,
@@ -471,8 +471,11 @@ def allreduce_sweep(sweep, cp, torch):
         del outs, sig
     faster = [r["bytes_per_rank"] for r in res
               if r["ring"]["graph_us_per_call"] < r["one_shot"]["graph_us_per_call"]]
+    best = {r["bytes_per_rank"]: min(("one_shot", "ring", "two_shot"), key=lambda k: r[k]["graph_us_per_call"])
+            for r in res}
     return {"cp_size": W, "dtype": "f32", "sizes": res,
-            "ring_faster_from_bytes": min(faster) if faster else None}
+            "ring_faster_from_bytes": min(faster) if faster else None,
+            "fastest_graph_replayed": best}
 
 
 def main():

@@ -425,12 +425,13 @@ int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t 
 /* ------------------------------------------------------------ all-reduce */
 #define CP_ALLREDUCE_ONE_SHOT 0
 #define CP_ALLREDUCE_RING     1
+#define CP_ALLREDUCE_TWO_SHOT 2
 
 /*
  * cp_allreduce - all W ranks, emulated by W buffers on this device, end with
  * the sum of all W inputs: out[r][k] = in[0][k] + ... + in[W-1][k] for every
- * rank r.  The two algorithms of [LL] (the all-reduce menu by message size;
- * exercises 2-3, one-shot against ring over 1 KB - 16 MB):
+ * rank r.  The algorithms of [LL] (the all-reduce menu by message size;
+ * exercises 2-3, one-shot against ring over 1 KB - 16 MB), and a two-shot:
  *   CP_ALLREDUCE_ONE_SHOT  one launch: every rank reads all W inputs and sums
  *       them in rank order 0..W-1 in fp32 (seeded with in[0]), rounding once
  *       to dtype.  Every rank's out holds the same bits as cp_slot_sum.
@@ -444,7 +445,13 @@ int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t 
  *       every add.  All-gather: W-1 steps; in step s rank r copies chunk
  *       (r-s) mod W from out[r-1].  2(W-1) launches, stream-ordered; W = 1 is
  *       one copy.  out[r] is the rank's working buffer throughout.
- *   algo         CP_ALLREDUCE_ONE_SHOT or CP_ALLREDUCE_RING (else CP_ERR_ARG)
+ *   CP_ALLREDUCE_TWO_SHOT  not named by [LL]: the direct two-step algorithm
+ *       between the two (on an all-to-all fabric every byte crosses a link
+ *       twice, in two dependent steps).  Same chunks as the ring; one launch in
+ *       which rank r sums chunk r of all W inputs in rank order (fp32, one
+ *       rounding) into out[r], then one launch in which every rank copies each
+ *       other rank's reduced chunk.  Same bits as the one-shot.
+ *   algo         a CP_ALLREDUCE_* value (else CP_ERR_ARG)
  *   cp_size      W in [1, 64]
  *   in, out      host tables [W] of device buffers of n_elems `dtype` each;
  *                outputs must not overlap any input or each other

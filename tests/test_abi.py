@@ -175,9 +175,9 @@ def test_host_checks_before_any_hip_call(cp):
     assert ss(2, tab, FAKE, 10, cp.CP_F32, cp.CP_F32, 0x20, None) == cp.CP_ERR_ARG
     # all-reduce: algorithm, dtype, rank count, NULLs, sizes; empty is a no-op
     ar = lib.cp_allreduce
-    assert ar(2, 2, tab, tab, 10, cp.CP_F32, None) == cp.CP_ERR_ARG
+    assert ar(3, 2, tab, tab, 10, cp.CP_F32, None) == cp.CP_ERR_ARG
     assert ar(-1, 2, tab, tab, 10, cp.CP_F32, None) == cp.CP_ERR_ARG
-    for algo in (cp.CP_ALLREDUCE_ONE_SHOT, cp.CP_ALLREDUCE_RING):
+    for algo in (cp.CP_ALLREDUCE_ONE_SHOT, cp.CP_ALLREDUCE_RING, cp.CP_ALLREDUCE_TWO_SHOT):
         assert ar(algo, 2, tab, tab, 10, cp.CP_F16, None) == cp.CP_ERR_UNSUPPORTED
         assert ar(algo, 2, tab, tab, 10, cp.CP_FP8_E5M2, None) == cp.CP_ERR_UNSUPPORTED
         assert ar(algo, 2, tab, tab, 10, 42, None) == cp.CP_ERR_ARG

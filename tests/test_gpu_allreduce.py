@@ -1,8 +1,9 @@
-"""GPU parity of the all-reduce of W rank buffers (one-shot and ring), through the
-C ABI, bit-exact against the CPU oracle: every rank's output, for every rank
-count, size (empty and short chunks, ragged tails, unaligned views), dtype and
-the W = 8, 1 KiB - 16 MiB sizes of the latency sweep; special values; errors
-the host rejects; and both algorithms captured in a HIP graph and replayed."""
+"""GPU parity of the all-reduce of W rank buffers (one-shot, ring, two-shot and the
+ring in one launch), through the C ABI, bit-exact against the CPU oracle: every
+rank's output, for every rank count, size (empty and short chunks, ragged tails,
+unaligned views), dtype and the W = 8, 1 KiB - 16 MiB sizes of the latency sweep;
+special values; errors the host rejects; the launch-per-step algorithms captured
+in a HIP graph and replayed."""
 import ctypes
 
 import numpy as np
@@ -14,7 +15,7 @@ from gpu_util import DEV, O, bits_equal, say, to_np
 pytestmark = pytest.mark.gpu
 
 TAG = {torch.float32: "f32", torch.bfloat16: "bf16"}
-REF = {"one_shot": O.allreduce_one_shot, "ring": O.allreduce_ring}
+REF = {"one_shot": O.allreduce_one_shot, "ring": O.allreduce_ring, "two_shot": O.allreduce_two_shot}
 
 
 @pytest.fixture(scope="module")
@@ -41,7 +42,7 @@ def check(cp, algo, xs, outs):
         assert bits_equal(to_np(o), ref[r]), (algo, r)
 
 
-@pytest.mark.parametrize("algo", ["one_shot", "ring"])
+@pytest.mark.parametrize("algo", ["one_shot", "ring", "two_shot"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("W,n", [(1, 1000), (2, 1), (2, 130), (3, 64), (3, 65), (4, 511), (4, 512),
                                  (5, 4099), (8, 256), (8, 300), (8, 4096), (8, 100003), (16, 1 << 16),
@@ -55,7 +56,7 @@ def test_allreduce_matches_oracle(cp, algo, dtype, W, n):
     check(cp, algo, xs, outs)
 
 
-@pytest.mark.parametrize("algo", ["one_shot", "ring"])
+@pytest.mark.parametrize("algo", ["one_shot", "ring", "two_shot"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("offset", [1, 2, 3])
 def test_unaligned_views(cp, algo, dtype, offset):
@@ -69,7 +70,7 @@ def test_unaligned_views(cp, algo, dtype, offset):
     check(cp, algo, xs, outs)
 
 
-@pytest.mark.parametrize("algo", ["one_shot", "ring"])
+@pytest.mark.parametrize("algo", ["one_shot", "ring", "two_shot"])
 @pytest.mark.parametrize("size", [1024 << k for k in range(15)])
 def test_sweep_sizes(cp, algo, size):
     """W = 8 fp32 buffers of 1 KiB ... 16 MiB, as timed by the benchmark."""
@@ -90,7 +91,7 @@ def test_random_configurations(cp, seed):
     W = int(rng.choice([1, 2, 3, 4, 6, 8, 11, 16, 32]))
     n = int(rng.choice([int(rng.integers(0, 200)), int(rng.integers(200, 5000)), int(rng.integers(5000, 300000))]))
     dtype = [torch.float32, torch.bfloat16][int(rng.integers(0, 2))]
-    algo = ["one_shot", "ring", "ring_one_launch"][int(rng.integers(0, 3))]
+    algo = ["one_shot", "ring", "two_shot", "ring_one_launch"][int(rng.integers(0, 4))]
     off_in, off_out = (int(v) for v in rng.choice([0, 0, 0, 1, 3], size=2))
     say(f"case allreduce random seed={seed}: {algo} W={W} n={n} {dtype} offsets={off_in},{off_out}")
     xs = rank_inputs(W, n, dtype, seed=seed, offset=off_in)
@@ -106,7 +107,7 @@ def test_random_configurations(cp, seed):
     check(cp, algo, xs, outs)
 
 
-@pytest.mark.parametrize("algo", ["one_shot", "ring", "ring_one_launch"])
+@pytest.mark.parametrize("algo", ["one_shot", "ring", "two_shot", "ring_one_launch"])
 def test_special_values(cp, algo):
     """Signed zeros, infinities, NaN, overflow to inf, denormals; NaN results are
     compared as NaN (payloads of two NaNs meeting are not fixed by IEEE)."""
@@ -143,7 +144,7 @@ def test_shared_input_buffer(cp):
     say("case allreduce shared input")
     x = rank_inputs(1, 5000, torch.float32, seed=3)[0]
     xs = [x, x, x]
-    for algo in ("one_shot", "ring"):
+    for algo in ("one_shot", "ring", "two_shot"):
         outs = nan_outputs(3, 5000, torch.float32)
         cp.cp_allreduce(xs, outs, algo=algo)
         torch.cuda.synchronize()
@@ -155,7 +156,7 @@ def test_repeated_calls_overwrite(cp):
     say("case allreduce repeated calls")
     W = 8
     outs = nan_outputs(W, 10000, torch.float32)
-    for algo in ("one_shot", "ring"):
+    for algo in ("one_shot", "ring", "two_shot"):
         for n, seed in ((10000, 1), (6001, 2)):
             xs = rank_inputs(W, n, torch.float32, seed=seed)
             view = [o[:n] for o in outs]
@@ -171,7 +172,7 @@ def test_errors_rejected_before_launch(cp):
     xs = rank_inputs(W, n, torch.float32, seed=5)
     outs = nan_outputs(W, n, torch.float32)
     tab = lambda ts: (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])  # noqa: E731
-    for algo in (cp.CP_ALLREDUCE_ONE_SHOT, cp.CP_ALLREDUCE_RING):
+    for algo in (cp.CP_ALLREDUCE_ONE_SHOT, cp.CP_ALLREDUCE_RING, cp.CP_ALLREDUCE_TWO_SHOT):
         # an output that is an input, or two outputs that overlap
         assert lib.cp_allreduce(algo, W, tab(xs), tab([xs[1]] + outs[1:]), n, cp.CP_F32, None) == cp.CP_ERR_ALIAS
         assert lib.cp_allreduce(algo, W, tab(xs), tab([outs[0], outs[0][10:]] + outs[2:]), n - 10,
@@ -188,7 +189,7 @@ def test_errors_rejected_before_launch(cp):
         cp.cp_allreduce(xs, outs[:3])
 
 
-@pytest.mark.parametrize("algo", ["one_shot", "ring"])
+@pytest.mark.parametrize("algo", ["one_shot", "ring", "two_shot"])
 def test_graph_capture_replays(cp, algo):
     """Both algorithms record only kernel launches: captured once, replayed with
     new inputs written eagerly between replays, every replay is exact."""

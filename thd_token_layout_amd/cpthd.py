@@ -46,7 +46,7 @@ CP_CALL_POLICY_MISMATCH = 0x0800
 CP_CALL_USED_INVALID_META = 0x1000
 CP_CALL_DOCS_MISMATCH = 0x2000
 CP_ATTN_MAGIC = 0x54414350
-CP_ALLREDUCE_ONE_SHOT, CP_ALLREDUCE_RING = 0, 1
+CP_ALLREDUCE_ONE_SHOT, CP_ALLREDUCE_RING, CP_ALLREDUCE_TWO_SHOT = 0, 1, 2
 
 POLICY = {"dual_chunk_swap": CP_POLICY_DUAL_CHUNK_SWAP,
           "packed_contiguous": CP_POLICY_PACKED_CONTIGUOUS}
@@ -363,7 +363,8 @@ def cp_slot_sum(slots: Sequence[torch.Tensor], out: torch.Tensor, accumulate: bo
     return out
 
 
-ALLREDUCE_ALGOS = {"one_shot": CP_ALLREDUCE_ONE_SHOT, "ring": CP_ALLREDUCE_RING}
+ALLREDUCE_ALGOS = {"one_shot": CP_ALLREDUCE_ONE_SHOT, "ring": CP_ALLREDUCE_RING,
+                   "two_shot": CP_ALLREDUCE_TWO_SHOT}
 
 
 def _uniform_table(ts, dtype, n: int) -> "ctypes.Array":

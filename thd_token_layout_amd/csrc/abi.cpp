@@ -623,7 +623,8 @@ int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t 
 
 int cp_allreduce(int32_t algo, int32_t cp_size, const void* const* in, void* const* out,
                  int64_t n_elems, int32_t dtype, cp_stream_t stream) {
-  if (algo != CP_ALLREDUCE_ONE_SHOT && algo != CP_ALLREDUCE_RING) return CP_ERR_ARG;
+  if (algo != CP_ALLREDUCE_ONE_SHOT && algo != CP_ALLREDUCE_RING && algo != CP_ALLREDUCE_TWO_SHOT)
+    return CP_ERR_ARG;
   if (is_fp8(dtype) || dtype == CP_F16) return CP_ERR_UNSUPPORTED;
   if (dtype != CP_F32 && dtype != CP_BF16) return CP_ERR_ARG;
   if (cp_size < 1 || cp_size > CP_MAX_CP_SIZE || n_elems < 0) return CP_ERR_ARG;
@@ -657,6 +658,7 @@ int cp_allreduce(int32_t algo, int32_t cp_size, const void* const* in, void* con
   a.chunk = (n_elems + granule - 1) / granule * 64;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (algo == CP_ALLREDUCE_ONE_SHOT) return hip_status(launch_allreduce_one_shot(a, s));
+  if (algo == CP_ALLREDUCE_TWO_SHOT) return hip_status(launch_allreduce_two_shot(a, s));
   if (cp_size == 1) return hip_status(launch_ring_gather_step(a, 0, true, s));
   for (int step = 0; step < cp_size - 1; ++step)
     if ((st = hip_status(launch_ring_reduce_step(a, step, s))) != CP_OK) return st;

@@ -21,16 +21,26 @@ namespace {
 // rank, as W devices would each do their own share).
 
 // One-shot: rank r's workgroups sum all W inputs in rank order (seeded with
-// input 0, one fp32 add per further input) and write out[r].
-template <int T, int WB, bool VEC, int UPT>
+// input 0, one fp32 add per further input) and write out[r].  CHUNKED (the
+// two-shot's reduce-scatter): rank r sums and writes only chunk r.
+template <int T, int WB, bool VEC, int UPT, bool CHUNKED>
 __global__ void __launch_bounds__(kBlock) allreduce_one_shot_kernel(AllreduceArgs a) {
   const int W = a.cp_size;
-  char* const out = a.out.p[blockIdx.y];
+  const int r = blockIdx.y;
+  constexpr int64_t eb = T == CP_F32 ? 4 : 2;
+  int64_t lo = 0, len = a.n_elems;
+  if constexpr (CHUNKED) {
+    lo = (int64_t)r * a.chunk < a.n_elems ? (int64_t)r * a.chunk : a.n_elems;
+    const int64_t hi = lo + a.chunk < a.n_elems ? lo + a.chunk : a.n_elems;
+    len = hi - lo;
+  }
+  const int64_t off0 = lo * eb;
+  char* const out = a.out.p[r] + off0;
   constexpr bool SPLIT = split_layout<T, T>();
   int64_t done = 0;
   if constexpr (VEC) {
     constexpr int64_t G = unit_group_elems<T, T>();
-    const int64_t nunits = a.n_elems / G * (G / 8);
+    const int64_t nunits = len / G * (G / 8);
     const int64_t ntiles = (nunits + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
       int64_t unit[UPT], off[UPT];
@@ -39,7 +49,7 @@ __global__ void __launch_bounds__(kBlock) allreduce_one_shot_kernel(AllreduceArg
       for (int u = 0; u < UPT; ++u) {
         unit[u] = tile * kBlock * UPT + (int64_t)u * kBlock + threadIdx.x;
         ok[u] = unit[u] < nunits;
-        off[u] = 0;
+        off[u] = off0;
       }
       F8 acc[UPT];
       sum_units<T, SPLIT, WB, UPT, false>(acc, a.in, W, off, unit, ok);
@@ -50,9 +60,9 @@ __global__ void __launch_bounds__(kBlock) allreduce_one_shot_kernel(AllreduceArg
     done = nunits * 8;
   }
   const int64_t gstride = (int64_t)gridDim.x * kBlock;
-  for (int64_t k = done + (int64_t)blockIdx.x * kBlock + threadIdx.x; k < a.n_elems; k += gstride) {
-    float acc = load_elem<T>(a.in.p[0], k);
-    for (int w = 1; w < W; ++w) acc = acc + load_elem<T>(a.in.p[w], k);
+  for (int64_t k = done + (int64_t)blockIdx.x * kBlock + threadIdx.x; k < len; k += gstride) {
+    float acc = load_elem<T>(a.in.p[0] + off0, k);
+    for (int w = 1; w < W; ++w) acc = acc + load_elem<T>(a.in.p[w] + off0, k);
     store_elem<T>(out, k, acc);
   }
 }
@@ -115,22 +125,14 @@ __global__ void __launch_bounds__(kBlock) ring_reduce_step_kernel(AllreduceArgs 
     store_elem<T>(dst, k, load_elem<T>(recv, k) + load_elem<T>(own, k));
 }
 
-// Ring all-gather step: rank r copies chunk c = (r-step) mod W from rank
-// r-1's working buffer, bit for bit.  FROM_IN (one rank): copy the input.
-template <int EB, bool VEC, bool FROM_IN>
-__global__ void __launch_bounds__(kBlock) ring_gather_step_kernel(AllreduceArgs a, int32_t step) {
-  const int W = a.cp_size;
-  const int r = blockIdx.y;
-  const int prev = r == 0 ? W - 1 : r - 1;
-  const int c = ((r - step) % W + W) % W;
-  int64_t lo, hi;
-  ring_chunk(a, c, lo, hi);
-  const char* const src = (FROM_IN ? a.in.p[r] : a.out.p[prev]) + lo * EB;
-  char* const dst = a.out.p[r] + lo * EB;
-  const int64_t len = hi - lo;
+// Copy len elements of EB bytes from src to dst, bit for bit: 16-byte units
+// (4 per thread and tile) when VEC, then the tail element by element; tiles
+// over blockIdx.x.
+template <int EB, bool VEC>
+__device__ __forceinline__ void copy_span(const char* src, char* dst, int64_t len) {
   int64_t done = 0;
   if constexpr (VEC) {
-    constexpr int kUpt = 4;  // 16-byte units per thread and tile
+    constexpr int kUpt = 4;
     const int64_t n16 = len * EB / 16;
     const int64_t ntiles = (n16 + (int64_t)kBlock * kUpt - 1) / ((int64_t)kBlock * kUpt);
     const u32x4* s16 = reinterpret_cast<const u32x4*>(src);
@@ -156,6 +158,30 @@ __global__ void __launch_bounds__(kBlock) ring_gather_step_kernel(AllreduceArgs 
   for (int64_t k = done + (int64_t)blockIdx.x * kBlock + threadIdx.x; k < len; k += gstride) de[k] = se[k];
 }
 
+// Ring all-gather step: rank r copies chunk c = (r-step) mod W from rank
+// r-1's working buffer, bit for bit.  FROM_IN (one rank): copy the input.
+template <int EB, bool VEC, bool FROM_IN>
+__global__ void __launch_bounds__(kBlock) ring_gather_step_kernel(AllreduceArgs a, int32_t step) {
+  const int W = a.cp_size;
+  const int r = blockIdx.y;
+  const int prev = r == 0 ? W - 1 : r - 1;
+  const int c = ((r - step) % W + W) % W;
+  int64_t lo, hi;
+  ring_chunk(a, c, lo, hi);
+  copy_span<EB, VEC>((FROM_IN ? a.in.p[r] : a.out.p[prev]) + lo * EB, a.out.p[r] + lo * EB, hi - lo);
+}
+
+// Two-shot all-gather: rank r (blockIdx.y) copies chunk c = (r+1+z) mod W
+// (z = blockIdx.z < W-1) from its owner's output, bit for bit.
+template <int EB, bool VEC>
+__global__ void __launch_bounds__(kBlock) two_shot_gather_kernel(AllreduceArgs a) {
+  const int W = a.cp_size;
+  const int r = blockIdx.y;
+  const int c = (r + 1 + (int)blockIdx.z) % W;
+  int64_t lo, hi;
+  ring_chunk(a, c, lo, hi);
+  copy_span<EB, VEC>(a.out.p[c] + lo * EB, a.out.p[r] + lo * EB, hi - lo);
+}
 
 // The ring in one launch (the persistent, in-kernel-signalling form of the
 // pages' design): workgroup (t, r) is rank r's share of tile t of every chunk.
@@ -299,40 +325,60 @@ __global__ void __launch_bounds__(kBlock) ring_signal_kernel(AllreduceArgs a, Ri
 }
 
 // ---- all-reduce launches --------------------------------------------------------
-template <int T, int WB>
+template <int T, int WB, bool CHUNKED>
 hipError_t launch_one_shot_wb(const AllreduceArgs& a, bool vec, hipStream_t stream) {
   constexpr int UPT = sum_upt(WB);
-  static const std::string names[2] = {
-      std::string("allreduce_one_shot<") + dtype_tag(T) + "," + std::to_string(WB) + ",s>",
-      std::string("allreduce_one_shot<") + dtype_tag(T) + "," + std::to_string(WB) + ",v" +
-          std::to_string(UPT) + ">"};
+  const std::string tag = std::string(CHUNKED ? "two_shot_reduce<" : "allreduce_one_shot<") + dtype_tag(T) +
+                          "," + std::to_string(WB) + ",";
+  static const std::string names[2] = {tag + "s>", tag + "v" + std::to_string(UPT) + ">"};
+  const int64_t len = CHUNKED ? (a.chunk < a.n_elems ? a.chunk : a.n_elems) : a.n_elems;  // longest range
   int64_t blocks;
   if (vec) {
     constexpr int64_t G = unit_group_elems<T, T>();
-    blocks = (a.n_elems / G * (G / 8) + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
+    blocks = (len / G * (G / 8) + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
   } else {
-    blocks = (a.n_elems + kBlock - 1) / kBlock;
+    blocks = (len + kBlock - 1) / kBlock;
   }
   if (blocks > kMaxGrid) blocks = kMaxGrid;
   if (blocks < 1) blocks = 1;
   const dim3 grid((unsigned)blocks, (unsigned)a.cp_size);
   profile_before(names[vec ? 1 : 0].c_str(), stream);
   if (vec)
-    hipLaunchKernelGGL((allreduce_one_shot_kernel<T, WB, true, UPT>), grid, dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((allreduce_one_shot_kernel<T, WB, true, UPT, CHUNKED>), grid, dim3(kBlock), 0, stream, a);
   else
-    hipLaunchKernelGGL((allreduce_one_shot_kernel<T, WB, false, 1>), grid, dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((allreduce_one_shot_kernel<T, WB, false, 1, CHUNKED>), grid, dim3(kBlock), 0, stream, a);
   hipError_t e = hipGetLastError();
   profile_after(stream);
   return e;
 }
 
-template <int T>
+template <int T, bool CHUNKED>
 hipError_t launch_one_shot_typed(const AllreduceArgs& a, bool vec, hipStream_t stream) {
   const int W = a.cp_size;
-  if (W <= 1) return launch_one_shot_wb<T, 1>(a, vec, stream);
-  if (W <= 2) return launch_one_shot_wb<T, 2>(a, vec, stream);
-  if (W <= 4) return launch_one_shot_wb<T, 4>(a, vec, stream);
-  return launch_one_shot_wb<T, 8>(a, vec, stream);
+  if (W <= 1) return launch_one_shot_wb<T, 1, CHUNKED>(a, vec, stream);
+  if (W <= 2) return launch_one_shot_wb<T, 2, CHUNKED>(a, vec, stream);
+  if (W <= 4) return launch_one_shot_wb<T, 4, CHUNKED>(a, vec, stream);
+  return launch_one_shot_wb<T, 8, CHUNKED>(a, vec, stream);
+}
+
+template <int EB>
+hipError_t launch_two_shot_gather_typed(const AllreduceArgs& a, bool vec, hipStream_t stream) {
+  static const std::string names[2] = {std::string("two_shot_gather<") + std::to_string(EB) + "B,s>",
+                                       std::string("two_shot_gather<") + std::to_string(EB) + "B,v>"};
+  const int64_t len = a.chunk < a.n_elems ? a.chunk : a.n_elems;
+  int64_t blocks = vec ? (len * EB / 16 + (int64_t)kBlock * 4 - 1) / ((int64_t)kBlock * 4)
+                       : (len + kBlock - 1) / kBlock;
+  if (blocks > kMaxGrid) blocks = kMaxGrid;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks, (unsigned)a.cp_size, (unsigned)(a.cp_size - 1));
+  profile_before(names[vec ? 1 : 0].c_str(), stream);
+  if (vec)
+    hipLaunchKernelGGL((two_shot_gather_kernel<EB, true>), grid, dim3(kBlock), 0, stream, a);
+  else
+    hipLaunchKernelGGL((two_shot_gather_kernel<EB, false>), grid, dim3(kBlock), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  profile_after(stream);
+  return e;
 }
 
 bool allreduce_aligned(const AllreduceArgs& a) {
@@ -419,9 +465,21 @@ int ring_signal_resident_blocks() {
 hipError_t launch_allreduce_one_shot(const AllreduceArgs& a, hipStream_t stream) {
   if (a.n_elems == 0) return hipSuccess;
   const bool vec = allreduce_aligned(a);
-  if (a.dtype == CP_F32) return launch_one_shot_typed<CP_F32>(a, vec, stream);
-  if (a.dtype == CP_BF16) return launch_one_shot_typed<CP_BF16>(a, vec, stream);
+  if (a.dtype == CP_F32) return launch_one_shot_typed<CP_F32, false>(a, vec, stream);
+  if (a.dtype == CP_BF16) return launch_one_shot_typed<CP_BF16, false>(a, vec, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_allreduce_two_shot(const AllreduceArgs& a, hipStream_t stream) {
+  if (a.n_elems == 0) return hipSuccess;
+  const bool vec = allreduce_aligned(a);
+  hipError_t e;
+  if (a.dtype == CP_F32) e = launch_one_shot_typed<CP_F32, true>(a, vec, stream);
+  else if (a.dtype == CP_BF16) e = launch_one_shot_typed<CP_BF16, true>(a, vec, stream);
+  else return hipErrorInvalidValue;
+  if (e != hipSuccess || a.cp_size == 1) return e;
+  return a.dtype == CP_F32 ? launch_two_shot_gather_typed<4>(a, vec, stream)
+                           : launch_two_shot_gather_typed<2>(a, vec, stream);
 }
 
 hipError_t launch_ring_reduce_step(const AllreduceArgs& a, int32_t step, hipStream_t stream) {

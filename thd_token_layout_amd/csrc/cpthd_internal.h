@@ -135,6 +135,9 @@ struct AllreduceArgs {
   int32_t vec;        // all pointers 16-byte aligned (set by the launch functions)
 };
 hipError_t launch_allreduce_one_shot(const AllreduceArgs& a, hipStream_t stream);
+// Two-shot: rank r sums chunk r of all inputs in rank order into out[r]
+// (one launch), then every rank copies the other ranks' chunks (one launch).
+hipError_t launch_allreduce_two_shot(const AllreduceArgs& a, hipStream_t stream);
 // Reduce-scatter step `step` (0..W-2) of the ring for all ranks in one launch.
 hipError_t launch_ring_reduce_step(const AllreduceArgs& a, int32_t step, hipStream_t stream);
 // All-gather step `step` (0..W-2) for all ranks; with from_input (W = 1 only)
