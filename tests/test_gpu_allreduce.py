@@ -316,3 +316,37 @@ def test_signal_ring_errors(cp):
     assert (sig == 0).all()
     assert cp.cp_allreduce_signal_bytes(0) == 0 and cp.cp_allreduce_signal_bytes(65) == 0
     assert lib.cp_allreduce_signal(W, None, None, 0, cp.CP_F32, None, 0, 1, 0, None) == cp.CP_OK  # empty
+
+
+@pytest.mark.parametrize("algo", ["one_shot", "ring", "two_shot", "ring_one_launch"])
+def test_largest_sizes(cp, algo):
+    """W = 2 fp32 buffers of 2^31 + 160 elements (8 GiB each): every offset past
+    2^31 elements.  With two ranks every algorithm computes x0 + x1 (one fp32 add,
+    commutative), checked on sampled elements, chunk edges and the last element."""
+    W, n = 2, (1 << 31) + 160
+    say(f"case allreduce largest size {algo} n={n}")
+    torch.cuda.empty_cache()
+    xs = [torch.empty(n, device=DEV) for _ in range(W)]
+    gen = torch.Generator(device=DEV).manual_seed(31)
+    for x in xs:
+        x.normal_(generator=gen)
+    outs = [torch.empty(n, device=DEV) for _ in range(W)]
+    if algo == "ring_one_launch":
+        sig = torch.zeros(cp.cp_allreduce_signal_bytes(W), dtype=torch.uint8, device=DEV)
+        cp.cp_allreduce_signal(xs, sig, epoch=1, outs=outs, wait_timeout_us=2000000)
+        assert cp.cp_allreduce_signal_status(sig, W, 1) == cp.CP_OK
+    else:
+        cp.cp_allreduce(xs, outs, algo=algo)
+    torch.cuda.synchronize()
+    q = O.ring_chunks(n, W)[1][0]
+    rng = np.random.default_rng(7)
+    idx = np.unique(np.concatenate([rng.integers(0, n, size=2000), [0, q - 1, q, q + 1, n - 2, n - 1],
+                                    (1 << 31) + np.arange(-3, 4)]))
+    idx_t = torch.from_numpy(idx).to(DEV)
+    a, b = (x[idx_t].cpu().numpy() for x in xs)
+    want = (a + b).astype(np.float32)
+    for r in range(W):
+        got = outs[r][idx_t].cpu().numpy()
+        assert bits_equal(got, want), r
+    del xs, outs
+    torch.cuda.empty_cache()
