@@ -166,7 +166,8 @@ typedef struct cp_meta_header {
 } cp_meta_header;
 
 /* Bytes the caller must allocate for the metadata of B documents and W ranks
- * (a multiple of 256).  Returns 0 for B < 0 or W outside [1, CP_MAX_CP_SIZE]. */
+ * (a multiple of 256).  Returns 0 for B outside [0, 2^31 - 2] or W outside
+ * [1, CP_MAX_CP_SIZE]. */
 size_t cp_meta_bytes(int32_t num_docs, int32_t cp_size);
 
 /*
@@ -178,7 +179,7 @@ size_t cp_meta_bytes(int32_t num_docs, int32_t cp_size);
  * o receives chunks o and 2N-1-o, sized from cp_size).
  *
  *   cu_seqlens    device int32[num_docs+1]
- *   num_docs      B >= 0
+ *   num_docs      B in [0, 2^31 - 2] (B + 1 entries must fit an int32 count)
  *   total_tokens  T, 0 <= T < 2^31
  *   cp_size       W in [1, 64]
  *   policy        enum cp_policy
@@ -258,7 +259,7 @@ typedef struct cp_attn_header {
 } cp_attn_header;
 
 /* Bytes of the attention-step metadata of B documents and W ranks (a multiple
- * of 256); 0 for B < 0 or W outside [1, CP_MAX_CP_SIZE]. */
+ * of 256); 0 for B outside [0, 2^31 - 2] or W outside [1, CP_MAX_CP_SIZE]. */
 size_t cp_attn_meta_bytes(int32_t num_docs, int32_t cp_size);
 
 /*

@@ -24,3 +24,39 @@ def test_c_program_links_and_runs(tmp_path):
     res = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert res.returncode == 0, res.stdout + res.stderr
     assert "c consumer ok" in res.stdout
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None or shutil.which("g++") is None, reason="gcc/g++ not available")
+def test_host_validation_under_sanitizers(tmp_path):
+    """The host layer (abi.cpp, every argument check of every entry point) built
+    with AddressSanitizer and UBSan, the launch functions replaced by stand-ins
+    that report an error, and driven by tests/c_validation_fuzz.c: seeded random
+    arguments (integer edge values, NULL and fake pointers) through every entry
+    point; every call returns a known status, with no memory error, leak or
+    undefined behaviour (an int32 overflow in the size helpers was found this way)."""
+    rocm_inc, rocm_lib = "/opt/rocm/include", "/opt/rocm/lib"
+    if not os.path.exists(os.path.join(rocm_lib, "libamdhip64.so")):
+        pytest.skip("HIP runtime library not found")
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined"]
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"), "-I", rocm_inc,
+           "-D__HIP_PLATFORM_AMD__"]
+    objs = []
+    for src in (os.path.join(PKG, "csrc", "abi.cpp"), os.path.join(ROOT, "tests", "abi_stubs.cpp")):
+        obj = str(tmp_path / (os.path.basename(src) + ".o"))
+        subprocess.run(["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-Wall", *san, *inc, "-c", src, "-o", obj],
+                       check=True, capture_output=True, text=True)
+        objs.append(obj)
+    lib = str(tmp_path / "libcpthd_san.so")
+    subprocess.run(["g++", "-shared", "-fPIC", *san, *objs, f"-L{rocm_lib}", "-lamdhip64",
+                    f"-Wl,-rpath,{rocm_lib}", "-o", lib], check=True, capture_output=True, text=True)
+    exe = str(tmp_path / "fuzz")
+    subprocess.run(["gcc", "-std=c11", "-O1", "-g", "-Wall", "-Wextra", "-pedantic", "-Werror", *san,
+                    "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_validation_fuzz.c"),
+                    f"-L{tmp_path}", "-lcpthd_san", f"-Wl,-rpath,{tmp_path}", f"-L{rocm_lib}",
+                    f"-Wl,-rpath-link,{rocm_lib}", "-o", exe], check=True, capture_output=True, text=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:halt_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    for seed in ("0", "1", "2"):
+        res = subprocess.run([exe, seed, "20000"], capture_output=True, text=True, timeout=300, env=env)
+        assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-4000:]
+        assert "fuzz ok" in res.stdout

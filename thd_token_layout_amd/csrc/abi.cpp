@@ -239,8 +239,8 @@ using namespace cpthd;
 extern "C" {
 
 size_t cp_meta_bytes(int32_t num_docs, int32_t cp_size) {
-  if (num_docs < 0 || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return 0;
-  const size_t bytes = 64 + 4 * (size_t)(num_docs + 1) * (size_t)(cp_size + 1) + 4 * (size_t)cp_size;
+  if (num_docs < 0 || num_docs >= INT32_MAX || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return 0;
+  const size_t bytes = 64 + 4 * ((size_t)num_docs + 1) * ((size_t)cp_size + 1) + 4 * (size_t)cp_size;
   return (bytes + 255) & ~(size_t)255;
 }
 
@@ -248,7 +248,7 @@ int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tok
                   int32_t cp_size, int32_t policy, void* meta, size_t meta_bytes,
                   cp_stream_t stream) {
   if (cu_seqlens == nullptr || meta == nullptr) return CP_ERR_ARG;
-  if (num_docs < 0 || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return CP_ERR_ARG;
+  if (num_docs < 0 || num_docs >= INT32_MAX || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return CP_ERR_ARG;
   if (total_tokens < 0 || total_tokens > INT32_MAX) return CP_ERR_ARG;
   if (policy != CP_POLICY_DUAL_CHUNK_SWAP && policy != CP_POLICY_PACKED_CONTIGUOUS) return CP_ERR_ARG;
   if (policy == CP_POLICY_PACKED_CONTIGUOUS && total_tokens % cp_size != 0) return CP_ERR_SHAPE;
@@ -256,10 +256,10 @@ int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tok
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
   AllocCache cache;
-  if ((st = check_device_buf(cu_seqlens, 4 * (int64_t)(num_docs + 1), dev, &cache)) != CP_OK) return st;
+  if ((st = check_device_buf(cu_seqlens, 4 * ((int64_t)num_docs + 1), dev, &cache)) != CP_OK) return st;
   if ((st = check_device_buf(meta, (int64_t)cp_meta_bytes(num_docs, cp_size), dev, &cache)) != CP_OK) return st;
   if ((st = check_alias({range_of(meta, (int64_t)meta_bytes)},
-                        {range_of(cu_seqlens, 4 * (int64_t)(num_docs + 1))})) != CP_OK)
+                        {range_of(cu_seqlens, 4 * ((int64_t)num_docs + 1))})) != CP_OK)
     return st;
   if ((st = hip_status(launch_build_meta(cu_seqlens, num_docs, total_tokens, cp_size, policy, meta,
                                          reinterpret_cast<hipStream_t>(stream)))) != CP_OK)
@@ -269,7 +269,7 @@ int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tok
 }
 
 size_t cp_attn_meta_bytes(int32_t num_docs, int32_t cp_size) {
-  if (num_docs < 0 || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return 0;
+  if (num_docs < 0 || num_docs >= INT32_MAX || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return 0;
   const size_t bytes = 64 + 2 * (size_t)cp_size * (size_t)attn_record_bytes(num_docs);
   return (bytes + 255) & ~(size_t)255;
 }
@@ -277,7 +277,7 @@ size_t cp_attn_meta_bytes(int32_t num_docs, int32_t cp_size) {
 int cp_build_attn_meta(const void* meta, int32_t num_docs, int32_t cp_size, void* attn,
                        size_t attn_bytes, cp_stream_t stream) {
   if (meta == nullptr || attn == nullptr) return CP_ERR_ARG;
-  if (num_docs < 0 || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return CP_ERR_ARG;
+  if (num_docs < 0 || num_docs >= INT32_MAX || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return CP_ERR_ARG;
   if (attn_bytes < cp_attn_meta_bytes(num_docs, cp_size)) return CP_ERR_SHAPE;
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;

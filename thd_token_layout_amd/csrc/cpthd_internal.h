@@ -18,9 +18,9 @@ constexpr int64_t kMaxGrid = int64_t(1) << 22;
 
 // Byte offsets inside the metadata buffer (layout documented in cpthd.h).
 __host__ __device__ inline int64_t meta_cu_offset() { return 64; }
-__host__ __device__ inline int64_t meta_local_cu_offset(int32_t B) { return 64 + 4 * (int64_t)(B + 1); }
+__host__ __device__ inline int64_t meta_local_cu_offset(int32_t B) { return 64 + 4 * ((int64_t)B + 1); }
 __host__ __device__ inline int64_t meta_n_local_offset(int32_t B, int32_t W) {
-  return 64 + 4 * (int64_t)(B + 1) * (W + 1);
+  return 64 + 4 * ((int64_t)B + 1) * ((int64_t)W + 1);
 }
 
 // Fixed-capacity pointer table passed by value in the kernel arguments.
@@ -47,7 +47,7 @@ hipError_t launch_build_meta(const int32_t* cu, int32_t B, int64_t T, int32_t W,
 
 // Attention-step records (layout documented in cpthd.h): 64-byte header, then
 // 2W records of 32 + 16(B+1) bytes.
-__host__ __device__ inline int64_t attn_record_bytes(int32_t B) { return 32 + 16 * (int64_t)(B + 1); }
+__host__ __device__ inline int64_t attn_record_bytes(int32_t B) { return 32 + 16 * ((int64_t)B + 1); }
 __host__ __device__ inline int64_t attn_record_offset(int32_t B, int32_t index) {
   return 64 + (int64_t)index * attn_record_bytes(B);
 }
