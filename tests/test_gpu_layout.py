@@ -292,23 +292,30 @@ def test_buffers_smaller_than_the_sizes_are_rejected(cp):
 def test_extent_check_inside_one_allocation(cp):
     """Buffers of one call that lie in one allocation are checked against that
     allocation's end even when the runtime is asked about it only once: a slot
-    that starts 256 bytes before the end and runs 512 bytes is refused."""
+    that starts 256 bytes before the end and runs 512 bytes is refused.  The
+    allocation is made with hipMalloc directly, so its extent is exactly known
+    (through the library's own handle: the HIP runtime this process already uses)."""
     say("case extent of a second buffer in the same allocation")
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    big = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
-    segs = [sg for sg in torch.cuda.memory._snapshot()["segments"]
-            if sg["address"] <= big.data_ptr() < sg["address"] + sg["total_size"]]
-    if len(segs) != 1 or segs[0]["address"] != big.data_ptr() or segs[0]["total_size"] != big.numel():
-        pytest.skip("the caching allocator did not give this tensor an allocation of its own")
-    out = torch.zeros(128, dtype=torch.float32, device=DEV)
-    end = big.data_ptr() + big.numel()
-    slots = (ctypes.c_void_p * 2)(big.data_ptr(), end - 256)
-    assert cp.lib.cp_slot_sum(2, slots, out.data_ptr(), 128, cp.CP_F32, cp.CP_F32, 0, None) == cp.CP_ERR_SHAPE
-    slots = (ctypes.c_void_p * 2)(big.data_ptr(), end - 512)  # ends exactly at the allocation's end
-    assert cp.lib.cp_slot_sum(2, slots, out.data_ptr(), 128, cp.CP_F32, cp.CP_F32, 0, None) == cp.CP_OK
-    torch.cuda.synchronize()
-    assert (out == 0).all()
+    hip = ctypes.CDLL(cp.LIB_PATH)
+    hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    hip.hipMemset.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t]
+    hip.hipFree.argtypes = [ctypes.c_void_p]
+    size = 64 << 20
+    base = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(base), size) == 0
+    try:
+        assert hip.hipMemset(base, 0, size) == 0
+        out = torch.zeros(128, dtype=torch.float32, device=DEV)
+        end = base.value + size
+        slots = (ctypes.c_void_p * 2)(base.value, end - 256)
+        assert cp.lib.cp_slot_sum(2, slots, out.data_ptr(), 128, cp.CP_F32, cp.CP_F32, 0, None) == cp.CP_ERR_SHAPE
+        slots = (ctypes.c_void_p * 2)(base.value, end - 512)  # ends exactly at the allocation's end
+        assert cp.lib.cp_slot_sum(2, slots, out.data_ptr(), 128, cp.CP_F32, cp.CP_F32, 0, None) == cp.CP_OK
+        torch.cuda.synchronize()
+        assert (out == 0).all()
+    finally:
+        torch.cuda.synchronize()
+        hip.hipFree(base)
 
 
 def test_stale_host_record_changes_no_result(cp):
