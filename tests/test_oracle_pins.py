@@ -175,3 +175,34 @@ def test_exhaustive_small_layouts():
                         assert o.rank_rows(cu, T, W, o.DUAL_CHUNK_SWAP, r).tolist() == rows[r]
                 count += 1
     assert count > 500
+
+
+@settings(max_examples=80, deadline=None, derandomize=True)
+@given(st.integers(1, 9), st.integers(0, 3000), st.sampled_from(["f32", "bf16"]), st.integers(0, 2 ** 31))
+def test_allreduce_random(W, n, dt, seed):
+    """All-reduce invariants on random sizes: every rank ends with the same bits
+    under every algorithm; the two-shot equals the one-shot (both sum each element
+    in rank order); the ring equals the closed rotated-order sum per chunk;
+    integer-valued data gives the exact sum under all three."""
+    rng = np.random.default_rng(seed)
+    xs = [rng.standard_normal(n).astype(np.float32) for _ in range(W)]
+    data = xs if dt == "f32" else [o.f32_to_bf16_rne(x) for x in xs]
+    one = o.allreduce_one_shot(data, dt)
+    two = o.allreduce_two_shot(data, dt)
+    ring = o.allreduce_ring(data, dt)
+    for res in (one, two, ring):
+        assert len(res) == W and all(r.tobytes() == res[0].tobytes() for r in res)
+    assert two[0].tobytes() == one[0].tobytes()
+    want = np.empty_like(data[0])
+    for k, (a, b) in enumerate(o.ring_chunks(n, W)):
+        acc = data[k][a:b]
+        for j in range(1, W):
+            x = data[(k + j) % W][a:b]
+            acc = (acc + x).astype(np.float32) if dt == "f32" else \
+                o.f32_to_bf16_rne(o.bf16_to_f32(acc) + o.bf16_to_f32(x))
+        want[a:b] = acc
+    assert ring[0].tobytes() == want.tobytes()
+    ints = [rng.integers(-500, 500, size=n).astype(np.float32) for _ in range(W)]
+    exact = np.sum([i.astype(np.float64) for i in ints], axis=0) if n else np.zeros(0)
+    for fn in (o.allreduce_one_shot, o.allreduce_two_shot, o.allreduce_ring):
+        assert np.array_equal(fn(ints, "f32")[0].astype(np.float64), exact)
