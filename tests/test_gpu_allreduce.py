@@ -350,3 +350,38 @@ def test_largest_sizes(cp, algo):
         assert bits_equal(got, want), r
     del xs, outs
     torch.cuda.empty_cache()
+
+
+def test_every_small_size(cp):
+    """Every n in 0..200 for W = 1..8 (chunk edges, empty chunks, tails of every
+    length) under one-shot, ring, two-shot and the ring in one launch, fp32,
+    against the oracle; one buffer set reused, outputs poisoned before each call."""
+    say("case allreduce every small size")
+    gen = torch.Generator(device=DEV).manual_seed(123)
+    big_in = [torch.randn(256, generator=gen, device=DEV) for _ in range(8)]
+    big_out = [torch.empty(256, device=DEV) for _ in range(8)]
+    host_in = [to_np(x) for x in big_in]
+    epoch = 0
+    for W in range(1, 9):
+        say(f"  W={W}")
+        sig_w = torch.zeros(cp.cp_allreduce_signal_bytes(W), dtype=torch.uint8, device=DEV)
+        first_epoch = epoch + 1
+        for n in range(0, 201):
+            xs = [x[:n] for x in big_in[:W]]
+            outs = [o[:n] for o in big_out[:W]]
+            hx = [h[:n] for h in host_in[:W]]
+            for algo in ("one_shot", "ring", "two_shot", "ring_one_launch"):
+                for o in big_out:
+                    o.fill_(float("nan"))
+                if algo == "ring_one_launch":
+                    epoch += 1
+                    cp.cp_allreduce_signal(xs, sig_w, epoch, outs=outs, wait_timeout_us=500000)
+                    ref = O.allreduce_ring(hx, "f32")
+                else:
+                    cp.cp_allreduce(xs, outs, algo=algo)
+                    ref = REF[algo](hx, "f32")
+                torch.cuda.synchronize()
+                for r in range(W):
+                    assert bits_equal(to_np(outs[r]), ref[r]), (W, n, algo, r)
+        # no call of this W timed out or found a stale epoch
+        assert cp.cp_allreduce_signal_status(sig_w, W, first_epoch) == cp.CP_OK
