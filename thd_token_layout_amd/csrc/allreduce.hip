@@ -1,5 +1,5 @@
 // All-reduce of W rank buffers held on one device: one-shot, ring (one launch
-// per step) and the ring in one launch with in-kernel signalling.
+// per step), two-shot, and the ring in one launch with in-kernel signalling.
 #include "units.h"
 
 #include <atomic>
@@ -9,13 +9,15 @@
 namespace cpthd {
 namespace {
 
-// ---- all-reduce: one-shot and ring ---------------------------------------------
+// ---- all-reduce: one-shot, ring, two-shot ----------------------------------------
 // "Low Latency Communication Kernels with NVSHMEM": the all-reduce algorithms
 // picked by message size and the exercise comparing a one-shot all-reduce
 // with a ring over 1 KB - 16 MB.  One-shot: every rank sums all W buffers
 // itself.  Ring: a reduce-scatter then an all-gather, W-1 steps each, every
 // rank passing one chunk to rank r+1 per step; partials travel in the buffer
-// type, so a bf16 ring rounds after each add.
+// type, so a bf16 ring rounds after each add.  Two-shot (not named by the
+// pages; the direct algorithm between the two): rank r sums chunk r of all
+// buffers, then every rank copies every reduced chunk.
 // All W ranks' buffers sit in this device's HBM; each launch does one step of
 // the algorithm for every rank, ranks in blockIdx.y (dispatch runs rank by
 // rank, as W devices would each do their own share).
