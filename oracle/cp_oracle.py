@@ -408,42 +408,53 @@ def slot_sum(slots, in_dtype, out_dtype, into=None):
     return _narrow(acc, out_dtype)
 
 
-def grad_scatter(grads, cu, cp_size, policy=DUAL_CHUNK_SWAP):
+def _owner_list(cp_size, owners):
+    return range(cp_size) if owners is None else [int(o) for o in owners]
+
+
+def grad_scatter(grads, cu, cp_size, policy=DUAL_CHUNK_SWAP, owners=None):
     """Writer w puts the rows owner o owns into slot [o][w].
 
     grads: list over writers of global [T, ...] arrays.  Returns
     slots[o][w] = grads[w][g_o(:)], i.e. partition(grads[w])[o]: the two-chunk
     layout under DualChunkSwap, the owner's contiguous slice under
-    packed-contiguous.
+    packed-contiguous.  `owners` (default: all) restricts the work to those
+    owners; the other owners' entries are None.  Every owner's slots depend on
+    that owner's rows only, so a restricted call gives the same arrays.
     """
     W = cp_size
     T = grads[0].shape[0]
     slots = [[None] * W for _ in range(W)]
-    for w in range(W):
-        for o in range(W):
-            slots[o][w] = grads[w][rank_rows(cu, T, W, policy, o)]
+    for o in _owner_list(W, owners):
+        rows = rank_rows(cu, T, W, policy, o)
+        for w in range(W):
+            slots[o][w] = grads[w][rows]
     return slots
 
 
-def grad_return(grads, cu, cp_size, in_dtype, out_dtype, policy=DUAL_CHUNK_SWAP, into=None):
+def grad_return(grads, cu, cp_size, in_dtype, out_dtype, policy=DUAL_CHUNK_SWAP, into=None,
+                owners=None):
     """Scatter, then each owner sums its W writer slots in order 0..W-1.
 
     Returns (slots, out) with out[o] = sum_w slots[o][w]; with `into` (a list
     over owners of their current gradients) out[o] = into[o] + slot 0 + ... .
+    `owners` (default: all) restricts the work to those owners (None elsewhere).
     """
-    slots = grad_scatter(grads, cu, cp_size, policy)
-    out = [slot_sum(slots[o], in_dtype, out_dtype, None if into is None else into[o])
-           for o in range(cp_size)]
+    slots = grad_scatter(grads, cu, cp_size, policy, owners)
+    out = [None] * cp_size
+    for o in _owner_list(cp_size, owners):
+        out[o] = slot_sum(slots[o], in_dtype, out_dtype, None if into is None else into[o])
     return slots, out
 
 
-def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=DUAL_CHUNK_SWAP, into=None):
+def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=DUAL_CHUNK_SWAP, into=None,
+                      owners=None):
     """No slots: out[o][i] = sum over w (in order) of grads[w][g_o(i)]
-    (after into[o][i] when accumulating)."""
+    (after into[o][i] when accumulating).  `owners` as in grad_return."""
     W = cp_size
     T = grads[0].shape[0]
-    out = []
-    for o in range(W):
+    out = [None] * W
+    for o in _owner_list(W, owners):
         rows = rank_rows(cu, T, W, policy, o)
         if into is None:
             acc = _widen(grads[0][rows], in_dtype).astype(np.float32, copy=True)
@@ -454,7 +465,7 @@ def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=DUAL_CHUNK
         with np.errstate(over="ignore", invalid="ignore"):
             for w in range(first, W):
                 acc = (acc + _widen(grads[w][rows], in_dtype)).astype(np.float32)
-        out.append(_narrow(acc, out_dtype))
+        out[o] = _narrow(acc, out_dtype)
     return out
 
 

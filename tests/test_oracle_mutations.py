@@ -133,30 +133,31 @@ def _bf16_half_up(o):
 
 
 def _scatter_transposed(o):
-    def grad_scatter(grads, cu, cp_size, policy=o.DUAL_CHUNK_SWAP):
+    def grad_scatter(grads, cu, cp_size, policy=o.DUAL_CHUNK_SWAP, owners=None):
         W = cp_size
         T = grads[0].shape[0]
         slots = [[None] * W for _ in range(W)]
         for w in range(W):
-            for own in range(W):
+            for own in (range(W) if owners is None else owners):
                 slots[own][w] = grads[own][o.rank_rows(cu, T, W, policy, w)]
         return slots
     return grad_scatter
 
 
 def _fused_reversed(o):
-    def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=o.DUAL_CHUNK_SWAP, into=None):
+    def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=o.DUAL_CHUNK_SWAP, into=None,
+                          owners=None):
         W = cp_size
         T = grads[0].shape[0]
-        out = []
-        for own in range(W):
+        out = [None] * W
+        for own in (range(W) if owners is None else owners):
             rows = o.rank_rows(cu, T, W, policy, own)
             acc = o._widen(grads[W - 1][rows], in_dtype).astype(np.float32, copy=True)
             for w in range(W - 2, -1, -1):
                 acc = (acc + o._widen(grads[w][rows], in_dtype)).astype(np.float32)
             if into is not None:
                 acc = (acc + o._widen(into[own], out_dtype)).astype(np.float32)
-            out.append(o._narrow(acc, out_dtype))
+            out[own] = o._narrow(acc, out_dtype)
         return out
     return grad_return_fused
 
@@ -191,24 +192,26 @@ def _acc_added_once(o):
 def _acc_ignored(o):
     orig = o.grad_return_fused
 
-    def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=o.DUAL_CHUNK_SWAP, into=None):
-        return orig(grads, cu, cp_size, in_dtype, out_dtype, policy)
+    def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=o.DUAL_CHUNK_SWAP, into=None,
+                          owners=None):
+        return orig(grads, cu, cp_size, in_dtype, out_dtype, policy, owners=owners)
     return grad_return_fused
 
 
 def _grad_policy_ignored(o):
     orig = o.grad_scatter
 
-    def grad_scatter(grads, cu, cp_size, policy=o.DUAL_CHUNK_SWAP):
-        return orig(grads, cu, cp_size, o.DUAL_CHUNK_SWAP)
+    def grad_scatter(grads, cu, cp_size, policy=o.DUAL_CHUNK_SWAP, owners=None):
+        return orig(grads, cu, cp_size, o.DUAL_CHUNK_SWAP, owners)
     return grad_scatter
 
 
 def _fused_policy_ignored(o):
     orig = o.grad_return_fused
 
-    def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=o.DUAL_CHUNK_SWAP, into=None):
-        return orig(grads, cu, cp_size, in_dtype, out_dtype, o.DUAL_CHUNK_SWAP, into)
+    def grad_return_fused(grads, cu, cp_size, in_dtype, out_dtype, policy=o.DUAL_CHUNK_SWAP, into=None,
+                          owners=None):
+        return orig(grads, cu, cp_size, in_dtype, out_dtype, o.DUAL_CHUNK_SWAP, into, owners)
     return grad_return_fused
 
 

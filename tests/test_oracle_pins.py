@@ -206,3 +206,30 @@ def test_allreduce_random(W, n, dt, seed):
     exact = np.sum([i.astype(np.float64) for i in ints], axis=0) if n else np.zeros(0)
     for fn in (o.allreduce_one_shot, o.allreduce_two_shot, o.allreduce_ring):
         assert np.array_equal(fn(ints, "f32")[0].astype(np.float64), exact)
+
+
+@settings(max_examples=30, deadline=None, derandomize=True)
+@given(dcs_case(), st.booleans(), st.integers(0, 2**31 - 1))
+def test_owner_subsets_match_the_full_call(case, pc, seed):
+    """The oracle's gradient functions restricted to some owners give exactly the
+    full call's arrays for those owners (and None for the others): the full-size
+    GPU checks compare one owner at a time through these restricted calls."""
+    W, lengths = case
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    pol = o.PACKED_CONTIGUOUS if pc else o.DUAL_CHUNK_SWAP
+    rng = np.random.default_rng(seed)
+    grads = [rng.standard_normal((T, 2)).astype(np.float32) for _ in range(W)]
+    into = [rng.standard_normal((T // W, 2)).astype(np.float32) for _ in range(W)]
+    full_slots, full_out = o.grad_return(grads, cu, W, "f32", "bf16", policy=pol)
+    full_fused = o.grad_return_fused(grads, cu, W, "f32", "f32", policy=pol, into=into)
+    owners = sorted(set(rng.integers(0, W, size=2).tolist()))
+    slots, out = o.grad_return(grads, cu, W, "f32", "bf16", policy=pol, owners=owners)
+    fused = o.grad_return_fused(grads, cu, W, "f32", "f32", policy=pol, into=into, owners=owners)
+    for own in range(W):
+        if own in owners:
+            assert all(slots[own][w].tobytes() == full_slots[own][w].tobytes() for w in range(W))
+            assert out[own].tobytes() == full_out[own].tobytes()
+            assert fused[own].tobytes() == full_fused[own].tobytes()
+        else:
+            assert out[own] is None and fused[own] is None and all(s is None for s in slots[own])
