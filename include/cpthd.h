@@ -45,8 +45,19 @@
  *    output byte) when the metadata is invalid or does not match the call;
  *    the mismatch is recorded as a sticky CP_CALL_* flag, and
  *    cp_meta_status reports both.
+ *  - The metadata buffer (`meta`) is passed as a non-const pointer to every
+ *    call whose kernels may write it: they OR the sticky CP_CALL_* flags into
+ *    its header, and the gradient return's epoch wait records its timeout mask
+ *    there (both atomically, so calls on several streams may share one
+ *    metadata buffer).  Nothing else in the buffer is written after
+ *    cp_build_meta.
  *  - Outputs must not overlap inputs or each other (CP_ERR_ALIAS); [GR]
- *    "Description" (self-alias assertions on the rank-self slots).
+ *    "Description" (self-alias assertions on the rank-self slots).  The
+ *    metadata header counts as an output of every call that takes `meta`, its
+ *    tables (cu_seqlens and the per-rank tables after the header) as an input:
+ *    over the whole cp_meta_bytes(B, W) extent when the call names B and W or
+ *    the host built the metadata at that address for the call's token count
+ *    (and CP size), else over the header alone.
  *  - Every buffer must be device memory of the current device (else
  *    CP_ERR_DEVICE) and, as far as the runtime reports allocation extents,
  *    lie inside one allocation for the byte count the call's sizes imply
@@ -274,7 +285,7 @@ size_t cp_attn_meta_bytes(int32_t num_docs, int32_t cp_size);
  * CP_CALL_* flag (read with cp_meta_status), and the attention header's magic
  * is written as 0 with no step record written (fail-closed).
  */
-int cp_build_attn_meta(const void* meta, int32_t num_docs, int32_t cp_size, void* attn,
+int cp_build_attn_meta(void* meta, int32_t num_docs, int32_t cp_size, void* attn,
                        size_t attn_bytes, cp_stream_t stream);
 
 /* ------------------------------------------------------------ token layout */
@@ -296,7 +307,7 @@ int cp_build_attn_meta(const void* meta, int32_t num_docs, int32_t cp_size, void
  * meta flags and the kernel writes nothing.
  */
 int cp_partition_thd(const void* x, void* parts, int64_t total_tokens, int32_t heads,
-                     int32_t head_dim, int32_t dtype, const void* meta, cp_stream_t stream);
+                     int32_t head_dim, int32_t dtype, void* meta, cp_stream_t stream);
 
 /*
  * cp_gather_thd - inverse of cp_partition_thd: x[g_r(i)] = parts[r][i]
@@ -305,7 +316,7 @@ int cp_partition_thd(const void* x, void* parts, int64_t total_tokens, int32_t h
  * Same arguments, roles of x and parts swapped (parts input, x output).
  */
 int cp_gather_thd(const void* parts, void* x, int64_t total_tokens, int32_t heads,
-                  int32_t head_dim, int32_t dtype, const void* meta, cp_stream_t stream);
+                  int32_t head_dim, int32_t dtype, void* meta, cp_stream_t stream);
 
 /*
  * cp_partition_thd_multi / cp_gather_thd_multi - the same operations on
@@ -319,10 +330,10 @@ int cp_gather_thd(const void* parts, void* x, int64_t total_tokens, int32_t head
  */
 int cp_partition_thd_multi(int32_t n_tensors, const void* const* xs, void* const* parts,
                            int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
-                           const void* meta, cp_stream_t stream);
+                           void* meta, cp_stream_t stream);
 int cp_gather_thd_multi(int32_t n_tensors, const void* const* parts, void* const* xs,
                         int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
-                        const void* meta, cp_stream_t stream);
+                        void* meta, cp_stream_t stream);
 
 /* ------------------------------------------------------------ gradient return */
 /*
@@ -387,7 +398,7 @@ int cp_gather_thd_multi(int32_t n_tensors, const void* const* parts, void* const
 int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors,
                    const void* const* grads, void* const* slots, void* const* out,
                    int64_t total_tokens, int32_t heads, int32_t head_dim,
-                   int32_t in_dtype, int32_t out_dtype, const void* meta,
+                   int32_t in_dtype, int32_t out_dtype, void* meta,
                    uint32_t* epochs, uint32_t epoch, int64_t wait_timeout_us,
                    int32_t phases, cp_stream_t stream);
 
@@ -406,7 +417,7 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors,
 int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
                          const void* const* grads, void* const* out, int64_t total_tokens,
                          int32_t heads, int32_t head_dim, int32_t in_dtype,
-                         int32_t out_dtype, const void* meta, int32_t flags,
+                         int32_t out_dtype, void* meta, int32_t flags,
                          cp_stream_t stream);
 
 /*

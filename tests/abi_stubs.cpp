@@ -9,7 +9,7 @@ namespace cpthd {
 hipError_t launch_build_meta(const int32_t*, int32_t, int64_t, int32_t, int32_t, void*, hipStream_t) {
   return hipErrorNotSupported;
 }
-hipError_t launch_build_attn_meta(const void*, int32_t, int32_t, void*, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_build_attn_meta(cp_meta_header*, int32_t, int32_t, void*, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_permute(const PermuteArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_slot_sum(const SlotSumArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_fused(const FusedArgs&, hipStream_t) { return hipErrorNotSupported; }

@@ -60,3 +60,19 @@ def test_host_validation_under_sanitizers(tmp_path):
         res = subprocess.run([exe, seed, "20000"], capture_output=True, text=True, timeout=300, env=env)
         assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-4000:]
         assert "fuzz ok" in res.stdout
+
+
+@pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="hipcc not available")
+@pytest.mark.parametrize("flags", [["-O0", "-fwrapv"], ["-O2"]], ids=["O0-wrapv", "O2"])
+def test_find_doc_near_int32_max(tmp_path, flags):
+    """The document search of the permutation and metadata kernels, built for the
+    host, at document counts up to 2^31 - 1 (tables computed on the fly).  With
+    wrapping int32 arithmetic the former midpoint (lo + hi + 1) / 2 overflowed and
+    the search never ended; the timeout turns such a hang into a failure."""
+    exe = str(tmp_path / "find_doc_host")
+    subprocess.run(["/opt/rocm/bin/hipcc", "-x", "hip", "--cuda-host-only", "-std=c++17", *flags,
+                    "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+                    os.path.join(ROOT, "tests", "find_doc_host.hip"), "-o", exe],
+                   check=True, capture_output=True, text=True)
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0 and "find_doc ok" in res.stdout, res.stdout + res.stderr

@@ -63,6 +63,34 @@ Range range_of(const void* p, int64_t bytes) {
   return Range{a, a + (uintptr_t)(bytes > 0 ? bytes : 0)};
 }
 
+// Byte ranges of a metadata buffer for one call's checks.  The kernels write
+// the 64-byte header (sticky call flags, the epoch wait's timeout mask), so it
+// is an output of the call; the tables after it are only read, an input.  The
+// tables' extent is known when the call names B and W (num_docs >= 0), or when
+// the host built the metadata at this address for the call's token count (and
+// CP size, when the call has one); otherwise the header alone is covered.
+struct MetaSpan {
+  int64_t bytes;  // extent checked against the allocation
+  Range header;
+  Range tables;   // empty when unknown
+};
+
+MetaSpan meta_span(const void* meta, int64_t total_tokens, int32_t cp_size, int32_t num_docs) {
+  int64_t bytes = (int64_t)sizeof(cp_meta_header);
+  if (num_docs >= 0 && cp_size > 0) {
+    bytes = (int64_t)cp_meta_bytes(num_docs, cp_size);
+  } else {
+    std::lock_guard<std::mutex> lock(g_records_mu);
+    auto it = g_records.find(meta);
+    if (it != g_records.end() && it->second.total_tokens == total_tokens &&
+        (cp_size <= 0 || it->second.cp_size == cp_size))
+      bytes = (int64_t)cp_meta_bytes(it->second.num_docs, it->second.cp_size);
+  }
+  if (bytes < (int64_t)sizeof(cp_meta_header)) bytes = (int64_t)sizeof(cp_meta_header);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(meta);
+  return MetaSpan{bytes, Range{a, a + sizeof(cp_meta_header)}, Range{a + sizeof(cp_meta_header), a + (uintptr_t)bytes}};
+}
+
 bool overlap(const Range& a, const Range& b) {
   if (a.lo == a.hi || b.lo == b.hi) return false;
   return a.lo < b.hi && b.lo < a.hi;
@@ -274,7 +302,7 @@ size_t cp_attn_meta_bytes(int32_t num_docs, int32_t cp_size) {
   return (bytes + 255) & ~(size_t)255;
 }
 
-int cp_build_attn_meta(const void* meta, int32_t num_docs, int32_t cp_size, void* attn,
+int cp_build_attn_meta(void* meta, int32_t num_docs, int32_t cp_size, void* attn,
                        size_t attn_bytes, cp_stream_t stream) {
   if (meta == nullptr || attn == nullptr) return CP_ERR_ARG;
   if (num_docs < 0 || num_docs >= INT32_MAX || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return CP_ERR_ARG;
@@ -282,12 +310,13 @@ int cp_build_attn_meta(const void* meta, int32_t num_docs, int32_t cp_size, void
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
   AllocCache cache;
-  if ((st = check_device_buf(meta, (int64_t)cp_meta_bytes(num_docs, cp_size), dev, &cache)) != CP_OK) return st;
+  const MetaSpan ms = meta_span(meta, -1, cp_size, num_docs);
+  if ((st = check_device_buf(meta, ms.bytes, dev, &cache)) != CP_OK) return st;
   if ((st = check_device_buf(attn, (int64_t)cp_attn_meta_bytes(num_docs, cp_size), dev, &cache)) != CP_OK) return st;
-  if ((st = check_alias({range_of(attn, (int64_t)attn_bytes)},
-                        {range_of(meta, (int64_t)cp_meta_bytes(num_docs, cp_size))})) != CP_OK)
+  if ((st = check_alias({range_of(attn, (int64_t)attn_bytes), ms.header}, {ms.tables})) != CP_OK)
     return st;
-  return hip_status(launch_build_attn_meta(meta, num_docs, cp_size, attn, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(launch_build_attn_meta(static_cast<cp_meta_header*>(meta), num_docs, cp_size, attn,
+                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
 int cp_meta_status(const void* meta, cp_stream_t stream, int32_t* flags_out,
@@ -318,7 +347,7 @@ int cp_meta_status(const void* meta, cp_stream_t stream, int32_t* flags_out,
 
 static int layout_call(int32_t n_tensors, const void* const* ins, void* const* outs,
                        int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
-                       const void* meta, cp_stream_t stream, bool to_local) {
+                       void* meta, cp_stream_t stream, bool to_local) {
   if (is_fp8(dtype)) return CP_ERR_UNSUPPORTED;
   if (!valid_layout_dtype(dtype)) return CP_ERR_ARG;
   if (n_tensors < 1 || n_tensors > kMaxLayoutTensors) return CP_ERR_ARG;
@@ -333,8 +362,9 @@ static int layout_call(int32_t n_tensors, const void* const* ins, void* const* o
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
   AllocCache cache;
-  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev, &cache)) != CP_OK) return st;
-  std::vector<Range> in_ranges{range_of(meta, sizeof(cp_meta_header))}, out_ranges;
+  const MetaSpan ms = meta_span(meta, total_tokens, -1, -1);
+  if ((st = check_device_buf(meta, ms.bytes, dev, &cache)) != CP_OK) return st;
+  std::vector<Range> in_ranges{ms.tables}, out_ranges{ms.header};
   for (int t = 0; t < n_tensors; ++t) {
     if ((st = check_device_buf(ins[t], bytes, dev, &cache)) != CP_OK) return st;
     if ((st = check_device_buf(outs[t], bytes, dev, &cache)) != CP_OK) return st;
@@ -344,7 +374,7 @@ static int layout_call(int32_t n_tensors, const void* const* ins, void* const* o
   if ((st = check_alias(out_ranges, in_ranges)) != CP_OK) return st;
   PermuteArgs a;
   memset(&a, 0, sizeof(a));
-  a.meta = const_cast<cp_meta_header*>(static_cast<const cp_meta_header*>(meta));
+  a.meta = static_cast<cp_meta_header*>(meta);
   a.n_tensors = n_tensors;
   for (int t = 0; t < n_tensors; ++t) {
     a.global[t] = static_cast<char*>(to_local ? const_cast<void*>(ins[t]) : outs[t]);
@@ -361,24 +391,24 @@ static int layout_call(int32_t n_tensors, const void* const* ins, void* const* o
 }
 
 int cp_partition_thd(const void* x, void* parts, int64_t total_tokens, int32_t heads,
-                     int32_t head_dim, int32_t dtype, const void* meta, cp_stream_t stream) {
+                     int32_t head_dim, int32_t dtype, void* meta, cp_stream_t stream) {
   return layout_call(1, &x, &parts, total_tokens, heads, head_dim, dtype, meta, stream, true);
 }
 
 int cp_gather_thd(const void* parts, void* x, int64_t total_tokens, int32_t heads,
-                  int32_t head_dim, int32_t dtype, const void* meta, cp_stream_t stream) {
+                  int32_t head_dim, int32_t dtype, void* meta, cp_stream_t stream) {
   return layout_call(1, &parts, &x, total_tokens, heads, head_dim, dtype, meta, stream, false);
 }
 
 int cp_partition_thd_multi(int32_t n_tensors, const void* const* xs, void* const* parts,
                            int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
-                           const void* meta, cp_stream_t stream) {
+                           void* meta, cp_stream_t stream) {
   return layout_call(n_tensors, xs, parts, total_tokens, heads, head_dim, dtype, meta, stream, true);
 }
 
 int cp_gather_thd_multi(int32_t n_tensors, const void* const* parts, void* const* xs,
                         int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
-                        const void* meta, cp_stream_t stream) {
+                        void* meta, cp_stream_t stream) {
   return layout_call(n_tensors, parts, xs, total_tokens, heads, head_dim, dtype, meta, stream, false);
 }
 
@@ -402,9 +432,78 @@ static int grad_scalar_checks(int32_t rank, int32_t cp_size, int32_t n_tensors, 
   return CP_OK;
 }
 
+// The launches of the gradient return after validation: scatter (writers of
+// this call into every owner's slot), epoch publish and wait, owner sums.
+// rank < 0: every rank in stream order.  out[t][o] and grads[t][w] are
+// flattened host tables as in cp_grad_return; S(t, o, w) gives the device
+// address of slot [t][o][w].
+extern "C++" {
+template <typename SlotFn>
+static int grad_return_launches(int rank, int W, int n_tensors, const void* const* grads,
+                                 SlotFn S, void* const* out, int64_t total_tokens,
+                                 int64_t in_row, int64_t row_elems, int32_t in_dtype, int32_t out_dtype,
+                                 cp_meta_header* h, uint32_t* epochs, uint32_t epoch, int64_t ticks,
+                                 int32_t phases, hipStream_t s) {
+  const bool all = rank < 0;
+  const int64_t n = total_tokens / W;
+  const int w_lo = all ? 0 : rank, w_hi = all ? W : rank + 1;  // writers this call acts for
+  const int o_lo = w_lo, o_hi = w_hi;                           // owners this call sums for
+  auto G = [&](int t, int w) { return grads[(size_t)t * W + w]; };
+  auto O = [&](int t, int o) { return out[(size_t)t * W + o]; };
+  int st;
+  // 1. scatter: writer w's global gradient -> slot [o][w] of every owner o
+  for (int t = 0; t < n_tensors && (phases & CP_PHASE_SCATTER); ++t) {
+    for (int w = w_lo; w < w_hi; ++w) {
+      PermuteArgs a;
+      memset(&a, 0, sizeof(a));
+      a.meta = h;
+      a.n_tensors = 1;
+      a.global[0] = static_cast<char*>(const_cast<void*>(G(t, w)));
+      for (int o = 0; o < W; ++o) a.table.p[o] = static_cast<char*>(S(t, o, w));
+      a.local_table = true;
+      a.to_local = true;
+      a.total_tokens = total_tokens;
+      a.row_bytes = in_row;
+      a.expect_cp_size = W;
+      a.expect_policy = -1;  // the owner's rows follow the metadata's policy
+      hint_from_record(h, total_tokens, W, &a);
+      if ((st = hip_status(launch_permute(a, s))) != CP_OK) return st;
+    }
+  }
+  // 2-3. publish this call's writer epochs, wait for this call's owners
+  if (epochs && (phases & (CP_PHASE_PUBLISH | CP_PHASE_WAIT))) {
+    if ((phases & CP_PHASE_PUBLISH) &&
+        (st = hip_status(launch_epoch_publish(epochs, W, all ? -1 : rank, epoch, s))) != CP_OK)
+      return st;
+    if ((phases & CP_PHASE_WAIT) &&
+        (st = hip_status(launch_epoch_wait(epochs, W, all ? -1 : rank, epoch, ticks, h, s))) != CP_OK)
+      return st;
+  }
+  // 4. owner o: out = slot 0 + slot 1 + ... + slot W-1 (after out itself when accumulating)
+  for (int t = 0; t < n_tensors && (phases & CP_PHASE_SUM); ++t) {
+    for (int o = o_lo; o < o_hi; ++o) {
+      SlotSumArgs a;
+      memset(&a, 0, sizeof(a));
+      for (int w = 0; w < W; ++w) a.in.p[w] = static_cast<const char*>(S(t, o, w));
+      a.out = static_cast<char*>(O(t, o));
+      a.num_slots = W;
+      a.n_elems = n * row_elems;
+      a.in_dtype = in_dtype;
+      a.out_dtype = out_dtype;
+      a.gate_meta = h;
+      a.gate_T = total_tokens;
+      a.owner = epochs ? o : -1;
+      a.accumulate = (phases & CP_SUM_ACCUMULATE) != 0;
+      if ((st = hip_status(launch_slot_sum(a, s))) != CP_OK) return st;
+    }
+  }
+  return CP_OK;
+}
+}  // extern "C++"
+
 int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void* const* grads,
                    void* const* slots, void* const* out, int64_t total_tokens, int32_t heads,
-                   int32_t head_dim, int32_t in_dtype, int32_t out_dtype, const void* meta,
+                   int32_t head_dim, int32_t in_dtype, int32_t out_dtype, void* meta,
                    uint32_t* epochs, uint32_t epoch, int64_t wait_timeout_us,
                    int32_t phases, cp_stream_t stream) {
   int st;
@@ -443,10 +542,10 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
   int dev;
   if ((st = current_device(&dev)) != CP_OK) return st;
   AllocCache cache;
-  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev, &cache)) != CP_OK) return st;
+  const MetaSpan ms = meta_span(meta, total_tokens, W, -1);
+  if ((st = check_device_buf(meta, ms.bytes, dev, &cache)) != CP_OK) return st;
   if (epochs && (st = check_device_buf(epochs, 4 * (int64_t)W * W, dev, &cache)) != CP_OK) return st;
-  std::vector<Range> ins, outs;
-  ins.push_back(range_of(meta, sizeof(cp_meta_header)));
+  std::vector<Range> ins{ms.tables}, outs{ms.header};
   for (int t = 0; t < n_tensors; ++t) {
     for (int w = w_lo; w < w_hi; ++w) {
       if ((st = check_device_buf(G(t, w), total_tokens * in_row, dev, &cache)) != CP_OK) return st;
@@ -471,62 +570,16 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
   }
   if ((st = check_alias(outs, ins)) != CP_OK) return st;
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  cp_meta_header* h = const_cast<cp_meta_header*>(static_cast<const cp_meta_header*>(meta));
-  // 1. scatter: writer w's global gradient -> slot [o][w] of every owner o
-  for (int t = 0; t < n_tensors && (phases & CP_PHASE_SCATTER); ++t) {
-    for (int w = w_lo; w < w_hi; ++w) {
-      PermuteArgs a;
-      memset(&a, 0, sizeof(a));
-      a.meta = h;
-      a.n_tensors = 1;
-      a.global[0] = static_cast<char*>(const_cast<void*>(G(t, w)));
-      for (int o = 0; o < W; ++o) a.table.p[o] = static_cast<char*>(S(t, o, w));
-      a.local_table = true;
-      a.to_local = true;
-      a.total_tokens = total_tokens;
-      a.row_bytes = in_row;
-      a.expect_cp_size = W;
-      a.expect_policy = -1;  // the owner's rows follow the metadata's policy
-      hint_from_record(meta, total_tokens, W, &a);
-      if ((st = hip_status(launch_permute(a, s))) != CP_OK) return st;
-    }
-  }
-  // 2-3. publish this call's writer epochs, wait for this call's owners
-  if (epochs && (phases & (CP_PHASE_PUBLISH | CP_PHASE_WAIT))) {
-    const int64_t ticks = wait_ticks(dev, wait_timeout_us);
-    if ((phases & CP_PHASE_PUBLISH) &&
-        (st = hip_status(launch_epoch_publish(epochs, W, all ? -1 : rank, epoch, s))) != CP_OK)
-      return st;
-    if ((phases & CP_PHASE_WAIT) &&
-        (st = hip_status(launch_epoch_wait(epochs, W, all ? -1 : rank, epoch, ticks, h, s))) != CP_OK)
-      return st;
-  }
-  // 4. owner o: out = slot 0 + slot 1 + ... + slot W-1 (after out itself when accumulating)
-  for (int t = 0; t < n_tensors && (phases & CP_PHASE_SUM); ++t) {
-    for (int o = o_lo; o < o_hi; ++o) {
-      SlotSumArgs a;
-      memset(&a, 0, sizeof(a));
-      for (int w = 0; w < W; ++w) a.in.p[w] = static_cast<const char*>(S(t, o, w));
-      a.out = static_cast<char*>(O(t, o));
-      a.num_slots = W;
-      a.n_elems = n * row_elems;
-      a.in_dtype = in_dtype;
-      a.out_dtype = out_dtype;
-      a.gate_meta = h;
-      a.gate_T = total_tokens;
-      a.owner = epochs ? o : -1;
-      a.accumulate = (phases & CP_SUM_ACCUMULATE) != 0;
-      if ((st = hip_status(launch_slot_sum(a, s))) != CP_OK) return st;
-    }
-  }
-  return CP_OK;
+  return grad_return_launches(all ? -1 : rank, W, n_tensors, grads, S, out, total_tokens, in_row,
+                              row_elems, in_dtype, out_dtype, static_cast<cp_meta_header*>(meta), epochs, epoch,
+                              epochs && (phases & (CP_PHASE_PUBLISH | CP_PHASE_WAIT)) ? wait_ticks(dev, wait_timeout_us) : 0,
+                              phases, reinterpret_cast<hipStream_t>(stream));
 }
 
 int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
                          const void* const* grads, void* const* out, int64_t total_tokens,
                          int32_t heads, int32_t head_dim, int32_t in_dtype, int32_t out_dtype,
-                         const void* meta, int32_t flags, cp_stream_t stream) {
+                         void* meta, int32_t flags, cp_stream_t stream) {
   int st;
   if ((st = grad_scalar_checks(rank, cp_size, n_tensors, total_tokens, heads, head_dim, in_dtype,
                                out_dtype, meta)) != CP_OK)
@@ -550,9 +603,9 @@ int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
   int dev;
   if ((st = current_device(&dev)) != CP_OK) return st;
   AllocCache cache;
-  if ((st = check_device_buf(meta, (int64_t)sizeof(cp_meta_header), dev, &cache)) != CP_OK) return st;
-  std::vector<Range> ins, outs;
-  ins.push_back(range_of(meta, sizeof(cp_meta_header)));
+  const MetaSpan ms = meta_span(meta, total_tokens, W, -1);
+  if ((st = check_device_buf(meta, ms.bytes, dev, &cache)) != CP_OK) return st;
+  std::vector<Range> ins{ms.tables}, outs{ms.header};
   for (int t = 0; t < n_tensors; ++t) {
     for (int w = 0; w < W; ++w) {
       const void* g = grads[(size_t)t * W + w];
@@ -570,7 +623,7 @@ int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
   for (int t = 0; t < n_tensors; ++t) {
     FusedArgs a;
     memset(&a, 0, sizeof(a));
-    a.meta = const_cast<cp_meta_header*>(static_cast<const cp_meta_header*>(meta));
+    a.meta = static_cast<cp_meta_header*>(meta);
     for (int w = 0; w < W; ++w) a.grads.p[w] = static_cast<const char*>(grads[(size_t)t * W + w]);
     for (int o = o_lo; o < o_hi; ++o) a.out.p[o] = static_cast<char*>(out[(size_t)t * W + o]);
     a.cp_size = W;

@@ -51,7 +51,7 @@ __host__ __device__ inline int64_t attn_record_bytes(int32_t B) { return 32 + 16
 __host__ __device__ inline int64_t attn_record_offset(int32_t B, int32_t index) {
   return 64 + (int64_t)index * attn_record_bytes(B);
 }
-hipError_t launch_build_attn_meta(const void* meta, int32_t B, int32_t W, void* attn, hipStream_t stream);
+hipError_t launch_build_attn_meta(cp_meta_header* meta, int32_t B, int32_t W, void* attn, hipStream_t stream);
 
 // ---------------------------------------------------------------- row permutation
 // One launch moves all T rows of n_tensors tensors (same T, row size and

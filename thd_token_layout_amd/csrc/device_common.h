@@ -46,10 +46,14 @@ __device__ __forceinline__ bool meta_ok(cp_meta_header* h, int64_t T, int32_t ex
 
 // Largest b in [0, B) with bound[b] <= v, for a nondecreasing bound[] with
 // bound[0] <= v < bound[B]: the non-empty document holding position v.
-__device__ __forceinline__ int find_doc(const int32_t* bound, int32_t B, int64_t v) {
-  int lo = 0, hi = B - 1;
+// `bound` is a pointer or anything indexable; the midpoint is formed without
+// overflow for every B up to 2^31 - 1 (callable on the host, so this holds in
+// a CPU test near that size).
+template <typename Bound>
+__host__ __device__ __forceinline__ int32_t find_doc(const Bound& bound, int32_t B, int64_t v) {
+  int32_t lo = 0, hi = B - 1;
   while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
+    const int32_t mid = lo + ((hi - lo + 1) >> 1);
     if ((int64_t)bound[mid] <= v) lo = mid; else hi = mid - 1;
   }
   return lo;

@@ -44,9 +44,10 @@ build_meta_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t T, int32_t 
   __syncthreads();
 
   int flags = 0;
-  int running = 0;  // packed-contiguous: boundaries kept so far
-  for (int base = 0; base <= B; base += kBlock) {
-    const int b = base + tid;
+  int64_t running = 0;  // packed-contiguous: boundaries kept so far
+  // 64-bit document indexes throughout: B + kBlock may exceed 2^31 - 1.
+  for (int64_t base = 0; base <= B; base += kBlock) {
+    const int64_t b = base + tid;
     const bool in = b <= B;
     const int32_t v = in ? cu[b] : 0;
     if (r == 0 && in) {
@@ -76,7 +77,7 @@ build_meta_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t T, int32_t 
         wave_prefix += (k < wave) ? c : 0;
         chunk_total += c;
       }
-      const int pos = 1 + running + wave_prefix + lane_prefix;
+      const int64_t pos = 1 + running + wave_prefix + lane_prefix;
       if (keep && pos <= B) lcu[pos] = (int32_t)((int64_t)v - lo);
       running += chunk_total;
       __syncthreads();  // s_wave_count is reused by the next chunk
@@ -84,10 +85,10 @@ build_meta_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t T, int32_t 
   }
 
   if (policy == CP_POLICY_PACKED_CONTIGUOUS) {
-    const int kept = running < B ? running : B;  // cannot exceed B-1 for valid input
+    const int64_t kept = running < B ? running : B;  // cannot exceed B-1 for valid input
     if (tid == 0) lcu[0] = 0;
-    for (int k = kept + 1 + tid; k <= B; k += kBlock) lcu[k] = (int32_t)n;
-    if (tid == 0) nloc[r] = (n == 0) ? 0 : (kept + 1 <= B ? kept + 1 : B);
+    for (int64_t k = kept + 1 + tid; k <= B; k += kBlock) lcu[k] = (int32_t)n;
+    if (tid == 0) nloc[r] = (n == 0) ? 0 : (int32_t)(kept + 1 <= B ? kept + 1 : B);
   } else {
     if (tid == 0) nloc[r] = B;
   }
@@ -163,7 +164,7 @@ build_attn_meta_kernel(cp_meta_header* h, int32_t B, int32_t W, char* __restrict
     const int32_t k = step == 0 ? r : 2 * W - 1 - r;  // the step's chunk index
     const int32_t two_w = 2 * W;
     int32_t max_c = 0;
-    for (int j = tid; j <= B; j += kBlock) {
+    for (int64_t j = tid; j <= B; j += kBlock) {
       const int32_t v = cu[j];
       const int32_t before = v / two_w;  // chunk length summed over documents 0..j-1
       cuq[j] = before;
@@ -193,7 +194,7 @@ build_attn_meta_kernel(cp_meta_header* h, int32_t B, int32_t W, char* __restrict
 
   // packed-contiguous: one step; the second record of a rank is empty.
   if (step == 1) {
-    for (int j = tid; j <= B; j += kBlock) {
+    for (int64_t j = tid; j <= B; j += kBlock) {
       cuq[j] = 0;
       cukv[j] = 0;
       qoff[j] = n;
@@ -213,7 +214,7 @@ build_attn_meta_kernel(cp_meta_header* h, int32_t B, int32_t W, char* __restrict
     back = first - doc_start;  // keys of the first segment before the rank's slice
   }
   int32_t max_q = 0, max_kv = 0;
-  for (int j = tid; j <= B; j += kBlock) {
+  for (int64_t j = tid; j <= B; j += kBlock) {
     const int32_t l = lcu[j];  // padded with n after entry m
     cuq[j] = l;
     qoff[j] = l;
@@ -239,10 +240,9 @@ build_attn_meta_kernel(cp_meta_header* h, int32_t B, int32_t W, char* __restrict
 
 }  // namespace
 
-hipError_t launch_build_attn_meta(const void* meta, int32_t B, int32_t W, void* attn, hipStream_t stream) {
+hipError_t launch_build_attn_meta(cp_meta_header* meta, int32_t B, int32_t W, void* attn, hipStream_t stream) {
   profile_before("build_attn_meta", stream);
-  hipLaunchKernelGGL(build_attn_meta_kernel, dim3(2 * W), dim3(kBlock), 0, stream,
-                     const_cast<cp_meta_header*>(static_cast<const cp_meta_header*>(meta)), B, W,
+  hipLaunchKernelGGL(build_attn_meta_kernel, dim3(2 * W), dim3(kBlock), 0, stream, meta, B, W,
                      static_cast<char*>(attn));
   hipError_t e = hipGetLastError();
   profile_after(stream);
