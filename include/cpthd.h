@@ -90,8 +90,10 @@ enum cp_status {
   CP_ERR_ALIAS = 5,       /* an output overlaps an input or another output   */
   CP_ERR_HIP = 6,         /* a HIP runtime call failed                       */
   CP_ERR_TIMEOUT = 7,     /* device-reported: an epoch wait hit its limit    */
-  CP_ERR_META = 8         /* device-reported: invalid cu_seqlens, or a call
+  CP_ERR_META = 8,        /* device-reported: invalid cu_seqlens, or a call
                              that did not match its metadata                 */
+  CP_ERR_TOO_LARGE = 9    /* the call needs more workspace than the static
+                             one of cp_grad_return_noalloc holds             */
 };
 
 /* ownership policies ([PC] "Why" and commit messages) */
@@ -433,6 +435,36 @@ int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
  */
 int cp_slot_sum(int32_t num_slots, const void* const* slots, void* out, int64_t n_elems,
                 int32_t in_dtype, int32_t out_dtype, int32_t flags, cp_stream_t stream);
+
+/*
+ * cp_grad_return_noalloc - cp_grad_return for every rank in stream order
+ * (rank = CP_ALL_RANKS, no epochs), with the owner slots kept in the library's
+ * own static device workspace instead of caller buffers.  For callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The call allocates nothing; the
+ * workspace is one fixed array of CP_NOALLOC_SCRATCH_BYTES bytes on each GPU,
+ * reserved when the library's device code is loaded on that GPU and held until
+ * the process ends.
+ *
+ *   cp_size, n_tensors, grads, out, total_tokens, heads, head_dim, in_dtype,
+ *   out_dtype, meta   as cp_grad_return (grads [n_tensors][W] inputs, out
+ *                     [n_tensors][W] outputs, every entry used)
+ *   flags             0 or CP_SUM_ACCUMULATE
+ * Slot [t][o][w] (T/W rows of writer w's tensor t for owner o) takes
+ * (T/W) * H * D * size(in_dtype) bytes rounded up to a multiple of 256;
+ * n_tensors * W * W slots must fit in CP_NOALLOC_SCRATCH_BYTES, else
+ * CP_ERR_TOO_LARGE and nothing is launched.  The results are the bits
+ * cp_grad_return gives with CP_ALL_RANKS, no epochs and the same flags.
+ * Every call on one GPU shares that GPU's workspace, which keeps the last
+ * call's slots: calls that overlap in time on one GPU (unordered streams, or
+ * several host threads) race and give undefined results.  Other errors as
+ * cp_grad_return.
+ */
+#define CP_NOALLOC_SCRATCH_BYTES 67108864 /* 64 MiB */
+int cp_grad_return_noalloc(int32_t cp_size, int32_t n_tensors, const void* const* grads,
+                           void* const* out, int64_t total_tokens, int32_t heads,
+                           int32_t head_dim, int32_t in_dtype, int32_t out_dtype, void* meta,
+                           int32_t flags, cp_stream_t stream);
 
 /* ------------------------------------------------------------ all-reduce */
 #define CP_ALLREDUCE_ONE_SHOT 0

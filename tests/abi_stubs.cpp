@@ -21,6 +21,10 @@ int ring_signal_tiles(const AllreduceArgs&, int64_t*) { return 0; }
 hipError_t launch_ring_signal(const AllreduceArgs&, const RingSignalArgs&, int, hipStream_t) {
   return hipErrorNotSupported;
 }
+hipError_t noalloc_scratch(void** p) {
+  *p = nullptr;
+  return hipErrorNotSupported;
+}
 hipError_t launch_epoch_publish(uint32_t*, int32_t, int32_t, uint32_t, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_epoch_wait(const uint32_t*, int32_t, int32_t, uint32_t, int64_t, cp_meta_header*, hipStream_t) {
   return hipErrorNotSupported;

@@ -48,7 +48,7 @@ static void* fake(void) {
   return choices[next() % 4];
 }
 
-static int known(int st) { return st >= CP_OK && st <= CP_ERR_META; }
+static int known(int st) { return st >= CP_OK && st <= CP_ERR_TOO_LARGE; }
 
 int main(int argc, char** argv) {
   int bad = 0;
@@ -85,6 +85,8 @@ int main(int argc, char** argv) {
                              pick64(), pick32(), NULL);
     st[n++] = cp_grad_return_fused(pick32(), pick32(), pick_small(-1, 8), ctable, table, pick64(), pick32(),
                                    pick32(), pick32(), pick32(), fake(), pick32(), NULL);
+    st[n++] = cp_grad_return_noalloc(pick32(), pick_small(-1, 8), ctable, table, pick64(), pick32(), pick32(),
+                                     pick32(), pick32(), fake(), pick32(), NULL);
     st[n++] = cp_slot_sum(pick32(), ctable, fake(), pick64(), pick32(), pick32(), pick32(), NULL);
     st[n++] = cp_allreduce(pick32(), pick32(), ctable, table, pick64(), pick32(), NULL);
     st[n++] = cp_allreduce_signal(pick32(), ctable, table, pick64(), pick32(), fake(), (size_t)pick64(),

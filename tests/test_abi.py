@@ -81,7 +81,7 @@ def test_attn_meta_bytes_closed_form(cp):
 
 
 def test_status_strings(cp):
-    for s in range(9):
+    for s in range(10):
         assert cp.cp_status_string(s) and cp.cp_status_string(s) != "unknown status"
     assert cp.cp_status_string(99) == "unknown status"
     assert cp.cp_version() >= 100
@@ -214,3 +214,31 @@ def test_library_has_no_oracle_dependency():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
                 assert "cp_oracle" not in text, f
+
+
+def test_noalloc_host_checks(cp):
+    """cp_grad_return_noalloc refuses, before any HIP call, slots that would not fit its
+    static workspace (CP_ERR_TOO_LARGE), as well as the argument errors cp_grad_return
+    refuses; an empty call is a no-op."""
+    lib = cp.lib
+    tab = (ctypes.c_void_p * 64)(*([0x10000] * 64))
+    na = lib.cp_grad_return_noalloc
+    # the S=262144 fp32 shape needs 2 x 16 slots of 640 MiB: far beyond 64 MiB
+    assert na(4, 2, tab, tab, 262144, 20, 128, cp.CP_F32, cp.CP_F32, FAKE, 0, None) == cp.CP_ERR_TOO_LARGE
+    # exactly at the limit passes the size check (then fails on the fake pointers),
+    # one 256-byte slot stride more does not
+    W, H, D = 4, 1, 64                       # 256-byte rows of fp32
+    rows_fit = cp.CP_NOALLOC_SCRATCH_BYTES // (W * W * 256)   # one tensor, slots of rows_fit rows
+    st_fit = na(W, 1, tab, tab, W * rows_fit, H, D, cp.CP_F32, cp.CP_F32, FAKE, 0, None)
+    assert st_fit in (cp.CP_ERR_DEVICE, cp.CP_ERR_HIP), st_fit
+    assert na(W, 1, tab, tab, W * (rows_fit + 1), H, D, cp.CP_F32, cp.CP_F32, FAKE, 0, None) \
+        == cp.CP_ERR_TOO_LARGE
+    assert na(W, 2, tab, tab, W * rows_fit, H, D, cp.CP_F32, cp.CP_F32, FAKE, 0, None) == cp.CP_ERR_TOO_LARGE
+    # argument errors shared with cp_grad_return
+    assert na(4, 2, tab, tab, 48, 2, 8, cp.CP_FP8_E4M3, cp.CP_F32, FAKE, 0, None) == cp.CP_ERR_UNSUPPORTED
+    assert na(0, 2, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, 0, None) == cp.CP_ERR_ARG
+    assert na(4, 0, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, 0, None) == cp.CP_ERR_ARG
+    assert na(4, 2, tab, tab, 46, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, 0, None) == cp.CP_ERR_SHAPE
+    assert na(4, 2, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, 0x20, None) == cp.CP_ERR_ARG
+    assert na(4, 2, None, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, 0, None) == cp.CP_ERR_ARG
+    assert na(4, 2, None, None, 0, 2, 8, cp.CP_F32, cp.CP_F32, None, 0, None) == cp.CP_OK

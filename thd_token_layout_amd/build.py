@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcpthd.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["meta.hip", "permute.hip", "reduce.hip", "allreduce.hip"]
+HIP_SOURCES = ["meta.hip", "permute.hip", "reduce.hip", "allreduce.hip", "scratch.hip"]
 HOST_SOURCES = ["abi.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]

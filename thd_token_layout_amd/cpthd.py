@@ -25,7 +25,7 @@ LIB_PATH = _LIB_PATH
 
 # ---------------------------------------------------------------- constants (cpthd.h)
 CP_OK, CP_ERR_ARG, CP_ERR_UNSUPPORTED, CP_ERR_SHAPE, CP_ERR_DEVICE = 0, 1, 2, 3, 4
-CP_ERR_ALIAS, CP_ERR_HIP, CP_ERR_TIMEOUT, CP_ERR_META = 5, 6, 7, 8
+CP_ERR_ALIAS, CP_ERR_HIP, CP_ERR_TIMEOUT, CP_ERR_META, CP_ERR_TOO_LARGE = 5, 6, 7, 8, 9
 CP_POLICY_DUAL_CHUNK_SWAP, CP_POLICY_PACKED_CONTIGUOUS = 0, 1
 CP_F32, CP_BF16, CP_F16, CP_FP8_E4M3, CP_FP8_E5M2 = 0, 1, 2, 3, 4
 CP_ALL_RANKS = -1
@@ -33,6 +33,7 @@ CP_MAX_CP_SIZE = 64
 CP_PHASE_SCATTER, CP_PHASE_PUBLISH, CP_PHASE_WAIT, CP_PHASE_SUM = 0x1, 0x2, 0x4, 0x8
 CP_PHASE_ALL = 0xF
 CP_SUM_ACCUMULATE = 0x10
+CP_NOALLOC_SCRATCH_BYTES = 64 << 20
 CP_META_MAGIC = 0x48545043
 CP_META_FIRST_NOT_ZERO = 0x0001
 CP_META_DECREASING = 0x0002
@@ -74,6 +75,9 @@ lib.cp_gather_thd_multi.argtypes = [_i32, _c.POINTER(_vp), _c.POINTER(_vp), _i64
 lib.cp_grad_return.restype = _c.c_int
 lib.cp_grad_return.argtypes = [_i32, _i32, _i32, _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_vp),
                                _i64, _i32, _i32, _i32, _i32, _vp, _vp, _u32, _i64, _i32, _vp]
+lib.cp_grad_return_noalloc.restype = _c.c_int
+lib.cp_grad_return_noalloc.argtypes = [_i32, _i32, _c.POINTER(_vp), _c.POINTER(_vp), _i64, _i32, _i32, _i32,
+                                       _i32, _vp, _i32, _vp]
 lib.cp_grad_return_fused.restype = _c.c_int
 lib.cp_grad_return_fused.argtypes = [_i32, _i32, _i32, _c.POINTER(_vp), _c.POINTER(_vp), _i64, _i32,
                                      _i32, _i32, _i32, _vp, _i32, _vp]
@@ -354,6 +358,18 @@ def cp_grad_return_fused(grads, out, meta: Meta, rank: int = CP_ALL_RANKS, accum
     _check(st, "cp_grad_return_fused")
 
 
+def cp_grad_return_noalloc(grads, out, meta: Meta, accumulate: bool = False, stream=None) -> None:
+    """cp_grad_return for every rank in stream order with the owner slots in the library's
+    static device workspace: grads[t][w] [T,H,D], out[t][o] [T/W,H,D]."""
+    n_tensors = len(grads)
+    W = len(grads[0])
+    T, H, D = grads[0][0].shape
+    st = lib.cp_grad_return_noalloc(W, n_tensors, _table(_flat2(grads)), _table(_flat2(out)), T, H, D,
+                                    dtype_code(grads[0][0].dtype), dtype_code(out[0][0].dtype), meta.ptr(),
+                                    CP_SUM_ACCUMULATE if accumulate else 0, _stream(stream, grads[0][0]))
+    _check(st, "cp_grad_return_noalloc")
+
+
 def cp_slot_sum(slots: Sequence[torch.Tensor], out: torch.Tensor, accumulate: bool = False,
                 stream=None) -> torch.Tensor:
     st = lib.cp_slot_sum(len(slots), _table(slots), _ptr(out), out.numel(),
@@ -442,7 +458,7 @@ def cp_profile_read(capacity: int = 64):
 EXPORTED = ["cp_meta_bytes", "cp_build_meta", "cp_meta_status", "cp_attn_meta_bytes", "cp_build_attn_meta",
             "cp_partition_thd", "cp_gather_thd",
             "cp_partition_thd_multi", "cp_gather_thd_multi",
-            "cp_grad_return", "cp_grad_return_fused", "cp_slot_sum", "cp_allreduce",
+            "cp_grad_return", "cp_grad_return_noalloc", "cp_grad_return_fused", "cp_slot_sum", "cp_allreduce",
             "cp_allreduce_signal_bytes", "cp_allreduce_signal", "cp_allreduce_signal_status",
             "cp_status_string", "cp_version",
             "cp_profile_enable", "cp_profile_read"]

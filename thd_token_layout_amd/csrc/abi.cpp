@@ -576,6 +576,62 @@ int cp_grad_return(int32_t rank, int32_t cp_size, int32_t n_tensors, const void*
                               phases, reinterpret_cast<hipStream_t>(stream));
 }
 
+int cp_grad_return_noalloc(int32_t cp_size, int32_t n_tensors, const void* const* grads,
+                           void* const* out, int64_t total_tokens, int32_t heads, int32_t head_dim,
+                           int32_t in_dtype, int32_t out_dtype, void* meta, int32_t flags,
+                           cp_stream_t stream) {
+  int st;
+  if ((st = grad_scalar_checks(CP_ALL_RANKS, cp_size, n_tensors, total_tokens, heads, head_dim, in_dtype,
+                               out_dtype, meta)) != CP_OK)
+    return st;
+  if ((flags & ~CP_SUM_ACCUMULATE) != 0) return CP_ERR_ARG;
+  if (total_tokens == 0) return CP_OK;  // nothing to move; empty tensors may have NULL data
+  if (grads == nullptr || out == nullptr) return CP_ERR_ARG;
+  const int W = cp_size;
+  const int64_t n = total_tokens / W;
+  const int64_t row_elems = (int64_t)heads * head_dim;
+  const int64_t in_row = row_elems * dtype_bytes(in_dtype);
+  const int64_t out_row = row_elems * dtype_bytes(out_dtype);
+  // Slot [t][o][w] at ((t W + o) W + w) * stride in the static workspace; every
+  // slot starts 256-byte aligned.  Sizes beyond the workspace are refused.
+  const int64_t slot_bytes = checked_bytes(n, in_row);
+  if (slot_bytes < 0 || slot_bytes > kNoallocScratchBytes) return CP_ERR_TOO_LARGE;
+  const int64_t stride = (slot_bytes + 255) / 256 * 256;
+  const int64_t slots_per_tensor = (int64_t)W * W;
+  if ((int64_t)n_tensors > kNoallocScratchBytes / (slots_per_tensor * stride)) return CP_ERR_TOO_LARGE;
+  for (int t = 0; t < n_tensors; ++t)
+    for (int w = 0; w < W; ++w)
+      if (grads[(size_t)t * W + w] == nullptr || out[(size_t)t * W + w] == nullptr) return CP_ERR_ARG;
+  int dev;
+  if ((st = current_device(&dev)) != CP_OK) return st;
+  AllocCache cache;
+  const MetaSpan ms = meta_span(meta, total_tokens, W, -1);
+  if ((st = check_device_buf(meta, ms.bytes, dev, &cache)) != CP_OK) return st;
+  std::vector<Range> ins{ms.tables}, outs{ms.header};
+  for (int t = 0; t < n_tensors; ++t) {
+    for (int w = 0; w < W; ++w) {
+      const void* g = grads[(size_t)t * W + w];
+      if ((st = check_device_buf(g, total_tokens * in_row, dev, &cache)) != CP_OK) return st;
+      ins.push_back(range_of(g, total_tokens * in_row));
+      void* p = out[(size_t)t * W + w];
+      if ((st = check_device_buf(p, n * out_row, dev, &cache)) != CP_OK) return st;
+      outs.push_back(range_of(p, n * out_row));
+    }
+  }
+  if ((st = check_alias(outs, ins)) != CP_OK) return st;
+  // The workspace's device address on this device (never the host-side name).
+  void* base = nullptr;
+  if ((st = hip_status(noalloc_scratch(&base))) != CP_OK) return st;
+  char* const ws = static_cast<char*>(base);
+  auto S = [&](int t, int o, int w) -> void* {
+    return ws + (((int64_t)t * W + o) * W + w) * stride;
+  };
+  return grad_return_launches(-1, W, n_tensors, grads, S, out, total_tokens, in_row, row_elems, in_dtype,
+                              out_dtype, static_cast<cp_meta_header*>(meta), nullptr, 0, 0,
+                              CP_PHASE_SCATTER | CP_PHASE_SUM | (flags & CP_SUM_ACCUMULATE),
+                              reinterpret_cast<hipStream_t>(stream));
+}
+
 int cp_grad_return_fused(int32_t rank, int32_t cp_size, int32_t n_tensors,
                          const void* const* grads, void* const* out, int64_t total_tokens,
                          int32_t heads, int32_t head_dim, int32_t in_dtype, int32_t out_dtype,
@@ -809,6 +865,7 @@ const char* cp_status_string(int status) {
     case CP_ERR_HIP: return "HIP runtime error";
     case CP_ERR_TIMEOUT: return "epoch wait timed out";
     case CP_ERR_META: return "invalid metadata or call/metadata mismatch";
+    case CP_ERR_TOO_LARGE: return "the call needs more than the static workspace holds";
     default: return "unknown status";
   }
 }

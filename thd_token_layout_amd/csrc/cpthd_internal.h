@@ -174,6 +174,13 @@ hipError_t launch_epoch_publish(uint32_t* epochs, int32_t W, int32_t writer, uin
 hipError_t launch_epoch_wait(const uint32_t* epochs, int32_t W, int32_t owner, uint32_t epoch,
                              int64_t timeout_ticks, cp_meta_header* meta, hipStream_t stream);
 
+// ---------------------------------------------------------------- static workspace
+// Device address (on the current device) of the library's static workspace of
+// kNoallocScratchBytes bytes, 256-byte aligned (scratch.hip); looked up once
+// per device.
+constexpr int64_t kNoallocScratchBytes = (int64_t)CP_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** ptr);
+
 // ---------------------------------------------------------------- timing hooks
 // Called by every launch function around its kernel launch.
 void profile_before(const char* name, hipStream_t stream);
