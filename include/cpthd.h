@@ -480,8 +480,8 @@ int cp_grad_return_noalloc(int32_t cp_size, int32_t n_tensors, const void* const
  *       them in rank order 0..W-1 in fp32 (seeded with in[0]), rounding once
  *       to dtype.  Every rank's out holds the same bits as cp_slot_sum.
  *   CP_ALLREDUCE_RING      the buffer is cut into W chunks of q elements,
- *       q = 64 * ceil(n_elems / (64 W)) (chunk c = [c q, (c+1) q) clipped to
- *       n_elems; trailing chunks may be empty).  Reduce-scatter: W-1 steps;
+ *       q = ceil(n_elems / W) (chunk c = [c q, (c+1) q) clipped to n_elems;
+ *       the last non-empty chunk may be shorter, trailing chunks empty).  Reduce-scatter: W-1 steps;
  *       in step s rank r takes chunk (r-1-s) mod W from rank r-1 (rank r-1's
  *       input at s = 0, its out after) and writes that plus its own input
  *       chunk, added in fp32 and rounded to dtype, into out[r].  Chunk c is

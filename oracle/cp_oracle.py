@@ -54,7 +54,8 @@ Readings where the pages are silent (the design notes list them all):
   * the all-reduce algorithms take their textbook forms: one-shot = every
     rank sums all W buffers in rank order, fp32, one rounding; ring = a
     reduce-scatter then an all-gather of W-1 steps each, passing to rank r+1,
-    over W chunks of a 64-element-aligned length; ring partials travel in the
+    over W chunks of ceil(n/W) elements (the last ones shorter or empty); ring
+    partials travel in the
     buffer type (a bf16 ring rounds after every add); the two-shot (not named by
     the pages; the direct two-step algorithm between the two) reduces chunk c at
     rank c in rank order, then every rank copies every reduced chunk.
@@ -493,14 +494,12 @@ def epochs_after(cp_size, epoch):
 #     bf16 ring rounds after every add.
 # Buffers are one-dimensional arrays of n elements (f32, or bf16 as uint16).
 # --------------------------------------------------------------------------
-RING_CHUNK_ALIGN = 64  # elements
-
-
 def ring_chunks(n, cp_size):
-    """Chunk k of the ring is [min(k*q, n), min((k+1)*q, n)), q = n/W rounded
-    up to a multiple of 64 elements (chunk starts stay 256-byte aligned for
-    fp32); trailing chunks may be empty for small n."""
-    q = -(-n // (RING_CHUNK_ALIGN * cp_size)) * RING_CHUNK_ALIGN
+    """The buffer cut into W chunks for the ring: chunk k is
+    [min(k*q, n), min((k+1)*q, n)) with q = ceil(n / W), the plain equal split.
+    Every chunk but the last non-empty one holds q elements; trailing chunks are
+    empty when (W-1)*q >= n (for instance n = 9, W = 4, or n < W)."""
+    q = -(-n // cp_size)
     return [(min(k * q, n), min((k + 1) * q, n)) for k in range(cp_size)]
 
 

@@ -496,12 +496,17 @@ def check_attention_meta_closed_forms(o):
 
 # ---------------------------------------------------------------- all-reduce (one-shot, ring)
 def check_ring_chunks(o):
-    # hand-worked: 64-element granules, W chunks covering [0, n), empties at the end
-    assert o.ring_chunks(300, 8) == [(0, 64), (64, 128), (128, 192), (192, 256), (256, 300),
-                                     (300, 300), (300, 300), (300, 300)]
+    # hand-worked: the plain equal split, q = ceil(n / W) elements per chunk,
+    # W chunks covering [0, n), the last non-empty one shorter, empties at the end
+    assert o.ring_chunks(300, 8) == [(0, 38), (38, 76), (76, 114), (114, 152), (152, 190),
+                                     (190, 228), (228, 266), (266, 300)]
+    assert o.ring_chunks(10, 4) == [(0, 3), (3, 6), (6, 9), (9, 10)]
+    assert o.ring_chunks(9, 4) == [(0, 3), (3, 6), (6, 9), (9, 9)]
+    assert o.ring_chunks(5, 8) == [(0, 1), (1, 2), (2, 3), (3, 4), (4, 5), (5, 5), (5, 5), (5, 5)]
     assert o.ring_chunks(1, 4) == [(0, 1), (1, 1), (1, 1), (1, 1)]
     assert o.ring_chunks(0, 3) == [(0, 0), (0, 0), (0, 0)]
     assert o.ring_chunks(4194304, 8)[1] == (524288, 1048576)   # 16 MiB of fp32, 8 ranks
+    assert o.ring_chunks(100003, 7)[6] == (85722, 100003)      # q = 14287
     assert o.ring_chunks(1000, 1) == [(0, 1000)]
     for n in (0, 1, 63, 64, 65, 511, 512, 4097, 100000):
         for W in (1, 2, 3, 7, 8, 16):
@@ -512,13 +517,13 @@ def check_ring_chunks(o):
             full = [L for L in lens if L > 0]
             assert lens[:len(full)] == full           # empty chunks only at the end
             if len(full) <= 1:
-                assert n <= 64 or W == 1
+                assert n <= 1 or W == 1
             else:
                 # equal chunks but the last; their length is the smallest
-                # multiple of 64 with which W chunks cover n
+                # with which W chunks cover n
                 q = full[0]
                 assert all(L == q for L in full[:-1]) and 0 < full[-1] <= q
-                assert q % 64 == 0 and W * q >= n and W * (q - 64) < n
+                assert W * q >= n and W * (q - 1) < n
 
 
 def check_allreduce_integer(o):
@@ -612,9 +617,7 @@ def check_allreduce_rotated_sums(o, seed=12):
             ring = o.allreduce_ring(data, dt)
             one = o.allreduce_one_shot(data, dt)
             want = np.empty_like(data[0])
-            q = -(-n // (64 * W)) * 64
-            for k in range(W):
-                a, b = min(k * q, n), min((k + 1) * q, n)
+            for k, (a, b) in enumerate(o.ring_chunks(n, W)):  # pinned by check_ring_chunks
                 acc = data[k][a:b]
                 for j in range(1, W):
                     x = data[(k + j) % W][a:b]

@@ -309,10 +309,25 @@ def _ring_rank_order(o):
     return allreduce_ring
 
 
-def _ring_chunks_unaligned(o):
-    def ring_chunks(n, cp_size):
-        q = -(-n // cp_size)
+def _ring_chunks_floor(o):
+    def ring_chunks(n, cp_size):  # q = floor(n / W), the last chunk takes the rest
+        q = n // cp_size
+        return [(k * q, (k + 1) * q if k < cp_size - 1 else n) for k in range(cp_size)]
+    return ring_chunks
+
+
+def _ring_chunks_aligned(o):
+    def ring_chunks(n, cp_size):  # chunk length rounded up to 64 elements
+        q = -(-n // (64 * cp_size)) * 64
         return [(min(k * q, n), min((k + 1) * q, n)) for k in range(cp_size)]
+    return ring_chunks
+
+
+def _ring_chunks_balanced(o):
+    def ring_chunks(n, cp_size):  # the first n % W chunks one element longer
+        q, rem = divmod(n, cp_size)
+        bounds = [k * q + min(k, rem) for k in range(cp_size + 1)]
+        return [(bounds[k], bounds[k + 1]) for k in range(cp_size)]
     return ring_chunks
 
 
@@ -379,7 +394,9 @@ MUTATIONS = {
     "ring_bf16_rounds_once": ("allreduce_ring", _ring_bf16_rounds_once),
     "ring_short_allgather": ("allreduce_ring", _ring_short_allgather),
     "ring_in_rank_order": ("allreduce_ring", _ring_rank_order),
-    "ring_chunks_unaligned": ("ring_chunks", _ring_chunks_unaligned),
+    "ring_chunks_floor": ("ring_chunks", _ring_chunks_floor),
+    "ring_chunks_aligned": ("ring_chunks", _ring_chunks_aligned),
+    "ring_chunks_balanced": ("ring_chunks", _ring_chunks_balanced),
     "one_shot_reversed": ("allreduce_one_shot", _one_shot_reversed),
     "two_shot_wrong_owner": ("allreduce_two_shot", _two_shot_wrong_owner),
     "two_shot_no_gather": ("allreduce_two_shot", _two_shot_no_gather),

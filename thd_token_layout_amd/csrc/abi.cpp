@@ -763,8 +763,7 @@ int cp_allreduce(int32_t algo, int32_t cp_size, const void* const* in, void* con
   a.cp_size = cp_size;
   a.n_elems = n_elems;
   a.dtype = dtype;
-  const int64_t granule = 64 * (int64_t)cp_size;
-  a.chunk = (n_elems + granule - 1) / granule * 64;
+  a.chunk = (n_elems + cp_size - 1) / cp_size;  // the ring's chunks: ceil(n / W) elements
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (algo == CP_ALLREDUCE_ONE_SHOT) return hip_status(launch_allreduce_one_shot(a, s));
   if (algo == CP_ALLREDUCE_TWO_SHOT) return hip_status(launch_allreduce_two_shot(a, s));
@@ -819,8 +818,7 @@ int cp_allreduce_signal(int32_t cp_size, const void* const* in, void* const* out
   a.cp_size = cp_size;
   a.n_elems = n_elems;
   a.dtype = dtype;
-  const int64_t granule = 64 * (int64_t)cp_size;
-  a.chunk = (n_elems + granule - 1) / granule * 64;
+  a.chunk = (n_elems + cp_size - 1) / cp_size;  // the ring's chunks: ceil(n / W) elements
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (cp_size == 1) return hip_status(launch_ring_gather_step(a, 0, true, s));
   RingSignalArgs g;

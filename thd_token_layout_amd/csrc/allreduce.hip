@@ -9,6 +9,39 @@
 namespace cpthd {
 namespace {
 
+// ---- element ranges that start anywhere -------------------------------------------
+// The ring's chunks start at multiples of ceil(n / W) elements, so a chunk need
+// not start on a 16-byte boundary even when every buffer does.  A range
+// [lo, hi) is split into a head [lo, vlo) up to the first 16-byte boundary, a
+// vector section [vlo, vend) of whole unit groups, and a tail [vend, hi); the
+// head and tail are done element by element.  Without the vector path the whole
+// range is scalar (vlo = vend = lo).
+struct Span {
+  int64_t lo, vlo, vend, hi;
+  int64_t nunits;  // vector units (8 elements, or 16 bytes for copies) in [vlo, vend)
+};
+
+// A = elements per 16 bytes, G = elements per vector unit group, U = elements per unit.
+template <int64_t A, int64_t G, int64_t U>
+__device__ __forceinline__ Span split_span(int64_t lo, int64_t hi, bool vec) {
+  Span s{lo, lo, lo, hi, 0};
+  if (!vec || hi <= lo) return s;
+  int64_t v = (lo + A - 1) / A * A;
+  if (v > hi) v = hi;
+  s.vlo = v;
+  s.nunits = (hi - v) / G * (G / U);
+  s.vend = v + s.nunits * U;
+  return s;
+}
+__device__ __forceinline__ int64_t span_scalar_count(const Span& s) { return (s.vlo - s.lo) + (s.hi - s.vend); }
+// Element index of the j-th scalar element: the head first, then the tail.
+__device__ __forceinline__ int64_t span_scalar(const Span& s, int64_t j) {
+  const int64_t h = s.vlo - s.lo;
+  return j < h ? s.lo + j : s.vend + (j - h);
+}
+template <int T>
+constexpr int64_t elems_per_16B() { return T == CP_F32 ? 4 : 8; }
+
 // ---- all-reduce: one-shot, ring, two-shot ----------------------------------------
 // "Low Latency Communication Kernels with NVSHMEM": the all-reduce algorithms
 // picked by message size and the exercise comparing a one-shot all-reduce
@@ -30,19 +63,17 @@ __global__ void __launch_bounds__(kBlock) allreduce_one_shot_kernel(AllreduceArg
   const int W = a.cp_size;
   const int r = blockIdx.y;
   constexpr int64_t eb = T == CP_F32 ? 4 : 2;
-  int64_t lo = 0, len = a.n_elems;
+  int64_t lo = 0, hi = a.n_elems;
   if constexpr (CHUNKED) {
     lo = (int64_t)r * a.chunk < a.n_elems ? (int64_t)r * a.chunk : a.n_elems;
-    const int64_t hi = lo + a.chunk < a.n_elems ? lo + a.chunk : a.n_elems;
-    len = hi - lo;
+    hi = lo + a.chunk < a.n_elems ? lo + a.chunk : a.n_elems;
   }
-  const int64_t off0 = lo * eb;
-  char* const out = a.out.p[r] + off0;
   constexpr bool SPLIT = split_layout<T, T>();
-  int64_t done = 0;
+  const Span sp = split_span<elems_per_16B<T>(), unit_group_elems<T, T>(), 8>(lo, hi, VEC);
+  const int64_t off0 = sp.vlo * eb;
+  char* const out = a.out.p[r] + off0;
   if constexpr (VEC) {
-    constexpr int64_t G = unit_group_elems<T, T>();
-    const int64_t nunits = len / G * (G / 8);
+    const int64_t nunits = sp.nunits;
     const int64_t ntiles = (nunits + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
       int64_t unit[UPT], off[UPT];
@@ -59,13 +90,14 @@ __global__ void __launch_bounds__(kBlock) allreduce_one_shot_kernel(AllreduceArg
       for (int u = 0; u < UPT; ++u)
         if (ok[u]) store_unit<T, SPLIT>(out, unit[u], acc[u]);
     }
-    done = nunits * 8;
   }
   const int64_t gstride = (int64_t)gridDim.x * kBlock;
-  for (int64_t k = done + (int64_t)blockIdx.x * kBlock + threadIdx.x; k < len; k += gstride) {
-    float acc = load_elem<T>(a.in.p[0] + off0, k);
-    for (int w = 1; w < W; ++w) acc = acc + load_elem<T>(a.in.p[w] + off0, k);
-    store_elem<T>(out, k, acc);
+  const int64_t nscalar = span_scalar_count(sp);
+  for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < nscalar; j += gstride) {
+    const int64_t k = span_scalar(sp, j);
+    float acc = load_elem<T>(a.in.p[0], k);
+    for (int w = 1; w < W; ++w) acc = acc + load_elem<T>(a.in.p[w], k);
+    store_elem<T>(a.out.p[r], k, acc);
   }
 }
 
@@ -88,16 +120,15 @@ __global__ void __launch_bounds__(kBlock) ring_reduce_step_kernel(AllreduceArgs 
   const int c = ((r - 1 - step) % W + W) % W;
   int64_t lo, hi;
   ring_chunk(a, c, lo, hi);
-  const int64_t len = hi - lo;
   constexpr int64_t eb = T == CP_F32 ? 4 : 2;
-  const char* const recv = (step == 0 ? a.in.p[prev] : a.out.p[prev]) + lo * eb;
-  const char* const own = a.in.p[r] + lo * eb;
-  char* const dst = a.out.p[r] + lo * eb;
+  const Span sp = split_span<elems_per_16B<T>(), unit_group_elems<T, T>(), 8>(lo, hi, VEC);
+  const char* const recv_base = step == 0 ? a.in.p[prev] : a.out.p[prev];
+  const char* const recv = recv_base + sp.vlo * eb;
+  const char* const own = a.in.p[r] + sp.vlo * eb;
+  char* const dst = a.out.p[r] + sp.vlo * eb;
   constexpr bool SPLIT = split_layout<T, T>();
-  int64_t done = 0;
   if constexpr (VEC) {
-    constexpr int64_t G = unit_group_elems<T, T>();
-    const int64_t nunits = len / G * (G / 8);
+    const int64_t nunits = sp.nunits;
     const int64_t ntiles = (nunits + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
       F8 x[UPT], y[UPT];
@@ -120,25 +151,27 @@ __global__ void __launch_bounds__(kBlock) ring_reduce_step_kernel(AllreduceArgs 
           store_unit<T, SPLIT>(dst, unit[u], x[u]);
         }
     }
-    done = nunits * 8;
   }
   const int64_t gstride = (int64_t)gridDim.x * kBlock;
-  for (int64_t k = done + (int64_t)blockIdx.x * kBlock + threadIdx.x; k < len; k += gstride)
-    store_elem<T>(dst, k, load_elem<T>(recv, k) + load_elem<T>(own, k));
+  const int64_t nscalar = span_scalar_count(sp);
+  for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < nscalar; j += gstride) {
+    const int64_t k = span_scalar(sp, j);
+    store_elem<T>(a.out.p[r], k, load_elem<T>(recv_base, k) + load_elem<T>(a.in.p[r], k));
+  }
 }
 
-// Copy len elements of EB bytes from src to dst, bit for bit: 16-byte units
-// (4 per thread and tile) when VEC, then the tail element by element; tiles
-// over blockIdx.x.
+// Copy elements [lo, hi) of EB bytes from buffer src to buffer dst, bit for
+// bit: 16-byte units (4 per thread and tile) from the first 16-byte boundary
+// when VEC, the head and tail element by element; tiles over blockIdx.x.
 template <int EB, bool VEC>
-__device__ __forceinline__ void copy_span(const char* src, char* dst, int64_t len) {
-  int64_t done = 0;
+__device__ __forceinline__ void copy_range(const char* src, char* dst, int64_t lo, int64_t hi) {
+  const Span sp = split_span<16 / EB, 16 / EB, 16 / EB>(lo, hi, VEC);
   if constexpr (VEC) {
     constexpr int kUpt = 4;
-    const int64_t n16 = len * EB / 16;
+    const int64_t n16 = sp.nunits;
     const int64_t ntiles = (n16 + (int64_t)kBlock * kUpt - 1) / ((int64_t)kBlock * kUpt);
-    const u32x4* s16 = reinterpret_cast<const u32x4*>(src);
-    u32x4* d16 = reinterpret_cast<u32x4*>(dst);
+    const u32x4* s16 = reinterpret_cast<const u32x4*>(src + sp.vlo * EB);
+    u32x4* d16 = reinterpret_cast<u32x4*>(dst + sp.vlo * EB);
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
       u32x4 v[kUpt];
       int64_t unit[kUpt];
@@ -151,13 +184,16 @@ __device__ __forceinline__ void copy_span(const char* src, char* dst, int64_t le
       for (int u = 0; u < kUpt; ++u)
         if (unit[u] < n16) __builtin_nontemporal_store(v[u], d16 + unit[u]);
     }
-    done = n16 * 16 / EB;
   }
   typedef typename std::conditional<EB == 4, unsigned int, unsigned short>::type E;
   const E* se = reinterpret_cast<const E*>(src);
   E* de = reinterpret_cast<E*>(dst);
   const int64_t gstride = (int64_t)gridDim.x * kBlock;
-  for (int64_t k = done + (int64_t)blockIdx.x * kBlock + threadIdx.x; k < len; k += gstride) de[k] = se[k];
+  const int64_t nscalar = span_scalar_count(sp);
+  for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < nscalar; j += gstride) {
+    const int64_t k = span_scalar(sp, j);
+    de[k] = se[k];
+  }
 }
 
 // Ring all-gather step: rank r copies chunk c = (r-step) mod W from rank
@@ -170,7 +206,7 @@ __global__ void __launch_bounds__(kBlock) ring_gather_step_kernel(AllreduceArgs 
   const int c = ((r - step) % W + W) % W;
   int64_t lo, hi;
   ring_chunk(a, c, lo, hi);
-  copy_span<EB, VEC>((FROM_IN ? a.in.p[r] : a.out.p[prev]) + lo * EB, a.out.p[r] + lo * EB, hi - lo);
+  copy_range<EB, VEC>(FROM_IN ? a.in.p[r] : a.out.p[prev], a.out.p[r], lo, hi);
 }
 
 // Two-shot all-gather: rank r (blockIdx.y) copies chunk c = (r+1+z) mod W
@@ -182,7 +218,7 @@ __global__ void __launch_bounds__(kBlock) two_shot_gather_kernel(AllreduceArgs a
   const int c = (r + 1 + (int)blockIdx.z) % W;
   int64_t lo, hi;
   ring_chunk(a, c, lo, hi);
-  copy_span<EB, VEC>(a.out.p[c] + lo * EB, a.out.p[r] + lo * EB, hi - lo);
+  copy_range<EB, VEC>(a.out.p[c], a.out.p[r], lo, hi);
 }
 
 // The ring in one launch (the persistent, in-kernel-signalling form of the
@@ -268,12 +304,13 @@ __global__ void __launch_bounds__(kBlock) ring_signal_kernel(AllreduceArgs a, Ri
     if (tlo > hi) tlo = hi;
     int64_t thi = tlo + g.tile_elems;
     if (thi > hi) thi = hi;
-    const int64_t len = thi - tlo;
-    char* const dst = out_mine + tlo * eb;
     if (reduce) {
-      const char* const recv = (s == 0 ? in_prev : out_prev) + tlo * eb;
-      const char* const own = in_mine + tlo * eb;
-      const int64_t nunits = vec ? len / G * (G / 8) : 0;
+      const Span sp = split_span<elems_per_16B<T>(), G, 8>(tlo, thi, vec);
+      const char* const recv_base = s == 0 ? in_prev : out_prev;
+      const char* const recv = recv_base + sp.vlo * eb;
+      const char* const own = in_mine + sp.vlo * eb;
+      char* const dst = out_mine + sp.vlo * eb;
+      const int64_t nunits = sp.nunits;
       constexpr int kU = 4;  // units in flight per thread
       for (int64_t u0 = threadIdx.x; u0 < nunits; u0 += kBlock * kU) {
         F8 x[kU], y[kU];
@@ -295,11 +332,16 @@ __global__ void __launch_bounds__(kBlock) ring_signal_kernel(AllreduceArgs a, Ri
           }
         }
       }
-      for (int64_t q = nunits * 8 + threadIdx.x; q < len; q += kBlock)
-        store_elem<T>(dst, q, load_elem<T>(recv, q) + load_elem<T>(own, q));
+      const int64_t nscalar = span_scalar_count(sp);
+      for (int64_t j = threadIdx.x; j < nscalar; j += kBlock) {
+        const int64_t q = span_scalar(sp, j);
+        store_elem<T>(out_mine, q, load_elem<T>(recv_base, q) + load_elem<T>(in_mine, q));
+      }
     } else {
-      const char* const src = out_prev + tlo * eb;
-      const int64_t n16 = vec ? len * eb / 16 : 0;
+      const Span sp = split_span<16 / eb, 16 / eb, 16 / eb>(tlo, thi, vec);
+      const char* const src = out_prev + sp.vlo * eb;
+      char* const dst = out_mine + sp.vlo * eb;
+      const int64_t n16 = sp.nunits;
       constexpr int kC = 8;  // 16-byte units in flight per thread
       for (int64_t u0 = threadIdx.x; u0 < n16; u0 += kBlock * kC) {
         u32x4 v[kC];
@@ -315,8 +357,11 @@ __global__ void __launch_bounds__(kBlock) ring_signal_kernel(AllreduceArgs a, Ri
         }
       }
       typedef typename std::conditional<eb == 4, unsigned int, unsigned short>::type E;
-      for (int64_t q = n16 * 16 / eb + threadIdx.x; q < len; q += kBlock)
-        reinterpret_cast<E*>(dst)[q] = reinterpret_cast<const E*>(src)[q];
+      const int64_t nscalar = span_scalar_count(sp);
+      for (int64_t j = threadIdx.x; j < nscalar; j += kBlock) {
+        const int64_t q = span_scalar(sp, j);
+        reinterpret_cast<E*>(out_mine)[q] = reinterpret_cast<const E*>(out_prev)[q];
+      }
     }
     // The barrier completes every wave's stores into this XCD's L2; lane 0's
     // agent-scope release then writes the L2 back before the flag is stored.

@@ -130,7 +130,7 @@ struct AllreduceArgs {
   RankPtrs out;       // [W] outputs, n elements each (ring: the working buffers)
   int32_t cp_size;
   int64_t n_elems;
-  int64_t chunk;      // ring chunk length in elements (a multiple of 64)
+  int64_t chunk;      // ring chunk length in elements, ceil(n / W); chunks start anywhere
   int32_t dtype;      // CP_F32 or CP_BF16, inputs and outputs alike
   int32_t vec;        // all pointers 16-byte aligned (set by the launch functions)
 };
