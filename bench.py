@@ -16,7 +16,9 @@ input already resident in HBM:
 
 Prints one JSON line: whole-step algorithmic HBM bytes / step time in GB/s,
 the roofline of the dominant kernel (HIP events on its launch stream over the
-timed region) and the CPU oracle's rate on a bounded sample of the same step.
+timed region) beside the ceiling a plain stream of the same read/write mix and
+size reaches on this GPU, and the CPU oracle's rate on the same step, on one
+core and on the host's cores.
 """
 from __future__ import annotations
 
@@ -65,10 +67,12 @@ class Step:
         self.workloads = (w_dcs, w_pc, w_gr)
         W = w_dcs.cp_size
         H, D = w_dcs.heads, w_dcs.head_dim
-        # ---- layout inputs (same Q,K,V under both policies: matched inputs)
-        cu_dcs = torch.from_numpy(WL.cu_seqlens(w_dcs)).to(dev)
-        cu_pc = torch.from_numpy(WL.cu_seqlens(w_pc)).to(dev)
-        cu_gr = torch.from_numpy(WL.cu_seqlens(w_gr)).to(dev)
+        # ---- layout inputs: the same Q, K, V under both policies, each policy with the
+        # document set of its own workload (dcs_s256k_w4: log-uniform lengths, multiples
+        # of 8; pc_s256k_w4: U{1..4096}).  per_config() also runs both policies on one
+        # document set, where the policy is the only difference.
+        self.cu_np = (WL.cu_seqlens(w_dcs), WL.cu_seqlens(w_pc), WL.cu_seqlens(w_gr))
+        cu_dcs, cu_pc, cu_gr = (torch.from_numpy(c).to(dev) for c in self.cu_np)
         self.num_docs = (cu_dcs.numel() - 1, cu_pc.numel() - 1)
         self.qkv = WL.random_tensors(w_dcs, 3, device=dev)
         self.parts = [torch.empty((W, S // W, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
@@ -130,6 +134,14 @@ class Step:
             "owner_sum": (Wg + 1) * n * row_f32,        # one owner, one tensor: read W slots, write 1
             "fused": (Wg + 1) * S * row_f32,            # one tensor, all owners
         }
+        # read/write mix of each kernel role: (inputs, bytes per input and of the output),
+        # for the plain stream that bounds it
+        self.kernel_mix = {
+            "scatter": (1, S * row_f32),
+            "owner_sum": (Wg, n * row_f32),
+            "fused": (Wg, S * row_f32),
+            "layout": (1, S * row_bf16),
+        }
 
     @property
     def step_bytes(self) -> int:
@@ -143,29 +155,36 @@ class Step:
 def attribute_kernels(step: Step, cp, torch):
     """Run each op once with timing hooks on and map kernel name -> bytes per launch."""
     per_kernel = {}
+    mix = {}
     torch.cuda.synchronize()
     cp.cp_profile_enable(True)
     for name, nbytes, fn in step.ops:
         fn()
         prof = cp.cp_profile_read()
         for kname, (count, _) in prof.items():
+            role = None
             if name.startswith("grad_return dK"):
                 role = "scatter" if kname.startswith("permute") else \
                     "owner_sum" if kname.startswith("slot_sum") else None
                 b = step.kernel_bytes[role] if role else 0
             elif name.startswith("grad_return_fused"):
+                role = "fused"
                 b = step.kernel_bytes["fused"]
             elif name.startswith(("partition", "gather")):
                 b = nbytes / count  # Q, K, V: one launch each, or one launch for all three
+                if count == 3:
+                    role = "layout"
             elif name.startswith("slot_sum sweep"):
                 b = nbytes / count
             else:
                 b = 0
             per_kernel.setdefault(kname, []).append((count, b))
+            if role is not None:
+                mix[kname] = step.kernel_mix[role]
     cp.cp_profile_enable(False)
-    # bytes per step per kernel name
+    # bytes per step per kernel name, launches per step, stream mix per kernel name
     return {k: sum(c * b for c, b in v) for k, v in per_kernel.items()}, \
-        {k: sum(c for c, _ in v) for k, v in per_kernel.items()}
+        {k: sum(c for c, _ in v) for k, v in per_kernel.items()}, mix
 
 
 def counted_traffic(kernel: str):
@@ -192,56 +211,194 @@ def counted_traffic(kernel: str):
     return int(round(rec["traffic_bytes_per_launch"]))
 
 
-def cpu_baseline(S_sample: int, WL, passes: int = 3):
-    """The CPU oracle, as it stands, on the same step at S_sample tokens, `passes` times."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_inputs(step, torch):
+    """Host copies of the step's inputs for the CPU oracle (bf16 as uint16 bits)."""
     import numpy as np
-    import torch
+
+    def bits(t):
+        t = t.detach()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    return {"cu": step.cu_np, "qkv": [bits(x) for x in step.qkv],
+            "grads": [[bits(g) for g in gt] for gt in step.grads],
+            "sweep": [(nb, [bits(x) for x in slots]) for nb, slots, _ in step.sweep],
+            "S": step.S, "W": step.workloads[0].cp_size, "Wg": step.workloads[2].cp_size,
+            "row_bf16": step.workloads[0].heads * step.workloads[0].head_dim * 2,
+            "row_f32": step.workloads[2].heads * step.workloads[2].head_dim * 4}
+
+
+def cpu_baseline(h, step_bytes: int, threads: int):
+    """The CPU oracle, as it stands, on the whole step over the same inputs as the GPU
+    (S = 262144): metadata and attention-step tables, DCS and PC partition + gather of
+    Q, K, V, unfused and fused dK/dV gradient return, the W=8 sweep.  Timed once on one
+    thread and once with the work split over `threads` threads (numpy releases the GIL):
+    the items are independent oracle calls, one per tensor and policy for the layouts,
+    one per owner and tensor for the gradient returns (the oracle's owners= argument)."""
+    import time as _time
+    from concurrent.futures import ThreadPoolExecutor
 
     from oracle import cp_oracle as O
 
-    w_dcs, w_pc, w_gr = (WL.scaled(WL.WORKLOADS[n], total_tokens=S_sample)
-                         for n in ("dcs_s256k_w4", "pc_s256k_w4", "grad_s256k_w4"))
-    cu_dcs, cu_pc, cu_gr = WL.cu_seqlens(w_dcs), WL.cu_seqlens(w_pc), WL.cu_seqlens(w_gr)
-    qkv = [t.view(torch.int16).numpy().view(np.uint16) for t in WL.random_tensors(w_dcs, 3)]
-    Wg = w_gr.cp_size
-    vals = [t.numpy() for t in WL.random_tensors(w_gr, 2 * Wg)]
-    grads = [vals[:Wg], vals[Wg:]]
-    sweep_sizes = [nb for nb in WL.SWEEP_BYTES if nb <= (1 << 24)]
-    rng = np.random.default_rng(6)
-    sweep = [[rng.standard_normal(nb // 4).astype(np.float32) for _ in range(8)] for nb in sweep_sizes]
-    row_bf16 = w_dcs.heads * w_dcs.head_dim * 2
-    row_f32 = w_gr.heads * w_gr.head_dim * 4
-    nbytes = 0
-    t0 = time.perf_counter()
-    for _ in range(passes):
-        for cu, pol, W in ((cu_dcs, O.DUAL_CHUNK_SWAP, w_dcs.cp_size),
-                           (cu_pc, O.PACKED_CONTIGUOUS, w_pc.cp_size)):
-            O.local_cu_seqlens(cu, S_sample, W, pol)
-            O.attention_meta(cu, S_sample, W, pol)
-            for x in qkv:
-                parts = O.partition(x, cu, W, pol)
-                O.gather(parts, cu, W, pol)
-                nbytes += 2 * 2 * S_sample * row_bf16
-        for gt in grads:
-            O.grad_return(gt, cu_gr, Wg, "f32", "f32")
-            nbytes += (3 * Wg + 1) * S_sample * row_f32
-            O.grad_return_fused(gt, cu_gr, Wg, "f32", "f32")
-            nbytes += (Wg + 1) * S_sample * row_f32
-        for nb, s in zip(sweep_sizes, sweep):
-            O.slot_sum(s, "f32", "f32")
-            nbytes += 9 * nb
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} passes of the full step (metadata and attention-step tables, DCS and "
-                      f"PC partition+gather of "
-                      f"Q,K,V, unfused and fused dK/dV gradient return, W=8 sweep) at S={S_sample} "
-                      f"instead of 262144, same heads, head_dim, cp_size, dtypes and distributions; "
-                      f"numpy, one thread; {nbytes / 1e9:.2f} GB algorithmic in {dt:.1f} s"}
+    S, W, Wg = h["S"], h["W"], h["Wg"]
+    cu_dcs, cu_pc, cu_gr = h["cu"]
+    items = []
+    for cu, pol in ((cu_dcs, O.DUAL_CHUNK_SWAP), (cu_pc, O.PACKED_CONTIGUOUS)):
+        items.append(lambda cu=cu, pol=pol: (O.local_cu_seqlens(cu, S, W, pol), O.attention_meta(cu, S, W, pol)))
+        for x in h["qkv"]:
+            items.append(lambda x=x, cu=cu, pol=pol: O.gather(O.partition(x, cu, W, pol), cu, W, pol))
+    items.append(lambda: O.local_cu_seqlens(cu_gr, S, Wg, O.DUAL_CHUNK_SWAP))
+    for gt in h["grads"]:
+        for o in range(Wg):
+            items.append(lambda gt=gt, o=o: O.grad_return(gt, cu_gr, Wg, "f32", "f32", owners=[o]))
+            items.append(lambda gt=gt, o=o: O.grad_return_fused(gt, cu_gr, Wg, "f32", "f32", owners=[o]))
+    for _, slots in h["sweep"]:
+        items.append(lambda slots=slots: O.slot_sum(slots, "f32", "f32"))
+    order = list(range(len(items)))
+    res = {}
+    for n_thr in (1, threads):
+        t0 = _time.perf_counter()
+        if n_thr == 1:
+            for k in order:
+                items[k]()
+        else:
+            with ThreadPoolExecutor(max_workers=n_thr) as ex:
+                list(ex.map(lambda k: items[k](), order))
+        res[n_thr] = _time.perf_counter() - t0
+    one, many = res[1], res[threads]
+    return {"value": round(step_bytes / many / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "value_1core": round(step_bytes / one / 1e9, 3), "seconds_1core": round(one, 2),
+            "seconds_ncore": round(many, 2), "cpu_model": cpu_model(),
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"one pass of the whole step at S={S} (the GPU step's own inputs, copied to the host): "
+                      f"metadata and attention-step tables, DCS and PC partition+gather of Q,K,V "
+                      f"[{S},20,128] bf16, unfused and fused dK/dV gradient return W={Wg} [{S},20,128] fp32, "
+                      f"W=8 fp32 sweep 1 KiB..16 MiB; {step_bytes / 1e9:.1f} GB algorithmic; numpy oracle "
+                      f"timed on 1 thread ({one:.1f} s) and on {threads} threads ({many:.1f} s), "
+                      f"work split into {len(items)} independent oracle calls"}
 
 
-def per_config(cp, WL, torch, dev, reps: int = 10):
+def load_roofline_lib():
+    """libcpthd_roofline.so: plain streaming kernels under the library's schedule."""
+    import ctypes
+
+    path = os.path.join(ROOT, "thd_token_layout_amd", "libcpthd_roofline.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not built: run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.cprl_stream.restype = ctypes.c_int
+    lib.cprl_stream.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_int64,
+                                ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+class Ceiling:
+    """What a plain stream of a read/write mix reaches on this GPU: n_in inputs of
+    `nbytes` each read and (write) one output of `nbytes` written, by the streaming
+    kernels of libcpthd_roofline.so (full grid, contiguous tiles, 16-byte non-temporal
+    accesses, as the library's kernels), the best of 1, 2 and 3 units per thread (4, 8 and
+    12 KiB tiles).  Timed like per_config: median of `reps` launches per shape, each after
+    a 1 GiB write that flushes the last-level cache, with HIP events on the stream the
+    kernel is launched on.  Results are cached by mix."""
+
+    def __init__(self, torch, dev, reps: int = 10):
+        self.lib = load_roofline_lib()
+        self.torch, self.dev, self.reps = torch, dev, reps
+        self.cache = {}
+        self.flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        self.sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+
+    def rate(self, n_in: int, nbytes: int, write: bool = True):
+        import ctypes
+        import statistics
+
+        torch = self.torch
+        nbytes = (int(nbytes) + 15) // 16 * 16
+        key = (n_in, nbytes, write)
+        if key in self.cache:
+            return self.cache[key]
+        ins = [torch.empty(nbytes, dtype=torch.uint8, device=self.dev) for _ in range(n_in)]
+        out = torch.empty(nbytes, dtype=torch.uint8, device=self.dev) if write else None
+        tab = (ctypes.c_void_p * max(n_in, 1))(*[t.data_ptr() for t in ins])
+        outp = ctypes.c_void_p(out.data_ptr()) if write else None
+        sink = ctypes.c_void_p(self.sink.data_ptr())
+
+        def launch(np_):
+            stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            st = self.lib.cprl_stream(n_in, tab, outp, nbytes, np_, sink, stream)
+            if st != 0:
+                raise RuntimeError(f"cprl_stream: status {st}")
+
+        by_shape = {}
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for np_ in (1, 2, 3):
+            launch(np_)
+            ts = []
+            for _ in range(self.reps):
+                self.flush.fill_(1.0)
+                e0.record()
+                launch(np_)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1000.0)
+            by_shape[np_] = statistics.median(ts)
+        best = min(by_shape, key=by_shape.get)
+        us = by_shape[best]
+        moved = nbytes * (n_in + (1 if write else 0))
+        mix = f"{n_in}:{1 if write else 0}" if n_in else "0:1"
+        res = {"mix": mix, "bytes_per_buffer": nbytes, "moved_bytes": moved, "median_us": round(us, 2),
+               "gbs": round(moved / us / 1e3, 1), "units_per_thread": best,
+               "gbs_by_units_per_thread": {k: round(moved / v / 1e3, 1) for k, v in by_shape.items()}}
+        self.cache[key] = res
+        del ins, out
+        torch.cuda.empty_cache()
+        return res
+
+    def standard(self, S: int):
+        """The mixes and sizes of the step's kernels at S tokens, plus pure read and write."""
+        row_bf16, row_f32 = 20 * 128 * 2, 20 * 128 * 4
+        return {
+            "copy 1:1, one layout tensor (S x 5 KiB)": self.rate(1, S * row_bf16),
+            "copy 1:1, one writer's gradient (S x 10 KiB; the scatter)": self.rate(1, S * row_f32),
+            "4:1, four owner slots (S/4 x 10 KiB each; the owner sum)": self.rate(4, S // 4 * row_f32),
+            "4:1, four writers' gradients (S x 10 KiB each; the fused sum)": self.rate(4, S * row_f32),
+            "read only (S x 10 KiB)": self.rate(1, S * row_f32, write=False),
+            "write only (S x 10 KiB)": self.rate(0, S * row_f32),
+        }
+
+
+def attn_summary(cp, meta):
+    """Attention-step counts and sizes from the tables cp_build_attn_meta writes: steps per
+    rank, segments over all ranks and steps, summed query and key rows, longest key range."""
+    attn = cp.cp_build_attn_meta(meta)
+    magic, t = cp.read_attn_meta(attn, meta.num_docs, meta.cp_size)
+    if magic != cp.CP_ATTN_MAGIC:
+        raise RuntimeError("attention tables were not built")
+    seg = t["num_segments"]
+    return {"steps_per_rank": int((seg > 0).sum(dim=1).max()), "segments": int(seg.sum()),
+            "total_q": int(t["total_q"].sum()), "total_kv": int(t["total_kv"].sum()),
+            "max_seqlen_kv": int(t["max_seqlen_kv"].max())}
+
+
+def per_config(cp, WL, torch, dev, reps: int = 10, ceiling=None, names=None):
     """Each workload's ops timed on their own: median of `reps` HIP-event timings,
-    each preceded by a 1 GiB write that flushes the 256 MB last-level cache."""
+    each preceded by a 1 GiB write that flushes the 256 MB last-level cache.  With a
+    Ceiling, each single-kernel row also gets the plain stream of the same read/write mix
+    and size, and the row's fraction of it.  The dual-chunk-swap S=262144 workload is also
+    run under packed-contiguous ownership with the same documents and the same Q, K, V
+    (the policy the only difference), with each policy's attention-step tables summarised."""
     import statistics
 
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -260,32 +417,51 @@ def per_config(cp, WL, torch, dev, reps: int = 10):
             ts.append(e0.elapsed_time(e1) * 1000.0)
         return statistics.median(ts)
 
-    def add(cfg, op, nbytes, us):
-        results.append({"config": cfg, "op": op, "bytes": nbytes, "median_us": round(us, 1),
-                        "gbs": round(nbytes / us / 1e3, 1), "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+    def add(cfg, op, nbytes, us, mix=None, **extra):
+        row = {"config": cfg, "op": op, "bytes": nbytes, "median_us": round(us, 1),
+               "gbs": round(nbytes / us / 1e3, 1), "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        if ceiling is not None and mix is not None and nbytes:
+            c = ceiling.rate(*mix)
+            row["ceiling_gbs"] = c["gbs"]
+            row["frac_of_ceiling"] = round(row["gbs"] / c["gbs"], 4)
+        row.update(extra)
+        results.append(row)
 
-    for name in ("dcs_t32k_w4", "pc_t64k_w4", "dcs_s256k_w4", "pc_s256k_w4", "dcs1_s256k_w4"):
+    layout = ("dcs_t32k_w4", "pc_t64k_w4", "dcs_s256k_w4", "pc_s256k_w4", "dcs1_s256k_w4")
+    for name in layout:
+        if names and name not in names:
+            continue
         w = WL.WORKLOADS[name]
-        cu = torch.from_numpy(WL.cu_seqlens(w)).to(dev)
-        meta = cp.cp_build_meta(cu, w.total_tokens, w.cp_size, cp.POLICY[w.policy], check=True)
+        cu_np = WL.cu_seqlens(w)
+        cu = torch.from_numpy(cu_np).to(dev)
         xs = WL.random_tensors(w, w.n_tensors, device=dev)
         parts = [torch.empty((w.cp_size, w.total_tokens // w.cp_size, w.heads, w.head_dim),
                              dtype=x.dtype, device=dev) for x in xs]
         back = [torch.empty_like(x) for x in xs]
         nbytes = sum(2 * x.numel() * x.element_size() for x in xs)
-        add(name, "partition Q,K,V (multi-tensor call)", nbytes,
-            timed(lambda: cp.cp_partition_thd_multi(xs, meta, parts=parts)))
-        add(name, "gather Q,K,V (multi-tensor call)", nbytes,
-            timed(lambda: cp.cp_gather_thd_multi(parts, meta, xs=back)))
-        add(name, "partition Q,K,V (three single-tensor calls)", nbytes,
-            timed(lambda: [cp.cp_partition_thd(x, meta, parts=p) for x, p in zip(xs, parts)]))
-        add(name, "metadata", 0, timed(lambda: cp.cp_build_meta(cu, w.total_tokens, w.cp_size,
-                                                                  cp.POLICY[w.policy], meta=meta.buf)))
-        attn = cp.cp_build_attn_meta(meta)
-        add(name, "attention-step metadata", 0, timed(lambda: cp.cp_build_attn_meta(meta, attn=attn)))
+        policies = [(w.policy, cp.POLICY[w.policy])]
+        if name == "dcs_s256k_w4":  # matched inputs: the same documents and tensors under both policies
+            policies.append(("packed_contiguous", cp.CP_POLICY_PACKED_CONTIGUOUS))
+        for pname, pol in policies:
+            meta = cp.cp_build_meta(cu, w.total_tokens, w.cp_size, pol, check=True)
+            cfg = name if pol == cp.POLICY[w.policy] else f"{name} as packed_contiguous (same documents and Q,K,V)"
+            docs = {"documents": int(cu.numel() - 1), "attention": attn_summary(cp, meta)}
+            add(cfg, "partition Q,K,V (multi-tensor call)", nbytes,
+                timed(lambda: cp.cp_partition_thd_multi(xs, meta, parts=parts)), mix=(1, nbytes // 2), **docs)
+            add(cfg, "gather Q,K,V (multi-tensor call)", nbytes,
+                timed(lambda: cp.cp_gather_thd_multi(parts, meta, xs=back)), mix=(1, nbytes // 2))
+            add(cfg, "partition Q,K,V (three single-tensor calls)", nbytes,
+                timed(lambda: [cp.cp_partition_thd(x, meta, parts=p) for x, p in zip(xs, parts)]),
+                mix=(1, nbytes // 2))
+            add(cfg, "metadata", 0, timed(lambda: cp.cp_build_meta(cu, w.total_tokens, w.cp_size, pol,
+                                                                     meta=meta.buf)))
+            attn = cp.cp_build_attn_meta(meta)
+            add(cfg, "attention-step metadata", 0, timed(lambda: cp.cp_build_attn_meta(meta, attn=attn)))
         del xs, parts, back
         torch.cuda.empty_cache()
     for name in ("grad_s256k_w4", "fused_s128k_w8"):
+        if names and name not in names:
+            continue
         w = WL.WORKLOADS[name]
         W, S = w.cp_size, w.total_tokens
         n = S // W
@@ -298,7 +474,7 @@ def per_config(cp, WL, torch, dev, reps: int = 10):
         out = [[torch.empty((n, w.heads, w.head_dim), dtype=dt, device=dev) for _ in range(W)]
                for _ in range(2)]
         add(name, "fused grad return dK,dV", 2 * (W + 1) * S * row_in,
-            timed(lambda: cp.cp_grad_return_fused(grads, out, meta)))
+            timed(lambda: cp.cp_grad_return_fused(grads, out, meta)), mix=(W, S * row_in))
         slots = [[[torch.empty((n, w.heads, w.head_dim), dtype=dt, device=dev) for _ in range(W)]
                   for _ in range(W)] for _ in range(2)]
         epochs = torch.zeros((W, W), dtype=torch.int32, device=dev)
@@ -312,11 +488,11 @@ def per_config(cp, WL, torch, dev, reps: int = 10):
             timed(unfused))
         # accumulate mode: the owner's gradient is read as well (one more row per output row)
         add(name, "fused grad return dK,dV, accumulate", 2 * (W + 2) * S * row_in,
-            timed(lambda: cp.cp_grad_return_fused(grads, out, meta, accumulate=True)))
+            timed(lambda: cp.cp_grad_return_fused(grads, out, meta, accumulate=True)), mix=(W + 1, S * row_in))
         # the same tensors under packed-contiguous ownership (owner o: tokens [o S/W, (o+1) S/W))
         meta_pc = cp.cp_build_meta(cu, S, W, cp.CP_POLICY_PACKED_CONTIGUOUS, check=True)
         add(name, "fused grad return dK,dV, packed-contiguous owners", 2 * (W + 1) * S * row_in,
-            timed(lambda: cp.cp_grad_return_fused(grads, out, meta_pc)))
+            timed(lambda: cp.cp_grad_return_fused(grads, out, meta_pc)), mix=(W, S * row_in))
 
         def unfused_pc():
             state["e"] += 1
@@ -484,8 +660,16 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tokens", type=int, default=262144, help="S (default 262144)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the CPU oracle's N-core run (default: the usable host CPUs, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the plain-stream ceiling measurements")
+    ap.add_argument("--only-ceiling", action="store_true",
+                    help="run only the plain-stream ceilings of the step's mixes and print them as one JSON "
+                         "line (for profiling them on their own; not the benchmark line)")
+    ap.add_argument("--config-names", default="",
+                    help="comma-separated workloads for --only-configs (default: all)")
     ap.add_argument("--no-sweep-latency", action="store_true")
     ap.add_argument("--no-allreduce", action="store_true",
                     help="skip the one-shot / ring all-reduce sweep")
@@ -529,13 +713,19 @@ def main():
         return
     if args.only_configs:
         log("[bench] per-config measurements only")
-        print(json.dumps({"per_config": per_config(cp, WL, torch, dev)}), flush=True)
+        names = [n for n in args.config_names.split(",") if n] or None
+        ceil = None if args.no_ceiling else Ceiling(torch, dev)
+        print(json.dumps({"per_config": per_config(cp, WL, torch, dev, ceiling=ceil, names=names)}), flush=True)
+        return
+    if args.only_ceiling:
+        log("[bench] plain-stream ceilings only")
+        print(json.dumps({"ceiling": Ceiling(torch, dev).standard(args.tokens)}), flush=True)
         return
     log(f"[bench] building inputs S={args.tokens}")
     step = Step(cp, WL, torch, args.tokens, dev)
     torch.cuda.synchronize()
     log("[bench] attributing kernels")
-    kbytes, kcount = attribute_kernels(step, cp, torch)
+    kbytes, kcount, kmix = attribute_kernels(step, cp, torch)
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step.run()
@@ -580,12 +770,34 @@ def main():
     allreduce = None if args.no_allreduce else allreduce_sweep(step.sweep, cp, torch)
     num_docs = step.num_docs
     ops = [{"op": n, "bytes": b} for n, b, _ in step.ops]
+    host = None
+    if not args.no_cpu_baseline:
+        log("[bench] copying the step's inputs to the host for the CPU oracle")
+        host = host_inputs(step, torch)
+    del step  # free the step's buffers (~70 GB) before the ceiling and per-workload runs
+    torch.cuda.empty_cache()
+    ceiling = None
+    if not args.no_ceiling:
+        log("[bench] plain-stream ceilings")
+        ceil = Ceiling(torch, dev)
+        ceiling = ceil.standard(args.tokens)
+        for k in kernels:
+            if k["kernel"] in kmix:
+                c = ceil.rate(*kmix[k["kernel"]])
+                k["ceiling_mix"] = c["mix"]
+                k["ceiling_gbs"] = c["gbs"]
+                if k["gbs"]:
+                    k["frac_of_ceiling"] = round(k["gbs"] / c["gbs"], 4)
+        if dom["kernel"] in kmix:
+            c = ceil.rate(*kmix[dom["kernel"]])
+            roofline["ceiling"] = {"mix": c["mix"], "gbs": c["gbs"], "bytes_per_buffer": c["bytes_per_buffer"],
+                                   "what": "a plain stream of the same read/write mix and size under the same "
+                                           "schedule (libcpthd_roofline.so), HIP-event median of 10"}
+            roofline["frac_of_ceiling"] = round(achieved / c["gbs"], 4) if achieved else None
     configs = None
     if not args.no_configs:
-        del step  # free the step's buffers (~70 GB) before the per-workload runs
-        torch.cuda.empty_cache()
         log("[bench] per-config measurements")
-        configs = per_config(cp, WL, torch, dev)
+        configs = per_config(cp, WL, torch, dev, ceiling=None if args.no_ceiling else ceil)
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -614,11 +826,13 @@ def main():
         "sweep_latency": sweep,
         "allreduce_sweep": allreduce,
         "per_config": configs,
+        "ceiling": ceiling,
         "device": torch.cuda.get_device_name(0),
     }
-    if not args.no_cpu_baseline:
-        log(f"[bench] CPU oracle baseline at S={args.cpu_sample_tokens}")
-        result["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens, WL)
+    if host is not None:
+        threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+        log(f"[bench] CPU oracle baseline at S={args.tokens}, 1 thread and {threads} threads")
+        result["cpu_baseline"] = cpu_baseline(host, step_bytes, threads)
     print(json.dumps(result), flush=True)
 
 

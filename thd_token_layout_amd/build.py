@@ -2,7 +2,10 @@
 
     python -m thd_token_layout_amd.build          # or: python thd_token_layout_amd/build.py
 
-Compiles every time it is called.  Output: thd_token_layout_amd/libcpthd.so.
+Compiles every time it is called.  Outputs: thd_token_layout_amd/libcpthd.so
+(the library) and thd_token_layout_amd/libcpthd_roofline.so (plain streaming
+kernels the benchmark measures the chip's ceiling with; not part of the
+library).
 """
 from __future__ import annotations
 
@@ -17,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcpthd.so")
+ROOFLINE_LIB = os.path.join(PKG, "libcpthd_roofline.so")
+ROOFLINE_SOURCE = "roofline.hip"
 
 ARCH = "gfx950"
 HIP_SOURCES = ["meta.hip", "permute.hip", "reduce.hip", "allreduce.hip", "scratch.hip"]
@@ -51,6 +56,9 @@ def build(verbose: bool = False) -> str:
         cmd = [cc, *COMMON, "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, src), "-o", obj]
         jobs.append((src, cmd))
         objs.append(obj)
+    roofline_obj = os.path.join(BUILD, ROOFLINE_SOURCE + ".o")
+    jobs.append((ROOFLINE_SOURCE, [cc, *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, ROOFLINE_SOURCE),
+                                   "-o", roofline_obj]))
     procs = []
     for src, cmd in jobs:
         if verbose:
@@ -75,6 +83,12 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
     os.replace(tmp, LIB)
+    tmp = ROOFLINE_LIB + ".tmp"
+    r = subprocess.run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", roofline_obj, "-o", tmp],
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
+    os.replace(tmp, ROOFLINE_LIB)
     return LIB
 
 
