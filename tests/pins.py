@@ -132,17 +132,26 @@ def check_bf16_rne_against_torch(o, exhaustive=False):
     chunks = [(hi[:, None] | lows[None, :]).ravel()]
     chunks.append(rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32))
     if exhaustive:
-        chunks = [np.arange(s, s + (1 << 26), dtype=np.uint64).astype(np.uint32)
-                  for s in range(0, 1 << 32, 1 << 26)]
+        chunks = (np.arange(s, s + (1 << 26), dtype=np.uint64).astype(np.uint32)
+                  for s in range(0, 1 << 32, 1 << 26))
     for bits in chunks:
-        f = bits.view(np.float32)
-        ours = o.f32_to_bf16_rne(f)
-        ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-        nan = np.isnan(f)
-        assert (ours[~nan] == ref[~nan]).all()
-        # NaN: quiet, sign kept
-        assert ((ours[nan] & 0x7FC0) == 0x7FC0).all()
-        assert ((ours[nan] >> 15) == (bits[nan] >> 31)).all()
+        check_bf16_rne_bits(o, bits)
+
+
+def check_bf16_rne_bits(o, bits):
+    """The oracle's fp32 -> bf16 rounding of the fp32 values with bit patterns
+    `bits` (uint32) against torch's CPU cast; a NaN must stay a quiet NaN with
+    its sign (torch's NaN payload is not compared)."""
+    import torch
+
+    f = bits.view(np.float32)
+    ours = o.f32_to_bf16_rne(f)
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(f)
+    assert (ours[~nan] == ref[~nan]).all()
+    # NaN: quiet, sign kept
+    assert ((ours[nan] & 0x7FC0) == 0x7FC0).all()
+    assert ((ours[nan] >> 15) == (bits[nan] >> 31)).all()
 
 
 def check_bf16_widen_exact(o):

@@ -131,9 +131,28 @@ def test_epochs_after():
     assert e.shape == (4, 4) and (e == 7).all()
 
 
-@pytest.mark.slow
 def test_bf16_rne_exhaustive():
-    pins.check_bf16_rne_against_torch(o, exhaustive=True)
+    """Every one of the 2^32 fp32 bit patterns through the oracle's bf16 rounding
+    against torch's CPU cast, in 256 chunks of 2^24 spread over threads (numpy and
+    torch release the GIL)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+
+    step = 1 << 24
+
+    def run(start):
+        pins.check_bf16_rne_bits(o, np.arange(start, start + step, dtype=np.uint64).astype(np.uint32))
+
+    threads = max(1, min(8, len(os.sched_getaffinity(0))))
+    torch_threads = torch.get_num_threads()
+    torch.set_num_threads(1)  # one torch thread per worker: no oversubscription
+    try:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(run, range(0, 1 << 32, step)))
+    finally:
+        torch.set_num_threads(torch_threads)
 
 
 def _compositions(total, parts_max=None):
