@@ -4,6 +4,9 @@ equal outputs on consecutive calls of falling size, both policies, fp32 and
 bf16, overwrite and accumulate; a call beyond the workspace is refused on the
 host and writes nothing."""
 import ctypes
+import os
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -93,3 +96,61 @@ def test_noalloc_refuses_more_than_the_workspace(cp):
     with pytest.raises(cp.CpError) as e:
         cp.cp_grad_return_noalloc(grads, out, meta)
     assert e.value.status == cp.CP_ERR_TOO_LARGE
+
+
+def test_noalloc_captured_in_a_graph(cp):
+    """The use it exists for: captured in a HIP graph (torch.cuda.CUDAGraph), then
+    replayed four times with new gradients written eagerly between replays and other
+    eager work in between; every replay equals cp_grad_return run eagerly on the same
+    inputs, bit for bit.  The call records only kernel launches."""
+    W, H, D, T = 4, 4, 128, 256
+    cu = np.array([0, 64, 64, 192, 256], dtype=np.int32)
+    n = T // W
+    say("case noalloc graph capture and replay")
+    meta = cp.cp_build_meta(torch.from_numpy(cu).to(DEV), T, W, cp.CP_POLICY_DUAL_CHUNK_SWAP, check=True)
+    grads = [[torch.empty((T, H, D), device=DEV) for _ in range(W)] for _ in range(2)]
+    got = [[torch.empty((n, H, D), device=DEV) for _ in range(W)] for _ in range(2)]
+    ref = [[torch.empty((n, H, D), device=DEV) for _ in range(W)] for _ in range(2)]
+    slots = [[[torch.empty((n, H, D), device=DEV) for _ in range(W)] for _ in range(W)] for _ in range(2)]
+    gen = torch.Generator(device=DEV).manual_seed(5)
+
+    def fresh():
+        for row in grads:
+            for g in row:
+                g.copy_(torch.randn(g.shape, generator=gen, device=DEV))
+
+    fresh()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        assert noalloc(cp, grads, got, meta) == cp.CP_OK  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        assert noalloc(cp, grads, got, meta) == cp.CP_OK
+    for replay in range(4):
+        fresh()
+        a = torch.randn((256, 256), generator=gen, device=DEV)
+        (a @ a).sum().item()  # unrelated eager work and a synchronization between replays
+        for row in got:
+            for o in row:
+                o.fill_(float("nan"))
+        graph.replay()
+        cp.cp_grad_return(grads, slots, ref, meta)
+        torch.cuda.synchronize()
+        assert cp.cp_meta_status(meta)[0] == cp.CP_OK
+        for t in range(2):
+            for o in range(W):
+                assert bits_equal(to_np(got[t][o]), to_np(ref[t][o])), (replay, t, o)
+
+
+def test_noalloc_first_call_under_capture():
+    """The one-time lookup of the workspace's device address also works when a process's
+    first call is made under graph capture (in a child process, so the call really is its
+    first)."""
+    say("case noalloc first call under capture (child process)")
+    child = os.path.join(os.path.dirname(os.path.abspath(__file__)), "noalloc_capture_child.py")
+    res = subprocess.run([sys.executable, child], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-2000:]
+    assert "first call captured ok" in res.stdout, res.stdout[-2000:]
