@@ -50,7 +50,8 @@
  *    its header, and the gradient return's epoch wait records its timeout mask
  *    there (both atomically, so calls on several streams may share one
  *    metadata buffer).  Nothing else in the buffer is written after
- *    cp_build_meta.
+ *    cp_build_meta.  `meta` must be 16-byte aligned (CP_ERR_ARG otherwise):
+ *    kernels read its 64-byte header in one scalar load.
  *  - Outputs must not overlap inputs or each other (CP_ERR_ALIAS); [GR]
  *    "Description" (self-alias assertions on the rank-self slots).  The
  *    metadata header counts as an output of every call that takes `meta`, its

@@ -242,3 +242,30 @@ def test_noalloc_host_checks(cp):
     assert na(4, 2, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, 0x20, None) == cp.CP_ERR_ARG
     assert na(4, 2, None, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, FAKE, 0, None) == cp.CP_ERR_ARG
     assert na(4, 2, None, None, 0, 2, 8, cp.CP_F32, cp.CP_F32, None, 0, None) == cp.CP_OK
+
+
+def test_misaligned_meta_refused(cp):
+    """Every entry point that takes the metadata refuses a pointer that is not 16-byte
+    aligned (the kernels read its header in one scalar load) with CP_ERR_ARG, before
+    any HIP call; the same calls with an aligned fake pointer get past that check."""
+    lib = cp.lib
+    tab = (ctypes.c_void_p * 64)(*([0x10000] * 64))
+    fl = ctypes.c_int32(0)
+    to = ctypes.c_uint64(0)
+    for off in (4, 8, 12, 1):
+        bad = ctypes.c_void_p(0x10000 + off)
+        assert lib.cp_build_meta(FAKE, 3, 48, 2, cp.CP_POLICY_DUAL_CHUNK_SWAP, bad, 1 << 20, None) == cp.CP_ERR_ARG
+        assert lib.cp_meta_status(bad, None, ctypes.byref(fl), ctypes.byref(to)) == cp.CP_ERR_ARG
+        assert lib.cp_build_attn_meta(bad, 3, 2, FAKE, 1 << 20, None) == cp.CP_ERR_ARG
+        assert lib.cp_partition_thd(FAKE, FAKE, 48, 2, 8, cp.CP_F32, bad, None) == cp.CP_ERR_ARG
+        assert lib.cp_gather_thd(FAKE, FAKE, 48, 2, 8, cp.CP_F32, bad, None) == cp.CP_ERR_ARG
+        assert lib.cp_partition_thd_multi(2, tab, tab, 48, 2, 8, cp.CP_F32, bad, None) == cp.CP_ERR_ARG
+        assert lib.cp_gather_thd_multi(2, tab, tab, 48, 2, 8, cp.CP_F32, bad, None) == cp.CP_ERR_ARG
+        assert lib.cp_grad_return(cp.CP_ALL_RANKS, 2, 1, tab, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, bad,
+                                  None, 0, 0, cp.CP_PHASE_ALL, None) == cp.CP_ERR_ARG
+        assert lib.cp_grad_return_fused(cp.CP_ALL_RANKS, 2, 1, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, bad,
+                                        0, None) == cp.CP_ERR_ARG
+        assert lib.cp_grad_return_noalloc(2, 1, tab, tab, 48, 2, 8, cp.CP_F32, cp.CP_F32, bad, 0,
+                                          None) == cp.CP_ERR_ARG
+    # aligned: the alignment check passes and a later (device) check fails instead
+    assert lib.cp_partition_thd(FAKE, FAKE, 48, 2, 8, cp.CP_F32, FAKE, None) in (cp.CP_ERR_DEVICE, cp.CP_ERR_HIP)

@@ -63,6 +63,11 @@ Range range_of(const void* p, int64_t bytes) {
   return Range{a, a + (uintptr_t)(bytes > 0 ? bytes : 0)};
 }
 
+// NULL, or not 16-byte aligned (the kernels read the header in one scalar load).
+bool bad_meta_ptr(const void* meta) {
+  return meta == nullptr || (reinterpret_cast<uintptr_t>(meta) & 15) != 0;
+}
+
 // Byte ranges of a metadata buffer for one call's checks.  The kernels write
 // the 64-byte header (sticky call flags, the epoch wait's timeout mask), so it
 // is an output of the call; the tables after it are only read, an input.  The
@@ -275,7 +280,7 @@ size_t cp_meta_bytes(int32_t num_docs, int32_t cp_size) {
 int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tokens,
                   int32_t cp_size, int32_t policy, void* meta, size_t meta_bytes,
                   cp_stream_t stream) {
-  if (cu_seqlens == nullptr || meta == nullptr) return CP_ERR_ARG;
+  if (cu_seqlens == nullptr || bad_meta_ptr(meta)) return CP_ERR_ARG;
   if (num_docs < 0 || num_docs >= INT32_MAX || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return CP_ERR_ARG;
   if (total_tokens < 0 || total_tokens > INT32_MAX) return CP_ERR_ARG;
   if (policy != CP_POLICY_DUAL_CHUNK_SWAP && policy != CP_POLICY_PACKED_CONTIGUOUS) return CP_ERR_ARG;
@@ -304,7 +309,7 @@ size_t cp_attn_meta_bytes(int32_t num_docs, int32_t cp_size) {
 
 int cp_build_attn_meta(void* meta, int32_t num_docs, int32_t cp_size, void* attn,
                        size_t attn_bytes, cp_stream_t stream) {
-  if (meta == nullptr || attn == nullptr) return CP_ERR_ARG;
+  if (bad_meta_ptr(meta) || attn == nullptr) return CP_ERR_ARG;
   if (num_docs < 0 || num_docs >= INT32_MAX || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return CP_ERR_ARG;
   if (attn_bytes < cp_attn_meta_bytes(num_docs, cp_size)) return CP_ERR_SHAPE;
   int dev, st;
@@ -321,7 +326,7 @@ int cp_build_attn_meta(void* meta, int32_t num_docs, int32_t cp_size, void* attn
 
 int cp_meta_status(const void* meta, cp_stream_t stream, int32_t* flags_out,
                    uint64_t* timeouts_out) {
-  if (meta == nullptr) return CP_ERR_ARG;
+  if (bad_meta_ptr(meta)) return CP_ERR_ARG;
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
   AllocCache cache;
@@ -353,7 +358,7 @@ static int layout_call(int32_t n_tensors, const void* const* ins, void* const* o
   if (n_tensors < 1 || n_tensors > kMaxLayoutTensors) return CP_ERR_ARG;
   if (total_tokens < 0 || total_tokens > INT32_MAX || heads < 1 || head_dim < 1) return CP_ERR_ARG;
   if (total_tokens == 0) return CP_OK;  // nothing to move; empty tensors may have NULL data
-  if (ins == nullptr || outs == nullptr || meta == nullptr) return CP_ERR_ARG;
+  if (ins == nullptr || outs == nullptr || bad_meta_ptr(meta)) return CP_ERR_ARG;
   for (int t = 0; t < n_tensors; ++t)
     if (ins[t] == nullptr || outs[t] == nullptr) return CP_ERR_ARG;
   const int64_t row_bytes = checked_bytes((int64_t)heads * head_dim, dtype_bytes(dtype));
@@ -425,7 +430,7 @@ static int grad_scalar_checks(int32_t rank, int32_t cp_size, int32_t n_tensors, 
   // T % W under either policy; dual-chunk-swap metadata also guarantees T % 2W
   // (every document is a multiple of 2W), which the kernels check on the device.
   if (total_tokens % (int64_t)cp_size != 0) return CP_ERR_SHAPE;
-  if (total_tokens > 0 && meta == nullptr) return CP_ERR_ARG;
+  if (total_tokens > 0 && bad_meta_ptr(meta)) return CP_ERR_ARG;
   // every buffer size fits comfortably in 64 bits
   const int64_t row_elems = (int64_t)heads * head_dim;
   if (checked_bytes(total_tokens, checked_bytes(row_elems, 4)) < 0) return CP_ERR_ARG;

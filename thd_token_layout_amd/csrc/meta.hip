@@ -130,20 +130,21 @@ __device__ int32_t block_max(int32_t v) {
 __global__ void __launch_bounds__(kBlock)
 build_attn_meta_kernel(cp_meta_header* h, int32_t B, int32_t W, char* __restrict__ attn) {
   const int tid = threadIdx.x;
-  bool ok = meta_ok(h, h->total_tokens, W, -1);
-  if (ok && h->num_docs != B) {
+  const cp_meta_header hv = read_header(h);
+  bool ok = meta_ok(h, hv, hv.total_tokens, W, -1);
+  if (ok && hv.num_docs != B) {
     ok = false;
     if (blockIdx.x == 0 && tid == 0) atomicOr(&h->flags, CP_CALL_DOCS_MISMATCH);
   }
   if (blockIdx.x == 0 && tid == 0) {
     cp_attn_header* a = reinterpret_cast<cp_attn_header*>(attn);
-    a->policy = ok ? h->policy : -1;
+    a->policy = ok ? hv.policy : -1;
     a->cp_size = W;
     a->num_docs = B;
-    a->num_steps = ok ? (h->policy == CP_POLICY_DUAL_CHUNK_SWAP ? 2 : 1) : 0;
+    a->num_steps = ok ? (hv.policy == CP_POLICY_DUAL_CHUNK_SWAP ? 2 : 1) : 0;
     a->reserved0 = 0;
-    a->total_tokens = ok ? h->total_tokens : 0;
-    a->local_tokens = ok ? h->local_tokens : 0;
+    a->total_tokens = ok ? hv.total_tokens : 0;
+    a->local_tokens = ok ? hv.local_tokens : 0;
     for (int k = 0; k < 6; ++k) a->reserved[k] = 0;
     a->magic = ok ? CP_ATTN_MAGIC : 0u;
   }
@@ -151,8 +152,8 @@ build_attn_meta_kernel(cp_meta_header* h, int32_t B, int32_t W, char* __restrict
 
   const int32_t r = blockIdx.x >> 1;
   const int32_t step = blockIdx.x & 1;
-  const int32_t T = (int32_t)h->total_tokens;
-  const int32_t n = (int32_t)h->local_tokens;
+  const int32_t T = (int32_t)hv.total_tokens;
+  const int32_t n = (int32_t)hv.local_tokens;
   const int32_t* cu = meta_cu(h);
   int32_t* scal = reinterpret_cast<int32_t*>(attn + attn_record_offset(B, blockIdx.x));
   int32_t* cuq = scal + 8;
@@ -160,7 +161,7 @@ build_attn_meta_kernel(cp_meta_header* h, int32_t B, int32_t W, char* __restrict
   int32_t* qoff = cukv + (B + 1);
   int32_t* kvoff = qoff + (B + 1);
 
-  if (h->policy == CP_POLICY_DUAL_CHUNK_SWAP) {
+  if (hv.policy == CP_POLICY_DUAL_CHUNK_SWAP) {
     const int32_t k = step == 0 ? r : 2 * W - 1 - r;  // the step's chunk index
     const int32_t two_w = 2 * W;
     int32_t max_c = 0;

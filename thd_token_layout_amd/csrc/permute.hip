@@ -149,7 +149,7 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
   const int64_t n = h->local_tokens;
   const bool dcs = h->policy == CP_POLICY_DUAL_CHUNK_SWAP;
   const int32_t* cu = meta_cu(h);
-  const int32_t* lcu = meta_local_cu0(h);
+  const int32_t* lcu = meta_local_cu0(h, B);
   const int64_t upr = a.row_bytes / (int64_t)sizeof(U);  // units per row
 
   const int lane = threadIdx.x & 63;
@@ -256,25 +256,26 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
   __shared__ int32_t s_cu[kFlatMaxDocs + 1];
   __shared__ int32_t s_lcu[kFlatMaxDocs + 1];
   cp_meta_header* h = a.meta;
-  if (!meta_ok(h, a.total_tokens, a.expect_cp_size, a.expect_policy)) return;
+  const cp_meta_header hv = read_header(h);
+  if (!meta_ok(h, hv, a.total_tokens, a.expect_cp_size, a.expect_policy)) return;
 
   const int64_t T = a.total_tokens;
-  const int32_t W = h->cp_size;
-  const int32_t B = h->num_docs;
-  const int64_t n = h->local_tokens;
-  const bool dcs = h->policy == CP_POLICY_DUAL_CHUNK_SWAP;
+  const int32_t W = hv.cp_size;
+  const int32_t B = hv.num_docs;
+  const int64_t n = hv.local_tokens;
+  const bool dcs = hv.policy == CP_POLICY_DUAL_CHUNK_SWAP;
   // Document tables: staged in LDS when small enough, else read from the metadata.
   const bool staged = dcs && B <= kFlatMaxDocs;
   if (staged) {
     const int32_t* mcu = meta_cu(h);
-    const int32_t* mlcu = meta_local_cu0(h);
+    const int32_t* mlcu = meta_local_cu0(h, B);
     for (int k = threadIdx.x; k <= B; k += kBlock) {
       s_cu[k] = mcu[k];
       s_lcu[k] = mlcu[k];
     }
   }
   const int32_t* cu = staged ? s_cu : meta_cu(h);
-  const int32_t* lcu = staged ? s_lcu : meta_local_cu0(h);
+  const int32_t* lcu = staged ? s_lcu : meta_local_cu0(h, B);
   const int64_t upr = a.row_bytes / 16;
   const int64_t total = T * upr;
   constexpr int64_t kTileUnits = (int64_t)kBlock * NP;

@@ -34,6 +34,9 @@ namespace {
 
 // Gradient-return kernels need metadata built for W ranks and T tokens (either
 // policy: the owner's rows are those the partition gives it).
+__device__ __forceinline__ bool grad_meta_ok(cp_meta_header* h, const cp_meta_header& v, int64_t T, int32_t W) {
+  return meta_ok(h, v, T, W, -1);
+}
 __device__ __forceinline__ bool grad_meta_ok(cp_meta_header* h, int64_t T, int32_t W) {
   return meta_ok(h, T, W, -1);
 }
@@ -45,8 +48,9 @@ template <int IN, int OUT, int WB, bool VEC, int UPT, bool ACC>
 __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
   if (a.gate_meta != nullptr) {
     cp_meta_header* h = a.gate_meta;
-    if (!grad_meta_ok(h, a.gate_T, a.num_slots)) return;
-    if (a.owner >= 0 && ((h->wait_timeout_ranks >> a.owner) & 1ull)) return;
+    const cp_meta_header hv = read_header(h);
+    if (!grad_meta_ok(h, hv, a.gate_T, a.num_slots)) return;
+    if (a.owner >= 0 && ((hv.wait_timeout_ranks >> a.owner) & 1ull)) return;
   }
   const int W = a.num_slots;
   constexpr bool SPLIT = split_layout<IN, OUT>();
@@ -95,8 +99,9 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
   const int32_t W = a.cp_size;
   const int32_t B = h->num_docs;
   const int64_t n = h->local_tokens;
+  const int32_t policy = h->policy;
   const int32_t* cu = meta_cu(h);
-  const int32_t* lcu = meta_local_cu0(h);
+  const int32_t* lcu = meta_local_cu0(h, B);
   const int in_bytes = IN == CP_F32 ? 4 : 2;
   const int out_bytes = OUT == CP_F32 ? 4 : 2;
 
@@ -112,7 +117,7 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
     if (q >= rows) continue;
     const int32_t o = a.owner_begin + (int32_t)(q / n);
     const int64_t i = q - (int64_t)(o - a.owner_begin) * n;
-    const int64_t g = owner_global_row(h->policy, o, i, n, W, B, cu, lcu);
+    const int64_t g = owner_global_row(policy, o, i, n, W, B, cu, lcu);
     const int64_t src_off = g * a.row_elems * in_bytes;  // same row in every writer's view
     char* row_dst = a.out.p[o] + i * a.row_elems * out_bytes;
     if constexpr (VEC) {
@@ -163,8 +168,9 @@ __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_
   const int32_t W = a.cp_size;
   const int32_t B = h->num_docs;
   const int64_t n = h->local_tokens;
+  const int32_t policy = h->policy;
   const int32_t* cu = meta_cu(h);
-  const int32_t* lcu = meta_local_cu0(h);
+  const int32_t* lcu = meta_local_cu0(h, B);
   const int in_bytes = IN == CP_F32 ? 4 : 2;
   const int out_bytes = OUT == CP_F32 ? 4 : 2;
   const int64_t upr = a.row_elems / 8;
@@ -182,7 +188,7 @@ __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_
       const int64_t q = row0 + threadIdx.x;
       const int32_t o = a.owner_begin + (int32_t)(q / n);
       const int64_t i = q - (int64_t)(o - a.owner_begin) * n;
-      s_src[threadIdx.x] = owner_global_row(h->policy, o, i, n, W, B, cu, lcu) * a.row_elems * in_bytes;
+      s_src[threadIdx.x] = owner_global_row(policy, o, i, n, W, B, cu, lcu) * a.row_elems * in_bytes;
       s_dst[threadIdx.x] = a.out.p[o] + i * a.row_elems * out_bytes;
     }
     __syncthreads();
