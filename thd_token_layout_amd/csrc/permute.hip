@@ -55,12 +55,34 @@ __device__ __forceinline__ void load_doc(Cursor& k, const int32_t* cu, const int
   k.c = (k.lend - k.lstart) >> 1;
 }
 
+// find_doc run by a whole wave at once (wave-uniform arguments, every lane
+// active): each round the 64 lanes test 64 entries of `bound` at a stride that
+// shrinks 63-fold from ceil((B+1)/63) to 1 and keep the last entry <= v, so
+// the search costs ceil(log63(B+1)) dependent loads instead of log2(B).
+// Measured on MI355X for the row tiles in local order: the 10 KiB-row gradient
+// scatter 1-5% faster at 116-32768 documents, the layouts' partition
+// unchanged; in global order (the gather) 1-2% slower, so the gather keeps
+// find_doc.
+__device__ __forceinline__ int32_t wave_find_doc(const int32_t* bound, int32_t B, int64_t v) {
+  const int lane = threadIdx.x & 63;
+  int32_t lo = 0;  // bound[lo] <= v throughout
+  for (int32_t s = (int32_t)(((int64_t)B + 63) / 63);; s = (s + 62) / 63) {
+    const int64_t idx = (int64_t)lo + (int64_t)lane * s;
+    const bool le = idx < B && (int64_t)bound[idx] <= v;
+    const int cnt = __popcll(__ballot(le));
+    lo += (cnt > 1 ? cnt - 1 : 0) * s;
+    if (s == 1) return lo;
+  }
+}
+
+// WAVE: the caller is a whole wave with wave-uniform arguments.
+template <bool WAVE>
 __device__ __forceinline__ void seek(Cursor& k, int64_t p, int64_t n, int32_t B, bool dcs,
                                      const int32_t* cu, const int32_t* lcu) {
   k.r = (int32_t)(p / n);
   k.i = p - (int64_t)k.r * n;
   if (!dcs) return;
-  k.b = find_doc(lcu, B, k.i);
+  k.b = WAVE ? wave_find_doc(lcu, B, k.i) : find_doc(lcu, B, k.i);
   load_doc(k, cu, lcu);
 }
 
@@ -197,7 +219,7 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
     } else {
       // p0 indexes local rows (flat r*n + i); rows are visited in local order.
       Cursor k;
-      seek(k, p0, n, B, dcs, cu, lcu);
+      seek<true>(k, p0, n, B, dcs, cu, lcu);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         ok[g] = p0 + g < T;
@@ -307,7 +329,7 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
         }
       } else {
         Cursor k;
-        seek(k, p, n, B, dcs, cu, lcu);
+        seek<false>(k, p, n, B, dcs, cu, lcu);
         r = k.r;
         i = k.i;
         g = global_row(k, W, n, dcs);
