@@ -309,9 +309,11 @@ class Ceiling:
     `nbytes` each read and (write) one output of `nbytes` written, by the streaming
     kernels of libcpthd_roofline.so (full grid, contiguous tiles, 16-byte non-temporal
     accesses, as the library's kernels), the best of 1, 2 and 3 units per thread (4, 8 and
-    12 KiB tiles).  Timed like per_config: median of `reps` launches per shape, each after
-    a 1 GiB write that flushes the last-level cache, with HIP events on the stream the
-    kernel is launched on.  Results are cached by mix."""
+    12 KiB tiles).  With `launches` = k, k such streams on k sets of buffers launched back
+    to back and timed together (the ceiling of an operation that makes k launches of that
+    size).  Timed like per_config: median of `reps` runs per shape, each after a 1 GiB
+    write that flushes the last-level cache, with HIP events on the stream the kernels
+    are launched on.  Results are cached by mix, size and launch count."""
 
     def __init__(self, torch, dev, reps: int = 10):
         self.lib = load_roofline_lib()
@@ -320,26 +322,30 @@ class Ceiling:
         self.flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         self.sink = torch.zeros(1024, dtype=torch.int32, device=dev)
 
-    def rate(self, n_in: int, nbytes: int, write: bool = True):
+    def rate(self, n_in: int, nbytes: int, write: bool = True, launches: int = 1):
         import ctypes
         import statistics
 
         torch = self.torch
         nbytes = (int(nbytes) + 15) // 16 * 16
-        key = (n_in, nbytes, write)
+        key = (n_in, nbytes, write, launches)
         if key in self.cache:
             return self.cache[key]
-        ins = [torch.empty(nbytes, dtype=torch.uint8, device=self.dev) for _ in range(n_in)]
-        out = torch.empty(nbytes, dtype=torch.uint8, device=self.dev) if write else None
-        tab = (ctypes.c_void_p * max(n_in, 1))(*[t.data_ptr() for t in ins])
-        outp = ctypes.c_void_p(out.data_ptr()) if write else None
+        sets = []
+        for _ in range(launches):
+            ins = [torch.empty(nbytes, dtype=torch.uint8, device=self.dev) for _ in range(n_in)]
+            out = torch.empty(nbytes, dtype=torch.uint8, device=self.dev) if write else None
+            tab = (ctypes.c_void_p * max(n_in, 1))(*[t.data_ptr() for t in ins])
+            outp = ctypes.c_void_p(out.data_ptr()) if write else None
+            sets.append((ins, out, tab, outp))
         sink = ctypes.c_void_p(self.sink.data_ptr())
 
         def launch(np_):
             stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-            st = self.lib.cprl_stream(n_in, tab, outp, nbytes, np_, sink, stream)
-            if st != 0:
-                raise RuntimeError(f"cprl_stream: status {st}")
+            for _, _, tab, outp in sets:
+                st = self.lib.cprl_stream(n_in, tab, outp, nbytes, np_, sink, stream)
+                if st != 0:
+                    raise RuntimeError(f"cprl_stream: status {st}")
 
         by_shape = {}
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -356,13 +362,15 @@ class Ceiling:
             by_shape[np_] = statistics.median(ts)
         best = min(by_shape, key=by_shape.get)
         us = by_shape[best]
-        moved = nbytes * (n_in + (1 if write else 0))
+        moved = nbytes * (n_in + (1 if write else 0)) * launches
         mix = f"{n_in}:{1 if write else 0}" if n_in else "0:1"
         res = {"mix": mix, "bytes_per_buffer": nbytes, "moved_bytes": moved, "median_us": round(us, 2),
                "gbs": round(moved / us / 1e3, 1), "units_per_thread": best,
                "gbs_by_units_per_thread": {k: round(moved / v / 1e3, 1) for k, v in by_shape.items()}}
+        if launches > 1:
+            res["launches"] = launches
         self.cache[key] = res
-        del ins, out
+        del sets
         torch.cuda.empty_cache()
         return res
 
@@ -417,6 +425,15 @@ def per_config(cp, WL, torch, dev, reps: int = 10, ceiling=None, names=None):
             ts.append(e0.elapsed_time(e1) * 1000.0)
         return statistics.median(ts)
 
+    def n_launches(fn):
+        """Library launches one call of `fn` makes (its ceiling is that many plain streams)."""
+        torch.cuda.synchronize()
+        cp.cp_profile_enable(True)
+        fn()
+        prof = cp.cp_profile_read()
+        cp.cp_profile_enable(False)
+        return max(1, sum(c for c, _ in prof.values()))
+
     def add(cfg, op, nbytes, us, mix=None, **extra):
         row = {"config": cfg, "op": op, "bytes": nbytes, "median_us": round(us, 1),
                "gbs": round(nbytes / us / 1e3, 1), "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
@@ -446,13 +463,16 @@ def per_config(cp, WL, torch, dev, reps: int = 10, ceiling=None, names=None):
             meta = cp.cp_build_meta(cu, w.total_tokens, w.cp_size, pol, check=True)
             cfg = name if pol == cp.POLICY[w.policy] else f"{name} as packed_contiguous (same documents and Q,K,V)"
             docs = {"documents": int(cu.numel() - 1), "attention": attn_summary(cp, meta)}
-            add(cfg, "partition Q,K,V (multi-tensor call)", nbytes,
-                timed(lambda: cp.cp_partition_thd_multi(xs, meta, parts=parts)), mix=(1, nbytes // 2), **docs)
-            add(cfg, "gather Q,K,V (multi-tensor call)", nbytes,
-                timed(lambda: cp.cp_gather_thd_multi(parts, meta, xs=back)), mix=(1, nbytes // 2))
-            add(cfg, "partition Q,K,V (three single-tensor calls)", nbytes,
-                timed(lambda: [cp.cp_partition_thd(x, meta, parts=p) for x, p in zip(xs, parts)]),
-                mix=(1, nbytes // 2))
+            # a ceiling of as many plain streams as the call makes launches (the multi-tensor
+            # call launches once, or once per tensor when each tensor moves >= 1 GiB)
+            part_multi = lambda: cp.cp_partition_thd_multi(xs, meta, parts=parts)
+            gather_multi = lambda: cp.cp_gather_thd_multi(parts, meta, xs=back)
+            part_single = lambda: [cp.cp_partition_thd(x, meta, parts=p) for x, p in zip(xs, parts)]
+            for op, fn, kw in (("partition Q,K,V (multi-tensor call)", part_multi, docs),
+                               ("gather Q,K,V (multi-tensor call)", gather_multi, {}),
+                               ("partition Q,K,V (three single-tensor calls)", part_single, {})):
+                k = n_launches(fn)
+                add(cfg, op, nbytes, timed(fn), mix=(1, nbytes // 2 // k, True, k), **kw)
             add(cfg, "metadata", 0, timed(lambda: cp.cp_build_meta(cu, w.total_tokens, w.cp_size, pol,
                                                                      meta=meta.buf)))
             attn = cp.cp_build_attn_meta(meta)
@@ -474,7 +494,7 @@ def per_config(cp, WL, torch, dev, reps: int = 10, ceiling=None, names=None):
         out = [[torch.empty((n, w.heads, w.head_dim), dtype=dt, device=dev) for _ in range(W)]
                for _ in range(2)]
         add(name, "fused grad return dK,dV", 2 * (W + 1) * S * row_in,
-            timed(lambda: cp.cp_grad_return_fused(grads, out, meta)), mix=(W, S * row_in))
+            timed(lambda: cp.cp_grad_return_fused(grads, out, meta)), mix=(W, S * row_in, True, 2))
         slots = [[[torch.empty((n, w.heads, w.head_dim), dtype=dt, device=dev) for _ in range(W)]
                   for _ in range(W)] for _ in range(2)]
         epochs = torch.zeros((W, W), dtype=torch.int32, device=dev)
@@ -488,11 +508,11 @@ def per_config(cp, WL, torch, dev, reps: int = 10, ceiling=None, names=None):
             timed(unfused))
         # accumulate mode: the owner's gradient is read as well (one more row per output row)
         add(name, "fused grad return dK,dV, accumulate", 2 * (W + 2) * S * row_in,
-            timed(lambda: cp.cp_grad_return_fused(grads, out, meta, accumulate=True)), mix=(W + 1, S * row_in))
+            timed(lambda: cp.cp_grad_return_fused(grads, out, meta, accumulate=True)), mix=(W + 1, S * row_in, True, 2))
         # the same tensors under packed-contiguous ownership (owner o: tokens [o S/W, (o+1) S/W))
         meta_pc = cp.cp_build_meta(cu, S, W, cp.CP_POLICY_PACKED_CONTIGUOUS, check=True)
         add(name, "fused grad return dK,dV, packed-contiguous owners", 2 * (W + 1) * S * row_in,
-            timed(lambda: cp.cp_grad_return_fused(grads, out, meta_pc)), mix=(W, S * row_in))
+            timed(lambda: cp.cp_grad_return_fused(grads, out, meta_pc)), mix=(W, S * row_in, True, 2))
 
         def unfused_pc():
             state["e"] += 1
