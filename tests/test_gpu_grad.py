@@ -107,6 +107,24 @@ def test_random_documents(cp, W, in_dt, out_dt):
     run_and_check_full(cp, grads, cu, W, out_dt)
 
 
+@pytest.mark.parametrize("B,H,D", [(4100, 2, 64), (4000, 20, 128)])
+def test_thousands_of_documents(cp, B, H, D):
+    """The gradient return under dual-chunk-swap metadata of more than 3969 documents (a
+    three-round wave search in the scatter's row tiles), 512-byte and 10 KiB fp32 rows:
+    every slot, the unfused and the fused output against the oracle."""
+    say(f"case grad return {B} documents [{H},{D}]")
+    rng = np.random.default_rng(B + 7)
+    lengths = rng.integers(0, 3, size=B) * 8
+    lengths[0] = max(int(lengths[0]), 8)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    W = 4
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(B)
+    grads = [[torch.randn((T, H, D), device=DEV, generator=gen) for _ in range(W)]]
+    run_and_check_full(cp, grads, cu, W, torch.float32)
+
+
 @pytest.mark.parametrize("W,H,D,in_dt,out_dt", [
     (4, 4, 128, torch.float32, torch.float32), (4, 8, 128, torch.float32, torch.bfloat16),
     (8, 4, 128, torch.bfloat16, torch.bfloat16), (4, 4, 128, torch.bfloat16, torch.float32),

@@ -181,6 +181,24 @@ def test_w64_and_many_documents(cp):
     check_layout(cp, x, cu, 4, cp.CP_POLICY_PACKED_CONTIGUOUS)
 
 
+@pytest.mark.parametrize("B,H,D,dtype", [(4100, 2, 8, torch.float32),      # 64 B rows: 4 rows per wave
+                                         (40000, 1, 16, torch.float32),    # 64 B rows, 40000 documents
+                                         (4500, 20, 128, torch.bfloat16),  # 5 KiB rows (the Q,K,V shape)
+                                         (4000, 20, 128, torch.float32)])  # 10 KiB rows: 2 waves per row
+def test_thousands_of_documents(cp, B, H, D, dtype):
+    """Dual-chunk-swap metadata of more than 63^2 = 3969 documents (empty ones among them):
+    the row tiles' wave search over the document table takes three rounds of 64 probes
+    (below that one or two).  Every element of partition and gather against the oracle."""
+    say(f"case {B} documents [{H},{D}] {dtype}")
+    rng = np.random.default_rng(B + H)
+    lengths = rng.integers(0, 4, size=B) * 8
+    lengths[0] = max(int(lengths[0]), 8)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    x = torch.randn((T, H, D), device=DEV).to(dtype)
+    check_layout(cp, x, cu, 4, cp.CP_POLICY_DUAL_CHUNK_SWAP)
+
+
 @pytest.mark.parametrize("H,D,dtype", [(3, 5, torch.bfloat16),     # 30 B rows: 2-byte units
                                        (1, 6, torch.float32),      # 24 B rows: 8-byte units
                                        (3, 3, torch.float32),      # 36 B rows: 4-byte units
