@@ -300,7 +300,7 @@ def load_roofline_lib():
     lib = ctypes.CDLL(path)
     lib.cprl_stream.restype = ctypes.c_int
     lib.cprl_stream.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_int64,
-                                ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+                                ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     return lib
 
 
@@ -308,8 +308,9 @@ class Ceiling:
     """What a plain stream of a read/write mix reaches on this GPU: n_in inputs of
     `nbytes` each read and (write) one output of `nbytes` written, by the streaming
     kernels of libcpthd_roofline.so (full grid, contiguous tiles, 16-byte non-temporal
-    accesses, as the library's kernels), the best of 1, 2 and 3 units per thread (4, 8 and
-    12 KiB tiles).  With `launches` = k, k such streams on k sets of buffers launched back
+    loads, as the library's kernels), the best of 1, 2 and 3 units per thread (4, 8 and
+    12 KiB tiles) and, when writing, of two store policies (non-temporal global stores;
+    buffer stores with the nt and sc1 cache policy).  With `launches` = k, k such streams on k sets of buffers launched back
     to back and timed together (the ceiling of an operation that makes k launches of that
     size).  Timed like per_config: median of `reps` runs per shape, each after a 1 GiB
     write that flushes the last-level cache, with HIP events on the stream the kernels
@@ -340,33 +341,37 @@ class Ceiling:
             sets.append((ins, out, tab, outp))
         sink = ctypes.c_void_p(self.sink.data_ptr())
 
-        def launch(np_):
+        def launch(shape):
+            np_, pol = shape
             stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
             for _, _, tab, outp in sets:
-                st = self.lib.cprl_stream(n_in, tab, outp, nbytes, np_, sink, stream)
+                st = self.lib.cprl_stream(n_in, tab, outp, nbytes, np_, sink, pol, stream)
                 if st != 0:
                     raise RuntimeError(f"cprl_stream: status {st}")
 
         by_shape = {}
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for np_ in (1, 2, 3):
-            launch(np_)
+        shapes = [(np_, pol) for pol in ((0, 1) if write else (0,)) for np_ in (1, 2, 3)]
+        for shape in shapes:
+            launch(shape)
             ts = []
             for _ in range(self.reps):
                 self.flush.fill_(1.0)
                 e0.record()
-                launch(np_)
+                launch(shape)
                 e1.record()
                 torch.cuda.synchronize()
                 ts.append(e0.elapsed_time(e1) * 1000.0)
-            by_shape[np_] = statistics.median(ts)
+            by_shape[shape] = statistics.median(ts)
         best = min(by_shape, key=by_shape.get)
         us = by_shape[best]
         moved = nbytes * (n_in + (1 if write else 0)) * launches
         mix = f"{n_in}:{1 if write else 0}" if n_in else "0:1"
+        policy = ("nt", "nt+sc1")
         res = {"mix": mix, "bytes_per_buffer": nbytes, "moved_bytes": moved, "median_us": round(us, 2),
-               "gbs": round(moved / us / 1e3, 1), "units_per_thread": best,
-               "gbs_by_units_per_thread": {k: round(moved / v / 1e3, 1) for k, v in by_shape.items()}}
+               "gbs": round(moved / us / 1e3, 1), "units_per_thread": best[0], "stores": policy[best[1]],
+               "gbs_by_shape": {f"{k[0]} units/thread, {policy[k[1]]} stores": round(moved / v / 1e3, 1)
+                                for k, v in by_shape.items()}}
         if launches > 1:
             res["launches"] = launches
         self.cache[key] = res

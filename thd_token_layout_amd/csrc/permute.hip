@@ -28,6 +28,19 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// Raw buffer resources: word 3 of the descriptor (32-bit data format, no
+// swizzle) and the cache-policy operand of a store (2 = nt, 16 = sc1).
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kStoreNtSc1 = 2 | 16;
+
+// A pointer every lane holds the same value of, as a wave-uniform value.
+__device__ __forceinline__ char* uniform_ptr(char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<char*>(((uint64_t)hi << 32) | lo);
+}
+
 template <typename U>
 __device__ __forceinline__ U load_nt(const U* p) {
   return __builtin_nontemporal_load(p);
@@ -275,6 +288,7 @@ template <int NP, bool GORDER>
 __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uint32_t upr_magic) {
   __shared__ const u32x4* s_src[kFlatMaxRows];
   __shared__ u32x4* s_dst[kFlatMaxRows];
+  __shared__ int32_t s_rank[kFlatMaxRows];
   __shared__ int32_t s_cu[kFlatMaxDocs + 1];
   __shared__ int32_t s_lcu[kFlatMaxDocs + 1];
   cp_meta_header* h = a.meta;
@@ -338,6 +352,7 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
       char* lptr = a.local_table ? a.table.p[r] + i * a.row_bytes : lbase + ((int64_t)r * n + i) * a.row_bytes;
       s_src[threadIdx.x] = reinterpret_cast<const u32x4*>(a.to_local ? gptr : lptr);
       s_dst[threadIdx.x] = reinterpret_cast<u32x4*>(a.to_local ? lptr : gptr);
+      s_rank[threadIdx.x] = r;
     }
     __syncthreads();
     const int64_t base = u0 - row0 * upr;  // offset of the tile's first unit inside row0
@@ -353,9 +368,23 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
       col[m] = (int64_t)f - (int64_t)row[m] * upr;
       if (ok[m]) v[m] = load_nt(s_src[row[m]] + col[m]);
     }
+    // The tile's written units are contiguous in memory (the parts buffer in
+    // local order, the global tensor in global order, one owner's slot of the
+    // scatter unless the tile straddles two owners): stores through one buffer
+    // resource over them, with the nt and sc1 cache policy.
+    const bool contiguous = GORDER || !a.local_table || wave_uniform(s_rank[0] == s_rank[nrows - 1]);
+    if (contiguous) {
+      char* const wtile = uniform_ptr(reinterpret_cast<char*>(s_dst[0])) + (u0 - row0 * upr) * 16;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(wtile, 0, (int)((u_end - u0) * 16), kRawBufferWord3);
 #pragma unroll
-    for (int m = 0; m < NP; ++m)
-      if (ok[m]) store_nt(s_dst[row[m]] + col[m], v[m]);
+      for (int m = 0; m < NP; ++m)
+        if (ok[m]) __builtin_amdgcn_raw_buffer_store_b128(v[m], rs, (m * kBlock + (int)threadIdx.x) * 16, 0, kStoreNtSc1);
+    } else {
+#pragma unroll
+      for (int m = 0; m < NP; ++m)
+        if (ok[m]) store_nt(s_dst[row[m]] + col[m], v[m]);
+    }
   }
 }
 

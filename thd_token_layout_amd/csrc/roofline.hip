@@ -1,9 +1,11 @@
 // Plain streaming kernels for the benchmark's ceiling measurement: what one
 // MI355X streams for a given read/write mix and size with the library's
 // schedule (a full grid, one contiguous tile of kBlock * NP 16-byte units per
-// workgroup, non-temporal loads and stores) and the best of NP = 1, 2, 3 units
-// per thread.  A plain copy streams best with one unit per thread (4 KiB per
-// workgroup); the library's kernels need 8-20 KiB tiles to amortise their
+// workgroup, non-temporal loads) and the best of NP = 1, 2, 3 units per thread
+// and of two store policies: non-temporal global stores, or buffer stores over
+// the workgroup's tile with the nt and sc1 cache policy (measured faster on
+// MI355X for a copy).  A plain copy streams best with one unit per thread (4 KiB
+// per workgroup); the library's kernels need 8-20 KiB tiles to amortise their
 // per-tile row lookup, so the ceiling is taken over the tile shapes, not at the
 // library's.  The layout, scatter and sum kernels are compared with the stream
 // of the same mix and size.  Built into its own library
@@ -29,7 +31,12 @@ struct InPtrs {
   const u32x4* p[kMaxIn];
 };
 
-template <int NIN, bool WRITE, int NP>
+// Raw buffer descriptor word 3 (32-bit data format, no swizzle) and the store
+// cache policy nt | sc1.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kStoreNtSc1 = 2 | 16;
+
+template <int NIN, bool WRITE, int NP, bool SC1>
 __global__ void __launch_bounds__(kBlock) stream_kernel(InPtrs in, u32x4* out, int64_t units, uint32_t* sink) {
   constexpr int64_t kTile = (int64_t)kBlock * NP;
   const int64_t ntiles = (units + kTile - 1) / kTile;
@@ -48,11 +55,21 @@ __global__ void __launch_bounds__(kBlock) stream_kernel(InPtrs in, u32x4* out, i
         for (int k = 1; k < NIN; ++k) v[m] ^= __builtin_nontemporal_load(in.p[k] + u);
       }
     }
+    if constexpr (WRITE && SC1) {
+      // the tile's units [tile * kTile, min(+kTile, units)) through one buffer resource
+      const int64_t t_units = units - tile * kTile < kTile ? units - tile * kTile : kTile;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<char*>(out + tile * kTile), 0, (int)(t_units * 16), kRawBufferWord3);
 #pragma unroll
-    for (int m = 0; m < NP; ++m) {
-      const int64_t u = tile * kTile + (int64_t)m * kBlock + threadIdx.x;
-      if (WRITE && ok[m]) __builtin_nontemporal_store(v[m], out + u);
-      if (!WRITE && ok[m]) fold ^= v[m];
+      for (int m = 0; m < NP; ++m)
+        if (ok[m]) __builtin_amdgcn_raw_buffer_store_b128(v[m], rs, (m * kBlock + (int)threadIdx.x) * 16, 0, kStoreNtSc1);
+    } else {
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        const int64_t u = tile * kTile + (int64_t)m * kBlock + threadIdx.x;
+        if (WRITE && ok[m]) __builtin_nontemporal_store(v[m], out + u);
+        if (!WRITE && ok[m]) fold ^= v[m];
+      }
     }
   }
   if (!WRITE && fold.x == 0xFFFFFFFFu && fold.y == 0x00000001u && fold.z == 0xFFFFFFFFu && fold.w == 0x00000001u)
@@ -62,13 +79,14 @@ __global__ void __launch_bounds__(kBlock) stream_kernel(InPtrs in, u32x4* out, i
 typedef void (*StreamFn)(InPtrs, u32x4*, int64_t, uint32_t*);
 
 template <int NIN, int NP>
-StreamFn pick_np(bool write) {
-  return write ? stream_kernel<NIN, true, NP> : stream_kernel<NIN, false, NP>;
+StreamFn pick_np(bool write, bool sc1) {
+  return !write ? stream_kernel<NIN, false, NP, false>
+                : sc1 ? stream_kernel<NIN, true, NP, true> : stream_kernel<NIN, true, NP, false>;
 }
 
 template <int NIN>
-StreamFn pick(bool write, int np) {
-  return np == 1 ? pick_np<NIN, 1>(write) : np == 2 ? pick_np<NIN, 2>(write) : pick_np<NIN, 3>(write);
+StreamFn pick(bool write, int np, bool sc1) {
+  return np == 1 ? pick_np<NIN, 1>(write, sc1) : np == 2 ? pick_np<NIN, 2>(write, sc1) : pick_np<NIN, 3>(write, sc1);
 }
 
 }  // namespace
@@ -77,14 +95,16 @@ extern "C" {
 
 // Stream n_in (0..9) inputs of `bytes` each into `out` (NULL: read only), or
 // write `out` alone (n_in = 0), with `units_per_thread` (1..3) 16-byte units
-// per thread and tile.  bytes must be a positive multiple of 16 and every
+// per thread and tile; `store_policy` 0: non-temporal global stores, 1: buffer
+// stores with nt | sc1.  bytes must be a positive multiple of 16 and every
 // pointer 16-byte aligned; read-only runs need `sink` (>= 4 KiB, never written
 // in practice).  Asynchronous on `stream`.  Returns 0, or -1 on bad arguments
 // (nothing launched), or the HIP error of the launch.
 int cprl_stream(int n_in, const void* const* in, void* out, int64_t bytes, int units_per_thread, void* sink,
-                hipStream_t stream) {
+                int store_policy, hipStream_t stream) {
   if (n_in < 0 || n_in > kMaxIn || bytes <= 0 || bytes % 16 != 0) return -1;
   if (units_per_thread < 1 || units_per_thread > 3) return -1;
+  if (store_policy != 0 && store_policy != 1) return -1;
   if (n_in == 0 && out == nullptr) return -1;
   if (out == nullptr && sink == nullptr) return -1;
   InPtrs p{};
@@ -98,9 +118,11 @@ int cprl_stream(int n_in, const void* const* in, void* out, int64_t bytes, int u
   int64_t blocks = (units + (int64_t)kBlock * np - 1) / ((int64_t)kBlock * np);
   if (blocks > kMaxGrid) blocks = kMaxGrid;
   const bool w = out != nullptr;
-  StreamFn fns[kMaxIn + 1] = {pick<0>(true, np), pick<1>(w, np), pick<2>(w, np), pick<3>(w, np),
-                              pick<4>(w, np),    pick<5>(w, np), pick<6>(w, np), pick<7>(w, np),
-                              pick<8>(w, np),    pick<9>(w, np)};
+  const bool sc1 = store_policy == 1;
+  StreamFn fns[kMaxIn + 1] = {pick<0>(true, np, sc1), pick<1>(w, np, sc1), pick<2>(w, np, sc1),
+                              pick<3>(w, np, sc1),    pick<4>(w, np, sc1), pick<5>(w, np, sc1),
+                              pick<6>(w, np, sc1),    pick<7>(w, np, sc1), pick<8>(w, np, sc1),
+                              pick<9>(w, np, sc1)};
   hipLaunchKernelGGL(fns[n_in], dim3((unsigned)blocks), dim3(kBlock), 0, stream, p, static_cast<u32x4*>(out),
                      units, static_cast<uint32_t*>(sink));
   return (int)hipGetLastError();
