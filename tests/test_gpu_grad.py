@@ -107,6 +107,35 @@ def test_random_documents(cp, W, in_dt, out_dt):
     run_and_check_full(cp, grads, cu, W, out_dt)
 
 
+@pytest.mark.parametrize("policy", ["dual_chunk_swap", "packed_contiguous"])
+@pytest.mark.parametrize("T", [56, 200])
+def test_unit_tiles_straddling_owners(cp, policy, T):
+    """The scatter's unit tiles write each tile through one buffer resource when its rows lie
+    in one owner's slot, and row by row when the tile straddles two owners: with 2 KiB rows a
+    tile covers 6 rows, so T/W = 14 or 50 rows per owner puts owner boundaries inside tiles.
+    The unit-tile kernel is the one launched (checked), every slot and output against the
+    oracle."""
+    W, H, D = 4, 4, 128
+    say(f"case straddling tiles {policy} T={T}")
+    cu = np.array([0, 24, T], dtype=np.int32)  # two documents, each a multiple of 2W
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(T)
+    grads = [[torch.randn((T, H, D), device=DEV, generator=gen) for _ in range(W)]]
+    pol = cp.POLICY[policy]
+    meta = cp.cp_build_meta(torch.from_numpy(cu).to(DEV), T, W, pol, check=True)
+    slots, out = alloc(grads, W, torch.float32)
+    cp.cp_profile_enable(True)
+    cp.cp_grad_return(grads, slots, out, meta)
+    prof = cp.cp_profile_read()
+    cp.cp_profile_enable(False)
+    assert any(k.startswith("permute_flat") for k in prof), prof
+    ref_slots, ref_out = O.grad_return([to_np(g) for g in grads[0]], cu, W, "f32", "f32", policy=policy)
+    for o in range(W):
+        for w in range(W):
+            assert bits_equal(to_np(slots[0][o][w]), ref_slots[o][w]), (o, w)
+        assert bits_equal(to_np(out[0][o]), ref_out[o]), o
+
+
 @pytest.mark.parametrize("B,H,D", [(4100, 2, 64), (4000, 20, 128)])
 def test_thousands_of_documents(cp, B, H, D):
     """The gradient return under dual-chunk-swap metadata of more than 3969 documents (a
