@@ -149,6 +149,17 @@ enum cp_dtype {
  *                        (r+1)*T/W} + {T/W}, i.e. the documents clipped at the
  *                        rank's slice, without empty segments; n_local[r] = its
  *                        length - 1; the entries after it are T/W.
+ *
+ * Optional row maps (dual-chunk-swap with more than 64 documents; with fewer
+ * the kernels stage the document table itself), written when the buffer holds
+ * at least cp_meta_bytes_row_maps(B, W, T) bytes; cp_meta_header.row_maps is
+ * then 1:
+ *   offset cp_meta_bytes(B, W)       int32 row_of_local[T]: global row of the
+ *                                    flat local row p = r*(T/W) + i
+ *   offset cp_meta_bytes(B, W) + 4T  int32 local_of_row[T]: the inverse
+ * The permutation kernels then find any row's source and destination with one
+ * load instead of searching the document table (the tables alone give the same
+ * results; the maps are a lookup aid, 8 bytes per token).
  */
 #define CP_META_MAGIC 0x48545043u /* "CPTH" */
 
@@ -176,13 +187,19 @@ typedef struct cp_meta_header {
   int64_t total_tokens;       /* T                                               */
   int64_t local_tokens;       /* T / W                                           */
   uint64_t wait_timeout_ranks;/* bit o set: owner o's last epoch wait timed out  */
-  int32_t reserved[4];
+  int32_t row_maps;           /* 1: the row maps follow the tables, else 0       */
+  int32_t reserved[3];
 } cp_meta_header;
 
 /* Bytes the caller must allocate for the metadata of B documents and W ranks
  * (a multiple of 256).  Returns 0 for B outside [0, 2^31 - 2] or W outside
  * [1, CP_MAX_CP_SIZE]. */
 size_t cp_meta_bytes(int32_t num_docs, int32_t cp_size);
+
+/* Bytes for the metadata plus the optional row maps of T tokens:
+ * cp_meta_bytes(B, W) + 8T rounded up to a multiple of 256.  Returns 0 for B
+ * or W out of range (as cp_meta_bytes) or T outside [0, 2^31). */
+size_t cp_meta_bytes_row_maps(int32_t num_docs, int32_t cp_size, int64_t total_tokens);
 
 /*
  * cp_build_meta - validate cu_seqlens and build the per-rank metadata.
@@ -197,7 +214,10 @@ size_t cp_meta_bytes(int32_t num_docs, int32_t cp_size);
  *   total_tokens  T, 0 <= T < 2^31
  *   cp_size       W in [1, 64]
  *   policy        enum cp_policy
- *   meta          device buffer of at least meta_bytes >= cp_meta_bytes(B, W)
+ *   meta          device buffer of at least meta_bytes >= cp_meta_bytes(B, W),
+ *                 16-byte aligned; under dual-chunk-swap with B > 64 and
+ *                 meta_bytes >= cp_meta_bytes_row_maps(B, W, T) the row maps
+ *                 are written too
  * Host errors: CP_ERR_ARG (range, NULL), CP_ERR_SHAPE (packed-contiguous with
  * T % W != 0; meta_bytes too small), CP_ERR_DEVICE, CP_ERR_ALIAS (meta overlaps
  * cu_seqlens), CP_ERR_HIP.  Data errors (cu[0] != 0, decreasing cu, cu[B] != T,

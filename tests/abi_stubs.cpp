@@ -6,7 +6,7 @@
 
 namespace cpthd {
 
-hipError_t launch_build_meta(const int32_t*, int32_t, int64_t, int32_t, int32_t, void*, hipStream_t) {
+hipError_t launch_build_meta(const int32_t*, int32_t, int64_t, int32_t, int32_t, bool, void*, hipStream_t) {
   return hipErrorNotSupported;
 }
 hipError_t launch_build_attn_meta(cp_meta_header*, int32_t, int32_t, void*, hipStream_t) { return hipErrorNotSupported; }

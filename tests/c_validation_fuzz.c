@@ -67,6 +67,7 @@ int main(int argc, char** argv) {
     int32_t flags = 0;
     uint64_t timeouts = 0;
     (void)cp_meta_bytes(pick32(), pick32());
+    (void)cp_meta_bytes_row_maps(pick32(), pick32(), pick64());
     (void)cp_attn_meta_bytes(pick32(), pick32());
     (void)cp_allreduce_signal_bytes(pick32());
     (void)cp_status_string(pick32());

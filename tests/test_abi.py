@@ -70,6 +70,16 @@ def test_meta_bytes_closed_form(cp):
     assert cp.cp_meta_bytes(3, 65) == 0
 
 
+def test_meta_bytes_row_maps_closed_form(cp):
+    """The tables, then two int32 row maps of T entries, rounded up to 256 bytes."""
+    for B, W, T in ((0, 1, 0), (1, 4, 8), (3, 2, 48), (115, 4, 262144), (1000, 64, 128000), (2, 4, (1 << 31) - 8)):
+        assert cp.cp_meta_bytes_row_maps(B, W, T) == cp.cp_meta_bytes(B, W) + (8 * T + 255) // 256 * 256
+    assert cp.cp_meta_bytes_row_maps(-1, 4, 8) == 0
+    assert cp.cp_meta_bytes_row_maps(3, 65, 8) == 0
+    assert cp.cp_meta_bytes_row_maps(3, 4, -1) == 0
+    assert cp.cp_meta_bytes_row_maps(3, 4, 1 << 31) == 0
+
+
 def test_attn_meta_bytes_closed_form(cp):
     for B in (0, 1, 3, 115, 1000):
         for W in (1, 2, 4, 8, 64):

@@ -21,9 +21,9 @@ def cp():
     return cpthd
 
 
-def build(cp, cu_np, T, W, policy, check=True):
+def build(cp, cu_np, T, W, policy, check=True, row_maps=True):
     cu = torch.from_numpy(np.asarray(cu_np, dtype=np.int32)).to(DEV)
-    return cp.cp_build_meta(cu, T, W, policy, check=check)
+    return cp.cp_build_meta(cu, T, W, policy, check=check, row_maps=row_maps)
 
 
 def check_meta_against_oracle(cp, meta, cu_np, T, W, pol):
@@ -33,11 +33,11 @@ def check_meta_against_oracle(cp, meta, cu_np, T, W, pol):
     assert bits_equal(n_local.numpy(), ref_n), (n_local, ref_n)
 
 
-def check_layout(cp, x, cu_np, W, pol_code, full=True, sample_rows=4096, seed=0):
+def check_layout(cp, x, cu_np, W, pol_code, full=True, sample_rows=4096, seed=0, row_maps=True):
     """partition vs oracle, gather vs oracle, round trip; returns parts."""
     T = x.shape[0]
     pol = policy_name(pol_code)
-    meta = build(cp, cu_np, T, W, pol_code)
+    meta = build(cp, cu_np, T, W, pol_code, row_maps=row_maps)
     check_meta_against_oracle(cp, meta, cu_np, T, W, pol)
     parts = cp.cp_partition_thd(x, meta)
     back = cp.cp_gather_thd(parts, meta)
@@ -181,22 +181,53 @@ def test_w64_and_many_documents(cp):
     check_layout(cp, x, cu, 4, cp.CP_POLICY_PACKED_CONTIGUOUS)
 
 
+@pytest.mark.parametrize("row_maps", [False, True])
 @pytest.mark.parametrize("B,H,D,dtype", [(4100, 2, 8, torch.float32),      # 64 B rows: 4 rows per wave
                                          (40000, 1, 16, torch.float32),    # 64 B rows, 40000 documents
                                          (4500, 20, 128, torch.bfloat16),  # 5 KiB rows (the Q,K,V shape)
                                          (4000, 20, 128, torch.float32)])  # 10 KiB rows: 2 waves per row
-def test_thousands_of_documents(cp, B, H, D, dtype):
-    """Dual-chunk-swap metadata of more than 63^2 = 3969 documents (empty ones among them):
-    the row tiles' wave search over the document table takes three rounds of 64 probes
-    (below that one or two).  Every element of partition and gather against the oracle."""
-    say(f"case {B} documents [{H},{D}] {dtype}")
+def test_thousands_of_documents(cp, B, H, D, dtype, row_maps):
+    """Dual-chunk-swap metadata of more than 63^2 = 3969 documents (empty ones among them),
+    with and without the row maps: without them the row tiles' wave search over the document
+    table takes three rounds of 64 probes (below that one or two); with them the unit tiles
+    look rows up in the maps (rows of at least ~1 KiB).  Every element of partition and gather
+    against the oracle."""
+    say(f"case {B} documents [{H},{D}] {dtype} row maps {row_maps}")
     rng = np.random.default_rng(B + H)
     lengths = rng.integers(0, 4, size=B) * 8
     lengths[0] = max(int(lengths[0]), 8)
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     T = int(cu[-1])
     x = torch.randn((T, H, D), device=DEV).to(dtype)
-    check_layout(cp, x, cu, 4, cp.CP_POLICY_DUAL_CHUNK_SWAP)
+    check_layout(cp, x, cu, 4, cp.CP_POLICY_DUAL_CHUNK_SWAP, row_maps=row_maps)
+
+
+@pytest.mark.parametrize("B,W,T", [(65, 4, 65 * 8 * 3), (200, 8, 200 * 16 * 2), (3000, 2, 3000 * 4 * 5),
+                                   (66, 64, 66 * 128)])
+def test_row_maps_equal_the_oracle_map(cp, B, W, T):
+    """The row maps cp_build_meta writes (more than 64 documents, a buffer of
+    cp_meta_bytes_row_maps bytes) hold exactly the oracle's ownership map: row_of_local[r n + i]
+    is the global row of rank r's local row i, local_of_row its inverse.  Fewer documents, or
+    a buffer of cp_meta_bytes only, give no maps (header field 0)."""
+    say(f"case row maps B={B} W={W} T={T}")
+    rng = np.random.default_rng(B * W)
+    lengths = rng.multinomial(T // (2 * W) - B, np.ones(B) / B) * 2 * W + 2 * W
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    assert cu[-1] == T
+    pol = cp.CP_POLICY_DUAL_CHUNK_SWAP
+    meta = build(cp, cu, T, W, pol)
+    assert meta.buf.numel() >= cp.cp_meta_bytes_row_maps(B, W, T)
+    l2g, g2l = cp.read_row_maps(meta)
+    ref = O.partition(np.arange(T, dtype=np.int64)[:, None], cu, W, policy_name(pol)).reshape(-1)
+    assert (l2g.numpy() == ref).all()
+    inv = np.empty(T, dtype=np.int64)
+    inv[ref] = np.arange(T)
+    assert (g2l.numpy() == inv).all()
+    # no maps: a buffer of the tables alone, or <= 64 documents
+    small = build(cp, cu, T, W, pol, row_maps=False)
+    assert cp.read_row_maps(small) is None
+    few = build(cp, np.array([0, T], dtype=np.int32), T, W, pol)
+    assert cp.read_row_maps(few) is None
 
 
 @pytest.mark.parametrize("H,D,dtype", [(3, 5, torch.bfloat16),     # 30 B rows: 2-byte units

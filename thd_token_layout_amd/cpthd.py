@@ -58,6 +58,8 @@ _i32, _i64, _u32, _u64, _sz = _c.c_int32, _c.c_int64, _c.c_uint32, _c.c_uint64, 
 
 lib.cp_meta_bytes.restype = _sz
 lib.cp_meta_bytes.argtypes = [_i32, _i32]
+lib.cp_meta_bytes_row_maps.restype = _sz
+lib.cp_meta_bytes_row_maps.argtypes = [_i32, _i32, _i64]
 lib.cp_build_meta.restype = _c.c_int
 lib.cp_build_meta.argtypes = [_vp, _i32, _i64, _i32, _i32, _vp, _sz, _vp]
 lib.cp_meta_status.restype = _c.c_int
@@ -190,10 +192,16 @@ def cp_meta_bytes(num_docs: int, cp_size: int) -> int:
     return lib.cp_meta_bytes(num_docs, cp_size)
 
 
+def cp_meta_bytes_row_maps(num_docs: int, cp_size: int, total_tokens: int) -> int:
+    return lib.cp_meta_bytes_row_maps(num_docs, cp_size, total_tokens)
+
+
 def cp_build_meta(cu_seqlens: torch.Tensor, total_tokens: int, cp_size: int, policy,
-                  meta: Optional[torch.Tensor] = None, stream=None, check: bool = False) -> Meta:
+                  meta: Optional[torch.Tensor] = None, stream=None, check: bool = False,
+                  row_maps: bool = True) -> Meta:
     """Validate cu_seqlens on the device and build per-rank metadata.
 
+    A new buffer holds the row maps too under dual-chunk-swap (row_maps=True).
     With check=True the stream is synchronized and a data error raises CpError.
     """
     if isinstance(policy, str):
@@ -202,6 +210,8 @@ def cp_build_meta(cu_seqlens: torch.Tensor, total_tokens: int, cp_size: int, pol
         raise TypeError("cu_seqlens must be int32")
     B = cu_seqlens.numel() - 1
     nbytes = cp_meta_bytes(B, cp_size)
+    if row_maps and policy == CP_POLICY_DUAL_CHUNK_SWAP and total_tokens > 0:
+        nbytes = cp_meta_bytes_row_maps(B, cp_size, int(total_tokens)) or nbytes
     if meta is None:
         meta = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=cu_seqlens.device)
     st = lib.cp_build_meta(_ptr(cu_seqlens), B, int(total_tokens), int(cp_size), int(policy),
@@ -234,6 +244,18 @@ def read_local_cu(meta: Meta):
     local = words[base: base + W * (B + 1)].reshape(W, B + 1).clone()
     n_local = words[base + W * (B + 1): base + W * (B + 1) + W].clone()
     return local, n_local
+
+
+def read_row_maps(meta: Meta):
+    """(row_of_local [T], local_of_row [T]) int32 copied from the device metadata, or None
+    when it was built without them (synchronizes)."""
+    header = meta.buf[:64].cpu().view(torch.int32)
+    if int(header[12]) != 1:  # cp_meta_header.row_maps (byte offset 48)
+        return None
+    T = meta.total_tokens
+    off = cp_meta_bytes(meta.num_docs, meta.cp_size)
+    words = meta.buf[off: off + 8 * T].cpu().view(torch.int32)
+    return words[:T].clone(), words[T:].clone()
 
 
 def cp_attn_meta_bytes(num_docs: int, cp_size: int) -> int:
@@ -455,7 +477,7 @@ def cp_profile_read(capacity: int = 64):
     return res
 
 
-EXPORTED = ["cp_meta_bytes", "cp_build_meta", "cp_meta_status", "cp_attn_meta_bytes", "cp_build_attn_meta",
+EXPORTED = ["cp_meta_bytes", "cp_meta_bytes_row_maps", "cp_build_meta", "cp_meta_status", "cp_attn_meta_bytes", "cp_build_attn_meta",
             "cp_partition_thd", "cp_gather_thd",
             "cp_partition_thd_multi", "cp_gather_thd_multi",
             "cp_grad_return", "cp_grad_return_noalloc", "cp_grad_return_fused", "cp_slot_sum", "cp_allreduce",

@@ -33,6 +33,7 @@ struct Range {
 struct MetaRecord {
   int32_t policy, num_docs, cp_size;
   int64_t total_tokens;
+  bool row_maps;
 };
 std::mutex g_records_mu;
 std::unordered_map<const void*, MetaRecord> g_records;
@@ -49,6 +50,7 @@ void remember_meta(const void* meta, const MetaRecord& r) {
 void hint_from_record(const void* meta, int64_t total_tokens, int32_t cp_size, PermuteArgs* a) {
   a->hint_policy = -1;
   a->hint_docs = -1;
+  a->hint_row_maps = false;
   std::lock_guard<std::mutex> lock(g_records_mu);
   auto it = g_records.find(meta);
   if (it == g_records.end()) return;
@@ -56,6 +58,7 @@ void hint_from_record(const void* meta, int64_t total_tokens, int32_t cp_size, P
   if (r.total_tokens != total_tokens || (cp_size > 0 && r.cp_size != cp_size)) return;
   a->hint_policy = r.policy;
   a->hint_docs = r.num_docs;
+  a->hint_row_maps = r.row_maps;
 }
 
 Range range_of(const void* p, int64_t bytes) {
@@ -89,7 +92,9 @@ MetaSpan meta_span(const void* meta, int64_t total_tokens, int32_t cp_size, int3
     auto it = g_records.find(meta);
     if (it != g_records.end() && it->second.total_tokens == total_tokens &&
         (cp_size <= 0 || it->second.cp_size == cp_size))
-      bytes = (int64_t)cp_meta_bytes(it->second.num_docs, it->second.cp_size);
+      bytes = (int64_t)(it->second.row_maps
+                            ? cp_meta_bytes_row_maps(it->second.num_docs, it->second.cp_size, total_tokens)
+                            : cp_meta_bytes(it->second.num_docs, it->second.cp_size));
   }
   if (bytes < (int64_t)sizeof(cp_meta_header)) bytes = (int64_t)sizeof(cp_meta_header);
   const uintptr_t a = reinterpret_cast<uintptr_t>(meta);
@@ -273,8 +278,13 @@ extern "C" {
 
 size_t cp_meta_bytes(int32_t num_docs, int32_t cp_size) {
   if (num_docs < 0 || num_docs >= INT32_MAX || cp_size < 1 || cp_size > CP_MAX_CP_SIZE) return 0;
-  const size_t bytes = 64 + 4 * ((size_t)num_docs + 1) * ((size_t)cp_size + 1) + 4 * (size_t)cp_size;
-  return (bytes + 255) & ~(size_t)255;
+  return (size_t)meta_tables_bytes(num_docs, cp_size);
+}
+
+size_t cp_meta_bytes_row_maps(int32_t num_docs, int32_t cp_size, int64_t total_tokens) {
+  const size_t tables = cp_meta_bytes(num_docs, cp_size);
+  if (tables == 0 || total_tokens < 0 || total_tokens > INT32_MAX) return 0;
+  return tables + (((size_t)total_tokens * 8 + 255) & ~(size_t)255);
 }
 
 int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tokens,
@@ -286,18 +296,25 @@ int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tok
   if (policy != CP_POLICY_DUAL_CHUNK_SWAP && policy != CP_POLICY_PACKED_CONTIGUOUS) return CP_ERR_ARG;
   if (policy == CP_POLICY_PACKED_CONTIGUOUS && total_tokens % cp_size != 0) return CP_ERR_SHAPE;
   if (meta_bytes < cp_meta_bytes(num_docs, cp_size)) return CP_ERR_SHAPE;
+  // Row maps when the buffer holds them and they help: dual-chunk-swap with
+  // more documents than the unit tiles stage in LDS (packed-contiguous rows
+  // follow from arithmetic; a few documents are searched in LDS as fast).
+  const bool row_maps = policy == CP_POLICY_DUAL_CHUNK_SWAP && total_tokens > 0 && num_docs > kStagedMaxDocs &&
+                        meta_bytes >= cp_meta_bytes_row_maps(num_docs, cp_size, total_tokens);
+  const int64_t used = (int64_t)(row_maps ? cp_meta_bytes_row_maps(num_docs, cp_size, total_tokens)
+                                          : cp_meta_bytes(num_docs, cp_size));
   int dev, st;
   if ((st = current_device(&dev)) != CP_OK) return st;
   AllocCache cache;
   if ((st = check_device_buf(cu_seqlens, 4 * ((int64_t)num_docs + 1), dev, &cache)) != CP_OK) return st;
-  if ((st = check_device_buf(meta, (int64_t)cp_meta_bytes(num_docs, cp_size), dev, &cache)) != CP_OK) return st;
+  if ((st = check_device_buf(meta, used, dev, &cache)) != CP_OK) return st;
   if ((st = check_alias({range_of(meta, (int64_t)meta_bytes)},
                         {range_of(cu_seqlens, 4 * ((int64_t)num_docs + 1))})) != CP_OK)
     return st;
-  if ((st = hip_status(launch_build_meta(cu_seqlens, num_docs, total_tokens, cp_size, policy, meta,
+  if ((st = hip_status(launch_build_meta(cu_seqlens, num_docs, total_tokens, cp_size, policy, row_maps, meta,
                                          reinterpret_cast<hipStream_t>(stream)))) != CP_OK)
     return st;
-  remember_meta(meta, MetaRecord{policy, num_docs, cp_size, total_tokens});
+  remember_meta(meta, MetaRecord{policy, num_docs, cp_size, total_tokens, row_maps});
   return CP_OK;
 }
 

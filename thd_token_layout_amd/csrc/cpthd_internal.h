@@ -22,6 +22,15 @@ __host__ __device__ inline int64_t meta_local_cu_offset(int32_t B) { return 64 +
 __host__ __device__ inline int64_t meta_n_local_offset(int32_t B, int32_t W) {
   return 64 + 4 * ((int64_t)B + 1) * ((int64_t)W + 1);
 }
+// Unit tiles stage the dual-chunk-swap document tables of up to this many
+// documents in LDS; cp_build_meta writes the row maps only above it.
+constexpr int32_t kStagedMaxDocs = 64;
+
+// cp_meta_bytes(B, W): header and tables, rounded up to 256 bytes; the
+// optional row maps (row_of_local[T], then local_of_row[T]) start there.
+__host__ __device__ inline int64_t meta_tables_bytes(int32_t B, int32_t W) {
+  return (meta_n_local_offset(B, W) + 4 * (int64_t)W + 255) / 256 * 256;
+}
 
 // Fixed-capacity pointer table passed by value in the kernel arguments.
 struct RankPtrs {
@@ -42,8 +51,10 @@ inline int dtype_bytes(int32_t dt) {
 }
 
 // ---------------------------------------------------------------- metadata
+// row_maps: also write the row maps after the tables (dual-chunk-swap only;
+// the caller has checked that the buffer holds them).
 hipError_t launch_build_meta(const int32_t* cu, int32_t B, int64_t T, int32_t W, int32_t policy,
-                             void* meta, hipStream_t stream);
+                             bool row_maps, void* meta, hipStream_t stream);
 
 // Attention-step records (layout documented in cpthd.h): 64-byte header, then
 // 2W records of 32 + 16(B+1) bytes.
@@ -78,6 +89,7 @@ struct PermuteArgs {
   // kernels read the metadata itself on the device.
   int32_t hint_policy;
   int32_t hint_docs;
+  bool hint_row_maps;  // the metadata was built with its row maps
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 

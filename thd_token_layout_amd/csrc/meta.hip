@@ -25,7 +25,7 @@ namespace {
 
 __global__ void __launch_bounds__(kBlock)
 build_meta_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t T, int32_t W,
-                  int32_t policy, char* __restrict__ meta) {
+                  int32_t policy, int32_t row_maps, char* __restrict__ meta) {
   const int r = blockIdx.x;  // one workgroup per rank
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -106,9 +106,38 @@ build_meta_kernel(const int32_t* __restrict__ cu, int32_t B, int64_t T, int32_t 
       h->total_tokens = T;
       h->local_tokens = n;
       h->wait_timeout_ranks = 0;
-      for (int k = 0; k < 4; ++k) h->reserved[k] = 0;
+      h->row_maps = row_maps;
+      for (int k = 0; k < 3; ++k) h->reserved[k] = 0;
       h->magic = CP_META_MAGIC;
     }
+  }
+}
+
+// The dual-chunk-swap row maps after the tables (layout in cpthd.h): thread p
+// maps flat local row p = r n + i to its global row through the rank-0 local
+// cu (= cu / W) and writes both directions.  Runs after build_meta_kernel on
+// the same stream; writes nothing when that kernel flagged the cu_seqlens.
+__global__ void __launch_bounds__(kBlock) build_row_maps_kernel(char* __restrict__ meta) {
+  const cp_meta_header* h = reinterpret_cast<const cp_meta_header*>(meta);
+  if (h->magic != CP_META_MAGIC || (h->flags & CP_META_BUILD_MASK) != 0 || h->row_maps != 1) return;
+  const int32_t W = h->cp_size;
+  const int32_t B = h->num_docs;
+  const int64_t T = h->total_tokens;
+  const int64_t n = h->local_tokens;
+  const int32_t* cu = reinterpret_cast<const int32_t*>(meta + meta_cu_offset());
+  const int32_t* lcu = reinterpret_cast<const int32_t*>(meta + meta_local_cu_offset(B));
+  int32_t* row_of_local = reinterpret_cast<int32_t*>(meta + meta_tables_bytes(B, W));
+  int32_t* local_of_row = row_of_local + T;
+  for (int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x; p < T; p += (int64_t)gridDim.x * kBlock) {
+    const int32_t r = (int32_t)(p / n);
+    const int64_t i = p - (int64_t)r * n;
+    const int32_t b = find_doc(lcu, B, i);
+    const int64_t lstart = lcu[b];
+    const int64_t c = (lcu[b + 1] - lstart) >> 1;
+    const int64_t j = i - lstart;
+    const int64_t g = j < c ? cu[b] + (int64_t)r * c + j : cu[b] + (int64_t)(2 * W - 1 - r) * c + (j - c);
+    row_of_local[p] = (int32_t)g;
+    local_of_row[g] = (int32_t)p;
   }
 }
 
@@ -251,11 +280,18 @@ hipError_t launch_build_attn_meta(cp_meta_header* meta, int32_t B, int32_t W, vo
 }
 
 hipError_t launch_build_meta(const int32_t* cu, int32_t B, int64_t T, int32_t W, int32_t policy,
-                             void* meta, hipStream_t stream) {
+                             bool row_maps, void* meta, hipStream_t stream) {
   profile_before("build_meta", stream);
   hipLaunchKernelGGL(build_meta_kernel, dim3(W), dim3(kBlock), 0, stream, cu, B, T, W, policy,
-                     static_cast<char*>(meta));
+                     row_maps ? 1 : 0, static_cast<char*>(meta));
   hipError_t e = hipGetLastError();
+  profile_after(stream);
+  if (e != hipSuccess || !row_maps || T == 0) return e;
+  int64_t blocks = (T + kBlock - 1) / kBlock;
+  if (blocks > kMaxGrid) blocks = kMaxGrid;
+  profile_before("build_row_maps", stream);
+  hipLaunchKernelGGL(build_row_maps_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, static_cast<char*>(meta));
+  e = hipGetLastError();
   profile_after(stream);
   return e;
 }

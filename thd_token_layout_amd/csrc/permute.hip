@@ -285,7 +285,7 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
 // single-document metadata, +3..5% at 32-64 documents, slower from ~128
 // documents (the staging then costs more than it saves).
 constexpr int kFlatMaxRows = 16;
-constexpr int kFlatMaxDocs = 64;
+constexpr int kFlatMaxDocs = kStagedMaxDocs;
 
 template <int NP, bool GORDER>
 __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uint32_t upr_magic) {
@@ -303,8 +303,14 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
   const int32_t B = hv.num_docs;
   const int64_t n = hv.local_tokens;
   const bool dcs = hv.policy == CP_POLICY_DUAL_CHUNK_SWAP;
-  // Document tables: staged in LDS when small enough, else read from the metadata.
-  const bool staged = dcs && B <= kFlatMaxDocs;
+  // Dual-chunk-swap rows: from the row maps when the metadata has them (one
+  // load per row), else from the document tables, staged in LDS when small
+  // enough (searched there), else searched in the metadata.
+  const bool maps = dcs && hv.row_maps == 1;
+  const int32_t* row_of_local = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(h) +
+                                                                 meta_tables_bytes(B, W));
+  const int32_t* local_of_row = row_of_local + T;
+  const bool staged = dcs && !maps && B <= kFlatMaxDocs;
   if (staged) {
     const int32_t* mcu = meta_cu(h);
     const int32_t* mlcu = meta_local_cu0(h, B);
@@ -334,7 +340,20 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
       const int64_t p = row0 + threadIdx.x;
       int32_t r;
       int64_t i, g;
-      if constexpr (GORDER) {
+      if (maps) {
+        // map entries are clamped to [0, T): rows stay inside the tensors
+        // whatever the buffer holds
+        const int64_t q = GORDER ? (int64_t)local_of_row[p] : p;
+        const int64_t qc = q < 0 ? 0 : (q >= T ? T - 1 : q);
+        r = (int32_t)(qc / n);
+        i = qc - (int64_t)r * n;
+        if constexpr (GORDER) {
+          g = p;
+        } else {
+          const int64_t gm = row_of_local[p];
+          g = gm < 0 ? 0 : (gm >= T ? T - 1 : gm);
+        }
+      } else if constexpr (GORDER) {
         g = p;
         if (dcs) {
           GCursor gc;
@@ -426,15 +445,17 @@ Variant g_variants[4][7] = {
     CP_VARIANTS_FOR(unsigned short, "2B"),
 };
 
-// Flat tiles (see permute_flat_kernel): NP units per thread, by the policy and
-// document count the host recorded when it built the metadata.  Swept on
-// MI355X over 2, 5, 8 and 10 KiB rows: packed-contiguous streams best with 2
-// units per thread (8 KiB tiles), dual-chunk-swap with <= 64 documents with 3.
-// 0: keep the row tiles.
+// Flat tiles (see permute_flat_kernel): NP units per thread, by the policy,
+// document count and row maps the host recorded when it built the metadata.
+// Swept on MI355X over 2, 5, 8 and 10 KiB rows: packed-contiguous streams best
+// with 2 units per thread (8 KiB tiles), dual-chunk-swap with 3 (with <= 64
+// documents, or any number when the row maps were built).  0: keep the row
+// tiles.
 int flat_units_per_thread(const PermuteArgs& a, int64_t upr) {
   int np = 0;
   if (a.hint_policy == CP_POLICY_PACKED_CONTIGUOUS) np = 2;
-  else if (a.hint_policy == CP_POLICY_DUAL_CHUNK_SWAP && a.hint_docs >= 1 && a.hint_docs <= kFlatMaxDocs) np = 3;
+  else if (a.hint_policy == CP_POLICY_DUAL_CHUNK_SWAP && a.hint_docs >= 1 &&
+           (a.hint_docs <= kFlatMaxDocs || a.hint_row_maps)) np = 3;
   if (np == 0 || upr <= 0) return 0;
   const int64_t tile_units = (int64_t)kBlock * np;
   if (tile_units / upr + 2 > kFlatMaxRows) return 0;            // short rows: row tiles
@@ -442,8 +463,11 @@ int flat_units_per_thread(const PermuteArgs& a, int64_t upr) {
   return np;
 }
 
-const char* const kFlatNames[2][2] = {{"permute_flat<16B,2>", "permute_flat<16B,2,g>"},
-                                      {"permute_flat<16B,3>", "permute_flat<16B,3,g>"}};
+// [NP - 2][order][row maps]
+const char* const kFlatNames[2][2][2] = {{{"permute_flat<16B,2>", "permute_flat<16B,2,maps>"},
+                                          {"permute_flat<16B,2,g>", "permute_flat<16B,2,maps,g>"}},
+                                         {{"permute_flat<16B,3>", "permute_flat<16B,3,maps>"},
+                                          {"permute_flat<16B,3,g>", "permute_flat<16B,3,maps,g>"}}};
 
 }  // namespace
 
@@ -479,7 +503,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   if (np != 0) {
     flat_fn = np == 2 ? (order ? permute_flat_kernel<2, true> : permute_flat_kernel<2, false>)
                       : (order ? permute_flat_kernel<3, true> : permute_flat_kernel<3, false>);
-    name = kFlatNames[np - 2][order];
+    name = kFlatNames[np - 2][order][a.hint_row_maps ? 1 : 0];
     tiles = (a.total_tokens * upr + (int64_t)kBlock * np - 1) / ((int64_t)kBlock * np);
     magic = (uint32_t)(((uint64_t(1) << 32) + (uint64_t)upr - 1) / (uint64_t)upr);
   }
