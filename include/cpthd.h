@@ -150,10 +150,8 @@ enum cp_dtype {
  *                        rank's slice, without empty segments; n_local[r] = its
  *                        length - 1; the entries after it are T/W.
  *
- * Optional row maps (dual-chunk-swap with more than 64 documents; with fewer
- * the kernels stage the document table itself), written when the buffer holds
- * at least cp_meta_bytes_row_maps(B, W, T) bytes; cp_meta_header.row_maps is
- * then 1:
+ * Optional row maps (dual-chunk-swap), written when the buffer holds at least
+ * cp_meta_bytes_row_maps(B, W, T) bytes; cp_meta_header.row_maps is then 1:
  *   offset cp_meta_bytes(B, W)       int32 row_of_local[T]: global row of the
  *                                    flat local row p = r*(T/W) + i
  *   offset cp_meta_bytes(B, W) + 4T  int32 local_of_row[T]: the inverse
@@ -215,9 +213,8 @@ size_t cp_meta_bytes_row_maps(int32_t num_docs, int32_t cp_size, int64_t total_t
  *   cp_size       W in [1, 64]
  *   policy        enum cp_policy
  *   meta          device buffer of at least meta_bytes >= cp_meta_bytes(B, W),
- *                 16-byte aligned; under dual-chunk-swap with B > 64 and
- *                 meta_bytes >= cp_meta_bytes_row_maps(B, W, T) the row maps
- *                 are written too
+ *                 16-byte aligned; under dual-chunk-swap with meta_bytes >=
+ *                 cp_meta_bytes_row_maps(B, W, T) the row maps are written too
  * Host errors: CP_ERR_ARG (range, NULL), CP_ERR_SHAPE (packed-contiguous with
  * T % W != 0; meta_bytes too small), CP_ERR_DEVICE, CP_ERR_ALIAS (meta overlaps
  * cu_seqlens), CP_ERR_HIP.  Data errors (cu[0] != 0, decreasing cu, cu[B] != T,

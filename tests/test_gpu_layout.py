@@ -205,10 +205,10 @@ def test_thousands_of_documents(cp, B, H, D, dtype, row_maps):
 @pytest.mark.parametrize("B,W,T", [(65, 4, 65 * 8 * 3), (200, 8, 200 * 16 * 2), (3000, 2, 3000 * 4 * 5),
                                    (66, 64, 66 * 128)])
 def test_row_maps_equal_the_oracle_map(cp, B, W, T):
-    """The row maps cp_build_meta writes (more than 64 documents, a buffer of
-    cp_meta_bytes_row_maps bytes) hold exactly the oracle's ownership map: row_of_local[r n + i]
-    is the global row of rank r's local row i, local_of_row its inverse.  Fewer documents, or
-    a buffer of cp_meta_bytes only, give no maps (header field 0)."""
+    """The row maps cp_build_meta writes (dual-chunk-swap, a buffer of cp_meta_bytes_row_maps
+    bytes) hold exactly the oracle's ownership map: row_of_local[r n + i] is the global row of
+    rank r's local row i, local_of_row its inverse.  A buffer of cp_meta_bytes only, or
+    packed-contiguous metadata, gives no maps (header field 0)."""
     say(f"case row maps B={B} W={W} T={T}")
     rng = np.random.default_rng(B * W)
     lengths = rng.multinomial(T // (2 * W) - B, np.ones(B) / B) * 2 * W + 2 * W
@@ -223,11 +223,16 @@ def test_row_maps_equal_the_oracle_map(cp, B, W, T):
     inv = np.empty(T, dtype=np.int64)
     inv[ref] = np.arange(T)
     assert (g2l.numpy() == inv).all()
-    # no maps: a buffer of the tables alone, or <= 64 documents
+    # one document: the maps of Megatron's native layout
+    one = build(cp, np.array([0, T], dtype=np.int32), T, W, pol)
+    l2g1, _ = cp.read_row_maps(one)
+    ref1 = O.partition(np.arange(T, dtype=np.int64)[:, None], np.array([0, T]), W, policy_name(pol)).reshape(-1)
+    assert (l2g1.numpy() == ref1).all()
+    # no maps: a buffer of the tables alone, or packed-contiguous metadata
     small = build(cp, cu, T, W, pol, row_maps=False)
     assert cp.read_row_maps(small) is None
-    few = build(cp, np.array([0, T], dtype=np.int32), T, W, pol)
-    assert cp.read_row_maps(few) is None
+    pc = build(cp, cu, T, W, cp.CP_POLICY_PACKED_CONTIGUOUS)
+    assert cp.read_row_maps(pc) is None
 
 
 @pytest.mark.parametrize("H,D,dtype", [(3, 5, torch.bfloat16),     # 30 B rows: 2-byte units

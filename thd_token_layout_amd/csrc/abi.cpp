@@ -296,10 +296,9 @@ int cp_build_meta(const int32_t* cu_seqlens, int32_t num_docs, int64_t total_tok
   if (policy != CP_POLICY_DUAL_CHUNK_SWAP && policy != CP_POLICY_PACKED_CONTIGUOUS) return CP_ERR_ARG;
   if (policy == CP_POLICY_PACKED_CONTIGUOUS && total_tokens % cp_size != 0) return CP_ERR_SHAPE;
   if (meta_bytes < cp_meta_bytes(num_docs, cp_size)) return CP_ERR_SHAPE;
-  // Row maps when the buffer holds them and they help: dual-chunk-swap with
-  // more documents than the unit tiles stage in LDS (packed-contiguous rows
-  // follow from arithmetic; a few documents are searched in LDS as fast).
-  const bool row_maps = policy == CP_POLICY_DUAL_CHUNK_SWAP && total_tokens > 0 && num_docs > kStagedMaxDocs &&
+  // Row maps when the buffer holds them, under dual-chunk-swap (packed-
+  // contiguous rows follow from arithmetic).
+  const bool row_maps = policy == CP_POLICY_DUAL_CHUNK_SWAP && total_tokens > 0 &&
                         meta_bytes >= cp_meta_bytes_row_maps(num_docs, cp_size, total_tokens);
   const int64_t used = (int64_t)(row_maps ? cp_meta_bytes_row_maps(num_docs, cp_size, total_tokens)
                                           : cp_meta_bytes(num_docs, cp_size));

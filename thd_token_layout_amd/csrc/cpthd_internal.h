@@ -23,7 +23,7 @@ __host__ __device__ inline int64_t meta_n_local_offset(int32_t B, int32_t W) {
   return 64 + 4 * ((int64_t)B + 1) * ((int64_t)W + 1);
 }
 // Unit tiles stage the dual-chunk-swap document tables of up to this many
-// documents in LDS; cp_build_meta writes the row maps only above it.
+// documents in LDS (when they do not use the row maps).
 constexpr int32_t kStagedMaxDocs = 64;
 
 // cp_meta_bytes(B, W): header and tables, rounded up to 256 bytes; the

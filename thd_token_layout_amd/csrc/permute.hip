@@ -287,7 +287,10 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
 constexpr int kFlatMaxRows = 16;
 constexpr int kFlatMaxDocs = kStagedMaxDocs;
 
-template <int NP, bool GORDER>
+// MAPS: the instantiation for metadata the host built with row maps (a
+// separate kernel, so profiles tell the two lookups apart); it still checks the
+// header and searches the tables when the maps are absent.
+template <int NP, bool GORDER, bool MAPS>
 __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uint32_t upr_magic) {
   __shared__ const u32x4* s_src[kFlatMaxRows];
   __shared__ u32x4* s_dst[kFlatMaxRows];
@@ -306,7 +309,7 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
   // Dual-chunk-swap rows: from the row maps when the metadata has them (one
   // load per row), else from the document tables, staged in LDS when small
   // enough (searched there), else searched in the metadata.
-  const bool maps = dcs && hv.row_maps == 1;
+  const bool maps = MAPS && dcs && hv.row_maps == 1;
   const int32_t* row_of_local = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(h) +
                                                                  meta_tables_bytes(B, W));
   const int32_t* local_of_row = row_of_local + T;
@@ -501,9 +504,21 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   int64_t tiles = (a.total_tokens + v.rows_per_tile - 1) / v.rows_per_tile;
   uint32_t magic = 0;
   if (np != 0) {
-    flat_fn = np == 2 ? (order ? permute_flat_kernel<2, true> : permute_flat_kernel<2, false>)
-                      : (order ? permute_flat_kernel<3, true> : permute_flat_kernel<3, false>);
-    name = kFlatNames[np - 2][order][a.hint_row_maps ? 1 : 0];
+    // [NP - 2][order][row maps]
+    static void (*const kFlat[2][2][2])(PermuteArgs, uint32_t) = {
+        {{permute_flat_kernel<2, false, false>, permute_flat_kernel<2, false, true>},
+         {permute_flat_kernel<2, true, false>, permute_flat_kernel<2, true, true>}},
+        {{permute_flat_kernel<3, false, false>, permute_flat_kernel<3, false, true>},
+         {permute_flat_kernel<3, true, false>, permute_flat_kernel<3, true, true>}}};
+    // The row maps when the metadata has them, except for the gradient scatter
+    // (a per-owner pointer table) with few documents: measured on MI355X the
+    // maps speed up the layouts at any document count (one document: -2.7%)
+    // and the scatter from 65 documents on, but slow the few-document scatter
+    // (+0.6%) against the tables staged in LDS.
+    const bool staged_scatter = a.local_table && a.hint_docs <= kFlatMaxDocs;
+    const int m = a.hint_row_maps && a.hint_policy == CP_POLICY_DUAL_CHUNK_SWAP && !staged_scatter ? 1 : 0;
+    flat_fn = kFlat[np - 2][order][m];
+    name = kFlatNames[np - 2][order][m];
     tiles = (a.total_tokens * upr + (int64_t)kBlock * np - 1) / ((int64_t)kBlock * np);
     magic = (uint32_t)(((uint64_t(1) << 32) + (uint64_t)upr - 1) / (uint64_t)upr);
   }
