@@ -22,9 +22,9 @@ def cp():
     return cpthd
 
 
-def make_meta(cp, cu_np, T, W):
+def make_meta(cp, cu_np, T, W, row_maps=True):
     cu = torch.from_numpy(np.asarray(cu_np, dtype=np.int32)).to(DEV)
-    return cp.cp_build_meta(cu, T, W, cp.CP_POLICY_DUAL_CHUNK_SWAP, check=True)
+    return cp.cp_build_meta(cu, T, W, cp.CP_POLICY_DUAL_CHUNK_SWAP, check=True, row_maps=row_maps)
 
 
 def alloc(grads, W, out_dtype, fill=None):
@@ -269,14 +269,17 @@ def sampled_check(cp, grads, slots, out, cu, W, out_dtype, n_samples=256, seed=0
                     assert bits_equal(to_np(slots[t][o][w].index_select(0, lidx)), src[w]), (t, o, w)
 
 
-def test_grad_return_s256k_w4(cp):
+@pytest.mark.parametrize("row_maps", [True, False])
+def test_grad_return_s256k_w4(cp, row_maps):
+    """Both lookups of the scatter's unit tiles: the row maps, and without them the
+    document tables staged in LDS."""
     w = WL.WORKLOADS["grad_s256k_w4"]
-    say("case grad_s256k_w4 (full size)")
+    say(f"case grad_s256k_w4 (full size) row maps {row_maps}")
     cu = WL.cu_seqlens(w)
     W = w.cp_size
     vals = WL.random_tensors(w, 2 * W, device=DEV)
     grads = [vals[:W], vals[W:]]  # dK, dV of writers 0..3
-    meta = make_meta(cp, cu, w.total_tokens, W)
+    meta = make_meta(cp, cu, w.total_tokens, W, row_maps=row_maps)
     slots, out = alloc(grads, W, torch.float32)
     epochs = torch.zeros((W, W), dtype=torch.int32, device=DEV)
     cp.cp_grad_return(grads, slots, out, meta, epochs=epochs, epoch=1)

@@ -83,14 +83,17 @@ def test_tiny_dcs_and_pc(cp):
         assert got == g["dual_chunk_swap"][str(W)]["rows"]
 
 
+@pytest.mark.parametrize("row_maps", [True, False])
 @pytest.mark.parametrize("name", ["dcs_t32k_w4", "pc_t64k_w4"])
-def test_packed_documents_full_size(cp, name):
+def test_packed_documents_full_size(cp, name, row_maps):
+    """Without the row maps the 18-document dual-chunk-swap workload stages its document
+    tables in LDS; with them it looks rows up in the maps."""
     w = WL.WORKLOADS[name]
-    say(f"case {name}")
+    say(f"case {name} row maps {row_maps}")
     cu = WL.cu_seqlens(w)
     pol = cp.POLICY[w.policy]
     for x in WL.random_tensors(w, w.n_tensors, device=DEV):  # Q, K, V
-        check_layout(cp, x, cu, w.cp_size, pol)
+        check_layout(cp, x, cu, w.cp_size, pol, row_maps=row_maps)
 
 
 @pytest.mark.parametrize("name", ["dcs_t32k_w4", "pc_t64k_w4"])

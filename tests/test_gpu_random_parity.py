@@ -56,10 +56,11 @@ def test_random_case(cp, seed):
                      (torch.bfloat16, torch.bfloat16), (torch.bfloat16, torch.float32)][int(rng.integers(0, 4))]
     n_t = int(rng.integers(1, 4))
     accumulate = bool(rng.integers(0, 2))
+    row_maps = seed % 2 == 0  # half the cases build the dual-chunk-swap row maps
     say(f"case random seed={seed}: W={W} policy={pol} B={B} T={T} row=[{H},{D}] layout={layout_dt} "
-        f"grad {in_dt}->{out_dt} tensors={n_t} accumulate={accumulate}")
+        f"grad {in_dt}->{out_dt} tensors={n_t} accumulate={accumulate} row maps={row_maps}")
     gen = torch.Generator(device=DEV).manual_seed(seed)
-    meta = cp.cp_build_meta(torch.from_numpy(cu).to(DEV), T, W, pol, check=True)
+    meta = cp.cp_build_meta(torch.from_numpy(cu).to(DEV), T, W, pol, check=True, row_maps=row_maps)
 
     # metadata and attention-step tables
     local, n_local = cp.read_local_cu(meta)
