@@ -309,8 +309,9 @@ class Ceiling:
     `nbytes` each read and (write) one output of `nbytes` written, by the streaming
     kernels of libcpthd_roofline.so (full grid, contiguous tiles, 16-byte non-temporal
     loads, as the library's kernels), the best of 1, 2 and 3 units per thread (4, 8 and
-    12 KiB tiles) and, when writing, of two store policies (non-temporal global stores;
-    buffer stores with the nt and sc1 cache policy).  With `launches` = k, k such streams on k sets of buffers launched back
+    12 KiB tiles), of two load schedules (a thread's loads all in flight, or one at a
+    time) and, when writing, of two store policies (non-temporal global stores; buffer
+    stores with the nt and sc1 cache policy).  With `launches` = k, k such streams on k sets of buffers launched back
     to back and timed together (the ceiling of an operation that makes k launches of that
     size).  Timed like per_config: median of `reps` runs per shape, each after a 1 GiB
     write that flushes the last-level cache, with HIP events on the stream the kernels
@@ -342,16 +343,18 @@ class Ceiling:
         sink = ctypes.c_void_p(self.sink.data_ptr())
 
         def launch(shape):
-            np_, pol = shape
+            np_, pol, ser = shape
             stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
             for _, _, tab, outp in sets:
-                st = self.lib.cprl_stream(n_in, tab, outp, nbytes, np_, sink, pol, stream)
+                st = self.lib.cprl_stream(n_in, tab, outp, nbytes, np_, sink, pol | (2 if ser else 0), stream)
                 if st != 0:
                     raise RuntimeError(f"cprl_stream: status {st}")
 
         by_shape = {}
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        shapes = [(np_, pol) for pol in ((0, 1) if write else (0,)) for np_ in (1, 2, 3)]
+        # one load in flight differs from all in flight only with several loads per thread
+        shapes = [(np_, pol, ser) for ser in (0, 1) for pol in ((0, 1) if write else (0,)) for np_ in (1, 2, 3)
+                  if not ser or np_ * max(n_in, 1) > 1]
         for shape in shapes:
             launch(shape)
             ts = []
@@ -368,10 +371,12 @@ class Ceiling:
         moved = nbytes * (n_in + (1 if write else 0)) * launches
         mix = f"{n_in}:{1 if write else 0}" if n_in else "0:1"
         policy = ("nt", "nt+sc1")
+        loads = ("all in flight", "one in flight")
         res = {"mix": mix, "bytes_per_buffer": nbytes, "moved_bytes": moved, "median_us": round(us, 2),
                "gbs": round(moved / us / 1e3, 1), "units_per_thread": best[0], "stores": policy[best[1]],
-               "gbs_by_shape": {f"{k[0]} units/thread, {policy[k[1]]} stores": round(moved / v / 1e3, 1)
-                                for k, v in by_shape.items()}}
+               "loads": loads[best[2]],
+               "gbs_by_shape": {f"{k[0]} units/thread, {policy[k[1]]} stores, loads {loads[k[2]]}":
+                                round(moved / v / 1e3, 1) for k, v in by_shape.items()}}
         if launches > 1:
             res["launches"] = launches
         self.cache[key] = res

@@ -45,11 +45,14 @@ void remember_meta(const void* meta, const MetaRecord& r) {
   g_records[meta] = r;
 }
 
-// Fill the tile-shape hints of `a` from the record of `meta` when it matches
+// Fill the hints of `a` (tile shape, and the shape the unit-tile kernels start
+// their lookups from) from the record of `meta` when it matches
 // the call's token count (and CP size, when the call has one).
 void hint_from_record(const void* meta, int64_t total_tokens, int32_t cp_size, PermuteArgs* a) {
   a->hint_policy = -1;
   a->hint_docs = -1;
+  a->hint_cp_size = 0;
+  a->hint_local_tokens = 0;
   a->hint_row_maps = false;
   std::lock_guard<std::mutex> lock(g_records_mu);
   auto it = g_records.find(meta);
@@ -58,6 +61,8 @@ void hint_from_record(const void* meta, int64_t total_tokens, int32_t cp_size, P
   if (r.total_tokens != total_tokens || (cp_size > 0 && r.cp_size != cp_size)) return;
   a->hint_policy = r.policy;
   a->hint_docs = r.num_docs;
+  a->hint_cp_size = r.cp_size;
+  a->hint_local_tokens = r.total_tokens / r.cp_size;
   a->hint_row_maps = r.row_maps;
 }
 

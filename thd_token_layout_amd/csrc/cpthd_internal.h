@@ -84,12 +84,15 @@ struct PermuteArgs {
   int64_t row_bytes;
   int32_t expect_cp_size;   // -1: any
   int32_t expect_policy;    // -1: any
-  // Host-side record of the metadata (policy and document count when the host
-  // built it at this address; -1: unknown).  Chooses the tile shape only: the
-  // kernels read the metadata itself on the device.
+  // Host-side record of the metadata (policy, document count and CP size when
+  // the host built it at this address; -1 / 0: unknown).  Chooses the tile
+  // shape; the unit-tile kernels also start their first lookups from it and
+  // check it against the header before they touch the tensors.
   int32_t hint_policy;
   int32_t hint_docs;
-  bool hint_row_maps;  // the metadata was built with its row maps
+  int32_t hint_cp_size;
+  int64_t hint_local_tokens;  // T / W of the record
+  bool hint_row_maps;         // the metadata was built with its row maps
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 

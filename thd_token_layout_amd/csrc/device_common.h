@@ -41,6 +41,31 @@ __device__ __forceinline__ cp_meta_header read_header(const cp_meta_header* h) {
   return v;
 }
 
+// The same copy read in two steps, through vector memory into LDS: each wave
+// issues one 64-byte load straight into its own 16 LDS words
+// (load_header_lds), and later reads them back (header_from_lds, after
+// waiting for everything in flight).  Scalar loads return out of order and
+// share their counter with LDS accesses, so a kernel that waits for anything
+// scalar or in LDS also waits for a scalar header read in flight; a vector
+// load completes in order with the kernel's other global loads, so the header
+// can stay in flight during lookups issued after it, and landing in LDS it
+// holds no registers meanwhile.  `words` is the wave's 16 words of LDS.
+__device__ __forceinline__ void load_header_lds(const cp_meta_header* h, uint32_t* words) {
+  static_assert(sizeof(cp_meta_header) == 64, "the header is 64 bytes");
+  const int lane = threadIdx.x & 63;
+  if (lane < 4)
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(h) + 4 * lane, words, 16, 0, 0);
+}
+__device__ __forceinline__ cp_meta_header header_from_lds(const uint32_t* words) {
+  __builtin_amdgcn_s_waitcnt(0);
+  uint32_t u[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) u[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)words[k]);
+  cp_meta_header v;
+  __builtin_memcpy(&v, u, sizeof(v));
+  return v;
+}
+
 // Returns false, and records why in the sticky call flags of `h`, when a
 // kernel must not write any output: metadata never built, built from invalid
 // cu_seqlens, or built for another token count, CP size (expect_W >= 0) or

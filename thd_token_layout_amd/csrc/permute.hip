@@ -18,7 +18,8 @@
 //    16-byte units whatever the row length, with the touched rows looked up
 //    into LDS; used where that lookup is cheap (see there).
 // Lanes move 16-byte units with non-temporal loads, fully coalesced (a wave
-// touches 1 KiB contiguous per instruction).  Row tiles store with
+// touches 1 KiB contiguous per instruction); in the unit tiles each lane has
+// one load in flight at a time (see there).  Row tiles store with
 // non-temporal global stores; unit tiles store a tile's contiguous units
 // through a buffer resource with the nt and sc1 cache policy (measured on
 // MI355X: 1.5-4% faster for unit tiles, slower for row tiles).
@@ -287,43 +288,95 @@ __global__ void __launch_bounds__(kBlock) permute_rows_kernel(PermuteArgs a) {
 constexpr int kFlatMaxRows = 16;
 constexpr int kFlatMaxDocs = kStagedMaxDocs;
 
+// The metadata's shape as the unit-tile kernel uses it, and which dual-chunk-
+// swap lookup follows from it: the row maps when the metadata has them (one
+// load per row), else the document tables, staged in LDS when small enough
+// (searched there), else searched in the metadata.
+struct FlatShape {
+  int32_t W, B, policy;
+  int64_t n;  // T / W
+  bool dcs, maps, staged;
+};
+
+template <bool MAPS>
+__device__ __forceinline__ FlatShape flat_shape(int32_t W, int32_t B, int32_t policy, int64_t n, int32_t row_maps) {
+  FlatShape s;
+  s.W = W;
+  s.B = B;
+  s.policy = policy;
+  s.n = n;
+  s.dcs = policy == CP_POLICY_DUAL_CHUNK_SWAP;
+  s.maps = MAPS && s.dcs && row_maps == 1;
+  s.staged = s.dcs && !s.maps && B <= kFlatMaxDocs;
+  return s;
+}
+
 // MAPS: the instantiation for metadata the host built with row maps (a
 // separate kernel, so profiles tell the two lookups apart); it still checks the
 // header and searches the tables when the maps are absent.
-template <int NP, bool GORDER, bool MAPS>
+//
+// When the host has a record of the metadata (its shape when the host built
+// it at this address, in the hint_* arguments), the first tile's lookups start
+// from that shape while the header is still in flight, and the header is
+// checked before anything is loaded from the tensors: a header that fails the
+// check stops the kernel, one whose shape differs from the record (the buffer
+// rewritten since) has the lookups redone from the header.  Every load issued
+// before the check stays inside the metadata extent the host checked for the
+// record, or inside the tensors.  The header is read into LDS (no registers
+// held while it is in flight, so occupancy stays at 8 waves per SIMD), and the
+// gradient scatter's per-owner pointers are staged in LDS with it.  Measured
+// on MI355X against the header read first and the pointers read per row: the
+// gradient scatter 2-3% faster, the row-map layouts 1-1.5%.
+// TABLE: the gradient scatter's instantiation (the local side is a per-owner
+// pointer table); the layouts' instantiations carry no table code.
+template <int NP, bool GORDER, bool MAPS, bool TABLE>
 __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uint32_t upr_magic) {
   __shared__ const u32x4* s_src[kFlatMaxRows];
   __shared__ u32x4* s_dst[kFlatMaxRows];
   __shared__ int32_t s_rank[kFlatMaxRows];
   __shared__ int32_t s_cu[kFlatMaxDocs + 1];
   __shared__ int32_t s_lcu[kFlatMaxDocs + 1];
+  __shared__ char* s_owner[kMaxRanks];
+  __shared__ uint32_t s_header[kWavesPerBlock][16];
   cp_meta_header* h = a.meta;
-  const cp_meta_header hv = read_header(h);
-  if (!meta_ok(h, hv, a.total_tokens, a.expect_cp_size, a.expect_policy)) return;
-
+  uint32_t* const my_header = s_header[wave_uniform(threadIdx.x >> 6)];
   const int64_t T = a.total_tokens;
-  const int32_t W = hv.cp_size;
-  const int32_t B = hv.num_docs;
-  const int64_t n = hv.local_tokens;
-  const bool dcs = hv.policy == CP_POLICY_DUAL_CHUNK_SWAP;
-  // Dual-chunk-swap rows: from the row maps when the metadata has them (one
-  // load per row), else from the document tables, staged in LDS when small
-  // enough (searched there), else searched in the metadata.
-  const bool maps = MAPS && dcs && hv.row_maps == 1;
-  const int32_t* row_of_local = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(h) +
-                                                                 meta_tables_bytes(B, W));
-  const int32_t* local_of_row = row_of_local + T;
-  const bool staged = dcs && !maps && B <= kFlatMaxDocs;
-  if (staged) {
-    const int32_t* mcu = meta_cu(h);
-    const int32_t* mlcu = meta_local_cu0(h, B);
-    for (int k = threadIdx.x; k <= B; k += kBlock) {
-      s_cu[k] = mcu[k];
-      s_lcu[k] = mlcu[k];
+  // The host launches this kernel only with a record; without one the lookups
+  // start from a one-rank packed-contiguous shape (no table reads), which the
+  // header then replaces.
+  const bool hinted = a.hint_policy >= 0 && a.hint_cp_size > 0 && a.hint_docs >= 1 && a.hint_local_tokens > 0;
+  FlatShape s = flat_shape<MAPS>(hinted ? a.hint_cp_size : 1, hinted ? a.hint_docs : 1,
+                                 hinted ? a.hint_policy : (int32_t)CP_POLICY_PACKED_CONTIGUOUS,
+                                 hinted ? a.hint_local_tokens : T, hinted && a.hint_row_maps ? 1 : 0);
+  bool checked = false;
+  // LDS copies of the per-owner pointers (gradient scatter) and of the
+  // document tables (staged lookups): every load is issued before the first
+  // LDS write waits for them.  The row-map instantiation stages nothing before
+  // its first lookups (the host launches it for metadata recorded with maps),
+  // so its header read stays in flight through them.
+  static_assert(kBlock > kMaxRanks && kBlock > kFlatMaxDocs, "one element per thread");
+  auto stage = [&](bool owners) {
+    const int k = threadIdx.x;
+    char* own = nullptr;
+    int32_t c = 0, l = 0;
+    if (owners && k < kMaxRanks) own = a.table.p[k];
+    if (s.staged && k <= s.B) {
+      c = meta_cu(h)[k];
+      l = meta_local_cu0(h, s.B)[k];
     }
+    if (owners && k < kMaxRanks) s_owner[k] = own;
+    if (s.staged && k <= s.B) {
+      s_cu[k] = c;
+      s_lcu[k] = l;
+    }
+  };
+  // A barrier waits for every load into LDS in flight: the instantiations
+  // that stage tables issue the header read with them, the row-map one after
+  // its first barrier, ahead of its first lookups.
+  if constexpr (TABLE || !MAPS) {
+    load_header_lds(h, my_header);
+    stage(TABLE);
   }
-  const int32_t* cu = staged ? s_cu : meta_cu(h);
-  const int32_t* lcu = staged ? s_lcu : meta_local_cu0(h, B);
   const int64_t upr = a.row_bytes / 16;
   const int64_t total = T * upr;
   constexpr int64_t kTileUnits = (int64_t)kBlock * NP;
@@ -337,47 +390,71 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
     const int64_t row0 = u0 / upr;
     const int64_t u_end = u0 + kTileUnits < total ? u0 + kTileUnits : total;
     const int nrows = (int)((u_end - 1) / upr - row0 + 1);
-    __syncthreads();  // staged tables written; the previous tile's s_src / s_dst consumed
-    if ((int)threadIdx.x < nrows) {
-      // row p of the written side: a global row (gather) or a flat local row r*n + i
-      const int64_t p = row0 + threadIdx.x;
-      int32_t r;
-      int64_t i, g;
-      if (maps) {
-        // map entries are clamped to [0, T): rows stay inside the tensors
-        // whatever the buffer holds
-        const int64_t q = GORDER ? (int64_t)local_of_row[p] : p;
-        const int64_t qc = q < 0 ? 0 : (q >= T ? T - 1 : q);
-        r = (int32_t)(qc / n);
-        i = qc - (int64_t)r * n;
-        if constexpr (GORDER) {
-          g = p;
-        } else {
-          const int64_t gm = row_of_local[p];
-          g = gm < 0 ? 0 : (gm >= T ? T - 1 : gm);
-        }
-      } else if constexpr (GORDER) {
-        g = p;
-        if (dcs) {
-          GCursor gc;
-          gseek(gc, p, B, cu, lcu);
-          glocal(gc, W, &r, &i);
-        } else {
-          r = (int32_t)(p / n);
-          i = p - (int64_t)r * n;
-        }
-      } else {
-        Cursor k;
-        seek<false>(k, p, n, B, dcs, cu, lcu);
-        r = k.r;
-        i = k.i;
-        g = global_row(k, W, n, dcs);
+    for (;;) {
+      __syncthreads();  // staged tables written; the previous tile's s_src / s_dst consumed
+      if constexpr (MAPS && !TABLE) {
+        if (!checked) load_header_lds(h, my_header);
       }
-      char* gptr = gbase + g * a.row_bytes;
-      char* lptr = a.local_table ? a.table.p[r] + i * a.row_bytes : lbase + ((int64_t)r * n + i) * a.row_bytes;
-      s_src[threadIdx.x] = reinterpret_cast<const u32x4*>(a.to_local ? gptr : lptr);
-      s_dst[threadIdx.x] = reinterpret_cast<u32x4*>(a.to_local ? lptr : gptr);
-      s_rank[threadIdx.x] = r;
+      if ((int)threadIdx.x < nrows) {
+        const int32_t W = s.W, B = s.B;
+        const int64_t n = s.n;
+        const int32_t* cu = s.staged ? s_cu : meta_cu(h);
+        const int32_t* lcu = s.staged ? s_lcu : meta_local_cu0(h, B);
+        // row p of the written side: a global row (gather) or a flat local row r*n + i
+        const int64_t p = row0 + threadIdx.x;
+        int32_t r;
+        int64_t i, g;
+        if (s.maps) {
+          // map entries are clamped to [0, T): rows stay inside the tensors
+          // whatever the buffer holds
+          const int32_t* row_of_local = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(h) +
+                                                                         meta_tables_bytes(B, W));
+          const int32_t* local_of_row = row_of_local + T;
+          const int64_t q = GORDER ? (int64_t)local_of_row[p] : p;
+          const int64_t qc = q < 0 ? 0 : (q >= T ? T - 1 : q);
+          r = (int32_t)(qc / n);
+          i = qc - (int64_t)r * n;
+          if constexpr (GORDER) {
+            g = p;
+          } else {
+            const int64_t gm = row_of_local[p];
+            g = gm < 0 ? 0 : (gm >= T ? T - 1 : gm);
+          }
+        } else if constexpr (GORDER) {
+          g = p;
+          if (s.dcs) {
+            GCursor gc;
+            gseek(gc, p, B, cu, lcu);
+            glocal(gc, W, &r, &i);
+          } else {
+            r = (int32_t)(p / n);
+            i = p - (int64_t)r * n;
+          }
+        } else {
+          Cursor k;
+          seek<false>(k, p, n, B, s.dcs, cu, lcu);
+          r = k.r;
+          i = k.i;
+          g = global_row(k, W, n, s.dcs);
+        }
+        r = r < 0 ? 0 : (r >= W ? W - 1 : r);  // only a shape the header has not confirmed yet strays
+        char* gptr = gbase + g * a.row_bytes;
+        char* lptr = TABLE ? s_owner[r] + i * a.row_bytes : lbase + ((int64_t)r * n + i) * a.row_bytes;
+        s_src[threadIdx.x] = reinterpret_cast<const u32x4*>(a.to_local ? gptr : lptr);
+        s_dst[threadIdx.x] = reinterpret_cast<u32x4*>(a.to_local ? lptr : gptr);
+        s_rank[threadIdx.x] = r;
+      }
+      if (checked) break;
+      // the record's shape, checked against the header (uniform: every
+      // workgroup takes the same branch)
+      checked = true;
+      const cp_meta_header hv = header_from_lds(my_header);
+      if (!meta_ok(h, hv, T, a.expect_cp_size, a.expect_policy)) return;
+      const FlatShape hs = flat_shape<MAPS>(hv.cp_size, hv.num_docs, hv.policy, hv.local_tokens, hv.row_maps);
+      if (hs.W == s.W && hs.B == s.B && hs.policy == s.policy && hs.n == s.n && hs.maps == s.maps) break;
+      s = hs;
+      __syncthreads();  // every lookup above done before the tables are restaged
+      stage(false);
     }
     __syncthreads();
     const int64_t base = u0 - row0 * upr;  // offset of the tile's first unit inside row0
@@ -385,6 +462,11 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
     int row[NP];
     int64_t col[NP];
     bool ok[NP];
+    // One load in flight per lane: each is waited for before the next is
+    // issued.  Measured on MI355X: 3-7% faster than the tile's loads all in
+    // flight (the same trend as plain streams, which run fastest with one
+    // 16-byte load in flight per lane: HBM saturates with ~8 MiB in flight, and
+    // more only queues).
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
       const uint32_t f = (uint32_t)(base + (int64_t)m * kBlock + threadIdx.x);
@@ -392,12 +474,13 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
       row[m] = ok[m] ? (int)__umulhi(f, upr_magic) : 0;
       col[m] = (int64_t)f - (int64_t)row[m] * upr;
       if (ok[m]) v[m] = load_nt(s_src[row[m]] + col[m]);
+      __builtin_amdgcn_s_waitcnt(0);
     }
     // The tile's written units are contiguous in memory (the parts buffer in
     // local order, the global tensor in global order, one owner's slot of the
     // scatter unless the tile straddles two owners): stores through one buffer
     // resource over them, with the nt and sc1 cache policy.
-    const bool contiguous = GORDER || !a.local_table || wave_uniform(s_rank[0] == s_rank[nrows - 1]);
+    const bool contiguous = GORDER || !TABLE || wave_uniform(s_rank[0] == s_rank[nrows - 1]);
     if (contiguous) {
       char* const wtile = uniform_ptr(reinterpret_cast<char*>(s_dst[0])) + (u0 - row0 * upr) * 16;
       const __amdgpu_buffer_rsrc_t rs =
@@ -448,29 +531,32 @@ Variant g_variants[4][7] = {
     CP_VARIANTS_FOR(unsigned short, "2B"),
 };
 
-// Flat tiles (see permute_flat_kernel): NP units per thread, by the policy,
-// document count and row maps the host recorded when it built the metadata.
-// Swept on MI355X over 2, 5, 8 and 10 KiB rows: packed-contiguous streams best
-// with 2 units per thread (8 KiB tiles), dual-chunk-swap with 3 (with <= 64
-// documents, or any number when the row maps were built).  0: keep the row
-// tiles.
+// Flat tiles (see permute_flat_kernel) of kFlatUnits units per thread, for
+// metadata the host recorded when it built it: packed-contiguous, and
+// dual-chunk-swap with <= kFlatMaxDocs documents or with the row maps.
+// Swept on MI355X over 2, 5, 8 and 10 KiB rows with one load in flight per
+// lane: 3 units per thread (12 KiB tiles) streamed best under both policies
+// (packed-contiguous 1-1.5% ahead of 2 units, dual-chunk-swap 2-4% ahead of
+// 4).  0: keep the row tiles.
+constexpr int kFlatUnits = 3;
+
 int flat_units_per_thread(const PermuteArgs& a, int64_t upr) {
-  int np = 0;
-  if (a.hint_policy == CP_POLICY_PACKED_CONTIGUOUS) np = 2;
-  else if (a.hint_policy == CP_POLICY_DUAL_CHUNK_SWAP && a.hint_docs >= 1 &&
-           (a.hint_docs <= kFlatMaxDocs || a.hint_row_maps)) np = 3;
-  if (np == 0 || upr <= 0) return 0;
-  const int64_t tile_units = (int64_t)kBlock * np;
+  if (a.hint_cp_size <= 0 || a.hint_local_tokens <= 0 || a.hint_docs < 1) return 0;  // no record
+  if (a.local_table && !a.to_local) return 0;  // owner tables are only written in local order
+  const bool flat = a.hint_policy == CP_POLICY_PACKED_CONTIGUOUS ||
+                    (a.hint_policy == CP_POLICY_DUAL_CHUNK_SWAP && (a.hint_docs <= kFlatMaxDocs || a.hint_row_maps));
+  if (!flat || upr <= 0) return 0;
+  const int64_t tile_units = (int64_t)kBlock * kFlatUnits;
   if (tile_units / upr + 2 > kFlatMaxRows) return 0;            // short rows: row tiles
   if ((tile_units + upr) * upr >= (int64_t(1) << 32)) return 0;  // row split would not be exact
-  return np;
+  return kFlatUnits;
 }
 
-// [NP - 2][order][row maps]
-const char* const kFlatNames[2][2][2] = {{{"permute_flat<16B,2>", "permute_flat<16B,2,maps>"},
-                                          {"permute_flat<16B,2,g>", "permute_flat<16B,2,maps,g>"}},
-                                         {{"permute_flat<16B,3>", "permute_flat<16B,3,maps>"},
-                                          {"permute_flat<16B,3,g>", "permute_flat<16B,3,maps,g>"}}};
+// [kind: local order, global order, owner table][row maps]
+const char* const kFlatNames[3][2] = {{"permute_flat<16B,3>", "permute_flat<16B,3,maps>"},
+                                      {"permute_flat<16B,3,g>", "permute_flat<16B,3,maps,g>"},
+                                      {"permute_flat<16B,3,owners>", "permute_flat<16B,3,maps,owners>"}};
+static_assert(kFlatUnits == 3, "kFlatNames spell the unit count");
 
 }  // namespace
 
@@ -504,21 +590,21 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   int64_t tiles = (a.total_tokens + v.rows_per_tile - 1) / v.rows_per_tile;
   uint32_t magic = 0;
   if (np != 0) {
-    // [NP - 2][order][row maps]
-    static void (*const kFlat[2][2][2])(PermuteArgs, uint32_t) = {
-        {{permute_flat_kernel<2, false, false>, permute_flat_kernel<2, false, true>},
-         {permute_flat_kernel<2, true, false>, permute_flat_kernel<2, true, true>}},
-        {{permute_flat_kernel<3, false, false>, permute_flat_kernel<3, false, true>},
-         {permute_flat_kernel<3, true, false>, permute_flat_kernel<3, true, true>}}};
+    // [kind][row maps]
+    static void (*const kFlat[3][2])(PermuteArgs, uint32_t) = {
+        {permute_flat_kernel<kFlatUnits, false, false, false>, permute_flat_kernel<kFlatUnits, false, true, false>},
+        {permute_flat_kernel<kFlatUnits, true, false, false>, permute_flat_kernel<kFlatUnits, true, true, false>},
+        {permute_flat_kernel<kFlatUnits, false, false, true>, permute_flat_kernel<kFlatUnits, false, true, true>}};
+    const int kind = a.local_table ? 2 : order;
     // The row maps when the metadata has them, except for the gradient scatter
     // (a per-owner pointer table) with few documents: measured on MI355X the
     // maps speed up the layouts at any document count (one document: -2.7%)
     // and the scatter from 65 documents on, but slow the few-document scatter
-    // (+0.6%) against the tables staged in LDS.
+    // (one document: +1.8%) against the tables staged in LDS.
     const bool staged_scatter = a.local_table && a.hint_docs <= kFlatMaxDocs;
     const int m = a.hint_row_maps && a.hint_policy == CP_POLICY_DUAL_CHUNK_SWAP && !staged_scatter ? 1 : 0;
-    flat_fn = kFlat[np - 2][order][m];
-    name = kFlatNames[np - 2][order][m];
+    flat_fn = kFlat[kind][m];
+    name = kFlatNames[kind][m];
     tiles = (a.total_tokens * upr + (int64_t)kBlock * np - 1) / ((int64_t)kBlock * np);
     magic = (uint32_t)(((uint64_t(1) << 32) + (uint64_t)upr - 1) / (uint64_t)upr);
   }

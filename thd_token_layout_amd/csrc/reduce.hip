@@ -44,7 +44,9 @@ __device__ __forceinline__ bool grad_meta_ok(cp_meta_header* h, int64_t T, int32
 // ---- slot sum ----------------------------------------------------------------
 // A workgroup owns a tile of kBlock*UPT consecutive 8-element units; thread t
 // takes units t, t + kBlock, ... of the tile (coalesced per load instruction).
-template <int IN, int OUT, int WB, bool VEC, int UPT, bool ACC>
+// MODE 0: elements (unaligned pointers); 1: 8-element units, the loads of a
+// batch of slots in flight together; 2: 16-byte pieces, one load in flight.
+template <int IN, int OUT, int WB, int MODE, int UPT, bool ACC>
 __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
   if (a.gate_meta != nullptr) {
     cp_meta_header* h = a.gate_meta;
@@ -55,7 +57,34 @@ __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
   const int W = a.num_slots;
   constexpr bool SPLIT = split_layout<IN, OUT>();
   int64_t done = 0;
-  if constexpr (VEC) {
+  if constexpr (MODE == 2) {
+    static_assert(piece_layout<IN, OUT>(), "no piece layout for bf16 -> fp32");
+    // 16-byte input pieces, one load in flight per lane (units.h)
+    constexpr int E = piece_elems<IN>();
+    const int64_t npieces = a.n_elems / E;
+    const int64_t ntiles = (npieces + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+      int64_t piece[UPT], off[UPT];
+      bool ok[UPT];
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        piece[u] = tile * kBlock * UPT + (int64_t)u * kBlock + threadIdx.x;
+        ok[u] = piece[u] < npieces;
+        off[u] = 0;
+      }
+      F8 acc[UPT] = {};
+      if constexpr (ACC) {
+#pragma unroll
+        for (int u = 0; u < UPT; ++u)
+          if (ok[u]) load_out_piece<IN, OUT>(acc[u], a.out, piece[u]);
+      }
+      sum_pieces<IN, WB, UPT, ACC>(acc, a.in, W, off, piece, ok);
+#pragma unroll
+      for (int u = 0; u < UPT; ++u)
+        if (ok[u]) store_piece<IN, OUT>(a.out, piece[u], acc[u]);
+    }
+    done = npieces * E;
+  } else if constexpr (MODE == 1) {
     const int64_t nunits = a.n_elems / unit_group_elems<IN, OUT>() * (unit_group_elems<IN, OUT>() / 8);
     const int64_t ntiles = (nunits + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -159,8 +188,11 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
 // exact while the in-tile offset times units_per_row stays below 2^32.
 constexpr int kMaxTileRows = 16;
 
-template <int IN, int OUT, int WB, int NP, bool ACC>
+// PIECES: 16-byte pieces with one load in flight (units.h), else 8-element
+// units with the loads of a batch of writers in flight together.
+template <int IN, int OUT, int WB, int NP, bool ACC, bool PIECES>
 __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_t upr_magic) {
+  static_assert(!PIECES || piece_layout<IN, OUT>(), "no piece layout for bf16 -> fp32");
   __shared__ int64_t s_src[kMaxTileRows];
   __shared__ char* s_dst[kMaxTileRows];
   cp_meta_header* h = a.meta;
@@ -173,7 +205,7 @@ __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_
   const int32_t* lcu = meta_local_cu0(h, B);
   const int in_bytes = IN == CP_F32 ? 4 : 2;
   const int out_bytes = OUT == CP_F32 ? 4 : 2;
-  const int64_t upr = a.row_elems / 8;
+  const int64_t upr = a.row_elems / (PIECES ? piece_elems<IN>() : 8);  // units (pieces) per row
   const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * n;
   const int64_t total = rows * upr;
   constexpr int64_t kTileUnits = (int64_t)kBlock * NP;
@@ -204,16 +236,28 @@ __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_
       unit[m] = (int64_t)f - (int64_t)row[m] * upr;
       off[m] = s_src[row[m]];
     }
-    F8 acc[NP];
-    if constexpr (ACC) {
+    F8 acc[NP] = {};
+    if constexpr (PIECES) {
+      if constexpr (ACC) {
+#pragma unroll
+        for (int m = 0; m < NP; ++m)
+          if (ok[m]) load_out_piece<IN, OUT>(acc[m], s_dst[row[m]], unit[m]);
+      }
+      sum_pieces<IN, WB, NP, ACC>(acc, a.grads, W, off, unit, ok);
 #pragma unroll
       for (int m = 0; m < NP; ++m)
-        if (ok[m]) load_unit<OUT, split_layout<IN, OUT>()>(acc[m], s_dst[row[m]], unit[m]);
-    }
-    sum_units<IN, split_layout<IN, OUT>(), WB, NP, ACC>(acc, a.grads, W, off, unit, ok);
+        if (ok[m]) store_piece<IN, OUT>(s_dst[row[m]], unit[m], acc[m]);
+    } else {
+      if constexpr (ACC) {
 #pragma unroll
-    for (int m = 0; m < NP; ++m)
-      if (ok[m]) store_unit<OUT, split_layout<IN, OUT>()>(s_dst[row[m]], unit[m], acc[m]);
+        for (int m = 0; m < NP; ++m)
+          if (ok[m]) load_unit<OUT, split_layout<IN, OUT>()>(acc[m], s_dst[row[m]], unit[m]);
+      }
+      sum_units<IN, split_layout<IN, OUT>(), WB, NP, ACC>(acc, a.grads, W, off, unit, ok);
+#pragma unroll
+      for (int m = 0; m < NP; ++m)
+        if (ok[m]) store_unit<OUT, split_layout<IN, OUT>()>(s_dst[row[m]], unit[m], acc[m]);
+    }
     __syncthreads();  // s_src / s_dst are rewritten by the next tile
   }
 }
@@ -279,15 +323,23 @@ constexpr int kFusedWpr = 4;
 
 template <int IN, int OUT, int WB, bool ACC>
 hipError_t launch_sum_wb(const SlotSumArgs& a, bool vec, hipStream_t stream) {
-  constexpr int UPT = sum_upt(WB);
+  constexpr int UPT_UNITS = sum_upt(WB);
+  constexpr int UPT_PIECES = kSumPiecesPerThread;
   const std::string tag = std::string(ACC ? "slot_sum_acc<" : "slot_sum<") + dtype_tag(IN) + "," +
                           dtype_tag(OUT) + "," + std::to_string(WB) + ",";
-  static const std::string names[2] = {tag + "s>", tag + "v" + std::to_string(UPT) + ">"};
+  static const std::string names[3] = {tag + "s>", tag + "v" + std::to_string(UPT_UNITS) + ">",
+                                       tag + "p" + std::to_string(UPT_PIECES) + ">"};
+  const int64_t slot_bytes = a.n_elems * (IN == CP_F32 ? 4 : 2);
+  const int mode =
+      !vec ? 0 : piece_layout<IN, OUT>() && slot_bytes >= kPieceMinBytes && a.num_slots <= kPieceMaxSlots ? 2 : 1;
   int64_t blocks;
-  if (vec) {
+  if (mode == 2) {
+    const int64_t pieces = a.n_elems / piece_elems<IN>();
+    blocks = (pieces + (int64_t)kBlock * UPT_PIECES - 1) / ((int64_t)kBlock * UPT_PIECES);
+  } else if (mode == 1) {
     constexpr int64_t G = unit_group_elems<IN, OUT>();
     const int64_t units = a.n_elems / G * (G / 8);
-    blocks = (units + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
+    blocks = (units + (int64_t)kBlock * UPT_UNITS - 1) / ((int64_t)kBlock * UPT_UNITS);
     const int64_t tail = a.n_elems - units * 8;  // elements left to the scalar loop
     if (blocks == 0 && tail > 0) blocks = 1;
   } else {
@@ -295,12 +347,17 @@ hipError_t launch_sum_wb(const SlotSumArgs& a, bool vec, hipStream_t stream) {
   }
   if (blocks > kMaxGrid) blocks = kMaxGrid;
   if (blocks < 1) blocks = 1;
-  profile_before(names[vec ? 1 : 0].c_str(), stream);
-  if (vec)
-    hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, true, UPT, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0,
+  profile_before(names[mode].c_str(), stream);
+  if constexpr (piece_layout<IN, OUT>()) {
+    if (mode == 2)
+      hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, 2, UPT_PIECES, ACC>), dim3((unsigned)blocks), dim3(kBlock),
+                         0, stream, a);
+  }
+  if (mode == 1)
+    hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, 1, UPT_UNITS, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0,
                        stream, a);
-  else
-    hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, false, 1, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0,
+  else if (mode == 0)
+    hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, 0, 1, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0,
                        stream, a);
   hipError_t e = hipGetLastError();
   profile_after(stream);
@@ -322,42 +379,55 @@ hipError_t launch_sum_typed(const SlotSumArgs& a, bool vec, hipStream_t stream) 
                       : launch_sum_acc<IN, OUT, false>(a, vec, stream);
 }
 
+template <int IN, int OUT, int WB, int NP, bool ACC, bool PIECES>
+void launch_fused_flat(const FusedArgs& a, int64_t blocks, uint32_t magic, hipStream_t stream) {
+  hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, NP, ACC, PIECES>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                     stream, a, magic);
+}
+
 template <int IN, int OUT, int WB, bool ACC>
 hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
+  const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * (a.total_tokens / a.cp_size);
+  const int64_t writer_bytes = rows * a.row_elems * (IN == CP_F32 ? 4 : 2);  // read from each writer
+  // pieces by size and writer count (layout checked below)
+  const bool large = piece_layout<IN, OUT>() && writer_bytes >= kPieceMinBytes && a.cp_size <= kPieceMaxSlots;
   const std::string tag = std::string(ACC ? "fused_grad_return_acc<" : "fused_grad_return<") + dtype_tag(IN) +
                           "," + dtype_tag(OUT) + "," + std::to_string(WB) + ",";
-  static const std::string names[4] = {tag + "s>", tag + "flat1>", tag + "flat2>",
-                                       tag + "v" + std::to_string(fused_upl(WB)) + "/" +
-                                           std::to_string(kFusedWpr) + ">"};
-  vec = vec && a.row_elems % unit_group_elems<IN, OUT>() == 0;  // whole unit groups per row
-  const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * (a.total_tokens / a.cp_size);
-  const int64_t upr = a.row_elems / 8;
-  const int np = a.cp_size <= 4 ? 2 : 1;
-  const int64_t tile_units = (int64_t)kBlock * np;
-  // Flat unit tiles need the rows a tile touches to fit kMaxTileRows and
+  // [scalar, 4 waves per row, flat tiles of 1 or 2 units per thread, of pieces]
+  static const std::string names[5] = {
+      tag + "s>", tag + "v" + std::to_string(fused_upl(WB)) + "/" + std::to_string(kFusedWpr) + ">",
+      tag + "flat1>", tag + "flat2>", tag + "pieces" + std::to_string(kFusedPiecesPerThread) + ">"};
+  // Flat tiles need the rows a tile touches to fit kMaxTileRows and
   // (tile units + units_per_row) * units_per_row < 2^32 for the row split.
-  const bool flat_ok = upr > 0 && tile_units / upr + 2 <= kMaxTileRows &&
-                       (tile_units + upr) * upr < (int64_t(1) << 32);
-  // kind 0: scalar; 1, 2: flat unit tiles with NP = 1, 2; 3: 4 waves per row (very long rows)
-  const int kind = !vec ? 0 : !flat_ok ? 3 : np;
+  auto flat_fits = [](int64_t upr, int64_t tile_units) {
+    return upr > 0 && tile_units / upr + 2 <= kMaxTileRows && (tile_units + upr) * upr < (int64_t(1) << 32);
+  };
+  const bool vec_units = vec && a.row_elems % unit_group_elems<IN, OUT>() == 0;  // whole unit groups per row
+  const bool pieces = large && vec && a.row_elems % piece_elems<IN>() == 0 &&
+                      flat_fits(a.row_elems / piece_elems<IN>(), (int64_t)kBlock * kFusedPiecesPerThread);
+  const int64_t upr = a.row_elems / (pieces ? piece_elems<IN>() : 8);  // units (pieces) per row
+  const int np = pieces ? kFusedPiecesPerThread : a.cp_size <= 4 ? 2 : 1;
+  const int64_t tile_units = (int64_t)kBlock * np;
+  // kind 0: scalar; 1: 4 waves per row (very long rows); 2: flat tiles
+  const int kind = pieces ? 2 : !vec_units ? 0 : !flat_fits(upr, tile_units) ? 1 : 2;
   int64_t blocks;
-  if (kind == 1 || kind == 2) {
+  if (kind == 2) {
     blocks = (rows * upr + tile_units - 1) / tile_units;
   } else {
-    const int64_t rows_per_block = kind == 3 ? kWavesPerBlock / kFusedWpr : kWavesPerBlock;
+    const int64_t rows_per_block = kind == 1 ? kWavesPerBlock / kFusedWpr : kWavesPerBlock;
     blocks = (rows + rows_per_block - 1) / rows_per_block;
   }
   if (blocks > kMaxGrid) blocks = kMaxGrid;
   if (blocks < 1) blocks = 1;
   const uint32_t magic = upr > 0 ? (uint32_t)(((uint64_t(1) << 32) + (uint64_t)upr - 1) / (uint64_t)upr) : 0;
-  profile_before(names[kind].c_str(), stream);
-  if (kind == 1) {
-    hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, 1, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0, stream,
-                       a, magic);
+  profile_before(names[kind == 2 ? (pieces ? 4 : 1 + np) : kind].c_str(), stream);
+  if (kind == 2 && pieces) {
+    if constexpr (piece_layout<IN, OUT>())
+      launch_fused_flat<IN, OUT, WB, kFusedPiecesPerThread, ACC, true>(a, blocks, magic, stream);
   } else if (kind == 2) {
-    hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, 2, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0, stream,
-                       a, magic);
-  } else if (kind == 3) {
+    if (np == 1) launch_fused_flat<IN, OUT, WB, 1, ACC, false>(a, blocks, magic, stream);
+    else launch_fused_flat<IN, OUT, WB, 2, ACC, false>(a, blocks, magic, stream);
+  } else if (kind == 1) {
     hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, true, kFusedWpr, fused_upl(WB), ACC>),
                        dim3((unsigned)blocks), dim3(kBlock), 0, stream, a);
   } else {

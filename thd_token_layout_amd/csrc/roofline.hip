@@ -1,15 +1,17 @@
 // Plain streaming kernels for the benchmark's ceiling measurement: what one
 // MI355X streams for a given read/write mix and size with the library's
 // schedule (a full grid, one contiguous tile of kBlock * NP 16-byte units per
-// workgroup, non-temporal loads) and the best of NP = 1, 2, 3 units per thread
-// and of two store policies: non-temporal global stores, or buffer stores over
-// the workgroup's tile with the nt and sc1 cache policy (measured faster on
-// MI355X for a copy).  A plain copy streams best with one unit per thread (4 KiB
-// per workgroup); the library's kernels need 8-20 KiB tiles to amortise their
-// per-tile row lookup, so the ceiling is taken over the tile shapes, not at the
-// library's.  The layout, scatter and sum kernels are compared with the stream
-// of the same mix and size.  Built into its own library
-// (libcpthd_roofline.so), not part of the cpthd boundary.
+// workgroup, non-temporal loads) and the best of NP = 1, 2, 3 units per thread,
+// of two store policies (non-temporal global stores, or buffer stores over the
+// workgroup's tile with the nt and sc1 cache policy, measured faster on MI355X
+// for a copy) and of two load schedules (a thread's loads all in flight, or one
+// at a time, each waited for before the next: measured faster on MI355X for
+// every mix with several loads per thread).  A plain copy streams best with
+// one unit per thread (4 KiB per workgroup); the library's kernels need 8-20
+// KiB tiles to amortise their per-tile row lookup, so the ceiling is taken over
+// the tile shapes, not at the library's.  The layout, scatter and sum kernels
+// are compared with the stream of the same mix and size.  Built into its own
+// library (libcpthd_roofline.so), not part of the cpthd boundary.
 //
 //   n_in inputs, an output:   out[u] = in_0[u] ^ ... ^ in_{n_in-1}[u]
 //   n_in inputs, no output:   read only (each workgroup folds what it read
@@ -36,7 +38,7 @@ struct InPtrs {
 constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kStoreNtSc1 = 2 | 16;
 
-template <int NIN, bool WRITE, int NP, bool SC1>
+template <int NIN, bool WRITE, int NP, bool SC1, bool SER>
 __global__ void __launch_bounds__(kBlock) stream_kernel(InPtrs in, u32x4* out, int64_t units, uint32_t* sink) {
   constexpr int64_t kTile = (int64_t)kBlock * NP;
   const int64_t ntiles = (units + kTile - 1) / kTile;
@@ -51,8 +53,12 @@ __global__ void __launch_bounds__(kBlock) stream_kernel(InPtrs in, u32x4* out, i
       v[m] = u32x4{(uint32_t)u, (uint32_t)(u >> 32), 0x9E3779B9u, 0x7F4A7C15u};
       if (NIN > 0 && ok[m]) {
         v[m] = __builtin_nontemporal_load(in.p[0] + u);
+        if constexpr (SER) __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-        for (int k = 1; k < NIN; ++k) v[m] ^= __builtin_nontemporal_load(in.p[k] + u);
+        for (int k = 1; k < NIN; ++k) {
+          v[m] ^= __builtin_nontemporal_load(in.p[k] + u);
+          if constexpr (SER) __builtin_amdgcn_s_waitcnt(0);
+        }
       }
     }
     if constexpr (WRITE && SC1) {
@@ -78,15 +84,22 @@ __global__ void __launch_bounds__(kBlock) stream_kernel(InPtrs in, u32x4* out, i
 
 typedef void (*StreamFn)(InPtrs, u32x4*, int64_t, uint32_t*);
 
-template <int NIN, int NP>
+template <int NIN, int NP, bool SER>
 StreamFn pick_np(bool write, bool sc1) {
-  return !write ? stream_kernel<NIN, false, NP, false>
-                : sc1 ? stream_kernel<NIN, true, NP, true> : stream_kernel<NIN, true, NP, false>;
+  return !write ? stream_kernel<NIN, false, NP, false, SER>
+                : sc1 ? stream_kernel<NIN, true, NP, true, SER> : stream_kernel<NIN, true, NP, false, SER>;
+}
+
+template <int NIN, bool SER>
+StreamFn pick_ser(bool write, int np, bool sc1) {
+  return np == 1   ? pick_np<NIN, 1, SER>(write, sc1)
+         : np == 2 ? pick_np<NIN, 2, SER>(write, sc1)
+                   : pick_np<NIN, 3, SER>(write, sc1);
 }
 
 template <int NIN>
-StreamFn pick(bool write, int np, bool sc1) {
-  return np == 1 ? pick_np<NIN, 1>(write, sc1) : np == 2 ? pick_np<NIN, 2>(write, sc1) : pick_np<NIN, 3>(write, sc1);
+StreamFn pick(bool write, int np, bool sc1, bool ser) {
+  return ser ? pick_ser<NIN, true>(write, np, sc1) : pick_ser<NIN, false>(write, np, sc1);
 }
 
 }  // namespace
@@ -95,16 +108,17 @@ extern "C" {
 
 // Stream n_in (0..9) inputs of `bytes` each into `out` (NULL: read only), or
 // write `out` alone (n_in = 0), with `units_per_thread` (1..3) 16-byte units
-// per thread and tile; `store_policy` 0: non-temporal global stores, 1: buffer
-// stores with nt | sc1.  bytes must be a positive multiple of 16 and every
-// pointer 16-byte aligned; read-only runs need `sink` (>= 4 KiB, never written
-// in practice).  Asynchronous on `stream`.  Returns 0, or -1 on bad arguments
-// (nothing launched), or the HIP error of the launch.
+// per thread and tile.  `policy` bit 0: buffer stores with nt | sc1 (else
+// non-temporal global stores); bit 1: one load in flight per thread (else all
+// of a thread's loads in flight together).  bytes must be a positive multiple
+// of 16 and every pointer 16-byte aligned; read-only runs need `sink` (>= 4
+// KiB, never written in practice).  Asynchronous on `stream`.  Returns 0, or -1
+// on bad arguments (nothing launched), or the HIP error of the launch.
 int cprl_stream(int n_in, const void* const* in, void* out, int64_t bytes, int units_per_thread, void* sink,
-                int store_policy, hipStream_t stream) {
+                int policy, hipStream_t stream) {
   if (n_in < 0 || n_in > kMaxIn || bytes <= 0 || bytes % 16 != 0) return -1;
   if (units_per_thread < 1 || units_per_thread > 3) return -1;
-  if (store_policy != 0 && store_policy != 1) return -1;
+  if (policy < 0 || policy > 3) return -1;
   if (n_in == 0 && out == nullptr) return -1;
   if (out == nullptr && sink == nullptr) return -1;
   InPtrs p{};
@@ -118,11 +132,12 @@ int cprl_stream(int n_in, const void* const* in, void* out, int64_t bytes, int u
   int64_t blocks = (units + (int64_t)kBlock * np - 1) / ((int64_t)kBlock * np);
   if (blocks > kMaxGrid) blocks = kMaxGrid;
   const bool w = out != nullptr;
-  const bool sc1 = store_policy == 1;
-  StreamFn fns[kMaxIn + 1] = {pick<0>(true, np, sc1), pick<1>(w, np, sc1), pick<2>(w, np, sc1),
-                              pick<3>(w, np, sc1),    pick<4>(w, np, sc1), pick<5>(w, np, sc1),
-                              pick<6>(w, np, sc1),    pick<7>(w, np, sc1), pick<8>(w, np, sc1),
-                              pick<9>(w, np, sc1)};
+  const bool sc1 = (policy & 1) != 0;
+  const bool ser = (policy & 2) != 0;
+  StreamFn fns[kMaxIn + 1] = {pick<0>(true, np, sc1, ser), pick<1>(w, np, sc1, ser), pick<2>(w, np, sc1, ser),
+                              pick<3>(w, np, sc1, ser),    pick<4>(w, np, sc1, ser), pick<5>(w, np, sc1, ser),
+                              pick<6>(w, np, sc1, ser),    pick<7>(w, np, sc1, ser), pick<8>(w, np, sc1, ser),
+                              pick<9>(w, np, sc1, ser)};
   hipLaunchKernelGGL(fns[n_in], dim3((unsigned)blocks), dim3(kBlock), 0, stream, p, static_cast<u32x4*>(out),
                      units, static_cast<uint32_t*>(sink));
   return (int)hipGetLastError();

@@ -168,6 +168,83 @@ __device__ __forceinline__ void sum_units(F8 (&acc)[UPT], const ConstRankPtrs& i
   }
 }
 
+// ---- 16-byte input pieces ----------------------------------------------------
+// The layout with one load per lane and slot: a piece is the elements one
+// 16-byte load of the input holds (4 fp32 or 8 bf16), piece p being elements
+// [E p, E p + E), and the output keeps them at the same positions in its own
+// type (16 bytes for fp32 -> fp32 and bf16 -> bf16, 8 bytes for fp32 -> bf16),
+// so every wave instruction covers one contiguous span on both sides.  bf16 ->
+// fp32 would store 32 bytes per lane and keeps the split units above.
+template <int IN, int OUT>
+constexpr bool piece_layout() { return !(IN == CP_BF16 && OUT == CP_F32); }
+template <int IN>
+constexpr int piece_elems() { return IN == CP_F32 ? 4 : 8; }
+
+template <int IN>
+__device__ __forceinline__ void load_in_piece(F8& x, const char* base, int64_t piece) {
+  const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + piece);
+  if constexpr (IN == CP_F32) {
+    f32x4_from(x.v, a);
+  } else {
+    bf16x4_to_f32(x.v, u32x2{a.x, a.y});
+    bf16x4_to_f32(x.v + 4, u32x2{a.z, a.w});
+  }
+}
+
+// The output's piece (the accumulate mode's seed), widened to fp32.
+template <int IN, int OUT>
+__device__ __forceinline__ void load_out_piece(F8& x, const char* base, int64_t piece) {
+  static_assert(piece_layout<IN, OUT>(), "no piece layout for bf16 -> fp32");
+  if constexpr (OUT == CP_BF16 && IN == CP_F32)
+    bf16x4_to_f32(x.v, __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base) + piece));
+  else
+    load_in_piece<OUT>(x, base, piece);
+}
+
+template <int IN, int OUT>
+__device__ __forceinline__ void store_piece(char* base, int64_t piece, const F8& x) {
+  static_assert(piece_layout<IN, OUT>(), "no piece layout for bf16 -> fp32");
+  if constexpr (OUT == CP_F32) {
+    __builtin_nontemporal_store(f32x4_bits(x.v), reinterpret_cast<u32x4*>(base) + piece);
+  } else if constexpr (IN == CP_F32) {
+    __builtin_nontemporal_store(bf16x4_bits(x.v), reinterpret_cast<u32x2*>(base) + piece);
+  } else {
+    const u32x2 lo = bf16x4_bits(x.v), hi = bf16x4_bits(x.v + 4);
+    __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y}, reinterpret_cast<u32x4*>(base) + piece);
+  }
+}
+
+// Sum NP pieces over slots 0..W-1 in order, with one load in flight per lane:
+// every load is waited for before the next is issued.  Measured on MI355X
+// (plain 4:1 streams, 2.7 GB buffers): one 16-byte load in flight per lane
+// streams 6.4 TB/s, two 6.1, four 5.9-6.0.  `in` is the kernel argument table
+// (uniform), off[m] a byte offset applied to every slot for piece m, ok[m]
+// masks pieces past the end.  Without ACC the accumulator is seeded with slot
+// 0; with ACC the caller has seeded it and every slot is added.
+template <int IN, int WB, int NP, bool ACC>
+__device__ __forceinline__ void sum_pieces(F8 (&acc)[NP], const ConstRankPtrs& in, int W,
+                                           const int64_t (&off)[NP], const int64_t (&piece)[NP],
+                                           const bool (&ok)[NP]) {
+  constexpr int E = piece_elems<IN>();
+  auto add = [&](const char* slot, bool first) {
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+      F8 x{};
+      if (ok[m]) load_in_piece<IN>(x, slot + off[m], piece[m]);
+      __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[m].v[e] = first && !ACC ? x.v[e] : acc[m].v[e] + x.v[e];
+    }
+  };
+#pragma unroll
+  for (int w = 0; w < WB; ++w)
+    if (w < W) add(in.p[w], w == 0);
+  for (int w0 = WB; w0 < W; w0 += WB)
+#pragma unroll
+    for (int w = 0; w < WB; ++w)
+      if (w0 + w < W) add(in.p[w0 + w], false);
+}
+
 // Seed of the accumulate mode: the owner's current values, widened to fp32.
 template <int OUT, bool SPLIT, int UPT>
 __device__ __forceinline__ void seed_units(F8 (&acc)[UPT], const char* out, const int64_t (&unit)[UPT],
@@ -187,6 +264,21 @@ inline const char* dtype_tag(int dt) { return dt == CP_F32 ? "f32" : "bf16"; }
 // register use enough to lower occupancy (a W=8 bf16 sum with 2 units per
 // thread measured 25% slower).
 constexpr int sum_upt(int wb) { return wb <= 2 ? 4 : wb <= 4 ? 2 : 1; }
+// The piece layout (one load in flight per lane) serves sums of at most
+// kPieceMaxSlots slots of at least kPieceMinBytes each; smaller ones are
+// latency-bound, and with eight slots the serial chain per lane grows long
+// enough that a batch of loads in flight streams better (measured on MI355X:
+// eight 134 MB bf16 slots 197 us batched against 212 us one at a time; fused
+// return of eight 1 GiB writers 1552 against 1580 us), so those keep the
+// units.  Pieces per thread from a sweep (owner sum of four 671 MB fp32
+// slots: 536 us with one, 550 with two; fused return of four 2.7 GB writers:
+// 2105 us with two, 2288 with one, 2142-2164 with three or four): the owner
+// sum streams best with one, the fused return, which looks up its rows per
+// tile, with two.
+constexpr int64_t kPieceMinBytes = int64_t(32) << 20;
+constexpr int kPieceMaxSlots = 4;
+constexpr int kSumPiecesPerThread = 1;
+constexpr int kFusedPiecesPerThread = 2;
 
 }  // namespace
 }  // namespace cpthd
