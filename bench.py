@@ -354,7 +354,7 @@ class Ceiling:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         # one load in flight differs from all in flight only with several loads per thread
         shapes = [(np_, pol, ser) for ser in (0, 1) for pol in ((0, 1) if write else (0,)) for np_ in (1, 2, 3)
-                  if not ser or np_ * max(n_in, 1) > 1]
+                  if not ser or np_ * n_in > 1]
         for shape in shapes:
             launch(shape)
             ts = []
