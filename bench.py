@@ -310,8 +310,9 @@ class Ceiling:
     kernels of libcpthd_roofline.so (full grid, contiguous tiles, 16-byte non-temporal
     loads, as the library's kernels), the best of 1, 2 and 3 units per thread (4, 8 and
     12 KiB tiles), of two load schedules (a thread's loads all in flight, or one at a
-    time) and, when writing, of two store policies (non-temporal global stores; buffer
-    stores with the nt and sc1 cache policy).  With `launches` = k, k such streams on k sets of buffers launched back
+    time), with one unit per thread of 256- and 64-thread workgroups, and, when writing,
+    of two store policies (non-temporal global stores; buffer stores with the nt and sc1
+    cache policy).  With `launches` = k, k such streams on k sets of buffers launched back
     to back and timed together (the ceiling of an operation that makes k launches of that
     size).  Timed like per_config: median of `reps` runs per shape, each after a 1 GiB
     write that flushes the last-level cache, with HIP events on the stream the kernels
@@ -343,18 +344,20 @@ class Ceiling:
         sink = ctypes.c_void_p(self.sink.data_ptr())
 
         def launch(shape):
-            np_, pol, ser = shape
+            np_, pol, ser, small = shape
             stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
             for _, _, tab, outp in sets:
-                st = self.lib.cprl_stream(n_in, tab, outp, nbytes, np_, sink, pol | (2 if ser else 0), stream)
+                st = self.lib.cprl_stream(n_in, tab, outp, nbytes, np_, sink,
+                                          pol | (2 if ser else 0) | (4 if small else 0), stream)
                 if st != 0:
                     raise RuntimeError(f"cprl_stream: status {st}")
 
         by_shape = {}
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         # one load in flight differs from all in flight only with several loads per thread
-        shapes = [(np_, pol, ser) for ser in (0, 1) for pol in ((0, 1) if write else (0,)) for np_ in (1, 2, 3)
-                  if not ser or np_ * n_in > 1]
+        # 64-thread workgroups only with one unit per thread
+        shapes = [(np_, pol, ser, small) for small in (0, 1) for ser in (0, 1) for pol in ((0, 1) if write else (0,))
+                  for np_ in (1, 2, 3) if (not ser or np_ * n_in > 1) and (not small or np_ == 1)]
         for shape in shapes:
             launch(shape)
             ts = []
@@ -374,9 +377,10 @@ class Ceiling:
         loads = ("all in flight", "one in flight")
         res = {"mix": mix, "bytes_per_buffer": nbytes, "moved_bytes": moved, "median_us": round(us, 2),
                "gbs": round(moved / us / 1e3, 1), "units_per_thread": best[0], "stores": policy[best[1]],
-               "loads": loads[best[2]],
-               "gbs_by_shape": {f"{k[0]} units/thread, {policy[k[1]]} stores, loads {loads[k[2]]}":
-                                round(moved / v / 1e3, 1) for k, v in by_shape.items()}}
+               "loads": loads[best[2]], "threads_per_workgroup": 64 if best[3] else 256,
+               "gbs_by_shape": {f"{k[0]} units/thread, {policy[k[1]]} stores, loads {loads[k[2]]}, "
+                                f"{64 if k[3] else 256} threads": round(moved / v / 1e3, 1)
+                                for k, v in by_shape.items()}}
         if launches > 1:
             res["launches"] = launches
         self.cache[key] = res

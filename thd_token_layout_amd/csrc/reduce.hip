@@ -42,12 +42,13 @@ __device__ __forceinline__ bool grad_meta_ok(cp_meta_header* h, int64_t T, int32
 }
 
 // ---- slot sum ----------------------------------------------------------------
-// A workgroup owns a tile of kBlock*UPT consecutive 8-element units; thread t
-// takes units t, t + kBlock, ... of the tile (coalesced per load instruction).
+// A workgroup of BS threads owns a tile of BS*UPT consecutive units (8-element
+// units, or 16-byte pieces); thread t takes units t, t + BS, ... of the tile
+// (coalesced per load instruction).
 // MODE 0: elements (unaligned pointers); 1: 8-element units, the loads of a
 // batch of slots in flight together; 2: 16-byte pieces, one load in flight.
-template <int IN, int OUT, int WB, int MODE, int UPT, bool ACC>
-__global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
+template <int IN, int OUT, int WB, int MODE, int UPT, bool ACC, int BS = kBlock>
+__global__ void __launch_bounds__(BS) slot_sum_kernel(SlotSumArgs a) {
   if (a.gate_meta != nullptr) {
     cp_meta_header* h = a.gate_meta;
     const cp_meta_header hv = read_header(h);
@@ -62,13 +63,13 @@ __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
     // 16-byte input pieces, one load in flight per lane (units.h)
     constexpr int E = piece_elems<IN>();
     const int64_t npieces = a.n_elems / E;
-    const int64_t ntiles = (npieces + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
+    const int64_t ntiles = (npieces + (int64_t)BS * UPT - 1) / ((int64_t)BS * UPT);
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
       int64_t piece[UPT], off[UPT];
       bool ok[UPT];
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
-        piece[u] = tile * kBlock * UPT + (int64_t)u * kBlock + threadIdx.x;
+        piece[u] = tile * BS * UPT + (int64_t)u * BS + threadIdx.x;
         ok[u] = piece[u] < npieces;
         off[u] = 0;
       }
@@ -86,13 +87,13 @@ __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
     done = npieces * E;
   } else if constexpr (MODE == 1) {
     const int64_t nunits = a.n_elems / unit_group_elems<IN, OUT>() * (unit_group_elems<IN, OUT>() / 8);
-    const int64_t ntiles = (nunits + (int64_t)kBlock * UPT - 1) / ((int64_t)kBlock * UPT);
+    const int64_t ntiles = (nunits + (int64_t)BS * UPT - 1) / ((int64_t)BS * UPT);
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
       int64_t unit[UPT], off[UPT];
       bool ok[UPT];
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
-        unit[u] = tile * kBlock * UPT + (int64_t)u * kBlock + threadIdx.x;
+        unit[u] = tile * BS * UPT + (int64_t)u * BS + threadIdx.x;
         ok[u] = unit[u] < nunits;
         off[u] = 0;
       }
@@ -105,8 +106,8 @@ __global__ void __launch_bounds__(kBlock) slot_sum_kernel(SlotSumArgs a) {
     }
     done = nunits * 8;
   }
-  const int64_t gtid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  const int64_t gstride = (int64_t)gridDim.x * kBlock;
+  const int64_t gtid = (int64_t)blockIdx.x * BS + threadIdx.x;
+  const int64_t gstride = (int64_t)gridDim.x * BS;
   for (int64_t k = done + gtid; k < a.n_elems; k += gstride) {
     float acc = ACC ? load_elem<OUT>(a.out, k) + load_elem<IN>(a.in.p[0], k) : load_elem<IN>(a.in.p[0], k);
     for (int w = 1; w < W; ++w) acc = acc + load_elem<IN>(a.in.p[w], k);
@@ -179,9 +180,10 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
 }
 
 // Flat-tile variant: the owners' output rows are one flat range of
-// rows * units_per_row 8-element units, and a workgroup owns kBlock*NP
-// consecutive units of it (a tile may start and end inside a row), so every
-// thread does exactly NP units in one pass, as in the slot sum.  The first
+// rows * units_per_row units (8 elements, or 16-byte pieces), and a workgroup
+// of BS threads owns BS*NP consecutive units of it (a tile may start and end
+// inside a row), so every thread does exactly NP units in one pass, as in the
+// slot sum.  The first
 // threads look up the source offset and destination of the <= kMaxTileRows
 // rows the tile touches and share them through LDS.  The row of a unit is
 // found with a multiply-high by `upr_magic` = ceil(2^32 / units_per_row),
@@ -190,8 +192,8 @@ constexpr int kMaxTileRows = 16;
 
 // PIECES: 16-byte pieces with one load in flight (units.h), else 8-element
 // units with the loads of a batch of writers in flight together.
-template <int IN, int OUT, int WB, int NP, bool ACC, bool PIECES>
-__global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_t upr_magic) {
+template <int IN, int OUT, int WB, int NP, bool ACC, bool PIECES, int BS = kBlock>
+__global__ void __launch_bounds__(BS) fused_flat_kernel(FusedArgs a, uint32_t upr_magic) {
   static_assert(!PIECES || piece_layout<IN, OUT>(), "no piece layout for bf16 -> fp32");
   __shared__ int64_t s_src[kMaxTileRows];
   __shared__ char* s_dst[kMaxTileRows];
@@ -208,7 +210,7 @@ __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_
   const int64_t upr = a.row_elems / (PIECES ? piece_elems<IN>() : 8);  // units (pieces) per row
   const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * n;
   const int64_t total = rows * upr;
-  constexpr int64_t kTileUnits = (int64_t)kBlock * NP;
+  constexpr int64_t kTileUnits = (int64_t)BS * NP;
   const int64_t ntiles = (total + kTileUnits - 1) / kTileUnits;
 
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -230,8 +232,8 @@ __global__ void __launch_bounds__(kBlock) fused_flat_kernel(FusedArgs a, uint32_
     bool ok[NP];
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
-      const uint32_t f = (uint32_t)(base + (int64_t)m * kBlock + threadIdx.x);
-      ok[m] = u0 + (int64_t)m * kBlock + threadIdx.x < u_end;
+      const uint32_t f = (uint32_t)(base + (int64_t)m * BS + threadIdx.x);
+      ok[m] = u0 + (int64_t)m * BS + threadIdx.x < u_end;
       row[m] = ok[m] ? (int)__umulhi(f, upr_magic) : 0;
       unit[m] = (int64_t)f - (int64_t)row[m] * upr;
       off[m] = s_src[row[m]];
@@ -330,16 +332,17 @@ hipError_t launch_sum_wb(const SlotSumArgs& a, bool vec, hipStream_t stream) {
   static const std::string names[3] = {tag + "s>", tag + "v" + std::to_string(UPT_UNITS) + ">",
                                        tag + "p" + std::to_string(UPT_PIECES) + ">"};
   const int64_t slot_bytes = a.n_elems * (IN == CP_F32 ? 4 : 2);
-  const int mode =
-      !vec ? 0 : piece_layout<IN, OUT>() && slot_bytes >= kPieceMinBytes && a.num_slots <= kPieceMaxSlots ? 2 : 1;
+  const bool large = slot_bytes >= kPieceMinBytes;  // one-wave workgroups, pieces for <= kPieceMaxSlots slots
+  const int mode = !vec ? 0 : piece_layout<IN, OUT>() && large && a.num_slots <= kPieceMaxSlots ? 2 : 1;
+  const int64_t bs = large ? kSumBlock : kBlock;
   int64_t blocks;
   if (mode == 2) {
     const int64_t pieces = a.n_elems / piece_elems<IN>();
-    blocks = (pieces + (int64_t)kBlock * UPT_PIECES - 1) / ((int64_t)kBlock * UPT_PIECES);
+    blocks = (pieces + (int64_t)kSumBlock * UPT_PIECES - 1) / ((int64_t)kSumBlock * UPT_PIECES);
   } else if (mode == 1) {
     constexpr int64_t G = unit_group_elems<IN, OUT>();
     const int64_t units = a.n_elems / G * (G / 8);
-    blocks = (units + (int64_t)kBlock * UPT_UNITS - 1) / ((int64_t)kBlock * UPT_UNITS);
+    blocks = (units + bs * UPT_UNITS - 1) / (bs * UPT_UNITS);
     const int64_t tail = a.n_elems - units * 8;  // elements left to the scalar loop
     if (blocks == 0 && tail > 0) blocks = 1;
   } else {
@@ -350,10 +353,13 @@ hipError_t launch_sum_wb(const SlotSumArgs& a, bool vec, hipStream_t stream) {
   profile_before(names[mode].c_str(), stream);
   if constexpr (piece_layout<IN, OUT>()) {
     if (mode == 2)
-      hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, 2, UPT_PIECES, ACC>), dim3((unsigned)blocks), dim3(kBlock),
-                         0, stream, a);
+      hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, 2, UPT_PIECES, ACC, kSumBlock>), dim3((unsigned)blocks),
+                         dim3(kSumBlock), 0, stream, a);
   }
-  if (mode == 1)
+  if (mode == 1 && large)
+    hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, 1, UPT_UNITS, ACC, kSumBlock>), dim3((unsigned)blocks),
+                       dim3(kSumBlock), 0, stream, a);
+  else if (mode == 1)
     hipLaunchKernelGGL((slot_sum_kernel<IN, OUT, WB, 1, UPT_UNITS, ACC>), dim3((unsigned)blocks), dim3(kBlock), 0,
                        stream, a);
   else if (mode == 0)
@@ -379,9 +385,9 @@ hipError_t launch_sum_typed(const SlotSumArgs& a, bool vec, hipStream_t stream) 
                       : launch_sum_acc<IN, OUT, false>(a, vec, stream);
 }
 
-template <int IN, int OUT, int WB, int NP, bool ACC, bool PIECES>
+template <int IN, int OUT, int WB, int NP, bool ACC, bool PIECES, int BS = kBlock>
 void launch_fused_flat(const FusedArgs& a, int64_t blocks, uint32_t magic, hipStream_t stream) {
-  hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, NP, ACC, PIECES>), dim3((unsigned)blocks), dim3(kBlock), 0,
+  hipLaunchKernelGGL((fused_flat_kernel<IN, OUT, WB, NP, ACC, PIECES, BS>), dim3((unsigned)blocks), dim3(BS), 0,
                      stream, a, magic);
 }
 
@@ -389,8 +395,9 @@ template <int IN, int OUT, int WB, bool ACC>
 hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
   const int64_t rows = (int64_t)(a.owner_end - a.owner_begin) * (a.total_tokens / a.cp_size);
   const int64_t writer_bytes = rows * a.row_elems * (IN == CP_F32 ? 4 : 2);  // read from each writer
-  // pieces by size and writer count (layout checked below)
-  const bool large = piece_layout<IN, OUT>() && writer_bytes >= kPieceMinBytes && a.cp_size <= kPieceMaxSlots;
+  // one-wave workgroups by size, pieces also by writer count (layout checked below)
+  const bool large = writer_bytes >= kPieceMinBytes;
+  const bool large_pieces = piece_layout<IN, OUT>() && large && a.cp_size <= kPieceMaxSlots;
   const std::string tag = std::string(ACC ? "fused_grad_return_acc<" : "fused_grad_return<") + dtype_tag(IN) +
                           "," + dtype_tag(OUT) + "," + std::to_string(WB) + ",";
   // [scalar, 4 waves per row, flat tiles of 1 or 2 units per thread, of pieces]
@@ -403,11 +410,11 @@ hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
     return upr > 0 && tile_units / upr + 2 <= kMaxTileRows && (tile_units + upr) * upr < (int64_t(1) << 32);
   };
   const bool vec_units = vec && a.row_elems % unit_group_elems<IN, OUT>() == 0;  // whole unit groups per row
-  const bool pieces = large && vec && a.row_elems % piece_elems<IN>() == 0 &&
-                      flat_fits(a.row_elems / piece_elems<IN>(), (int64_t)kBlock * kFusedPiecesPerThread);
+  const bool pieces = large_pieces && vec && a.row_elems % piece_elems<IN>() == 0 &&
+                      flat_fits(a.row_elems / piece_elems<IN>(), (int64_t)kSumBlock * kFusedPiecesPerThread);
   const int64_t upr = a.row_elems / (pieces ? piece_elems<IN>() : 8);  // units (pieces) per row
   const int np = pieces ? kFusedPiecesPerThread : a.cp_size <= 4 ? 2 : 1;
-  const int64_t tile_units = (int64_t)kBlock * np;
+  const int64_t tile_units = (int64_t)(large ? kSumBlock : kBlock) * np;
   // kind 0: scalar; 1: 4 waves per row (very long rows); 2: flat tiles
   const int kind = pieces ? 2 : !vec_units ? 0 : !flat_fits(upr, tile_units) ? 1 : 2;
   int64_t blocks;
@@ -423,10 +430,15 @@ hipError_t launch_fused_wb(const FusedArgs& a, bool vec, hipStream_t stream) {
   profile_before(names[kind == 2 ? (pieces ? 4 : 1 + np) : kind].c_str(), stream);
   if (kind == 2 && pieces) {
     if constexpr (piece_layout<IN, OUT>())
-      launch_fused_flat<IN, OUT, WB, kFusedPiecesPerThread, ACC, true>(a, blocks, magic, stream);
+      launch_fused_flat<IN, OUT, WB, kFusedPiecesPerThread, ACC, true, kSumBlock>(a, blocks, magic, stream);
   } else if (kind == 2) {
-    if (np == 1) launch_fused_flat<IN, OUT, WB, 1, ACC, false>(a, blocks, magic, stream);
-    else launch_fused_flat<IN, OUT, WB, 2, ACC, false>(a, blocks, magic, stream);
+    if (large) {
+      if (np == 1) launch_fused_flat<IN, OUT, WB, 1, ACC, false, kSumBlock>(a, blocks, magic, stream);
+      else launch_fused_flat<IN, OUT, WB, 2, ACC, false, kSumBlock>(a, blocks, magic, stream);
+    } else {
+      if (np == 1) launch_fused_flat<IN, OUT, WB, 1, ACC, false>(a, blocks, magic, stream);
+      else launch_fused_flat<IN, OUT, WB, 2, ACC, false>(a, blocks, magic, stream);
+    }
   } else if (kind == 1) {
     hipLaunchKernelGGL((fused_kernel<IN, OUT, WB, true, kFusedWpr, fused_upl(WB), ACC>),
                        dim3((unsigned)blocks), dim3(kBlock), 0, stream, a);

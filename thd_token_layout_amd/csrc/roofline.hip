@@ -6,8 +6,9 @@
 // workgroup's tile with the nt and sc1 cache policy, measured faster on MI355X
 // for a copy) and of two load schedules (a thread's loads all in flight, or one
 // at a time, each waited for before the next: measured faster on MI355X for
-// every mix with several loads per thread).  A plain copy streams best with
-// one unit per thread (4 KiB per workgroup); the library's kernels need 8-20
+// every mix with several loads per thread) and, with one unit per thread, of
+// 256- and 64-thread workgroups.  A plain copy streams best with one unit per
+// thread in 64-thread workgroups (1 KiB each); the library's kernels need 8-20
 // KiB tiles to amortise their per-tile row lookup, so the ceiling is taken over
 // the tile shapes, not at the library's.  The layout, scatter and sum kernels
 // are compared with the stream of the same mix and size.  Built into its own
@@ -38,9 +39,9 @@ struct InPtrs {
 constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kStoreNtSc1 = 2 | 16;
 
-template <int NIN, bool WRITE, int NP, bool SC1, bool SER>
-__global__ void __launch_bounds__(kBlock) stream_kernel(InPtrs in, u32x4* out, int64_t units, uint32_t* sink) {
-  constexpr int64_t kTile = (int64_t)kBlock * NP;
+template <int NIN, bool WRITE, int NP, bool SC1, bool SER, int BS>
+__global__ void __launch_bounds__(BS) stream_kernel(InPtrs in, u32x4* out, int64_t units, uint32_t* sink) {
+  constexpr int64_t kTile = (int64_t)BS * NP;
   const int64_t ntiles = (units + kTile - 1) / kTile;
   u32x4 fold = {0u, 0u, 0u, 0u};
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -48,7 +49,7 @@ __global__ void __launch_bounds__(kBlock) stream_kernel(InPtrs in, u32x4* out, i
     bool ok[NP];
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
-      const int64_t u = tile * kTile + (int64_t)m * kBlock + threadIdx.x;
+      const int64_t u = tile * kTile + (int64_t)m * BS + threadIdx.x;
       ok[m] = u < units;
       v[m] = u32x4{(uint32_t)u, (uint32_t)(u >> 32), 0x9E3779B9u, 0x7F4A7C15u};
       if (NIN > 0 && ok[m]) {
@@ -68,11 +69,11 @@ __global__ void __launch_bounds__(kBlock) stream_kernel(InPtrs in, u32x4* out, i
           reinterpret_cast<char*>(out + tile * kTile), 0, (int)(t_units * 16), kRawBufferWord3);
 #pragma unroll
       for (int m = 0; m < NP; ++m)
-        if (ok[m]) __builtin_amdgcn_raw_buffer_store_b128(v[m], rs, (m * kBlock + (int)threadIdx.x) * 16, 0, kStoreNtSc1);
+        if (ok[m]) __builtin_amdgcn_raw_buffer_store_b128(v[m], rs, (m * BS + (int)threadIdx.x) * 16, 0, kStoreNtSc1);
     } else {
 #pragma unroll
       for (int m = 0; m < NP; ++m) {
-        const int64_t u = tile * kTile + (int64_t)m * kBlock + threadIdx.x;
+        const int64_t u = tile * kTile + (int64_t)m * BS + threadIdx.x;
         if (WRITE && ok[m]) __builtin_nontemporal_store(v[m], out + u);
         if (!WRITE && ok[m]) fold ^= v[m];
       }
@@ -84,10 +85,10 @@ __global__ void __launch_bounds__(kBlock) stream_kernel(InPtrs in, u32x4* out, i
 
 typedef void (*StreamFn)(InPtrs, u32x4*, int64_t, uint32_t*);
 
-template <int NIN, int NP, bool SER>
+template <int NIN, int NP, bool SER, int BS = kBlock>
 StreamFn pick_np(bool write, bool sc1) {
-  return !write ? stream_kernel<NIN, false, NP, false, SER>
-                : sc1 ? stream_kernel<NIN, true, NP, true, SER> : stream_kernel<NIN, true, NP, false, SER>;
+  return !write ? stream_kernel<NIN, false, NP, false, SER, BS>
+                : sc1 ? stream_kernel<NIN, true, NP, true, SER, BS> : stream_kernel<NIN, true, NP, false, SER, BS>;
 }
 
 template <int NIN, bool SER>
@@ -97,8 +98,10 @@ StreamFn pick_ser(bool write, int np, bool sc1) {
                    : pick_np<NIN, 3, SER>(write, sc1);
 }
 
+// 64-thread workgroups: one unit per thread only.
 template <int NIN>
-StreamFn pick(bool write, int np, bool sc1, bool ser) {
+StreamFn pick(bool write, int np, bool sc1, bool ser, bool small) {
+  if (small) return ser ? pick_np<NIN, 1, true, 64>(write, sc1) : pick_np<NIN, 1, false, 64>(write, sc1);
   return ser ? pick_ser<NIN, true>(write, np, sc1) : pick_ser<NIN, false>(write, np, sc1);
 }
 
@@ -110,7 +113,8 @@ extern "C" {
 // write `out` alone (n_in = 0), with `units_per_thread` (1..3) 16-byte units
 // per thread and tile.  `policy` bit 0: buffer stores with nt | sc1 (else
 // non-temporal global stores); bit 1: one load in flight per thread (else all
-// of a thread's loads in flight together).  bytes must be a positive multiple
+// of a thread's loads in flight together); bit 2: 64-thread workgroups (else
+// 256; with one unit per thread only).  bytes must be a positive multiple
 // of 16 and every pointer 16-byte aligned; read-only runs need `sink` (>= 4
 // KiB, never written in practice).  Asynchronous on `stream`.  Returns 0, or -1
 // on bad arguments (nothing launched), or the HIP error of the launch.
@@ -118,7 +122,9 @@ int cprl_stream(int n_in, const void* const* in, void* out, int64_t bytes, int u
                 int policy, hipStream_t stream) {
   if (n_in < 0 || n_in > kMaxIn || bytes <= 0 || bytes % 16 != 0) return -1;
   if (units_per_thread < 1 || units_per_thread > 3) return -1;
-  if (policy < 0 || policy > 3) return -1;
+  if (policy < 0 || policy > 7) return -1;
+  const bool small = (policy & 4) != 0;
+  if (small && units_per_thread != 1) return -1;
   if (n_in == 0 && out == nullptr) return -1;
   if (out == nullptr && sink == nullptr) return -1;
   InPtrs p{};
@@ -129,16 +135,18 @@ int cprl_stream(int n_in, const void* const* in, void* out, int64_t bytes, int u
   if (out != nullptr && (reinterpret_cast<uintptr_t>(out) & 15) != 0) return -1;
   const int64_t units = bytes / 16;
   const int np = units_per_thread;
-  int64_t blocks = (units + (int64_t)kBlock * np - 1) / ((int64_t)kBlock * np);
+  const int64_t bs = small ? 64 : kBlock;
+  int64_t blocks = (units + bs * np - 1) / (bs * np);
   if (blocks > kMaxGrid) blocks = kMaxGrid;
   const bool w = out != nullptr;
   const bool sc1 = (policy & 1) != 0;
   const bool ser = (policy & 2) != 0;
-  StreamFn fns[kMaxIn + 1] = {pick<0>(true, np, sc1, ser), pick<1>(w, np, sc1, ser), pick<2>(w, np, sc1, ser),
-                              pick<3>(w, np, sc1, ser),    pick<4>(w, np, sc1, ser), pick<5>(w, np, sc1, ser),
-                              pick<6>(w, np, sc1, ser),    pick<7>(w, np, sc1, ser), pick<8>(w, np, sc1, ser),
-                              pick<9>(w, np, sc1, ser)};
-  hipLaunchKernelGGL(fns[n_in], dim3((unsigned)blocks), dim3(kBlock), 0, stream, p, static_cast<u32x4*>(out),
+  StreamFn fns[kMaxIn + 1] = {
+      pick<0>(true, np, sc1, ser, small), pick<1>(w, np, sc1, ser, small), pick<2>(w, np, sc1, ser, small),
+      pick<3>(w, np, sc1, ser, small),    pick<4>(w, np, sc1, ser, small), pick<5>(w, np, sc1, ser, small),
+      pick<6>(w, np, sc1, ser, small),    pick<7>(w, np, sc1, ser, small), pick<8>(w, np, sc1, ser, small),
+      pick<9>(w, np, sc1, ser, small)};
+  hipLaunchKernelGGL(fns[n_in], dim3((unsigned)blocks), dim3((unsigned)bs), 0, stream, p, static_cast<u32x4*>(out),
                      units, static_cast<uint32_t*>(sink));
   return (int)hipGetLastError();
 }
