@@ -17,10 +17,12 @@
 // an agent-scope release store, the wait is a bounded spin with agent-scope
 // acquire loads (gfx950 has one L2 per XCD, so plain loads could stay stale).
 //
-// Design: HBM-bound streaming.  A thread handles units of 8 elements (laid out
-// so that every wave instruction touches one contiguous span; units.h),
-// issues the loads of a batch of WB slots before adding them in order, and
-// writes with non-temporal stores.
+// Design: HBM-bound streaming, two unit layouts (units.h), every wave
+// instruction touching one contiguous span.  Large sums of at most four slots
+// read 16-byte pieces, one load in flight per lane, slot after slot; other
+// sums handle units of 8 elements and issue the loads of a batch of WB slots
+// before adding them in order.  Both write with non-temporal stores.  Large
+// sums run in one-wave workgroups, smaller ones in 256-thread workgroups.
 // Launches cover all work with one small contiguous tile per workgroup (a full
 // grid rather than a resident-capacity persistent loop, which streams HBM less
 // contiguously and measured slower on MI355X).
@@ -319,9 +321,10 @@ epoch_wait_kernel(const uint32_t* epochs, int32_t W, int32_t owner, uint32_t epo
 // ---- dispatch -------------------------------------------------------------------
 constexpr int fused_upl(int wb) { return wb <= 2 ? 2 : 1; }
 constexpr int kFusedWpr = 4;
-// Fused shapes, from a sweep on the S=262144 (W=4 fp32) and S=131072 (W=8
-// bf16) shapes: flat unit tiles, 2 units per thread for W <= 4 (6.20 TB/s,
-// against 6.05 for a wave per row), 1 unit per thread above.
+// Fused shapes of the batched units, from a sweep on the S=262144 (W=4 fp32)
+// and S=131072 (W=8 bf16) shapes: flat unit tiles, 2 units per thread for
+// W <= 4 (6.20 TB/s, against 6.05 for a wave per row), 1 unit per thread
+// above.  The piece layout's shape is in units.h.
 
 template <int IN, int OUT, int WB, bool ACC>
 hipError_t launch_sum_wb(const SlotSumArgs& a, bool vec, hipStream_t stream) {
