@@ -153,15 +153,18 @@ class Step:
 
 
 def attribute_kernels(step: Step, cp, torch):
-    """Run each op once with timing hooks on and map kernel name -> bytes per launch."""
+    """Run each op once with timing hooks on and map kernel name -> bytes per launch;
+    also returns each kernel's milliseconds in that pass (which kernel dominates)."""
     per_kernel = {}
     mix = {}
+    ms = {}
     torch.cuda.synchronize()
     cp.cp_profile_enable(True)
     for name, nbytes, fn in step.ops:
         fn()
         prof = cp.cp_profile_read()
-        for kname, (count, _) in prof.items():
+        for kname, (count, kms) in prof.items():
+            ms[kname] = ms.get(kname, 0.0) + kms
             role = None
             if name.startswith("grad_return dK"):
                 role = "scatter" if kname.startswith("permute") else \
@@ -184,7 +187,7 @@ def attribute_kernels(step: Step, cp, torch):
     cp.cp_profile_enable(False)
     # bytes per step per kernel name, launches per step, stream mix per kernel name
     return {k: sum(c * b for c, b in v) for k, v in per_kernel.items()}, \
-        {k: sum(c for c, _ in v) for k, v in per_kernel.items()}, mix
+        {k: sum(c for c, _ in v) for k, v in per_kernel.items()}, mix, ms
 
 
 def counted_traffic(kernel: str):
@@ -759,13 +762,18 @@ def main():
     step = Step(cp, WL, torch, args.tokens, dev)
     torch.cuda.synchronize()
     log("[bench] attributing kernels")
-    kbytes, kcount, kmix = attribute_kernels(step, cp, torch)
+    kbytes, kcount, kmix, kms = attribute_kernels(step, cp, torch)
+    dominant = max(kms, key=kms.get)  # the kernel with the most time in one pass
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
 
-    log(f"[bench] timing {args.steps} steps")
+    # The timed steps record events around the dominant kernel's launches only:
+    # an event pair around every launch would add about 0.5 ms of GPU time per
+    # step (two event records per launch, about 55 launches).
+    log(f"[bench] timing {args.steps} steps (HIP events around {dominant})")
+    cp.cp_profile_select(dominant)
     cp.cp_profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -774,21 +782,34 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     cp.cp_profile_enable(False)
-    prof = cp.cp_profile_read(capacity=256)
+    cp.cp_profile_select(None)
+    prof_dom = cp.cp_profile_read(capacity=256)
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     step_bytes = step.step_bytes
     value = step_bytes / (ms_per_step / 1000.0) / 1e9
     log(f"[bench] {ms_per_step:.3f} ms/step, {value:.1f} GB/s")
+    # every kernel's time, from two more steps with events around every launch
+    prof_steps = 2
+    cp.cp_profile_enable(True)
+    for _ in range(prof_steps):
+        step.run()
+    torch.cuda.synchronize()
+    cp.cp_profile_enable(False)
+    prof_all = cp.cp_profile_read(capacity=256)
 
-    kernels = []
-    for name, (count, total_ms) in prof.items():
-        b = kbytes.get(name, 0) * args.steps
-        kernels.append({"kernel": name, "launches": count, "avg_us": round(total_ms * 1000 / count, 2),
-                        "total_ms": round(total_ms, 3),
-                        "gbs": round(b / (total_ms / 1000.0) / 1e9, 1) if total_ms > 0 and b else None,
-                        "bytes_per_launch": int(b / count) if count else 0})
+    def kernel_row(name, count, total_ms, steps, where):
+        b = kbytes.get(name, 0) * steps
+        return {"kernel": name, "launches": count, "avg_us": round(total_ms * 1000 / count, 2),
+                "total_ms": round(total_ms, 3),
+                "gbs": round(b / (total_ms / 1000.0) / 1e9, 1) if total_ms > 0 and b else None,
+                "bytes_per_launch": int(b / count) if count else 0, "timed": where}
+
+    kernels = [kernel_row(n, c, t, prof_steps, "profiled steps after the timed region")
+               for n, (c, t) in prof_all.items() if n != dominant]
     kernels.sort(key=lambda k: -k["total_ms"])
-    dom = kernels[0]
+    c, t = prof_dom[dominant]
+    dom = kernel_row(dominant, c, t, args.steps, "timed region")
+    kernels.insert(0, dom)
     achieved = dom["gbs"] or 0.0
     traffic = counted_traffic(dom["kernel"])
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

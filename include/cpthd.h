@@ -29,8 +29,10 @@
  *    supplied by the caller).  The library allocates no device memory.  The
  *    only host state kept between calls is the timing record of cp_profile_*
  *    and, per metadata buffer built by cp_build_meta, its policy and sizes,
- *    used to choose kernel tile shapes only (every kernel reads the metadata
- *    itself, so a buffer rewritten by other means still gives exact results).
+ *    used to choose kernel tile shapes and the shape the unit-tile kernels
+ *    start their row lookups from (every kernel checks the metadata itself and
+ *    follows it, so a buffer rewritten by other means still gives exact
+ *    results).
  *  - Host pointer tables (const void* const*) are read only during the call.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream) and never synchronizes, except cp_meta_status and
@@ -51,7 +53,7 @@
  *    there (both atomically, so calls on several streams may share one
  *    metadata buffer).  Nothing else in the buffer is written after
  *    cp_build_meta.  `meta` must be 16-byte aligned (CP_ERR_ARG otherwise):
- *    kernels read its 64-byte header in one scalar load.
+ *    kernels read its 64-byte header with 16-byte loads.
  *  - Outputs must not overlap inputs or each other (CP_ERR_ALIAS); [GR]
  *    "Description" (self-alias assertions on the rank-self slots).  The
  *    metadata header counts as an output of every call that takes `meta`, its
@@ -590,8 +592,14 @@ int cp_version(void);
  * number of distinct kernels (or a negative cp_status) and clears the record.
  * Meant for one calling thread: launches issued from several threads at once
  * while recording is on may be attributed to the wrong kernel name.
+ * cp_profile_select(name) limits the recording to the kernels reported under
+ * exactly that name (NULL or "": every kernel again); each recorded launch
+ * adds two event records to its stream, a few microseconds of GPU time, so a
+ * benchmark that times whole passes records only the kernel it reports.
+ * Returns CP_OK, or CP_ERR_ARG for a name longer than 127 characters.
  */
 int cp_profile_enable(int enable);
+int cp_profile_select(const char* name);
 int cp_profile_read(char* names, int64_t* counts, double* total_ms, int capacity);
 
 #ifdef __cplusplus

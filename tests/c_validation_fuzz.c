@@ -93,6 +93,20 @@ int main(int argc, char** argv) {
     st[n++] = cp_allreduce_signal(pick32(), ctable, table, pick64(), pick32(), fake(), (size_t)pick64(),
                                   (uint64_t)pick64(), pick64(), NULL);
     st[n++] = cp_allreduce_signal_status(fake(), pick32(), (uint64_t)pick64(), NULL);
+    {
+      char sel[160];
+      const int len = pick_small(0, 159);
+      for (int j = 0; j < len; ++j) sel[j] = (char)('a' + (next() % 26));
+      sel[len] = '\0';
+      const int use = (int)(next() & 1);
+      const int want = use && len > 127 ? CP_ERR_ARG : CP_OK;
+      const int got = cp_profile_select(use ? sel : NULL);
+      if (got != want) {
+        printf("iteration %ld: cp_profile_select returned %d\n", i, got);
+        ++bad;
+      }
+      (void)cp_profile_select(NULL);
+    }
     const int cap = pick_small(-2, 4);
     const int k = cp_profile_read(names, counts, ms, cap);
     if (k > 4 || k < -CP_ERR_META) {

@@ -136,6 +136,33 @@ def test_unit_tiles_straddling_owners(cp, policy, T):
         assert bits_equal(to_np(out[0][o]), ref_out[o]), o
 
 
+def test_profile_select_records_one_kernel(cp):
+    """cp_profile_select limits the launch timing to one kernel name; None restores all."""
+    say("case profile select")
+    T, W = 4096, 4
+    cu = np.array([0, T], dtype=np.int32)
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    grads = [[torch.randn((T, 4, 128), device=DEV, generator=gen) for _ in range(W)]]
+    meta = make_meta(cp, cu, T, W)
+    slots, out = alloc(grads, W, torch.float32)
+    cp.cp_profile_enable(True)
+    cp.cp_grad_return(grads, slots, out, meta)
+    every = cp.cp_profile_read()
+    scatter = next(k for k in every if k.startswith("permute_flat"))
+    assert any(k.startswith("slot_sum") for k in every), every
+    cp.cp_profile_select(scatter)
+    cp.cp_grad_return(grads, slots, out, meta)
+    only = cp.cp_profile_read()
+    cp.cp_profile_select(None)
+    cp.cp_grad_return(grads, slots, out, meta)
+    again = cp.cp_profile_read()
+    cp.cp_profile_enable(False)
+    assert list(only) == [scatter] and only[scatter][0] == W, only
+    assert set(again) == set(every), (again, every)
+    with pytest.raises(cp.CpError):
+        cp.cp_profile_select("k" * 200)
+
+
 @pytest.mark.parametrize("B,H,D", [(4100, 2, 64), (4000, 20, 128)])
 def test_thousands_of_documents(cp, B, H, D):
     """The gradient return under dual-chunk-swap metadata of more than 3969 documents (a

@@ -104,6 +104,8 @@ lib.cp_version.restype = _c.c_int
 lib.cp_version.argtypes = []
 lib.cp_profile_enable.restype = _c.c_int
 lib.cp_profile_enable.argtypes = [_c.c_int]
+lib.cp_profile_select.restype = _c.c_int
+lib.cp_profile_select.argtypes = [_c.c_char_p]
 lib.cp_profile_read.restype = _c.c_int
 lib.cp_profile_read.argtypes = [_c.c_char_p, _c.POINTER(_i64), _c.POINTER(_c.c_double), _c.c_int]
 
@@ -462,6 +464,11 @@ def cp_profile_enable(enable: bool = True) -> None:
     _check(lib.cp_profile_enable(1 if enable else 0), "cp_profile_enable")
 
 
+def cp_profile_select(name: Optional[str] = None) -> None:
+    """Record only the kernel reported under `name` (None: every kernel)."""
+    _check(lib.cp_profile_select(name.encode() if name else None), "cp_profile_select")
+
+
 def cp_profile_read(capacity: int = 64):
     """{kernel name: (launches, total ms)} recorded since the last read (synchronizes)."""
     names = ctypes.create_string_buffer(128 * capacity)
@@ -483,4 +490,4 @@ EXPORTED = ["cp_meta_bytes", "cp_meta_bytes_row_maps", "cp_build_meta", "cp_meta
             "cp_grad_return", "cp_grad_return_noalloc", "cp_grad_return_fused", "cp_slot_sum", "cp_allreduce",
             "cp_allreduce_signal_bytes", "cp_allreduce_signal", "cp_allreduce_signal_status",
             "cp_status_string", "cp_version",
-            "cp_profile_enable", "cp_profile_read"]
+            "cp_profile_enable", "cp_profile_select", "cp_profile_read"]

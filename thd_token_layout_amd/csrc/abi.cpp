@@ -223,6 +223,7 @@ struct ProfileRecord {
 };
 std::mutex g_prof_mutex;
 bool g_prof_enabled = false;
+std::string g_prof_only;  // record only this kernel name ("" = every kernel)
 std::vector<ProfileRecord> g_prof_records;
 std::vector<hipEvent_t> g_prof_free;
 std::string g_prof_pending_name;
@@ -249,6 +250,7 @@ hipEvent_t take_event() {
 void profile_before(const char* name, hipStream_t stream) {
   std::lock_guard<std::mutex> lock(g_prof_mutex);
   if (!g_prof_enabled || g_prof_records.size() >= kProfCapacity) return;
+  if (!g_prof_only.empty() && g_prof_only != name) return;
   hipEvent_t e = take_event();
   if (e == nullptr) return;
   if (hipEventRecord(e, stream) != hipSuccess) {
@@ -899,6 +901,13 @@ int cp_version(void) { return 300; }
 int cp_profile_enable(int enable) {
   std::lock_guard<std::mutex> lock(g_prof_mutex);
   g_prof_enabled = enable != 0;
+  return CP_OK;
+}
+
+int cp_profile_select(const char* name) {
+  if (name != nullptr && strnlen(name, 128) > 127) return CP_ERR_ARG;
+  std::lock_guard<std::mutex> lock(g_prof_mutex);
+  g_prof_only = name != nullptr ? name : "";
   return CP_OK;
 }
 
