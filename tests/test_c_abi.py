@@ -76,3 +76,18 @@ def test_find_doc_near_int32_max(tmp_path, flags):
                    check=True, capture_output=True, text=True)
     res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0 and "find_doc ok" in res.stdout, res.stdout + res.stderr
+
+
+@pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="hipcc not available")
+def test_row_chunk_index_arithmetic(tmp_path):
+    """The row-chunk kernel's index arithmetic (chunk_map.h), built for the host and run
+    over whole grids: every workgroup's row and chunk, every row's rank, local row and
+    global row against plain division and the ownership formula, all in range, each
+    global row written once; the magic-number division at edge and random arguments."""
+    exe = str(tmp_path / "chunk_map_host")
+    subprocess.run(["/opt/rocm/bin/hipcc", "-x", "hip", "--cuda-host-only", "-std=c++17", "-O2",
+                    "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+                    os.path.join(ROOT, "tests", "chunk_map_host.hip"), "-o", exe],
+                   check=True, capture_output=True, text=True)
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=240)
+    assert res.returncode == 0 and "chunk_map ok" in res.stdout, res.stdout + res.stderr

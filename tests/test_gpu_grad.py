@@ -111,11 +111,12 @@ def test_random_documents(cp, W, in_dt, out_dt):
 @pytest.mark.parametrize("T", [56, 200])
 def test_unit_tiles_straddling_owners(cp, policy, T):
     """The scatter's unit tiles write each tile through one buffer resource when its rows lie
-    in one owner's slot, and row by row when the tile straddles two owners: with 2 KiB rows a
-    tile covers 6 rows, so T/W = 14 or 50 rows per owner puts owner boundaries inside tiles.
-    The unit-tile kernel is the one launched (checked), every slot and output against the
-    oracle."""
-    W, H, D = 4, 4, 128
+    in one owner's slot, and row by row when the tile straddles two owners: with 1.5 KiB rows a
+    tile covers 8 rows, so T/W = 14 or 50 rows per owner puts owner boundaries inside tiles.
+    The unit-tile kernel is the one launched (checked; rows of 1.5 KiB, not a multiple of
+    1 KiB, keep packed-contiguous metadata off the row chunks), every slot and output
+    against the oracle."""
+    W, H, D = 4, 3, 128
     say(f"case straddling tiles {policy} T={T}")
     cu = np.array([0, 24, T], dtype=np.int32)  # two documents, each a multiple of 2W
     gen = torch.Generator(device=DEV)
@@ -148,7 +149,7 @@ def test_profile_select_records_one_kernel(cp):
     cp.cp_profile_enable(True)
     cp.cp_grad_return(grads, slots, out, meta)
     every = cp.cp_profile_read()
-    scatter = next(k for k in every if k.startswith("permute_flat"))
+    scatter = next(k for k in every if k.startswith("permute"))
     assert any(k.startswith("slot_sum") for k in every), every
     cp.cp_profile_select(scatter)
     cp.cp_grad_return(grads, slots, out, meta)

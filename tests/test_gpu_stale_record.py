@@ -1,12 +1,15 @@
 """The unit-tile permutation kernels start their row lookups from the host's
 record of the metadata (the shape it had when the host built it at that
-address) and check the header before they load anything from the tensors; a
-header whose shape differs from the record (the buffer rewritten behind the
-host's back, here by a device copy of other metadata) has the lookups redone
-from the header.  Every such case must still give the oracle's layout, inverse
-layout and gradient return for the metadata the buffer now holds: record and
-header differing in policy, in document count across the staged-table limit,
-and in whether the row maps are present."""
+address) and check the header before they load anything from the tensors; the
+row-chunk kernel (records of packed-contiguous or one-document metadata; the
+1 KiB bf16 rows and 2 KiB fp32 gradients here take it) loads its row under the
+recorded shape and checks the header before it stores.  A header whose shape
+differs from the record (the buffer rewritten behind the host's back, here by a
+device copy of other metadata) has the rows redone from the header.  Every such
+case must still give the oracle's layout, inverse layout and gradient return
+for the metadata the buffer now holds: record and header differing in policy,
+in document count (one, across the staged-table limit), and in whether the row
+maps are present."""
 import numpy as np
 import pytest
 import torch
@@ -70,7 +73,8 @@ def rewritten(cp, rec_kind, rec_maps, now_kind, now_maps):
 
 CASES = [("dcs116", True, "pc", False), ("dcs116", True, "dcs18", False), ("dcs116", True, "dcs1", True),
          ("pc", False, "dcs18", False), ("pc", False, "dcs116", True), ("dcs18", False, "dcs116", False),
-         ("dcs18", False, "pc", False), ("dcs1", True, "dcs116", False)]
+         ("dcs18", False, "pc", False), ("dcs1", True, "dcs116", False), ("dcs1", False, "pc", False),
+         ("pc", False, "dcs1", False)]
 
 
 @pytest.mark.parametrize("rec_kind,rec_maps,now_kind,now_maps", CASES)
