@@ -29,10 +29,10 @@
  *    supplied by the caller).  The library allocates no device memory.  The
  *    only host state kept between calls is the timing record of cp_profile_*
  *    and, per metadata buffer built by cp_build_meta, its policy and sizes,
- *    used to choose kernel tile shapes and the shape the unit-tile kernels
- *    start their row lookups from (every kernel checks the metadata itself and
- *    follows it, so a buffer rewritten by other means still gives exact
- *    results).
+ *    used to choose kernel tile shapes and the shape the permutation kernels
+ *    start their row lookups (or closed-form row maps) from (every kernel
+ *    checks the metadata itself and follows it, so a buffer rewritten by other
+ *    means still gives exact results).
  *  - Host pointer tables (const void* const*) are read only during the call.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream) and never synchronizes, except cp_meta_status and

@@ -5,24 +5,27 @@
 // dual-chunk-swap rank r holds chunk r then chunk 2W-1-r of every document;
 // under packed-contiguous rank r holds tokens [r n, (r+1) n), n = T/W.
 //
-// Design (gfx950): pure data movement, HBM-bound.  Two tilings, both with a
+// Design (gfx950): pure data movement, HBM-bound.  Three tilings, all with a
 // full grid (one tile per workgroup; measured on MI355X, concurrently running
 // workgroups then stream one contiguous window of HBM, while a resident-
 // capacity grid-stride loop, or several tiles per workgroup, streamed 5-20%
 // slower):
+//  - row chunks (permute_chunk_kernel): where the row map has a closed form
+//    (packed-contiguous, one-document dual-chunk-swap), one wave moves 1 KiB
+//    of one row, mapped by the formula in wave-uniform code (see there);
+//  - unit tiles (permute_flat_kernel): a workgroup owns a fixed number of
+//    16-byte units whatever the row length, with the touched rows looked up
+//    into LDS; used where that lookup is cheap (see there);
 //  - row tiles (permute_rows_kernel): a workgroup (4 waves) owns 8-20 KiB of
 //    consecutive local rows; the row map is computed once per group in
 //    wave-uniform code, a search of the per-rank document table and then an
-//    incremental cursor, so each wave runs independently;
-//  - unit tiles (permute_flat_kernel): a workgroup owns a fixed number of
-//    16-byte units whatever the row length, with the touched rows looked up
-//    into LDS; used where that lookup is cheap (see there).
+//    incremental cursor, so each wave runs independently.
 // Lanes move 16-byte units with non-temporal loads, fully coalesced (a wave
-// touches 1 KiB contiguous per instruction); in the unit tiles each lane has
-// one load in flight at a time (see there).  Row tiles store with
-// non-temporal global stores; unit tiles store a tile's contiguous units
-// through a buffer resource with the nt and sc1 cache policy (measured on
-// MI355X: 1.5-4% faster for unit tiles, slower for row tiles).
+// touches 1 KiB contiguous per instruction); in the row chunks and unit tiles
+// each lane has one load in flight at a time (see there).  Row tiles store
+// with non-temporal global stores; row chunks and unit tiles store their
+// contiguous units through a buffer resource with the nt and sc1 cache policy
+// (measured on MI355X: 1.5-4% faster for unit tiles, slower for row tiles).
 #include "chunk_map.h"
 #include "device_common.h"
 
