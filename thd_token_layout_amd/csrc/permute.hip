@@ -511,11 +511,12 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
 // the data load and checked before the store (a header that fails the check
 // stops the workgroup; one whose shape differs from the record, the buffer
 // rewritten since, has the row redone from the header's tables).  Measured on
-// MI355X against the unit tiles, S=262144: the one-document gradient scatter
-// of 10 KiB rows 822 -> 804 us, the one-document gather of 5 KiB rows -1%,
-// the partition -0.4%; packed-contiguous partition equal.  (With the row maps
-// the same shape is 5-8% slower than the unit tiles: the map read then sits on
-// each workgroup's path before its data load.)
+// MI355X against the unit tiles, S=262144, interleaved: the one-document
+// gradient scatter of 10 KiB rows 837 -> 809 us, the packed-contiguous
+// partition and gather of 5 KiB rows 410 -> 400 and 409 -> 403 us, the
+// one-document dual-chunk-swap ones -0.3..-0.7%.  (With the row maps the same
+// shape is 5-8% slower than the unit tiles: the map read then sits on each
+// workgroup's path before its only data load.)
 // GORDER: the gather (rows written in global order); else partition or, with
 // TABLE, the gradient scatter (rows written in local order, into the owners'
 // slots of the pointer table).
