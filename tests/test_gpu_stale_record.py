@@ -109,3 +109,38 @@ def test_grad_return_follows_the_header(cp, rec_kind, rec_maps, now_kind, now_ma
         for w in range(W):
             assert bits_equal(to_np(slots[0][o][w]), ref_slots[o][w]), (o, w)
         assert bits_equal(to_np(out[0][o]), ref_out[o]), o
+
+
+@pytest.mark.parametrize("rec_kind,rec_maps", [("pc", False), ("dcs1", True), ("dcs1", False), ("dcs116", True),
+                                               ("dcs18", False)])
+def test_rewritten_for_another_token_count_writes_nothing(cp, rec_kind, rec_maps):
+    """The buffer rewritten with metadata of another token count (T/2) while the host's
+    record still says T: every kernel loads under the record's shape (inside the tensors and
+    the recorded metadata extent), then the header check fails, so nothing is stored and the
+    call records a token-count mismatch; the row chunks (pc, dcs1 records) and the unit tiles
+    (dcs116, dcs18) alike."""
+    say(f"case stale record {rec_kind}{'+maps' if rec_maps else ''} -> header for T/2")
+    rec_bytes = (8 << 10) if rec_kind != "pc" and not rec_maps else (96 << 10)
+    rec, _ = build(cp, rec_kind, 3, rec_maps, rec_bytes)
+    half = cp.cp_build_meta(torch.tensor([0, T // 2], dtype=torch.int32, device=DEV), T // 2, W,
+                            cp.CP_POLICY_DUAL_CHUNK_SWAP, check=True, row_maps=False)
+    assert half.buf.numel() <= rec.buf.numel()
+    rec.buf[: half.buf.numel()].copy_(half.buf)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device=DEV).manual_seed(9)
+    x = torch.randn((T, H, D), generator=gen, device=DEV).to(torch.bfloat16)
+    parts = torch.full((W, T // W, H, D), 5.0, dtype=torch.bfloat16, device=DEV)
+    back = torch.full_like(x, 5.0)
+    cp.cp_partition_thd(x, rec, parts=parts)
+    cp.cp_gather_thd(x.view(W, T // W, H, D), rec, x=back)
+    grads = [[torch.randn((T, H, D), generator=gen, device=DEV) for _ in range(W)]]
+    slots = [[[torch.full((T // W, H, D), 5.0, device=DEV) for _ in range(W)] for _ in range(W)]]
+    out = [[torch.full((T // W, H, D), 5.0, device=DEV) for _ in range(W)]]
+    cp.cp_grad_return(grads, slots, out, rec)
+    st, flags, _ = cp.cp_meta_status(rec)
+    assert st == cp.CP_ERR_META and flags & cp.CP_CALL_TOKENS_MISMATCH, (st, flags)
+    assert (parts == 5.0).all() and (back == 5.0).all()
+    for o in range(W):
+        assert (out[0][o] == 5.0).all()
+        for w in range(W):
+            assert (slots[0][o][w] == 5.0).all()
