@@ -10,6 +10,7 @@
 // chunks of c = n / 2 rows and gives rank r chunk r, then chunk 2W-1-r.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace cpthd {
