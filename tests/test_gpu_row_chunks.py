@@ -4,8 +4,8 @@ are a multiple of 1 KiB: one wave per 1 KiB of a written row, the row's source a
 destination from the ownership formula.  Partition, gather and gradient scatter against
 the oracle element by element, for row lengths of 1, 2, 5 and 10 KiB, W = 1, 2, 3, 4 and
 8, the degenerate shapes (n = T/W = 1 or 2, so a chunk of one row under dual-chunk-swap),
-several tensors in one call, and a check of which kernel each call launched (rows of
-1.5 KiB and metadata of two documents keep the unit tiles)."""
+several tensors in one call, tensors not 256-byte aligned, and a check of which kernel each
+call launched (rows of 1.5 KiB and metadata of two documents keep the unit tiles)."""
 import numpy as np
 import pytest
 import torch
@@ -143,3 +143,53 @@ def test_other_shapes_keep_unit_tiles(cp, what):
     want = "permute_rows" if what == "no record" else "permute_flat"
     assert len(names) == 1 and names[0].startswith(want), names
     assert bits_equal(to_np(parts), O.partition(to_np(x), np.array(cu, np.int32), W, DCS))
+
+
+@pytest.mark.parametrize("policy", [PC, DCS])
+@pytest.mark.parametrize("offset", [16, 48, 1040])
+def test_unaligned_to_the_chunk(cp, policy, offset):
+    """Tensors that start 16, 48 or 1040 bytes into an allocation (16-byte aligned, so the
+    row chunks still serve them, but neither 256-byte nor 1 KiB aligned), rows of 1 KiB (fp16
+    layouts, bf16 gradients): layouts and gradient scatter against the oracle, bytes around
+    the layout outputs untouched."""
+    T, W, H, D = 1032, 4, 4, 128
+    say(f"case row chunks at byte offset {offset} {policy}")
+    cu = np.array([0, T], np.int32)
+    meta = meta_for(cp, cu, T, W, policy)
+    rb = H * D * 2
+    gen = torch.Generator(device=DEV).manual_seed(offset)
+
+    def view(shape, fill=None, dt=torch.float16):
+        n = int(np.prod(shape)) * 2
+        raw = torch.empty(n + offset + 1024, dtype=torch.uint8, device=DEV)
+        if fill is None:
+            raw.copy_(torch.randint(0, 256, raw.shape, generator=gen, device=DEV, dtype=torch.int64).to(torch.uint8))
+        else:
+            raw.fill_(fill)
+        return raw, raw[offset: offset + n].view(dt).view(shape)
+
+    _, x = view((T, H, D))
+    x.copy_(torch.randn((T, H, D), generator=gen, device=DEV).to(torch.float16))
+    raw_p, parts = view((W, T // W, H, D), fill=0xA5)
+    raw_b, back = view((T, H, D), fill=0x5A)
+    names = launched(cp, lambda: cp.cp_partition_thd(x, meta, parts=parts))
+    names += launched(cp, lambda: cp.cp_gather_thd(parts, meta, x=back))
+    assert names == ["permute_chunk<1KiB>", "permute_chunk<1KiB,g>"], names
+    assert bits_equal(to_np(parts), O.partition(to_np(x), cu, W, policy))
+    assert bits_equal(to_np(back), to_np(x))
+    for raw, n in ((raw_p, parts.numel() * 2), (raw_b, back.numel() * 2)):
+        fill = 0xA5 if raw is raw_p else 0x5A
+        assert (raw[:offset] == fill).all() and (raw[offset + n:] == fill).all()
+    assert rb == 1024
+    bf = torch.bfloat16
+    grads = [[view((T, H, D), dt=bf)[1] for _ in range(W)]]
+    for g in grads[0]:
+        g.copy_(torch.randn((T, H, D), generator=gen, device=DEV).to(bf))
+    slots = [[[view((T // W, H, D), dt=bf)[1] for _ in range(W)] for _ in range(W)]]
+    out = [[view((T // W, H, D), dt=bf)[1] for _ in range(W)]]
+    assert launched(cp, lambda: cp.cp_grad_return(grads, slots, out, meta)) == ["permute_chunk<1KiB,owners>"]
+    ref_slots, ref_out = O.grad_return([to_np(g) for g in grads[0]], cu, W, "bf16", "bf16", policy=policy)
+    for o in range(W):
+        for w in range(W):
+            assert bits_equal(to_np(slots[0][o][w]), ref_slots[o][w]), (o, w)
+        assert bits_equal(to_np(out[0][o]), ref_out[o]), o
