@@ -1,7 +1,8 @@
 """Every document split of small token counts through the GPU path: metadata,
 attention-step tables, partition and gather, each bit-exact against the oracle
 (packed-contiguous: T <= 8; dual-chunk-swap: up to 4 chunk-lengths per rank;
-W = 1..4)."""
+W = 1..4), the layouts in rows of 64 bytes (row tiles) and of 1 KiB (row chunks for
+packed-contiguous and one-document metadata, unit tiles with row maps otherwise)."""
 import numpy as np
 import pytest
 import torch
@@ -61,6 +62,12 @@ def test_every_small_document_split(cp, W):
             parts = cp.cp_partition_thd(x, meta)
             assert bits_equal(to_np(parts), O.partition(to_np(x), cu, W, POL[pol])), tag
             assert bits_equal(to_np(cp.cp_gather_thd(parts, meta)), to_np(x)), tag
+            # 1 KiB rows: the row chunks (packed-contiguous, one document) and the unit tiles
+            # with row maps (several documents)
+            y = torch.arange(T * 256, dtype=torch.float32, device=DEV).reshape(T, 2, 128)
+            py = cp.cp_partition_thd(y, meta)
+            assert bits_equal(to_np(py), O.partition(to_np(y), cu, W, POL[pol])), tag
+            assert bits_equal(to_np(cp.cp_gather_thd(py, meta)), to_np(y)), tag
         n_cases += 1
     say(f"case exhaustive small splits W={W}: {n_cases} splits")
     assert n_cases > 10
