@@ -5,7 +5,8 @@ destination from the ownership formula.  Partition, gather and gradient scatter 
 the oracle element by element, for row lengths of 1, 2, 5 and 10 KiB, W = 1, 2, 3, 4 and
 8, the degenerate shapes (n = T/W = 1 or 2, so a chunk of one row under dual-chunk-swap),
 several tensors in one call, tensors not 256-byte aligned, and a check of which kernel each
-call launched (rows of 1.5 KiB and metadata of two documents keep the unit tiles)."""
+call launched (rows of 1.5 KiB and metadata of two documents, with or without row maps,
+keep the unit tiles)."""
 import numpy as np
 import pytest
 import torch
@@ -120,15 +121,15 @@ def test_grad_scatter(cp, T, W, policy, H, D, dt):
         assert bits_equal(to_np(out[0][o]), ref_out[o]), o
 
 
-@pytest.mark.parametrize("what", ["rows of 1.5 KiB", "two documents", "no record"])
+@pytest.mark.parametrize("what", ["rows of 1.5 KiB", "two documents", "two documents, no row maps", "no record"])
 def test_other_shapes_keep_unit_tiles(cp, what):
-    """Rows not a multiple of 1 KiB, or a row map that needs the document tables, take the
-    unit tiles; metadata the host has no record of takes the row tiles.  Results against
-    the oracle either way."""
+    """Rows not a multiple of 1 KiB, or a row map that needs the row maps or the document
+    tables, take the unit tiles; metadata the host has no record of takes the row tiles.
+    Results against the oracle either way."""
     T, W = 4096, 4
     say(f"case row chunks not taken: {what}")
     H, cu = (6, [0, T]) if what == "rows of 1.5 KiB" else (4, [0, 1024, T])
-    meta = meta_for(cp, cu, T, W, DCS)
+    meta = meta_for(cp, cu, T, W, DCS, row_maps=what != "two documents, no row maps")
     if what == "no record":
         # a copy at an address no buffer of the allocator starts at (272 bytes into a new
         # allocation), so no metadata was ever built there

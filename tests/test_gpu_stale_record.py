@@ -3,7 +3,8 @@ record of the metadata (the shape it had when the host built it at that
 address) and check the header before they load anything from the tensors; the
 row-chunk kernel (records of packed-contiguous or one-document metadata; the
 1 KiB bf16 rows and 2 KiB fp32 gradients here take it) loads its row under the
-recorded shape and checks the header before it stores.  A header whose shape
+recorded shape and checks the header before it stores.  The layouts also run in
+1.5 KiB rows, which take the unit tiles whatever the record.  A header whose shape
 differs from the record (the buffer rewritten behind the host's back, here by a
 device copy of other metadata) has the rows redone from the header.  Every such
 case must still give the oracle's layout, inverse layout and gradient return
@@ -83,13 +84,14 @@ def test_layout_follows_the_header(cp, rec_kind, rec_maps, now_kind, now_maps):
         f"{'+maps' if now_maps else ''}")
     stale, cu, _ = rewritten(cp, rec_kind, rec_maps, now_kind, now_maps)
     gen = torch.Generator(device=DEV).manual_seed(7)
-    x = torch.randn((T, H, D), generator=gen, device=DEV).to(torch.bfloat16)
-    parts = cp.cp_partition_thd(x, stale)
-    back = cp.cp_gather_thd(parts, stale)
-    assert cp.cp_meta_status(stale)[0] == cp.CP_OK
-    ref = O.partition(to_np(x), cu, W, POLICY[now_kind])
-    assert bits_equal(to_np(parts), ref)
-    assert bits_equal(to_np(back), to_np(x))
+    for h in (H, 6):  # 1 KiB rows (the record decides the kernel), 1.5 KiB rows (never row chunks)
+        x = torch.randn((T, h, D), generator=gen, device=DEV).to(torch.bfloat16)
+        parts = cp.cp_partition_thd(x, stale)
+        back = cp.cp_gather_thd(parts, stale)
+        assert cp.cp_meta_status(stale)[0] == cp.CP_OK
+        ref = O.partition(to_np(x), cu, W, POLICY[now_kind])
+        assert bits_equal(to_np(parts), ref), h
+        assert bits_equal(to_np(back), to_np(x)), h
 
 
 @pytest.mark.parametrize("rec_kind,rec_maps,now_kind,now_maps", CASES)

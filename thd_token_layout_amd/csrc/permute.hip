@@ -515,8 +515,9 @@ __global__ void __launch_bounds__(kBlock) permute_flat_kernel(PermuteArgs a, uin
 // gradient scatter of 10 KiB rows 837 -> 809 us, the packed-contiguous
 // partition and gather of 5 KiB rows 410 -> 400 and 409 -> 403 us, the
 // one-document dual-chunk-swap ones -0.3..-0.7%.  (With the row maps the same
-// shape is 5-8% slower than the unit tiles: the map read then sits on each
-// workgroup's path before its only data load.)
+// shape is 5-8% slower than the unit tiles at S=262144, the map read then
+// sitting on each workgroup's path before its only data load, and no faster
+// at T=32768: 28.1-28.4 against 27.9 us per 67 MB tensor.)
 // GORDER: the gather (rows written in global order); else partition or, with
 // TABLE, the gradient scatter (rows written in local order, into the owners'
 // slots of the pointer table).
@@ -547,8 +548,16 @@ __global__ void __launch_bounds__(64) permute_chunk_kernel(PermuteArgs a, ChunkD
   auto written = [&](int32_t r_, int64_t i_) {
     return TABLE ? a.table.p[r_] + i_ * rb : (GORDER ? gbase : lbase) + (int64_t)p * rb;
   };
-  char* wrow = written(r, i);
   u32x4 v = load_nt(source(r, i, g, n));
+  char* wrow = written(r, i);
+  // The written row's address (the scatter's owner pointer) and the argument
+  // fields the check compares are read from the kernel arguments while the
+  // data load is in flight: left to the compiler, those scalar loads sat
+  // between the data's arrival and the store, one wait each (measured on
+  // MI355X: the scatter 0.3-0.8% faster with them in flight).
+  __builtin_amdgcn_sched_barrier(0);
+  __asm__ volatile("" : : "s"(wrow), "s"(a.hint_policy), "s"(a.hint_docs), "s"(a.expect_cp_size),
+                   "s"(a.expect_policy), "s"(a.total_tokens));
   const cp_meta_header hv = header_from_lds(words);  // waits for the load too
   if (!meta_ok(h, hv, a.total_tokens, a.expect_cp_size, a.expect_policy)) return;
   if (hv.policy != a.hint_policy || hv.cp_size != W || hv.local_tokens != n || (dcs && hv.num_docs != 1)) {
