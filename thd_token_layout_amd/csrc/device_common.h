@@ -26,12 +26,14 @@ __device__ __forceinline__ const int32_t* meta_local_cu0(const cp_meta_header* h
   return meta_cu(h) + (B + 1);
 }
 
-// A kernel's copy of the header: read once, first thing, before the kernel
-// stores anything, so one 64-byte scalar read serves the check and every later
-// use of a header field.  Measured on MI355X, per kernel: the unit-tile
-// permutation and the slot sum run 1-2% faster with the copy; the row-tile
-// permutation and the fused sum run 1-4% slower with it, so those read the
-// fields from the metadata as the check reaches them (the overload below).
+// A kernel's copy of the header: read once, before the kernel stores
+// anything, so one 64-byte scalar read serves the check and every later use of
+// a header field.  Measured on MI355X, per kernel: the slot sum runs 1-2%
+// faster with the copy read first; the row-chunk permutation reads it while
+// its data load is in flight; the row-tile permutation and the fused sum run
+// 1-4% slower with a copy, so those read the fields from the metadata as the
+// check reaches them (the overload below); the unit-tile permutation reads it
+// through LDS (below).
 __device__ __forceinline__ cp_meta_header read_header(const cp_meta_header* h) {
   typedef uint32_t u32x16 __attribute__((ext_vector_type(16), aligned(8)));
   static_assert(sizeof(cp_meta_header) == sizeof(u32x16), "the header is 64 bytes");
